@@ -1,0 +1,134 @@
+"""CPU oracle for the SSD scan and decode step (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never loads it, and the
+two share no code.
+
+* :func:`scan` / :func:`step` wrap the fp64 token-by-token recurrence in
+  ``ssd_oracle.c`` (the definition of the operation).
+* :mod:`oracle.chunked` is an fp64 numpy version of the chunked algorithm
+  (per-chunk matrix form plus a scan of chunk states), used to check the
+  recurrence and to give per-stage values.
+
+Every function takes numpy arrays or CPU torch tensors of any float dtype and
+converts them to float64 exactly (bf16 and fp32 values are representable).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.c_int64
+
+
+def build() -> str:
+    """Compile ssd_oracle.c with gcc (no fast-math, no FMA contraction, OpenMP)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call([
+        "gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-ffp-contract=off",
+        "-fno-fast-math", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm",
+    ])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.ssd_oracle_scan.argtypes = [_I64] * 6 + [_D] * 9 + [ctypes.c_int]
+        lib.ssd_oracle_scan.restype = ctypes.c_int
+        lib.ssd_oracle_step.argtypes = [_I64] * 5 + [_D] * 8 + [ctypes.c_int]
+        lib.ssd_oracle_step.restype = ctypes.c_int
+        lib.ssd_oracle_max_threads.argtypes = []
+        lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def f64(a) -> np.ndarray | None:
+    """Exact conversion of a numpy array or CPU torch tensor to contiguous float64."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        import torch
+        return np.ascontiguousarray(a.detach().to("cpu", torch.float64).numpy())
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def max_threads() -> int:
+    return _load().ssd_oracle_max_threads()
+
+
+def scan(x, dt, A, B, C, D=None, init=None, nthreads: int = 0):
+    """fp64 recurrence over the whole sequence.  Returns (y, final_state)."""
+    x, dt, A, B, C, D, init = (f64(v) for v in (x, dt, A, B, C, D, init))
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (Bt, L, H) and A.shape == (H,)
+    assert B.shape == (Bt, L, G, N) and C.shape == B.shape
+    assert D is None or D.shape == (H,)
+    assert init is None or init.shape == (Bt, H, P, N)
+    y = np.empty((Bt, L, H, P))
+    final = np.empty((Bt, H, P, N))
+    rc = _load().ssd_oracle_scan(Bt, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final),
+                                 int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape")
+    return y, final
+
+
+def step(state, x, dt, A, B, C, D=None, nthreads: int = 0):
+    """One fp64 decode step.  Returns (y, new_state); the input state is not modified."""
+    s = f64(state).copy()
+    x, dt, A, B, C, D = (f64(v) for v in (x, dt, A, B, C, D))
+    Bt, H, P, N = s.shape
+    G = B.shape[1]
+    assert x.shape == (Bt, H, P) and dt.shape == (Bt, H) and A.shape == (H,)
+    assert B.shape == (Bt, G, N) and C.shape == B.shape
+    y = np.empty((Bt, H, P))
+    rc = _load().ssd_oracle_step(Bt, H, P, N, G, _ptr(s), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                 _ptr(C), _ptr(D), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle: invalid shape")
+    return y, s
+
+
+def scan_heads(inputs: dict, pairs, nthreads: int = 0):
+    """Recurrence for selected (batch, head) pairs only.
+
+    ``inputs`` holds x, dt, A, B, C, D, init as produced for the full problem.
+    Returns {(b, h): (y [L,P], final [P,N])}.  Each pair is an independent
+    one-head problem, so sampled checks at large sizes stay cheap.
+    """
+    x, B = inputs["x"], inputs["B"]
+    H, G = x.shape[2], B.shape[2]
+    R = H // G
+    out = {}
+    for b, h in pairs:
+        g = h // R
+        init = inputs.get("init")
+        y, fin = scan(
+            x[b:b + 1, :, h:h + 1, :], inputs["dt"][b:b + 1, :, h:h + 1],
+            inputs["A"][h:h + 1], B[b:b + 1, :, g:g + 1, :], inputs["C"][b:b + 1, :, g:g + 1, :],
+            None if inputs.get("D") is None else inputs["D"][h:h + 1],
+            None if init is None else init[b:b + 1, h:h + 1],
+            nthreads=nthreads)
+        out[(b, h)] = (y[0, :, 0, :], fin[0, 0])
+    return out

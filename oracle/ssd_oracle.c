@@ -1,0 +1,148 @@
+/*
+ * CPU oracle for the Mamba-2 SSD selective scan and its cached decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no source, header or table with the HIP
+ * library.
+ *
+ * What it computes.  State-space duality makes A a single scalar per head, so
+ * the discretised transition of the selective recurrence is one scalar
+ * exponential per token and head ("Compiler-First State Space Duality and
+ * Portable O(1) Autoregressive Caching for Inference", paperlayer summary,
+ * §3 Method, "State-space duality"; B, C and the step size are inputs that vary
+ * per token).  With a = A[h], g the group of head h (heads split into ngroups
+ * contiguous blocks), for each batch row b, head h and channel p:
+ *
+ *     s     <- init_state[b,h,p,:]            (zero when no init state)
+ *     for t = 0 .. L-1:
+ *         r      = exp(dt[b,t,h] * a)
+ *         s[n]   = r * s[n] + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
+ *         y[b,t,h,p] = sum_n C[b,t,g,n] * s[n] + D[h] * x[b,t,h,p]
+ *     final_state[b,h,p,:] = s
+ *
+ * The output of token t therefore uses the state after token t's own update.
+ * The decode step is the loop body once, with the state carried between calls
+ * ("Compiler-First ...", §3 "Autoregressive cache": a fixed-size state makes
+ * each next-token update independent of the prefix length).  The chunk size of
+ * the chunked algorithm does not appear here: the recurrence is its definition.
+ *
+ * All arithmetic is IEEE double.  Rows (b, h, p) are independent and are the
+ * only thing run in parallel (OpenMP); inside a row the order is the token
+ * order above.  Build without fast-math and without FMA contraction.
+ *
+ * Layouts (row-major, contiguous):
+ *   x [Bt,L,H,P]  dt [Bt,L,H]  A [H]  B,C [Bt,L,G,N]  D [H]
+ *   init, final [Bt,H,P,N]  y [Bt,L,H,P]
+ * Decode step:  state [Bt,H,P,N] (in/out)  x [Bt,H,P]  dt [Bt,H]
+ *   B,C [Bt,G,N]  y [Bt,H,P]
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One token of one (b,h,p) row: update the N-vector state in place and return
+ * the output.  Shared by the scan and the step so that L steps reproduce the
+ * scan exactly. */
+static double row_update(double *s, int64_t N, double dt, double a, double xv,
+                         const double *Bt_row, const double *Ct_row, double Dh)
+{
+    const double r = exp(dt * a);
+    const double u = dt * xv;
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        s[n] = r * s[n] + u * Bt_row[n];
+        acc += Ct_row[n] * s[n];
+    }
+    return acc + Dh * xv;
+}
+
+static int bad_shape(int64_t Bt, int64_t H, int64_t P, int64_t N, int64_t G)
+{
+    return Bt < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0;
+}
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+/* Returns the number of threads OpenMP will use for the next parallel region. */
+int ssd_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full-sequence scan.  D, init and final_state may be NULL (D, init -> 0;
+ * final -> not written).  Returns 0, or -1 for an invalid shape. */
+int ssd_oracle_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                    const double *x, const double *dt, const double *A,
+                    const double *Bm, const double *Cm, const double *D,
+                    const double *init, double *y, double *final_state, int nthreads)
+{
+    if (bad_shape(Bt, H, P, N, G) || L < 0) return -1;
+    set_threads(nthreads);
+    const int64_t R = H / G;
+    const int64_t rows = Bt * H * P;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)N * sizeof(double));
+#pragma omp for schedule(static)
+        for (int64_t row = 0; row < rows; ++row) {
+            const int64_t p = row % P;
+            const int64_t h = (row / P) % H;
+            const int64_t b = row / (P * H);
+            const int64_t g = h / R;
+            const double a = A[h];
+            const double Dh = D ? D[h] : 0.0;
+            const int64_t sbase = ((b * H + h) * P + p) * N;
+            for (int64_t n = 0; n < N; ++n) s[n] = init ? init[sbase + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t bt = b * L + t;
+                const double dtv = dt[bt * H + h];
+                const double xv = x[(bt * H + h) * P + p];
+                const double *Brow = Bm + (bt * G + g) * N;
+                const double *Crow = Cm + (bt * G + g) * N;
+                y[(bt * H + h) * P + p] = row_update(s, N, dtv, a, xv, Brow, Crow, Dh);
+            }
+            if (final_state)
+                for (int64_t n = 0; n < N; ++n) final_state[sbase + n] = s[n];
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/* One cached decode step for every (b,h,p) row; the state is updated in place.
+ * D may be NULL.  Returns 0, or -1 for an invalid shape. */
+int ssd_oracle_step(int64_t Bt, int64_t H, int64_t P, int64_t N, int64_t G,
+                    double *state, const double *x, const double *dt, const double *A,
+                    const double *Bm, const double *Cm, const double *D, double *y,
+                    int nthreads)
+{
+    if (bad_shape(Bt, H, P, N, G)) return -1;
+    set_threads(nthreads);
+    const int64_t R = H / G;
+    const int64_t rows = Bt * H * P;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row) {
+        const int64_t h = (row / P) % H;
+        const int64_t b = row / (P * H);
+        const int64_t g = h / R;
+        y[row] = row_update(state + row * N, N, dt[b * H + h], A[h], x[row],
+                            Bm + (b * G + g) * N, Cm + (b * G + g) * N, D ? D[h] : 0.0);
+    }
+    return 0;
+}
