@@ -1,0 +1,161 @@
+/*
+ * ssd.h - C ABI of libssd, the MI355X (gfx950) Mamba-2 SSD selective scan.
+ *
+ * The operation.  Per batch row b, head h (group g = h / (nheads/ngroups)) and
+ * channel p, with a = A[h] and the state s[n] carried over tokens t:
+ *
+ *     s[n]        = exp(dt[b,t,h] * a) * s[n] + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
+ *     y[b,t,h,p]  = sum_n C[b,t,g,n] * s[n] + D[h] * x[b,t,h,p]
+ *
+ * starting from init_state (zero when NULL) and ending in final_state.  A is
+ * one scalar per head, which is what reduces the transition to a scalar
+ * exponential ("Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching for Inference", paperlayer summary, §3 Method,
+ * "State-space duality").  ssd_scan_fwd evaluates it with the chunked
+ * algorithm of the same section ("Chunked recurrence"): a matrix form inside
+ * each chunk of `chunk` tokens and a sequential pass of one summary state per
+ * chunk; results do not depend on the chunk size beyond rounding.  ssd_step is
+ * one token of the recurrence on a caller-owned, fixed-size state (§3,
+ * "Autoregressive cache"), updated in place as the block-level step method of
+ * the pyshine "Mamba" repository tour describes.
+ *
+ * Conventions for every entry point.
+ *  - Pointers are DEVICE pointers, 16-byte aligned, to contiguous row-major
+ *    arrays with the layouts given below.  The caller owns every buffer,
+ *    including the workspace; the library never allocates or frees memory,
+ *    never synchronises, and keeps no state between calls (reentrant).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns at once.  Asynchronous faults surface at the caller's
+ *    next synchronisation.
+ *  - Every argument check runs before the first HIP call; on error nothing is
+ *    enqueued.  After enqueueing, a launch failure reported by
+ *    hipGetLastError is returned as SSD_ERR_HIP.  No C++ exception crosses
+ *    this interface.
+ *  - Values are not checked: NaN/Inf propagate.  dt >= 0 and A <= 0 are
+ *    preconditions (decays must not exceed 1); they are not verified.
+ *  - dtype (SSD_F32 or SSD_BF16) applies to x, B, C and y.  dt, A, D and all
+ *    states are always fp32.  bf16 results are rounded to nearest even from
+ *    fp32 accumulators.
+ *  - Index arithmetic is 64-bit; any size that fits device memory is accepted.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL_PTR = 1,    /* a required pointer is NULL                       */
+    SSD_ERR_SHAPE = 2,       /* negative/zero dimension, nheads % ngroups != 0   */
+    SSD_ERR_UNSUPPORTED = 3, /* chunk, headdim or dstate outside the limits below,
+                                unknown dtype                                    */
+    SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
+    SSD_ERR_WORKSPACE = 5,   /* workspace smaller than ssd_scan_workspace_size   */
+    SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch      */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Shape of a prefill call.  batch >= 0, seqlen >= 0, nheads >= 1,
+ * 1 <= ngroups, nheads % ngroups == 0.
+ * chunk: 16, 32, 64, 128 or 256.  headdim: 1..256.  dstate: 4..256, a power of
+ * two.  seqlen need not be a multiple of chunk (the last chunk is short). */
+typedef struct ssd_scan_desc {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t dtype; /* ssd_dtype */
+    int32_t reserved; /* must be 0 */
+} ssd_scan_desc;
+
+/* Shape of a decode step: as above without seqlen and chunk. */
+typedef struct ssd_step_desc {
+    int64_t batch, nheads, headdim, dstate, ngroups;
+    int32_t dtype; /* ssd_dtype */
+    int32_t reserved; /* must be 0 */
+} ssd_step_desc;
+
+/* Static English text for a status code (never NULL). */
+const char *ssd_status_string(int status);
+
+/* ABI version of this header: 1. */
+int ssd_abi_version(void);
+
+/* ---------------------------------------------------------------- prefill */
+
+/* Bytes of device workspace ssd_scan_fwd needs for shape *d (0 is possible). */
+ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes);
+
+/* Chunked SSD scan over a whole sequence ("Compiler-First ...", §3,
+ * "Chunked recurrence"; the contractions of B.5).
+ *   x           [batch, seqlen, nheads, headdim]      dtype
+ *   dt          [batch, seqlen, nheads]               fp32, final step sizes
+ *                                                    (no bias/softplus applied here)
+ *   A           [nheads]                              fp32
+ *   B, C        [batch, seqlen, ngroups, dstate]      dtype
+ *   D           [nheads] fp32, or NULL (no skip term)
+ *   init_state  [batch, nheads, headdim, dstate] fp32, or NULL (zero state)
+ *   y           [batch, seqlen, nheads, headdim]      dtype, written
+ *   final_state [batch, nheads, headdim, dstate] fp32, or NULL (not written);
+ *               may equal init_state (in-place continuation); no other aliasing.
+ *   workspace   device buffer of at least ssd_scan_workspace_size bytes
+ *               (may be NULL when that size is 0).
+ * seqlen == 0 writes final_state = init_state (or zeros); batch == 0 is a no-op. */
+ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
+                        const float *A, const void *B, const void *C, const float *D,
+                        const float *init_state, void *y, float *final_state,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------- decode step */
+
+/* One cached decode token ("Compiler-First ...", §3 "Autoregressive cache"):
+ *   state [batch, nheads, headdim, dstate] fp32, read and updated in place
+ *   x     [batch, nheads, headdim]  dtype      dt [batch, nheads] fp32
+ *   A     [nheads] fp32             B, C [batch, ngroups, dstate] dtype
+ *   D     [nheads] fp32 or NULL     y [batch, nheads, headdim] dtype, written
+ * y uses the state after this token's update. */
+ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const float *dt,
+                    const float *A, const void *B, const void *C, const float *D, void *y,
+                    void *stream);
+
+/* ------------------------------------------------- stages of the prefill scan
+ * The four steps of ssd_scan_fwd, callable one at a time for stage checks.
+ * Shapes as for ssd_scan_fwd; T = ceil(seqlen / chunk); chunk c covers tokens
+ * [c*chunk, min(seqlen, (c+1)*chunk)).  Intermediate layouts:
+ *   Acs    [batch, nheads, seqlen] fp32   within-chunk inclusive cumsum of dt*A
+ *   states [batch, T, nheads, headdim, dstate] fp32
+ */
+
+/* Acs[b,h,t] = sum over tokens k of t's chunk with k <= t of dt[b,k,h]*A[h]. */
+ssd_status ssd_chunk_cumsum(const ssd_scan_desc *d, const float *dt, const float *A,
+                            float *Acs, void *stream);
+
+/* states[b,c,h,p,n] = sum_{j in chunk c} x[b,j,h,p] * dt[b,j,h]
+ *                       * exp(Acs[b,h,last(c)] - Acs[b,h,j]) * B[b,j,g,n]
+ * (the state chunk c alone contributes, starting from zero). */
+ssd_status ssd_chunk_state(const ssd_scan_desc *d, const void *x, const void *B,
+                           const float *dt, const float *Acs, float *states, void *stream);
+
+/* In place over chunks, per (b,h): H_0 = init_state (or 0);
+ *   H_{c+1} = exp(Acs[b,h,last(c)]) * H_c + states[c];  states[c] <- H_c.
+ * On return states[c] holds the state ENTERING chunk c and final_state (if not
+ * NULL) holds H_T.  final_state may equal init_state. */
+ssd_status ssd_state_passing(const ssd_scan_desc *d, float *states, const float *Acs,
+                             const float *init_state, float *final_state, void *stream);
+
+/* y for every chunk from the chunk-entry states:
+ *   y[t] = sum_{j <= t in chunk} (C_t . B_j) exp(Acs_t - Acs_j) dt_j x_j
+ *          + exp(Acs_t) (C_t . H_c) + D x_t
+ * with H_c = states[c] as left by ssd_state_passing. */
+ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
+                          const void *B, const void *C, const float *D, const float *Acs,
+                          const float *states, void *y, void *stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* SSD_H */

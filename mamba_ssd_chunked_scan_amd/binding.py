@@ -1,0 +1,276 @@
+"""ctypes binding of libssd (include/ssd.h).
+
+Argument marshalling only: shapes and dtypes are checked, output tensors are
+allocated with torch on the inputs' device, and the C entry point of the same
+name runs the work on torch's current HIP stream.  There is no CPU or PyTorch
+fallback: if libssd.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssd.so")
+
+SSD_OK = 0
+SSD_F32, SSD_BF16 = 0, 1
+_STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
+                 3: "SSD_ERR_UNSUPPORTED", 4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE",
+                 6: "SSD_ERR_HIP"}
+
+# Every function include/ssd.h declares.
+EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
+           "ssd_step", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
+           "ssd_chunk_scan")
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} returned {_STATUS_NAMES.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m mamba_ssd_chunked_scan_amd.build`"
+                " (or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssd_status_string.argtypes = [ctypes.c_int]
+        L.ssd_status_string.restype = ctypes.c_char_p
+        L.ssd_abi_version.argtypes = []
+        L.ssd_abi_version.restype = ctypes.c_int
+        L.ssd_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_fwd.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [ctypes.c_size_t, _P]
+        L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [_P] * 9
+        L.ssd_chunk_cumsum.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 4
+        L.ssd_chunk_state.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 6
+        L.ssd_state_passing.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 5
+        L.ssd_chunk_scan.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 9
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ssd_status_string(status).decode()
+
+
+def _check(fn, status):
+    if status != SSD_OK:
+        raise SSDError(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _io_dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise ValueError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scan_desc(x, B, chunk):
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return ScanDesc(Bt, L, H, P, N, G, chunk, _io_dtype(x), 0)
+
+
+def _check_scan_inputs(x, dt, A, B, C, D):
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim], B [batch, seqlen, ngroups, dstate]")
+    if x.device.type != "cuda":
+        raise ValueError("inputs must be device tensors")
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev, io = x.device, x.dtype
+    _need(x, "x", (Bt, L, H, P), io, dev)
+    _need(dt, "dt", (Bt, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (Bt, L, G, N), io, dev)
+    if C is not None:
+        _need(C, "C", (Bt, L, G, N), io, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    return Bt, L, H, P, N, G
+
+
+def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype) -> int:
+    d = ScanDesc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                 SSD_BF16 if dtype == torch.bfloat16 else SSD_F32, 0)
+    n = ctypes.c_size_t(0)
+    _check("ssd_scan_workspace_size", lib().ssd_scan_workspace_size(ctypes.byref(d),
+                                                                    ctypes.byref(n)))
+    return n.value
+
+
+def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
+             return_final_state: bool = True, final_state=None, workspace=None, y=None):
+    """Chunked SSD scan.  Returns (y, final_state); final_state is None when not requested.
+
+    ``final_state`` may be a preallocated [batch, nheads, headdim, dstate] fp32
+    tensor (it may be ``init_state`` itself); ``workspace`` a uint8 device tensor
+    of at least :func:`workspace_size` bytes; ``y`` a preallocated output.
+    """
+    Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
+    dev = x.device
+    if init_state is not None:
+        _need(init_state, "init_state", (Bt, H, P, N), torch.float32, dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _need(final_state, "final_state", (Bt, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, x.dtype, dev)
+    desc = _scan_desc(x, B, chunk)
+    n = ctypes.c_size_t(0)
+    _check("ssd_scan_workspace_size", lib().ssd_scan_workspace_size(ctypes.byref(desc),
+                                                                    ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < n.value or workspace.device != dev:
+        raise ValueError(f"workspace needs {n.value} bytes on {dev}")
+    st = lib().ssd_scan_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                            _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("ssd_scan_fwd", st)
+    return y, final_state
+
+
+def step(state, x, dt, A, B, C, D=None, y=None):
+    """One decode token; ``state`` [batch, nheads, headdim, dstate] fp32 is updated in place."""
+    if state.dim() != 4 or x.dim() != 3 or B.dim() != 3:
+        raise ValueError("state [b,h,p,n], x [b,h,p], B/C [b,g,n] expected")
+    Bt, H, P, N = state.shape
+    G = B.shape[1]
+    dev, io = state.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be device tensors")
+    _need(state, "state", (Bt, H, P, N), torch.float32, dev)
+    _need(x, "x", (Bt, H, P), io, dev)
+    _need(dt, "dt", (Bt, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (Bt, G, N), io, dev)
+    _need(C, "C", (Bt, G, N), io, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, io, dev)
+    desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
+    st = lib().ssd_step(ctypes.byref(desc), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                        _ptr(C), _ptr(D), _ptr(y), _stream(dev))
+    _check("ssd_step", st)
+    return y
+
+
+def chunk_cumsum(dt, A, chunk: int, x_like):
+    """Stage 1: Acs [batch, nheads, seqlen] fp32.  ``x_like`` gives the shape/dtype desc."""
+    x, B = x_like
+    desc = _scan_desc(x, B, chunk)
+    Bt, L, H = dt.shape
+    _need(dt, "dt", (Bt, L, H), torch.float32, x.device)
+    _need(A, "A", (H,), torch.float32, x.device)
+    Acs = torch.empty((Bt, H, L), dtype=torch.float32, device=x.device)
+    _check("ssd_chunk_cumsum", lib().ssd_chunk_cumsum(ctypes.byref(desc), _ptr(dt), _ptr(A),
+                                                      _ptr(Acs), _stream(x.device)))
+    return Acs
+
+
+def chunk_state(x, B, dt, Acs, chunk: int):
+    """Stage 2: states [batch, T, nheads, headdim, dstate] fp32 (each chunk alone)."""
+    Bt, L, H, P, N, G = _check_scan_inputs(x, dt, torch.empty(x.shape[2], device=x.device),
+                                           B, None, None)
+    _need(Acs, "Acs", (Bt, H, L), torch.float32, x.device)
+    T = -(-L // chunk)
+    states = torch.empty((Bt, T, H, P, N), dtype=torch.float32, device=x.device)
+    desc = _scan_desc(x, B, chunk)
+    _check("ssd_chunk_state", lib().ssd_chunk_state(ctypes.byref(desc), _ptr(x), _ptr(B),
+                                                    _ptr(dt), _ptr(Acs), _ptr(states),
+                                                    _stream(x.device)))
+    return states
+
+
+def state_passing(states, Acs, chunk: int, x_like, init_state=None, final_state=None):
+    """Stage 3, in place: states[c] becomes the state entering chunk c.  Returns final_state."""
+    x, B = x_like
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    T = -(-L // chunk)
+    dev = x.device
+    _need(states, "states", (Bt, T, H, P, N), torch.float32, dev)
+    _need(Acs, "Acs", (Bt, H, L), torch.float32, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (Bt, H, P, N), torch.float32, dev)
+    if final_state is None:
+        final_state = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    desc = _scan_desc(x, B, chunk)
+    _check("ssd_state_passing", lib().ssd_state_passing(ctypes.byref(desc), _ptr(states),
+                                                        _ptr(Acs), _ptr(init_state),
+                                                        _ptr(final_state), _stream(dev)))
+    return final_state
+
+
+def chunk_scan(x, dt, B, C, D, Acs, states, chunk: int):
+    """Stage 4: y from the chunk-entry states."""
+    Bt, L, H, P, N, G = _check_scan_inputs(x, dt, torch.empty(x.shape[2], device=x.device),
+                                           B, C, D)
+    T = -(-L // chunk)
+    _need(Acs, "Acs", (Bt, H, L), torch.float32, x.device)
+    _need(states, "states", (Bt, T, H, P, N), torch.float32, x.device)
+    y = torch.empty_like(x)
+    desc = _scan_desc(x, B, chunk)
+    _check("ssd_chunk_scan", lib().ssd_chunk_scan(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(B),
+                                                  _ptr(C), _ptr(D), _ptr(Acs), _ptr(states),
+                                                  _ptr(y), _stream(x.device)))
+    return y

@@ -1,0 +1,63 @@
+// Device helpers shared by the libssd kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+constexpr int kWave = 64;
+
+// bf16 is carried as its 16-bit pattern; arithmetic is always fp32.
+using bf16 = uint16_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; NaN stays NaN (quietened).
+__device__ __forceinline__ bf16 f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16)(u >> 16);
+}
+
+// Two fp32 values -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Storage-type traits: load a value as fp32 / store an fp32 value.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16> {
+    static __device__ __forceinline__ float ld(const bf16 *p, int64_t i) {
+        return bf16_to_f32(p[i]);
+    }
+    static __device__ __forceinline__ void st(bf16 *p, int64_t i, float v) {
+        p[i] = f32_to_bf16(v);
+    }
+};
+
+// exp(v) through the hardware base-2 exponential.  Arguments here are
+// differences of cumulative log-decays, so v <= 0 in valid use; results below
+// the fp32 range flush to 0, which is the correct limit.
+__device__ __forceinline__ float ssd_exp(float v) {
+    return __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        float o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+}  // namespace ssd

@@ -1,0 +1,354 @@
+// Generic kernels of the chunked SSD scan and the decode step.
+//
+// These handle every supported shape and both storage dtypes with fp32 VALU
+// arithmetic.  They are the fp32 path and the fallback for shapes the MFMA
+// kernels do not tile; the chunk-cumsum and state-passing kernels here serve
+// every path.  The stages follow the chunked algorithm of "Compiler-First
+// State Space Duality and Portable O(1) Autoregressive Caching for Inference"
+// (paperlayer summary, §3 Method, "Chunked recurrence"; contractions of B.5):
+// a within-chunk cumulative log-decay, each chunk's own state, a sequential
+// pass of states across chunks, and the chunk output from its diagonal block
+// plus the entering state.
+#include "common.hpp"
+#include "launch.hpp"
+#include "ssd.h"
+
+namespace ssd {
+namespace {
+
+// ---------------------------------------------------------------- cumsum
+// Acs[b,h,t] = within-chunk inclusive cumsum of dt*A.  One block per
+// (batch, chunk) and 32 heads; the [chunk x 32] tile of dt is read row-wise
+// (coalesced along heads) into LDS, then each wave scans one head at a time:
+// every lane holds Q/64 consecutive tokens (sequential sum), and the lane
+// totals are combined with a wave prefix scan.
+constexpr int kCsHeads = 32;
+
+__global__ void __launch_bounds__(256)
+k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
+               float *__restrict__ Acs, int64_t L, int H, int Q, int T) {
+    __shared__ float tile[256][kCsHeads + 1];
+    const int64_t b = blockIdx.x / T;
+    const int c = blockIdx.x % T;
+    const int h0 = blockIdx.y * kCsHeads;
+    const int64_t t0 = (int64_t)c * Q;
+    const int q = (int)min((int64_t)Q, L - t0);
+    const int nh = min(kCsHeads, H - h0);
+    for (int e = threadIdx.x; e < Q * kCsHeads; e += 256) {
+        const int i = e / kCsHeads, hh = e % kCsHeads;
+        float v = 0.f;
+        if (i < q && hh < nh) v = dt[(b * L + t0 + i) * H + h0 + hh] * A[h0 + hh];
+        tile[i][hh] = v;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int E = Q >= 64 ? Q / 64 : 1;  // tokens per lane (<= 4)
+    for (int hh = wave; hh < nh; hh += 4) {
+        float v[4];
+        float run = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = lane * E + k;
+            if (k < E && i < Q) run += tile[i][hh];
+            v[k] = run;
+        }
+        const float incl = wave_inclusive_scan(run, lane);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 0.f;
+        float *out = Acs + ((b * H + h0 + hh) * L) + t0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int i = lane * E + k;
+            if (k < E && i < q) out[i] = v[k] + excl;
+        }
+    }
+}
+
+// ---------------------------------------------------------- chunk state
+// states[b,c,h,p,n] = sum_j x[j,p] * w_j * B[j,n],  w_j = dt_j exp(Acs_last - Acs_j).
+// One block per (b, c, h) and 1024 outputs; thread k-loop over the chunk.
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
+                      const float *__restrict__ dt, const float *__restrict__ Acs,
+                      float *__restrict__ states, int64_t L, int H, int P, int N, int G, int Q,
+                      int T) {
+    __shared__ float w[256];
+    const int h = blockIdx.x % H;
+    const int64_t bc = blockIdx.x / H;
+    const int c = (int)(bc % T);
+    const int64_t b = bc / T;
+    const int g = h / (H / G);
+    const int64_t t0 = (int64_t)c * Q;
+    const int q = (int)min((int64_t)Q, L - t0);
+    const float *acs = Acs + (b * H + h) * L + t0;
+    const float last = acs[q - 1];
+    for (int j = threadIdx.x; j < q; j += 256)
+        w[j] = dt[(b * L + t0 + j) * H + h] * ssd_exp(last - acs[j]);
+    __syncthreads();
+    const int64_t PN = (int64_t)P * N;
+    int pe[4], ne[4];
+    bool ok[4];
+    float acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t e = (int64_t)blockIdx.y * 1024 + threadIdx.x + 256 * k;
+        ok[k] = e < PN;
+        pe[k] = ok[k] ? (int)(e / N) : 0;
+        ne[k] = ok[k] ? (int)(e % N) : 0;
+        acc[k] = 0.f;
+    }
+    for (int j = 0; j < q; ++j) {
+        const Tin *xr = x + ((b * L + t0 + j) * H + h) * P;
+        const Tin *br = Bm + ((b * L + t0 + j) * G + g) * N;
+        const float wj = w[j];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (ok[k]) acc[k] += (Elem<Tin>::ld(xr, pe[k]) * wj) * Elem<Tin>::ld(br, ne[k]);
+    }
+    float *out = states + (((b * T + c) * H + h) * PN);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (ok[k]) out[(int64_t)pe[k] * N + ne[k]] = acc[k];
+}
+
+// -------------------------------------------------------- state passing
+// Per (b, h) and 4 consecutive state elements per thread, sequential over
+// chunks: states[c] <- H_c, H_{c+1} = exp(dA_c) H_c + S_c.  Loads run four
+// chunks ahead of the dependent update so that several are in flight.
+__global__ void __launch_bounds__(256)
+k_state_passing(float *__restrict__ states, const float *__restrict__ Acs,
+                const float *init, float *fin, int64_t L, int H, int64_t PN, int Q, int T) {
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+    if (e >= PN) return;
+    float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init) hv = *reinterpret_cast<const float4 *>(init + bh * PN + e);
+    const float *acs = Acs + bh * L;
+    const int64_t cstride = (int64_t)H * PN;
+    float *base = states + (b * T * H + h) * PN + e;
+    for (int c0 = 0; c0 < T; c0 += 4) {
+        float4 s[4];
+        float r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + k;
+            if (c < T) {
+                s[k] = *reinterpret_cast<const float4 *>(base + c * cstride);
+                r[k] = ssd_exp(acs[min(L, (int64_t)(c + 1) * Q) - 1]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = c0 + k;
+            if (c < T) {
+                *reinterpret_cast<float4 *>(base + c * cstride) = hv;
+                hv.x = r[k] * hv.x + s[k].x;
+                hv.y = r[k] * hv.y + s[k].y;
+                hv.z = r[k] * hv.z + s[k].z;
+                hv.w = r[k] * hv.w + s[k].w;
+            }
+        }
+    }
+    if (fin) *reinterpret_cast<float4 *>(fin + bh * PN + e) = hv;
+}
+
+// ----------------------------------------------------------- chunk scan
+// One block per (b, c, h) and 16 output rows.  M[i][j] = (C_i.B_j) exp(Acs_i -
+// Acs_j) dt_j for j <= i is built in LDS, then each output (i, p) is
+// sum_j M[i][j] x[j,p] + exp(Acs_i) (C_i . H_c[p]) + D x[i,p].
+constexpr int kScanRows = 16;
+
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
+                     const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
+                     const float *__restrict__ D, const float *__restrict__ Acs,
+                     const float *__restrict__ states, Tin *__restrict__ y, int64_t L, int H,
+                     int P, int N, int G, int Q, int T) {
+    __shared__ float Ms[kScanRows][257];
+    __shared__ float Cs[kScanRows][257];
+    __shared__ float acs_s[256];
+    __shared__ float dt_s[256];
+    const int h = blockIdx.x % H;
+    const int64_t bc = blockIdx.x / H;
+    const int c = (int)(bc % T);
+    const int64_t b = bc / T;
+    const int g = h / (H / G);
+    const int64_t t0 = (int64_t)c * Q;
+    const int q = (int)min((int64_t)Q, L - t0);
+    const int i0 = blockIdx.y * kScanRows;
+    if (i0 >= q) return;
+    const int rows = min(kScanRows, q - i0);
+    for (int j = threadIdx.x; j < q; j += 256) {
+        acs_s[j] = Acs[(b * H + h) * L + t0 + j];
+        dt_s[j] = dt[(b * L + t0 + j) * H + h];
+    }
+    for (int e = threadIdx.x; e < kScanRows * N; e += 256) {
+        const int ii = e / N, n = e % N;
+        Cs[ii][n] = ii < rows ? Elem<Tin>::ld(Cm, ((b * L + t0 + i0 + ii) * G + g) * N + n) : 0.f;
+    }
+    __syncthreads();
+    const int jmax = i0 + rows;  // columns j < jmax can be non-zero
+    for (int e = threadIdx.x; e < kScanRows * jmax; e += 256) {
+        const int ii = e / jmax, j = e % jmax;
+        const int i = i0 + ii;
+        float m = 0.f;
+        if (ii < rows && j <= i) {
+            const Tin *br = Bm + ((b * L + t0 + j) * G + g) * N;
+            float dot = 0.f;
+            for (int n = 0; n < N; ++n) dot += Cs[ii][n] * Elem<Tin>::ld(br, n);
+            m = dot * ssd_exp(acs_s[i] - acs_s[j]) * dt_s[j];
+        }
+        Ms[ii][j] = m;
+    }
+    __syncthreads();
+    const float Dh = D ? D[h] : 0.f;
+    const float *Hc = states + ((b * T + c) * H + h) * (int64_t)P * N;
+    for (int e = threadIdx.x; e < rows * P; e += 256) {
+        const int ii = e / P, p = e % P;
+        const int i = i0 + ii;
+        float acc = 0.f;
+        for (int j = 0; j <= i; ++j)
+            acc += Ms[ii][j] * Elem<Tin>::ld(x, ((b * L + t0 + j) * H + h) * P + p);
+        float off = 0.f;
+        const float *hr = Hc + (int64_t)p * N;
+        for (int n = 0; n < N; ++n) off += Cs[ii][n] * hr[n];
+        const int64_t xi = ((b * L + t0 + i) * H + h) * P + p;
+        const float yv = acc + ssd_exp(acs_s[i]) * off + Dh * Elem<Tin>::ld(x, xi);
+        Elem<Tin>::st(y, xi, yv);
+    }
+}
+
+// ----------------------------------------------------------- misc
+__global__ void k_copy_or_zero(float *dst, const float *src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// ---------------------------------------------------------- decode step
+// Each thread owns 4 consecutive state elements of one (b,h,p) row; the N/4
+// lanes of a row are adjacent in the wave and reduce C.s with xor shuffles.
+template <typename Tin>
+__device__ __forceinline__ void ld4(const Tin *p, int64_t i, float v[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = Elem<Tin>::ld(p, i + k);
+}
+
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
+       const float *__restrict__ A, const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
+       const float *__restrict__ D, Tin *__restrict__ y, int64_t rows, int H, int P, int N,
+       int G, int lpr_log2) {
+    const int lpr = 1 << lpr_log2;
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gt >> lpr_log2;
+    const int sub = (int)(gt & (lpr - 1));
+    const bool active = row < rows;
+    float part = 0.f, xv = 0.f;
+    int h = 0;
+    if (active) {
+        const int64_t bh = row / P;
+        h = (int)(bh % H);
+        const int64_t b = bh / H;
+        const int g = h / (H / G);
+        const float d = dt[b * H + h];
+        const float r = ssd_exp(d * A[h]);
+        xv = Elem<Tin>::ld(x, row);
+        const float u = d * xv;
+        float4 *sp = reinterpret_cast<float4 *>(state + row * N) + sub;
+        float4 s = *sp;
+        float bv[4], cv[4];
+        ld4(Bm, (b * G + g) * N + sub * 4, bv);
+        ld4(Cm, (b * G + g) * N + sub * 4, cv);
+        s.x = r * s.x + u * bv[0];
+        s.y = r * s.y + u * bv[1];
+        s.z = r * s.z + u * bv[2];
+        s.w = r * s.w + u * bv[3];
+        *sp = s;
+        part = cv[0] * s.x + cv[1] * s.y + cv[2] * s.z + cv[3] * s.w;
+    }
+    for (int off = lpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+    if (active && sub == 0) Elem<Tin>::st(y, row, part + (D ? D[h] : 0.f) * xv);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers
+void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, float *Acs,
+                         hipStream_t st) {
+    dim3 grid((unsigned)(s.B * s.T), (unsigned)((s.H + kCsHeads - 1) / kCsHeads));
+    k_chunk_cumsum<<<grid, 256, 0, st>>>(dt, A, Acs, s.L, (int)s.H, (int)s.Q, (int)s.T);
+}
+
+void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const float *dt,
+                        const float *Acs, float *states, hipStream_t st) {
+    if (mfma_supported(s)) {
+        launch_chunk_state_mfma(s, x, Bm, dt, Acs, states, st);
+        return;
+    }
+    dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.P * s.N + 1023) / 1024));
+    if (s.dtype == SSD_BF16)
+        k_chunk_state_generic<bf16><<<grid, 256, 0, st>>>(
+            (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+    else
+        k_chunk_state_generic<float><<<grid, 256, 0, st>>>(
+            (const float *)x, (const float *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+}
+
+void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
+                          const float *init, float *fin, hipStream_t st) {
+    const int64_t PN = s.P * s.N;
+    dim3 grid((unsigned)(s.B * s.H), (unsigned)((PN / 4 + 255) / 256));
+    k_state_passing<<<grid, 256, 0, st>>>(states, Acs, init, fin, s.L, (int)s.H, PN,
+                                           (int)s.Q, (int)s.T);
+}
+
+void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
+                       const void *Cm, const float *D, const float *Acs, const float *states,
+                       void *y, hipStream_t st) {
+    if (mfma_supported(s)) {
+        launch_chunk_scan_mfma(s, x, dt, Bm, Cm, D, Acs, states, y, st);
+        return;
+    }
+    dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.Q + kScanRows - 1) / kScanRows));
+    if (s.dtype == SSD_BF16)
+        k_chunk_scan_generic<bf16><<<grid, 256, 0, st>>>(
+            (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y,
+            s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+    else
+        k_chunk_scan_generic<float><<<grid, 256, 0, st>>>(
+            (const float *)x, dt, (const float *)Bm, (const float *)Cm, D, Acs, states,
+            (float *)y, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+}
+
+void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {
+    if (n <= 0 || dst == src) return;
+    k_copy_or_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, src, n);
+}
+
+void launch_step(const StepShape &s, float *state, const void *x, const float *dt,
+                 const float *A, const void *Bm, const void *Cm, const float *D, void *y,
+                 hipStream_t st) {
+    const int64_t rows = s.B * s.H * s.P;
+    int lpr_log2 = 0;
+    while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
+    const int64_t threads = rows << lpr_log2;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (s.dtype == SSD_BF16)
+        k_step<bf16><<<blocks, 256, 0, st>>>(state, (const bf16 *)x, dt, A, (const bf16 *)Bm,
+                                             (const bf16 *)Cm, D, (bf16 *)y, rows, (int)s.H,
+                                             (int)s.P, (int)s.N, (int)s.G, lpr_log2);
+    else
+        k_step<float><<<blocks, 256, 0, st>>>(state, (const float *)x, dt, A,
+                                              (const float *)Bm, (const float *)Cm, D,
+                                              (float *)y, rows, (int)s.H, (int)s.P, (int)s.N,
+                                              (int)s.G, lpr_log2);
+}
+
+}  // namespace ssd

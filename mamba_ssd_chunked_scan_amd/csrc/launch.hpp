@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer (ssd_api.cpp) and the
+// kernels.  Shapes arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct ScanShape {
+    int64_t B, L, H, P, N, G, Q, T;  // T = ceil(L / Q)
+    int dtype;                        // SSD_F32 or SSD_BF16
+};
+
+struct StepShape {
+    int64_t B, H, P, N, G;
+    int dtype;
+};
+
+// Stage kernels of the chunked scan (layouts as in include/ssd.h).
+void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, float *Acs,
+                         hipStream_t st);
+void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const float *dt,
+                        const float *Acs, float *states, hipStream_t st);
+void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
+                          const float *init, float *fin, hipStream_t st);
+void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
+                       const void *Cm, const float *D, const float *Acs, const float *states,
+                       void *y, hipStream_t st);
+
+// dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
+void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
+
+// One decode token.
+void launch_step(const StepShape &s, float *state, const void *x, const float *dt,
+                 const float *A, const void *Bm, const void *Cm, const float *D, void *y,
+                 hipStream_t st);
+
+// Whether the MFMA kernels handle this shape (otherwise the generic ones run).
+bool mfma_supported(const ScanShape &s);
+void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
+                             const float *dt, const float *Acs, float *states, hipStream_t st);
+void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt,
+                            const void *Bm, const void *Cm, const float *D, const float *Acs,
+                            const float *states, void *y, hipStream_t st);
+
+}  // namespace ssd

@@ -1,0 +1,220 @@
+// C-ABI layer of libssd: argument validation, workspace carving and the
+// launch sequence.  Every check happens before the first HIP call; the only
+// HIP calls made here are kernel launches (through the launchers) and
+// hipGetLastError.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "ssd.h"
+
+using ssd::ScanShape;
+using ssd::StepShape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Largest grid dimension the launchers use is batch*T*nheads blocks.
+constexpr int64_t kMaxBlocks = 0x7fffffffLL;
+
+ssd_status check_common(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                        int64_t ngroups, int32_t dtype, int32_t reserved) {
+    if (batch < 0 || nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 ||
+        nheads % ngroups != 0)
+        return SSD_ERR_SHAPE;
+    if (dtype != SSD_F32 && dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (reserved != 0) return SSD_ERR_UNSUPPORTED;
+    if (headdim > 256 || dstate < 4 || dstate > 256 || !pow2(dstate)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status check_scan(const ssd_scan_desc *d, ScanShape *s) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    if (d->seqlen < 0) return SSD_ERR_SHAPE;
+    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                 d->dtype, d->reserved);
+    if (st != SSD_OK) return st;
+    if (d->chunk < 16 || d->chunk > 256 || !pow2(d->chunk)) return SSD_ERR_UNSUPPORTED;
+    s->B = d->batch;
+    s->L = d->seqlen;
+    s->H = d->nheads;
+    s->P = d->headdim;
+    s->N = d->dstate;
+    s->G = d->ngroups;
+    s->Q = d->chunk;
+    s->T = (d->seqlen + d->chunk - 1) / d->chunk;
+    s->dtype = d->dtype;
+    // grid-size limit (also guards the products below against overflow)
+    if (s->T > 0 && s->B > kMaxBlocks / s->T / s->H) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status check_ptrs(std::initializer_list<const void *> required,
+                      std::initializer_list<const void *> optional) {
+    for (const void *p : required)
+        if (!p) return SSD_ERR_NULL_PTR;
+    for (const void *p : required)
+        if (!aligned16(p)) return SSD_ERR_ALIGN;
+    for (const void *p : optional)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
+size_t acs_bytes(const ScanShape &s) { return round_up((size_t)(s.B * s.H * s.L) * 4); }
+
+size_t states_bytes(const ScanShape &s) {
+    return round_up((size_t)(s.B * s.T * s.H) * (size_t)(s.P * s.N) * 4);
+}
+
+size_t workspace_bytes(const ScanShape &s) {
+    if (s.B == 0 || s.L == 0) return 0;
+    return acs_bytes(s) + states_bytes(s);
+}
+
+ssd_status after_launch() {
+    return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+hipStream_t as_stream(void *stream) { return reinterpret_cast<hipStream_t>(stream); }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(int status) {
+    switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL_PTR: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid shape (negative or zero dimension, or nheads % ngroups != 0)";
+    case SSD_ERR_UNSUPPORTED:
+        return "unsupported argument (chunk, headdim, dstate, dtype or reserved field)";
+    case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case SSD_ERR_WORKSPACE: return "workspace is smaller than ssd_scan_workspace_size";
+    case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+int ssd_abi_version(void) { return 1; }
+
+ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
+    if (!bytes) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    *bytes = workspace_bytes(s);
+    return SSD_OK;
+}
+
+ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        void *y, float *final_state, void *workspace, size_t ws_bytes,
+                        void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0) return SSD_OK;
+    if (s.L == 0) {
+        st = check_ptrs({}, {init_state, final_state});
+        if (st != SSD_OK) return st;
+        if (final_state)
+            ssd::launch_copy_or_zero(final_state, init_state, s.B * s.H * s.P * s.N,
+                                     as_stream(stream));
+        return after_launch();
+    }
+    st = check_ptrs({x, dt, A, B, C, y}, {D, init_state, final_state, workspace});
+    if (st != SSD_OK) return st;
+    const size_t need = workspace_bytes(s);
+    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL_PTR;
+    float *Acs = static_cast<float *>(workspace);
+    float *states = reinterpret_cast<float *>(static_cast<char *>(workspace) + acs_bytes(s));
+    hipStream_t hs = as_stream(stream);
+    ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
+    ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
+    ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
+    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, y, hs);
+    return after_launch();
+}
+
+ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const float *dt,
+                    const float *A, const void *B, const void *C, const float *D, void *y,
+                    void *stream) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                 d->dtype, d->reserved);
+    if (st != SSD_OK) return st;
+    if (d->batch == 0) return SSD_OK;
+    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D});
+    if (st != SSD_OK) return st;
+    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
+    ssd::launch_step(s, state, x, dt, A, B, C, D, y, as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_scan_desc *d, const float *dt, const float *A,
+                            float *Acs, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0 || s.L == 0) return SSD_OK;
+    st = check_ptrs({dt, A, Acs}, {});
+    if (st != SSD_OK) return st;
+    ssd::launch_chunk_cumsum(s, dt, A, Acs, as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_chunk_state(const ssd_scan_desc *d, const void *x, const void *B,
+                           const float *dt, const float *Acs, float *states, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0 || s.L == 0) return SSD_OK;
+    st = check_ptrs({x, B, dt, Acs, states}, {});
+    if (st != SSD_OK) return st;
+    ssd::launch_chunk_state(s, x, B, dt, Acs, states, as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_state_passing(const ssd_scan_desc *d, float *states, const float *Acs,
+                             const float *init_state, float *final_state, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0) return SSD_OK;
+    if (s.L == 0) {
+        st = check_ptrs({}, {init_state, final_state});
+        if (st != SSD_OK) return st;
+        if (final_state)
+            ssd::launch_copy_or_zero(final_state, init_state, s.B * s.H * s.P * s.N,
+                                     as_stream(stream));
+        return after_launch();
+    }
+    st = check_ptrs({states, Acs}, {init_state, final_state});
+    if (st != SSD_OK) return st;
+    ssd::launch_state_passing(s, states, Acs, init_state, final_state, as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
+                          const void *B, const void *C, const float *D, const float *Acs,
+                          const float *states, void *y, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0 || s.L == 0) return SSD_OK;
+    st = check_ptrs({x, dt, B, C, Acs, states, y}, {D});
+    if (st != SSD_OK) return st;
+    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, y, as_stream(stream));
+    return after_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+any HIP call.  Every call here is built to fail validation (or to be a
+documented no-op), so nothing is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_ssd_chunked_scan_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP = range(7)
+
+# fake device addresses: never dereferenced, since validation fails first
+P16 = 0x10000
+P_MIS = 0x10008
+
+
+@pytest.fixture(scope="module")
+def L():
+    return binding.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    declared = header_functions()
+    assert set(declared) == set(binding.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    assert L.ssd_abi_version() == 1
+    for s in range(7):
+        assert binding.status_string(s)
+    assert binding.status_string(99) == "unknown status"
+
+
+def desc(**kw):
+    d = dict(batch=1, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=256,
+             dtype=1, reserved=0)
+    d.update(kw)
+    return binding.ScanDesc(**d)
+
+
+def sdesc(**kw):
+    d = dict(batch=2, nheads=8, headdim=64, dstate=128, ngroups=2, dtype=1, reserved=0)
+    d.update(kw)
+    return binding.StepDesc(**d)
+
+
+def wsize(L, d):
+    n = ctypes.c_size_t(12345)
+    st = L.ssd_scan_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size(L):
+    st, n = wsize(L, desc())
+    T = 2
+    acs = 1 * 8 * 512 * 4
+    states = 1 * T * 8 * 64 * 128 * 4
+    r = lambda v: (v + 255) // 256 * 256
+    assert st == OK and n == r(acs) + r(states)
+    # ragged last chunk counts as a chunk
+    st, n = wsize(L, desc(seqlen=300, chunk=128))
+    assert st == OK and n == r(8 * 300 * 4) + r(3 * 8 * 64 * 128 * 4)
+    assert wsize(L, desc(seqlen=0)) == (OK, 0)
+    assert wsize(L, desc(batch=0)) == (OK, 0)
+    assert L.ssd_scan_workspace_size(ctypes.byref(desc()), None) == NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), SHAPE), (dict(seqlen=-5), SHAPE), (dict(nheads=0), SHAPE),
+    (dict(headdim=0), SHAPE), (dict(dstate=0), SHAPE), (dict(ngroups=0), SHAPE),
+    (dict(nheads=6, ngroups=4), SHAPE),
+    (dict(chunk=48), UNSUP), (dict(chunk=8), UNSUP), (dict(chunk=512), UNSUP),
+    (dict(dstate=96), UNSUP), (dict(dstate=2), UNSUP), (dict(dstate=512), UNSUP),
+    (dict(headdim=257), UNSUP), (dict(dtype=2), UNSUP), (dict(reserved=1), UNSUP),
+])
+def test_scan_shape_errors(L, kw, status):
+    d = desc(**kw)
+    assert wsize(L, d)[0] == status
+    ws = 1 << 30
+    st = L.ssd_scan_fwd(ctypes.byref(d), P16, P16, P16, P16, P16, P16, P16, P16, P16, P16, ws,
+                        None)
+    assert st == status
+    assert L.ssd_chunk_cumsum(ctypes.byref(d), P16, P16, P16, None) == status
+    assert L.ssd_chunk_state(ctypes.byref(d), P16, P16, P16, P16, P16, None) == status
+    assert L.ssd_state_passing(ctypes.byref(d), P16, P16, P16, P16, None) == status
+    assert L.ssd_chunk_scan(ctypes.byref(d), P16, P16, P16, P16, P16, P16, P16, P16,
+                            None) == status
+
+
+def test_null_desc(L):
+    assert L.ssd_scan_fwd(None, *([P16] * 10), 0, None) == NULL
+    assert L.ssd_step(None, *([P16] * 8), None) == NULL
+    assert L.ssd_chunk_cumsum(None, P16, P16, P16, None) == NULL
+
+
+@pytest.mark.parametrize("which", range(6))
+def test_scan_null_required_pointer(L, which):
+    ptrs = [P16] * 10   # x dt A B C D init y final ws
+    req = [0, 1, 2, 3, 4, 7]
+    ptrs[req[which]] = None
+    st = L.ssd_scan_fwd(ctypes.byref(desc()), *ptrs, 1 << 30, None)
+    assert st == NULL
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_scan_misaligned_pointer(L, which):
+    ptrs = [P16] * 10
+    ptrs[which] = P_MIS
+    st = L.ssd_scan_fwd(ctypes.byref(desc()), *ptrs, 1 << 30, None)
+    assert st == ALIGN
+
+
+def test_scan_workspace_too_small(L):
+    d = desc()
+    _, need = wsize(L, d)
+    st = L.ssd_scan_fwd(ctypes.byref(d), *([P16] * 10), need - 1, None)
+    assert st == WS
+    ptrs = [P16] * 9 + [None]
+    assert L.ssd_scan_fwd(ctypes.byref(d), *ptrs, need, None) == NULL
+
+
+def test_empty_batch_is_noop(L):
+    d = desc(batch=0)
+    # all pointers NULL: nothing is touched and nothing is launched
+    assert L.ssd_scan_fwd(ctypes.byref(d), *([None] * 10), 0, None) == OK
+    assert L.ssd_chunk_cumsum(ctypes.byref(d), None, None, None, None) == OK
+    s = sdesc(batch=0)
+    assert L.ssd_step(ctypes.byref(s), *([None] * 8), None) == OK
+
+
+def test_empty_sequence_checks_alignment(L):
+    d = desc(seqlen=0)
+    st = L.ssd_scan_fwd(ctypes.byref(d), *([None] * 6), P_MIS, None, P16, None, 0, None)
+    assert st == ALIGN
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), SHAPE), (dict(nheads=0), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
+    (dict(dstate=3), UNSUP), (dict(dstate=100), UNSUP), (dict(headdim=300), UNSUP),
+    (dict(dtype=5), UNSUP), (dict(reserved=3), UNSUP),
+])
+def test_step_shape_errors(L, kw, status):
+    assert L.ssd_step(ctypes.byref(sdesc(**kw)), *([P16] * 8), None) == status
+
+
+@pytest.mark.parametrize("which", range(8))
+def test_step_pointer_errors(L, which):
+    ptrs = [P16] * 8   # state x dt A B C D y
+    ptrs[which] = P_MIS
+    assert L.ssd_step(ctypes.byref(sdesc()), *ptrs, None) == ALIGN
+    if which != 6:   # D is optional
+        ptrs[which] = None
+        assert L.ssd_step(ctypes.byref(sdesc()), *ptrs, None) == NULL
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libssd.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()
