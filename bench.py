@@ -1,0 +1,265 @@
+"""Benchmark of the SSD hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one ssd_scan_fwd call (all prefill stages: chunk cumsum, chunk
+states, state passing, chunk scan) on the Mamba-2 2.7B head shape: batch 1,
+seqlen 4096, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
+x/B/C, fp32 dt/A/D and a random fp32 initial state, with inputs resident in
+HBM.  W untimed steps, then exactly K timed steps between device
+synchronisations.  The cached decode step (ssd_step) at the same head shape
+is timed alongside at batch 1 and 64.  Prints ONE JSON line.
+
+`value` is prefill tokens/s.  `roofline` is for the dominant kernel: its
+algorithmic HBM bytes per launch over its average launch time, measured here
+with HIP events on the stream it runs on.  `cpu_baseline` is the fp64 CPU
+oracle on the same workload.  A second GPU is never used.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "SSD prefill tokens/s (% MFMA peak) + decode step GB/s (% HBM) at 2.7B shape"
+WORKLOAD = "m2p7b_bf16"
+
+
+def prefill_bytes(s) -> dict:
+    """Algorithmic HBM bytes of one prefill call and of each stage."""
+    B, L, H, P, N, G, T = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.nchunks
+    e = 2 if s.dtype == "bf16" else 4
+    x = B * L * H * P * e
+    bc = B * L * G * N * e
+    dt = B * L * H * 4
+    acs = B * H * L * 4
+    st = B * T * H * P * N * 4
+    hst = B * H * P * N * 4
+    small = 2 * H * 4                               # A and D
+    return {
+        "call": x + x + 2 * bc + dt + hst + hst + small,       # x, y, B, C, dt, init, final
+        "chunk_cumsum": dt + acs + H * 4,
+        "chunk_state": x + bc + dt + acs + st,
+        "state_passing": 2 * st + B * H * T * 4 + 2 * hst,
+        "chunk_scan": x + 2 * bc + dt + acs + st + x + H * 4,
+    }
+
+
+def prefill_flops(s) -> float:
+    """Causal algorithmic flop count of one prefill call: per (batch, chunk),
+    H*[Q(Q+1)P + 2QPN + 2QPN] + G*Q(Q+1)N (masked M.X, chunk states, state
+    to output, C.B once per group)."""
+    Q, P, N, H, G = s.chunk, s.headdim, s.dstate, s.nheads, s.ngroups
+    per = H * (Q * (Q + 1) * P + 4 * Q * P * N) + G * Q * (Q + 1) * N
+    return float(per) * s.batch * (s.seqlen // Q)
+
+
+def decode_bytes(batch, H, P, N, G, e=2) -> int:
+    return 2 * batch * H * P * N * 4 + 2 * batch * H * P * e + batch * H * 4 \
+        + 2 * batch * G * N * e + 2 * H * 4
+
+
+def time_launches(torch, fn, iters, warmup=2):
+    """Average milliseconds per launch of fn.
+
+    ``iters`` launches are captured into one HIP graph and replayed between two
+    HIP events on torch's current stream (the stream the library launches on),
+    so host-side call overhead does not appear as idle GPU time.
+    """
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+class Lean:
+    """A C-ABI entry point with its arguments marshalled once; each call only
+    looks up torch's current stream (which changes under graph capture)."""
+
+    def __init__(self, torch, fn, *args):
+        self.torch, self.fn, self.args = torch, fn, args
+
+    def __call__(self):
+        import ctypes
+        st = self.fn(*self.args, ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"status {st}")
+
+
+def cpu_baseline(spec, inp, budget_s=10.0):
+    import oracle
+    args = {k: oracle.f64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init")}
+    cores = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.scan(**args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= 2 and el >= budget_s:
+            break
+        if reps >= 50:
+            break
+    tokens = spec.batch * spec.seqlen * reps
+    return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"full {spec.name} prefill ({spec.batch}x{spec.seqlen} tokens, "
+                      f"{spec.nheads} heads) repeated {reps}x in {el:.1f} s, fp64 recurrence "
+                      f"with {cores} OpenMP threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(prefill would shard over batch and head groups with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_ssd_chunked_scan_amd as ssd
+    from mamba_ssd_chunked_scan_amd import binding, synth
+
+    dev = "cuda:0"
+    spec = synth.WORKLOADS[WORKLOAD]
+    inp = synth.scan_inputs(spec)
+    d = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
+    Bt, L, H, P, N, G, Q = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate,
+                            spec.ngroups, spec.chunk)
+    y = torch.empty_like(d["x"])
+    fin = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    wsb = ssd.workspace_size(Bt, L, H, P, N, G, Q, torch.bfloat16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    import ctypes
+    lib = binding.lib()
+    P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    desc = binding.ScanDesc(Bt, L, H, P, N, G, Q, binding.SSD_BF16, 0)
+    dref = ctypes.byref(desc)
+    call = Lean(torch, lib.ssd_scan_fwd, dref, P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]),
+                P_(d["C"]), P_(d["D"]), P_(d["init"]), P_(y), P_(fin), P_(ws), ws.numel())
+
+    # ---- timed prefill steps: K back-to-back C-ABI calls from a lean host loop
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    tokens_per_s = Bt * L * args.steps / elapsed
+    graph_ms = time_launches(torch, call, max(10, args.steps))
+
+    # ---- per-stage launch times (HIP events around graph replays)
+    Tn = spec.nchunks
+    Acs = torch.empty((Bt, H, L), dtype=torch.float32, device=dev)
+    states = torch.empty((Bt, Tn, H, P, N), dtype=torch.float32, device=dev)
+    states2 = torch.empty_like(states)
+    y2 = torch.empty_like(y)
+    fin2 = torch.empty_like(fin)
+    stage_fns = {
+        "chunk_cumsum": Lean(torch, lib.ssd_chunk_cumsum, dref, P_(d["dt"]), P_(d["A"]), P_(Acs)),
+        "chunk_state": Lean(torch, lib.ssd_chunk_state, dref, P_(d["x"]), P_(d["B"]),
+                            P_(d["dt"]), P_(Acs), P_(states)),
+        "state_passing": Lean(torch, lib.ssd_state_passing, dref, P_(states2), P_(Acs),
+                              P_(d["init"]), P_(fin2)),
+        "chunk_scan": Lean(torch, lib.ssd_chunk_scan, dref, P_(d["x"]), P_(d["dt"]), P_(d["B"]),
+                           P_(d["C"]), P_(d["D"]), P_(Acs), P_(states), P_(y2)),
+    }
+    stage_fns["chunk_cumsum"]()
+    stage_fns["chunk_state"]()
+    states2.copy_(states)
+    torch.cuda.synchronize()
+    iters = max(10, args.steps)
+    stage_ms = {k: time_launches(torch, f, iters) for k, f in stage_fns.items()}
+    bytes_ = prefill_bytes(spec)
+    dom = max(stage_ms, key=stage_ms.get)
+    dom_gbs = bytes_[dom] / (stage_ms[dom] * 1e-3) / 1e9
+
+    flops = prefill_flops(spec)
+    tflops = flops / (ms * 1e-3) / 1e12
+    call_gbs = bytes_["call"] / (ms * 1e-3) / 1e9
+
+    # ---- decode steps
+    decode = {}
+    for db in (1, 64):
+        dspec = synth.DecodeSpec(f"decode_2p7b_b{db}", db, H, P, N, 1, 1, "bf16", 5)
+        ds = synth.DecodeStream(dspec)
+        state = ds.state.to(dev)
+        s0 = ds.next_step()
+        xs, dts, Bs, Cs = (s0[k].to(dev) for k in ("x", "dt", "B", "C"))
+        A, D = ds.A.to(dev), ds.D.to(dev)
+        yd = torch.empty_like(xs)
+        sdesc = binding.StepDesc(db, H, P, N, 1, binding.SSD_BF16, 0)
+        fn = Lean(torch, lib.ssd_step, ctypes.byref(sdesc), P_(state), P_(xs), P_(dts), P_(A),
+                  P_(Bs), P_(Cs), P_(D), P_(yd))
+        dms = time_launches(torch, fn, args.decode_steps, warmup=5)
+        db_bytes = decode_bytes(db, H, P, N, 1)
+        gbs = db_bytes / (dms * 1e-3) / 1e9
+        decode[f"batch{db}"] = {"us_per_step": round(dms * 1e3, 3), "GB_s": round(gbs, 1),
+                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                "bytes_per_step": db_bytes, "note": "warm (state may be "
+                                "resident in the 256 MB Infinity Cache)"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name} prefill: batch {Bt}, seqlen {L}, nheads {H}, "
+                               f"headdim {P}, dstate {N}, ngroups {G}, chunk {Q}, bf16 x/B/C, "
+                               "fp32 dt/A/D, random fp32 init state",
+                   "global_batch": Bt, "seq_len": L, "parallelism": "single GPU"},
+        "prefill": {"tflops_causal": round(tflops, 2),
+                    "us_per_call_graph": round(graph_ms * 1e3, 2),
+                    "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "hbm_GB_s_algorithmic": round(call_gbs, 1),
+                    "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),
+                    "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()}},
+        "decode": decode,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": bytes_[dom],
+                     "avg_launch_us": round(stage_ms[dom] * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, inp)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -15,17 +15,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// Round to nearest even; NaN stays NaN (quietened).
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+// fp32 -> bf16, round to nearest even, by the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ bf16 f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16)(u >> 16);
+    return __builtin_bit_cast(bf16, (__bf16)f);
 }
 
-// Two fp32 values -> packed bf16x2 (low half = a).
+// Two fp32 values -> packed bf16x2 (low half = a), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Storage-type traits: load a value as fp32 / store an fp32 value.

@@ -18,49 +18,41 @@ namespace {
 
 // ---------------------------------------------------------------- cumsum
 // Acs[b,h,t] = within-chunk inclusive cumsum of dt*A.  One block per
-// (batch, chunk) and 32 heads; the [chunk x 32] tile of dt is read row-wise
-// (coalesced along heads) into LDS, then each wave scans one head at a time:
-// every lane holds Q/64 consecutive tokens (sequential sum), and the lane
-// totals are combined with a wave prefix scan.
-constexpr int kCsHeads = 32;
-
+// (batch, chunk) and 4 heads, one wave per head: each lane holds Q/64
+// consecutive tokens (summed sequentially), and the lane totals are combined
+// with a wave prefix scan.  All products and sums are fp32.
 __global__ void __launch_bounds__(256)
 k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
                float *__restrict__ Acs, int64_t L, int H, int Q, int T) {
-    __shared__ float tile[256][kCsHeads + 1];
     const int64_t b = blockIdx.x / T;
     const int c = blockIdx.x % T;
-    const int h0 = blockIdx.y * kCsHeads;
+    const int lane = threadIdx.x & 63;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (h >= H) return;  // wave-uniform
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
-    const int nh = min(kCsHeads, H - h0);
-    for (int e = threadIdx.x; e < Q * kCsHeads; e += 256) {
-        const int i = e / kCsHeads, hh = e % kCsHeads;
-        float v = 0.f;
-        if (i < q && hh < nh) v = dt[(b * L + t0 + i) * H + h0 + hh] * A[h0 + hh];
-        tile[i][hh] = v;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int E = Q >= 64 ? Q / 64 : 1;  // tokens per lane (<= 4)
-    for (int hh = wave; hh < nh; hh += 4) {
-        float v[4];
-        float run = 0.f;
+    const float a = A[h];
+    float v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = lane * E + k;
-            if (k < E && i < Q) run += tile[i][hh];
-            v[k] = run;
-        }
-        const float incl = wave_inclusive_scan(run, lane);
-        float excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.f;
-        float *out = Acs + ((b * H + h0 + hh) * L) + t0;
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * E + k;
+        v[k] = (k < E && i < q) ? dt[(b * L + t0 + i) * H + h] * a : 0.f;
+    }
+    float run = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int i = lane * E + k;
-            if (k < E && i < q) out[i] = v[k] + excl;
-        }
+    for (int k = 0; k < 4; ++k) {
+        run += v[k];
+        v[k] = run;
+    }
+    const float incl = wave_inclusive_scan(run, lane);
+    float excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.f;
+    float *out = Acs + (b * H + h) * L + t0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * E + k;
+        if (k < E && i < q) out[i] = v[k] + excl;
     }
 }
 
@@ -280,7 +272,7 @@ k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__rest
 // ------------------------------------------------------------ launchers
 void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, float *Acs,
                          hipStream_t st) {
-    dim3 grid((unsigned)(s.B * s.T), (unsigned)((s.H + kCsHeads - 1) / kCsHeads));
+    dim3 grid((unsigned)(s.B * s.T), (unsigned)((s.H + 3) / 4));
     k_chunk_cumsum<<<grid, 256, 0, st>>>(dt, A, Acs, s.L, (int)s.H, (int)s.Q, (int)s.T);
 }
 

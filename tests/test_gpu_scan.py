@@ -39,6 +39,7 @@ def check_full(inp, chunk, dtype):
     y, fin = run_gpu(inp, chunk)
     yo, fo = oracle.scan(**oracle_args(inp))
     ey, ef = rel_err(f64(y), yo), rel_err(f64(fin), fo)
+    print(f"  rel_err y {ey:.3e} final {ef:.3e} (bar {TOL[dtype]:.0e})", flush=True)
     assert ey <= TOL[dtype], f"y rel err {ey:.3e}"
     assert ef <= TOL[dtype], f"final rel err {ef:.3e}"
     return ey, ef
@@ -61,6 +62,7 @@ def sampled_check(inp, chunk, pairs, dtype):
     yo = np.stack([ref[p][0] for p in pairs])
     fo = np.stack([ref[p][1] for p in pairs])
     ey, ef = rel_err(yg, yo), rel_err(fg, fo)
+    print(f"  rel_err y {ey:.3e} final {ef:.3e} (bar {TOL[dtype]:.0e})", flush=True)
     assert ey <= TOL[dtype], f"y rel err {ey:.3e}"
     assert ef <= TOL[dtype], f"final rel err {ef:.3e}"
 
