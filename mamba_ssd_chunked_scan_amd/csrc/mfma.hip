@@ -13,10 +13,22 @@
 // implementation" in the same section): tiles above the diagonal are skipped
 // outright and only the diagonal 32x32 tiles are masked element by element.
 //
-// MFMA used: v_mfma_f32_32x32x16_bf16 (D[32x32] += A[32x16] B[16x32]).  Lane l
-// supplies row (A) or column (B) l%32 and 8 consecutive k slots 8*(l/32)+e.
-// The accumulator holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 in its
-// register r (r = 0..15).
+// gfx950 specifics used here:
+//  * v_mfma_f32_32x32x16_bf16 (D[32x32] += A[32x16] B[16x32]).  Lane l
+//    supplies row (A) or column (B) l%32 and the 8 k slots 8*(l/32)+e; the
+//    accumulator holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 in its
+//    register r (r = 0..15).
+//  * ds_read_b64_tr_b16, the LDS transpose read: within each group of 16
+//    lanes, lane i receives element (i & 3) of the 8-byte reads of lanes
+//    (i >> 2) + 4k, k = 0..3.  It turns a row-major [k][outer] tile into
+//    k-contiguous MFMA operands, so every tile is staged in its natural layout
+//    with plain 16-byte stores.
+//  * v_cvt_pk_bf16_f32 for round-to-nearest-even packing.
+//  * blocks are dealt to the 8 XCDs round-robin; the block index is remapped
+//    so that the heads of one (batch, chunk) run on one XCD and share its L2
+//    copy of the chunk's B and C rows.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "ssd.h"
@@ -24,9 +36,12 @@
 namespace ssd {
 namespace {
 
-constexpr int kP = 64;  // headdim handled here
+constexpr int kP = 64;   // headdim handled here
+constexpr int kJT = 32;  // tokens per streamed stage (one 32-row tile)
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short v4i16 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -34,46 +49,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// element e (0..7) of 8 packed bf16
-__device__ __forceinline__ float elem8(u32x4 v, int e) {
-    const uint32_t w = v[e >> 1];
-    return (e & 1) ? hi_bf16(w) : lo_bf16(w);
-}
-
-// 16-bit half e&1 of word e>>1 of two rows, packed as (row0, row1)
-__device__ __forceinline__ uint32_t pair16(u32x4 r0, u32x4 r1, int e) {
-    const uint32_t a = r0[e >> 1], b = r1[e >> 1];
-    return (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-}
-
-__device__ __forceinline__ u32x4 pack8(const float m[8]) {
-    u32x4 v;
-    v[0] = pack_bf16x2(m[0], m[1]);
-    v[1] = pack_bf16x2(m[2], m[3]);
-    v[2] = pack_bf16x2(m[4], m[5]);
-    v[3] = pack_bf16x2(m[6], m[7]);
-    return v;
-}
-
-// m = hi + lo with hi = bf16(m) and lo = bf16(m - hi): about 16 significant
-// bits in two bf16 operands, with the full fp32 exponent range.
-__device__ __forceinline__ void pack8_split(const float m[8], u32x4 &hi, u32x4 &lo) {
-    float r[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = m[e] - bf16_to_f32(f32_to_bf16(m[e]));
-    hi = pack8(m);
-    lo = pack8(r);
-}
-
-__device__ __forceinline__ uint32_t split_pair(float a, float b, uint32_t &lo) {
-    const bf16 ha = f32_to_bf16(a), hb = f32_to_bf16(b);
-    lo = pack_bf16x2(a - bf16_to_f32(ha), b - bf16_to_f32(hb));
-    return (uint32_t)ha | ((uint32_t)hb << 16);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -88,126 +63,185 @@ __device__ __forceinline__ u32x4 masked(u32x4 v, bool keep) {
     return u32x4{v[0] & m, v[1] & m, v[2] & m, v[3] & m};
 }
 
-// Loads rows [0, Q) of one head's x chunk (64 bf16 per row) into registers:
-// thread (seg = tid%8, rp = tid/8) takes the 16-byte segment seg of rows
-// 2rp + 64i and 2rp + 64i + 1.  Row addresses are clamped to q-1 so every load
-// is in bounds; rows at or beyond q are zeroed afterwards.  All loads are
-// issued before any is consumed.
-template <int Q>
-__device__ __forceinline__ void load_x_rows(u32x4 (&r)[Q / 32], const bf16 *xrow0,
-                                            int64_t rstride, int q) {
-    const int seg = threadIdx.x & 7, rp = threadIdx.x >> 3;
-#pragma unroll
-    for (int i = 0; i < Q / 32; ++i) {
-        const int j = 2 * rp + 64 * (i >> 1) + (i & 1);
-        r[i] = *reinterpret_cast<const u32x4 *>(xrow0 + min(j, q - 1) * rstride + seg * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < Q / 32; ++i) r[i] = masked(r[i], 2 * rp + 64 * (i >> 1) + (i & 1) < q);
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Splits two fp32 values into a packed bf16 pair hi = bf16(v) and the packed
+// residual lo = bf16(v - hi): about 16 significant bits in two bf16 operands,
+// with the full fp32 exponent range.
+__device__ __forceinline__ uint32_t split2(float a, float b, uint32_t &lo) {
+    const uint32_t h = pack_bf16x2(a, b);
+    lo = pack_bf16x2(a - lo_bf16(h), b - hi_bf16(h));
+    return h;
 }
 
-// Writes the rows loaded by load_x_rows transposed, xT[p*LD + j], two rows per
-// 32-bit store.  With a weight array the values are scaled by w[j] in fp32 and
-// stored as a hi/lo bf16 pair (xT and xTlo).
-template <int Q, int LD>
-__device__ __forceinline__ void store_x_transposed(const u32x4 (&r)[Q / 32], bf16 *xT,
-                                                   const float *w, bf16 *xTlo) {
-    const int seg = threadIdx.x & 7, rp = threadIdx.x >> 3;
+__device__ __forceinline__ void split8(const float m[8], u32x4 &hi, u32x4 &lo) {
 #pragma unroll
-    for (int i = 0; i < Q / 64; ++i) {
-        const int j = 2 * rp + 64 * i;
-        const u32x4 r0 = r[2 * i], r1 = r[2 * i + 1];
-        uint32_t *dst = reinterpret_cast<uint32_t *>(xT + seg * 8 * LD + j);
-        if (w) {
-            uint32_t *dlo = reinterpret_cast<uint32_t *>(xTlo + seg * 8 * LD + j);
-            const float w0 = w[j], w1 = w[j + 1];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t lo;
-                dst[e * (LD / 2)] = split_pair(elem8(r0, e) * w0, elem8(r1, e) * w1, lo);
-                dlo[e * (LD / 2)] = lo;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e * (LD / 2)] = pair16(r0, r1, e);
-        }
+    for (int k = 0; k < 4; ++k) {
+        uint32_t l;
+        hi[k] = split2(m[2 * k], m[2 * k + 1], l);
+        lo[k] = l;
     }
 }
+
+// ds_read_b64_tr_b16 on a generic pointer into LDS.
+__device__ __forceinline__ u32x2 ds_read_tr16(const bf16 *p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand from a row-major [k][outer] bf16 tile in LDS (row stride ld):
+// this lane gets outer index outer0 + lane%32 and the k rows of its slots.
+// kperm = false: slots e -> k0 + 8*(lane/32) + e (a plain 16-deep k step).
+// kperm = true:  slots e -> k0 + 8*(e/4) + 4*(lane/32) + e%4, the row order
+//                of a 32x32 accumulator, used when the other operand is built
+//                from accumulator registers.
+template <bool kperm>
+__device__ __forceinline__ u32x4 tr_operand(const bf16 *tile, int ld, int k0, int outer0) {
+    const int lane = threadIdx.x & 63, G = lane >> 4, s = lane & 15;
+    const int kb = kperm ? k0 + 4 * (G >> 1) : k0 + 8 * (G >> 1);
+    const bf16 *p = tile + (kb + (s >> 2)) * ld + outer0 + 16 * (G & 1) + 4 * (s & 3);
+    const u32x2 a = ds_read_tr16(p);
+    const u32x2 b = ds_read_tr16(p + (kperm ? 8 : 4) * ld);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Logical block index: block b runs on XCD b % 8, so XCD x receives logical
+// blocks [x*per, (x+1)*per) with per = gridDim.x / 8 (the grid is padded to a
+// multiple of 8).
+__device__ __forceinline__ int64_t xcd_block() {
+    const int64_t per = gridDim.x / 8;
+    return (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+}
+
+unsigned padded_grid(int64_t blocks) { return (unsigned)((blocks + 7) / 8 * 8); }
+
+// Registers holding one 32-token stage between its global load and its LDS
+// store: one 16-byte x segment and NBV 16-byte B segments per thread.  Two sets
+// give a prefetch distance of two stages.
+template <int NBV>
+struct StageRegs {
+    u32x4 x;
+    u32x4 b[NBV];
+};
+
+using P0 = std::integral_constant<int, 0>;
+using P1 = std::integral_constant<int, 1>;
 
 // ------------------------------------------------------------ chunk state
-// One block (4 waves) per (b, c, h).  S (64 x N fp32) = xw^T B with both
-// operands staged transposed in LDS (the contraction runs over tokens, which
-// are the rows in memory).  xw = x * w is formed in fp32 and carried as a
-// hi/lo bf16 pair, so its rounding stays near fp32 level.  Output tiles
+// One block (4 waves) per (b, c, h).  S (64 x N fp32) = xw^T B, streamed over
+// the chunk in 32-token stages (double-buffered; the next stage's global loads
+// are in flight while the current one is multiplied).  xw = x * w is formed in
+// fp32 and stored as a hi/lo bf16 pair, so its rounding stays near fp32
+// level.  Both operands are read with the LDS transpose read.  Output tiles
 // 32x32: wave w owns tiles w and w+4 of the (p-tile, n-tile) grid.
 template <int Q, int N>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ Acs,
-                   float *__restrict__ states, int64_t L, int H, int G, int T) {
-    constexpr int LD = Q + 8;
-    __shared__ __attribute__((aligned(16))) bf16 xT[kP * LD];
-    __shared__ __attribute__((aligned(16))) bf16 xTlo[kP * LD];
-    __shared__ __attribute__((aligned(16))) bf16 BT[N * LD];
+                   float *__restrict__ states, int64_t L, int H, int G, int T, int64_t nblocks) {
+    constexpr int LDX = kP + 16;              // x stage row stride (bf16)
+    constexpr int LDB = N + 16;               // B stage row stride (bf16)
+    constexpr int NST = Q / kJT;              // stages per chunk
+    constexpr int BSEG = N / 8;               // 16-byte segments per B row
+    constexpr int NBV = kJT * BSEG / 256;     // B segments per thread per stage
+    __shared__ __attribute__((aligned(16))) bf16 xhi[2][kJT * LDX];
+    __shared__ __attribute__((aligned(16))) bf16 xlo[2][kJT * LDX];
+    __shared__ __attribute__((aligned(16))) bf16 bst[2][kJT * LDB];
     __shared__ float w[Q];
+    const int64_t lb = xcd_block();
+    if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.x % H;
-    const int64_t bc = blockIdx.x / H;
+    const int h = (int)(lb % H);
+    const int64_t bc = lb / H;
     const int c = (int)(bc % T);
     const int64_t b = bc / T;
     const int g = h / (H / G);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
-    // issue every global load of the block first
-    u32x4 xr[Q / 32];
-    load_x_rows<Q>(xr, x + ((b * L + t0) * H + h) * kP, (int64_t)H * kP, q);
-    constexpr int SEGS = N / 8, RP = 256 / SEGS, NB = Q / RP;  // NB rows per thread
-    const int bseg = tid % SEGS, brp = tid / SEGS;
-    const bf16 *brow0 = Bm + ((b * L + t0) * G + g) * N + bseg * 8;
-    const int64_t brs = (int64_t)G * N;
-    u32x4 br[NB];
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int j = 2 * brp + 2 * RP * (i >> 1) + (i & 1);
-        br[i] = *reinterpret_cast<const u32x4 *>(brow0 + min(j, q - 1) * brs);
+    const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
+    const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
+    // per-thread offsets are unsigned 32-bit from block-uniform bases (a
+    // chunk spans < 2^31 elements of x, B, C and y), so loads and stores use
+    // the scalar-base + 32-bit-offset address form and no 64-bit addresses
+    // are kept in vector registers
+    const unsigned xrs = H * kP, brs = G * N;
+    const int xrow = tid >> 3, xseg = tid & 7;
+
+    // weights first: every stage needs them
+    {
+        const float *acs = Acs + (b * H + h) * L + t0;
+        const float last = acs[q - 1];
+        for (int j = tid; j < Q; j += 256) {
+            const int jj = min(j, q - 1);
+            const float v = dt[(b * L + t0 + jj) * H + h] * ssd_exp(last - acs[jj]);
+            w[j] = j < q ? v : 0.f;
+        }
     }
-    const float *acs = Acs + (b * H + h) * L + t0;
-    const float last = acs[q - 1];
-    for (int j = tid; j < Q; j += 256) {
-        const int jj = min(j, q - 1);
-        const float v = dt[(b * L + t0 + jj) * H + h] * ssd_exp(last - acs[jj]);
-        w[j] = j < q ? v : 0.f;
-    }
+    StageRegs<NBV> R[2];
+    auto load_stage = [&](int st, StageRegs<NBV> &r) {
+        const int j = st * kJT + xrow;
+        r.x = *reinterpret_cast<const u32x4 *>(xbase + ((unsigned)min(j, q - 1) * xrs + xseg * 8u));
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-        br[i] = masked(br[i], 2 * brp + 2 * RP * (i >> 1) + (i & 1) < q);
+        for (int i = 0; i < NBV; ++i) {
+            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
+            r.b[i] = *reinterpret_cast<const u32x4 *>(bbase + ((unsigned)min(st * kJT + rr, q - 1) * brs + sg * 8u));
+        }
+    };
+    auto store_stage = [&](int st, int buf, const StageRegs<NBV> &r) {
+        const int j = st * kJT + xrow;
+        const float wj = w[j];  // zero at and beyond q
+        float v[8];
 #pragma unroll
-    for (int i = 0; i < NB / 2; ++i) {
-        const int j = 2 * brp + 2 * RP * i;
-        uint32_t *dst = reinterpret_cast<uint32_t *>(BT + bseg * 8 * LD + j);
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = lo_bf16(r.x[k]) * wj;
+            v[2 * k + 1] = hi_bf16(r.x[k]) * wj;
+        }
+        u32x4 hi, lo;
+        split8(v, hi, lo);
+        *reinterpret_cast<u32x4 *>(&xhi[buf][xrow * LDX + xseg * 8]) = masked(hi, j < q);
+        *reinterpret_cast<u32x4 *>(&xlo[buf][xrow * LDX + xseg * 8]) = masked(lo, j < q);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e * (LD / 2)] = pair16(br[2 * i], br[2 * i + 1], e);
-    }
+        for (int i = 0; i < NBV; ++i) {
+            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
+            *reinterpret_cast<u32x4 *>(&bst[buf][rr * LDB + sg * 8]) =
+                masked(r.b[i], st * kJT + rr < q);
+        }
+    };
+
+    // prefetch distance two: stage s+2's loads are issued while stage s is
+    // multiplied and stage s+1 (already in registers) is written to LDS
+    load_stage(0, R[0]);
+    load_stage(1, R[1]);
     __syncthreads();  // w complete
-    store_x_transposed<Q, LD>(xr, xT, w, xTlo);
+    store_stage(0, 0, R[0]);
     __syncthreads();
+
     constexpr int NT = N / 32, TPW = (2 * NT) / 4;
-    const int row = lane & 31, kh = (lane >> 5) * 8;
     f32x16 acc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = zero16();
-#pragma unroll 4
-    for (int k0 = 0; k0 < Q; k0 += 16) {
+    auto step = [&](int st, auto par) {
+        constexpr int PAR = decltype(par)::value;  // st % 2, the LDS buffer
+        if (st + 2 < NST) load_stage(st + 2, R[PAR]);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int tile = wave + 4 * t, pt = tile / NT, nt = tile % NT;
-            const int ao = (pt * 32 + row) * LD + k0 + kh;
-            const u32x4 a = *reinterpret_cast<const u32x4 *>(xT + ao);
-            const u32x4 al = *reinterpret_cast<const u32x4 *>(xTlo + ao);
-            const u32x4 bb = *reinterpret_cast<const u32x4 *>(BT + (nt * 32 + row) * LD + k0 + kh);
-            acc[t] = mfma32(a, bb, acc[t]);
-            acc[t] = mfma32(al, bb, acc[t]);
+        for (int ks = 0; ks < kJT / 16; ++ks) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int tile = wave + 4 * t, pt = tile / NT, nt = tile % NT;
+                const u32x4 ah = tr_operand<false>(xhi[PAR], LDX, 16 * ks, 32 * pt);
+                const u32x4 al = tr_operand<false>(xlo[PAR], LDX, 16 * ks, 32 * pt);
+                const u32x4 bb = tr_operand<false>(bst[PAR], LDB, 16 * ks, 32 * nt);
+                acc[t] = mfma32(ah, bb, acc[t]);
+                acc[t] = mfma32(al, bb, acc[t]);
+            }
         }
+        if (st + 1 < NST) store_stage(st + 1, PAR ^ 1, R[PAR ^ 1]);
+        __syncthreads();
+    };
+    for (int st = 0; st < NST; st += 2) {  // NST is even
+        step(st, P0{});
+        step(st + 1, P1{});
     }
     float *out = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
 #pragma unroll
@@ -216,68 +250,113 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int p = pt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            out[p * N + nt * 32 + row] = acc[t][r];
+            out[p * N + nt * 32 + (lane & 31)] = acc[t][r];
         }
     }
 }
 
 // ------------------------------------------------------------- chunk scan
-// One block (4 waves) per (b, c, h); 32-row output tiles i, wave w owns tiles
-// {w, NI-1-w} when the chunk has 8 tiles (equal causal work) and tile w
-// otherwise.  Per output tile the wave computes Y^T (64 x 32, two
-// accumulators over p):
-//   off-diagonal j-tiles:  S^T = B_j C_i^T (MFMA), scaled per column j by
-//       cf[j] = exp(Acs_k - Acs_j) dt_j with k the tile's first row, then
-//       Y^T += X_j^T M^T;  afterwards Y^T *= exp(Acs_i - Acs_k) per row i;
-//   state term:            Y^T += exp(Acs_i) H C_i^T;
-//   diagonal j-tile:       M^T[j][i] = S^T exp(Acs_i - Acs_j) dt_j for j <= i;
-//   epilogue:              y = Y + D x, rounded to bf16.
-// Both exponent splits keep every exponent <= 0, so nothing overflows.  The
-// operands formed inside the kernel (M and the entering state H) are carried
-// as hi/lo bf16 pairs (two MFMAs each), so only x, B and C, which arrive in
-// bf16, are single bf16 operands.
+// One block (4 waves) per (b, c, h); 32-row output tiles.  Wave w owns tiles
+// {w, NI-1-w} when the chunk has 8 tiles (equal causal work), else tile w.
+// Per owned tile the wave keeps Y^T (64 x 32, two accumulators over p) and
+// the tile's C rows in registers; the two tiles share every operand read of
+// a step, so their MFMA chains interleave.
+//
+//  prologue: the entering state H (hi/lo bf16) is staged in LDS and the state
+//            term starts each accumulator: Y^T = exp(Acs_k) H C_i^T, k the
+//            tile's first row;
+//  j loop:   32-token stages of B (natural layout) and x (natural layout, read
+//            transposed) stream through two LDS buffers, loaded two stages
+//            ahead.  For each owned tile i >= j:  S^T = B_j C_i^T (MFMA);
+//              off-diagonal: M^T = S^T * cf[j], cf[j] = exp(Acs_k - Acs_j) dt_j;
+//              diagonal:     Y^T *= exp(Acs_i - Acs_k) first, then
+//                            M^T[j][i] = S^T exp(Acs_i - Acs_j) dt_j for j <= i;
+//            Y^T += X_j^T M^T (M as a hi/lo pair).
+//  epilogue: one step after its diagonal (when the wave has no other work for
+//            that tile) the tile's y = Y + D x is staged in LDS and written as
+//            full 128-byte rows.
+// The row factor exp(Acs_i - Acs_k) times exp(Acs_k) gives the state term its
+// exp(Acs_i); every exponent used is <= 0.
 template <int Q, int N>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                   const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
                   const float *__restrict__ D, const float *__restrict__ Acs,
                   const float *__restrict__ states, bf16 *__restrict__ y, int64_t L, int H, int G,
-                  int T) {
+                  int T, int64_t nblocks) {
     constexpr int NI = Q / 32;
-    constexpr int LDX = Q + 8;
-    constexpr int LDB = N + 8;
     constexpr int KS = N / 16;
-    __shared__ __attribute__((aligned(16))) bf16 xT[kP * LDX];
-    __shared__ __attribute__((aligned(16))) bf16 Bs[Q * LDB];
-    __shared__ __attribute__((aligned(16))) bf16 Hs[kP * LDB];
-    __shared__ __attribute__((aligned(16))) bf16 Hlo[kP * LDB];
+    constexpr int LDH = N + 8;   // H rows, read as plain 16-byte operands
+    constexpr int LDB = N + 8;   // B stage rows, read as plain 16-byte operands
+    constexpr int LDX = kP + 16; // x stage rows, read transposed
+    constexpr int LDY = kP + 8;  // bf16 y staging rows
+    constexpr int H_BYTES = 2 * kP * LDH * 2;
+    constexpr int Y_BYTES = 4 * 32 * LDY * 2;
+    constexpr int HY_BYTES = H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES;
+    constexpr int BSEG = N / 8;
+    constexpr int NBV = kJT * BSEG / 256;
+    constexpr int NHV = kP * N / 4 / 256;
+    __shared__ __attribute__((aligned(16))) char hy[HY_BYTES];
+    __shared__ __attribute__((aligned(16))) bf16 bst[2][kJT * LDB];
+    __shared__ __attribute__((aligned(16))) bf16 xst[2][kJT * LDX];
+    __shared__ __attribute__((aligned(16))) float cf[NI][Q];
     __shared__ __attribute__((aligned(16))) float acs_s[Q];
     __shared__ __attribute__((aligned(16))) float dt_s[Q];
-    __shared__ __attribute__((aligned(16))) float cf[NI][Q];
+    const int64_t lb = xcd_block();
+    if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.x % H;
-    const int64_t bc = blockIdx.x / H;
+    const int il = lane & 31, g2 = lane >> 5;
+    const int h = (int)(lb % H);
+    const int64_t bc = lb / H;
     const int c = (int)(bc % T);
     const int64_t b = bc / T;
     const int g = h / (H / G);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
-    // issue every global load of the block first: x rows, B rows, entering state
-    u32x4 xr[Q / 32];
-    load_x_rows<Q>(xr, x + ((b * L + t0) * H + h) * kP, (int64_t)H * kP, q);
-    constexpr int SEGS = N / 8, NB = Q * SEGS / 256, NH = kP * N / 4 / 256;
-    const bf16 *brow0 = Bm + ((b * L + t0) * G + g) * N;
-    const int64_t brs = (int64_t)G * N;
-    u32x4 br[NB];
+    const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
+    const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
+    // per-thread offsets are unsigned 32-bit from block-uniform bases (a
+    // chunk spans < 2^31 elements of x, B, C and y), so loads and stores use
+    // the scalar-base + 32-bit-offset address form
+    const unsigned xrs = H * kP, brs = G * N;
+    const int xrow = tid >> 3, xseg = tid & 7;
+    bf16 *Hh = reinterpret_cast<bf16 *>(hy);
+    bf16 *Hl = Hh + kP * LDH;
+
+    const int ntiles = NI == 8 ? 2 : (wave < NI ? 1 : 0);
+    const int itile[2] = {wave, NI - 1 - wave};
+
+    StageRegs<NBV> R[2];
+    auto load_stage = [&](int st, StageRegs<NBV> &r) {
+        const int j = st * kJT + xrow;
+        r.x = *reinterpret_cast<const u32x4 *>(xbase + ((unsigned)min(j, q - 1) * xrs + xseg * 8u));
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int e = tid + 256 * i, j = e / SEGS, seg = e % SEGS;
-        br[i] = *reinterpret_cast<const u32x4 *>(brow0 + min(j, q - 1) * brs + seg * 8);
+        for (int i = 0; i < NBV; ++i) {
+            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
+            r.b[i] = *reinterpret_cast<const u32x4 *>(
+                bbase + ((unsigned)min(st * kJT + rr, q - 1) * brs + sg * 8u));
+        }
+    };
+    auto store_stage = [&](int st, int buf, const StageRegs<NBV> &r) {
+        *reinterpret_cast<u32x4 *>(&xst[buf][xrow * LDX + xseg * 8]) =
+            masked(r.x, st * kJT + xrow < q);
+#pragma unroll
+        for (int i = 0; i < NBV; ++i) {
+            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
+            *reinterpret_cast<u32x4 *>(&bst[buf][rr * LDB + sg * 8]) =
+                masked(r.b[i], st * kJT + rr < q);
+        }
+    };
+
+    // ---- prologue: issue the global loads first
+    float4 hv[NHV];
+    {
+        const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
+#pragma unroll
+        for (int i = 0; i < NHV; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + 256 * i));
     }
-    const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
-    float4 hr[NH];
-#pragma unroll
-    for (int i = 0; i < NH; ++i) hr[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + 256 * i));
+    load_stage(0, R[0]);
+    load_stage(1, R[1]);  // NI >= 2
     {
         const float *acs = Acs + (b * H + h) * L + t0;
         const float last = acs[q - 1];
@@ -288,167 +367,215 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             dt_s[j] = j < q ? d : 0.f;
         }
     }
-    store_x_transposed<Q, LDX>(xr, xT, nullptr, nullptr);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int e = tid + 256 * i, j = e / SEGS, seg = e % SEGS;
-        *reinterpret_cast<u32x4 *>(Bs + j * LDB + seg * 8) = masked(br[i], j < q);
-    }
-#pragma unroll
-    for (int i = 0; i < NH; ++i) {
+    for (int i = 0; i < NHV; ++i) {
         const int e = tid + 256 * i, p = e / (N / 4), n = (e % (N / 4)) * 4;
+        u32x2 hh, hl;
         uint32_t l0, l1;
-        u32x2 pk, pl;
-        pk[0] = split_pair(hr[i].x, hr[i].y, l0);
-        pk[1] = split_pair(hr[i].z, hr[i].w, l1);
-        pl[0] = l0;
-        pl[1] = l1;
-        *reinterpret_cast<u32x2 *>(Hs + p * LDB + n) = pk;
-        *reinterpret_cast<u32x2 *>(Hlo + p * LDB + n) = pl;
+        hh[0] = split2(hv[i].x, hv[i].y, l0);
+        hh[1] = split2(hv[i].z, hv[i].w, l1);
+        hl[0] = l0;
+        hl[1] = l1;
+        *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
+        *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
+    }
+    store_stage(0, 0, R[0]);
+    // C rows of the owned tiles stay in registers for the whole kernel
+    u32x4 creg[2][KS];
+    {
+        const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i_loc = itile[t] * 32 + il;
+            const unsigned coff = (unsigned)max(0, min(i_loc, q - 1)) * brs + 8u * g2;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                creg[t][s] = u32x4{0u, 0u, 0u, 0u};
+                if (t < ntiles)
+                    creg[t][s] = masked(*reinterpret_cast<const u32x4 *>(cbase + (coff + 16u * s)),
+                                        i_loc < q);
+            }
+        }
     }
     __syncthreads();
     for (int e = tid; e < NI * Q; e += 256) {
         const int kt = e / Q, j = e % Q;
         cf[kt][j] = j < 32 * kt ? ssd_exp(acs_s[32 * kt] - acs_s[j]) * dt_s[j] : 0.f;
     }
-    __syncthreads();
-
-    const float Dh = D ? D[h] : 0.f;
-    const int il = lane & 31, g2 = lane >> 5;
-    const int ntiles = NI == 8 ? 2 : (wave < NI ? 1 : 0);
-    for (int ti = 0; ti < ntiles; ++ti) {
-        const int it = ti == 0 ? wave : NI - 1 - wave;
-        const int i_loc = it * 32 + il;
-        const int64_t tok = b * L + t0 + i_loc;
-        u32x4 creg[KS];
-        const int64_t ctok = b * L + t0 + min(i_loc, q - 1);
+    // state term: Y^T = exp(Acs_k) H C_i^T, both tiles together (four chains)
+    f32x16 yacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            creg[s] = *reinterpret_cast<const u32x4 *>(Cm + (ctok * G + g) * N + 16 * s + 8 * g2);
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) creg[s] = masked(creg[s], i_loc < q);
-        const float acs_i = acs_s[i_loc];
-        const int k = it * 32;
-        f32x16 yacc[2] = {zero16(), zero16()};
-        // off-diagonal j-tiles (all j < k <= i)
-        for (int jt = 0; jt < it; ++jt) {
-            f32x16 s = zero16();
+        for (int pt = 0; pt < 2; ++pt) {
+            const int ho = (pt * 32 + il) * LDH + 16 * s + 8 * g2;
+            const u32x4 ah = *reinterpret_cast<const u32x4 *>(Hh + ho);
+            const u32x4 al = *reinterpret_cast<const u32x4 *>(Hl + ho);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(Bs + (jt * 32 + il) * LDB + 16 * ks + 8 * g2);
-                s = mfma32(a, creg[ks], s);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int jb = jt * 32 + 16 * u + 4 * g2;
-                const float4 c0 = *reinterpret_cast<const float4 *>(&cf[it][jb]);
-                const float4 c1 = *reinterpret_cast<const float4 *>(&cf[it][jb + 8]);
-                float m[8] = {s[8 * u + 0] * c0.x, s[8 * u + 1] * c0.y, s[8 * u + 2] * c0.z,
-                              s[8 * u + 3] * c0.w, s[8 * u + 4] * c1.x, s[8 * u + 5] * c1.y,
-                              s[8 * u + 6] * c1.z, s[8 * u + 7] * c1.w};
-                u32x4 bop, bopl;
-                pack8_split(m, bop, bopl);
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const bf16 *xr = xT + (pt * 32 + il) * LDX + jb;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(xr);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(xr + 8);
-                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                    yacc[pt] = mfma32(a, bop, yacc[pt]);
-                    yacc[pt] = mfma32(a, bopl, yacc[pt]);
+            for (int t = 0; t < 2; ++t) {
+                if (t < ntiles) {
+                    yacc[t][pt] = mfma32(ah, creg[t][s], yacc[t][pt]);
+                    yacc[t][pt] = mfma32(al, creg[t][s], yacc[t][pt]);
                 }
             }
         }
-        // state term
-        f32x16 z[2] = {zero16(), zero16()};
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float acs_i[2], ri[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                const int ho = (pt * 32 + il) * LDB + 16 * ks + 8 * g2;
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(Hs + ho);
-                const u32x4 al = *reinterpret_cast<const u32x4 *>(Hlo + ho);
-                z[pt] = mfma32(a, creg[ks], z[pt]);
-                z[pt] = mfma32(al, creg[ks], z[pt]);
-            }
-        }
-        const float ri = ssd_exp(acs_i - acs_s[k]);
-        const float ei = ssd_exp(acs_i);
+    for (int t = 0; t < 2; ++t) {
+        const int k = min(max(0, itile[t]), NI - 1) * 32;  // clamped for idle slots
+        acs_i[t] = acs_s[k + il];
+        ri[t] = ssd_exp(acs_i[t] - acs_s[k]);
+        const float ek = ssd_exp(acs_s[k]);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) yacc[pt][r] = yacc[pt][r] * ri + z[pt][r] * ei;
-        // diagonal tile
-        {
-            f32x16 s = zero16();
+            for (int r = 0; r < 16; ++r) yacc[t][pt][r] *= ek;
+    }
+    __syncthreads();  // cf complete; H no longer read (its LDS becomes y staging)
+
+    bf16 *ys = reinterpret_cast<bf16 *>(hy) + wave * 32 * LDY;
+    bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
+    const float Dh = D ? D[h] : 0.f;
+
+    // y tile t (D x already added) as bf16 via LDS, written as full rows
+    auto epilogue = [&](int t, int jt) {
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int p0 = pt * 32 + 8 * rg + 4 * g2;
+                u32x2 o;
+                o[0] = pack_bf16x2(yacc[t][pt][4 * rg + 0], yacc[t][pt][4 * rg + 1]);
+                o[1] = pack_bf16x2(yacc[t][pt][4 * rg + 2], yacc[t][pt][4 * rg + 3]);
+                *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
+            const int row = jt * 32 + r;  // formed in the loop: no hoisted 64-bit addresses
+            if (row < q) *reinterpret_cast<u32x4 *>(ybase + ((unsigned)row * xrs + 8u * sg)) = o;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    auto jstep = [&](int jt, auto par) {
+        constexpr int buf = decltype(par)::value;  // jt % 2, the LDS buffer
+        if (jt + 2 < NI) load_stage(jt + 2, R[buf]);
+        bool act[2], diag[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            act[t] = t < ntiles && itile[t] >= jt;
+            diag[t] = act[t] && itile[t] == jt;
+        }
+        if (act[0] || act[1]) {
+            f32x16 sacc[2] = {zero16(), zero16()};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(Bs + (k + il) * LDB + 16 * ks + 8 * g2);
-                s = mfma32(a, creg[ks], s);
+                    *reinterpret_cast<const u32x4 *>(&bst[buf][il * LDB + 16 * ks + 8 * g2]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (act[t]) sacc[t] = mfma32(a, creg[t][ks], sacc[t]);
             }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+                if (diag[t]) {
+                    // rescale the state term to exp(Acs_i) and add D x (x rows
+                    // of this tile are the current stage)
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const int p0 = pt * 32 + 8 * rg + 4 * g2;
+                            const u32x2 xr =
+                                *reinterpret_cast<const u32x2 *>(&xst[buf][il * LDX + p0]);
+                            const int r0 = 4 * rg;
+                            yacc[t][pt][r0 + 0] = yacc[t][pt][r0 + 0] * ri[t] + Dh * lo_bf16(xr[0]);
+                            yacc[t][pt][r0 + 1] = yacc[t][pt][r0 + 1] * ri[t] + Dh * hi_bf16(xr[0]);
+                            yacc[t][pt][r0 + 2] = yacc[t][pt][r0 + 2] * ri[t] + Dh * lo_bf16(xr[1]);
+                            yacc[t][pt][r0 + 3] = yacc[t][pt][r0 + 3] * ri[t] + Dh * hi_bf16(xr[1]);
+                        }
+                }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                float m[8];
+                // this lane's rows j of S^T in half u: j = jt*32 + 16u + 8(e/4) + 4 g2 + e%4
+                u32x4 bop[2], bopl[2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int jl = 16 * u + 8 * (e >> 2) + 4 * g2 + (e & 3);
-                    const int j = k + jl;
-                    m[e] = jl <= il ? s[8 * u + e] * ssd_exp(acs_i - acs_s[j]) * dt_s[j] : 0.f;
+                for (int t = 0; t < 2; ++t) {
+                    if (!act[t]) continue;
+                    float m[8];
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        const int jl = 16 * u + 8 * v + 4 * g2;
+                        float4 fv;
+                        if (!diag[t]) {
+                            fv = *reinterpret_cast<const float4 *>(&cf[itile[t]][jt * 32 + jl]);
+                        } else {
+                            const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[jt * 32 + jl]);
+                            const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[jt * 32 + jl]);
+                            fv.x = jl + 0 <= il ? ssd_exp(acs_i[t] - aj.x) * dj.x : 0.f;
+                            fv.y = jl + 1 <= il ? ssd_exp(acs_i[t] - aj.y) * dj.y : 0.f;
+                            fv.z = jl + 2 <= il ? ssd_exp(acs_i[t] - aj.z) * dj.z : 0.f;
+                            fv.w = jl + 3 <= il ? ssd_exp(acs_i[t] - aj.w) * dj.w : 0.f;
+                        }
+                        m[4 * v + 0] = sacc[t][8 * u + 4 * v + 0] * fv.x;
+                        m[4 * v + 1] = sacc[t][8 * u + 4 * v + 1] * fv.y;
+                        m[4 * v + 2] = sacc[t][8 * u + 4 * v + 2] * fv.z;
+                        m[4 * v + 3] = sacc[t][8 * u + 4 * v + 3] * fv.w;
+                    }
+                    split8(m, bop[t], bopl[t]);
                 }
-                u32x4 bop, bopl;
-                pack8_split(m, bop, bopl);
-                const int jb = k + 16 * u + 4 * g2;
 #pragma unroll
                 for (int pt = 0; pt < 2; ++pt) {
-                    const bf16 *xr = xT + (pt * 32 + il) * LDX + jb;
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(xr);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(xr + 8);
-                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                    yacc[pt] = mfma32(a, bop, yacc[pt]);
-                    yacc[pt] = mfma32(a, bopl, yacc[pt]);
+                    const u32x4 xa = tr_operand<true>(xst[buf], LDX, 16 * u, 32 * pt);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        if (act[t]) {
+                            yacc[t][pt] = mfma32(xa, bop[t], yacc[t][pt]);
+                            yacc[t][pt] = mfma32(xa, bopl[t], yacc[t][pt]);
+                        }
                 }
             }
         }
-        // epilogue: lane holds row i_loc and p = pt*32 + 8*(r/4) + 4*g2 + r%4
-        if (i_loc < q) {
-            bf16 *yr = y + (tok * H + h) * kP;
+        // finished tiles are written one step later, off the diagonal step
 #pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                    float v[4];
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const float xv = __uint_as_float((uint32_t)xT[(p0 + kk) * LDX + i_loc] << 16);
-                        v[kk] = yacc[pt][4 * rg + kk] + Dh * xv;
-                    }
-                    u32x2 pk;
-                    pk[0] = pack_bf16x2(v[0], v[1]);
-                    pk[1] = pack_bf16x2(v[2], v[3]);
-                    *reinterpret_cast<u32x2 *>(yr + p0) = pk;
-                }
-            }
-        }
+        for (int t = 0; t < 2; ++t)
+            if (t < ntiles && itile[t] == jt - 1) epilogue(t, jt - 1);
+        if (jt + 1 < NI) store_stage(jt + 1, buf ^ 1, R[buf ^ 1]);
+        __syncthreads();
+    };
+    for (int jt = 0; jt < NI; jt += 2) {  // NI is even
+        jstep(jt, P0{});
+        jstep(jt + 1, P1{});
     }
+    // the last tile (NI-1) finished in the final step
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        if (t < ntiles && itile[t] == NI - 1) epilogue(t, NI - 1);
 }
 
 template <int Q, int N>
 void launch_state_t(const ScanShape &s, const void *x, const void *Bm, const float *dt,
                     const float *Acs, float *states, hipStream_t st) {
-    k_chunk_state_mfma<Q, N><<<(unsigned)(s.B * s.T * s.H), 256, 0, st>>>(
-        (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T);
+    const int64_t nb = s.B * s.T * s.H;
+    k_chunk_state_mfma<Q, N><<<padded_grid(nb), 256, 0, st>>>(
+        (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T, nb);
 }
 
 template <int Q, int N>
 void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                    const void *Cm, const float *D, const float *Acs, const float *states, void *y,
                    hipStream_t st) {
-    k_chunk_scan_mfma<Q, N><<<(unsigned)(s.B * s.T * s.H), 256, 0, st>>>(
+    const int64_t nb = s.B * s.T * s.H;
+    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y, s.L,
-        (int)s.H, (int)s.G, (int)s.T);
+        (int)s.H, (int)s.G, (int)s.T, nb);
 }
 
 }  // namespace
