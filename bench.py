@@ -116,8 +116,6 @@ def cpu_baseline(spec, inp, budget_s=10.0):
         el = time.perf_counter() - t0
         if reps >= 2 and el >= budget_s:
             break
-        if reps >= 50:
-            break
     tokens = spec.batch * spec.seqlen * reps
     return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"full {spec.name} prefill ({spec.batch}x{spec.seqlen} tokens, "
@@ -182,6 +180,8 @@ def main():
     states2 = torch.empty_like(states)
     y2 = torch.empty_like(y)
     fin2 = torch.empty_like(fin)
+    cbn = binding.chunk_scan_workspace_size(Bt, L, H, P, N, G, Q, torch.bfloat16)
+    cbws = torch.empty(max(cbn, 1), dtype=torch.uint8, device=dev)
     stage_fns = {
         "chunk_cumsum": Lean(torch, lib.ssd_chunk_cumsum, dref, P_(d["dt"]), P_(d["A"]), P_(Acs)),
         "chunk_state": Lean(torch, lib.ssd_chunk_state, dref, P_(d["x"]), P_(d["B"]),
@@ -189,7 +189,8 @@ def main():
         "state_passing": Lean(torch, lib.ssd_state_passing, dref, P_(states2), P_(Acs),
                               P_(d["init"]), P_(fin2)),
         "chunk_scan": Lean(torch, lib.ssd_chunk_scan, dref, P_(d["x"]), P_(d["dt"]), P_(d["B"]),
-                           P_(d["C"]), P_(d["D"]), P_(Acs), P_(states), P_(y2)),
+                           P_(d["C"]), P_(d["D"]), P_(Acs), P_(states), P_(y2), P_(cbws),
+                           cbws.numel()),
     }
     stage_fns["chunk_cumsum"]()
     stage_fns["chunk_state"]()

@@ -55,7 +55,7 @@ typedef enum ssd_status {
     SSD_ERR_UNSUPPORTED = 3, /* chunk, headdim or dstate outside the limits below,
                                 unknown dtype                                    */
     SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
-    SSD_ERR_WORKSPACE = 5,   /* workspace smaller than ssd_scan_workspace_size   */
+    SSD_ERR_WORKSPACE = 5,   /* workspace smaller than its *_workspace_size      */
     SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch      */
 } ssd_status;
 
@@ -81,7 +81,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -146,13 +146,23 @@ ssd_status ssd_chunk_state(const ssd_scan_desc *d, const void *x, const void *B,
 ssd_status ssd_state_passing(const ssd_scan_desc *d, float *states, const float *Acs,
                              const float *init_state, float *final_state, void *stream);
 
+/* Bytes of device workspace ssd_chunk_scan needs for shape *d (0 is possible).
+ * It holds the within-chunk products C_t . B_j, which do not depend on the
+ * head and are formed once per (batch, chunk, group); its contents are
+ * internal and need no initialisation. */
+ssd_status ssd_chunk_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes);
+
 /* y for every chunk from the chunk-entry states:
  *   y[t] = sum_{j <= t in chunk} (C_t . B_j) exp(Acs_t - Acs_j) dt_j x_j
  *          + exp(Acs_t) (C_t . H_c) + D x_t
- * with H_c = states[c] as left by ssd_state_passing. */
+ * with H_c = states[c] as left by ssd_state_passing ("Compiler-First ...",
+ * §3, the intra-chunk output contraction of B.5).  workspace: device buffer
+ * of at least ssd_chunk_scan_workspace_size bytes (may be NULL when that size
+ * is 0); it must not overlap any other argument. */
 ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
                           const void *B, const void *C, const float *D, const float *Acs,
-                          const float *states, void *y, void *stream);
+                          const float *states, void *y, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -24,7 +24,7 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 # Every function include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
            "ssd_step", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-           "ssd_chunk_scan")
+           "ssd_chunk_scan_workspace_size", "ssd_chunk_scan")
 
 
 class ScanDesc(ctypes.Structure):
@@ -72,7 +72,10 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_cumsum.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 4
         L.ssd_chunk_state.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 6
         L.ssd_state_passing.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 5
-        L.ssd_chunk_scan.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 9
+        L.ssd_chunk_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_chunk_scan.argtypes = ([ctypes.POINTER(ScanDesc)] + [_P] * 9
+                                     + [ctypes.c_size_t, _P])
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -261,8 +264,19 @@ def state_passing(states, Acs, chunk: int, x_like, init_state=None, final_state=
     return final_state
 
 
-def chunk_scan(x, dt, B, C, D, Acs, states, chunk: int):
-    """Stage 4: y from the chunk-entry states."""
+def chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                              dtype) -> int:
+    d = ScanDesc(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                 SSD_BF16 if dtype == torch.bfloat16 else SSD_F32, 0)
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_scan_workspace_size",
+           lib().ssd_chunk_scan_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def chunk_scan(x, dt, B, C, D, Acs, states, chunk: int, workspace=None):
+    """Stage 4: y from the chunk-entry states (``workspace``: optional uint8
+    device tensor of at least :func:`chunk_scan_workspace_size` bytes)."""
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, torch.empty(x.shape[2], device=x.device),
                                            B, C, D)
     T = -(-L // chunk)
@@ -270,7 +284,14 @@ def chunk_scan(x, dt, B, C, D, Acs, states, chunk: int):
     _need(states, "states", (Bt, T, H, P, N), torch.float32, x.device)
     y = torch.empty_like(x)
     desc = _scan_desc(x, B, chunk)
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_scan_workspace_size",
+           lib().ssd_chunk_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    if workspace is None and n.value:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssd_chunk_scan", lib().ssd_chunk_scan(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(B),
                                                   _ptr(C), _ptr(D), _ptr(Acs), _ptr(states),
-                                                  _ptr(y), _stream(x.device)))
+                                                  _ptr(y), _ptr(workspace), ws_bytes,
+                                                  _stream(x.device)))
     return y

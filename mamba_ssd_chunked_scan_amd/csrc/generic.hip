@@ -301,11 +301,16 @@ void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
                                            (int)s.Q, (int)s.T);
 }
 
+size_t chunk_scan_ws_bytes(const ScanShape &s) {
+    return mfma_supported(s) ? chunk_cb_bytes(s) : 0;
+}
+
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       void *y, hipStream_t st) {
+                       void *ws, void *y, hipStream_t st) {
     if (mfma_supported(s)) {
-        launch_chunk_scan_mfma(s, x, dt, Bm, Cm, D, Acs, states, y, st);
+        launch_chunk_cb_mfma(s, Bm, Cm, ws, st);
+        launch_chunk_scan_mfma(s, x, dt, Cm, D, Acs, states, ws, y, st);
         return;
     }
     dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.Q + kScanRows - 1) / kScanRows));

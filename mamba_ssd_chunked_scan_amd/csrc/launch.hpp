@@ -24,9 +24,11 @@ void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const
                         const float *Acs, float *states, hipStream_t st);
 void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
                           const float *init, float *fin, hipStream_t st);
+// Device workspace of the chunk-output stage (0 when its kernel needs none).
+size_t chunk_scan_ws_bytes(const ScanShape &s);
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       void *y, hipStream_t st);
+                       void *ws, void *y, hipStream_t st);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
@@ -40,8 +42,12 @@ void launch_step(const StepShape &s, float *state, const void *x, const float *d
 bool mfma_supported(const ScanShape &s);
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
                              const float *dt, const float *Acs, float *states, hipStream_t st);
-void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt,
-                            const void *Bm, const void *Cm, const float *D, const float *Acs,
-                            const float *states, void *y, hipStream_t st);
+// C.B tiles of every (b, c, g), shared by the heads of a group (chunk_cb_bytes).
+size_t chunk_cb_bytes(const ScanShape &s);
+void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
+                          hipStream_t st);
+void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
+                            const float *D, const float *Acs, const float *states, const void *cb,
+                            void *y, hipStream_t st);
 
 }  // namespace ssd

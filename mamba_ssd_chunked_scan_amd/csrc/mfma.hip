@@ -116,6 +116,27 @@ __device__ __forceinline__ int64_t xcd_block() {
 
 unsigned padded_grid(int64_t blocks) { return (unsigned)((blocks + 7) / 8 * 8); }
 
+// Raw buffer resource over [base, base + bytes): 16-byte loads at or past the
+// end return zeros and stores there are dropped, and the per-lane offset is a
+// 32-bit register beside a scalar base.  Dword 3 is the gfx9 raw-buffer format.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// The same range starting `off` bytes in (wave-uniform): the resource's own
+// base and size move, so the range check covers the shift and the per-lane
+// offset stays a small register.
+__device__ __forceinline__ rsrc_t buffer_rsrc_at(const void *base, uint32_t bytes, uint32_t off) {
+    off = __builtin_amdgcn_readfirstlane(off);
+    return buffer_rsrc(static_cast<const char *>(base) + off, bytes > off ? bytes - off : 0u);
+}
+__device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buffer_store16(u32x4 v, rsrc_t r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+
 // Registers holding one 32-token stage between its global load and its LDS
 // store: one 16-byte x segment and NBV 16-byte B segments per thread.  Two sets
 // give a prefetch distance of two stages.
@@ -255,57 +276,129 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     }
 }
 
-// ------------------------------------------------------------- chunk scan
-// One block (4 waves) per (b, c, h); 32-row output tiles.  Wave w owns tiles
-// {w, NI-1-w} when the chunk has 8 tiles (equal causal work), else tile w.
-// Per owned tile the wave keeps Y^T (64 x 32, two accumulators over p) and
-// the tile's C rows in registers; the two tiles share every operand read of
-// a step, so their MFMA chains interleave.
-//
-//  prologue: the entering state H (hi/lo bf16) is staged in LDS and the state
-//            term starts each accumulator: Y^T = exp(Acs_k) H C_i^T, k the
-//            tile's first row;
-//  j loop:   32-token stages of B (natural layout) and x (natural layout, read
-//            transposed) stream through two LDS buffers, loaded two stages
-//            ahead.  For each owned tile i >= j:  S^T = B_j C_i^T (MFMA);
-//              off-diagonal: M^T = S^T * cf[j], cf[j] = exp(Acs_k - Acs_j) dt_j;
-//              diagonal:     Y^T *= exp(Acs_i - Acs_k) first, then
-//                            M^T[j][i] = S^T exp(Acs_i - Acs_j) dt_j for j <= i;
-//            Y^T += X_j^T M^T (M as a hi/lo pair).
-//  epilogue: one step after its diagonal (when the wave has no other work for
-//            that tile) the tile's y = Y + D x is staged in LDS and written as
-//            full 128-byte rows.
-// The row factor exp(Acs_i - Acs_k) times exp(Acs_k) gives the state term its
-// exp(Acs_i); every exponent used is <= 0.
+// ------------------------------------------------------------- C.B tiles
+// CB[i][j] = C_i . B_j for the causal 32x32 tiles (row tile ti >= column tile
+// jt) of one (b, c, g).  The product does not involve the head, so it is formed
+// once here and read by every head of group g.  One block per (b, c, g, ti);
+// wave w forms tiles jt = w, w+4, ... as S^T = B_jt C_ti^T (rows j, columns i).
+// Each tile is 4 KB, stored in the register layout of that 32x32 accumulator
+// (lane l: column i = l%32; register r: row j = 8(r/4) + 4(l/32) + r%4) so the
+// chunk scan reads it as an MFMA operand with one 16-byte load per lane and
+// 16-byte unit k*64 + lane:
+//   off-diagonal tile: k = 2u   -> bf16 hi part of registers 8u..8u+7,
+//                      k = 2u+1 -> bf16 residual lo of the same registers;
+//   diagonal tile:     k = v    -> fp32 registers 4v..4v+3 (the scan applies
+//                                  the per-head decay and the mask first).
+// Tiles of (b, c, g) are consecutive, tile (ti, jt) at ti(ti+1)/2 + jt.
 template <int Q, int N>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256)
+k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 *__restrict__ cb,
+                int64_t L, int G, int T, int64_t nblocks) {
+    constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
+    const int64_t lb = blockIdx.x;
+    if (lb >= nblocks) return;
+    const int lane = threadIdx.x & 63, il = lane & 31, g2 = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ti = (int)(lb % NI);
+    const int64_t bcg = lb / NI;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % T);
+    const int64_t b = bc / T;
+    const int64_t t0 = (int64_t)c * Q;
+    const int q = (int)min((int64_t)Q, L - t0);
+    const unsigned rs = G * N;
+    const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
+    const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
+    // rows past the end of a short chunk are clamped to its last row: finite
+    // values that the scan multiplies by zero (x and dt are zero there)
+    u32x4 crow[KS];
+    {
+        const unsigned off = (unsigned)min(32 * ti + il, q - 1) * rs + 8u * g2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) crow[s] = *reinterpret_cast<const u32x4 *>(cbase + (off + 16u * s));
+    }
+    u32x4 *out = cb + (bcg * NT + ti * (ti + 1) / 2) * 256;
+    for (int jt = wave; jt <= ti; jt += 4) {
+        const unsigned off = (unsigned)min(32 * jt + il, q - 1) * rs + 8u * g2;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            acc = mfma32(*reinterpret_cast<const u32x4 *>(bbase + (off + 16u * s)), crow[s], acc);
+        u32x4 *o = out + jt * 256;
+        if (jt < ti) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float m[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[e] = acc[8 * u + e];
+                u32x4 hi, lo;
+                split8(m, hi, lo);
+                o[(2 * u) * 64 + lane] = hi;
+                o[(2 * u + 1) * 64 + lane] = lo;
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
+                                         __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+        }
+    }
+}
+
+// ------------------------------------------------------------- chunk scan
+// One block per (b, c, h) with NI/2 waves (NI = Q/32 row tiles); wave w owns
+// row tiles ti0 = w and ti1 = NI-1-w, which together have NI+1 causal tile
+// visits for every wave.  Per owned tile the wave keeps Z = Y^T (64 x 32 fp32,
+// two accumulators over p).  With e(t) = 32t + 31 the last row of tile t and
+// Acs_{e(-1)} = 0, the output row i of tile ti is
+//   y_i = exp(Acs_i - Acs_{e(ti-1)}) Z_i + diagonal-tile part + D x_i,
+//   Z   = C_i.H, then for jt = 0..ti-1:
+//         Z <- exp(Acs_{e(jt)} - Acs_{e(jt-1)}) Z + sum_{j in jt} CB[i][j] xw_j,
+//         xw_j = exp(Acs_{e(jt)} - Acs_j) dt_j x_j,
+// which is the chunk output of the reference form regrouped by 32-row tiles:
+// every exponent is <= 0, so nothing overflows, and an underflow drops only
+// terms that are at least as small in the exact result.  xw depends on the
+// stage alone, so it is formed once per 32-token stage (as a hi/lo bf16 pair)
+// and shared by all waves; CB comes pre-split from the C.B tile kernel, and
+// the off-diagonal product takes three MFMAs (hi.hi, lo.hi, hi.lo).  The
+// diagonal tile applies exp(Acs_i - Acs_j) dt_j to the fp32 CB element by
+// element under the causal mask and multiplies raw x.
+//
+// Stages (raw x, xw hi, xw lo) stream through two LDS buffers, loaded two
+// stages ahead; the C.B tiles of the next step are loaded one step ahead.  The
+// tile loop branches on wave-uniform values only.  A tile's output goes out
+// one step after its diagonal, through LDS, as full 128-byte rows.
+template <int Q, int N>
+__global__ void __launch_bounds__(Q, 2) __attribute__((amdgpu_waves_per_eu(1, Q == 256 ? 2 : 1)))
 k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
-                  const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-                  const float *__restrict__ D, const float *__restrict__ Acs,
-                  const float *__restrict__ states, bf16 *__restrict__ y, int64_t L, int H, int G,
+                  const bf16 *__restrict__ Cm, const float *__restrict__ D,
+                  const float *__restrict__ Acs, const float *__restrict__ states,
+                  const u32x4 *__restrict__ cb, bf16 *__restrict__ y, int64_t L, int H, int G,
                   int T, int64_t nblocks) {
-    constexpr int NI = Q / 32;
-    constexpr int KS = N / 16;
-    constexpr int LDH = N + 8;   // H rows, read as plain 16-byte operands
-    constexpr int LDB = N + 8;   // B stage rows, read as plain 16-byte operands
-    constexpr int LDX = kP + 16; // x stage rows, read transposed
-    constexpr int LDY = kP + 8;  // bf16 y staging rows
+    constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
+    constexpr int TH = Q;                 // threads: NI/2 waves
+    constexpr int NW = TH / 64;
+    constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
+    constexpr int LDX = kP + 16;          // stage rows, read transposed
+    constexpr int LDY = kP + 8;           // bf16 y staging rows
     constexpr int H_BYTES = 2 * kP * LDH * 2;
-    constexpr int Y_BYTES = 4 * 32 * LDY * 2;
+    constexpr int Y_BYTES = NW * 32 * LDY * 2;
     constexpr int HY_BYTES = H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES;
-    constexpr int BSEG = N / 8;
-    constexpr int NBV = kJT * BSEG / 256;
-    constexpr int NHV = kP * N / 4 / 256;
+    constexpr int XV = 256 / TH;          // 16-byte x segments per thread per stage
+    constexpr int NHV = kP * N / 4 / TH;  // float4 of H per thread
+    constexpr int HB = NHV < 8 ? NHV : 8; // H float4 held in registers at a time
     __shared__ __attribute__((aligned(16))) char hy[HY_BYTES];
-    __shared__ __attribute__((aligned(16))) bf16 bst[2][kJT * LDB];
-    __shared__ __attribute__((aligned(16))) bf16 xst[2][kJT * LDX];
-    __shared__ __attribute__((aligned(16))) float cf[NI][Q];
+    __shared__ __attribute__((aligned(16))) bf16 xs[2][kJT * LDX];
+    __shared__ __attribute__((aligned(16))) bf16 xh[2][kJT * LDX];
+    __shared__ __attribute__((aligned(16))) bf16 xl[2][kJT * LDX];
     __shared__ __attribute__((aligned(16))) float acs_s[Q];
     __shared__ __attribute__((aligned(16))) float dt_s[Q];
     const int64_t lb = xcd_block();
     if (lb >= nblocks) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int il = lane & 31, g2 = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = (int)(lb % H);
     const int64_t bc = lb / H;
     const int c = (int)(bc % T);
@@ -314,250 +407,253 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
     const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
-    const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     // per-thread offsets are unsigned 32-bit from block-uniform bases (a
-    // chunk spans < 2^31 elements of x, B, C and y), so loads and stores use
-    // the scalar-base + 32-bit-offset address form
-    const unsigned xrs = H * kP, brs = G * N;
-    const int xrow = tid >> 3, xseg = tid & 7;
+    // chunk spans < 2^31 elements of x, C and y), so loads and stores use the
+    // scalar-base + 32-bit-offset address form
+    const unsigned xrs = H * kP, crs = G * N;
+    const u32x4 *cbg = cb + ((b * T + c) * G + g) * NT * 256;
+    const int ti0 = wave, ti1 = NI - 1 - wave;
+
+    // x rows of this chunk and head: bytes up to the end of row q-1, so rows
+    // past a short chunk's end read as zeros; y rows likewise (stores dropped)
+    const uint32_t xy_bytes = ((unsigned)(q - 1) * xrs + kP) * 2u;
+    u32x4 R[2][XV];
+    // thread (row, seg) of a stage: row = tid/8 + (TH/8) v, 8 bf16 at seg*8
+    const uint32_t xvoff = ((unsigned)(tid >> 3) * xrs + (tid & 7) * 8u) * 2u;
+    auto load_stage = [&](int st, u32x4 (&r)[XV]) {
+#pragma unroll
+        for (int v = 0; v < XV; ++v)
+            r[v] = buffer_load16(
+                buffer_rsrc_at(xbase, xy_bytes, (st * kJT + (TH / 8) * v) * xrs * 2u), xvoff);
+    };
+    // raw x and xw = exp(Acs_{e(st)} - Acs_j) dt_j x_j (hi/lo) of stage st
+    auto store_stage = [&](int st, int buf, const u32x4 (&r)[XV]) {
+        const float ae = acs_s[st * kJT + kJT - 1];
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+            const int e = tid + TH * v, row = e >> 3, seg = e & 7;
+            const int j = st * kJT + row;
+            const u32x4 raw = r[v];                              // zero past q
+            const float wj = ssd_exp(ae - acs_s[j]) * dt_s[j];  // dt_s is 0 past q
+            float m[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                m[2 * k] = lo_bf16(raw[k]) * wj;
+                m[2 * k + 1] = hi_bf16(raw[k]) * wj;
+            }
+            u32x4 hi, lo;
+            split8(m, hi, lo);
+            *reinterpret_cast<u32x4 *>(&xs[buf][row * LDX + seg * 8]) = raw;
+            *reinterpret_cast<u32x4 *>(&xh[buf][row * LDX + seg * 8]) = hi;
+            *reinterpret_cast<u32x4 *>(&xl[buf][row * LDX + seg * 8]) = lo;
+        }
+    };
+    // the 4 KB C.B tile (ti, jt) as four 16-byte operands of this lane
+    auto load_cb = [&](int ti, int jt, u32x4 (&o)[4]) {
+        const u32x4 *p = cbg + (ti * (ti + 1) / 2 + jt) * 256 + lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = p[k * 64];
+    };
+
+    // ---- prologue: global loads first
+    load_stage(0, R[0]);
+    if (NI > 1) load_stage(1, R[1]);
+    u32x4 cbr[2][2][4];  // [step parity][tile][operand]
+    load_cb(ti0, 0, cbr[0][0]);
+    load_cb(ti1, 0, cbr[0][1]);
+    {
+        const float *acs = Acs + (b * H + h) * L + t0;
+        const int jj = min(tid, q - 1);
+        const float a = acs[jj], d = dt[(b * L + t0 + jj) * H + h];
+        acs_s[tid] = tid < q ? a : acs[q - 1];
+        dt_s[tid] = tid < q ? d : 0.f;
+    }
     bf16 *Hh = reinterpret_cast<bf16 *>(hy);
     bf16 *Hl = Hh + kP * LDH;
-
-    const int ntiles = NI == 8 ? 2 : (wave < NI ? 1 : 0);
-    const int itile[2] = {wave, NI - 1 - wave};
-
-    StageRegs<NBV> R[2];
-    auto load_stage = [&](int st, StageRegs<NBV> &r) {
-        const int j = st * kJT + xrow;
-        r.x = *reinterpret_cast<const u32x4 *>(xbase + ((unsigned)min(j, q - 1) * xrs + xseg * 8u));
-#pragma unroll
-        for (int i = 0; i < NBV; ++i) {
-            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
-            r.b[i] = *reinterpret_cast<const u32x4 *>(
-                bbase + ((unsigned)min(st * kJT + rr, q - 1) * brs + sg * 8u));
-        }
-    };
-    auto store_stage = [&](int st, int buf, const StageRegs<NBV> &r) {
-        *reinterpret_cast<u32x4 *>(&xst[buf][xrow * LDX + xseg * 8]) =
-            masked(r.x, st * kJT + xrow < q);
-#pragma unroll
-        for (int i = 0; i < NBV; ++i) {
-            const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
-            *reinterpret_cast<u32x4 *>(&bst[buf][rr * LDB + sg * 8]) =
-                masked(r.b[i], st * kJT + rr < q);
-        }
-    };
-
-    // ---- prologue: issue the global loads first
-    float4 hv[NHV];
     {
         const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
 #pragma unroll
-        for (int i = 0; i < NHV; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + 256 * i));
-    }
-    load_stage(0, R[0]);
-    load_stage(1, R[1]);  // NI >= 2
-    {
-        const float *acs = Acs + (b * H + h) * L + t0;
-        const float last = acs[q - 1];
-        for (int j = tid; j < Q; j += 256) {
-            const int jj = min(j, q - 1);
-            const float a = acs[jj], d = dt[(b * L + t0 + jj) * H + h];
-            acs_s[j] = j < q ? a : last;
-            dt_s[j] = j < q ? d : 0.f;
+        for (int i0 = 0; i0 < NHV; i0 += HB) {
+            float4 hv[HB];
+#pragma unroll
+            for (int i = 0; i < HB; ++i)
+                hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * (i0 + i)));
+#pragma unroll
+            for (int i = 0; i < HB; ++i) {
+                const int e = tid + TH * (i0 + i), p = e / (N / 4), n = (e % (N / 4)) * 4;
+                u32x2 hh, hl;
+                uint32_t l0, l1;
+                hh[0] = split2(hv[i].x, hv[i].y, l0);
+                hh[1] = split2(hv[i].z, hv[i].w, l1);
+                hl[0] = l0;
+                hl[1] = l1;
+                *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
+                *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
+            }
         }
     }
-#pragma unroll
-    for (int i = 0; i < NHV; ++i) {
-        const int e = tid + 256 * i, p = e / (N / 4), n = (e % (N / 4)) * 4;
-        u32x2 hh, hl;
-        uint32_t l0, l1;
-        hh[0] = split2(hv[i].x, hv[i].y, l0);
-        hh[1] = split2(hv[i].z, hv[i].w, l1);
-        hl[0] = l0;
-        hl[1] = l1;
-        *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
-        *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
-    }
+    __syncthreads();  // acs_s, dt_s, H
     store_stage(0, 0, R[0]);
-    // C rows of the owned tiles stay in registers for the whole kernel
-    u32x4 creg[2][KS];
+    // state term Z = H C_i^T for both tiles (C rows straight from global)
+    f32x16 Z[2][2];
     {
         const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
+        const unsigned o0 = (unsigned)min(32 * ti0 + il, q - 1) * crs + 8u * g2;
+        const unsigned o1 = (unsigned)min(32 * ti1 + il, q - 1) * crs + 8u * g2;
+        u32x4 c0[KS], c1[KS];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int i_loc = itile[t] * 32 + il;
-            const unsigned coff = (unsigned)max(0, min(i_loc, q - 1)) * brs + 8u * g2;
+        for (int s = 0; s < KS; ++s) {
+            c0[s] = *reinterpret_cast<const u32x4 *>(cbase + (o0 + 16u * s));
+            c1[s] = *reinterpret_cast<const u32x4 *>(cbase + (o1 + 16u * s));
+        }
+        Z[0][0] = Z[0][1] = Z[1][0] = Z[1][1] = zero16();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                creg[t][s] = u32x4{0u, 0u, 0u, 0u};
-                if (t < ntiles)
-                    creg[t][s] = masked(*reinterpret_cast<const u32x4 *>(cbase + (coff + 16u * s)),
-                                        i_loc < q);
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const int ho = (pt * 32 + il) * LDH + 16 * s + 8 * g2;
+                const u32x4 ah = *reinterpret_cast<const u32x4 *>(Hh + ho);
+                const u32x4 al = *reinterpret_cast<const u32x4 *>(Hl + ho);
+                Z[0][pt] = mfma32(ah, c0[s], Z[0][pt]);
+                Z[1][pt] = mfma32(ah, c1[s], Z[1][pt]);
+                Z[0][pt] = mfma32(al, c0[s], Z[0][pt]);
+                Z[1][pt] = mfma32(al, c1[s], Z[1][pt]);
             }
         }
     }
-    __syncthreads();
-    for (int e = tid; e < NI * Q; e += 256) {
-        const int kt = e / Q, j = e % Q;
-        cf[kt][j] = j < 32 * kt ? ssd_exp(acs_s[32 * kt] - acs_s[j]) * dt_s[j] : 0.f;
-    }
-    // state term: Y^T = exp(Acs_k) H C_i^T, both tiles together (four chains)
-    f32x16 yacc[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+    __syncthreads();  // stage 0 visible; H no longer read (its LDS becomes y staging)
+
+    bf16 *ys = reinterpret_cast<bf16 *>(hy) + wave * 32 * LDY;
+    const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
+    const float Dh = D ? D[h] : 0.f;
+
+    auto scale = [&](f32x16 &z, float f) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+        for (int r = 0; r < 16; ++r) z[r] *= f;
+    };
+    // off-diagonal visit of column tile jt for the tiles in `mask` (bit t)
+    auto offdiag = [&](int jt, int buf, int mask, u32x4 (&cbt)[2][4]) {
+        const float f = ssd_exp(acs_s[jt * kJT + kJT - 1] - (jt > 0 ? acs_s[jt * kJT - 1] : 0.f));
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-            const int ho = (pt * 32 + il) * LDH + 16 * s + 8 * g2;
-            const u32x4 ah = *reinterpret_cast<const u32x4 *>(Hh + ho);
-            const u32x4 al = *reinterpret_cast<const u32x4 *>(Hl + ho);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                if (t < ntiles) {
-                    yacc[t][pt] = mfma32(ah, creg[t][s], yacc[t][pt]);
-                    yacc[t][pt] = mfma32(al, creg[t][s], yacc[t][pt]);
-                }
+        for (int t = 0; t < 2; ++t)
+            if (mask >> t & 1) {
+                scale(Z[t][0], f);
+                scale(Z[t][1], f);
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    float acs_i[2], ri[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int k = min(max(0, itile[t]), NI - 1) * 32;  // clamped for idle slots
-        acs_i[t] = acs_s[k + il];
-        ri[t] = ssd_exp(acs_i[t] - acs_s[k]);
-        const float ek = ssd_exp(acs_s[k]);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const u32x4 ah = tr_operand<true>(xh[buf], LDX, 16 * u, 32 * pt);
+                const u32x4 al = tr_operand<true>(xl[buf], LDX, 16 * u, 32 * pt);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (mask >> t & 1) {
+                        Z[t][pt] = mfma32(ah, cbt[t][2 * u], Z[t][pt]);
+                        Z[t][pt] = mfma32(al, cbt[t][2 * u], Z[t][pt]);
+                        Z[t][pt] = mfma32(ah, cbt[t][2 * u + 1], Z[t][pt]);
+                    }
+            }
+    };
+    // diagonal visit of tile t (row tile ti == jt)
+    auto diag = [&](int t, int ti, int buf, const u32x4 (&cbd)[4]) {
+        const float ai = acs_s[ti * kJT + il];
+        const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * kJT - 1] : 0.f));
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) yacc[t][pt][r] *= ek;
-    }
-    __syncthreads();  // cf complete; H no longer read (its LDS becomes y staging)
-
-    bf16 *ys = reinterpret_cast<bf16 *>(hy) + wave * 32 * LDY;
-    bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
-    const float Dh = D ? D[h] : 0.f;
-
-    // y tile t (D x already added) as bf16 via LDS, written as full rows
-    auto epilogue = [&](int t, int jt) {
+            for (int rg = 0; rg < 4; ++rg) {
+                const int p0 = pt * 32 + 8 * rg + 4 * g2;
+                const u32x2 xr = *reinterpret_cast<const u32x2 *>(&xs[buf][il * LDX + p0]);
+                const int r0 = 4 * rg;
+                Z[t][pt][r0 + 0] = Z[t][pt][r0 + 0] * rf + Dh * lo_bf16(xr[0]);
+                Z[t][pt][r0 + 1] = Z[t][pt][r0 + 1] * rf + Dh * hi_bf16(xr[0]);
+                Z[t][pt][r0 + 2] = Z[t][pt][r0 + 2] * rf + Dh * lo_bf16(xr[1]);
+                Z[t][pt][r0 + 3] = Z[t][pt][r0 + 3] * rf + Dh * hi_bf16(xr[1]);
+            }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float m[8];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                // registers 8u+4v..+3 hold rows jl..jl+3 of the tile
+                const int jl = 16 * u + 8 * v + 4 * g2;
+                const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[ti * kJT + jl]);
+                const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[ti * kJT + jl]);
+                const u32x4 cv = cbd[2 * u + v];
+                // computed for every element (the exponent clamped to <= 0 so
+                // masked ones stay finite), then selected: no divergent branch
+                const float e0 = __uint_as_float(cv[0]) * ssd_exp(fminf(ai - aj.x, 0.f)) * dj.x;
+                const float e1 = __uint_as_float(cv[1]) * ssd_exp(fminf(ai - aj.y, 0.f)) * dj.y;
+                const float e2 = __uint_as_float(cv[2]) * ssd_exp(fminf(ai - aj.z, 0.f)) * dj.z;
+                const float e3 = __uint_as_float(cv[3]) * ssd_exp(fminf(ai - aj.w, 0.f)) * dj.w;
+                m[4 * v + 0] = jl + 0 <= il ? e0 : 0.f;
+                m[4 * v + 1] = jl + 1 <= il ? e1 : 0.f;
+                m[4 * v + 2] = jl + 2 <= il ? e2 : 0.f;
+                m[4 * v + 3] = jl + 3 <= il ? e3 : 0.f;
+            }
+            u32x4 mh, ml;
+            split8(m, mh, ml);
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const u32x4 xa = tr_operand<true>(xs[buf], LDX, 16 * u, 32 * pt);
+                Z[t][pt] = mfma32(xa, mh, Z[t][pt]);
+                Z[t][pt] = mfma32(xa, ml, Z[t][pt]);
+            }
+        }
+    };
+    // y rows of tile t (already complete) as bf16 via LDS, written as full rows
+    auto epilogue = [&](int t, int ti) {
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int p0 = pt * 32 + 8 * rg + 4 * g2;
                 u32x2 o;
-                o[0] = pack_bf16x2(yacc[t][pt][4 * rg + 0], yacc[t][pt][4 * rg + 1]);
-                o[1] = pack_bf16x2(yacc[t][pt][4 * rg + 2], yacc[t][pt][4 * rg + 3]);
+                o[0] = pack_bf16x2(Z[t][pt][4 * rg + 0], Z[t][pt][4 * rg + 1]);
+                o[1] = pack_bf16x2(Z[t][pt][4 * rg + 2], Z[t][pt][4 * rg + 3]);
                 *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
             }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
+        const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
             const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
-            const int row = jt * 32 + r;  // formed in the loop: no hoisted 64-bit addresses
-            if (row < q) *reinterpret_cast<u32x4 *>(ybase + ((unsigned)row * xrs + 8u * sg)) = o;
+            buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (ti * 32 + 8 * kk) * xrs * 2u), yvoff);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
     };
 
     auto jstep = [&](int jt, auto par) {
-        constexpr int buf = decltype(par)::value;  // jt % 2, the LDS buffer
+        constexpr int buf = decltype(par)::value;  // jt % 2: LDS buffer and C.B register set
         if (jt + 2 < NI) load_stage(jt + 2, R[buf]);
-        bool act[2], diag[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            act[t] = t < ntiles && itile[t] >= jt;
-            diag[t] = act[t] && itile[t] == jt;
+        if (jt + 1 <= ti0) load_cb(ti0, jt + 1, cbr[buf ^ 1][0]);
+        if (jt + 1 <= ti1) load_cb(ti1, jt + 1, cbr[buf ^ 1][1]);
+        // wave-uniform cases (ti0 < ti1)
+        if (jt < ti0) {
+            offdiag(jt, buf, 3, cbr[buf]);
+        } else if (jt == ti0) {
+            offdiag(jt, buf, 2, cbr[buf]);
+            diag(0, ti0, buf, cbr[buf][0]);
+        } else if (jt < ti1) {
+            offdiag(jt, buf, 2, cbr[buf]);
+        } else if (jt == ti1) {
+            diag(1, ti1, buf, cbr[buf][1]);
         }
-        if (act[0] || act[1]) {
-            f32x16 sacc[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a =
-                    *reinterpret_cast<const u32x4 *>(&bst[buf][il * LDB + 16 * ks + 8 * g2]);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    if (act[t]) sacc[t] = mfma32(a, creg[t][ks], sacc[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                if (diag[t]) {
-                    // rescale the state term to exp(Acs_i) and add D x (x rows
-                    // of this tile are the current stage)
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-                        for (int rg = 0; rg < 4; ++rg) {
-                            const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                            const u32x2 xr =
-                                *reinterpret_cast<const u32x2 *>(&xst[buf][il * LDX + p0]);
-                            const int r0 = 4 * rg;
-                            yacc[t][pt][r0 + 0] = yacc[t][pt][r0 + 0] * ri[t] + Dh * lo_bf16(xr[0]);
-                            yacc[t][pt][r0 + 1] = yacc[t][pt][r0 + 1] * ri[t] + Dh * hi_bf16(xr[0]);
-                            yacc[t][pt][r0 + 2] = yacc[t][pt][r0 + 2] * ri[t] + Dh * lo_bf16(xr[1]);
-                            yacc[t][pt][r0 + 3] = yacc[t][pt][r0 + 3] * ri[t] + Dh * hi_bf16(xr[1]);
-                        }
-                }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                // this lane's rows j of S^T in half u: j = jt*32 + 16u + 8(e/4) + 4 g2 + e%4
-                u32x4 bop[2], bopl[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    if (!act[t]) continue;
-                    float m[8];
-#pragma unroll
-                    for (int v = 0; v < 2; ++v) {
-                        const int jl = 16 * u + 8 * v + 4 * g2;
-                        float4 fv;
-                        if (!diag[t]) {
-                            fv = *reinterpret_cast<const float4 *>(&cf[itile[t]][jt * 32 + jl]);
-                        } else {
-                            const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[jt * 32 + jl]);
-                            const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[jt * 32 + jl]);
-                            fv.x = jl + 0 <= il ? ssd_exp(acs_i[t] - aj.x) * dj.x : 0.f;
-                            fv.y = jl + 1 <= il ? ssd_exp(acs_i[t] - aj.y) * dj.y : 0.f;
-                            fv.z = jl + 2 <= il ? ssd_exp(acs_i[t] - aj.z) * dj.z : 0.f;
-                            fv.w = jl + 3 <= il ? ssd_exp(acs_i[t] - aj.w) * dj.w : 0.f;
-                        }
-                        m[4 * v + 0] = sacc[t][8 * u + 4 * v + 0] * fv.x;
-                        m[4 * v + 1] = sacc[t][8 * u + 4 * v + 1] * fv.y;
-                        m[4 * v + 2] = sacc[t][8 * u + 4 * v + 2] * fv.z;
-                        m[4 * v + 3] = sacc[t][8 * u + 4 * v + 3] * fv.w;
-                    }
-                    split8(m, bop[t], bopl[t]);
-                }
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const u32x4 xa = tr_operand<true>(xst[buf], LDX, 16 * u, 32 * pt);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t)
-                        if (act[t]) {
-                            yacc[t][pt] = mfma32(xa, bop[t], yacc[t][pt]);
-                            yacc[t][pt] = mfma32(xa, bopl[t], yacc[t][pt]);
-                        }
-                }
-            }
-        }
-        // finished tiles are written one step later, off the diagonal step
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-            if (t < ntiles && itile[t] == jt - 1) epilogue(t, jt - 1);
+        if (jt == ti0 + 1) epilogue(0, ti0);
+        if (jt == ti1 + 1) epilogue(1, ti1);
         if (jt + 1 < NI) store_stage(jt + 1, buf ^ 1, R[buf ^ 1]);
         __syncthreads();
     };
+#pragma unroll 1
     for (int jt = 0; jt < NI; jt += 2) {  // NI is even
         jstep(jt, P0{});
         jstep(jt + 1, P1{});
     }
-    // the last tile (NI-1) finished in the final step
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-        if (t < ntiles && itile[t] == NI - 1) epilogue(t, NI - 1);
+    if (ti1 == NI - 1) epilogue(1, ti1);
 }
 
 template <int Q, int N>
@@ -569,12 +665,19 @@ void launch_state_t(const ScanShape &s, const void *x, const void *Bm, const flo
 }
 
 template <int Q, int N>
-void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const void *Bm,
-                   const void *Cm, const float *D, const float *Acs, const float *states, void *y,
+void launch_cb_t(const ScanShape &s, const void *Bm, const void *Cm, void *cb, hipStream_t st) {
+    const int64_t nb = s.B * s.T * s.G * (Q / 32);
+    k_chunk_cb_mfma<Q, N><<<(unsigned)nb, 256, 0, st>>>((const bf16 *)Bm, (const bf16 *)Cm,
+                                                        (u32x4 *)cb, s.L, (int)s.G, (int)s.T, nb);
+}
+
+template <int Q, int N>
+void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const void *Cm,
+                   const float *D, const float *Acs, const float *states, const void *cb, void *y,
                    hipStream_t st) {
     const int64_t nb = s.B * s.T * s.H;
-    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), 256, 0, st>>>(
-        (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y, s.L,
+    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), Q, 0, st>>>(
+        (const bf16 *)x, dt, (const bf16 *)Cm, D, Acs, states, (const u32x4 *)cb, (bf16 *)y, s.L,
         (int)s.H, (int)s.G, (int)s.T, nb);
 }
 
@@ -603,10 +706,20 @@ void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
     SSD_DISPATCH_QN(launch_state_t, s, x, Bm, dt, Acs, states, st);
 }
 
-void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt,
-                            const void *Bm, const void *Cm, const float *D, const float *Acs,
-                            const float *states, void *y, hipStream_t st) {
-    SSD_DISPATCH_QN(launch_scan_t, s, x, dt, Bm, Cm, D, Acs, states, y, st);
+size_t chunk_cb_bytes(const ScanShape &s) {
+    const int64_t ni = s.Q / 32;
+    return (size_t)(s.B * s.T * s.G * (ni * (ni + 1) / 2)) * 4096;
+}
+
+void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
+                          hipStream_t st) {
+    SSD_DISPATCH_QN(launch_cb_t, s, Bm, Cm, cb, st);
+}
+
+void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
+                            const float *D, const float *Acs, const float *states, const void *cb,
+                            void *y, hipStream_t st) {
+    SSD_DISPATCH_QN(launch_scan_t, s, x, dt, Cm, D, Acs, states, cb, y, st);
 }
 
 }  // namespace ssd

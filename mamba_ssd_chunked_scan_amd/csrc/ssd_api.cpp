@@ -73,9 +73,14 @@ size_t states_bytes(const ScanShape &s) {
     return round_up((size_t)(s.B * s.T * s.H) * (size_t)(s.P * s.N) * 4);
 }
 
+size_t scan_ws_bytes(const ScanShape &s) {
+    if (s.B == 0 || s.L == 0) return 0;
+    return round_up(ssd::chunk_scan_ws_bytes(s));
+}
+
 size_t workspace_bytes(const ScanShape &s) {
     if (s.B == 0 || s.L == 0) return 0;
-    return acs_bytes(s) + states_bytes(s);
+    return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s);
 }
 
 ssd_status after_launch() {
@@ -96,13 +101,13 @@ const char *ssd_status_string(int status) {
     case SSD_ERR_UNSUPPORTED:
         return "unsupported argument (chunk, headdim, dstate, dtype or reserved field)";
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case SSD_ERR_WORKSPACE: return "workspace is smaller than ssd_scan_workspace_size";
+    case SSD_ERR_WORKSPACE: return "workspace is smaller than the size its query function reports";
     case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
     default: return "unknown status";
     }
 }
 
-int ssd_abi_version(void) { return 1; }
+int ssd_abi_version(void) { return 2; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -136,11 +141,12 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, 
     if (!workspace) return SSD_ERR_NULL_PTR;
     float *Acs = static_cast<float *>(workspace);
     float *states = reinterpret_cast<float *>(static_cast<char *>(workspace) + acs_bytes(s));
+    void *scan_ws = static_cast<char *>(workspace) + acs_bytes(s) + states_bytes(s);
     hipStream_t hs = as_stream(stream);
     ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
     ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
     ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
-    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, y, hs);
+    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, scan_ws, y, hs);
     return after_launch();
 }
 
@@ -204,16 +210,29 @@ ssd_status ssd_state_passing(const ssd_scan_desc *d, float *states, const float 
     return after_launch();
 }
 
+ssd_status ssd_chunk_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
+    if (!bytes) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    *bytes = scan_ws_bytes(s);
+    return SSD_OK;
+}
+
 ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
                           const void *B, const void *C, const float *D, const float *Acs,
-                          const float *states, void *y, void *stream) {
+                          const float *states, void *y, void *workspace, size_t ws_bytes,
+                          void *stream) {
     ScanShape s;
     ssd_status st = check_scan(d, &s);
     if (st != SSD_OK) return st;
     if (s.B == 0 || s.L == 0) return SSD_OK;
-    st = check_ptrs({x, dt, B, C, Acs, states, y}, {D});
+    st = check_ptrs({x, dt, B, C, Acs, states, y}, {D, workspace});
     if (st != SSD_OK) return st;
-    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, y, as_stream(stream));
+    const size_t need = scan_ws_bytes(s);
+    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    if (need && !workspace) return SSD_ERR_NULL_PTR;
+    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, workspace, y, as_stream(stream));
     return after_launch();
 }
 

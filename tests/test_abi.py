@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 1
+    assert L.ssd_abi_version() == 2
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -62,16 +62,49 @@ def wsize(L, d):
     return st, n.value
 
 
+def cb_size(L, d):
+    n = ctypes.c_size_t(12345)
+    st = L.ssd_chunk_scan_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+def test_chunk_scan_workspace_size(L):
+    # bf16, headdim 64, dstate 64/128, chunk 64/128/256: the MFMA kernels keep
+    # one 4 KB C.B tile per causal 32x32 tile pair of every (batch, chunk, group)
+    for chunk, ni in ((256, 8), (128, 4), (64, 2)):
+        for dstate in (64, 128):
+            st, n = cb_size(L, desc(chunk=chunk, dstate=dstate))
+            T = -(-512 // chunk)
+            assert st == OK and n == r256(1 * T * 2 * (ni * (ni + 1) // 2) * 4096)
+    # ragged last chunk counts as a chunk
+    assert cb_size(L, desc(seqlen=300, chunk=128)) == (OK, 3 * 2 * 10 * 4096)
+    # shapes the generic kernels run need none
+    assert cb_size(L, desc(dtype=0)) == (OK, 0)
+    assert cb_size(L, desc(headdim=32)) == (OK, 0)
+    assert cb_size(L, desc(chunk=32)) == (OK, 0)
+    assert cb_size(L, desc(dstate=256)) == (OK, 0)
+    assert cb_size(L, desc(seqlen=0)) == (OK, 0)
+    assert cb_size(L, desc(batch=0)) == (OK, 0)
+    assert L.ssd_chunk_scan_workspace_size(ctypes.byref(desc()), None) == NULL
+    assert cb_size(L, desc(chunk=48))[0] == UNSUP
+
+
 def test_workspace_size(L):
     st, n = wsize(L, desc())
     T = 2
     acs = 1 * 8 * 512 * 4
     states = 1 * T * 8 * 64 * 128 * 4
-    r = lambda v: (v + 255) // 256 * 256
-    assert st == OK and n == r(acs) + r(states)
+    assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc())[1]
     # ragged last chunk counts as a chunk
     st, n = wsize(L, desc(seqlen=300, chunk=128))
-    assert st == OK and n == r(8 * 300 * 4) + r(3 * 8 * 64 * 128 * 4)
+    assert st == OK and n == (r256(8 * 300 * 4) + r256(3 * 8 * 64 * 128 * 4)
+                              + cb_size(L, desc(seqlen=300, chunk=128))[1])
+    st, n = wsize(L, desc(dtype=0))
+    assert st == OK and n == r256(acs) + r256(states)
     assert wsize(L, desc(seqlen=0)) == (OK, 0)
     assert wsize(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_scan_workspace_size(ctypes.byref(desc()), None) == NULL
@@ -95,8 +128,8 @@ def test_scan_shape_errors(L, kw, status):
     assert L.ssd_chunk_cumsum(ctypes.byref(d), P16, P16, P16, None) == status
     assert L.ssd_chunk_state(ctypes.byref(d), P16, P16, P16, P16, P16, None) == status
     assert L.ssd_state_passing(ctypes.byref(d), P16, P16, P16, P16, None) == status
-    assert L.ssd_chunk_scan(ctypes.byref(d), P16, P16, P16, P16, P16, P16, P16, P16,
-                            None) == status
+    assert L.ssd_chunk_scan(ctypes.byref(d), P16, P16, P16, P16, P16, P16, P16, P16, P16,
+                            ws, None) == status
 
 
 def test_null_desc(L):
@@ -129,6 +162,20 @@ def test_scan_workspace_too_small(L):
     assert st == WS
     ptrs = [P16] * 9 + [None]
     assert L.ssd_scan_fwd(ctypes.byref(d), *ptrs, need, None) == NULL
+
+
+def test_chunk_scan_workspace_errors(L):
+    d = desc()
+    _, need = cb_size(L, d)
+    assert need > 0
+    args = [P16] * 8   # x dt B C D Acs states y
+    assert L.ssd_chunk_scan(ctypes.byref(d), *args, P16, need - 1, None) == WS
+    assert L.ssd_chunk_scan(ctypes.byref(d), *args, None, need, None) == NULL
+    assert L.ssd_chunk_scan(ctypes.byref(d), *args, P_MIS, need, None) == ALIGN
+    for which in (0, 1, 2, 3, 5, 6, 7):
+        a = list(args)
+        a[which] = None
+        assert L.ssd_chunk_scan(ctypes.byref(d), *a, P16, need, None) == NULL
 
 
 def test_empty_batch_is_noop(L):
