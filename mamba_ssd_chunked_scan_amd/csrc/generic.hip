@@ -10,6 +10,7 @@
 // pass of states across chunks, and the chunk output from its diagonal block
 // plus the entering state.
 #include "common.hpp"
+#include "stages.hpp"
 #include "launch.hpp"
 #include "ssd.h"
 
@@ -105,46 +106,13 @@ k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
 }
 
 // -------------------------------------------------------- state passing
-// Per (b, h) and 4 consecutive state elements per thread, sequential over
-// chunks: states[c] <- H_c, H_{c+1} = exp(dA_c) H_c + S_c.  Loads run four
-// chunks ahead of the dependent update so that several are in flight.
+// One thread per 4 consecutive state elements of one (b, h).
 __global__ void __launch_bounds__(256)
 k_state_passing(float *__restrict__ states, const float *__restrict__ Acs,
                 const float *init, float *fin, int64_t L, int H, int64_t PN, int Q, int T) {
-    const int64_t bh = blockIdx.x;
-    const int64_t b = bh / H;
-    const int h = (int)(bh % H);
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
-    float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (init) hv = *reinterpret_cast<const float4 *>(init + bh * PN + e);
-    const float *acs = Acs + bh * L;
-    const int64_t cstride = (int64_t)H * PN;
-    float *base = states + (b * T * H + h) * PN + e;
-    for (int c0 = 0; c0 < T; c0 += 4) {
-        float4 s[4];
-        float r[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int c = c0 + k;
-            if (c < T) {
-                s[k] = *reinterpret_cast<const float4 *>(base + c * cstride);
-                r[k] = ssd_exp(acs[min(L, (int64_t)(c + 1) * Q) - 1]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int c = c0 + k;
-            if (c < T) {
-                *reinterpret_cast<float4 *>(base + c * cstride) = hv;
-                hv.x = r[k] * hv.x + s[k].x;
-                hv.y = r[k] * hv.y + s[k].y;
-                hv.z = r[k] * hv.z + s[k].z;
-                hv.w = r[k] * hv.w + s[k].w;
-            }
-        }
-    }
-    if (fin) *reinterpret_cast<float4 *>(fin + bh * PN + e) = hv;
+    state_passing_body(states, Acs, init, fin, blockIdx.x, e, L, H, PN, Q, T);
 }
 
 // ----------------------------------------------------------- chunk scan

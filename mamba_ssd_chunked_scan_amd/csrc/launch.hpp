@@ -46,6 +46,12 @@ void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
 size_t chunk_cb_bytes(const ScanShape &s);
 void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
                           hipStream_t st);
+// ssd_scan_fwd on the MFMA path: three launches (the cumsum inside the
+// chunk-state kernel, the C.B tiles inside the state-passing launch).
+void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
+                            const void *Bm, const void *Cm, const float *D, const float *init,
+                            void *y, float *fin, float *Acs, float *states, void *cb,
+                            hipStream_t st);
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
                             const float *D, const float *Acs, const float *states, const void *cb,
                             void *y, hipStream_t st);

@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "stages.hpp"
 #include "ssd.h"
 
 namespace ssd {
@@ -128,7 +129,10 @@ __device__ __forceinline__ rsrc_t buffer_rsrc(const void *base, uint32_t bytes) 
 // offset stays a small register.
 __device__ __forceinline__ rsrc_t buffer_rsrc_at(const void *base, uint32_t bytes, uint32_t off) {
     off = __builtin_amdgcn_readfirstlane(off);
-    return buffer_rsrc(static_cast<const char *>(base) + off, bytes > off ? bytes - off : 0u);
+    // every field in scalar registers: a resource in vector registers would
+    // need a loop over lanes at each access
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes > off ? bytes - off : 0u);
+    return buffer_rsrc(static_cast<const char *>(base) + off, n);
 }
 __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
@@ -156,11 +160,16 @@ using P1 = std::integral_constant<int, 1>;
 // fp32 and stored as a hi/lo bf16 pair, so its rounding stays near fp32
 // level.  Both operands are read with the LDS transpose read.  Output tiles
 // 32x32: wave w owns tiles w and w+4 of the (p-tile, n-tile) grid.
-template <int Q, int N>
+//
+// kCumsum: the block also forms its chunk's cumulative log-decay (an in-block
+// prefix sum of dt*A over the chunk's tokens) and writes it to Acs for the
+// later stages, instead of reading it.
+template <int Q, int N, bool kCumsum>
 __global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
-                   const float *__restrict__ dt, const float *__restrict__ Acs,
-                   float *__restrict__ states, int64_t L, int H, int G, int T, int64_t nblocks) {
+                   const float *__restrict__ dt, const float *__restrict__ A,
+                   float *__restrict__ Acs, float *__restrict__ states, int64_t L, int H, int G,
+                   int T, int64_t nblocks) {
     constexpr int LDX = kP + 16;              // x stage row stride (bf16)
     constexpr int LDB = N + 16;               // B stage row stride (bf16)
     constexpr int NST = Q / kJT;              // stages per chunk
@@ -189,14 +198,27 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     const unsigned xrs = H * kP, brs = G * N;
     const int xrow = tid >> 3, xseg = tid & 7;
 
-    // weights first: every stage needs them
-    {
+    // weights first: every stage needs them (Q <= 256: one token per thread)
+    if constexpr (kCumsum) {
+        __shared__ float wsum[4];
+        __shared__ float last_s;
+        const float d = tid < q ? dt[(b * L + t0 + tid) * H + h] : 0.f;
+        const float v = wave_inclusive_scan(d * A[h], lane);
+        if (lane == 63) wsum[wave] = v;
+        __syncthreads();
+        float acs = v;
+        for (int k = 0; k < wave; ++k) acs += wsum[k];
+        if (tid < q) Acs[(b * H + h) * L + t0 + tid] = acs;
+        if (tid == q - 1) last_s = acs;
+        __syncthreads();
+        if (tid < Q) w[tid] = tid < q ? d * ssd_exp(last_s - acs) : 0.f;
+    } else {
         const float *acs = Acs + (b * H + h) * L + t0;
         const float last = acs[q - 1];
-        for (int j = tid; j < Q; j += 256) {
-            const int jj = min(j, q - 1);
+        if (tid < Q) {
+            const int jj = min(tid, q - 1);
             const float v = dt[(b * L + t0 + jj) * H + h] * ssd_exp(last - acs[jj]);
-            w[j] = j < q ? v : 0.f;
+            w[tid] = tid < q ? v : 0.f;
         }
     }
     StageRegs<NBV> R[2];
@@ -279,28 +301,28 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
 // ------------------------------------------------------------- C.B tiles
 // CB[i][j] = C_i . B_j for the causal 32x32 tiles (row tile ti >= column tile
 // jt) of one (b, c, g).  The product does not involve the head, so it is formed
-// once here and read by every head of group g.  One block per (b, c, g, ti);
-// wave w forms tiles jt = w, w+4, ... as S^T = B_jt C_ti^T (rows j, columns i).
-// Each tile is 4 KB, stored in the register layout of that 32x32 accumulator
-// (lane l: column i = l%32; register r: row j = 8(r/4) + 4(l/32) + r%4) so the
-// chunk scan reads it as an MFMA operand with one 16-byte load per lane and
-// 16-byte unit k*64 + lane:
+// once here and read by every head of group g.  One wave per tile: the tile is
+// S^T = B_jt C_ti^T (rows j, columns i), stored as 4 KB in the register layout
+// of that 32x32 accumulator (lane l: column i = l%32; register r: row
+// j = 8(r/4) + 4(l/32) + r%4) so the chunk scan reads it as an MFMA operand
+// with one 16-byte load per lane, 16-byte unit k*64 + lane:
 //   off-diagonal tile: k = 2u   -> bf16 hi part of registers 8u..8u+7,
 //                      k = 2u+1 -> bf16 residual lo of the same registers;
 //   diagonal tile:     k = v    -> fp32 registers 4v..4v+3 (the scan applies
 //                                  the per-head decay and the mask first).
 // Tiles of (b, c, g) are consecutive, tile (ti, jt) at ti(ti+1)/2 + jt.
+// Tile w (flat over (b, c, g) and the NT causal tiles) by one wave.
 template <int Q, int N>
-__global__ void __launch_bounds__(256)
-k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 *__restrict__ cb,
-                int64_t L, int G, int T, int64_t nblocks) {
+__device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+                                        u32x4 *__restrict__ cb, int64_t L, int G, int T,
+                                        int64_t w) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
-    const int64_t lb = blockIdx.x;
-    if (lb >= nblocks) return;
     const int lane = threadIdx.x & 63, il = lane & 31, g2 = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ti = (int)(lb % NI);
-    const int64_t bcg = lb / NI;
+    const int tile = (int)(w % NT);
+    const int64_t bcg = w / NT;
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= tile) ++ti;
+    const int jt = tile - ti * (ti + 1) / 2;
     const int g = (int)(bcg % G);
     const int64_t bc = bcg / G;
     const int c = (int)(bc % T);
@@ -312,38 +334,66 @@ k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 
     const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
     // rows past the end of a short chunk are clamped to its last row: finite
     // values that the scan multiplies by zero (x and dt are zero there)
-    u32x4 crow[KS];
-    {
-        const unsigned off = (unsigned)min(32 * ti + il, q - 1) * rs + 8u * g2;
+    const unsigned co = (unsigned)min(32 * ti + il, q - 1) * rs + 8u * g2;
+    const unsigned bo = (unsigned)min(32 * jt + il, q - 1) * rs + 8u * g2;
+    u32x4 crow[KS], brow[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) crow[s] = *reinterpret_cast<const u32x4 *>(cbase + (off + 16u * s));
+    for (int s = 0; s < KS; ++s) {
+        crow[s] = *reinterpret_cast<const u32x4 *>(cbase + (co + 16u * s));
+        brow[s] = *reinterpret_cast<const u32x4 *>(bbase + (bo + 16u * s));
     }
-    u32x4 *out = cb + (bcg * NT + ti * (ti + 1) / 2) * 256;
-    for (int jt = wave; jt <= ti; jt += 4) {
-        const unsigned off = (unsigned)min(32 * jt + il, q - 1) * rs + 8u * g2;
-        f32x16 acc = zero16();
+    f32x16 acc = zero16();
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            acc = mfma32(*reinterpret_cast<const u32x4 *>(bbase + (off + 16u * s)), crow[s], acc);
-        u32x4 *o = out + jt * 256;
-        if (jt < ti) {
+    for (int s = 0; s < KS; ++s) acc = mfma32(brow[s], crow[s], acc);
+    u32x4 *o = cb + (bcg * NT + tile) * 256;
+    if (jt < ti) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float m[8];
+        for (int u = 0; u < 2; ++u) {
+            float m[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) m[e] = acc[8 * u + e];
-                u32x4 hi, lo;
-                split8(m, hi, lo);
-                o[(2 * u) * 64 + lane] = hi;
-                o[(2 * u + 1) * 64 + lane] = lo;
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
-                                         __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+            for (int e = 0; e < 8; ++e) m[e] = acc[8 * u + e];
+            u32x4 hi, lo;
+            split8(m, hi, lo);
+            o[(2 * u) * 64 + lane] = hi;
+            o[(2 * u + 1) * 64 + lane] = lo;
         }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
+                                     __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
     }
+}
+
+template <int Q, int N>
+__global__ void __launch_bounds__(256)
+k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 *__restrict__ cb,
+                int64_t L, int G, int T, int64_t ntiles) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= ntiles) return;
+    cb_tile<Q, N>(Bm, Cm, cb, L, G, T, w);
+}
+
+// The inter-chunk state pass and the C.B tiles in one launch: the first
+// nsp blocks pass states (memory-bound), the rest form C.B tiles on the
+// otherwise idle matrix cores.  Both only read what the chunk-state stage
+// and the inputs provide, and both feed the chunk-output stage.
+template <int Q, int N>
+__global__ void __launch_bounds__(256)
+k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, const float *init,
+                   float *fin, int64_t L, int H, int64_t PN, int T, int64_t nsp, int ny,
+                   const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+                   u32x4 *__restrict__ cb, int G, int64_t ntiles) {
+    const int64_t blk = blockIdx.x;
+    if (blk < nsp) {
+        const int64_t e = ((blk % ny) * 256 + threadIdx.x) * 4;
+        if (e >= PN) return;
+        state_passing_body(states, Acs, init, fin, blk / ny, e, L, H, PN, Q, T);
+        return;
+    }
+    const int64_t w = (blk - nsp) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w >= ntiles) return;
+    cb_tile<Q, N>(Bm, Cm, cb, L, G, T, w);
 }
 
 // ------------------------------------------------------------- chunk scan
@@ -378,17 +428,13 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                   int T, int64_t nblocks) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     constexpr int TH = Q;                 // threads: NI/2 waves
-    constexpr int NW = TH / 64;
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
     constexpr int LDX = kP + 16;          // stage rows, read transposed
-    constexpr int LDY = kP + 8;           // bf16 y staging rows
     constexpr int H_BYTES = 2 * kP * LDH * 2;
-    constexpr int Y_BYTES = NW * 32 * LDY * 2;
-    constexpr int HY_BYTES = H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES;
     constexpr int XV = 256 / TH;          // 16-byte x segments per thread per stage
     constexpr int NHV = kP * N / 4 / TH;  // float4 of H per thread
     constexpr int HB = NHV < 8 ? NHV : 8; // H float4 held in registers at a time
-    __shared__ __attribute__((aligned(16))) char hy[HY_BYTES];
+    __shared__ __attribute__((aligned(16))) char hy[H_BYTES];
     __shared__ __attribute__((aligned(16))) bf16 xs[2][kJT * LDX];
     __shared__ __attribute__((aligned(16))) bf16 xh[2][kJT * LDX];
     __shared__ __attribute__((aligned(16))) bf16 xl[2][kJT * LDX];
@@ -448,48 +494,73 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             *reinterpret_cast<u32x4 *>(&xl[buf][row * LDX + seg * 8]) = lo;
         }
     };
-    // the 4 KB C.B tile (ti, jt) as four 16-byte operands of this lane
+    // the 4 KB C.B tile (ti, jt) as four 16-byte operands of this lane; a
+    // tile outside the causal range (jt > ti) gets an empty range: the loads
+    // still issue, so every path has the same loads in flight, but read zeros
+    // and touch no memory
+    const uint32_t cbvoff = lane * 16u;
     auto load_cb = [&](int ti, int jt, u32x4 (&o)[4]) {
-        const u32x4 *p = cbg + (ti * (ti + 1) / 2 + jt) * 256 + lane;
+        const int tile = ti * (ti + 1) / 2 + min(jt, ti);
+        const rsrc_t r = buffer_rsrc_at(cbg, jt <= ti ? (tile + 1) * 4096u : 0u, tile * 4096u);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = p[k * 64];
+        for (int k = 0; k < 4; ++k) o[k] = buffer_load16(r, cbvoff + k * 1024u);
     };
 
-    // ---- prologue: global loads first
-    load_stage(0, R[0]);
-    if (NI > 1) load_stage(1, R[1]);
-    u32x4 cbr[2][2][4];  // [step parity][tile][operand]
-    load_cb(ti0, 0, cbr[0][0]);
-    load_cb(ti1, 0, cbr[0][1]);
+    // ---- prologue: global loads in the order they are needed: acs/dt and H
+    // (before the first barrier), C rows (state term), stages 0-1, C.B tiles
+    float acs_v, dt_v;
     {
         const float *acs = Acs + (b * H + h) * L + t0;
         const int jj = min(tid, q - 1);
-        const float a = acs[jj], d = dt[(b * L + t0 + jj) * H + h];
-        acs_s[tid] = tid < q ? a : acs[q - 1];
-        dt_s[tid] = tid < q ? d : 0.f;
+        acs_v = acs[jj];
+        dt_v = dt[(b * L + t0 + jj) * H + h];
+        if (tid >= q) {
+            acs_v = acs[q - 1];
+            dt_v = 0.f;
+        }
     }
+    const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
+    float4 hv[HB];
+#pragma unroll
+    for (int i = 0; i < HB; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * i));
+    u32x4 c0[KS], c1[KS];
+    {
+        const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
+        const unsigned o0 = (unsigned)min(32 * ti0 + il, q - 1) * crs + 8u * g2;
+        const unsigned o1 = (unsigned)min(32 * ti1 + il, q - 1) * crs + 8u * g2;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            c0[s] = *reinterpret_cast<const u32x4 *>(cbase + (o0 + 16u * s));
+            c1[s] = *reinterpret_cast<const u32x4 *>(cbase + (o1 + 16u * s));
+        }
+    }
+    load_stage(0, R[0]);
+    load_stage(1, R[1]);
+    u32x4 cbr[2][2][4];  // [step parity][tile][operand]
+    load_cb(ti0, 0, cbr[0][0]);
+    load_cb(ti1, 0, cbr[0][1]);
+    acs_s[tid] = acs_v;
+    dt_s[tid] = dt_v;
     bf16 *Hh = reinterpret_cast<bf16 *>(hy);
     bf16 *Hl = Hh + kP * LDH;
-    {
-        const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
 #pragma unroll
-        for (int i0 = 0; i0 < NHV; i0 += HB) {
-            float4 hv[HB];
+    for (int i0 = 0; i0 < NHV; i0 += HB) {
+        if (i0 > 0) {
 #pragma unroll
             for (int i = 0; i < HB; ++i)
                 hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * (i0 + i)));
+        }
 #pragma unroll
-            for (int i = 0; i < HB; ++i) {
-                const int e = tid + TH * (i0 + i), p = e / (N / 4), n = (e % (N / 4)) * 4;
-                u32x2 hh, hl;
-                uint32_t l0, l1;
-                hh[0] = split2(hv[i].x, hv[i].y, l0);
-                hh[1] = split2(hv[i].z, hv[i].w, l1);
-                hl[0] = l0;
-                hl[1] = l1;
-                *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
-                *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
-            }
+        for (int i = 0; i < HB; ++i) {
+            const int e = tid + TH * (i0 + i), p = e / (N / 4), n = (e % (N / 4)) * 4;
+            u32x2 hh, hl;
+            uint32_t l0, l1;
+            hh[0] = split2(hv[i].x, hv[i].y, l0);
+            hh[1] = split2(hv[i].z, hv[i].w, l1);
+            hl[0] = l0;
+            hl[1] = l1;
+            *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
+            *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
         }
     }
     __syncthreads();  // acs_s, dt_s, H
@@ -497,15 +568,6 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     // state term Z = H C_i^T for both tiles (C rows straight from global)
     f32x16 Z[2][2];
     {
-        const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
-        const unsigned o0 = (unsigned)min(32 * ti0 + il, q - 1) * crs + 8u * g2;
-        const unsigned o1 = (unsigned)min(32 * ti1 + il, q - 1) * crs + 8u * g2;
-        u32x4 c0[KS], c1[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            c0[s] = *reinterpret_cast<const u32x4 *>(cbase + (o0 + 16u * s));
-            c1[s] = *reinterpret_cast<const u32x4 *>(cbase + (o1 + 16u * s));
-        }
         Z[0][0] = Z[0][1] = Z[1][0] = Z[1][1] = zero16();
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -521,9 +583,8 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             }
         }
     }
-    __syncthreads();  // stage 0 visible; H no longer read (its LDS becomes y staging)
+    __syncthreads();  // stage 0 visible
 
-    bf16 *ys = reinterpret_cast<bf16 *>(hy) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
     const float Dh = D ? D[h] : 0.f;
 
@@ -602,36 +663,30 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             }
         }
     };
-    // y rows of tile t (already complete) as bf16 via LDS, written as full rows
+    // y rows of tile t (complete): each lane holds 4 consecutive p of row
+    // i = 32 ti + l%32 per register group, written as 8 bytes; the lane pair
+    // (l, l+32) covers 16 contiguous bytes and the 8 stores cover whole rows
+    const uint32_t yvoff = ((unsigned)il * xrs + 4u * g2) * 2u;
     auto epilogue = [&](int t, int ti) {
+        const rsrc_t r = buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32) * xrs * 2u);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                const int p0 = pt * 32 + 8 * rg + 4 * g2;
                 u32x2 o;
                 o[0] = pack_bf16x2(Z[t][pt][4 * rg + 0], Z[t][pt][4 * rg + 1]);
                 o[1] = pack_bf16x2(Z[t][pt][4 * rg + 2], Z[t][pt][4 * rg + 3]);
-                *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
+                __builtin_amdgcn_raw_buffer_store_b64(o, r, yvoff + (pt * 32 + 8 * rg) * 2u, 0, 0);
             }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-        __builtin_amdgcn_wave_barrier();
-        const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
-            const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
-            buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (ti * 32 + 8 * kk) * xrs * 2u), yvoff);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
     };
 
     auto jstep = [&](int jt, auto par) {
         constexpr int buf = decltype(par)::value;  // jt % 2: LDS buffer and C.B register set
-        if (jt + 2 < NI) load_stage(jt + 2, R[buf]);
-        if (jt + 1 <= ti0) load_cb(ti0, jt + 1, cbr[buf ^ 1][0]);
-        if (jt + 1 <= ti1) load_cb(ti1, jt + 1, cbr[buf ^ 1][1]);
+        // unconditional prefetches (empty ranges past the end): the same loads
+        // are in flight on every path, so waits count exactly
+        load_stage(jt + 2, R[buf]);
+        load_cb(ti0, jt + 1, cbr[buf ^ 1][0]);
+        load_cb(ti1, jt + 1, cbr[buf ^ 1][1]);
         // wave-uniform cases (ti0 < ti1)
         if (jt < ti0) {
             offdiag(jt, buf, 3, cbr[buf]);
@@ -660,15 +715,18 @@ template <int Q, int N>
 void launch_state_t(const ScanShape &s, const void *x, const void *Bm, const float *dt,
                     const float *Acs, float *states, hipStream_t st) {
     const int64_t nb = s.B * s.T * s.H;
-    k_chunk_state_mfma<Q, N><<<padded_grid(nb), 256, 0, st>>>(
-        (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T, nb);
+    k_chunk_state_mfma<Q, N, false><<<padded_grid(nb), 256, 0, st>>>(
+        (const bf16 *)x, (const bf16 *)Bm, dt, nullptr, const_cast<float *>(Acs), states, s.L,
+        (int)s.H, (int)s.G, (int)s.T, nb);
 }
+
 
 template <int Q, int N>
 void launch_cb_t(const ScanShape &s, const void *Bm, const void *Cm, void *cb, hipStream_t st) {
-    const int64_t nb = s.B * s.T * s.G * (Q / 32);
-    k_chunk_cb_mfma<Q, N><<<(unsigned)nb, 256, 0, st>>>((const bf16 *)Bm, (const bf16 *)Cm,
-                                                        (u32x4 *)cb, s.L, (int)s.G, (int)s.T, nb);
+    constexpr int NI = Q / 32;
+    const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
+    k_chunk_cb_mfma<Q, N><<<(unsigned)((ntiles + 3) / 4), 256, 0, st>>>(
+        (const bf16 *)Bm, (const bf16 *)Cm, (u32x4 *)cb, s.L, (int)s.G, (int)s.T, ntiles);
 }
 
 template <int Q, int N>
@@ -679,6 +737,27 @@ void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const voi
     k_chunk_scan_mfma<Q, N><<<padded_grid(nb), Q, 0, st>>>(
         (const bf16 *)x, dt, (const bf16 *)Cm, D, Acs, states, (const u32x4 *)cb, (bf16 *)y, s.L,
         (int)s.H, (int)s.G, (int)s.T, nb);
+}
+
+// The whole chunked scan in three launches: chunk states with the in-block
+// cumsum, state passing with the C.B tiles, chunk output.
+template <int Q, int N>
+void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const float *A,
+                    const void *Bm, const void *Cm, const float *D, const float *init, void *y,
+                    float *fin, float *Acs, float *states, void *cb, hipStream_t st) {
+    constexpr int NI = Q / 32;
+    const int64_t nb = s.B * s.T * s.H;
+    k_chunk_state_mfma<Q, N, true><<<padded_grid(nb), 256, 0, st>>>(
+        (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T,
+        nb);
+    const int64_t PN = s.P * s.N;
+    const int ny = (int)((PN / 4 + 255) / 256);
+    const int64_t nsp = s.B * s.H * ny;
+    const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
+    k_state_passing_cb<Q, N><<<(unsigned)(nsp + (ntiles + 3) / 4), 256, 0, st>>>(
+        states, Acs, init, fin, s.L, (int)s.H, PN, (int)s.T, nsp, ny, (const bf16 *)Bm,
+        (const bf16 *)Cm, (u32x4 *)cb, (int)s.G, ntiles);
+    launch_scan_t<Q, N>(s, x, dt, Cm, D, Acs, states, cb, y, st);
 }
 
 }  // namespace
@@ -714,6 +793,13 @@ size_t chunk_cb_bytes(const ScanShape &s) {
 void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
                           hipStream_t st) {
     SSD_DISPATCH_QN(launch_cb_t, s, Bm, Cm, cb, st);
+}
+
+void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
+                            const void *Bm, const void *Cm, const float *D, const float *init,
+                            void *y, float *fin, float *Acs, float *states, void *cb,
+                            hipStream_t st) {
+    SSD_DISPATCH_QN(launch_fused_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb, st);
 }
 
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,

@@ -143,10 +143,15 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, 
     float *states = reinterpret_cast<float *>(static_cast<char *>(workspace) + acs_bytes(s));
     void *scan_ws = static_cast<char *>(workspace) + acs_bytes(s) + states_bytes(s);
     hipStream_t hs = as_stream(stream);
-    ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
-    ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
-    ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
-    ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, scan_ws, y, hs);
+    if (ssd::mfma_supported(s)) {
+        ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
+                                    scan_ws, hs);
+    } else {
+        ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
+        ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
+        ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
+        ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, scan_ws, y, hs);
+    }
     return after_launch();
 }
 
