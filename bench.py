@@ -44,12 +44,16 @@ def prefill_bytes(s) -> dict:
     st = B * T * H * P * N * 4
     hst = B * H * P * N * 4
     small = 2 * H * 4                               # A and D
+    ni = s.chunk // 32
+    cb = B * T * G * (ni * (ni + 1) // 2) * 4096    # C.B tiles (MFMA path), counted once
     return {
         "call": x + x + 2 * bc + dt + hst + hst + small,       # x, y, B, C, dt, init, final
         "chunk_cumsum": dt + acs + H * 4,
+        "chunk_cb": 2 * bc + cb,
         "chunk_state": x + bc + dt + acs + st,
         "state_passing": 2 * st + B * H * T * 4 + 2 * hst,
-        "chunk_scan": x + 2 * bc + dt + acs + st + x + H * 4,
+        # x, C, dt, Acs, entering states, the C.B tiles once, D; y written
+        "chunk_scan": x + bc + dt + acs + st + cb + H * 4 + x,
     }
 
 
@@ -65,6 +69,31 @@ def prefill_flops(s) -> float:
 def decode_bytes(batch, H, P, N, G, e=2) -> int:
     return 2 * batch * H * P * N * 4 + 2 * batch * H * P * e + batch * H * 4 \
         + 2 * batch * G * N * e + 2 * H * 4
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "chunk_scan_m2p7b_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "mamba_ssd_chunked_scan_amd", "csrc", "mfma.hip")
+
+
+def measured_traffic():
+    """HBM bytes per chunk-output launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter read for a
+    plain device copy of known size), or None when that summary is missing or
+    was taken on a different kernel source than the one built now."""
+    import hashlib
+    try:
+        text = open(COUNTERS).read()
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines()
+                  if line.startswith(("kernel_source_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("kernel_source_sha256", "").strip() != src:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 def time_launches(torch, fn, iters, warmup=2):
@@ -130,6 +159,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="end with a plain 256 MiB device copy (twice), the known-size kernel "
+                         "that hardware byte counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -188,11 +220,14 @@ def main():
                             P_(d["dt"]), P_(Acs), P_(states)),
         "state_passing": Lean(torch, lib.ssd_state_passing, dref, P_(states2), P_(Acs),
                               P_(d["init"]), P_(fin2)),
+        "chunk_cb": Lean(torch, lib.ssd_chunk_cb, dref, P_(d["B"]), P_(d["C"]), P_(cbws),
+                         cbws.numel()),
         "chunk_scan": Lean(torch, lib.ssd_chunk_scan, dref, P_(d["x"]), P_(d["dt"]), P_(d["B"]),
                            P_(d["C"]), P_(d["D"]), P_(Acs), P_(states), P_(y2), P_(cbws),
                            cbws.numel()),
     }
     stage_fns["chunk_cumsum"]()
+    stage_fns["chunk_cb"]()
     stage_fns["chunk_state"]()
     states2.copy_(states)
     torch.cuda.synchronize()
@@ -253,12 +288,20 @@ def main():
         "decode": decode,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic() if dom == "chunk_scan" else None,
                      "algorithmic_bytes_per_launch": bytes_[dom],
                      "avg_launch_us": round(stage_ms[dom] * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp)
+    if args.calibrate:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.mul(src, 2.0, out=dst)   # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
     print(json.dumps(out))
 
 

@@ -146,22 +146,32 @@ ssd_status ssd_chunk_state(const ssd_scan_desc *d, const void *x, const void *B,
 ssd_status ssd_state_passing(const ssd_scan_desc *d, float *states, const float *Acs,
                              const float *init_state, float *final_state, void *stream);
 
-/* Bytes of device workspace ssd_chunk_scan needs for shape *d (0 is possible).
- * It holds the within-chunk products C_t . B_j, which do not depend on the
- * head and are formed once per (batch, chunk, group); its contents are
- * internal and need no initialisation. */
+/* Bytes of device workspace that ssd_chunk_cb fills and ssd_chunk_scan reads
+ * for shape *d (0 is possible: then both ignore the workspace). */
 ssd_status ssd_chunk_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes);
+
+/* The within-chunk products CB[i][j] = C_i . B_j (j <= i, same chunk and
+ * group).  They do not involve the head, so they are formed once per
+ * (batch, chunk, group) and shared by the nheads/ngroups heads of the group
+ * ("Compiler-First ...", §3, "Primitive-level implementation" and the
+ * intra-chunk contraction of B.5).  The workspace layout is internal to the
+ * library; it is written here and read by ssd_chunk_scan for the same d, B
+ * and C.  workspace: at least ssd_chunk_scan_workspace_size bytes (may be NULL
+ * when that size is 0, in which case nothing is launched). */
+ssd_status ssd_chunk_cb(const ssd_scan_desc *d, const void *B, const void *C, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* y for every chunk from the chunk-entry states:
  *   y[t] = sum_{j <= t in chunk} (C_t . B_j) exp(Acs_t - Acs_j) dt_j x_j
  *          + exp(Acs_t) (C_t . H_c) + D x_t
- * with H_c = states[c] as left by ssd_state_passing ("Compiler-First ...",
- * §3, the intra-chunk output contraction of B.5).  workspace: device buffer
- * of at least ssd_chunk_scan_workspace_size bytes (may be NULL when that size
- * is 0); it must not overlap any other argument. */
+ * with H_c = states[c] as left by ssd_state_passing and C_t . B_j as left in
+ * the workspace by ssd_chunk_cb ("Compiler-First ...", §3, the intra-chunk
+ * output contraction of B.5).  workspace: the buffer ssd_chunk_cb filled for
+ * the same d, B and C (may be NULL when ssd_chunk_scan_workspace_size is 0);
+ * it must not overlap any other argument. */
 ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
                           const void *B, const void *C, const float *D, const float *Acs,
-                          const float *states, void *y, void *workspace,
+                          const float *states, void *y, const void *workspace,
                           size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus

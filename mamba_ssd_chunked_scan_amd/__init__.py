@@ -9,6 +9,6 @@ synthetic input generator used by the tests and the benchmark.
     y_t = step(state, x_t, dt_t, A, B_t, C_t, D)      # state updated in place
 """
 from .binding import (  # noqa: F401
-    SSDError, chunk_cumsum, chunk_scan, chunk_state, lib, scan_fwd, state_passing, step,
-    workspace_size,
+    SSDError, chunk_cb, chunk_cumsum, chunk_scan, chunk_scan_workspace_size, chunk_state, lib,
+    scan_fwd, state_passing, step, workspace_size,
 )

@@ -24,7 +24,7 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 # Every function include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
            "ssd_step", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-           "ssd_chunk_scan_workspace_size", "ssd_chunk_scan")
+           "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan")
 
 
 class ScanDesc(ctypes.Structure):
@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.ssd_state_passing.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 5
         L.ssd_chunk_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
                                                     ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_chunk_cb.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 3 + [ctypes.c_size_t, _P]
         L.ssd_chunk_scan.argtypes = ([ctypes.POINTER(ScanDesc)] + [_P] * 9
                                      + [ctypes.c_size_t, _P])
         for name in EXPORTS[2:]:
@@ -274,21 +275,39 @@ def chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, c
     return n.value
 
 
+def chunk_cb(x, B, C, chunk: int, workspace=None):
+    """Stage: the within-chunk C.B products of every (batch, chunk, group)
+    into a uint8 device workspace (returned; None when the shape needs none).
+    ``x`` only supplies the shape and dtype of the call."""
+    Bt, L, H, P, N, G = _check_scan_inputs(x, torch.empty(x.shape[:3], device=x.device),
+                                           torch.empty(x.shape[2], device=x.device), B, C, None)
+    desc = _scan_desc(x, B, chunk)
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_scan_workspace_size",
+           lib().ssd_chunk_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    if n.value == 0:
+        return None
+    if workspace is None:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("ssd_chunk_cb", lib().ssd_chunk_cb(ctypes.byref(desc), _ptr(B), _ptr(C),
+                                              _ptr(workspace), ws_bytes, _stream(x.device)))
+    return workspace
+
+
 def chunk_scan(x, dt, B, C, D, Acs, states, chunk: int, workspace=None):
-    """Stage 4: y from the chunk-entry states (``workspace``: optional uint8
-    device tensor of at least :func:`chunk_scan_workspace_size` bytes)."""
+    """Stage: y from the chunk-entry states.  ``workspace`` is what
+    :func:`chunk_cb` returned for the same B and C; when omitted it is formed
+    here first."""
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, torch.empty(x.shape[2], device=x.device),
                                            B, C, D)
     T = -(-L // chunk)
     _need(Acs, "Acs", (Bt, H, L), torch.float32, x.device)
     _need(states, "states", (Bt, T, H, P, N), torch.float32, x.device)
+    if workspace is None:
+        workspace = chunk_cb(x, B, C, chunk)
     y = torch.empty_like(x)
     desc = _scan_desc(x, B, chunk)
-    n = ctypes.c_size_t(0)
-    _check("ssd_chunk_scan_workspace_size",
-           lib().ssd_chunk_scan_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
-    if workspace is None and n.value:
-        workspace = torch.empty(n.value, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssd_chunk_scan", lib().ssd_chunk_scan(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(B),
                                                   _ptr(C), _ptr(D), _ptr(Acs), _ptr(states),

@@ -273,11 +273,14 @@ size_t chunk_scan_ws_bytes(const ScanShape &s) {
     return mfma_supported(s) ? chunk_cb_bytes(s) : 0;
 }
 
+void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *ws, hipStream_t st) {
+    if (mfma_supported(s)) launch_chunk_cb_mfma(s, Bm, Cm, ws, st);
+}
+
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       void *ws, void *y, hipStream_t st) {
+                       const void *ws, void *y, hipStream_t st) {
     if (mfma_supported(s)) {
-        launch_chunk_cb_mfma(s, Bm, Cm, ws, st);
         launch_chunk_scan_mfma(s, x, dt, Cm, D, Acs, states, ws, y, st);
         return;
     }

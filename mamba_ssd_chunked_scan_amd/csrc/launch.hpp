@@ -26,9 +26,11 @@ void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
                           const float *init, float *fin, hipStream_t st);
 // Device workspace of the chunk-output stage (0 when its kernel needs none).
 size_t chunk_scan_ws_bytes(const ScanShape &s);
+// C.B tiles into the chunk-output workspace (no-op when it needs none).
+void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *ws, hipStream_t st);
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       void *ws, void *y, hipStream_t st);
+                       const void *ws, void *y, hipStream_t st);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);

@@ -150,6 +150,7 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, 
         ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
         ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
         ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
+        ssd::launch_chunk_cb(s, B, C, scan_ws, hs);
         ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, scan_ws, y, hs);
     }
     return after_launch();
@@ -224,9 +225,23 @@ ssd_status ssd_chunk_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) 
     return SSD_OK;
 }
 
+ssd_status ssd_chunk_cb(const ssd_scan_desc *d, const void *B, const void *C, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    const size_t need = scan_ws_bytes(s);
+    if (need == 0) return SSD_OK;
+    st = check_ptrs({B, C, workspace}, {});
+    if (st != SSD_OK) return st;
+    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    ssd::launch_chunk_cb(s, B, C, workspace, as_stream(stream));
+    return after_launch();
+}
+
 ssd_status ssd_chunk_scan(const ssd_scan_desc *d, const void *x, const float *dt,
                           const void *B, const void *C, const float *D, const float *Acs,
-                          const float *states, void *y, void *workspace, size_t ws_bytes,
+                          const float *states, void *y, const void *workspace, size_t ws_bytes,
                           void *stream) {
     ScanShape s;
     ssd_status st = check_scan(d, &s);

@@ -164,6 +164,20 @@ def test_scan_workspace_too_small(L):
     assert L.ssd_scan_fwd(ctypes.byref(d), *ptrs, need, None) == NULL
 
 
+def test_chunk_cb_errors(L):
+    d = desc()
+    _, need = cb_size(L, d)
+    assert L.ssd_chunk_cb(ctypes.byref(d), P16, P16, P16, need - 1, None) == WS
+    assert L.ssd_chunk_cb(ctypes.byref(d), None, P16, P16, need, None) == NULL
+    assert L.ssd_chunk_cb(ctypes.byref(d), P16, None, P16, need, None) == NULL
+    assert L.ssd_chunk_cb(ctypes.byref(d), P16, P16, None, need, None) == NULL
+    assert L.ssd_chunk_cb(ctypes.byref(d), P_MIS, P16, P16, need, None) == ALIGN
+    assert L.ssd_chunk_cb(ctypes.byref(desc(chunk=48)), P16, P16, P16, need, None) == UNSUP
+    # shapes that need no workspace: a no-op, pointers untouched
+    for kw in (dict(dtype=0), dict(headdim=32), dict(seqlen=0), dict(batch=0)):
+        assert L.ssd_chunk_cb(ctypes.byref(desc(**kw)), None, None, None, 0, None) == OK
+
+
 def test_chunk_scan_workspace_errors(L):
     d = desc()
     _, need = cb_size(L, d)
