@@ -45,15 +45,17 @@ def prefill_bytes(s) -> dict:
     hst = B * H * P * N * 4
     small = 2 * H * 4                               # A and D
     ni = s.chunk // 32
-    cb = B * T * G * (ni * (ni + 1) // 2) * 4096    # C.B tiles (MFMA path), counted once
+    # C.B tiles and C operand fragments (MFMA path), counted once
+    cb = B * T * G * ((ni * (ni + 1) // 2) * 4096 + s.chunk * N * 2)
     return {
         "call": x + x + 2 * bc + dt + hst + hst + small,       # x, y, B, C, dt, init, final
         "chunk_cumsum": dt + acs + H * 4,
         "chunk_cb": 2 * bc + cb,
         "chunk_state": x + bc + dt + acs + st,
         "state_passing": 2 * st + B * H * T * 4 + 2 * hst,
-        # x, C, dt, Acs, entering states, the C.B tiles once, D; y written
-        "chunk_scan": x + bc + dt + acs + st + cb + H * 4 + x,
+        # x, dt, Acs, entering states, the C.B tiles and C fragments once, D;
+        # y written
+        "chunk_scan": x + dt + acs + st + cb + H * 4 + x,
     }
 
 

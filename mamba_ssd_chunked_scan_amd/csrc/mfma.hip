@@ -110,9 +110,19 @@ __device__ __forceinline__ u32x4 tr_operand(const bf16 *tile, int ld, int k0, in
 // Logical block index: block b runs on XCD b % 8, so XCD x receives logical
 // blocks [x*per, (x+1)*per) with per = gridDim.x / 8 (the grid is padded to a
 // multiple of 8).
-__device__ __forceinline__ int64_t xcd_block() {
-    const int64_t per = gridDim.x / 8;
-    return (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+__device__ __forceinline__ uint32_t xcd_block() {
+    const uint32_t per = gridDim.x / 8;
+    return (blockIdx.x % 8) * per + blockIdx.x / 8;
+}
+
+// (b, c, h) of logical block lb over a [B][T][H] grid: 32-bit scalar
+// arithmetic (a grid has fewer than 2^32 blocks).
+struct BCH {
+    uint32_t b, c, h;
+};
+__device__ __forceinline__ BCH split_bch(uint32_t lb, uint32_t H, uint32_t T) {
+    const uint32_t bc = lb / H;
+    return BCH{bc / T, bc % T, lb - bc * H};
 }
 
 unsigned padded_grid(int64_t blocks) { return (unsigned)((blocks + 7) / 8 * 8); }
@@ -179,13 +189,12 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     __shared__ __attribute__((aligned(16))) bf16 xlo[2][kJT * LDX];
     __shared__ __attribute__((aligned(16))) bf16 bst[2][kJT * LDB];
     __shared__ float w[Q];
-    const int64_t lb = xcd_block();
+    const uint32_t lb = xcd_block();
     if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = (int)(lb % H);
-    const int64_t bc = lb / H;
-    const int c = (int)(bc % T);
-    const int64_t b = bc / T;
+    const BCH ix = split_bch(lb, H, T);
+    const int h = ix.h, c = ix.c;
+    const int64_t b = ix.b;
     const int g = h / (H / G);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
@@ -311,11 +320,15 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
 //   diagonal tile:     k = v    -> fp32 registers 4v..4v+3 (the scan applies
 //                                  the per-head decay and the mask first).
 // Tiles of (b, c, g) are consecutive, tile (ti, jt) at ti(ti+1)/2 + jt.
+// The wave of each diagonal tile also stores the row tile's C rows as the
+// MFMA operands the chunk scan's state term uses (lane l: row 32 ti + l%32,
+// 8 values from column 16 s + 8 (l/32)), at cfr[((b,c,g) NI + ti) KS + s][lane],
+// so that the scan reads them as contiguous 1 KB wave loads.
 // Tile w (flat over (b, c, g) and the NT causal tiles) by one wave.
 template <int Q, int N>
 __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-                                        u32x4 *__restrict__ cb, int64_t L, int G, int T,
-                                        int64_t w) {
+                                        u32x4 *__restrict__ cb, u32x4 *__restrict__ cfr,
+                                        int64_t L, int G, int T, int64_t w) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     const int lane = threadIdx.x & 63, il = lane & 31, g2 = lane >> 5;
     const int tile = (int)(w % NT);
@@ -362,6 +375,9 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
         for (int v = 0; v < 4; ++v)
             o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
                                      __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+        u32x4 *cf = cfr + (bcg * NI + ti) * KS * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cf[s * 64] = crow[s];
     }
 }
 
@@ -371,7 +387,7 @@ k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 
                 int64_t L, int G, int T, int64_t ntiles) {
     const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= ntiles) return;
-    cb_tile<Q, N>(Bm, Cm, cb, L, G, T, w);
+    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w);
 }
 
 // The inter-chunk state pass and the C.B tiles in one launch: the first
@@ -393,15 +409,17 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
     }
     const int64_t w = (blk - nsp) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= ntiles) return;
-    cb_tile<Q, N>(Bm, Cm, cb, L, G, T, w);
+    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w);
 }
 
 // ------------------------------------------------------------- chunk scan
-// One block per (b, c, h) with NI/2 waves (NI = Q/32 row tiles); wave w owns
-// row tiles ti0 = w and ti1 = NI-1-w, which together have NI+1 causal tile
-// visits for every wave.  Per owned tile the wave keeps Z = Y^T (64 x 32 fp32,
-// two accumulators over p).  With e(t) = 32t + 31 the last row of tile t and
-// Acs_{e(-1)} = 0, the output row i of tile ti is
+// One block per (b, c, h) with one wave per 32-row output tile (NI = Q/32
+// waves).  Wave w owns tile w for w < NI/2 and tile 3NI/2-1-w otherwise, so
+// the two waves that share a SIMD (w and w + NI/2 when waves are dealt to the
+// 4 SIMDs in turn) together make NI+1 causal tile visits, and a CU running two
+// blocks keeps four waves per SIMD to hide latency.  The wave keeps Z = Y^T
+// of its tile (64 x 32 fp32, two accumulators over p).  With e(t) = 32t + 31
+// the last row of tile t and Acs_{e(-1)} = 0, the output row i of tile ti is
 //   y_i = exp(Acs_i - Acs_{e(ti-1)}) Z_i + diagonal-tile part + D x_i,
 //   Z   = C_i.H, then for jt = 0..ti-1:
 //         Z <- exp(Acs_{e(jt)} - Acs_{e(jt-1)}) Z + sum_{j in jt} CB[i][j] xw_j,
@@ -410,96 +428,103 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // every exponent is <= 0, so nothing overflows, and an underflow drops only
 // terms that are at least as small in the exact result.  xw depends on the
 // stage alone, so it is formed once per 32-token stage (as a hi/lo bf16 pair)
-// and shared by all waves; CB comes pre-split from the C.B tile kernel, and
+// by all threads together; CB comes pre-split from the C.B tile kernel, and
 // the off-diagonal product takes three MFMAs (hi.hi, lo.hi, hi.lo).  The
 // diagonal tile applies exp(Acs_i - Acs_j) dt_j to the fp32 CB element by
 // element under the causal mask and multiplies raw x.
 //
-// Stages (raw x, xw hi, xw lo) stream through two LDS buffers, loaded two
-// stages ahead; the C.B tiles of the next step are loaded one step ahead.  The
-// tile loop branches on wave-uniform values only.  A tile's output goes out
-// one step after its diagonal, through LDS, as full 128-byte rows.
+// Every global access is a whole-line wave access: x stages, H, the C
+// operand fragments and C.B tiles (1 KB each) from the C.B kernel, and y
+// rows, which go out through LDS as full 128-byte rows one step after their
+// tile's diagonal.  Stages (raw x, xw hi, xw lo) stream through two LDS
+// slots, loaded two stages ahead; the C.B tile of the next step is loaded one
+// step ahead.  The tile loop branches on wave-uniform values only.
 template <int Q, int N>
-__global__ void __launch_bounds__(Q, 2) __attribute__((amdgpu_waves_per_eu(1, Q == 256 ? 2 : 1)))
+__global__ void __launch_bounds__(Q * 2) __attribute__((amdgpu_waves_per_eu(Q == 256 ? 4 : 2)))
 k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
-                  const bf16 *__restrict__ Cm, const float *__restrict__ D,
-                  const float *__restrict__ Acs, const float *__restrict__ states,
-                  const u32x4 *__restrict__ cb, bf16 *__restrict__ y, int64_t L, int H, int G,
+                  const float *__restrict__ D, const float *__restrict__ Acs,
+                  const float *__restrict__ states, const u32x4 *__restrict__ cb,
+                  const u32x4 *__restrict__ cfr, bf16 *__restrict__ y, int64_t L, int H, int G,
                   int T, int64_t nblocks) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
-    constexpr int TH = Q;                 // threads: NI/2 waves
+    constexpr int TH = Q * 2;             // threads: NI waves
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
     constexpr int LDX = kP + 16;          // stage rows, read transposed
+    constexpr int LDY = kP + 8;           // bf16 y staging rows
     constexpr int H_BYTES = 2 * kP * LDH * 2;
-    constexpr int XV = 256 / TH;          // 16-byte x segments per thread per stage
+    constexpr int Y_BYTES = NI * 32 * LDY * 2;
+    constexpr int U_BYTES = H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES;
+    constexpr int XE = 2048 / TH;         // x elements per thread per stage (4, 8 or 16)
     constexpr int NHV = kP * N / 4 / TH;  // float4 of H per thread
-    constexpr int HB = NHV < 8 ? NHV : 8; // H float4 held in registers at a time
-    __shared__ __attribute__((aligned(16))) char hy[H_BYTES];
-    __shared__ __attribute__((aligned(16))) bf16 xs[2][kJT * LDX];
-    __shared__ __attribute__((aligned(16))) bf16 xh[2][kJT * LDX];
-    __shared__ __attribute__((aligned(16))) bf16 xl[2][kJT * LDX];
+    constexpr int SLOT = 3 * kJT * LDX;   // raw x, xw hi, xw lo of one stage
+    static_assert(XE == 4 || XE == 8 || XE == 16, "stage split");
+    typedef unsigned XR __attribute__((ext_vector_type(XE / 2)));
+    // H (prologue), then the per-wave y staging rows
+    __shared__ __attribute__((aligned(16))) char hu[U_BYTES];
+    __shared__ __attribute__((aligned(16))) bf16 sa[2 * SLOT];
     __shared__ __attribute__((aligned(16))) float acs_s[Q];
     __shared__ __attribute__((aligned(16))) float dt_s[Q];
-    const int64_t lb = xcd_block();
+    const uint32_t lb = xcd_block();
     if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int il = lane & 31, g2 = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int h = (int)(lb % H);
-    const int64_t bc = lb / H;
-    const int c = (int)(bc % T);
-    const int64_t b = bc / T;
+    const int ti = wave < NI / 2 ? wave : 3 * NI / 2 - 1 - wave;
+    const BCH ix = split_bch(lb, H, T);
+    const int h = ix.h, c = ix.c;
+    const int64_t b = ix.b;
     const int g = h / (H / G);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
     const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
     // per-thread offsets are unsigned 32-bit from block-uniform bases (a
-    // chunk spans < 2^31 elements of x, C and y), so loads and stores use the
+    // chunk spans < 2^31 bytes of x and y), so loads and stores use the
     // scalar-base + 32-bit-offset address form
-    const unsigned xrs = H * kP, crs = G * N;
-    const u32x4 *cbg = cb + ((b * T + c) * G + g) * NT * 256;
-    const int ti0 = wave, ti1 = NI - 1 - wave;
+    const unsigned xrs = H * kP;
+    const int64_t bcg = (b * T + c) * G + g;
+    const u32x4 *cbg = cb + bcg * NT * 256;
 
     // x rows of this chunk and head: bytes up to the end of row q-1, so rows
     // past a short chunk's end read as zeros; y rows likewise (stores dropped)
     const uint32_t xy_bytes = ((unsigned)(q - 1) * xrs + kP) * 2u;
-    u32x4 R[2][XV];
-    // thread (row, seg) of a stage: row = tid/8 + (TH/8) v, 8 bf16 at seg*8
-    const uint32_t xvoff = ((unsigned)(tid >> 3) * xrs + (tid & 7) * 8u) * 2u;
-    auto load_stage = [&](int st, u32x4 (&r)[XV]) {
-#pragma unroll
-        for (int v = 0; v < XV; ++v)
-            r[v] = buffer_load16(
-                buffer_rsrc_at(xbase, xy_bytes, (st * kJT + (TH / 8) * v) * xrs * 2u), xvoff);
+    // thread (row, seg) of a stage: XE consecutive p of one row
+    constexpr int SPR = kP / XE;          // threads per row
+    const int xrow = tid / SPR, xseg = tid % SPR;
+    const uint32_t xvoff = ((unsigned)xrow * xrs + xseg * XE) * 2u;
+    XR R[2];
+    auto load_stage = [&](int st, XR &r) __attribute__((always_inline)) {
+        const rsrc_t rs = buffer_rsrc_at(xbase, xy_bytes, (unsigned)(st * kJT) * xrs * 2u);
+        if constexpr (XE == 4) {
+            r = __builtin_bit_cast(XR, __builtin_amdgcn_raw_buffer_load_b64(rs, xvoff, 0, 0));
+        } else if constexpr (XE == 8) {
+            r = __builtin_bit_cast(XR, buffer_load16(rs, xvoff));
+        } else {
+            const u32x4 a = buffer_load16(rs, xvoff), b2 = buffer_load16(rs, xvoff + 16u);
+            r = XR{a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
+        }
     };
     // raw x and xw = exp(Acs_{e(st)} - Acs_j) dt_j x_j (hi/lo) of stage st
-    auto store_stage = [&](int st, int buf, const u32x4 (&r)[XV]) {
+    auto store_stage = [&](int st, bf16 *sl, const XR &raw) __attribute__((always_inline)) {
         const float ae = acs_s[st * kJT + kJT - 1];
+        const int j = st * kJT + xrow;
+        const float wj = ssd_exp(ae - acs_s[j]) * dt_s[j];  // dt_s is 0 past q (raw is 0 too)
+        XR hi, lo;
 #pragma unroll
-        for (int v = 0; v < XV; ++v) {
-            const int e = tid + TH * v, row = e >> 3, seg = e & 7;
-            const int j = st * kJT + row;
-            const u32x4 raw = r[v];                              // zero past q
-            const float wj = ssd_exp(ae - acs_s[j]) * dt_s[j];  // dt_s is 0 past q
-            float m[8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                m[2 * k] = lo_bf16(raw[k]) * wj;
-                m[2 * k + 1] = hi_bf16(raw[k]) * wj;
-            }
-            u32x4 hi, lo;
-            split8(m, hi, lo);
-            *reinterpret_cast<u32x4 *>(&xs[buf][row * LDX + seg * 8]) = raw;
-            *reinterpret_cast<u32x4 *>(&xh[buf][row * LDX + seg * 8]) = hi;
-            *reinterpret_cast<u32x4 *>(&xl[buf][row * LDX + seg * 8]) = lo;
+        for (int k = 0; k < XE / 2; ++k) {
+            uint32_t l;
+            hi[k] = split2(lo_bf16(raw[k]) * wj, hi_bf16(raw[k]) * wj, l);
+            lo[k] = l;
         }
+        *reinterpret_cast<XR *>(&sl[xrow * LDX + xseg * XE]) = raw;
+        *reinterpret_cast<XR *>(&sl[(kJT + xrow) * LDX + xseg * XE]) = hi;
+        *reinterpret_cast<XR *>(&sl[(2 * kJT + xrow) * LDX + xseg * XE]) = lo;
     };
     // the 4 KB C.B tile (ti, jt) as four 16-byte operands of this lane; a
     // tile outside the causal range (jt > ti) gets an empty range: the loads
     // still issue, so every path has the same loads in flight, but read zeros
     // and touch no memory
     const uint32_t cbvoff = lane * 16u;
-    auto load_cb = [&](int ti, int jt, u32x4 (&o)[4]) {
+    auto load_cb = [&](int jt, u32x4 (&o)[4]) __attribute__((always_inline)) {
         const int tile = ti * (ti + 1) / 2 + min(jt, ti);
         const rsrc_t r = buffer_rsrc_at(cbg, jt <= ti ? (tile + 1) * 4096u : 0u, tile * 4096u);
 #pragma unroll
@@ -507,9 +532,9 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     };
 
     // ---- prologue: global loads in the order they are needed: acs/dt and H
-    // (before the first barrier), C rows (state term), stages 0-1, C.B tiles
-    float acs_v, dt_v;
-    {
+    // (before the first barrier), C operands (state term), stages 0-1, C.B
+    float acs_v = 0.f, dt_v = 0.f;
+    if (tid < Q) {
         const float *acs = Acs + (b * H + h) * L + t0;
         const int jj = min(tid, q - 1);
         acs_v = acs[jj];
@@ -520,117 +545,92 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         }
     }
     const float *Hc = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
-    float4 hv[HB];
+    float4 hv[NHV];
 #pragma unroll
-    for (int i = 0; i < HB; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * i));
-    u32x4 c0[KS], c1[KS];
+    for (int i = 0; i < NHV; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * i));
+    u32x4 cf[KS];
     {
-        const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
-        const unsigned o0 = (unsigned)min(32 * ti0 + il, q - 1) * crs + 8u * g2;
-        const unsigned o1 = (unsigned)min(32 * ti1 + il, q - 1) * crs + 8u * g2;
+        const u32x4 *f = cfr + (bcg * NI + ti) * KS * 64 + lane;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            c0[s] = *reinterpret_cast<const u32x4 *>(cbase + (o0 + 16u * s));
-            c1[s] = *reinterpret_cast<const u32x4 *>(cbase + (o1 + 16u * s));
-        }
+        for (int s = 0; s < KS; ++s) cf[s] = f[s * 64];
     }
     load_stage(0, R[0]);
     load_stage(1, R[1]);
-    u32x4 cbr[2][2][4];  // [step parity][tile][operand]
-    load_cb(ti0, 0, cbr[0][0]);
-    load_cb(ti1, 0, cbr[0][1]);
-    acs_s[tid] = acs_v;
-    dt_s[tid] = dt_v;
-    bf16 *Hh = reinterpret_cast<bf16 *>(hy);
+    u32x4 cbr[4];  // this step's C.B tile; reloaded for the next step once read
+    load_cb(0, cbr);
+    if (tid < Q) {
+        acs_s[tid] = acs_v;
+        dt_s[tid] = dt_v;
+    }
+    bf16 *Hh = reinterpret_cast<bf16 *>(hu);
     bf16 *Hl = Hh + kP * LDH;
 #pragma unroll
-    for (int i0 = 0; i0 < NHV; i0 += HB) {
-        if (i0 > 0) {
-#pragma unroll
-            for (int i = 0; i < HB; ++i)
-                hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * (i0 + i)));
-        }
-#pragma unroll
-        for (int i = 0; i < HB; ++i) {
-            const int e = tid + TH * (i0 + i), p = e / (N / 4), n = (e % (N / 4)) * 4;
-            u32x2 hh, hl;
-            uint32_t l0, l1;
-            hh[0] = split2(hv[i].x, hv[i].y, l0);
-            hh[1] = split2(hv[i].z, hv[i].w, l1);
-            hl[0] = l0;
-            hl[1] = l1;
-            *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
-            *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
-        }
+    for (int i = 0; i < NHV; ++i) {
+        const int e = tid + TH * i, p = e / (N / 4), n = (e % (N / 4)) * 4;
+        u32x2 hh, hl;
+        uint32_t l0, l1;
+        hh[0] = split2(hv[i].x, hv[i].y, l0);
+        hh[1] = split2(hv[i].z, hv[i].w, l1);
+        hl[0] = l0;
+        hl[1] = l1;
+        *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
+        *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
     }
     __syncthreads();  // acs_s, dt_s, H
-    store_stage(0, 0, R[0]);
-    // state term Z = H C_i^T for both tiles (C rows straight from global)
-    f32x16 Z[2][2];
-    {
-        Z[0][0] = Z[0][1] = Z[1][0] = Z[1][1] = zero16();
+    store_stage(0, sa, R[0]);
+    // state term Z = H C_i^T
+    f32x16 Z[2] = {zero16(), zero16()};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                const int ho = (pt * 32 + il) * LDH + 16 * s + 8 * g2;
-                const u32x4 ah = *reinterpret_cast<const u32x4 *>(Hh + ho);
-                const u32x4 al = *reinterpret_cast<const u32x4 *>(Hl + ho);
-                Z[0][pt] = mfma32(ah, c0[s], Z[0][pt]);
-                Z[1][pt] = mfma32(ah, c1[s], Z[1][pt]);
-                Z[0][pt] = mfma32(al, c0[s], Z[0][pt]);
-                Z[1][pt] = mfma32(al, c1[s], Z[1][pt]);
-            }
+        for (int pt = 0; pt < 2; ++pt) {
+            const int ho = (pt * 32 + il) * LDH + 16 * s + 8 * g2;
+            const u32x4 ah = *reinterpret_cast<const u32x4 *>(Hh + ho);
+            const u32x4 al = *reinterpret_cast<const u32x4 *>(Hl + ho);
+            Z[pt] = mfma32(ah, cf[s], Z[pt]);
+            Z[pt] = mfma32(al, cf[s], Z[pt]);
         }
     }
-    __syncthreads();  // stage 0 visible
+    __syncthreads();  // stage 0 visible; H no longer read (its LDS becomes y staging)
 
+    bf16 *ys = reinterpret_cast<bf16 *>(hu) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
     const float Dh = D ? D[h] : 0.f;
 
-    auto scale = [&](f32x16 &z, float f) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) z[r] *= f;
-    };
-    // off-diagonal visit of column tile jt for the tiles in `mask` (bit t)
-    auto offdiag = [&](int jt, int buf, int mask, u32x4 (&cbt)[2][4]) {
+    // off-diagonal visit of column tile jt
+    auto offdiag = [&](int jt, const bf16 *sl, const u32x4 (&cbt)[4]) __attribute__((always_inline)) {
         const float f = ssd_exp(acs_s[jt * kJT + kJT - 1] - (jt > 0 ? acs_s[jt * kJT - 1] : 0.f));
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-            if (mask >> t & 1) {
-                scale(Z[t][0], f);
-                scale(Z[t][1], f);
-            }
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Z[pt][r] *= f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const u32x4 ah = tr_operand<true>(xh[buf], LDX, 16 * u, 32 * pt);
-                const u32x4 al = tr_operand<true>(xl[buf], LDX, 16 * u, 32 * pt);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    if (mask >> t & 1) {
-                        Z[t][pt] = mfma32(ah, cbt[t][2 * u], Z[t][pt]);
-                        Z[t][pt] = mfma32(al, cbt[t][2 * u], Z[t][pt]);
-                        Z[t][pt] = mfma32(ah, cbt[t][2 * u + 1], Z[t][pt]);
-                    }
+                const u32x4 ah = tr_operand<true>(sl + kJT * LDX, LDX, 16 * u, 32 * pt);
+                const u32x4 al = tr_operand<true>(sl + 2 * kJT * LDX, LDX, 16 * u, 32 * pt);
+                Z[pt] = mfma32(ah, cbt[2 * u], Z[pt]);
+                Z[pt] = mfma32(al, cbt[2 * u], Z[pt]);
+                Z[pt] = mfma32(ah, cbt[2 * u + 1], Z[pt]);
             }
     };
-    // diagonal visit of tile t (row tile ti == jt)
-    auto diag = [&](int t, int ti, int buf, const u32x4 (&cbd)[4]) {
+    // diagonal visit (jt == ti)
+    auto diag = [&](const bf16 *sl, const u32x4 (&cbd)[4]) __attribute__((always_inline)) {
         const float ai = acs_s[ti * kJT + il];
         const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * kJT - 1] : 0.f));
+        // rescale to exp(Acs_i) and add D x (x rows of this tile are this stage)
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                const u32x2 xr = *reinterpret_cast<const u32x2 *>(&xs[buf][il * LDX + p0]);
+                const u32x2 xr = *reinterpret_cast<const u32x2 *>(&sl[il * LDX + p0]);
                 const int r0 = 4 * rg;
-                Z[t][pt][r0 + 0] = Z[t][pt][r0 + 0] * rf + Dh * lo_bf16(xr[0]);
-                Z[t][pt][r0 + 1] = Z[t][pt][r0 + 1] * rf + Dh * hi_bf16(xr[0]);
-                Z[t][pt][r0 + 2] = Z[t][pt][r0 + 2] * rf + Dh * lo_bf16(xr[1]);
-                Z[t][pt][r0 + 3] = Z[t][pt][r0 + 3] * rf + Dh * hi_bf16(xr[1]);
+                Z[pt][r0 + 0] = Z[pt][r0 + 0] * rf + Dh * lo_bf16(xr[0]);
+                Z[pt][r0 + 1] = Z[pt][r0 + 1] * rf + Dh * hi_bf16(xr[0]);
+                Z[pt][r0 + 2] = Z[pt][r0 + 2] * rf + Dh * lo_bf16(xr[1]);
+                Z[pt][r0 + 3] = Z[pt][r0 + 3] * rf + Dh * hi_bf16(xr[1]);
             }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -657,50 +657,50 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             split8(m, mh, ml);
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const u32x4 xa = tr_operand<true>(xs[buf], LDX, 16 * u, 32 * pt);
-                Z[t][pt] = mfma32(xa, mh, Z[t][pt]);
-                Z[t][pt] = mfma32(xa, ml, Z[t][pt]);
+                const u32x4 xa = tr_operand<true>(sl, LDX, 16 * u, 32 * pt);
+                Z[pt] = mfma32(xa, mh, Z[pt]);
+                Z[pt] = mfma32(xa, ml, Z[pt]);
             }
         }
     };
-    // y rows of tile t (complete): each lane holds 4 consecutive p of row
-    // i = 32 ti + l%32 per register group, written as 8 bytes; the lane pair
-    // (l, l+32) covers 16 contiguous bytes and the 8 stores cover whole rows
-    const uint32_t yvoff = ((unsigned)il * xrs + 4u * g2) * 2u;
-    auto epilogue = [&](int t, int ti) {
-        const rsrc_t r = buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32) * xrs * 2u);
+    // y rows of the tile as bf16 via this wave's LDS rows, written as full
+    // 128-byte rows (8 lanes per row, 8 rows per store)
+    const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
+    auto epilogue = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
+                const int p0 = pt * 32 + 8 * rg + 4 * g2;
                 u32x2 o;
-                o[0] = pack_bf16x2(Z[t][pt][4 * rg + 0], Z[t][pt][4 * rg + 1]);
-                o[1] = pack_bf16x2(Z[t][pt][4 * rg + 2], Z[t][pt][4 * rg + 3]);
-                __builtin_amdgcn_raw_buffer_store_b64(o, r, yvoff + (pt * 32 + 8 * rg) * 2u, 0, 0);
+                o[0] = pack_bf16x2(Z[pt][4 * rg + 0], Z[pt][4 * rg + 1]);
+                o[1] = pack_bf16x2(Z[pt][4 * rg + 2], Z[pt][4 * rg + 3]);
+                *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
             }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
+            buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32 + 8 * kk) * xrs * 2u),
+                           yvoff);
+        }
     };
 
-    auto jstep = [&](int jt, auto par) {
-        constexpr int buf = decltype(par)::value;  // jt % 2: LDS buffer and C.B register set
+    auto jstep = [&](int jt, auto par) __attribute__((always_inline)) {
+        constexpr int cur = decltype(par)::value;  // jt % 2: LDS slot and stage registers
+        const bf16 *sl = sa + cur * SLOT;
         // unconditional prefetches (empty ranges past the end): the same loads
-        // are in flight on every path, so waits count exactly
-        load_stage(jt + 2, R[buf]);
-        load_cb(ti0, jt + 1, cbr[buf ^ 1][0]);
-        load_cb(ti1, jt + 1, cbr[buf ^ 1][1]);
-        // wave-uniform cases (ti0 < ti1)
-        if (jt < ti0) {
-            offdiag(jt, buf, 3, cbr[buf]);
-        } else if (jt == ti0) {
-            offdiag(jt, buf, 2, cbr[buf]);
-            diag(0, ti0, buf, cbr[buf][0]);
-        } else if (jt < ti1) {
-            offdiag(jt, buf, 2, cbr[buf]);
-        } else if (jt == ti1) {
-            diag(1, ti1, buf, cbr[buf][1]);
-        }
-        if (jt == ti0 + 1) epilogue(0, ti0);
-        if (jt == ti1 + 1) epilogue(1, ti1);
-        if (jt + 1 < NI) store_stage(jt + 1, buf ^ 1, R[buf ^ 1]);
+        // are in flight on every path, so waits count exactly.  The next C.B
+        // tile reuses this tile's registers once its MFMAs have read them.
+        load_stage(jt + 2, R[cur]);
+        if (jt < ti) offdiag(jt, sl, cbr);
+        else if (jt == ti) diag(sl, cbr);
+        load_cb(jt + 1, cbr);
+        // a finished tile is written one step later, off the diagonal step
+        if (jt == ti + 1) epilogue();
+        if (jt + 1 < NI) store_stage(jt + 1, sa + (cur ^ 1) * SLOT, R[cur ^ 1]);
         __syncthreads();
     };
 #pragma unroll 1
@@ -708,7 +708,7 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         jstep(jt, P0{});
         jstep(jt + 1, P1{});
     }
-    if (ti1 == NI - 1) epilogue(1, ti1);
+    if (ti == NI - 1) epilogue();
 }
 
 template <int Q, int N>
@@ -734,9 +734,12 @@ void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const voi
                    const float *D, const float *Acs, const float *states, const void *cb, void *y,
                    hipStream_t st) {
     const int64_t nb = s.B * s.T * s.H;
-    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), Q, 0, st>>>(
-        (const bf16 *)x, dt, (const bf16 *)Cm, D, Acs, states, (const u32x4 *)cb, (bf16 *)y, s.L,
-        (int)s.H, (int)s.G, (int)s.T, nb);
+    constexpr int NI = Q / 32;
+    const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
+    (void)Cm;  // C enters through the operand fragments the C.B kernel stored
+    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), Q * 2, 0, st>>>(
+        (const bf16 *)x, dt, D, Acs, states, (const u32x4 *)cb,
+        (const u32x4 *)cb + ntiles * 256, (bf16 *)y, s.L, (int)s.H, (int)s.G, (int)s.T, nb);
 }
 
 // The whole chunked scan in three launches: chunk states with the in-block
@@ -763,8 +766,12 @@ void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const fl
 }  // namespace
 
 bool mfma_supported(const ScanShape &s) {
+    // the kernels form byte offsets within one chunk (up to two stages past
+    // its end) in 32 bits: (Q + 64) rows of x/y, or of B/C, must stay below 2^31
+    const bool offsets32 = (s.Q + 64) * s.H * s.P * 2 < (int64_t(1) << 31) &&
+                           (s.Q + 64) * s.G * s.N * 2 < (int64_t(1) << 31);
     return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) &&
-           (s.Q == 64 || s.Q == 128 || s.Q == 256);
+           (s.Q == 64 || s.Q == 128 || s.Q == 256) && offsets32;
 }
 
 #define SSD_DISPATCH_QN(FN, ...)                                         \
@@ -786,8 +793,9 @@ void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
 }
 
 size_t chunk_cb_bytes(const ScanShape &s) {
+    // C.B tiles, then the C operand fragments (Q x N bf16 per (b, c, g))
     const int64_t ni = s.Q / 32;
-    return (size_t)(s.B * s.T * s.G * (ni * (ni + 1) / 2)) * 4096;
+    return (size_t)(s.B * s.T * s.G) * ((size_t)(ni * (ni + 1) / 2) * 4096 + (size_t)(s.Q * s.N * 2));
 }
 
 void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,

@@ -73,15 +73,17 @@ def r256(v):
 
 
 def test_chunk_scan_workspace_size(L):
-    # bf16, headdim 64, dstate 64/128, chunk 64/128/256: the MFMA kernels keep
-    # one 4 KB C.B tile per causal 32x32 tile pair of every (batch, chunk, group)
+    # bf16, headdim 64, dstate 64/128, chunk 64/128/256: the MFMA kernels keep,
+    # per (batch, chunk, group), one 4 KB C.B tile per causal 32x32 tile pair
+    # and the chunk's C rows as MFMA operands (chunk * dstate bf16)
     for chunk, ni in ((256, 8), (128, 4), (64, 2)):
         for dstate in (64, 128):
             st, n = cb_size(L, desc(chunk=chunk, dstate=dstate))
             T = -(-512 // chunk)
-            assert st == OK and n == r256(1 * T * 2 * (ni * (ni + 1) // 2) * 4096)
+            per = (ni * (ni + 1) // 2) * 4096 + chunk * dstate * 2
+            assert st == OK and n == r256(1 * T * 2 * per)
     # ragged last chunk counts as a chunk
-    assert cb_size(L, desc(seqlen=300, chunk=128)) == (OK, 3 * 2 * 10 * 4096)
+    assert cb_size(L, desc(seqlen=300, chunk=128)) == (OK, 3 * 2 * (10 * 4096 + 128 * 128 * 2))
     # shapes the generic kernels run need none
     assert cb_size(L, desc(dtype=0)) == (OK, 0)
     assert cb_size(L, desc(headdim=32)) == (OK, 0)
