@@ -431,7 +431,10 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // by all threads together; CB comes pre-split from the C.B tile kernel, and
 // the off-diagonal product takes three MFMAs (hi.hi, lo.hi, hi.lo).  The
 // diagonal tile applies exp(Acs_i - Acs_j) dt_j to the fp32 CB element by
-// element under the causal mask and multiplies raw x.
+// element under the causal mask and multiplies raw x; that masked matrix
+// (hi/lo) is built one step ahead by the wave of tile 0, which has no other
+// work after its own tile, and handed over through LDS, so the step's
+// critical path is MFMA work.
 //
 // Every global access is a whole-line wave access: x stages, H, the C
 // operand fragments and C.B tiles (1 KB each) from the C.B kernel, and y
@@ -464,6 +467,8 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     __shared__ __attribute__((aligned(16))) bf16 sa[2 * SLOT];
     __shared__ __attribute__((aligned(16))) float acs_s[Q];
     __shared__ __attribute__((aligned(16))) float dt_s[Q];
+    // masked diagonal matrix of the next diagonal tile: [buffer][u][hi/lo][lane]
+    __shared__ __attribute__((aligned(16))) u32x4 mdiag[2][4][64];
     const uint32_t lb = xcd_block();
     if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -531,6 +536,46 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         for (int k = 0; k < 4; ++k) o[k] = buffer_load16(r, cbvoff + k * 1024u);
     };
 
+    // masked diagonal matrix of row tile tt from its fp32 C.B tile: registers
+    // 8u+4v..+3 of this lane hold rows jl..jl+3, jl = 16u + 8v + 4(l/32);
+    // M[i][j] = CB[i][j] exp(Acs_i - Acs_j) dt_j for j <= i, as hi/lo pairs
+    // in o[2u] (hi) and o[2u+1] (lo).  Masked elements are computed anyway and
+    // replaced by 0 with a select (their exponent may be positive and their
+    // product not finite; the select discards it), so no branch diverges.
+    auto make_m = [&](int tt, const u32x4 (&cbd)[4], u32x4 (&o)[4]) __attribute__((always_inline)) {
+        const float ai = acs_s[tt * kJT + il];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float m[8];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int jl = 16 * u + 8 * v + 4 * g2;
+                const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[tt * kJT + jl]);
+                const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[tt * kJT + jl]);
+                const u32x4 cv = cbd[2 * u + v];
+                const float e0 = __uint_as_float(cv[0]) * ssd_exp(ai - aj.x) * dj.x;
+                const float e1 = __uint_as_float(cv[1]) * ssd_exp(ai - aj.y) * dj.y;
+                const float e2 = __uint_as_float(cv[2]) * ssd_exp(ai - aj.z) * dj.z;
+                const float e3 = __uint_as_float(cv[3]) * ssd_exp(ai - aj.w) * dj.w;
+                m[4 * v + 0] = jl + 0 <= il ? e0 : 0.f;
+                m[4 * v + 1] = jl + 1 <= il ? e1 : 0.f;
+                m[4 * v + 2] = jl + 2 <= il ? e2 : 0.f;
+                m[4 * v + 3] = jl + 3 <= il ? e3 : 0.f;
+            }
+            split8(m, o[2 * u], o[2 * u + 1]);
+        }
+    };
+    // the diagonal C.B tile (tt, tt) as four 16-byte operands of this lane
+    auto load_cbd = [&](int tt, u32x4 (&o)[4]) __attribute__((always_inline)) {
+        const int tile = tt * (tt + 1) / 2 + tt;
+        const rsrc_t r = buffer_rsrc_at(cbg, (tile + 1) * 4096u, tile * 4096u);
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) o[k2] = buffer_load16(r, cbvoff + k2 * 1024u);
+    };
+    auto store_m = [&](int mb, const u32x4 (&o)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) mdiag[mb][k2][lane] = o[k2];
+    };
     // ---- prologue: global loads in the order they are needed: acs/dt and H
     // (before the first barrier), C operands (state term), stages 0-1, C.B
     float acs_v = 0.f, dt_v = 0.f;
@@ -578,6 +623,17 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     }
     __syncthreads();  // acs_s, dt_s, H
     store_stage(0, sa, R[0]);
+    if (wave < 2) {  // masked diagonal matrices of tiles 0 and 1 (buffers 0, 1)
+        u32x4 cbd[4], mo[4];
+        if (wave == 0) {
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) cbd[k2] = cbr[k2];  // tile 0's C.B is its diagonal
+        } else {
+            load_cbd(1, cbd);
+        }
+        make_m(wave, cbd, mo);
+        store_m(wave, mo);
+    }
     // state term Z = H C_i^T
     f32x16 Z[2] = {zero16(), zero16()};
 #pragma unroll
@@ -615,10 +671,13 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                 Z[pt] = mfma32(ah, cbt[2 * u + 1], Z[pt]);
             }
     };
-    // diagonal visit (jt == ti)
-    auto diag = [&](const bf16 *sl, const u32x4 (&cbd)[4]) __attribute__((always_inline)) {
+    // diagonal visit (jt == ti) with M from LDS buffer mb
+    auto diag = [&](const bf16 *sl, int mb) __attribute__((always_inline)) {
         const float ai = acs_s[ti * kJT + il];
         const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * kJT - 1] : 0.f));
+        u32x4 mo[4];
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) mo[k2] = mdiag[mb][k2][lane];
         // rescale to exp(Acs_i) and add D x (x rows of this tile are this stage)
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
@@ -633,35 +692,13 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                 Z[pt][r0 + 3] = Z[pt][r0 + 3] * rf + Dh * hi_bf16(xr[1]);
             }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float m[8];
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                // registers 8u+4v..+3 hold rows jl..jl+3 of the tile
-                const int jl = 16 * u + 8 * v + 4 * g2;
-                const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[ti * kJT + jl]);
-                const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[ti * kJT + jl]);
-                const u32x4 cv = cbd[2 * u + v];
-                // computed for every element (the exponent clamped to <= 0 so
-                // masked ones stay finite), then selected: no divergent branch
-                const float e0 = __uint_as_float(cv[0]) * ssd_exp(fminf(ai - aj.x, 0.f)) * dj.x;
-                const float e1 = __uint_as_float(cv[1]) * ssd_exp(fminf(ai - aj.y, 0.f)) * dj.y;
-                const float e2 = __uint_as_float(cv[2]) * ssd_exp(fminf(ai - aj.z, 0.f)) * dj.z;
-                const float e3 = __uint_as_float(cv[3]) * ssd_exp(fminf(ai - aj.w, 0.f)) * dj.w;
-                m[4 * v + 0] = jl + 0 <= il ? e0 : 0.f;
-                m[4 * v + 1] = jl + 1 <= il ? e1 : 0.f;
-                m[4 * v + 2] = jl + 2 <= il ? e2 : 0.f;
-                m[4 * v + 3] = jl + 3 <= il ? e3 : 0.f;
-            }
-            u32x4 mh, ml;
-            split8(m, mh, ml);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 const u32x4 xa = tr_operand<true>(sl, LDX, 16 * u, 32 * pt);
-                Z[pt] = mfma32(xa, mh, Z[pt]);
-                Z[pt] = mfma32(xa, ml, Z[pt]);
+                Z[pt] = mfma32(xa, mo[2 * u], Z[pt]);
+                Z[pt] = mfma32(xa, mo[2 * u + 1], Z[pt]);
             }
-        }
     };
     // y rows of the tile as bf16 via this wave's LDS rows, written as full
     // 128-byte rows (8 lanes per row, 8 rows per store)
@@ -696,10 +733,19 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         // tile reuses this tile's registers once its MFMAs have read them.
         load_stage(jt + 2, R[cur]);
         if (jt < ti) offdiag(jt, sl, cbr);
-        else if (jt == ti) diag(sl, cbr);
+        else if (jt == ti) diag(sl, cur);
         load_cb(jt + 1, cbr);
         // a finished tile is written one step later, off the diagonal step
         if (jt == ti + 1) epilogue();
+        // tile 0's wave (done with its own tile) builds the masked diagonal
+        // matrix of tile jt+1 into buffer (jt+1) % 2, read last in step jt-1
+        // (before the barrier that ended it); the barrier below publishes it
+        if (wave == 0 && jt >= 1 && jt + 1 < NI) {
+            u32x4 cbd[4], mo[4];
+            load_cbd(jt + 1, cbd);
+            make_m(jt + 1, cbd, mo);
+            store_m(cur ^ 1, mo);
+        }
         if (jt + 1 < NI) store_stage(jt + 1, sa + (cur ^ 1) * SLOT, R[cur ^ 1]);
         __syncthreads();
     };
