@@ -257,12 +257,40 @@ def main():
         fn = Lean(torch, lib.ssd_step, ctypes.byref(sdesc), P_(state), P_(xs), P_(dts), P_(A),
                   P_(Bs), P_(Cs), P_(D), P_(yd))
         dms = time_launches(torch, fn, args.decode_steps, warmup=5)
+        # the same steps launched one by one from the host, for comparison
+        # with the graph-replayed (device-resident) loop above
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.decode_steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / args.decode_steps
         db_bytes = decode_bytes(db, H, P, N, 1)
         gbs = db_bytes / (dms * 1e-3) / 1e9
-        decode[f"batch{db}"] = {"us_per_step": round(dms * 1e3, 3), "GB_s": round(gbs, 1),
-                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                                "bytes_per_step": db_bytes, "note": "warm (state may be "
-                                "resident in the 256 MB Infinity Cache)"}
+        # K tokens per launch with the state kept in registers (ssd_step_multi)
+        K = 16
+        steps = [ds.next_step() for _ in range(K)]
+        xm, dtm, Bm_, Cm_ = (torch.stack([st[k] for st in steps], 1).to(dev).contiguous()
+                             for k in ("x", "dt", "B", "C"))
+        ym = torch.empty_like(xm)
+        fm = Lean(torch, lib.ssd_step_multi, ctypes.byref(sdesc), ctypes.c_int64(K), P_(state),
+                  P_(xm), P_(dtm), P_(A), P_(Bm_), P_(Cm_), P_(D), P_(ym))
+        mms = time_launches(torch, fm, max(10, args.decode_steps // K), warmup=3)
+        m_bytes = 2 * db * H * P * N * 4 + K * (decode_bytes(db, H, P, N, 1)
+                                                - 2 * db * H * P * N * 4)
+        decode[f"batch{db}"] = {
+            "us_per_step": round(dms * 1e3, 3), "GB_s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": db_bytes,
+            "eager_us_per_step": round(eager_ms * 1e3, 3),
+            "multi16_us_per_token": round(mms * 1e3 / K, 3),
+            "multi16_GB_s": round(m_bytes / (mms * 1e-3) / 1e9, 1),
+            "multi16_bytes_per_launch": m_bytes,
+            "note": "us_per_step: graph-replayed single steps; eager: the same launched one by "
+                    "one from the host; multi16: 16 tokens per ssd_step_multi launch (state "
+                    "read and written once); warm (state may be resident in the 256 MB "
+                    "Infinity Cache)"}
 
     out = {
         "metric": METRIC,

@@ -121,6 +121,23 @@ ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const f
                     const float *A, const void *B, const void *C, const float *D, void *y,
                     void *stream);
 
+/* nsteps consecutive decode tokens in one launch, for inputs that are all
+ * known up front (a short continuation of a cached sequence, draft tokens to
+ * verify): the same result as nsteps calls of ssd_step on the same stream,
+ * bit for bit, but the state is read and written once instead of once per
+ * token ("Compiler-First ...", §3 "Autoregressive cache", with the loop
+ * over tokens kept on the device).  Inputs use the prefill layout:
+ *   state [batch, nheads, headdim, dstate] fp32, read and updated in place
+ *   x     [batch, nsteps, nheads, headdim]  dtype
+ *   dt    [batch, nsteps, nheads]           fp32
+ *   A     [nheads] fp32                     D [nheads] fp32 or NULL
+ *   B, C  [batch, nsteps, ngroups, dstate]  dtype
+ *   y     [batch, nsteps, nheads, headdim]  dtype, written
+ * nsteps == 0 and batch == 0 are no-ops; nsteps < 0 is SSD_ERR_SHAPE. */
+ssd_status ssd_step_multi(const ssd_step_desc *d, int64_t nsteps, float *state, const void *x,
+                          const float *dt, const float *A, const void *B, const void *C,
+                          const float *D, void *y, void *stream);
+
 /* ------------------------------------------------- stages of the prefill scan
  * The four steps of ssd_scan_fwd, callable one at a time for stage checks.
  * Shapes as for ssd_scan_fwd; T = ceil(seqlen / chunk); chunk c covers tokens

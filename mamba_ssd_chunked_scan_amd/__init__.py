@@ -10,5 +10,5 @@ synthetic input generator used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
     SSDError, chunk_cb, chunk_cumsum, chunk_scan, chunk_scan_workspace_size, chunk_state, lib,
-    scan_fwd, state_passing, step, workspace_size,
+    scan_fwd, state_passing, step, step_multi, workspace_size,
 )

@@ -23,7 +23,7 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 
 # Every function include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
-           "ssd_step", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
+           "ssd_step", "ssd_step_multi", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan")
 
 
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [ctypes.c_size_t, _P]
         L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [_P] * 9
+        L.ssd_step_multi.argtypes = [ctypes.POINTER(StepDesc), ctypes.c_int64] + [_P] * 9
         L.ssd_chunk_cumsum.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 4
         L.ssd_chunk_state.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 6
         L.ssd_state_passing.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 5
@@ -215,6 +216,37 @@ def step(state, x, dt, A, B, C, D=None, y=None):
     st = lib().ssd_step(ctypes.byref(desc), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                         _ptr(C), _ptr(D), _ptr(y), _stream(dev))
     _check("ssd_step", st)
+    return y
+
+
+def step_multi(state, x, dt, A, B, C, D=None, y=None):
+    """nsteps decode tokens in one launch (inputs in the prefill layout: x
+    [batch, nsteps, nheads, headdim], dt [batch, nsteps, nheads], B/C
+    [batch, nsteps, ngroups, dstate]); ``state`` is updated in place.  Equal to
+    nsteps calls of :func:`step`."""
+    if state.dim() != 4 or x.dim() != 4 or B.dim() != 4:
+        raise ValueError("state [b,h,p,n], x [b,t,h,p], B/C [b,t,g,n] expected")
+    Bt, H, P, N = state.shape
+    T, G = x.shape[1], B.shape[2]
+    dev, io = state.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be device tensors")
+    _need(state, "state", (Bt, H, P, N), torch.float32, dev)
+    _need(x, "x", (Bt, T, H, P), io, dev)
+    _need(dt, "dt", (Bt, T, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (Bt, T, G, N), io, dev)
+    _need(C, "C", (Bt, T, G, N), io, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, io, dev)
+    desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
+    st = lib().ssd_step_multi(ctypes.byref(desc), T, _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
+                              _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
+    _check("ssd_step_multi", st)
     return y
 
 

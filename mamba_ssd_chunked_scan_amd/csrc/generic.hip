@@ -197,6 +197,18 @@ __device__ __forceinline__ void ld4(const Tin *p, int64_t i, float v[4]) {
     for (int k = 0; k < 4; ++k) v[k] = Elem<Tin>::ld(p, i + k);
 }
 
+// One token on this thread's 4 state elements: s <- r s + u B, returns the
+// partial C.s.  Written with explicit fused multiply-adds so that every
+// kernel using it performs the same operations in the same order.
+__device__ __forceinline__ float step_update(float4 &s, float r, float u, const float bv[4],
+                                             const float cv[4]) {
+    s.x = fmaf(r, s.x, u * bv[0]);
+    s.y = fmaf(r, s.y, u * bv[1]);
+    s.z = fmaf(r, s.z, u * bv[2]);
+    s.w = fmaf(r, s.w, u * bv[3]);
+    return fmaf(cv[3], s.w, fmaf(cv[2], s.z, fmaf(cv[1], s.y, cv[0] * s.x)));
+}
+
 template <typename Tin>
 __global__ void __launch_bounds__(256)
 k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
@@ -224,15 +236,194 @@ k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__rest
         float bv[4], cv[4];
         ld4(Bm, (b * G + g) * N + sub * 4, bv);
         ld4(Cm, (b * G + g) * N + sub * 4, cv);
-        s.x = r * s.x + u * bv[0];
-        s.y = r * s.y + u * bv[1];
-        s.z = r * s.z + u * bv[2];
-        s.w = r * s.w + u * bv[3];
+        part = step_update(s, r, u, bv, cv);
         *sp = s;
-        part = cv[0] * s.x + cv[1] * s.y + cv[2] * s.z + cv[3] * s.w;
     }
     for (int off = lpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-    if (active && sub == 0) Elem<Tin>::st(y, row, part + (D ? D[h] : 0.f) * xv);
+    if (active && sub == 0) Elem<Tin>::st(y, row, fmaf(D ? D[h] : 0.f, xv, part));
+}
+
+// nsteps consecutive decode tokens in one launch.  Same thread layout and
+// per-token arithmetic as k_step (so the result equals nsteps chained steps
+// bit for bit), but the thread's 4 state elements stay in registers across
+// the tokens: the state is read and written once per launch instead of once
+// per token.  Inputs are in the prefill layout ([B, nsteps, ...]); the next
+// token's inputs are loaded while the current one is applied.
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_step_multi(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
+             const float *__restrict__ A, const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
+             const float *__restrict__ D, Tin *__restrict__ y, int64_t rows, int64_t nsteps,
+             int H, int P, int N, int G, int lpr_log2) {
+    const int lpr = 1 << lpr_log2;
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gt >> lpr_log2;
+    const int sub = (int)(gt & (lpr - 1));
+    const bool active = row < rows;
+    // inactive lanes follow row 0's addresses so that every lane takes part
+    // in the row reductions; they load but never store
+    const int64_t rr = active ? row : 0;
+    const int64_t bh = rr / P;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int p = (int)(rr % P);
+    const int g = h / (H / G);
+    const float a = A[h];
+    const float Dh = D ? D[h] : 0.f;
+    // per-token strides in the [B, nsteps, ...] layouts
+    const int64_t xs = (int64_t)H * P, ds = H, bs = (int64_t)G * N;
+    const Tin *xp = x + (b * nsteps * H + h) * P + p;
+    const float *dp = dt + b * nsteps * H + h;
+    const Tin *bp = Bm + (b * nsteps * G + g) * N + sub * 4;
+    const Tin *cp = Cm + (b * nsteps * G + g) * N + sub * 4;
+    Tin *yp = y + (b * nsteps * H + h) * P + p;
+    float4 *sp = reinterpret_cast<float4 *>(state + rr * N) + sub;
+    float4 s = *sp;
+    float xv = 0.f, d = 0.f, bv[4], cv[4];
+    if (nsteps > 0) {
+        xv = Elem<Tin>::ld(xp, 0);
+        d = dp[0];
+        ld4(bp, 0, bv);
+        ld4(cp, 0, cv);
+    }
+    for (int64_t t = 0; t < nsteps; ++t) {
+        // next token's inputs (clamped to the last token: loaded, not used)
+        const int64_t tn = t + 1 < nsteps ? t + 1 : t;
+        const float xn = Elem<Tin>::ld(xp, tn * xs), dn = dp[tn * ds];
+        float bn[4], cn[4];
+        ld4(bp, tn * bs, bn);
+        ld4(cp, tn * bs, cn);
+        const float r = ssd_exp(d * a);
+        const float u = d * xv;
+        float part = step_update(s, r, u, bv, cv);
+        for (int off = lpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+        if (active && sub == 0) Elem<Tin>::st(yp, t * xs, fmaf(Dh, xv, part));
+        xv = xn;
+        d = dn;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bv[k] = bn[k];
+            cv[k] = cn[k];
+        }
+    }
+    if (active) *sp = s;
+}
+
+// k_step_multi for blocks whose rows all belong to one (b, h).  A lane keeps
+// 16 state elements of its row (L = N/16 lanes per row): the float4 groups
+// sub, sub+L, sub+2L, sub+3L of the N/4 groups that k_step spreads over N/4
+// lanes.  Adding those four partials as (g0 + g2) + (g1 + g3) and then
+// butterflying over the L lanes pairs the same values in the same order as
+// k_step's butterfly over N/4 lanes, so every token's y and the final state
+// are bit for bit those of chained k_step calls.  Per group of KC tokens the
+// block stages B and C of its group, x of its rows, the decay exp(dt*A) and
+// dt*x in LDS with one burst of loads, keeps y in LDS and writes it out
+// coalesced: the token loop makes no global memory access.
+template <typename Tin, int KC, int L>
+__global__ void __launch_bounds__(256)
+k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
+                 const float *__restrict__ dt, const float *__restrict__ A,
+                 const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
+                 const float *__restrict__ D, Tin *__restrict__ y, int64_t nsteps, int H, int P,
+                 int G) {
+    constexpr int N = 16 * L;
+    constexpr int RPB = 256 / L < 64 ? 256 / L : 64;  // rows per block
+    __shared__ float4 bs_[KC][N / 4], cs_[KC][N / 4];
+    __shared__ float xs_[KC][RPB], us_[KC][RPB], ys_[KC][RPB];
+    __shared__ float rs_[KC];
+    const int tid = threadIdx.x;
+    const int sub = tid % L, rl = tid / L;
+    const int64_t row0 = (int64_t)blockIdx.x * RPB;  // all RPB rows share (b, h)
+    const int64_t bh = row0 / P;
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const int p0 = (int)(row0 % P);
+    const int g = h / (H / G);
+    const float a = A[h];
+    const float Dh = D ? D[h] : 0.f;
+    const int64_t xst = (int64_t)H * P, bst = (int64_t)G * N;
+    const Tin *xb = x + (b * nsteps * H + h) * P + p0;
+    const float *db = dt + b * nsteps * H + h;
+    const Tin *bb = Bm + (b * nsteps * G + g) * N;
+    const Tin *cb = Cm + (b * nsteps * G + g) * N;
+    Tin *yb = y + (b * nsteps * H + h) * P + p0;
+    float4 *sp = reinterpret_cast<float4 *>(state + (row0 + rl) * N) + sub;
+    float4 s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = sp[j * L];
+    for (int64_t t0 = 0; t0 < nsteps; t0 += KC) {
+        const int kc = (int)min((int64_t)KC, nsteps - t0);
+        __syncthreads();  // the previous group's y has been written out
+        float *bsf = reinterpret_cast<float *>(bs_), *csf = reinterpret_cast<float *>(cs_);
+        for (int e = tid; e < kc * N; e += RPB * L) {
+            const int t = e / N, n = e - t * N;
+            bsf[e] = Elem<Tin>::ld(bb, (t0 + t) * bst + n);
+            csf[e] = Elem<Tin>::ld(cb, (t0 + t) * bst + n);
+        }
+        for (int e = tid; e < kc * RPB; e += RPB * L) {
+            const int t = e / RPB, r = e - t * RPB;
+            const float xv = Elem<Tin>::ld(xb, (t0 + t) * xst + r);
+            xs_[t][r] = xv;
+            us_[t][r] = db[(t0 + t) * H] * xv;
+        }
+        if (tid < kc) rs_[tid] = ssd_exp(db[(t0 + tid) * H] * a);
+        __syncthreads();
+        for (int t = 0; t < kc; ++t) {
+            const float r = rs_[t], u = us_[t][rl];
+            float q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 b4 = bs_[t][sub + j * L], c4 = cs_[t][sub + j * L];
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, cv[4] = {c4.x, c4.y, c4.z, c4.w};
+                q[j] = step_update(s[j], r, u, bv, cv);
+            }
+            float part = (q[0] + q[2]) + (q[1] + q[3]);
+#pragma unroll
+            for (int off = L >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+            if (sub == 0) ys_[t][rl] = fmaf(Dh, xs_[t][rl], part);
+        }
+        __syncthreads();
+        for (int e = tid; e < kc * RPB; e += RPB * L) {
+            const int t = e / RPB, r = e - t * RPB;
+            Elem<Tin>::st(yb, (t0 + t) * xst + r, ys_[t][r]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sp[j * L] = s[j];
+}
+
+template <typename Tin, int L>
+void launch_multi_lds(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                      const float *dt, const float *A, const void *Bm, const void *Cm,
+                      const float *D, void *y, hipStream_t st) {
+    constexpr int RPB = 256 / L < 64 ? 256 / L : 64;
+    const unsigned blocks = (unsigned)(s.B * s.H * s.P / RPB);
+    k_step_multi_lds<Tin, 16, L><<<blocks, RPB * L, 0, st>>>(
+        state, (const Tin *)x, dt, A, (const Tin *)Bm, (const Tin *)Cm, D, (Tin *)y, nsteps,
+        (int)s.H, (int)s.P, (int)s.G);
+}
+
+// Rows per block of k_step_multi_lds for a state size (0: not handled there).
+int multi_lds_rows(int64_t N) {
+    switch (N) {
+    case 16: case 32: case 64: return 64;
+    case 128: return 32;
+    case 256: return 16;
+    default: return 0;
+    }
+}
+
+template <typename Tin>
+void launch_multi_lds_n(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                        const float *dt, const float *A, const void *Bm, const void *Cm,
+                        const float *D, void *y, hipStream_t st) {
+    switch (s.N) {
+    case 16: launch_multi_lds<Tin, 1>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    case 32: launch_multi_lds<Tin, 2>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    case 64: launch_multi_lds<Tin, 4>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    case 128: launch_multi_lds<Tin, 8>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    default: launch_multi_lds<Tin, 16>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    }
 }
 
 }  // namespace
@@ -298,6 +489,32 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {
     if (n <= 0 || dst == src) return;
     k_copy_or_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, src, n);
+}
+
+void launch_step_multi(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                       const float *dt, const float *A, const void *Bm, const void *Cm,
+                       const float *D, void *y, hipStream_t st) {
+    const int64_t rows = s.B * s.H * s.P;
+    int lpr_log2 = 0;
+    while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
+    const int64_t threads = rows << lpr_log2;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const int rpb = multi_lds_rows(s.N);
+    if (rpb > 0 && s.P % rpb == 0) {  // each block's rows share one (b, h): stage in LDS
+        if (s.dtype == SSD_BF16)
+            launch_multi_lds_n<bf16>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st);
+        else
+            launch_multi_lds_n<float>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st);
+        return;
+    }
+    if (s.dtype == SSD_BF16)
+        k_step_multi<bf16><<<blocks, 256, 0, st>>>(
+            state, (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, (bf16 *)y, rows,
+            nsteps, (int)s.H, (int)s.P, (int)s.N, (int)s.G, lpr_log2);
+    else
+        k_step_multi<float><<<blocks, 256, 0, st>>>(
+            state, (const float *)x, dt, A, (const float *)Bm, (const float *)Cm, D, (float *)y,
+            rows, nsteps, (int)s.H, (int)s.P, (int)s.N, (int)s.G, lpr_log2);
 }
 
 void launch_step(const StepShape &s, float *state, const void *x, const float *dt,

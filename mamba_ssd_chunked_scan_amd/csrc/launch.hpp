@@ -40,6 +40,11 @@ void launch_step(const StepShape &s, float *state, const void *x, const float *d
                  const float *A, const void *Bm, const void *Cm, const float *D, void *y,
                  hipStream_t st);
 
+// nsteps decode tokens in one launch, inputs in the prefill layout.
+void launch_step_multi(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                       const float *dt, const float *A, const void *Bm, const void *Cm,
+                       const float *D, void *y, hipStream_t st);
+
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,

@@ -172,6 +172,23 @@ ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const f
     return after_launch();
 }
 
+ssd_status ssd_step_multi(const ssd_step_desc *d, int64_t nsteps, float *state, const void *x,
+                          const float *dt, const float *A, const void *B, const void *C,
+                          const float *D, void *y, void *stream) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                 d->dtype, d->reserved);
+    if (st != SSD_OK) return st;
+    if (nsteps < 0) return SSD_ERR_SHAPE;
+    if (d->batch == 0 || nsteps == 0) return SSD_OK;
+    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D});
+    if (st != SSD_OK) return st;
+    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
+    ssd::launch_step_multi(s, nsteps, state, x, dt, A, B, C, D, y, as_stream(stream));
+    return after_launch();
+}
+
 ssd_status ssd_chunk_cumsum(const ssd_scan_desc *d, const float *dt, const float *A,
                             float *Acs, void *stream) {
     ScanShape s;

@@ -194,6 +194,27 @@ def test_chunk_scan_workspace_errors(L):
         assert L.ssd_chunk_scan(ctypes.byref(d), *a, P16, need, None) == NULL
 
 
+def test_step_multi_errors(L):
+    d = sdesc()
+    ptrs = [P16] * 9   # state x dt A B C D y
+    assert L.ssd_step_multi(None, 4, *([P16] * 8), None) == NULL
+    assert L.ssd_step_multi(ctypes.byref(d), -1, *([P16] * 8), None) == SHAPE
+    for which in (0, 1, 2, 3, 4, 5, 7):
+        a = [P16] * 8
+        a[which] = None
+        assert L.ssd_step_multi(ctypes.byref(d), 4, *a, None) == NULL
+    for which in range(8):
+        a = [P16] * 8
+        a[which] = P_MIS
+        assert L.ssd_step_multi(ctypes.byref(d), 4, *a, None) == ALIGN
+    for kw, status in ((dict(nheads=6, ngroups=4), SHAPE), (dict(dstate=96), UNSUP),
+                       (dict(dtype=3), UNSUP), (dict(reserved=2), UNSUP)):
+        assert L.ssd_step_multi(ctypes.byref(sdesc(**kw)), 4, *([P16] * 8), None) == status
+    # nothing to do: no pointer is touched
+    assert L.ssd_step_multi(ctypes.byref(d), 0, *([None] * 8), None) == OK
+    assert L.ssd_step_multi(ctypes.byref(sdesc(batch=0)), 4, *([None] * 8), None) == OK
+
+
 def test_empty_batch_is_noop(L):
     d = desc(batch=0)
     # all pointers NULL: nothing is touched and nothing is launched

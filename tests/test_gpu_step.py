@@ -108,3 +108,126 @@ def test_decode_steps_match_prefill_on_gpu():
     assert rel_err(f64(torch.stack(ys, 1)), yo) <= TOL[torch.bfloat16]
     assert rel_err(f64(state), fo) <= TOL[torch.bfloat16]
     assert rel_err(f64(torch.stack(ys, 1)), f64(y)) <= 2 * TOL[torch.bfloat16]
+
+
+def _multi_inputs(Bt, T, H, P, N, G, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    state = torch.randn(Bt, H, P, N, generator=g) * 0.1
+    x = torch.randn(Bt, T, H, P, generator=g).to(dtype)
+    dt = torch.rand(Bt, T, H, generator=g) * 0.1
+    A = -torch.rand(H, generator=g) * 8
+    B = torch.randn(Bt, T, G, N, generator=g).to(dtype)
+    C = torch.randn(Bt, T, G, N, generator=g).to(dtype)
+    D = torch.randn(H, generator=g)
+    return state, x, dt, A, B, C, D
+
+
+@pytest.mark.parametrize("shape", [
+    # Bt, T, H, P, N, G, dtype
+    (1, 1, 4, 16, 16, 1, torch.float32),
+    (2, 7, 6, 5, 4, 3, torch.float32),
+    (3, 64, 8, 64, 128, 2, torch.bfloat16),
+    (2, 16, 4, 64, 256, 4, torch.bfloat16),
+    (1, 33, 80, 64, 128, 1, torch.bfloat16),
+    (2, 20, 3, 64, 16, 1, torch.float32),     # 64 rows per block, ragged token group
+    (2, 5, 2, 96, 32, 2, torch.float32),      # 32 rows per block, headdim 3 blocks
+    (1, 3, 2, 12, 32, 1, torch.bfloat16),     # headdim not a multiple of a block's rows
+])
+def test_step_multi_equals_chained_steps(shape):
+    """nsteps tokens in one launch: bit for bit the chained single steps, and
+    within tolerance of the oracle recurrence from the same state."""
+    Bt, T, H, P, N, G, dtype = shape
+    print(f"[case] step_multi {shape}", flush=True)
+    state, x, dt, A, B, C, D = _multi_inputs(Bt, T, H, P, N, G, dtype, seed=11 + T)
+    dv = [t.to(DEV) for t in (x, dt, A, B, C, D)]
+    xd, dtd, Ad, Bd, Cd, Dd = dv
+    s_multi = state.to(DEV)
+    y_multi = ssd.step_multi(s_multi, xd, dtd, Ad, Bd, Cd, Dd)
+    s_chain = state.to(DEV)
+    y_chain = torch.stack([
+        ssd.step(s_chain, xd[:, t].clone(), dtd[:, t].clone(), Ad,
+                 Bd[:, t].clone(), Cd[:, t].clone(), Dd) for t in range(T)], dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y_multi, y_chain)
+    assert torch.equal(s_multi, s_chain)
+    yo, fo = oracle.scan(x, dt, A, B, C, D, state)
+    assert rel_err(f64(y_multi), yo) <= TOL[dtype]
+    assert rel_err(f64(s_multi), fo) <= TOL[dtype]
+
+
+def test_step_multi_decode_workload_batch64():
+    """The 2.7B decode shape at batch 64, 32 tokens per launch, all rows
+    against the oracle."""
+    print("[case] step_multi batch 64", flush=True)
+    spec = synth.DECODE_WORKLOADS["decode_2p7b_b64"]
+    stream = synth.DecodeStream(spec)
+    steps = [stream.next_step() for _ in range(32)]
+    x = torch.stack([s["x"] for s in steps], dim=1)
+    dt = torch.stack([s["dt"] for s in steps], dim=1)
+    B = torch.stack([s["B"] for s in steps], dim=1)
+    C = torch.stack([s["C"] for s in steps], dim=1)
+    state0 = stream.state.clone()
+    sd = state0.to(DEV)
+    y = ssd.step_multi(sd, x.to(DEV), dt.to(DEV), stream.A.to(DEV), B.to(DEV), C.to(DEV),
+                       stream.D.to(DEV))
+    torch.cuda.synchronize()
+    yo, fo = oracle.scan(x, dt, stream.A, B, C, stream.D, state0)
+    assert rel_err(f64(y), yo) <= TOL[torch.bfloat16]
+    assert rel_err(f64(sd), fo) <= TOL[torch.bfloat16]
+
+
+def test_graph_captured_decode_chain():
+    """A chain of decode steps captured in one HIP graph (no host work between
+    tokens) reproduces the eager chain bit for bit on every replay, with eager
+    work on the stream between replays."""
+    print("[case] graph-captured decode", flush=True)
+    Bt, T, H, P, N, G = 2, 24, 8, 64, 128, 2
+    state, x, dt, A, B, C, D = _multi_inputs(Bt, T, H, P, N, G, torch.bfloat16, seed=5)
+    xd, dtd, Ad, Bd, Cd, Dd = (t.to(DEV) for t in (x, dt, A, B, C, D))
+    steps = [(xd[:, t].contiguous(), dtd[:, t].contiguous(), Bd[:, t].contiguous(),
+              Cd[:, t].contiguous()) for t in range(T)]
+    s_ref = state.to(DEV)
+    y_ref = torch.stack([ssd.step(s_ref, xs, ds, Ad, bs, cs, Dd) for xs, ds, bs, cs in steps], 1)
+    s_g = state.to(DEV)
+    ys = [torch.empty_like(y_ref[:, 0]) for _ in range(T)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t, (xs, ds, bs, cs) in enumerate(steps):
+            ssd.step(s_g, xs, ds, Ad, bs, cs, Dd, y=ys[t])
+    for rep in range(3):
+        s_g.copy_(state.to(DEV))
+        for yt in ys:
+            yt.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.stack(ys, 1), y_ref), f"replay {rep}"
+        assert torch.equal(s_g, s_ref), f"replay {rep}"
+
+
+def test_graph_captured_prefill():
+    """ssd_scan_fwd (three launches on the MFMA path) captured in a HIP graph
+    equals the eager call bit for bit on every replay."""
+    print("[case] graph-captured prefill", flush=True)
+    spec = synth.custom_spec(1, 1000, 16, 64, 128, 2, 256, "bf16", dt_rule="ranged",
+                             init="normal", seed=31)
+    d = to_dev(synth.scan_inputs(spec), DEV)
+    Bt, L, H, P, N, G = 1, 1000, 16, 64, 128, 2
+    y_ref, f_ref = ssd.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=256,
+                                init_state=d["init"])
+    ws = torch.empty(ssd.workspace_size(Bt, L, H, P, N, G, 256, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    y = torch.empty_like(y_ref)
+    fin = torch.empty_like(f_ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssd.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=256,
+                     init_state=d["init"], final_state=fin, workspace=ws, y=y)
+    for rep in range(3):
+        y.zero_()
+        fin.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
+        assert torch.equal(fin, f_ref), f"replay {rep}"
