@@ -23,6 +23,12 @@ Value recipes (synthetic stand-ins for real activations, no checkpoint needed):
                        describes ("Why You Need This");
   init state ~ N(0, 0.1) (standard deviation 0.1) or zero.
 Draw order is fixed: x, B, C, z, u, D, dt0, init.
+
+For the fused scan edges (dt bias, softplus and clamp applied inside the
+kernels, output gate silu(g)), scan_edge_inputs hands over the raw values
+instead of the activated dt: dt_raw = z, dt_bias_h = softplus^-1(dt0_h), and a
+gate g ~ N(0, 1) of x's shape, drawn after init.  Which activation to apply is
+the caller's business; this module applies none to them.
 """
 from __future__ import annotations
 
@@ -34,7 +40,7 @@ import torch
 
 __all__ = [
     "ScanSpec", "DecodeSpec", "WORKLOADS", "DECODE_WORKLOADS", "scan_inputs",
-    "DecodeStream", "custom_spec",
+    "DecodeStream", "custom_spec", "scan_edge_inputs", "edge_decode_inputs",
 ]
 
 
@@ -122,6 +128,50 @@ def _dt(rng_z: np.ndarray, rule: str, dt0: np.ndarray | None) -> np.ndarray:
 
 def scan_inputs(spec: ScanSpec, seed: int | None = None) -> dict:
     """CPU tensors for one prefill call: x, dt, A, B, C, D, init (None when zero)."""
+    return _scan_draw(spec, seed)[0]
+
+
+def scan_edge_inputs(spec: ScanSpec, seed: int | None = None) -> dict:
+    """scan_inputs plus the raw edge inputs: dt_raw [B, L, H] fp32 (the z of
+    the dt recipe, before any bias or activation), dt_bias [H] fp32 =
+    softplus^-1(dt0), and gate [B, L, H, P] in the storage dtype."""
+    out, rng, z, dt0 = _scan_draw(spec, seed)
+    g = rng.standard_normal((spec.batch, spec.seqlen, spec.nheads, spec.headdim),
+                            dtype=np.float32)
+    out["dt_raw"] = torch.from_numpy(z)
+    out["dt_bias"] = torch.from_numpy(np.log(np.expm1(dt0)).astype(np.float32))
+    out["gate"] = _storage(g, spec.dtype)
+    return out
+
+
+def edge_decode_inputs(batch, nsteps, nheads, headdim, dstate, ngroups, dtype, seed) -> dict:
+    """Raw inputs of nsteps decode tokens with fused edges, prefill layout:
+    state, x, dt_raw, A, B, C, D, dt_bias, gate (the recipes above)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    H, P, N = nheads, headdim, dstate
+    u = rng.uniform(0.0, math.log(16.0), size=H)
+    D = rng.standard_normal(H)
+    dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(0.1), size=H))
+    state = rng.standard_normal((batch, H, P, N), dtype=np.float32) * np.float32(0.1)
+    x = rng.standard_normal((batch, nsteps, H, P), dtype=np.float32)
+    Bm = rng.standard_normal((batch, nsteps, ngroups, N), dtype=np.float32)
+    Cm = rng.standard_normal((batch, nsteps, ngroups, N), dtype=np.float32)
+    z = rng.standard_normal((batch, nsteps, H), dtype=np.float32)
+    g = rng.standard_normal((batch, nsteps, H, P), dtype=np.float32)
+    return {
+        "state": torch.from_numpy(state),
+        "x": _storage(x, dtype),
+        "dt_raw": torch.from_numpy(z),
+        "A": torch.from_numpy((-np.exp(u)).astype(np.float32)),
+        "B": _storage(Bm, dtype),
+        "C": _storage(Cm, dtype),
+        "D": torch.from_numpy(D.astype(np.float32)),
+        "dt_bias": torch.from_numpy(np.log(np.expm1(dt0)).astype(np.float32)),
+        "gate": _storage(g, dtype),
+    }
+
+
+def _scan_draw(spec: ScanSpec, seed: int | None):
     rng = np.random.Generator(np.random.PCG64(spec.seed if seed is None else seed))
     Bt, L, H, P, N, G = spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate, spec.ngroups
     x = rng.standard_normal((Bt, L, H, P), dtype=np.float32)
@@ -145,7 +195,7 @@ def scan_inputs(spec: ScanSpec, seed: int | None = None) -> dict:
         "C": _storage(Cm, spec.dtype),
         "D": torch.from_numpy(D.astype(np.float32)),
         "init": init,
-    }
+    }, rng, z, dt0
 
 
 class DecodeStream:
