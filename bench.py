@@ -160,7 +160,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--calibrate", action="store_true",
                     help="end with a plain 256 MiB device copy (twice), the known-size kernel "
                          "that hardware byte counters are scaled by")
@@ -194,18 +194,34 @@ def main():
     call = Lean(torch, lib.ssd_scan_fwd, dref, P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]),
                 P_(d["C"]), P_(d["D"]), P_(d["init"]), P_(y), P_(fin), P_(ws), ws.numel())
 
-    # ---- timed prefill steps: K back-to-back C-ABI calls from a lean host loop
+    # ---- timed prefill steps: K back-to-back C-ABI calls from a lean host loop,
+    # with a HIP event between calls for the per-call median and minimum
     for _ in range(args.warmup):
         call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record()
+    for i in range(args.steps):
         call()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     ms = elapsed * 1e3 / args.steps
     tokens_per_s = Bt * L * args.steps / elapsed
     graph_ms = time_launches(torch, call, max(10, args.steps))
+
+    # ---- the same call with the fused edges on (dt bias + softplus + clamp
+    # in the first kernel, y * silu(z) in the output store)
+    einp = synth.scan_edge_inputs(spec)
+    ed = {k: einp[k].to(dev).contiguous() for k in ("dt_raw", "dt_bias", "gate")}
+    edges = binding.Edges(ed["dt_bias"].data_ptr(), ed["gate"].data_ptr(), 1e-3, 0.1, 1, 1)
+    ye = torch.empty_like(y)
+    call_edges = Lean(torch, lib.ssd_scan_fwd_ex, dref, ctypes.byref(edges), P_(d["x"]),
+                      P_(ed["dt_raw"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
+                      P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
+    edges_ms = time_launches(torch, call_edges, max(10, args.steps))
 
     # ---- per-stage launch times (HIP events around graph replays)
     Tn = spec.nchunks
@@ -243,8 +259,23 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     call_gbs = bytes_["call"] / (ms * 1e-3) / 1e9
 
+    # ---- plain device copy (1 GiB read + 1 GiB written): the attainable HBM rate
+    csrc_ = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst_ = torch.empty_like(csrc_)
+    cdst_.copy_(csrc_)
+    torch.cuda.synchronize()
+    ca, cb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record()
+    for _ in range(10):
+        cdst_.copy_(csrc_)
+    cb_.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc_.numel() * 4 * 10 / (ca.elapsed_time(cb_) * 1e-3) / 1e9
+    del csrc_, cdst_
+
     # ---- decode steps
     decode = {}
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     for db in (1, 64):
         dspec = synth.DecodeSpec(f"decode_2p7b_b{db}", db, H, P, N, 1, 1, "bf16", 5)
         ds = synth.DecodeStream(dspec)
@@ -267,6 +298,18 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / args.decode_steps
+        # cold: a 512 MB write evicts the state from L2 and the Infinity Cache
+        # before each step; events bracket the step launch alone
+        n_cold = 50
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_cold)]
+        for ca0, ca1 in cev:
+            flush.fill_(0.0)
+            ca0.record()
+            fn()
+            ca1.record()
+        torch.cuda.synchronize()
+        cold_ms = sorted(a.elapsed_time(b) for a, b in cev)[n_cold // 2]
         db_bytes = decode_bytes(db, H, P, N, 1)
         gbs = db_bytes / (dms * 1e-3) / 1e9
         # K tokens per launch with the state kept in registers (ssd_step_multi)
@@ -284,13 +327,17 @@ def main():
             "us_per_step": round(dms * 1e3, 3), "GB_s": round(gbs, 1),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": db_bytes,
             "eager_us_per_step": round(eager_ms * 1e3, 3),
+            "cold_us_per_step_median": round(cold_ms * 1e3, 3),
+            "cold_GB_s": round(db_bytes / (cold_ms * 1e-3) / 1e9, 1),
             "multi16_us_per_token": round(mms * 1e3 / K, 3),
             "multi16_GB_s": round(m_bytes / (mms * 1e-3) / 1e9, 1),
             "multi16_bytes_per_launch": m_bytes,
-            "note": "us_per_step: graph-replayed single steps; eager: the same launched one by "
-                    "one from the host; multi16: 16 tokens per ssd_step_multi launch (state "
-                    "read and written once); warm (state may be resident in the 256 MB "
-                    "Infinity Cache)"}
+            "note": f"us_per_step: {args.decode_steps} graph-replayed single steps, warm (the "
+                    "state may be resident in the 256 MB Infinity Cache); eager: the same "
+                    "launched one by one from the host; cold: median over 50 steps each "
+                    "after a 512 MB cache-evicting write, events around the step alone; "
+                    "multi16: 16 tokens per ssd_step_multi launch (state read and written "
+                    "once)"}
 
     out = {
         "metric": METRIC,
@@ -311,11 +358,17 @@ def main():
                    "global_batch": Bt, "seq_len": L, "parallelism": "single GPU"},
         "prefill": {"tflops_causal": round(tflops, 2),
                     "us_per_call_graph": round(graph_ms * 1e3, 2),
+                    "us_per_call_median": round(per_call[len(per_call) // 2] * 1e3, 2),
+                    "us_per_call_min": round(per_call[0] * 1e3, 2),
+                    "us_per_call_graph_fused_edges": round(edges_ms * 1e3, 2),
                     "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "hbm_GB_s_algorithmic": round(call_gbs, 1),
                     "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),
                     "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()}},
         "decode": decode,
+        "copy_GB_s": round(copy_gbs, 1),
+        "frac_of_copy": {f"prefill_{dom}": round(dom_gbs / copy_gbs, 4),
+                         "decode_batch64": round(decode["batch64"]["GB_s"] / copy_gbs, 4)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4),

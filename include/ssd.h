@@ -53,7 +53,7 @@ typedef enum ssd_status {
     SSD_ERR_NULL_PTR = 1,    /* a required pointer is NULL                       */
     SSD_ERR_SHAPE = 2,       /* negative/zero dimension, nheads % ngroups != 0   */
     SSD_ERR_UNSUPPORTED = 3, /* chunk, headdim or dstate outside the limits below,
-                                unknown dtype                                    */
+                                unknown dtype, or dt_limit with dt_min > dt_max  */
     SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     SSD_ERR_WORKSPACE = 5,   /* workspace smaller than its *_workspace_size      */
     SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch      */
@@ -81,7 +81,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -108,6 +108,41 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         const float *A, const void *B, const void *C, const float *D,
                         const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------- fused scan edges */
+
+/* The elementwise steps that surround the scan in a Mamba block, fused into
+ * the scan's own kernels (the pyshine "Mamba" repository tour, "Why You Need
+ * This": the block feeds the scan softplus(dt + dt_bias), with the bias set so
+ * that the result starts between dt_min and dt_max, and the scan kernels
+ * optionally gate their output with z).
+ *   dt_bias     [nheads] fp32, added to every dt before the activation, or NULL
+ *   dt_softplus 1: dt <- softplus(dt + bias) = log(1 + exp(dt + bias));
+ *               0: dt <- dt + bias
+ *   dt_limit    1: the activated dt is then clamped to [dt_min, dt_max]
+ *               (dt_min <= dt_max required); 0: no clamp
+ *   z           gate with the layout and dtype of x, or NULL: every output is
+ *               multiplied by silu(z) = z / (1 + exp(-z)) in fp32 before its
+ *               single rounding to the output dtype
+ * The step size the recurrence uses is the activated dt, everywhere dt enters
+ * (decay and input weight).  A NULL ssd_edges pointer, or one with every field
+ * zero / NULL, is the plain operation. */
+typedef struct ssd_edges {
+    const float *dt_bias;
+    const void *z;
+    float dt_min, dt_max;
+    int32_t dt_softplus;
+    int32_t dt_limit;
+} ssd_edges;
+
+/* ssd_scan_fwd with the edges above (edges may be NULL).  dt here is the raw
+ * pre-activation value; the first kernel to read it writes the activated dt
+ * into the workspace for the later ones.  Workspace as for ssd_scan_fwd. */
+ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const void *x,
+                           const float *dt, const float *A, const void *B, const void *C,
+                           const float *D, const float *init_state, void *y,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* ------------------------------------------------------------- decode step */
 
@@ -137,6 +172,17 @@ ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const f
 ssd_status ssd_step_multi(const ssd_step_desc *d, int64_t nsteps, float *state, const void *x,
                           const float *dt, const float *A, const void *B, const void *C,
                           const float *D, void *y, void *stream);
+
+/* ssd_step and ssd_step_multi with the fused edges (edges may be NULL); z has
+ * the layout of x.  ssd_step_multi_ex equals nsteps calls of ssd_step_ex bit
+ * for bit, as without edges. */
+ssd_status ssd_step_ex(const ssd_step_desc *d, const ssd_edges *edges, float *state,
+                       const void *x, const float *dt, const float *A, const void *B,
+                       const void *C, const float *D, void *y, void *stream);
+ssd_status ssd_step_multi_ex(const ssd_step_desc *d, const ssd_edges *edges, int64_t nsteps,
+                             float *state, const void *x, const float *dt, const float *A,
+                             const void *B, const void *C, const float *D, void *y,
+                             void *stream);
 
 /* ------------------------------------------------- stages of the prefill scan
  * The four steps of ssd_scan_fwd, callable one at a time for stage checks.

@@ -24,7 +24,8 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 # Every function include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
            "ssd_step", "ssd_step_multi", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
-           "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan")
+           "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
+           "ssd_step_ex", "ssd_step_multi_ex")
 
 
 class ScanDesc(ctypes.Structure):
@@ -40,6 +41,13 @@ class StepDesc(ctypes.Structure):
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
                 ("ngroups", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class Edges(ctypes.Structure):
+    """ssd_edges: the dt activation and output gate fused into the scan."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("dt_softplus", ctypes.c_int32), ("dt_limit", ctypes.c_int32)]
 
 
 class SSDError(RuntimeError):
@@ -78,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.ssd_chunk_cb.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 3 + [ctypes.c_size_t, _P]
         L.ssd_chunk_scan.argtypes = ([ctypes.POINTER(ScanDesc)] + [_P] * 9
                                      + [ctypes.c_size_t, _P])
+        L.ssd_scan_fwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
+                                      + [_P] * 10 + [ctypes.c_size_t, _P])
+        L.ssd_step_ex.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(Edges)] + [_P] * 9
+        L.ssd_step_multi_ex.argtypes = ([ctypes.POINTER(StepDesc), ctypes.POINTER(Edges),
+                                         ctypes.c_int64] + [_P] * 9)
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -156,13 +169,40 @@ def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype
     return n.value
 
 
+def _edges(x, H, dt_bias, dt_softplus, dt_limit, z):
+    """An Edges struct for the fused dt activation / output gate, or None
+    when none is requested (the plain operation)."""
+    if dt_bias is None and not dt_softplus and dt_limit is None and z is None:
+        return None
+    e = Edges()
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", (H,), torch.float32, x.device)
+        e.dt_bias = dt_bias.data_ptr()
+    if z is not None:
+        _need(z, "z", x.shape, x.dtype, x.device)
+        e.z = z.data_ptr()
+    e.dt_softplus = 1 if dt_softplus else 0
+    if dt_limit is not None:
+        lo, hi = dt_limit
+        e.dt_min, e.dt_max, e.dt_limit = float(lo), float(hi), 1
+    return e
+
+
+def _eref(e):
+    return None if e is None else ctypes.byref(e)
+
+
 def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
-             return_final_state: bool = True, final_state=None, workspace=None, y=None):
+             return_final_state: bool = True, final_state=None, workspace=None, y=None,
+             dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None):
     """Chunked SSD scan.  Returns (y, final_state); final_state is None when not requested.
 
     ``final_state`` may be a preallocated [batch, nheads, headdim, dstate] fp32
     tensor (it may be ``init_state`` itself); ``workspace`` a uint8 device tensor
     of at least :func:`workspace_size` bytes; ``y`` a preallocated output.
+    Fused edges: ``dt_bias`` [nheads] fp32 is added to dt, ``dt_softplus``
+    applies softplus, ``dt_limit`` = (lo, hi) clamps the result; ``z`` (x's
+    shape and dtype) gates the output, y * silu(z).
     """
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
     dev = x.device
@@ -184,15 +224,18 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < n.value or workspace.device != dev:
         raise ValueError(f"workspace needs {n.value} bytes on {dev}")
-    st = lib().ssd_scan_fwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                            _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
-                            _ptr(workspace), workspace.numel(), _stream(dev))
-    _check("ssd_scan_fwd", st)
+    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    st = lib().ssd_scan_fwd_ex(ctypes.byref(desc), _eref(e), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("ssd_scan_fwd_ex", st)
     return y, final_state
 
 
-def step(state, x, dt, A, B, C, D=None, y=None):
-    """One decode token; ``state`` [batch, nheads, headdim, dstate] fp32 is updated in place."""
+def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,
+         dt_limit=None, z=None):
+    """One decode token; ``state`` [batch, nheads, headdim, dstate] fp32 is updated in place.
+    Fused edges as for :func:`scan_fwd` (``z`` has x's shape)."""
     if state.dim() != 4 or x.dim() != 3 or B.dim() != 3:
         raise ValueError("state [b,h,p,n], x [b,h,p], B/C [b,g,n] expected")
     Bt, H, P, N = state.shape
@@ -213,17 +256,19 @@ def step(state, x, dt, A, B, C, D=None, y=None):
     else:
         _need(y, "y", x.shape, io, dev)
     desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
-    st = lib().ssd_step(ctypes.byref(desc), _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                        _ptr(C), _ptr(D), _ptr(y), _stream(dev))
-    _check("ssd_step", st)
+    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    st = lib().ssd_step_ex(ctypes.byref(desc), _eref(e), _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
+                           _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
+    _check("ssd_step_ex", st)
     return y
 
 
-def step_multi(state, x, dt, A, B, C, D=None, y=None):
+def step_multi(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,
+               dt_limit=None, z=None):
     """nsteps decode tokens in one launch (inputs in the prefill layout: x
     [batch, nsteps, nheads, headdim], dt [batch, nsteps, nheads], B/C
     [batch, nsteps, ngroups, dstate]); ``state`` is updated in place.  Equal to
-    nsteps calls of :func:`step`."""
+    nsteps calls of :func:`step` (fused edges likewise)."""
     if state.dim() != 4 or x.dim() != 4 or B.dim() != 4:
         raise ValueError("state [b,h,p,n], x [b,t,h,p], B/C [b,t,g,n] expected")
     Bt, H, P, N = state.shape
@@ -244,9 +289,10 @@ def step_multi(state, x, dt, A, B, C, D=None, y=None):
     else:
         _need(y, "y", x.shape, io, dev)
     desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
-    st = lib().ssd_step_multi(ctypes.byref(desc), T, _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
-                              _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
-    _check("ssd_step_multi", st)
+    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    st = lib().ssd_step_multi_ex(ctypes.byref(desc), _eref(e), T, _ptr(state), _ptr(x), _ptr(dt),
+                                 _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
+    _check("ssd_step_multi_ex", st)
     return y
 
 

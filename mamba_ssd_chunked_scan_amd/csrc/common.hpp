@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace ssd {
 
 constexpr int kWave = 64;
@@ -49,6 +51,28 @@ template <> struct Elem<bf16> {
 // the fp32 range flush to 0, which is the correct limit.
 __device__ __forceinline__ float ssd_exp(float v) {
     return __builtin_amdgcn_exp2f(v * 1.4426950408889634f);
+}
+
+// log(1 + e^v).  Above 20, e^-v is below half an ulp of v, so v itself is the
+// correctly rounded value (and e^v would overflow near 88).
+__device__ __forceinline__ float softplus_f(float v) {
+    return v > 20.f ? v : log1pf(expf(v));
+}
+
+// The dt activation (DtAct, launch.hpp); all fields zero does no arithmetic.
+__device__ __forceinline__ float act_dt(const DtAct &a, float d, int h) {
+    if (a.bias) d += a.bias[h];
+    if (a.softplus) d = softplus_f(d);
+    if (a.limit) d = fminf(fmaxf(d, a.lo), a.hi);
+    return d;
+}
+
+// The output gate silu(z) = z / (1 + e^-z), with the hardware base-2
+// exponential and reciprocal (each within ~1 ulp; the gate's error is a few
+// fp32 ulps, far below the output's rounding).  For z -> -inf, e^-z
+// overflows to inf and the reciprocal to 0: the correct limit -0.
+__device__ __forceinline__ float silu_f(float z) {
+    return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -21,10 +21,13 @@ namespace {
 // Acs[b,h,t] = within-chunk inclusive cumsum of dt*A.  One block per
 // (batch, chunk) and 4 heads, one wave per head: each lane holds Q/64
 // consecutive tokens (summed sequentially), and the lane totals are combined
-// with a wave prefix scan.  All products and sums are fp32.
+// with a wave prefix scan.  All products and sums are fp32.  With an active
+// dt activation the activated dt is used and, when dt_out is given, written
+// there (same layout as dt) for the later stages.
 __global__ void __launch_bounds__(256)
 k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
-               float *__restrict__ Acs, int64_t L, int H, int Q, int T) {
+               float *__restrict__ Acs, int64_t L, int H, int Q, int T, DtAct act,
+               float *__restrict__ dt_out) {
     const int64_t b = blockIdx.x / T;
     const int c = blockIdx.x % T;
     const int lane = threadIdx.x & 63;
@@ -38,7 +41,13 @@ k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = lane * E + k;
-        v[k] = (k < E && i < q) ? dt[(b * L + t0 + i) * H + h] * a : 0.f;
+        v[k] = 0.f;
+        if (k < E && i < q) {
+            const int64_t di = (b * L + t0 + i) * H + h;
+            const float d = act_dt(act, dt[di], h);
+            if (dt_out) dt_out[di] = d;
+            v[k] = d * a;
+        }
     }
     float run = 0.f;
 #pragma unroll
@@ -126,8 +135,9 @@ __global__ void __launch_bounds__(256)
 k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
                      const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
                      const float *__restrict__ D, const float *__restrict__ Acs,
-                     const float *__restrict__ states, Tin *__restrict__ y, int64_t L, int H,
-                     int P, int N, int G, int Q, int T) {
+                     const float *__restrict__ states, Tin *__restrict__ y,
+                     const Tin *__restrict__ z, int64_t L, int H, int P, int N, int G, int Q,
+                     int T) {
     __shared__ float Ms[kScanRows][257];
     __shared__ float Cs[kScanRows][257];
     __shared__ float acs_s[256];
@@ -177,7 +187,8 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
         const float *hr = Hc + (int64_t)p * N;
         for (int n = 0; n < N; ++n) off += Cs[ii][n] * hr[n];
         const int64_t xi = ((b * L + t0 + i) * H + h) * P + p;
-        const float yv = acc + ssd_exp(acs_s[i]) * off + Dh * Elem<Tin>::ld(x, xi);
+        float yv = acc + ssd_exp(acs_s[i]) * off + Dh * Elem<Tin>::ld(x, xi);
+        if (z) yv *= silu_f(Elem<Tin>::ld(z, xi));
         Elem<Tin>::st(y, xi, yv);
     }
 }
@@ -214,7 +225,7 @@ __global__ void __launch_bounds__(256)
 k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
        const float *__restrict__ A, const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
        const float *__restrict__ D, Tin *__restrict__ y, int64_t rows, int H, int P, int N,
-       int G, int lpr_log2) {
+       int G, int lpr_log2, DtAct act, const Tin *__restrict__ z) {
     const int lpr = 1 << lpr_log2;
     const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = gt >> lpr_log2;
@@ -227,7 +238,7 @@ k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__rest
         h = (int)(bh % H);
         const int64_t b = bh / H;
         const int g = h / (H / G);
-        const float d = dt[b * H + h];
+        const float d = act_dt(act, dt[b * H + h], h);
         const float r = ssd_exp(d * A[h]);
         xv = Elem<Tin>::ld(x, row);
         const float u = d * xv;
@@ -240,7 +251,11 @@ k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__rest
         *sp = s;
     }
     for (int off = lpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-    if (active && sub == 0) Elem<Tin>::st(y, row, fmaf(D ? D[h] : 0.f, xv, part));
+    if (active && sub == 0) {
+        float yv = fmaf(D ? D[h] : 0.f, xv, part);
+        if (z) yv *= silu_f(Elem<Tin>::ld(z, row));
+        Elem<Tin>::st(y, row, yv);
+    }
 }
 
 // nsteps consecutive decode tokens in one launch.  Same thread layout and
@@ -254,7 +269,7 @@ __global__ void __launch_bounds__(256)
 k_step_multi(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
              const float *__restrict__ A, const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
              const float *__restrict__ D, Tin *__restrict__ y, int64_t rows, int64_t nsteps,
-             int H, int P, int N, int G, int lpr_log2) {
+             int H, int P, int N, int G, int lpr_log2, DtAct act, const Tin *__restrict__ z) {
     const int lpr = 1 << lpr_log2;
     const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = gt >> lpr_log2;
@@ -277,19 +292,20 @@ k_step_multi(float *__restrict__ state, const Tin *__restrict__ x, const float *
     const Tin *bp = Bm + (b * nsteps * G + g) * N + sub * 4;
     const Tin *cp = Cm + (b * nsteps * G + g) * N + sub * 4;
     Tin *yp = y + (b * nsteps * H + h) * P + p;
+    const Tin *zp = z ? z + (b * nsteps * H + h) * P + p : nullptr;
     float4 *sp = reinterpret_cast<float4 *>(state + rr * N) + sub;
     float4 s = *sp;
     float xv = 0.f, d = 0.f, bv[4], cv[4];
     if (nsteps > 0) {
         xv = Elem<Tin>::ld(xp, 0);
-        d = dp[0];
+        d = act_dt(act, dp[0], h);
         ld4(bp, 0, bv);
         ld4(cp, 0, cv);
     }
     for (int64_t t = 0; t < nsteps; ++t) {
         // next token's inputs (clamped to the last token: loaded, not used)
         const int64_t tn = t + 1 < nsteps ? t + 1 : t;
-        const float xn = Elem<Tin>::ld(xp, tn * xs), dn = dp[tn * ds];
+        const float xn = Elem<Tin>::ld(xp, tn * xs), dn = act_dt(act, dp[tn * ds], h);
         float bn[4], cn[4];
         ld4(bp, tn * bs, bn);
         ld4(cp, tn * bs, cn);
@@ -297,7 +313,11 @@ k_step_multi(float *__restrict__ state, const Tin *__restrict__ x, const float *
         const float u = d * xv;
         float part = step_update(s, r, u, bv, cv);
         for (int off = lpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
-        if (active && sub == 0) Elem<Tin>::st(yp, t * xs, fmaf(Dh, xv, part));
+        if (active && sub == 0) {
+            float yv = fmaf(Dh, xv, part);
+            if (z) yv *= silu_f(Elem<Tin>::ld(zp, t * xs));
+            Elem<Tin>::st(yp, t * xs, yv);
+        }
         xv = xn;
         d = dn;
 #pragma unroll
@@ -325,7 +345,7 @@ k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
                  const float *__restrict__ dt, const float *__restrict__ A,
                  const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
                  const float *__restrict__ D, Tin *__restrict__ y, int64_t nsteps, int H, int P,
-                 int G) {
+                 int G, DtAct act, const Tin *__restrict__ z) {
     constexpr int N = 16 * L;
     constexpr int RPB = 256 / L < 64 ? 256 / L : 64;  // rows per block
     __shared__ float4 bs_[KC][N / 4], cs_[KC][N / 4];
@@ -347,6 +367,7 @@ k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
     const Tin *bb = Bm + (b * nsteps * G + g) * N;
     const Tin *cb = Cm + (b * nsteps * G + g) * N;
     Tin *yb = y + (b * nsteps * H + h) * P + p0;
+    const Tin *zb = z ? z + (b * nsteps * H + h) * P + p0 : nullptr;
     float4 *sp = reinterpret_cast<float4 *>(state + (row0 + rl) * N) + sub;
     float4 s[4];
 #pragma unroll
@@ -364,9 +385,9 @@ k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
             const int t = e / RPB, r = e - t * RPB;
             const float xv = Elem<Tin>::ld(xb, (t0 + t) * xst + r);
             xs_[t][r] = xv;
-            us_[t][r] = db[(t0 + t) * H] * xv;
+            us_[t][r] = act_dt(act, db[(t0 + t) * H], h) * xv;
         }
-        if (tid < kc) rs_[tid] = ssd_exp(db[(t0 + tid) * H] * a);
+        if (tid < kc) rs_[tid] = ssd_exp(act_dt(act, db[(t0 + tid) * H], h) * a);
         __syncthreads();
         for (int t = 0; t < kc; ++t) {
             const float r = rs_[t], u = us_[t][rl];
@@ -385,7 +406,9 @@ k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
         __syncthreads();
         for (int e = tid; e < kc * RPB; e += RPB * L) {
             const int t = e / RPB, r = e - t * RPB;
-            Elem<Tin>::st(yb, (t0 + t) * xst + r, ys_[t][r]);
+            float yv = ys_[t][r];
+            if (z) yv *= silu_f(Elem<Tin>::ld(zb, (t0 + t) * xst + r));
+            Elem<Tin>::st(yb, (t0 + t) * xst + r, yv);
         }
     }
 #pragma unroll
@@ -395,12 +418,12 @@ k_step_multi_lds(float *__restrict__ state, const Tin *__restrict__ x,
 template <typename Tin, int L>
 void launch_multi_lds(const StepShape &s, int64_t nsteps, float *state, const void *x,
                       const float *dt, const float *A, const void *Bm, const void *Cm,
-                      const float *D, void *y, hipStream_t st) {
+                      const float *D, void *y, const DtAct &act, const void *z, hipStream_t st) {
     constexpr int RPB = 256 / L < 64 ? 256 / L : 64;
     const unsigned blocks = (unsigned)(s.B * s.H * s.P / RPB);
     k_step_multi_lds<Tin, 16, L><<<blocks, RPB * L, 0, st>>>(
         state, (const Tin *)x, dt, A, (const Tin *)Bm, (const Tin *)Cm, D, (Tin *)y, nsteps,
-        (int)s.H, (int)s.P, (int)s.G);
+        (int)s.H, (int)s.P, (int)s.G, act, (const Tin *)z);
 }
 
 // Rows per block of k_step_multi_lds for a state size (0: not handled there).
@@ -416,23 +439,54 @@ int multi_lds_rows(int64_t N) {
 template <typename Tin>
 void launch_multi_lds_n(const StepShape &s, int64_t nsteps, float *state, const void *x,
                         const float *dt, const float *A, const void *Bm, const void *Cm,
-                        const float *D, void *y, hipStream_t st) {
+                        const float *D, void *y, const DtAct &act, const void *z,
+                        hipStream_t st) {
+#define SSD_MULTI_L(LL) \
+    launch_multi_lds<Tin, LL>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, act, z, st)
     switch (s.N) {
-    case 16: launch_multi_lds<Tin, 1>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
-    case 32: launch_multi_lds<Tin, 2>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
-    case 64: launch_multi_lds<Tin, 4>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
-    case 128: launch_multi_lds<Tin, 8>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
-    default: launch_multi_lds<Tin, 16>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st); break;
+    case 16: SSD_MULTI_L(1); break;
+    case 32: SSD_MULTI_L(2); break;
+    case 64: SSD_MULTI_L(4); break;
+    case 128: SSD_MULTI_L(8); break;
+    default: SSD_MULTI_L(16); break;
     }
+#undef SSD_MULTI_L
+}
+
+template <typename Tin>
+void launch_step_t(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                   const float *dt, const float *A, const void *Bm, const void *Cm,
+                   const float *D, void *y, const DtAct &act, const void *z, hipStream_t st) {
+    const int64_t rows = s.B * s.H * s.P;
+    int lpr_log2 = 0;
+    while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
+    const unsigned blocks = (unsigned)(((rows << lpr_log2) + 255) / 256);
+    if (nsteps < 0) {  // a single step, [B, ...] layouts
+        k_step<Tin><<<blocks, 256, 0, st>>>(state, (const Tin *)x, dt, A, (const Tin *)Bm,
+                                            (const Tin *)Cm, D, (Tin *)y, rows, (int)s.H,
+                                            (int)s.P, (int)s.N, (int)s.G, lpr_log2, act,
+                                            (const Tin *)z);
+        return;
+    }
+    const int rpb = multi_lds_rows(s.N);
+    if (rpb > 0 && s.P % rpb == 0) {  // each block's rows share one (b, h): stage in LDS
+        launch_multi_lds_n<Tin>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, act, z, st);
+        return;
+    }
+    k_step_multi<Tin><<<blocks, 256, 0, st>>>(state, (const Tin *)x, dt, A, (const Tin *)Bm,
+                                              (const Tin *)Cm, D, (Tin *)y, rows, nsteps,
+                                              (int)s.H, (int)s.P, (int)s.N, (int)s.G, lpr_log2,
+                                              act, (const Tin *)z);
 }
 
 }  // namespace
 
 // ------------------------------------------------------------ launchers
 void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, float *Acs,
-                         hipStream_t st) {
+                         hipStream_t st, const DtAct &act, float *dt_out) {
     dim3 grid((unsigned)(s.B * s.T), (unsigned)((s.H + 3) / 4));
-    k_chunk_cumsum<<<grid, 256, 0, st>>>(dt, A, Acs, s.L, (int)s.H, (int)s.Q, (int)s.T);
+    k_chunk_cumsum<<<grid, 256, 0, st>>>(dt, A, Acs, s.L, (int)s.H, (int)s.Q, (int)s.T, act,
+                                         dt_out);
 }
 
 void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const float *dt,
@@ -470,20 +524,21 @@ void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *w
 
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       const void *ws, void *y, hipStream_t st) {
+                       const void *ws, void *y, hipStream_t st, const void *z) {
     if (mfma_supported(s)) {
-        launch_chunk_scan_mfma(s, x, dt, Cm, D, Acs, states, ws, y, st);
+        launch_chunk_scan_mfma(s, x, dt, Cm, D, Acs, states, ws, y, st, z);
         return;
     }
     dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.Q + kScanRows - 1) / kScanRows));
     if (s.dtype == SSD_BF16)
         k_chunk_scan_generic<bf16><<<grid, 256, 0, st>>>(
             (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y,
-            s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+            (const bf16 *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
     else
         k_chunk_scan_generic<float><<<grid, 256, 0, st>>>(
             (const float *)x, dt, (const float *)Bm, (const float *)Cm, D, Acs, states,
-            (float *)y, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+            (float *)y, (const float *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q,
+            (int)s.T);
 }
 
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {
@@ -491,49 +546,13 @@ void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st
     k_copy_or_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, src, n);
 }
 
-void launch_step_multi(const StepShape &s, int64_t nsteps, float *state, const void *x,
-                       const float *dt, const float *A, const void *Bm, const void *Cm,
-                       const float *D, void *y, hipStream_t st) {
-    const int64_t rows = s.B * s.H * s.P;
-    int lpr_log2 = 0;
-    while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
-    const int64_t threads = rows << lpr_log2;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    const int rpb = multi_lds_rows(s.N);
-    if (rpb > 0 && s.P % rpb == 0) {  // each block's rows share one (b, h): stage in LDS
-        if (s.dtype == SSD_BF16)
-            launch_multi_lds_n<bf16>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st);
-        else
-            launch_multi_lds_n<float>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, st);
-        return;
-    }
+void launch_step(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                 const float *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                 void *y, const DtAct &act, const void *z, hipStream_t st) {
     if (s.dtype == SSD_BF16)
-        k_step_multi<bf16><<<blocks, 256, 0, st>>>(
-            state, (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, (bf16 *)y, rows,
-            nsteps, (int)s.H, (int)s.P, (int)s.N, (int)s.G, lpr_log2);
+        launch_step_t<bf16>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, act, z, st);
     else
-        k_step_multi<float><<<blocks, 256, 0, st>>>(
-            state, (const float *)x, dt, A, (const float *)Bm, (const float *)Cm, D, (float *)y,
-            rows, nsteps, (int)s.H, (int)s.P, (int)s.N, (int)s.G, lpr_log2);
-}
-
-void launch_step(const StepShape &s, float *state, const void *x, const float *dt,
-                 const float *A, const void *Bm, const void *Cm, const float *D, void *y,
-                 hipStream_t st) {
-    const int64_t rows = s.B * s.H * s.P;
-    int lpr_log2 = 0;
-    while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
-    const int64_t threads = rows << lpr_log2;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    if (s.dtype == SSD_BF16)
-        k_step<bf16><<<blocks, 256, 0, st>>>(state, (const bf16 *)x, dt, A, (const bf16 *)Bm,
-                                             (const bf16 *)Cm, D, (bf16 *)y, rows, (int)s.H,
-                                             (int)s.P, (int)s.N, (int)s.G, lpr_log2);
-    else
-        k_step<float><<<blocks, 256, 0, st>>>(state, (const float *)x, dt, A,
-                                              (const float *)Bm, (const float *)Cm, D,
-                                              (float *)y, rows, (int)s.H, (int)s.P, (int)s.N,
-                                              (int)s.G, lpr_log2);
+        launch_step_t<float>(s, nsteps, state, x, dt, A, Bm, Cm, D, y, act, z, st);
 }
 
 }  // namespace ssd

@@ -17,9 +17,20 @@ struct StepShape {
     int dtype;
 };
 
+// Activation of the raw step size fused into the first kernel that reads dt:
+// d <- d + bias[h] (bias non-null), softplus(d) (softplus != 0), clamp to
+// [lo, hi] (limit != 0).  Zero-initialised it is the identity.
+struct DtAct {
+    const float *bias;
+    float lo, hi;
+    int softplus, limit;
+};
+
 // Stage kernels of the chunked scan (layouts as in include/ssd.h).
+// With an active act, the activated dt is used and written to dt_out (when
+// non-null) in dt's layout for the later stages.
 void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, float *Acs,
-                         hipStream_t st);
+                         hipStream_t st, const DtAct &act = DtAct{}, float *dt_out = nullptr);
 void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const float *dt,
                         const float *Acs, float *states, hipStream_t st);
 void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
@@ -30,20 +41,17 @@ size_t chunk_scan_ws_bytes(const ScanShape &s);
 void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *ws, hipStream_t st);
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
-                       const void *ws, void *y, hipStream_t st);
+                       const void *ws, void *y, hipStream_t st, const void *z = nullptr);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
 
-// One decode token.
-void launch_step(const StepShape &s, float *state, const void *x, const float *dt,
-                 const float *A, const void *Bm, const void *Cm, const float *D, void *y,
-                 hipStream_t st);
-
-// nsteps decode tokens in one launch, inputs in the prefill layout.
-void launch_step_multi(const StepShape &s, int64_t nsteps, float *state, const void *x,
-                       const float *dt, const float *A, const void *Bm, const void *Cm,
-                       const float *D, void *y, hipStream_t st);
+// Decode: nsteps < 0 is one token with [B, ...] inputs; nsteps >= 1 tokens
+// in one launch with inputs in the prefill layout [B, nsteps, ...].  z (the
+// output gate, x's layout) may be null.
+void launch_step(const StepShape &s, int64_t nsteps, float *state, const void *x,
+                 const float *dt, const float *A, const void *Bm, const void *Cm, const float *D,
+                 void *y, const DtAct &act, const void *z, hipStream_t st);
 
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);
@@ -55,12 +63,15 @@ void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, vo
                           hipStream_t st);
 // ssd_scan_fwd on the MFMA path: three launches (the cumsum inside the
 // chunk-state kernel, the C.B tiles inside the state-passing launch).
+// With an active act, the chunk-state kernel writes the activated dt to
+// dt_out, which the chunk-output kernel then reads; z may be null.
 void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
                             void *y, float *fin, float *Acs, float *states, void *cb,
-                            hipStream_t st);
+                            hipStream_t st, const DtAct &act = DtAct{},
+                            float *dt_out = nullptr, const void *z = nullptr);
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
                             const float *D, const float *Acs, const float *states, const void *cb,
-                            void *y, hipStream_t st);
+                            void *y, hipStream_t st, const void *z = nullptr);
 
 }  // namespace ssd

@@ -173,13 +173,14 @@ using P1 = std::integral_constant<int, 1>;
 //
 // kCumsum: the block also forms its chunk's cumulative log-decay (an in-block
 // prefix sum of dt*A over the chunk's tokens) and writes it to Acs for the
-// later stages, instead of reading it.
+// later stages, instead of reading it.  It then also applies the dt
+// activation `act` and, when dt_out is given, writes the activated dt there.
 template <int Q, int N, bool kCumsum>
 __global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ A,
                    float *__restrict__ Acs, float *__restrict__ states, int64_t L, int H, int G,
-                   int T, int64_t nblocks) {
+                   int T, int64_t nblocks, DtAct act, float *__restrict__ dt_out) {
     constexpr int LDX = kP + 16;              // x stage row stride (bf16)
     constexpr int LDB = N + 16;               // B stage row stride (bf16)
     constexpr int NST = Q / kJT;              // stages per chunk
@@ -211,7 +212,12 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     if constexpr (kCumsum) {
         __shared__ float wsum[4];
         __shared__ float last_s;
-        const float d = tid < q ? dt[(b * L + t0 + tid) * H + h] : 0.f;
+        float d = 0.f;
+        if (tid < q) {
+            const int64_t di = (b * L + t0 + tid) * H + h;
+            d = act_dt(act, dt[di], h);
+            if (dt_out) dt_out[di] = d;
+        }
         const float v = wave_inclusive_scan(d * A[h], lane);
         if (lane == 63) wsum[wave] = v;
         __syncthreads();
@@ -442,13 +448,16 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // tile's diagonal.  Stages (raw x, xw hi, xw lo) stream through two LDS
 // slots, loaded two stages ahead; the C.B tile of the next step is loaded one
 // step ahead.  The tile loop branches on wave-uniform values only.
-template <int Q, int N>
+//
+// kGate: every y value is multiplied by silu(z) (z in y's layout) in fp32
+// before its rounding to bf16.
+template <int Q, int N, bool kGate>
 __global__ void __launch_bounds__(Q * 2) __attribute__((amdgpu_waves_per_eu(Q == 256 ? 4 : 2)))
 k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                   const float *__restrict__ D, const float *__restrict__ Acs,
                   const float *__restrict__ states, const u32x4 *__restrict__ cb,
-                  const u32x4 *__restrict__ cfr, bf16 *__restrict__ y, int64_t L, int H, int G,
-                  int T, int64_t nblocks) {
+                  const u32x4 *__restrict__ cfr, bf16 *__restrict__ y,
+                  const bf16 *__restrict__ z, int64_t L, int H, int G, int T, int64_t nblocks) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     constexpr int TH = Q * 2;             // threads: NI waves
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
@@ -651,6 +660,20 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
 
     bf16 *ys = reinterpret_cast<bf16 *>(hu) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
+    if constexpr (kGate) {
+        // the wave's z tile (32 rows x 128 bytes) copied straight into its
+        // staging rows, unpadded, four 1 KB buffer-to-LDS loads (lane i's 16
+        // bytes land at 16 i; rows past a short chunk's end arrive as zeros);
+        // the rows are not used for y until this wave's epilogue
+        static_assert(32 * kP * 2 <= 32 * LDY * 2, "z tile fits the staging rows");
+        const bf16 *zbase = z + ((b * L + t0) * H + h) * kP;
+        const rsrc_t zr = buffer_rsrc_at(zbase, xy_bytes, (unsigned)(ti * 32) * xrs * 2u);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                zr, (__attribute__((address_space(3))) void *)(ys + kk * 512), 16,
+                ((unsigned)((lane >> 3) + 8 * kk) * xrs + 8u * (lane & 7)) * 2u, 0, 0, 0);
+    }
     const float Dh = D ? D[h] : 0.f;
 
     // off-diagonal visit of column tile jt
@@ -704,6 +727,25 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     // 128-byte rows (8 lanes per row, 8 rows per store)
     const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
     auto epilogue = [&]() __attribute__((always_inline)) {
+        if constexpr (kGate) {
+            // z of this lane's accumulator elements (token il, channels
+            // p0..p0+3), from the copy the wave prefetched into its staging
+            // rows; the multiply is in fp32, before the single rounding below
+            const bf16 *zl = ys;
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int p0 = pt * 32 + 8 * rg + 4 * g2;
+                    const u32x2 zz = *reinterpret_cast<const u32x2 *>(&zl[il * kP + p0]);
+                    Z[pt][4 * rg + 0] *= silu_f(lo_bf16(zz[0]));
+                    Z[pt][4 * rg + 1] *= silu_f(hi_bf16(zz[0]));
+                    Z[pt][4 * rg + 2] *= silu_f(lo_bf16(zz[1]));
+                    Z[pt][4 * rg + 3] *= silu_f(hi_bf16(zz[1]));
+                }
+            // the z reads above feed the products the stores below write, so
+            // they have completed before the staging rows are overwritten
+        }
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -763,7 +805,7 @@ void launch_state_t(const ScanShape &s, const void *x, const void *Bm, const flo
     const int64_t nb = s.B * s.T * s.H;
     k_chunk_state_mfma<Q, N, false><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)x, (const bf16 *)Bm, dt, nullptr, const_cast<float *>(Acs), states, s.L,
-        (int)s.H, (int)s.G, (int)s.T, nb);
+        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr);
 }
 
 
@@ -778,14 +820,20 @@ void launch_cb_t(const ScanShape &s, const void *Bm, const void *Cm, void *cb, h
 template <int Q, int N>
 void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const void *Cm,
                    const float *D, const float *Acs, const float *states, const void *cb, void *y,
-                   hipStream_t st) {
+                   hipStream_t st, const void *z) {
     const int64_t nb = s.B * s.T * s.H;
     constexpr int NI = Q / 32;
     const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
     (void)Cm;  // C enters through the operand fragments the C.B kernel stored
-    k_chunk_scan_mfma<Q, N><<<padded_grid(nb), Q * 2, 0, st>>>(
-        (const bf16 *)x, dt, D, Acs, states, (const u32x4 *)cb,
-        (const u32x4 *)cb + ntiles * 256, (bf16 *)y, s.L, (int)s.H, (int)s.G, (int)s.T, nb);
+    const u32x4 *cbt = (const u32x4 *)cb, *cfr = cbt + ntiles * 256;
+    if (z)
+        k_chunk_scan_mfma<Q, N, true><<<padded_grid(nb), Q * 2, 0, st>>>(
+            (const bf16 *)x, dt, D, Acs, states, cbt, cfr, (bf16 *)y, (const bf16 *)z, s.L,
+            (int)s.H, (int)s.G, (int)s.T, nb);
+    else
+        k_chunk_scan_mfma<Q, N, false><<<padded_grid(nb), Q * 2, 0, st>>>(
+            (const bf16 *)x, dt, D, Acs, states, cbt, cfr, (bf16 *)y, nullptr, s.L, (int)s.H,
+            (int)s.G, (int)s.T, nb);
 }
 
 // The whole chunked scan in three launches: chunk states with the in-block
@@ -793,12 +841,13 @@ void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const voi
 template <int Q, int N>
 void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                     const void *Bm, const void *Cm, const float *D, const float *init, void *y,
-                    float *fin, float *Acs, float *states, void *cb, hipStream_t st) {
+                    float *fin, float *Acs, float *states, void *cb, hipStream_t st,
+                    const DtAct &act, float *dt_out, const void *z) {
     constexpr int NI = Q / 32;
     const int64_t nb = s.B * s.T * s.H;
     k_chunk_state_mfma<Q, N, true><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T,
-        nb);
+        nb, act, dt_out);
     const int64_t PN = s.P * s.N;
     const int ny = (int)((PN / 4 + 255) / 256);
     const int64_t nsp = s.B * s.H * ny;
@@ -806,7 +855,7 @@ void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const fl
     k_state_passing_cb<Q, N><<<(unsigned)(nsp + (ntiles + 3) / 4), 256, 0, st>>>(
         states, Acs, init, fin, s.L, (int)s.H, PN, (int)s.T, nsp, ny, (const bf16 *)Bm,
         (const bf16 *)Cm, (u32x4 *)cb, (int)s.G, ntiles);
-    launch_scan_t<Q, N>(s, x, dt, Cm, D, Acs, states, cb, y, st);
+    launch_scan_t<Q, N>(s, x, dt_out ? dt_out : dt, Cm, D, Acs, states, cb, y, st, z);
 }
 
 }  // namespace
@@ -852,14 +901,15 @@ void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, vo
 void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
                             void *y, float *fin, float *Acs, float *states, void *cb,
-                            hipStream_t st) {
-    SSD_DISPATCH_QN(launch_fused_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb, st);
+                            hipStream_t st, const DtAct &act, float *dt_out, const void *z) {
+    SSD_DISPATCH_QN(launch_fused_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb, st,
+                    act, dt_out, z);
 }
 
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
                             const float *D, const float *Acs, const float *states, const void *cb,
-                            void *y, hipStream_t st) {
-    SSD_DISPATCH_QN(launch_scan_t, s, x, dt, Cm, D, Acs, states, cb, y, st);
+                            void *y, hipStream_t st, const void *z) {
+    SSD_DISPATCH_QN(launch_scan_t, s, x, dt, Cm, D, Acs, states, cb, y, st, z);
 }
 
 }  // namespace ssd

@@ -78,10 +78,30 @@ size_t scan_ws_bytes(const ScanShape &s) {
     return round_up(ssd::chunk_scan_ws_bytes(s));
 }
 
+// the activated dt of ssd_scan_fwd_ex, [B, L, H] fp32
+size_t dt_eff_bytes(const ScanShape &s) { return round_up((size_t)(s.B * s.L * s.H) * 4); }
+
 size_t workspace_bytes(const ScanShape &s) {
     if (s.B == 0 || s.L == 0) return 0;
-    return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s);
+    return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s) + dt_eff_bytes(s);
 }
+
+// ssd_edges -> the kernels' dt activation and gate pointer (NULL: neither).
+ssd_status read_edges(const ssd_edges *e, ssd::DtAct *act, const void **z) {
+    *act = ssd::DtAct{};
+    *z = nullptr;
+    if (!e) return SSD_OK;
+    if (e->dt_limit && !(e->dt_min <= e->dt_max)) return SSD_ERR_UNSUPPORTED;
+    act->bias = e->dt_bias;
+    act->softplus = e->dt_softplus ? 1 : 0;
+    act->limit = e->dt_limit ? 1 : 0;
+    act->lo = e->dt_min;
+    act->hi = e->dt_max;
+    *z = e->z;
+    return SSD_OK;
+}
+
+bool act_active(const ssd::DtAct &a) { return a.bias || a.softplus || a.limit; }
 
 ssd_status after_launch() {
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
@@ -99,7 +119,8 @@ const char *ssd_status_string(int status) {
     case SSD_ERR_NULL_PTR: return "a required pointer is NULL";
     case SSD_ERR_SHAPE: return "invalid shape (negative or zero dimension, or nheads % ngroups != 0)";
     case SSD_ERR_UNSUPPORTED:
-        return "unsupported argument (chunk, headdim, dstate, dtype or reserved field)";
+        return "unsupported argument (chunk, headdim, dstate, dtype, reserved field, or "
+               "dt_limit with dt_min > dt_max)";
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SSD_ERR_WORKSPACE: return "workspace is smaller than the size its query function reports";
     case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
@@ -107,7 +128,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 2; }
+int ssd_abi_version(void) { return 3; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -118,12 +139,16 @@ ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     return SSD_OK;
 }
 
-ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, const float *A,
-                        const void *B, const void *C, const float *D, const float *init_state,
-                        void *y, float *final_state, void *workspace, size_t ws_bytes,
-                        void *stream) {
+ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const void *x,
+                           const float *dt, const float *A, const void *B, const void *C,
+                           const float *D, const float *init_state, void *y,
+                           float *final_state, void *workspace, size_t ws_bytes, void *stream) {
     ScanShape s;
     ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
     if (st != SSD_OK) return st;
     if (s.B == 0) return SSD_OK;
     if (s.L == 0) {
@@ -134,59 +159,94 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                                      as_stream(stream));
         return after_launch();
     }
-    st = check_ptrs({x, dt, A, B, C, y}, {D, init_state, final_state, workspace});
+    st = check_ptrs({x, dt, A, B, C, y}, {D, init_state, final_state, workspace, z, act.bias});
     if (st != SSD_OK) return st;
     const size_t need = workspace_bytes(s);
     if (ws_bytes < need) return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
-    float *Acs = static_cast<float *>(workspace);
-    float *states = reinterpret_cast<float *>(static_cast<char *>(workspace) + acs_bytes(s));
-    void *scan_ws = static_cast<char *>(workspace) + acs_bytes(s) + states_bytes(s);
+    char *ws = static_cast<char *>(workspace);
+    float *Acs = reinterpret_cast<float *>(ws);
+    float *states = reinterpret_cast<float *>(ws + acs_bytes(s));
+    void *scan_ws = ws + acs_bytes(s) + states_bytes(s);
+    float *dt_eff = act_active(act)
+                        ? reinterpret_cast<float *>(ws + acs_bytes(s) + states_bytes(s) +
+                                                    scan_ws_bytes(s))
+                        : nullptr;
     hipStream_t hs = as_stream(stream);
     if (ssd::mfma_supported(s)) {
         ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
-                                    scan_ws, hs);
+                                    scan_ws, hs, act, dt_eff, z);
     } else {
-        ssd::launch_chunk_cumsum(s, dt, A, Acs, hs);
-        ssd::launch_chunk_state(s, x, B, dt, Acs, states, hs);
+        ssd::launch_chunk_cumsum(s, dt, A, Acs, hs, act, dt_eff);
+        const float *dts = dt_eff ? dt_eff : dt;
+        ssd::launch_chunk_state(s, x, B, dts, Acs, states, hs);
         ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
         ssd::launch_chunk_cb(s, B, C, scan_ws, hs);
-        ssd::launch_chunk_scan(s, x, dt, B, C, D, Acs, states, scan_ws, y, hs);
+        ssd::launch_chunk_scan(s, x, dts, B, C, D, Acs, states, scan_ws, y, hs, z);
     }
+    return after_launch();
+}
+
+ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        void *y, float *final_state, void *workspace, size_t ws_bytes,
+                        void *stream) {
+    return ssd_scan_fwd_ex(d, nullptr, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                           ws_bytes, stream);
+}
+
+ssd_status ssd_step_multi_ex(const ssd_step_desc *d, const ssd_edges *edges, int64_t nsteps,
+                             float *state, const void *x, const float *dt, const float *A,
+                             const void *B, const void *C, const float *D, void *y,
+                             void *stream) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                 d->dtype, d->reserved);
+    if (st != SSD_OK) return st;
+    if (nsteps < 0) return SSD_ERR_SHAPE;
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
+    if (st != SSD_OK) return st;
+    if (d->batch == 0 || nsteps == 0) return SSD_OK;
+    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias});
+    if (st != SSD_OK) return st;
+    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
+    ssd::launch_step(s, nsteps, state, x, dt, A, B, C, D, y, act, z, as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_step_ex(const ssd_step_desc *d, const ssd_edges *edges, float *state,
+                       const void *x, const float *dt, const float *A, const void *B,
+                       const void *C, const float *D, void *y, void *stream) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
+                                 d->dtype, d->reserved);
+    if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
+    if (st != SSD_OK) return st;
+    if (d->batch == 0) return SSD_OK;
+    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias});
+    if (st != SSD_OK) return st;
+    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
+    ssd::launch_step(s, -1, state, x, dt, A, B, C, D, y, act, z, as_stream(stream));
     return after_launch();
 }
 
 ssd_status ssd_step(const ssd_step_desc *d, float *state, const void *x, const float *dt,
                     const float *A, const void *B, const void *C, const float *D, void *y,
                     void *stream) {
-    if (!d) return SSD_ERR_NULL_PTR;
-    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
-                                 d->dtype, d->reserved);
-    if (st != SSD_OK) return st;
-    if (d->batch == 0) return SSD_OK;
-    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
-    st = check_ptrs({state, x, dt, A, B, C, y}, {D});
-    if (st != SSD_OK) return st;
-    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
-    ssd::launch_step(s, state, x, dt, A, B, C, D, y, as_stream(stream));
-    return after_launch();
+    return ssd_step_ex(d, nullptr, state, x, dt, A, B, C, D, y, stream);
 }
 
 ssd_status ssd_step_multi(const ssd_step_desc *d, int64_t nsteps, float *state, const void *x,
                           const float *dt, const float *A, const void *B, const void *C,
                           const float *D, void *y, void *stream) {
-    if (!d) return SSD_ERR_NULL_PTR;
-    ssd_status st = check_common(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups,
-                                 d->dtype, d->reserved);
-    if (st != SSD_OK) return st;
-    if (nsteps < 0) return SSD_ERR_SHAPE;
-    if (d->batch == 0 || nsteps == 0) return SSD_OK;
-    if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
-    st = check_ptrs({state, x, dt, A, B, C, y}, {D});
-    if (st != SSD_OK) return st;
-    StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
-    ssd::launch_step_multi(s, nsteps, state, x, dt, A, B, C, D, y, as_stream(stream));
-    return after_launch();
+    return ssd_step_multi_ex(d, nullptr, nsteps, state, x, dt, A, B, C, D, y, stream);
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_scan_desc *d, const float *dt, const float *A,

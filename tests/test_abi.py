@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 2
+    assert L.ssd_abi_version() == 3
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -96,17 +96,18 @@ def test_chunk_scan_workspace_size(L):
 
 
 def test_workspace_size(L):
+    # Acs, chunk states, the chunk-output workspace, the activated dt
     st, n = wsize(L, desc())
     T = 2
     acs = 1 * 8 * 512 * 4
     states = 1 * T * 8 * 64 * 128 * 4
-    assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc())[1]
+    assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc())[1] + r256(acs)
     # ragged last chunk counts as a chunk
     st, n = wsize(L, desc(seqlen=300, chunk=128))
     assert st == OK and n == (r256(8 * 300 * 4) + r256(3 * 8 * 64 * 128 * 4)
-                              + cb_size(L, desc(seqlen=300, chunk=128))[1])
+                              + cb_size(L, desc(seqlen=300, chunk=128))[1] + r256(8 * 300 * 4))
     st, n = wsize(L, desc(dtype=0))
-    assert st == OK and n == r256(acs) + r256(states)
+    assert st == OK and n == r256(acs) + r256(states) + r256(acs)
     assert wsize(L, desc(seqlen=0)) == (OK, 0)
     assert wsize(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_scan_workspace_size(ctypes.byref(desc()), None) == NULL
@@ -213,6 +214,43 @@ def test_step_multi_errors(L):
     # nothing to do: no pointer is touched
     assert L.ssd_step_multi(ctypes.byref(d), 0, *([None] * 8), None) == OK
     assert L.ssd_step_multi(ctypes.byref(sdesc(batch=0)), 4, *([None] * 8), None) == OK
+
+
+def edges(**kw):
+    e = dict(dt_bias=None, z=None, dt_min=0.0, dt_max=0.0, dt_softplus=0, dt_limit=0)
+    e.update(kw)
+    return binding.Edges(**e)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt_limit=1, dt_min=0.1, dt_max=0.01), UNSUP),       # empty clamp range
+    (dict(dt_limit=1, dt_min=float("nan"), dt_max=1.0), UNSUP),
+    (dict(z=P_MIS), ALIGN), (dict(dt_bias=P_MIS), ALIGN),
+])
+def test_edges_errors(L, kw, status):
+    e = ctypes.byref(edges(**kw))
+    d = desc()
+    _, need = wsize(L, d)
+    assert L.ssd_scan_fwd_ex(ctypes.byref(d), e, *([P16] * 10), need, None) == status
+    assert L.ssd_step_ex(ctypes.byref(sdesc()), e, *([P16] * 8), None) == status
+    assert L.ssd_step_multi_ex(ctypes.byref(sdesc()), e, 3, *([P16] * 8), None) == status
+
+
+def test_edges_null_is_plain(L):
+    """A NULL ssd_edges is the plain call: the same checks in the same order."""
+    d = desc()
+    _, need = wsize(L, d)
+    for which in range(10):
+        ptrs = [P16] * 10
+        ptrs[which] = P_MIS
+        assert L.ssd_scan_fwd_ex(ctypes.byref(d), None, *ptrs, need, None) == ALIGN
+    assert L.ssd_scan_fwd_ex(ctypes.byref(d), None, *([P16] * 10), need - 1, None) == WS
+    assert L.ssd_scan_fwd_ex(None, None, *([P16] * 10), need, None) == NULL
+    assert L.ssd_step_ex(None, None, *([P16] * 8), None) == NULL
+    assert L.ssd_step_multi_ex(ctypes.byref(sdesc()), None, -2, *([P16] * 8), None) == SHAPE
+    # a valid clamp and softplus with an empty batch: nothing to do
+    e = ctypes.byref(edges(dt_softplus=1, dt_limit=1, dt_min=1e-3, dt_max=0.1))
+    assert L.ssd_scan_fwd_ex(ctypes.byref(desc(batch=0)), e, *([None] * 10), 0, None) == OK
 
 
 def test_empty_batch_is_noop(L):

@@ -1,0 +1,153 @@
+"""GPU parity of the fused scan edges (dt bias + softplus + clamp applied in
+the kernels, output gate y * silu(z) applied before the output rounding)
+against the fp64 oracle: oracle.edges applied around the oracle recurrence.
+
+Inputs are the raw edge inputs of the generator: dt before activation, the
+per-head bias softplus^-1(dt0), a N(0, 1) gate.  Bars as for the plain scan.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import edges as oe
+import mamba_ssd_chunked_scan_amd as ssd
+from mamba_ssd_chunked_scan_amd import synth
+
+from helpers import TOL, f64, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LIMIT = (1e-3, 0.1)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+SPECS = {
+    # MFMA path (bf16, headdim 64): several chunks and a ragged tail
+    "mfma_q256_n128": synth.custom_spec(2, 700, 8, 64, 128, 2, chunk=256, dtype="bf16",
+                                        dt_rule="ranged", init="normal", seed=21),
+    "mfma_q64_n64": synth.custom_spec(1, 300, 4, 64, 64, 1, chunk=64, dtype="bf16",
+                                      dt_rule="ranged", init="normal", seed=22),
+    # generic fp32 path
+    "generic_f32": synth.custom_spec(1, 333, 4, 16, 16, 2, chunk=64, dtype="f32",
+                                     dt_rule="ranged", init="normal", seed=23),
+}
+
+
+def _run(spec, which, inp):
+    use_dt = which in ("all", "dt")
+    use_gate = which in ("all", "gate")
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    kw = {}
+    if use_dt:
+        kw.update(dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=LIMIT)
+    if use_gate:
+        kw["z"] = d["gate"]
+    y, fin = ssd.scan_fwd(d["x"], d["dt_raw"] if use_dt else d["dt"], d["A"], d["B"], d["C"],
+                          d["D"], chunk=spec.chunk, init_state=d["init"], **kw)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _reference(inp, which):
+    use_dt = which in ("all", "dt")
+    dt = (oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT) if use_dt
+          else inp["dt"])
+    yo, fo = oracle.scan(inp["x"], dt, inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
+    if which in ("all", "gate"):
+        yo = oe.gate(yo, inp["gate"])
+    return yo, fo
+
+
+@pytest.mark.parametrize("which", ["all", "dt", "gate"])
+@pytest.mark.parametrize("name", list(SPECS))
+def test_scan_edges_vs_oracle(name, which):
+    spec = SPECS[name]
+    announce(f"scan edges {name} {which}")
+    inp = synth.scan_edge_inputs(spec)
+    y, fin = _run(spec, which, inp)
+    yo, fo = _reference(inp, which)
+    tol = TOL[inp["x"].dtype]
+    assert rel_err(f64(y), yo) <= tol
+    assert rel_err(f64(fin), fo) <= tol
+
+
+@pytest.mark.parametrize("name", list(SPECS))
+def test_zero_bias_equals_plain_call(name):
+    """A zero bias activates the edge path (the first kernel writes the
+    activated dt to the workspace and the later ones read it) without
+    changing a value: results are bit for bit those of the plain call."""
+    spec = SPECS[name]
+    announce(f"zero bias {name}")
+    inp = synth.scan_edge_inputs(spec)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"])
+    y0, f0 = ssd.scan_fwd(*args, chunk=spec.chunk, init_state=d["init"])
+    y1, f1 = ssd.scan_fwd(*args, chunk=spec.chunk, init_state=d["init"],
+                          dt_bias=torch.zeros_like(d["dt_bias"]))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+def test_edges_at_bench_workload_sampled():
+    """The 2.7B prefill workload (batch 1, 4096 tokens, 80 heads) with every
+    edge on, in the bench's launch configuration; 6 sampled heads against the
+    oracle one by one."""
+    spec = synth.WORKLOADS["m2p7b_bf16"]
+    announce("scan edges m2p7b sampled")
+    inp = synth.scan_edge_inputs(spec)
+    y, fin = _run(spec, "all", inp)
+    dt = oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT)
+    ref_in = dict(inp, dt=torch.from_numpy(dt))
+    heads = [0, 13, 31, 47, 64, 79]
+    ref = oracle.scan_heads(ref_in, [(0, h) for h in heads])
+    for h in heads:
+        yo, fo = ref[(0, h)]
+        yo = oe.gate(yo, inp["gate"][0, :, h])
+        assert rel_err(f64(y[0, :, h]), yo) <= TOL[torch.bfloat16], h
+        assert rel_err(f64(fin[0, h]), fo) <= TOL[torch.bfloat16], h
+
+
+@pytest.mark.parametrize("shape", [
+    # Bt, T, H, P, N, G, dtype  (LDS-staged and register-prefetch multi-step kernels)
+    (2, 20, 8, 64, 128, 2, torch.bfloat16),
+    (3, 5, 4, 12, 32, 1, torch.float32),
+])
+def test_step_edges(shape):
+    """Decode with every edge on: ssd_step_ex against the oracle step, and
+    ssd_step_multi_ex bit for bit equal to the chained single steps."""
+    Bt, T, H, P, N, G, dtype = shape
+    announce(f"step edges {shape}")
+    dn = "bf16" if dtype == torch.bfloat16 else "f32"
+    inp = synth.edge_decode_inputs(Bt, T, H, P, N, G, dn, seed=31 + T)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    ekw = dict(dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=LIMIT)
+    s_chain = d["state"].clone()
+    ys = []
+    for t in range(T):
+        ys.append(ssd.step(s_chain, d["x"][:, t].clone(), d["dt_raw"][:, t].clone(), d["A"],
+                           d["B"][:, t].clone(), d["C"][:, t].clone(), d["D"],
+                           z=d["gate"][:, t].clone(), **ekw))
+    y_chain = torch.stack(ys, 1)
+    s_multi = d["state"].clone()
+    y_multi = ssd.step_multi(s_multi, d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                             z=d["gate"], **ekw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_multi, y_chain)
+    assert torch.equal(s_multi, s_chain)
+    # oracle: activated dt, the recurrence token by token, then the gate
+    dt = oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT)
+    s = inp["state"]
+    yo = []
+    for t in range(T):
+        yt, s = oracle.step(s, inp["x"][:, t], dt[:, t], inp["A"], inp["B"][:, t],
+                            inp["C"][:, t], inp["D"])
+        yo.append(oe.gate(yt, inp["gate"][:, t]))
+    assert rel_err(f64(y_chain), np.stack(yo, 1)) <= TOL[dtype]
+    assert rel_err(f64(s_chain), s) <= TOL[dtype]
