@@ -6,6 +6,8 @@ two share no code.
 
 * :func:`scan` / :func:`step` wrap the fp64 token-by-token recurrence in
   ``ssd_oracle.c`` (the definition of the operation).
+* :func:`scan_varlen` runs a packed ragged batch sequence by sequence.
+* :mod:`oracle.edges` holds the fp64 dt activation and output gate.
 * :mod:`oracle.chunked` is an fp64 numpy version of the chunked algorithm
   (per-chunk matrix form plus a scan of chunk states), used to check the
   recurrence and to give per-stage values.
@@ -132,3 +134,29 @@ def scan_heads(inputs: dict, pairs, nthreads: int = 0):
             nthreads=nthreads)
         out[(b, h)] = (y[0, :, 0, :], fin[0, 0])
     return out
+
+
+def scan_varlen(cu_seqlens, x, dt, A, B, C, D=None, init=None, nthreads: int = 0):
+    """A ragged batch: sequence s is tokens [cu[s], cu[s+1]) of the packed
+    x [total, H, P], dt [total, H], B/C [total, G, N], each run through
+    :func:`scan` on its own from init[s] (zero when init is None).  Returns
+    (y [total, H, P], finals [nseq, H, P, N])."""
+    cu = [int(v) for v in np.asarray(cu_seqlens).reshape(-1)]
+    x, dt, B, C = f64(x), f64(dt), f64(B), f64(C)
+    init = f64(init)
+    nseq = len(cu) - 1
+    H, P = x.shape[1], x.shape[2]
+    N = B.shape[2]
+    y = np.zeros_like(x)
+    finals = np.zeros((nseq, H, P, N))
+    for s in range(nseq):
+        a, b = cu[s], cu[s + 1]
+        h0 = None if init is None else init[s:s + 1]
+        if b == a:
+            finals[s] = 0.0 if h0 is None else h0[0]
+            continue
+        ys, fs = scan(x[None, a:b], dt[None, a:b], A, B[None, a:b], C[None, a:b], D, h0,
+                      nthreads=nthreads)
+        y[a:b] = ys[0]
+        finals[s] = fs[0]
+    return y, finals
