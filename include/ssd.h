@@ -71,6 +71,15 @@ typedef struct ssd_scan_desc {
     int32_t reserved; /* must be 0 */
 } ssd_scan_desc;
 
+/* Shape of a variable-length (ragged) prefill: nseq sequences packed back to
+ * back along one token axis of `total` tokens.  nseq >= 0, total >= 0, both
+ * below 2^31 - 512; other fields as in ssd_scan_desc. */
+typedef struct ssd_varlen_desc {
+    int64_t nseq, total, nheads, headdim, dstate, ngroups, chunk;
+    int32_t dtype; /* ssd_dtype */
+    int32_t reserved; /* must be 0 */
+} ssd_varlen_desc;
+
 /* Shape of a decode step: as above without seqlen and chunk. */
 typedef struct ssd_step_desc {
     int64_t batch, nheads, headdim, dstate, ngroups;
@@ -81,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -143,6 +152,44 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
                            const float *D, const float *init_state, void *y,
                            float *final_state, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* ------------------------------------------------ variable-length prefill */
+
+/* Bytes of device workspace ssd_scan_fwd_varlen needs for shape *d. */
+ssd_status ssd_varlen_workspace_size(const ssd_varlen_desc *d, size_t *bytes);
+
+/* A ragged batch in one call, for serving requests of different lengths
+ * together ("Bringing blazing fast state space models to the Modular MAX
+ * framework", "What We Built": variable-length selective-scan kernels for
+ * batched serving; the pyshine "Mamba" repository tour: the CUDA core's
+ * variable-length strands): sequence s covers tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]) of the packed arrays, starts from its own
+ * init state, ends in its own final state, and never sees another
+ * sequence's tokens.  The result for each sequence is that of ssd_scan_fwd_ex
+ * on it alone (batch 1, same chunk size): each sequence is cut into chunks
+ * from its own first token, its last chunk may be short, and an empty
+ * sequence passes its init state through.
+ *   cu_seqlens   [nseq + 1] int32, device: 0 = cu[0] <= cu[1] <= ... <=
+ *                cu[nseq] = total.  Offsets outside that contract give
+ *                unspecified results but no access outside the arrays below
+ *                (they are clamped into [0, total] on the device).
+ *   x, y         [total, nheads, headdim]     dtype
+ *   dt           [total, nheads]              fp32 (raw when edges activate it)
+ *   B, C         [total, ngroups, dstate]     dtype
+ *   A, D         [nheads] fp32 (D may be NULL)
+ *   init_states  [nseq, nheads, headdim, dstate] fp32, or NULL (zero states)
+ *   final_states [nseq, nheads, headdim, dstate] fp32, or NULL; may equal
+ *                init_states
+ *   edges        as for ssd_scan_fwd_ex, or NULL (z in x's layout)
+ *   workspace    at least ssd_varlen_workspace_size bytes.
+ * nseq == 0 is a no-op; total == 0 writes final = init for every sequence.
+ * The chunk table is built on the device from cu_seqlens, so the call needs
+ * no host copy of the lengths and can be captured in a HIP graph. */
+ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
+                               const int32_t *cu_seqlens, const void *x, const float *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *init_states, void *y, float *final_states,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------- decode step */
 

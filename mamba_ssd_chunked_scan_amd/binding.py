@@ -25,11 +25,19 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
            "ssd_step", "ssd_step_multi", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
-           "ssd_step_ex", "ssd_step_multi_ex")
+           "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen")
 
 
 class ScanDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class VarlenDesc(ctypes.Structure):
+    _fields_ = [("nseq", ctypes.c_int64), ("total", ctypes.c_int64),
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32),
@@ -89,6 +97,10 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_fwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
                                       + [_P] * 10 + [ctypes.c_size_t, _P])
         L.ssd_step_ex.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(Edges)] + [_P] * 9
+        L.ssd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_fwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
+                                          + [_P] * 11 + [ctypes.c_size_t, _P])
         L.ssd_step_multi_ex.argtypes = ([ctypes.POINTER(StepDesc), ctypes.POINTER(Edges),
                                          ctypes.c_int64] + [_P] * 9)
         for name in EXPORTS[2:]:
@@ -230,6 +242,66 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _check("ssd_scan_fwd_ex", st)
     return y, final_state
+
+
+def varlen_workspace_size(nseq, total, nheads, headdim, dstate, ngroups, chunk, dtype) -> int:
+    d = VarlenDesc(nseq, total, nheads, headdim, dstate, ngroups, chunk,
+                   SSD_BF16 if dtype == torch.bfloat16 else SSD_F32, 0)
+    n = ctypes.c_size_t(0)
+    _check("ssd_varlen_workspace_size",
+           lib().ssd_varlen_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, chunk: int = 256, init_states=None,
+                    return_final_states: bool = True, final_states=None, workspace=None,
+                    y=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None):
+    """Ragged batch: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]) of
+    the packed x [total, nheads, headdim], dt [total, nheads], B/C [total,
+    ngroups, dstate]; cu_seqlens is an int32 device tensor [nseq + 1].
+    Returns (y, final_states [nseq, nheads, headdim, dstate] or None)."""
+    if x.dim() != 3 or B.dim() != 3 or dt.dim() != 2:
+        raise ValueError("x [total,h,p], dt [total,h], B/C [total,g,n] expected")
+    total, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev, io = x.device, x.dtype
+    if dev.type != "cuda":
+        raise ValueError("inputs must be device tensors")
+    if cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor [nseq + 1]")
+    nseq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (nseq + 1,), torch.int32, dev)
+    _need(dt, "dt", (total, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (total, G, N), io, dev)
+    _need(C, "C", (total, G, N), io, dev)
+    if D is not None:
+        _need(D, "D", (H,), torch.float32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (nseq, H, P, N), torch.float32, dev)
+    if final_states is None and return_final_states:
+        final_states = torch.empty((nseq, H, P, N), dtype=torch.float32, device=dev)
+    elif final_states is not None:
+        _need(final_states, "final_states", (nseq, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.shape, io, dev)
+    desc = VarlenDesc(nseq, total, H, P, N, G, chunk, _io_dtype(x), 0)
+    n = ctypes.c_size_t(0)
+    _check("ssd_varlen_workspace_size",
+           lib().ssd_varlen_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < n.value or workspace.device != dev:
+        raise ValueError(f"workspace needs {n.value} bytes on {dev}")
+    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    st = lib().ssd_scan_fwd_varlen(ctypes.byref(desc), _eref(e), _ptr(cu_seqlens), _ptr(x),
+                                   _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                   _ptr(init_states), _ptr(y), _ptr(final_states),
+                                   _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("ssd_scan_fwd_varlen", st)
+    return y, final_states
 
 
 def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,

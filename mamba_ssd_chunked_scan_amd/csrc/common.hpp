@@ -75,6 +75,22 @@ __device__ __forceinline__ float silu_f(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// First token (within its batch row) and length of chunk slot c.  Fixed
+// chunking: t0 = c*Q, q = min(Q, L - t0).  Variable-length batches: the slot's
+// entry of the chunk table (q = 0 for an unused slot).
+struct ChunkPos {
+    int64_t t0;
+    int q;
+};
+__device__ __forceinline__ ChunkPos chunk_pos(const int2 *ctab, int64_t c, int Q, int64_t L) {
+    if (ctab) {
+        const int2 e = ctab[c];
+        return ChunkPos{e.x, e.y};
+    }
+    const int64_t t0 = c * Q;
+    return ChunkPos{t0, (int)min((int64_t)Q, L - t0)};
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 #pragma unroll

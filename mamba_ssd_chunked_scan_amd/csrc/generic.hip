@@ -27,14 +27,16 @@ namespace {
 __global__ void __launch_bounds__(256)
 k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
                float *__restrict__ Acs, int64_t L, int H, int Q, int T, DtAct act,
-               float *__restrict__ dt_out) {
+               float *__restrict__ dt_out, const int2 *__restrict__ ctab) {
     const int64_t b = blockIdx.x / T;
     const int c = blockIdx.x % T;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (h >= H) return;  // wave-uniform
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;
     const int E = Q >= 64 ? Q / 64 : 1;  // tokens per lane (<= 4)
     const float a = A[h];
     float v[4];
@@ -74,15 +76,17 @@ __global__ void __launch_bounds__(256)
 k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
                       const float *__restrict__ dt, const float *__restrict__ Acs,
                       float *__restrict__ states, int64_t L, int H, int P, int N, int G, int Q,
-                      int T) {
+                      int T, const int2 *__restrict__ ctab) {
     __shared__ float w[256];
     const int h = blockIdx.x % H;
     const int64_t bc = blockIdx.x / H;
     const int c = (int)(bc % T);
     const int64_t b = bc / T;
     const int g = h / (H / G);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;
     const float *acs = Acs + (b * H + h) * L + t0;
     const float last = acs[q - 1];
     for (int j = threadIdx.x; j < q; j += 256)
@@ -118,10 +122,11 @@ k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
 // One thread per 4 consecutive state elements of one (b, h).
 __global__ void __launch_bounds__(256)
 k_state_passing(float *__restrict__ states, const float *__restrict__ Acs,
-                const float *init, float *fin, int64_t L, int H, int64_t PN, int Q, int T) {
+                const float *init, float *fin, int64_t L, int H, int64_t PN, int Q, int T,
+                const int2 *__restrict__ ctab, const int2 *__restrict__ sch) {
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
-    state_passing_body(states, Acs, init, fin, blockIdx.x, e, L, H, PN, Q, T);
+    state_passing_body(states, Acs, init, fin, blockIdx.x, e, L, H, PN, Q, T, ctab, sch);
 }
 
 // ----------------------------------------------------------- chunk scan
@@ -137,7 +142,7 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
                      const float *__restrict__ D, const float *__restrict__ Acs,
                      const float *__restrict__ states, Tin *__restrict__ y,
                      const Tin *__restrict__ z, int64_t L, int H, int P, int N, int G, int Q,
-                     int T) {
+                     int T, const int2 *__restrict__ ctab) {
     __shared__ float Ms[kScanRows][257];
     __shared__ float Cs[kScanRows][257];
     __shared__ float acs_s[256];
@@ -147,8 +152,9 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
     const int c = (int)(bc % T);
     const int64_t b = bc / T;
     const int g = h / (H / G);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
     const int i0 = blockIdx.y * kScanRows;
     if (i0 >= q) return;
     const int rows = min(kScanRows, q - i0);
@@ -191,6 +197,55 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
         if (z) yv *= silu_f(Elem<Tin>::ld(z, xi));
         Elem<Tin>::st(y, xi, yv);
     }
+}
+
+// ------------------------------------------------- variable-length batches
+// Chunk table of a packed batch of NS sequences from cu[0..NS] (the token
+// offsets of the sequences).  Sequence s covers tokens [cu[s], cu[s+1]) and
+// is cut into ceil(len/Q) chunks from its own first token, so no chunk spans
+// two sequences and every sequence starts from its own state.  Its chunks
+// take consecutive slots in sequence order: ctab[slot] = {first token,
+// length}, sch[s] = {first slot, slots}; slots past the last chunk get
+// length 0.  Offsets are clamped into [0, total] and slots past the end of
+// the table are dropped, so no offsets can lead a later kernel outside the
+// packed arrays (results for offsets that are not non-decreasing from 0 to
+// total are unspecified).  One block: each thread takes a contiguous range
+// of sequences, and a block prefix sum of the per-thread chunk counts places
+// them.
+__global__ void __launch_bounds__(1024)
+k_varlen_table(const int32_t *__restrict__ cu, int NS, int total, int Q, int slots,
+               int2 *__restrict__ ctab, int2 *__restrict__ sch) {
+    __shared__ int64_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (NS + 1023) / 1024;
+    const int s0 = min(NS, tid * per), s1 = min(NS, s0 + per);
+    auto start = [&](int s) { return min(max(cu[s], 0), total); };
+    auto length = [&](int s) { return max(0, min(cu[s + 1], total) - start(s)); };
+    // counts are 64-bit: offsets that overlap can add up to more than 2^31
+    int64_t cnt = 0;
+    for (int s = s0; s < s1; ++s) cnt += (length(s) + Q - 1) / Q;
+    int64_t v = cnt;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int64_t o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int64_t first = v - cnt, nall = 0;
+    for (int w = 0; w < 16; ++w) {
+        if (w < wave) first += wsum[w];
+        nall += wsum[w];
+    }
+    for (int s = s0; s < s1; ++s) {
+        const int t0 = start(s), len = length(s), nk = (len + Q - 1) / Q;
+        const int64_t room = max((int64_t)0, (int64_t)slots - first);
+        sch[s] = make_int2((int)min(first, (int64_t)slots), (int)min((int64_t)nk, room));
+        for (int j = 0; j < nk && j < room; ++j)
+            ctab[first + j] = make_int2(t0 + j * Q, min(Q, len - j * Q));
+        first += nk;
+    }
+    for (int64_t k = nall + tid; k < slots; k += 1024) ctab[k] = make_int2(0, 0);
 }
 
 // ----------------------------------------------------------- misc
@@ -486,7 +541,7 @@ void launch_chunk_cumsum(const ScanShape &s, const float *dt, const float *A, fl
                          hipStream_t st, const DtAct &act, float *dt_out) {
     dim3 grid((unsigned)(s.B * s.T), (unsigned)((s.H + 3) / 4));
     k_chunk_cumsum<<<grid, 256, 0, st>>>(dt, A, Acs, s.L, (int)s.H, (int)s.Q, (int)s.T, act,
-                                         dt_out);
+                                         dt_out, s.ctab);
 }
 
 void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const float *dt,
@@ -499,19 +554,21 @@ void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const
     if (s.dtype == SSD_BF16)
         k_chunk_state_generic<bf16><<<grid, 256, 0, st>>>(
             (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
-            (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
     else
         k_chunk_state_generic<float><<<grid, 256, 0, st>>>(
             (const float *)x, (const float *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
-            (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
 }
 
 void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
                           const float *init, float *fin, hipStream_t st) {
     const int64_t PN = s.P * s.N;
-    dim3 grid((unsigned)(s.B * s.H), (unsigned)((PN / 4 + 255) / 256));
+    const int64_t rows = s.sch ? s.NS : s.B;  // batch rows, or sequences
+    if (rows == 0) return;
+    dim3 grid((unsigned)(rows * s.H), (unsigned)((PN / 4 + 255) / 256));
     k_state_passing<<<grid, 256, 0, st>>>(states, Acs, init, fin, s.L, (int)s.H, PN,
-                                           (int)s.Q, (int)s.T);
+                                           (int)s.Q, (int)s.T, s.ctab, s.sch);
 }
 
 size_t chunk_scan_ws_bytes(const ScanShape &s) {
@@ -533,12 +590,18 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
     if (s.dtype == SSD_BF16)
         k_chunk_scan_generic<bf16><<<grid, 256, 0, st>>>(
             (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y,
-            (const bf16 *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T);
+            (const bf16 *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T,
+            s.ctab);
     else
         k_chunk_scan_generic<float><<<grid, 256, 0, st>>>(
             (const float *)x, dt, (const float *)Bm, (const float *)Cm, D, Acs, states,
             (float *)y, (const float *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q,
-            (int)s.T);
+            (int)s.T, s.ctab);
+}
+
+void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
+                         int2 *ctab, int2 *sch, hipStream_t st) {
+    k_varlen_table<<<1, 1024, 0, st>>>(cu, (int)NS, (int)total, (int)Q, (int)slots, ctab, sch);
 }
 
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {

@@ -10,6 +10,12 @@ namespace ssd {
 struct ScanShape {
     int64_t B, L, H, P, N, G, Q, T;  // T = ceil(L / Q)
     int dtype;                        // SSD_F32 or SSD_BF16
+    // Variable-length batches (null otherwise): B = 1, L = all tokens packed,
+    // T = chunk slots; ctab[T] = {first token, length} of every slot (length
+    // 0: unused), sch[NS] = {first slot, slots} of every sequence.
+    const int2 *ctab = nullptr;
+    const int2 *sch = nullptr;
+    int64_t NS = 0;
 };
 
 struct StepShape {
@@ -42,6 +48,11 @@ void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *w
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
                        const void *Cm, const float *D, const float *Acs, const float *states,
                        const void *ws, void *y, hipStream_t st, const void *z = nullptr);
+
+// Chunk table of a variable-length batch (ScanShape::ctab / sch) from the
+// sequences' token offsets cu[0..NS]; slots >= the number of chunks.
+void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
+                         int2 *ctab, int2 *sch, hipStream_t st);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);

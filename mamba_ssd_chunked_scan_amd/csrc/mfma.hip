@@ -180,7 +180,8 @@ __global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ A,
                    float *__restrict__ Acs, float *__restrict__ states, int64_t L, int H, int G,
-                   int T, int64_t nblocks, DtAct act, float *__restrict__ dt_out) {
+                   int T, int64_t nblocks, DtAct act, float *__restrict__ dt_out,
+                   const int2 *__restrict__ ctab) {
     constexpr int LDX = kP + 16;              // x stage row stride (bf16)
     constexpr int LDB = N + 16;               // B stage row stride (bf16)
     constexpr int NST = Q / kJT;              // stages per chunk
@@ -197,8 +198,10 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     const int h = ix.h, c = ix.c;
     const int64_t b = ix.b;
     const int g = h / (H / G);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
     const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
     const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     // per-thread offsets are unsigned 32-bit from block-uniform bases (a
@@ -334,7 +337,8 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
 template <int Q, int N>
 __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
                                         u32x4 *__restrict__ cb, u32x4 *__restrict__ cfr,
-                                        int64_t L, int G, int T, int64_t w) {
+                                        int64_t L, int G, int T, int64_t w,
+                                        const int2 *__restrict__ ctab) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     const int lane = threadIdx.x & 63, il = lane & 31, g2 = lane >> 5;
     const int tile = (int)(w % NT);
@@ -346,8 +350,10 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
     const int64_t bc = bcg / G;
     const int c = (int)(bc % T);
     const int64_t b = bc / T;
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
     const unsigned rs = G * N;
     const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
@@ -390,10 +396,10 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
 template <int Q, int N>
 __global__ void __launch_bounds__(256)
 k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 *__restrict__ cb,
-                int64_t L, int G, int T, int64_t ntiles) {
+                int64_t L, int G, int T, int64_t ntiles, const int2 *__restrict__ ctab) {
     const int64_t w = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= ntiles) return;
-    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w);
+    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w, ctab);
 }
 
 // The inter-chunk state pass and the C.B tiles in one launch: the first
@@ -405,17 +411,18 @@ __global__ void __launch_bounds__(256)
 k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, const float *init,
                    float *fin, int64_t L, int H, int64_t PN, int T, int64_t nsp, int ny,
                    const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-                   u32x4 *__restrict__ cb, int G, int64_t ntiles) {
+                   u32x4 *__restrict__ cb, int G, int64_t ntiles, const int2 *__restrict__ ctab,
+                   const int2 *__restrict__ sch) {
     const int64_t blk = blockIdx.x;
     if (blk < nsp) {
         const int64_t e = ((blk % ny) * 256 + threadIdx.x) * 4;
         if (e >= PN) return;
-        state_passing_body(states, Acs, init, fin, blk / ny, e, L, H, PN, Q, T);
+        state_passing_body(states, Acs, init, fin, blk / ny, e, L, H, PN, Q, T, ctab, sch);
         return;
     }
     const int64_t w = (blk - nsp) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= ntiles) return;
-    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w);
+    cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w, ctab);
 }
 
 // ------------------------------------------------------------- chunk scan
@@ -457,7 +464,8 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                   const float *__restrict__ D, const float *__restrict__ Acs,
                   const float *__restrict__ states, const u32x4 *__restrict__ cb,
                   const u32x4 *__restrict__ cfr, bf16 *__restrict__ y,
-                  const bf16 *__restrict__ z, int64_t L, int H, int G, int T, int64_t nblocks) {
+                  const bf16 *__restrict__ z, int64_t L, int H, int G, int T, int64_t nblocks,
+                  const int2 *__restrict__ ctab) {
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     constexpr int TH = Q * 2;             // threads: NI waves
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
@@ -488,8 +496,10 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     const int h = ix.h, c = ix.c;
     const int64_t b = ix.b;
     const int g = h / (H / G);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
     const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
     // per-thread offsets are unsigned 32-bit from block-uniform bases (a
     // chunk spans < 2^31 bytes of x and y), so loads and stores use the
@@ -805,7 +815,7 @@ void launch_state_t(const ScanShape &s, const void *x, const void *Bm, const flo
     const int64_t nb = s.B * s.T * s.H;
     k_chunk_state_mfma<Q, N, false><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)x, (const bf16 *)Bm, dt, nullptr, const_cast<float *>(Acs), states, s.L,
-        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr);
+        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr, s.ctab);
 }
 
 
@@ -814,7 +824,7 @@ void launch_cb_t(const ScanShape &s, const void *Bm, const void *Cm, void *cb, h
     constexpr int NI = Q / 32;
     const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
     k_chunk_cb_mfma<Q, N><<<(unsigned)((ntiles + 3) / 4), 256, 0, st>>>(
-        (const bf16 *)Bm, (const bf16 *)Cm, (u32x4 *)cb, s.L, (int)s.G, (int)s.T, ntiles);
+        (const bf16 *)Bm, (const bf16 *)Cm, (u32x4 *)cb, s.L, (int)s.G, (int)s.T, ntiles, s.ctab);
 }
 
 template <int Q, int N>
@@ -829,11 +839,11 @@ void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const voi
     if (z)
         k_chunk_scan_mfma<Q, N, true><<<padded_grid(nb), Q * 2, 0, st>>>(
             (const bf16 *)x, dt, D, Acs, states, cbt, cfr, (bf16 *)y, (const bf16 *)z, s.L,
-            (int)s.H, (int)s.G, (int)s.T, nb);
+            (int)s.H, (int)s.G, (int)s.T, nb, s.ctab);
     else
         k_chunk_scan_mfma<Q, N, false><<<padded_grid(nb), Q * 2, 0, st>>>(
             (const bf16 *)x, dt, D, Acs, states, cbt, cfr, (bf16 *)y, nullptr, s.L, (int)s.H,
-            (int)s.G, (int)s.T, nb);
+            (int)s.G, (int)s.T, nb, s.ctab);
 }
 
 // The whole chunked scan in three launches: chunk states with the in-block
@@ -847,14 +857,14 @@ void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const fl
     const int64_t nb = s.B * s.T * s.H;
     k_chunk_state_mfma<Q, N, true><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T,
-        nb, act, dt_out);
+        nb, act, dt_out, s.ctab);
     const int64_t PN = s.P * s.N;
     const int ny = (int)((PN / 4 + 255) / 256);
-    const int64_t nsp = s.B * s.H * ny;
+    const int64_t nsp = (s.sch ? s.NS : s.B) * s.H * ny;  // batch rows, or sequences
     const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
     k_state_passing_cb<Q, N><<<(unsigned)(nsp + (ntiles + 3) / 4), 256, 0, st>>>(
         states, Acs, init, fin, s.L, (int)s.H, PN, (int)s.T, nsp, ny, (const bf16 *)Bm,
-        (const bf16 *)Cm, (u32x4 *)cb, (int)s.G, ntiles);
+        (const bf16 *)Cm, (u32x4 *)cb, (int)s.G, ntiles, s.ctab, s.sch);
     launch_scan_t<Q, N>(s, x, dt_out ? dt_out : dt, Cm, D, Acs, states, cb, y, st, z);
 }
 

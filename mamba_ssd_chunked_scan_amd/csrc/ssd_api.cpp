@@ -103,6 +103,61 @@ ssd_status read_edges(const ssd_edges *e, ssd::DtAct *act, const void **z) {
 
 bool act_active(const ssd::DtAct &a) { return a.bias || a.softplus || a.limit; }
 
+// Chunk table and sequence table of a variable-length batch, after the rest.
+size_t varlen_table_bytes(const ScanShape &s) {
+    return round_up((size_t)s.T * 8) + round_up((size_t)s.NS * 8);
+}
+
+ssd_status check_varlen(const ssd_varlen_desc *d, ScanShape *s) {
+    if (!d) return SSD_ERR_NULL_PTR;
+    if (d->nseq < 0 || d->total < 0) return SSD_ERR_SHAPE;
+    ssd_status st = check_common(1, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype,
+                                 d->reserved);
+    if (st != SSD_OK) return st;
+    if (d->chunk < 16 || d->chunk > 256 || !pow2(d->chunk)) return SSD_ERR_UNSUPPORTED;
+    // token offsets and chunk slots are 32-bit in the chunk table
+    const int64_t lim = (int64_t(1) << 31) - 512;
+    if (d->total > lim || d->nseq > lim) return SSD_ERR_UNSUPPORTED;
+    const int64_t slots = d->total / d->chunk + d->nseq;  // >= sum of ceil(len / chunk)
+    if (slots > lim || (slots > 0 && d->nheads > kMaxBlocks / slots)) return SSD_ERR_UNSUPPORTED;
+    s->B = 1;
+    s->L = d->total;
+    s->H = d->nheads;
+    s->P = d->headdim;
+    s->N = d->dstate;
+    s->G = d->ngroups;
+    s->Q = d->chunk;
+    s->T = slots;
+    s->dtype = d->dtype;
+    s->NS = d->nseq;
+    return SSD_OK;
+}
+
+// The scan after argument checks: workspace = Acs | states | C.B tiles |
+// activated dt (layout of workspace_bytes).
+void run_scan(const ScanShape &s, const ssd::DtAct &act, const void *z, const void *x,
+              const float *dt, const float *A, const void *B, const void *C, const float *D,
+              const float *init_state, void *y, float *final_state, char *ws, hipStream_t hs) {
+    float *Acs = reinterpret_cast<float *>(ws);
+    float *states = reinterpret_cast<float *>(ws + acs_bytes(s));
+    void *scan_ws = ws + acs_bytes(s) + states_bytes(s);
+    float *dt_eff = act_active(act)
+                        ? reinterpret_cast<float *>(ws + acs_bytes(s) + states_bytes(s) +
+                                                    scan_ws_bytes(s))
+                        : nullptr;
+    if (ssd::mfma_supported(s)) {
+        ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
+                                    scan_ws, hs, act, dt_eff, z);
+    } else {
+        ssd::launch_chunk_cumsum(s, dt, A, Acs, hs, act, dt_eff);
+        const float *dts = dt_eff ? dt_eff : dt;
+        ssd::launch_chunk_state(s, x, B, dts, Acs, states, hs);
+        ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
+        ssd::launch_chunk_cb(s, B, C, scan_ws, hs);
+        ssd::launch_chunk_scan(s, x, dts, B, C, D, Acs, states, scan_ws, y, hs, z);
+    }
+}
+
 ssd_status after_launch() {
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
@@ -128,7 +183,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 3; }
+int ssd_abi_version(void) { return 4; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -164,26 +219,55 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     const size_t need = workspace_bytes(s);
     if (ws_bytes < need) return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
-    char *ws = static_cast<char *>(workspace);
-    float *Acs = reinterpret_cast<float *>(ws);
-    float *states = reinterpret_cast<float *>(ws + acs_bytes(s));
-    void *scan_ws = ws + acs_bytes(s) + states_bytes(s);
-    float *dt_eff = act_active(act)
-                        ? reinterpret_cast<float *>(ws + acs_bytes(s) + states_bytes(s) +
-                                                    scan_ws_bytes(s))
-                        : nullptr;
-    hipStream_t hs = as_stream(stream);
-    if (ssd::mfma_supported(s)) {
-        ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
-                                    scan_ws, hs, act, dt_eff, z);
-    } else {
-        ssd::launch_chunk_cumsum(s, dt, A, Acs, hs, act, dt_eff);
-        const float *dts = dt_eff ? dt_eff : dt;
-        ssd::launch_chunk_state(s, x, B, dts, Acs, states, hs);
-        ssd::launch_state_passing(s, states, Acs, init_state, final_state, hs);
-        ssd::launch_chunk_cb(s, B, C, scan_ws, hs);
-        ssd::launch_chunk_scan(s, x, dts, B, C, D, Acs, states, scan_ws, y, hs, z);
+    run_scan(s, act, z, x, dt, A, B, C, D, init_state, y, final_state,
+             static_cast<char *>(workspace), as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_varlen_workspace_size(const ssd_varlen_desc *d, size_t *bytes) {
+    if (!bytes) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_varlen(d, &s);
+    if (st != SSD_OK) return st;
+    *bytes = (s.NS == 0 || s.L == 0) ? 0 : workspace_bytes(s) + varlen_table_bytes(s);
+    return SSD_OK;
+}
+
+ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
+                               const int32_t *cu_seqlens, const void *x, const float *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *init_states, void *y, float *final_states,
+                               void *workspace, size_t ws_bytes, void *stream) {
+    ScanShape s;
+    ssd_status st = check_varlen(d, &s);
+    if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
+    if (st != SSD_OK) return st;
+    if (s.NS == 0) return SSD_OK;
+    if (s.L == 0) {  // every sequence is empty
+        st = check_ptrs({}, {init_states, final_states});
+        if (st != SSD_OK) return st;
+        if (final_states)
+            ssd::launch_copy_or_zero(final_states, init_states, s.NS * s.H * s.P * s.N,
+                                     as_stream(stream));
+        return after_launch();
     }
+    st = check_ptrs({cu_seqlens, x, dt, A, B, C, y},
+                    {D, init_states, final_states, workspace, z, act.bias});
+    if (st != SSD_OK) return st;
+    const size_t base = workspace_bytes(s);
+    if (ws_bytes < base + varlen_table_bytes(s)) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL_PTR;
+    char *ws = static_cast<char *>(workspace);
+    int2 *ctab = reinterpret_cast<int2 *>(ws + base);
+    int2 *sch = reinterpret_cast<int2 *>(ws + base + round_up((size_t)s.T * 8));
+    hipStream_t hs = as_stream(stream);
+    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, s.Q, s.T, ctab, sch, hs);
+    s.ctab = ctab;
+    s.sch = sch;
+    run_scan(s, act, z, x, dt, A, B, C, D, init_states, y, final_states, ws, hs);
     return after_launch();
 }
 

@@ -40,7 +40,8 @@ import torch
 
 __all__ = [
     "ScanSpec", "DecodeSpec", "WORKLOADS", "DECODE_WORKLOADS", "scan_inputs",
-    "DecodeStream", "custom_spec", "scan_edge_inputs", "edge_decode_inputs",
+    "DecodeStream", "custom_spec", "scan_edge_inputs", "edge_decode_inputs", "varlen_inputs",
+    "serving_lengths",
 ]
 
 
@@ -167,6 +168,46 @@ def edge_decode_inputs(batch, nsteps, nheads, headdim, dstate, ngroups, dtype, s
         "C": _storage(Cm, dtype),
         "D": torch.from_numpy(D.astype(np.float32)),
         "dt_bias": torch.from_numpy(np.log(np.expm1(dt0)).astype(np.float32)),
+        "gate": _storage(g, dtype),
+    }
+
+
+def serving_lengths(nseq: int, seed: int, lo: int = 16, hi: int = 4096) -> list[int]:
+    """Lengths of a ragged serving batch: log-uniform integers in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [int(v) for v in np.exp(rng.uniform(math.log(lo), math.log(hi + 1), size=nseq))]
+
+
+def varlen_inputs(lengths, nheads, headdim, dstate, ngroups, dtype, seed) -> dict:
+    """A packed ragged batch with the recipes above (dt rule "ranged", init
+    ~ N(0, 0.1) per sequence), plus the raw edge inputs: cu_seqlens int32
+    [nseq + 1], x [total, H, P], dt and dt_raw [total, H], B, C [total, G, N],
+    A, D, dt_bias [H], init [nseq, H, P, N], gate [total, H, P].
+    Draw order: x, B, C, z, u, D, dt0, init, gate."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = [int(v) for v in lengths]
+    total, nseq = sum(lengths), len(lengths)
+    H, P, N, G = nheads, headdim, dstate, ngroups
+    x = rng.standard_normal((total, H, P), dtype=np.float32)
+    Bm = rng.standard_normal((total, G, N), dtype=np.float32)
+    Cm = rng.standard_normal((total, G, N), dtype=np.float32)
+    z = rng.standard_normal((total, H), dtype=np.float32)
+    u = rng.uniform(0.0, math.log(16.0), size=H)
+    D = rng.standard_normal(H)
+    dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(0.1), size=H))
+    init = rng.standard_normal((nseq, H, P, N), dtype=np.float32) * np.float32(0.1)
+    g = rng.standard_normal((total, H, P), dtype=np.float32)
+    return {
+        "cu_seqlens": torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32),
+        "x": _storage(x, dtype),
+        "dt": torch.from_numpy(_dt(z, "ranged", dt0)),
+        "dt_raw": torch.from_numpy(z),
+        "A": torch.from_numpy((-np.exp(u)).astype(np.float32)),
+        "B": _storage(Bm, dtype),
+        "C": _storage(Cm, dtype),
+        "D": torch.from_numpy(D.astype(np.float32)),
+        "dt_bias": torch.from_numpy(np.log(np.expm1(dt0)).astype(np.float32)),
+        "init": torch.from_numpy(init),
         "gate": _storage(g, dtype),
     }
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 3
+    assert L.ssd_abi_version() == 4
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -251,6 +251,74 @@ def test_edges_null_is_plain(L):
     # a valid clamp and softplus with an empty batch: nothing to do
     e = ctypes.byref(edges(dt_softplus=1, dt_limit=1, dt_min=1e-3, dt_max=0.1))
     assert L.ssd_scan_fwd_ex(ctypes.byref(desc(batch=0)), e, *([None] * 10), 0, None) == OK
+
+
+def vdesc(**kw):
+    d = dict(nseq=3, total=700, nheads=8, headdim=64, dstate=128, ngroups=2, chunk=256,
+             dtype=1, reserved=0)
+    d.update(kw)
+    return binding.VarlenDesc(**d)
+
+
+def vwsize(L, d):
+    n = ctypes.c_size_t(12345)
+    st = L.ssd_varlen_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_varlen_workspace_size(L):
+    # the fixed-chunking workspace of one 700-token row with 700/256 + 3 = 5
+    # chunk slots (every sequence may end in a short chunk), then the chunk
+    # table (8 bytes a slot) and the sequence table (8 bytes a sequence)
+    slots = 700 // 256 + 3
+    acs = 8 * 700 * 4
+    states = slots * 8 * 64 * 128 * 4
+    cbw = slots * 2 * (36 * 4096 + 256 * 128 * 2)
+    st, n = vwsize(L, vdesc())
+    assert st == OK
+    assert n == r256(acs) + r256(states) + r256(cbw) + r256(acs) + r256(slots * 8) + r256(3 * 8)
+    assert vwsize(L, vdesc(nseq=0)) == (OK, 0)
+    assert vwsize(L, vdesc(total=0)) == (OK, 0)
+    assert L.ssd_varlen_workspace_size(ctypes.byref(vdesc()), None) == NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nseq=-1), SHAPE), (dict(total=-3), SHAPE), (dict(nheads=6, ngroups=4), SHAPE),
+    (dict(chunk=48), UNSUP), (dict(dstate=96), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(reserved=1), UNSUP), (dict(total=1 << 31), UNSUP), (dict(nseq=1 << 31), UNSUP),
+])
+def test_varlen_shape_errors(L, kw, status):
+    d = vdesc(**kw)
+    assert vwsize(L, d)[0] == status
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(d), None, *([P16] * 11), 1 << 30, None) == status
+
+
+def test_varlen_pointer_errors(L):
+    d = vdesc()
+    _, need = vwsize(L, d)
+    args = [P16] * 11   # cu x dt A B C D init y final ws
+    assert L.ssd_scan_fwd_varlen(None, None, *args, need, None) == NULL
+    for which in (0, 1, 2, 3, 4, 5, 8):   # required
+        a = list(args)
+        a[which] = None
+        assert L.ssd_scan_fwd_varlen(ctypes.byref(d), None, *a, need, None) == NULL
+    for which in range(11):
+        a = list(args)
+        a[which] = P_MIS
+        assert L.ssd_scan_fwd_varlen(ctypes.byref(d), None, *a, need, None) == ALIGN
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(d), None, *args, need - 1, None) == WS
+    a = list(args)
+    a[10] = None
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(d), None, *a, need, None) == NULL
+    e = ctypes.byref(edges(dt_limit=1, dt_min=1.0, dt_max=0.5))
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(d), e, *args, need, None) == UNSUP
+    # no sequences: nothing is touched
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(vdesc(nseq=0)), None, *([None] * 11), 0,
+                                 None) == OK
+    # no tokens: only the state pointers are checked
+    a = [None] * 11
+    a[7] = P_MIS
+    assert L.ssd_scan_fwd_varlen(ctypes.byref(vdesc(total=0)), None, *a, 0, None) == ALIGN
 
 
 def test_empty_batch_is_noop(L):
