@@ -223,6 +223,36 @@ def main():
                       P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
     edges_ms = time_launches(torch, call_edges, max(10, args.steps))
 
+    # ---- a ragged serving batch in one variable-length call, beside the
+    # same requests padded to the longest one in a fixed-length batch
+    lengths = synth.serving_lengths(32, seed=7)
+    vtot, vmax = sum(lengths), max(lengths)
+    vin = synth.varlen_inputs(lengths, H, P, N, 1, "bf16", seed=43)
+    vd = {k: v.to(dev).contiguous() for k, v in vin.items()}
+    vdesc = binding.VarlenDesc(len(lengths), vtot, H, P, N, 1, Q, binding.SSD_BF16, 0)
+    vwsb = binding.varlen_workspace_size(len(lengths), vtot, H, P, N, 1, Q, torch.bfloat16)
+    vws = torch.empty(max(vwsb, 1), dtype=torch.uint8, device=dev)
+    vy = torch.empty_like(vd["x"])
+    vfin = torch.empty((len(lengths), H, P, N), dtype=torch.float32, device=dev)
+    call_v = Lean(torch, lib.ssd_scan_fwd_varlen, ctypes.byref(vdesc), None,
+                  P_(vd["cu_seqlens"]), P_(vd["x"]), P_(vd["dt"]), P_(vd["A"]), P_(vd["B"]),
+                  P_(vd["C"]), P_(vd["D"]), P_(vd["init"]), P_(vy), P_(vfin), P_(vws), vws.numel())
+    varlen_ms = time_launches(torch, call_v, 10)
+    pB = len(lengths)
+    pdesc = binding.ScanDesc(pB, vmax, H, P, N, 1, Q, binding.SSD_BF16, 0)
+    pws = torch.empty(ssd.workspace_size(pB, vmax, H, P, N, 1, Q, torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
+    px = torch.zeros((pB, vmax, H, P), dtype=torch.bfloat16, device=dev)
+    pdt = torch.zeros((pB, vmax, H), dtype=torch.float32, device=dev)
+    pbc = torch.zeros((pB, vmax, 1, N), dtype=torch.bfloat16, device=dev)
+    py = torch.empty_like(px)
+    pfin = torch.empty((pB, H, P, N), dtype=torch.float32, device=dev)
+    call_p = Lean(torch, lib.ssd_scan_fwd, ctypes.byref(pdesc), P_(px), P_(pdt), P_(vd["A"]),
+                  P_(pbc), P_(pbc), P_(vd["D"]), P_(vd["init"]), P_(py), P_(pfin), P_(pws),
+                  pws.numel())
+    padded_ms = time_launches(torch, call_p, 5)
+    del px, py, pws
+
     # ---- per-stage launch times (HIP events around graph replays)
     Tn = spec.nchunks
     Acs = torch.empty((Bt, H, L), dtype=torch.float32, device=dev)
@@ -366,6 +396,12 @@ def main():
                     "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),
                     "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()}},
         "decode": decode,
+        "varlen": {"workload": f"{len(lengths)} requests, log-uniform lengths in [16, 4096] "
+                               f"(total {vtot}, longest {vmax}), 2.7B head shape, bf16",
+                   "us_per_call_graph": round(varlen_ms * 1e3, 2),
+                   "tokens_per_s": round(vtot / (varlen_ms * 1e-3), 1),
+                   "padded_batch_us_per_call_graph": round(padded_ms * 1e3, 2),
+                   "speedup_vs_padded": round(padded_ms / varlen_ms, 2)},
         "copy_GB_s": round(copy_gbs, 1),
         "frac_of_copy": {f"prefill_{dom}": round(dom_gbs / copy_gbs, 4),
                          "decode_batch64": round(decode["batch64"]["GB_s"] / copy_gbs, 4)},
