@@ -6,6 +6,7 @@ two share no code.
 
 * :func:`scan` / :func:`step` wrap the fp64 token-by-token recurrence in
   ``ssd_oracle.c`` (the definition of the operation).
+* :func:`scan_vjp` is the gradient of the scan (adjoint recurrence, fp64).
 * :func:`scan_varlen` runs a packed ragged batch sequence by sequence.
 * :mod:`oracle.edges` holds the fp64 dt activation and output gate.
 * :mod:`oracle.chunked` is an fp64 numpy version of the chunked algorithm
@@ -53,6 +54,8 @@ def _load():
         lib.ssd_oracle_scan.restype = ctypes.c_int
         lib.ssd_oracle_step.argtypes = [_I64] * 5 + [_D] * 8 + [ctypes.c_int]
         lib.ssd_oracle_step.restype = ctypes.c_int
+        lib.ssd_oracle_scan_vjp.argtypes = [_I64] * 6 + [_D] * 16 + [ctypes.c_int]
+        lib.ssd_oracle_scan_vjp.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.argtypes = []
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -160,3 +163,24 @@ def scan_varlen(cu_seqlens, x, dt, A, B, C, D=None, init=None, nthreads: int = 0
         y[a:b] = ys[0]
         finals[s] = fs[0]
     return y, finals
+
+
+def scan_vjp(x, dt, A, B, C, D=None, init=None, dy=None, dfinal=None, nthreads: int = 0) -> dict:
+    """Gradients of J = sum(dy * y) + sum(dfinal * final_state) with respect to
+    x, dt, A, B, C, D and init, by the adjoint recurrence in ssd_oracle.c.
+    dy is required; dfinal may be None (no final-state term).  Returns a dict
+    of float64 arrays: dx, ddt, dA, dB, dC, dD, dinit."""
+    x, dt, A, B, C, D, init, dy, dfinal = (f64(v) for v in (x, dt, A, B, C, D, init, dy, dfinal))
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape and (dfinal is None or dfinal.shape == (Bt, H, P, N))
+    out = {"dx": np.empty_like(x), "ddt": np.empty((Bt, L, H)), "dA": np.empty(H),
+           "dB": np.empty((Bt, L, G, N)), "dC": np.empty((Bt, L, G, N)), "dD": np.empty(H),
+           "dinit": np.empty((Bt, H, P, N))}
+    rc = _load().ssd_oracle_scan_vjp(
+        Bt, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
+        _ptr(dy), _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle vjp failed ({rc})")
+    return out

@@ -146,3 +146,111 @@ int ssd_oracle_step(int64_t Bt, int64_t H, int64_t P, int64_t N, int64_t G,
     }
     return 0;
 }
+
+/* Gradients of the scan (its vector-Jacobian product).  For the scalar
+ *     J = sum(dy * y) + sum(dfinal * final_state)
+ * the gradient with respect to every input, by the adjoint recurrence of the
+ * loop above run backwards in time.  Per (b, h, p) row, with lam the
+ * derivative of J with respect to the state s_t after token t:
+ *
+ *     lam   <- dfinal[b,h,p,:]                    (zero when dfinal is NULL)
+ *     for t = L-1 .. 0:   (r_t = exp(dt_t a), s_t the forward state, s_{-1} = init)
+ *         lam[n]  += dy[t,p] * C_t[n]              (y_t reads s_t)
+ *         dx[t,p]  = dt_t * sum_n B_t[n] lam[n] + D * dy[t,p]
+ *         dB_t[n] += dt_t * x[t,p] * lam[n]        (summed over heads of the group)
+ *         dC_t[n] += dy[t,p] * s_t[n]
+ *         ddt_t   += sum_n lam[n] * (x[t,p] B_t[n] + a r_t s_{t-1}[n])
+ *         dA      += sum_n lam[n] * dt_t r_t s_{t-1}[n]
+ *         dD      += dy[t,p] * x[t,p]
+ *         lam[n]  *= r_t                           (s_t = r_t s_{t-1} + ...)
+ *     dinit[b,h,p,:] = lam
+ *
+ * since s_t = r_t s_{t-1} + dt_t x_t B_t with r_t = exp(dt_t a) gives
+ * ds_t/ddt_t = a r_t s_{t-1} + x_t B_t and ds_t/da = dt_t r_t s_{t-1}.  The
+ * forward states of a row are recomputed and kept (L+1 vectors of N).
+ * Parallel over batch rows only; heads, channels and the per-head sums over
+ * batch rows run in a fixed order, so the result is deterministic.
+ * dfinal, D and init may be NULL; every output is written (dD even when D is
+ * NULL).  Returns 0, -1 for an invalid shape, -2 when out of memory. */
+int ssd_oracle_scan_vjp(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                        const double *x, const double *dt, const double *A,
+                        const double *Bm, const double *Cm, const double *D,
+                        const double *init, const double *dy, const double *dfinal,
+                        double *dx, double *ddt, double *dA, double *dB, double *dC,
+                        double *dD, double *dinit, int nthreads)
+{
+    if (bad_shape(Bt, H, P, N, G) || L < 0) return -1;
+    set_threads(nthreads);
+    const int64_t R = H / G;
+    /* per batch row partial sums of dA and dD, reduced in order afterwards */
+    double *pA = (double *)calloc((size_t)(Bt > 0 ? Bt : 1) * H, sizeof(double));
+    double *pD = (double *)calloc((size_t)(Bt > 0 ? Bt : 1) * H, sizeof(double));
+    if (!pA || !pD) { free(pA); free(pD); return -2; }
+    for (int64_t i = 0; i < Bt * L * G * N; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+    for (int64_t i = 0; i < Bt * L * H; ++i) ddt[i] = 0.0;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|:err)
+    for (int64_t b = 0; b < Bt; ++b) {
+        double *S = (double *)malloc((size_t)(L + 1) * N * sizeof(double));
+        double *lam = (double *)malloc((size_t)N * sizeof(double));
+        if (!S || !lam) { free(S); free(lam); err |= 1; continue; }
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t g = h / R;
+            const double a = A[h];
+            const double Dh = D ? D[h] : 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t sbase = ((b * H + h) * P + p) * N;
+                /* forward states: S[t+1] is s_t, S[0] is s_{-1} */
+                for (int64_t n = 0; n < N; ++n) S[n] = init ? init[sbase + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t bt = b * L + t;
+                    const double dtv = dt[bt * H + h];
+                    const double r = exp(dtv * a);
+                    const double u = dtv * x[(bt * H + h) * P + p];
+                    const double *Brow = Bm + (bt * G + g) * N;
+                    for (int64_t n = 0; n < N; ++n)
+                        S[(t + 1) * N + n] = r * S[t * N + n] + u * Brow[n];
+                }
+                for (int64_t n = 0; n < N; ++n) lam[n] = dfinal ? dfinal[sbase + n] : 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    const int64_t bt = b * L + t;
+                    const double dtv = dt[bt * H + h];
+                    const double r = exp(dtv * a);
+                    const double xv = x[(bt * H + h) * P + p];
+                    const double dyv = dy[(bt * H + h) * P + p];
+                    const double *Brow = Bm + (bt * G + g) * N;
+                    const double *Crow = Cm + (bt * G + g) * N;
+                    const double *s_t = S + (t + 1) * N, *s_prev = S + t * N;
+                    double *dBrow = dB + (bt * G + g) * N, *dCrow = dC + (bt * G + g) * N;
+                    double bl = 0.0, ddt_acc = 0.0, da_acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        lam[n] += dyv * Crow[n];
+                        bl += Brow[n] * lam[n];
+                        dBrow[n] += dtv * xv * lam[n];
+                        dCrow[n] += dyv * s_t[n];
+                        ddt_acc += lam[n] * (xv * Brow[n] + a * r * s_prev[n]);
+                        da_acc += lam[n] * dtv * r * s_prev[n];
+                    }
+                    dx[(bt * H + h) * P + p] = dtv * bl + Dh * dyv;
+                    ddt[bt * H + h] += ddt_acc;
+                    pA[b * H + h] += da_acc;
+                    pD[b * H + h] += dyv * xv;
+                    for (int64_t n = 0; n < N; ++n) lam[n] *= r;
+                }
+                if (dinit)
+                    for (int64_t n = 0; n < N; ++n) dinit[sbase + n] = lam[n];
+            }
+        }
+        free(S);
+        free(lam);
+    }
+    for (int64_t h = 0; h < H; ++h) {
+        double sa = 0.0, sd = 0.0;
+        for (int64_t b = 0; b < Bt; ++b) { sa += pA[b * H + h]; sd += pD[b * H + h]; }
+        dA[h] = sa;
+        if (dD) dD[h] = sd;
+    }
+    free(pA);
+    free(pD);
+    return err ? -2 : 0;
+}

@@ -1,0 +1,69 @@
+"""Pins for the oracle's gradient (adjoint recurrence): every input's
+gradient against central finite differences of the forward oracle (itself
+pinned in test_oracle.py), along random directions, in fp64.
+
+J(theta) = sum(dy * y) + sum(dfinal * final); for a direction V of input X,
+(J(X + eps V) - J(X - eps V)) / (2 eps) = <dJ/dX, V> + O(eps^2)."""
+import numpy as np
+import pytest
+
+import oracle
+from mamba_ssd_chunked_scan_amd import synth
+
+KEYS = ("x", "dt", "A", "B", "C", "D", "init")
+
+
+def problem(Bt, L, H, P, N, G, seed):
+    spec = synth.custom_spec(Bt, L, H, P, N, G, chunk=16, dtype="f32", dt_rule="shifted",
+                             init="normal", seed=seed)
+    inp = {k: oracle.f64(v) for k, v in synth.scan_inputs(spec).items()}
+    rng = np.random.default_rng(seed + 100)
+    dy = rng.standard_normal(inp["x"].shape)
+    dfinal = rng.standard_normal(inp["init"].shape)
+    return inp, dy, dfinal
+
+
+def J(inp, dy, dfinal):
+    y, fin = oracle.scan(**inp)
+    return float(np.sum(dy * y) + np.sum(dfinal * fin))
+
+
+@pytest.mark.parametrize("Bt,L,H,P,N,G", [(2, 13, 4, 3, 5, 2), (1, 40, 2, 2, 4, 1)])
+def test_vjp_matches_finite_differences(Bt, L, H, P, N, G):
+    inp, dy, dfinal = problem(Bt, L, H, P, N, G, seed=L)
+    g = oracle.scan_vjp(**inp, dy=dy, dfinal=dfinal)
+    rng = np.random.default_rng(7)
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "init": "dinit"}
+    for k in KEYS:
+        V = rng.standard_normal(inp[k].shape)
+        eps = 1e-6 * max(1.0, float(np.max(np.abs(inp[k]))))
+        plus = dict(inp, **{k: inp[k] + eps * V})
+        minus = dict(inp, **{k: inp[k] - eps * V})
+        fd = (J(plus, dy, dfinal) - J(minus, dy, dfinal)) / (2 * eps)
+        an = float(np.sum(g[names[k]] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, fd, an)
+
+
+def test_vjp_without_final_term_and_without_D():
+    """dfinal = None drops the final-state term; D = None gives the same dx as
+    D = 0, and dD is still the gradient a D would receive."""
+    inp, dy, _ = problem(1, 20, 2, 3, 4, 1, seed=3)
+    g1 = oracle.scan_vjp(**inp, dy=dy, dfinal=None)
+    g0 = oracle.scan_vjp(**inp, dy=dy, dfinal=np.zeros_like(inp["init"]))
+    for k in g1:
+        assert np.array_equal(g1[k], g0[k]), k
+    noD = dict(inp, D=None)
+    zD = dict(inp, D=np.zeros_like(inp["D"]))
+    a, b = oracle.scan_vjp(**noD, dy=dy), oracle.scan_vjp(**zD, dy=dy)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    # dD is the sum over tokens and channels of dy * x
+    assert np.allclose(a["dD"], np.einsum("blhp,blhp->h", dy, inp["x"]), rtol=1e-13)
+
+
+def test_vjp_is_deterministic():
+    inp, dy, dfinal = problem(3, 17, 4, 2, 4, 2, seed=9)
+    a = oracle.scan_vjp(**inp, dy=dy, dfinal=dfinal, nthreads=3)
+    b = oracle.scan_vjp(**inp, dy=dy, dfinal=dfinal, nthreads=1)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
