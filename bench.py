@@ -223,6 +223,46 @@ def main():
                       P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
     edges_ms = time_launches(torch, call_edges, max(10, args.steps))
 
+    # ---- the gradient (ssd_scan_bwd) at this workload, and forward plus
+    # backward at the 130M head shape with 512 tokens
+    def bwd_case(bspec, binp):
+        bd = {k: (None if v is None else v.to(dev).contiguous()) for k, v in binp.items()}
+        bB, bL, bH, bP, bN, bG, bQ = (bspec.batch, bspec.seqlen, bspec.nheads, bspec.headdim,
+                                      bspec.dstate, bspec.ngroups, bspec.chunk)
+        bdesc = binding.ScanDesc(bB, bL, bH, bP, bN, bG, bQ, binding.SSD_BF16, 0)
+        gdy = torch.randn_like(bd["x"].float()).to(bd["x"].dtype)
+        f32 = dict(dtype=torch.float32, device=dev)
+        outs = [torch.empty_like(bd["x"]), torch.empty((bB, bL, bH), **f32),
+                torch.empty(bH, **f32), torch.empty((bB, bL, bG, bN), **f32),
+                torch.empty((bB, bL, bG, bN), **f32), torch.empty(bH, **f32),
+                torch.empty((bB, bH, bP, bN), **f32)]
+        nb = ctypes.c_size_t(0)
+        lib.ssd_scan_bwd_workspace_size(ctypes.byref(bdesc), ctypes.byref(nb))
+        bws = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=dev)
+        init_ = bd["init"]
+        dfin = torch.randn((bB, bH, bP, bN), **f32)
+        fn_b = Lean(torch, lib.ssd_scan_bwd, ctypes.byref(bdesc), P_(bd["x"]), P_(bd["dt"]),
+                    P_(bd["A"]), P_(bd["B"]), P_(bd["C"]), P_(bd["D"]),
+                    None if init_ is None else P_(init_), P_(gdy), P_(dfin),
+                    *[P_(o) for o in outs], P_(bws), bws.numel())
+        fws = torch.empty(ssd.workspace_size(bB, bL, bH, bP, bN, bG, bQ, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        fy = torch.empty_like(bd["x"])
+        ffin = torch.empty((bB, bH, bP, bN), **f32)
+        fn_f = Lean(torch, lib.ssd_scan_fwd, ctypes.byref(bdesc), P_(bd["x"]), P_(bd["dt"]),
+                    P_(bd["A"]), P_(bd["B"]), P_(bd["C"]), P_(bd["D"]),
+                    None if init_ is None else P_(init_), P_(fy), P_(ffin), P_(fws),
+                    fws.numel())
+        b_ms = time_launches(torch, fn_b, 10)
+        f_ms = time_launches(torch, fn_f, 10)
+        return {"fwd_us": round(f_ms * 1e3, 2), "bwd_us": round(b_ms * 1e3, 2),
+                "fwd_plus_bwd_us": round((f_ms + b_ms) * 1e3, 2),
+                "bwd_tokens_per_s": round(bB * bL / (b_ms * 1e-3), 1)}
+    grad = {"m2p7b_4096": bwd_case(spec, inp)}
+    s130 = synth.custom_spec(1, 512, 24, 64, 128, 1, chunk=256, dtype="bf16", dt_rule="ranged",
+                             init="zero", seed=2, name="m130m_512")
+    grad["m130m_512"] = bwd_case(s130, synth.scan_inputs(s130))
+
     # ---- a ragged serving batch in one variable-length call, beside the
     # same requests padded to the longest one in a fixed-length batch
     lengths = synth.serving_lengths(32, seed=7)
@@ -396,6 +436,9 @@ def main():
                     "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),
                     "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()}},
         "decode": decode,
+        "gradient": dict(grad, note="ssd_scan_bwd: dx, ddt, dA, dB, dC, dD, dinit of a random "
+                                         "upstream dy and dfinal; graph-replayed; m130m_512 is "
+                                         "the 130M head shape (24 heads) at 512 tokens, batch 1"),
         "varlen": {"workload": f"{len(lengths)} requests, log-uniform lengths in [16, 4096] "
                                f"(total {vtot}, longest {vmax}), 2.7B head shape, bf16",
                    "us_per_call_graph": round(varlen_ms * 1e3, 2),

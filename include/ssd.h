@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -117,6 +117,39 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         const float *A, const void *B, const void *C, const float *D,
                         const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- gradient */
+
+/* Bytes of device workspace ssd_scan_bwd needs for shape *d. */
+ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes);
+
+/* Gradient of ssd_scan_fwd, for training ("Compiler-First ...", B.5 times
+ * forward plus backward): for the scalar
+ *     J = sum(dy * y) + sum(dfinal * final_state)
+ * (dy and dfinal the derivatives arriving from above), the derivatives of J
+ * with respect to every input of the forward call.  Inputs are the forward
+ * call's (same layouts; the forward outputs are not needed: the chunk states
+ * are recomputed) plus
+ *   dy      [batch, seqlen, nheads, headdim]  dtype
+ *   dfinal  [batch, nheads, headdim, dstate]  fp32, or NULL (no final-state term)
+ * Outputs (all overwritten):
+ *   dx      [batch, seqlen, nheads, headdim]  dtype
+ *   ddt     [batch, seqlen, nheads]           fp32
+ *   dA      [nheads]                          fp32
+ *   dB, dC  [batch, seqlen, ngroups, dstate]  fp32 (summed over the heads of a group)
+ *   dD      [nheads] fp32, or NULL (not computed)
+ *   dinit   [batch, nheads, headdim, dstate]  fp32, or NULL (not computed)
+ * dt is the activated step size (the edges of ssd_scan_fwd_ex are not
+ * differentiated here).  The kernels tile by 32 tokens whatever d->chunk is;
+ * like the forward, the result does not depend on the chunk beyond rounding.
+ * dB, dC, dA and dD are accumulated with floating-point atomics, so their
+ * last bits may differ between runs.  seqlen == 0 or batch == 0: dA = dD = 0
+ * and dinit = dfinal (or 0). */
+ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        const void *dy, const float *dfinal, void *dx, float *ddt, float *dA,
+                        float *dB, float *dC, float *dD, float *dinit, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------- fused scan edges */
 

@@ -25,7 +25,8 @@ _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
            "ssd_step", "ssd_step_multi", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
-           "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen")
+           "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen",
+           "ssd_scan_bwd_workspace_size", "ssd_scan_bwd")
 
 
 class ScanDesc(ctypes.Structure):
@@ -97,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_fwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
                                       + [_P] * 10 + [ctypes.c_size_t, _P])
         L.ssd_step_ex.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(Edges)] + [_P] * 9
+        L.ssd_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 17 + [ctypes.c_size_t, _P]
         L.ssd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
@@ -242,6 +246,43 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
                                _ptr(workspace), workspace.numel(), _stream(dev))
     _check("ssd_scan_fwd_ex", st)
     return y, final_state
+
+
+def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: int = 256,
+             workspace=None) -> dict:
+    """Gradient of :func:`scan_fwd`: derivatives of sum(dy * y) + sum(dfinal *
+    final_state) with respect to x, dt, A, B, C, D and init_state.  Returns a
+    dict: dx (x's dtype), ddt, dA, dB, dC (fp32), dD (None without D) and
+    dinit (None without init_state and dfinal)."""
+    Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
+    dev = x.device
+    _need(dy, "dy", x.shape, x.dtype, dev)
+    if init_state is not None:
+        _need(init_state, "init_state", (Bt, H, P, N), torch.float32, dev)
+    if dfinal is not None:
+        _need(dfinal, "dfinal", (Bt, H, P, N), torch.float32, dev)
+    desc = _scan_desc(x, B, chunk)
+    n = ctypes.c_size_t(0)
+    _check("ssd_scan_bwd_workspace_size",
+           lib().ssd_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < n.value or workspace.device != dev:
+        raise ValueError(f"workspace needs {n.value} bytes on {dev}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty((Bt, L, H), **f32),
+           "dA": torch.empty(H, **f32), "dB": torch.empty((Bt, L, G, N), **f32),
+           "dC": torch.empty((Bt, L, G, N), **f32),
+           "dD": torch.empty(H, **f32) if D is not None else None,
+           "dinit": (torch.empty((Bt, H, P, N), **f32)
+                     if init_state is not None or dfinal is not None else None)}
+    st = lib().ssd_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                            _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
+                            _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                            _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace),
+                            workspace.numel(), _stream(dev))
+    _check("ssd_scan_bwd", st)
+    return out
 
 
 def varlen_workspace_size(nseq, total, nheads, headdim, dstate, ngroups, chunk, dtype) -> int:

@@ -9,6 +9,8 @@
 // a within-chunk cumulative log-decay, each chunk's own state, a sequential
 // pass of states across chunks, and the chunk output from its diagonal block
 // plus the entering state.
+#include <algorithm>
+
 #include "common.hpp"
 #include "stages.hpp"
 #include "launch.hpp"
@@ -70,14 +72,22 @@ k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
 
 // ---------------------------------------------------------- chunk state
 // states[b,c,h,p,n] = sum_j x[j,p] * w_j * B[j,n],  w_j = dt_j exp(Acs_last - Acs_j).
-// One block per (b, c, h) and 1024 outputs; thread k-loop over the chunk.
-template <typename Tin>
+// kAdjoint (the gradient's chunk term, with x = dy and B = C): w_j = exp(Acs_j),
+// the decay from the chunk's entering state to token j.
+// One block per (b, c, h) and PB = min(P, 4096/N) rows of p; each thread
+// owns a 4 x 4 (p, n) tile.  The chunk streams through LDS 32 tokens at a
+// time (x rows restricted to the block's p range, whole B rows, both fp32),
+// so each token costs a thread two 16-byte LDS reads for 16 FMAs.
+constexpr int kStateJT = 32;
+
+template <typename Tin, bool kAdjoint = false>
 __global__ void __launch_bounds__(256)
 k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
                       const float *__restrict__ dt, const float *__restrict__ Acs,
                       float *__restrict__ states, int64_t L, int H, int P, int N, int G, int Q,
                       int T, const int2 *__restrict__ ctab) {
     __shared__ float w[256];
+    extern __shared__ __attribute__((aligned(16))) float st_sm[];
     const int h = blockIdx.x % H;
     const int64_t bc = blockIdx.x / H;
     const int c = (int)(bc % T);
@@ -87,35 +97,66 @@ k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
     const int64_t t0 = cp.t0;
     const int q = cp.q;
     if (q <= 0) return;
+    const int PB = min(P, 4096 / N);          // rows of p in this block
+    const int p0 = blockIdx.y * PB;
+    const int pb = min(PB, P - p0);
+    const int PBS = (PB + 3) & ~3;            // LDS row stride of x (16-byte rows)
+    float *xs = st_sm;                        // [JT][PBS]
+    float *bs = xs + kStateJT * PBS;          // [JT][N]
     const float *acs = Acs + (b * H + h) * L + t0;
     const float last = acs[q - 1];
     for (int j = threadIdx.x; j < q; j += 256)
-        w[j] = dt[(b * L + t0 + j) * H + h] * ssd_exp(last - acs[j]);
-    __syncthreads();
-    const int64_t PN = (int64_t)P * N;
-    int pe[4], ne[4];
-    bool ok[4];
-    float acc[4];
+        w[j] = kAdjoint ? ssd_exp(acs[j]) : dt[(b * L + t0 + j) * H + h] * ssd_exp(last - acs[j]);
+    const int nq = N / 4;
+    const int ni = threadIdx.x % nq, pi = threadIdx.x / nq;
+    const bool active = 4 * pi < pb;
+    float acc[4][4] = {};
+    const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
+    const Tin *xb = x + ((b * L + t0) * H + h) * P + p0;
+    const Tin *bb = Bm + ((b * L + t0) * G + g) * N;
+    for (int j0 = 0; j0 < q; j0 += kStateJT) {
+        const int jn = min(kStateJT, q - j0);
+        __syncthreads();  // w ready / the previous tile no longer read
+        for (int e = threadIdx.x; e < jn * PBS; e += 256) {
+            const int j = e / PBS, pl = e - j * PBS;
+            xs[e] = pl < pb ? Elem<Tin>::ld(xb, (j0 + j) * xrow + pl) : 0.f;
+        }
+        for (int e = threadIdx.x; e < jn * N; e += 256) {
+            const int j = e / N, n = e - j * N;
+            bs[e] = Elem<Tin>::ld(bb, (j0 + j) * brow + n);
+        }
+        __syncthreads();
+        if (active) {
+            for (int j = 0; j < jn; ++j) {
+                const float wj = w[j0 + j];
+                const float4 xv = *reinterpret_cast<const float4 *>(&xs[j * PBS + 4 * pi]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&bs[j * N + 4 * ni]);
+                const float xw[4] = {xv.x * wj, xv.y * wj, xv.z * wj, xv.w * wj};
+                const float bb4[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t e = (int64_t)blockIdx.y * 1024 + threadIdx.x + 256 * k;
-        ok[k] = e < PN;
-        pe[k] = ok[k] ? (int)(e / N) : 0;
-        ne[k] = ok[k] ? (int)(e % N) : 0;
-        acc[k] = 0.f;
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) acc[a][k] = fmaf(xw[a], bb4[k], acc[a][k]);
+            }
+        }
     }
-    for (int j = 0; j < q; ++j) {
-        const Tin *xr = x + ((b * L + t0 + j) * H + h) * P;
-        const Tin *br = Bm + ((b * L + t0 + j) * G + g) * N;
-        const float wj = w[j];
+    if (!active) return;
+    float *out = states + (((b * T + c) * H + h) * (int64_t)P + p0 + 4 * pi) * N + 4 * ni;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (ok[k]) acc[k] += (Elem<Tin>::ld(xr, pe[k]) * wj) * Elem<Tin>::ld(br, ne[k]);
-    }
-    float *out = states + (((b * T + c) * H + h) * PN);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        if (ok[k]) out[(int64_t)pe[k] * N + ne[k]] = acc[k];
+    for (int a = 0; a < 4; ++a)
+        if (4 * pi + a < pb)
+            *reinterpret_cast<float4 *>(out + (int64_t)a * N) =
+                make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+}
+
+// LDS bytes and grid of k_chunk_state_generic.
+size_t state_generic_lds(const ScanShape &s) {
+    const int64_t PB = std::min<int64_t>(s.P, 4096 / s.N);
+    return (size_t)kStateJT * (((PB + 3) & ~3LL) + s.N) * 4;
+}
+dim3 state_generic_grid(const ScanShape &s) {
+    const int64_t PB = std::min<int64_t>(s.P, 4096 / s.N);
+    return dim3((unsigned)(s.B * s.T * s.H), (unsigned)((s.P + PB - 1) / PB));
 }
 
 // -------------------------------------------------------- state passing
@@ -127,6 +168,52 @@ k_state_passing(float *__restrict__ states, const float *__restrict__ Acs,
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
     state_passing_body(states, Acs, init, fin, blockIdx.x, e, L, H, PN, Q, T, ctab, sch);
+}
+
+// Reverse pass of the gradient's chunk terms: per (b, h) and 4 consecutive
+// state elements, from the last chunk to the first, E <- dfinal (or 0); slot
+// c receives E, the derivative with respect to the state at the end of chunk
+// c, then E <- exp(Acs at the end of chunk c) E + dS_c (the derivative with
+// respect to the state entering chunk c).  What is left is the derivative
+// with respect to the initial state.  Loads run kPassAhead chunks ahead.
+__global__ void __launch_bounds__(256)
+k_state_passing_rev(float *__restrict__ ds, const float *__restrict__ Acs,
+                    const float *__restrict__ dfin, float *__restrict__ dinit, int64_t L, int H,
+                    int64_t PN, int Q, int T) {
+    const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+    if (e >= PN) return;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / H;
+    const int h = (int)(bh % H);
+    float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (dfin) E = *reinterpret_cast<const float4 *>(dfin + bh * PN + e);
+    const float *acs = Acs + bh * L;
+    const int64_t cstride = (int64_t)H * PN;
+    float *base = ds + (b * T * H + h) * PN + e;
+    for (int c0 = T - 1; c0 >= 0; c0 -= kPassAhead) {
+        float4 sv[kPassAhead];
+        float r[kPassAhead];
+#pragma unroll
+        for (int k = 0; k < kPassAhead; ++k) {
+            const int c = c0 - k;
+            if (c >= 0) {
+                sv[k] = *reinterpret_cast<const float4 *>(base + c * cstride);
+                r[k] = ssd_exp(acs[min(L, (int64_t)(c + 1) * Q) - 1]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPassAhead; ++k) {
+            const int c = c0 - k;
+            if (c >= 0) {
+                *reinterpret_cast<float4 *>(base + c * cstride) = E;
+                E.x = r[k] * E.x + sv[k].x;
+                E.y = r[k] * E.y + sv[k].y;
+                E.z = r[k] * E.z + sv[k].z;
+                E.w = r[k] * E.w + sv[k].w;
+            }
+        }
+    }
+    if (dinit) *reinterpret_cast<float4 *>(dinit + bh * PN + e) = E;
 }
 
 // ----------------------------------------------------------- chunk scan
@@ -550,15 +637,38 @@ void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const
         launch_chunk_state_mfma(s, x, Bm, dt, Acs, states, st);
         return;
     }
-    dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.P * s.N + 1023) / 1024));
+    const dim3 grid = state_generic_grid(s);
+    const size_t lds = state_generic_lds(s);
     if (s.dtype == SSD_BF16)
-        k_chunk_state_generic<bf16><<<grid, 256, 0, st>>>(
+        k_chunk_state_generic<bf16><<<grid, 256, lds, st>>>(
             (const bf16 *)x, (const bf16 *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
             (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
     else
-        k_chunk_state_generic<float><<<grid, 256, 0, st>>>(
+        k_chunk_state_generic<float><<<grid, 256, lds, st>>>(
             (const float *)x, (const float *)Bm, dt, Acs, states, s.L, (int)s.H, (int)s.P,
             (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
+}
+
+void launch_chunk_dstate(const ScanShape &s, const void *dy, const void *Cm, const float *Acs,
+                         float *dstates, hipStream_t st) {
+    const dim3 grid = state_generic_grid(s);
+    const size_t lds = state_generic_lds(s);
+    if (s.dtype == SSD_BF16)
+        k_chunk_state_generic<bf16, true><<<grid, 256, lds, st>>>(
+            (const bf16 *)dy, (const bf16 *)Cm, nullptr, Acs, dstates, s.L, (int)s.H, (int)s.P,
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, nullptr);
+    else
+        k_chunk_state_generic<float, true><<<grid, 256, lds, st>>>(
+            (const float *)dy, (const float *)Cm, nullptr, Acs, dstates, s.L, (int)s.H, (int)s.P,
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, nullptr);
+}
+
+void launch_state_passing_rev(const ScanShape &s, float *dstates, const float *Acs,
+                              const float *dfin, float *dinit, hipStream_t st) {
+    const int64_t PN = s.P * s.N;
+    dim3 grid((unsigned)(s.B * s.H), (unsigned)((PN / 4 + 255) / 256));
+    k_state_passing_rev<<<grid, 256, 0, st>>>(dstates, Acs, dfin, dinit, s.L, (int)s.H, PN,
+                                               (int)s.Q, (int)s.T);
 }
 
 void launch_state_passing(const ScanShape &s, float *states, const float *Acs,

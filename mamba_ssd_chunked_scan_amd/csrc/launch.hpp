@@ -64,6 +64,22 @@ void launch_step(const StepShape &s, int64_t nsteps, float *state, const void *x
                  const float *dt, const float *A, const void *Bm, const void *Cm, const float *D,
                  void *y, const DtAct &act, const void *z, hipStream_t st);
 
+// Gradient (fixed chunking, generic kernels):
+// dS_c = sum_s exp(Acs_s) dy_s C_s^T per chunk (states layout) ...
+void launch_chunk_dstate(const ScanShape &s, const void *dy, const void *Cm, const float *Acs,
+                         float *dstates, hipStream_t st);
+// ... turned in place, last chunk first, into the derivative with respect to
+// each chunk's end state; dinit (may be null) gets the initial state's.
+void launch_state_passing_rev(const ScanShape &s, float *dstates, const float *Acs,
+                              const float *dfin, float *dinit, hipStream_t st);
+// Per-chunk gradients from the entering states H and the end-state
+// derivatives E: dx and ddt written; dB, dC (fp32), dA, dD (may be null)
+// accumulated with atomics into zeroed buffers.  s.Q must be 32.
+void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const float *A,
+                      const void *Bm, const void *Cm, const float *D, const float *Acs,
+                      const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
+                      float *dB, float *dC, float *dA, float *dD, hipStream_t st);
+
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,

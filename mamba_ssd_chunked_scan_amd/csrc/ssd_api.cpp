@@ -103,6 +103,24 @@ ssd_status read_edges(const ssd_edges *e, ssd::DtAct *act, const void **z) {
 
 bool act_active(const ssd::DtAct &a) { return a.bias || a.softplus || a.limit; }
 
+// The gradient tiles by 32 tokens whatever the forward chunk (its results do
+// not depend on the chunk beyond rounding): Acs, entering states, end-state
+// derivatives at that chunk.
+ScanShape bwd_shape(const ScanShape &s) {
+    ScanShape b = s;
+    b.Q = 32;
+    b.T = (s.L + 31) / 32;
+    b.ctab = nullptr;
+    b.sch = nullptr;
+    return b;
+}
+
+size_t bwd_workspace_bytes(const ScanShape &s) {
+    if (s.B == 0 || s.L == 0) return 0;
+    const ScanShape b = bwd_shape(s);
+    return acs_bytes(b) + 2 * states_bytes(b);
+}
+
 // Chunk table and sequence table of a variable-length batch, after the rest.
 size_t varlen_table_bytes(const ScanShape &s) {
     return round_up((size_t)s.T * 8) + round_up((size_t)s.NS * 8);
@@ -183,7 +201,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 4; }
+int ssd_abi_version(void) { return 5; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -221,6 +239,62 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     if (!workspace) return SSD_ERR_NULL_PTR;
     run_scan(s, act, z, x, dt, A, B, C, D, init_state, y, final_state,
              static_cast<char *>(workspace), as_stream(stream));
+    return after_launch();
+}
+
+ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
+    if (!bytes) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    *bytes = bwd_workspace_bytes(s);
+    return SSD_OK;
+}
+
+ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        const void *dy, const float *dfinal, void *dx, float *ddt, float *dA,
+                        float *dB, float *dC, float *dD, float *dinit, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    hipStream_t hs = as_stream(stream);
+    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = 0, dinit = dfinal
+        st = check_ptrs({dA}, {dD, dinit, dfinal});
+        if (st != SSD_OK) return st;
+        ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
+        if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
+        if (dinit) ssd::launch_copy_or_zero(dinit, dfinal, s.B * s.H * s.P * s.N, hs);
+        return after_launch();
+    }
+    st = check_ptrs({x, dt, A, B, C, dy, dx, ddt, dA, dB, dC},
+                    {D, init_state, dfinal, dD, dinit, workspace});
+    if (st != SSD_OK) return st;
+    const size_t need = bwd_workspace_bytes(s);
+    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL_PTR;
+    const ScanShape b = bwd_shape(s);
+    char *ws = static_cast<char *>(workspace);
+    float *Acs = reinterpret_cast<float *>(ws);
+    float *Hst = reinterpret_cast<float *>(ws + acs_bytes(b));
+    float *Est = reinterpret_cast<float *>(ws + acs_bytes(b) + states_bytes(b));
+    // outputs accumulated with atomics start from zero (a fill kernel, so the
+    // call can be captured in a HIP graph)
+    const int64_t bcn = s.B * s.L * s.G * s.N;
+    ssd::launch_copy_or_zero(dB, nullptr, bcn, hs);
+    ssd::launch_copy_or_zero(dC, nullptr, bcn, hs);
+    ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
+    if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
+    // the forward's entering states at 32-token chunks
+    ssd::launch_chunk_cumsum(b, dt, A, Acs, hs);
+    ssd::launch_chunk_state(b, x, B, dt, Acs, Hst, hs);
+    ssd::launch_state_passing(b, Hst, Acs, init_state, nullptr, hs);
+    // derivatives with respect to every chunk's end state, and the initial state's
+    ssd::launch_chunk_dstate(b, dy, C, Acs, Est, hs);
+    ssd::launch_state_passing_rev(b, Est, Acs, dfinal, dinit, hs);
+    // per-chunk gradients
+    ssd::launch_chunk_bwd(b, x, dt, A, B, C, D, Acs, Hst, Est, dy, dx, ddt, dB, dC, dA, dD, hs);
     return after_launch();
 }
 

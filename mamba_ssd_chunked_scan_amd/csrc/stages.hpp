@@ -5,6 +5,9 @@
 
 namespace ssd {
 
+// Chunks whose loads the state passes issue ahead of the dependent updates.
+constexpr int kPassAhead = 8;
+
 // Inter-chunk state pass ("Compiler-First State Space Duality and Portable
 // O(1) Autoregressive Caching for Inference", paperlayer summary, §3 Method,
 // "Chunked recurrence"): per (row, h) and 4 consecutive state elements at
@@ -12,8 +15,8 @@ namespace ssd {
 // H_{c+1} = exp(Acs at the end of chunk c) H_c + S_c, H_0 = init (or 0).
 // A row is a batch row (fixed chunking: slots b*T .. b*T+T-1) or, with
 // sch/ctab, a sequence of a variable-length batch (its slots from sch, chunk
-// ends from ctab; Acs is [H, L] with L all packed tokens).  Loads run four
-// chunks ahead of the dependent update so that several are in flight.
+// ends from ctab; Acs is [H, L] with L all packed tokens).  Loads run
+// kPassAhead chunks ahead of the dependent update so that several are in flight.
 __device__ __forceinline__ void state_passing_body(float *__restrict__ states,
                                                    const float *__restrict__ Acs,
                                                    const float *init, float *fin, int64_t bh,
@@ -38,11 +41,11 @@ __device__ __forceinline__ void state_passing_body(float *__restrict__ states,
     if (init) hv = *reinterpret_cast<const float4 *>(init + bh * PN + e);
     const int64_t cstride = (int64_t)H * PN;
     float *base = states + (k0 * H + h) * PN + e;
-    for (int c0 = 0; c0 < n; c0 += 4) {
-        float4 s[4];
-        float r[4];
+    for (int c0 = 0; c0 < n; c0 += kPassAhead) {
+        float4 s[kPassAhead];
+        float r[kPassAhead];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kPassAhead; ++k) {
             const int c = c0 + k;
             if (c < n) {
                 s[k] = *reinterpret_cast<const float4 *>(base + c * cstride);
@@ -57,7 +60,7 @@ __device__ __forceinline__ void state_passing_body(float *__restrict__ states,
             }
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kPassAhead; ++k) {
             const int c = c0 + k;
             if (c < n) {
                 *reinterpret_cast<float4 *>(base + c * cstride) = hv;

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 4
+    assert L.ssd_abi_version() == 5
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -319,6 +319,35 @@ def test_varlen_pointer_errors(L):
     a = [None] * 11
     a[7] = P_MIS
     assert L.ssd_scan_fwd_varlen(ctypes.byref(vdesc(total=0)), None, *a, 0, None) == ALIGN
+
+
+def test_bwd_workspace_and_errors(L):
+    d = desc()   # batch 1, seqlen 512, 8 heads, headdim 64, dstate 128
+    n = ctypes.c_size_t(0)
+    assert L.ssd_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
+    T32 = 512 // 32
+    assert n.value == r256(8 * 512 * 4) + 2 * r256(T32 * 8 * 64 * 128 * 4)
+    need = n.value
+    args = [P16] * 16  # x dt A B C D init dy dfinal dx ddt dA dB dC dD dinit
+    assert L.ssd_scan_bwd(None, *args, P16, need, None) == NULL
+    for which in (0, 1, 2, 3, 4, 7, 9, 10, 11, 12, 13):   # required
+        a = list(args)
+        a[which] = None
+        assert L.ssd_scan_bwd(ctypes.byref(d), *a, P16, need, None) == NULL, which
+    for which in range(16):
+        a = list(args)
+        a[which] = P_MIS
+        assert L.ssd_scan_bwd(ctypes.byref(d), *a, P16, need, None) == ALIGN, which
+    assert L.ssd_scan_bwd(ctypes.byref(d), *args, P16, need - 1, None) == WS
+    assert L.ssd_scan_bwd(ctypes.byref(d), *args, None, need, None) == NULL
+    assert L.ssd_scan_bwd(ctypes.byref(desc(chunk=48)), *args, P16, need, None) == UNSUP
+    assert L.ssd_scan_bwd(ctypes.byref(desc(nheads=6, ngroups=4)), *args, P16, need,
+                          None) == SHAPE
+    # no tokens: only dA (required) and the optional state pointers are checked
+    a = [None] * 16
+    assert L.ssd_scan_bwd(ctypes.byref(desc(seqlen=0)), *a, None, 0, None) == NULL
+    a[11] = P_MIS
+    assert L.ssd_scan_bwd(ctypes.byref(desc(seqlen=0)), *a, None, 0, None) == ALIGN
 
 
 def test_empty_batch_is_noop(L):
