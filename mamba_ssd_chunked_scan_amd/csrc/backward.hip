@@ -36,17 +36,34 @@ namespace {
 
 constexpr int kBQ = 32;         // tokens per gradient chunk
 constexpr int kBThreads = 256;
-constexpr int kMaxItems = 8;    // (row, 4 state elements) items per thread: 32 * 256 / 4 / 256
+constexpr int kHeadsPerBlock = 4;
 
-// LDS layout (floats): x, dy [Q][P+1]; B, C [Q][N+1]; CB L, K L, GD [Q][Q+1]
-// (odd row strides: the 32 rows of a column fall in 32 different banks);
-// 6 vectors of Q; 8 scratch; then the E / H slice buffer (at least 8N floats:
-// it also holds the (N/4) x Q partial sums of two per-token reductions).
+// LDS layout (floats), rows padded to multiples of 4 plus 4 (16-byte rows,
+// staggered banks): B, C [Q][NS]; x, dy [Q][PS]; CB, CB L, K L, GD [Q][LQ];
+// 6 vectors of Q; 2 x 4 x Q cross-wave partials; 8 scratch; then the E / H
+// slice buffer.
+__host__ __device__ inline int bwd_ps(int P) { return ((P + 3) & ~3) + 4; }
+__host__ __device__ inline int bwd_ns(int N) { return N + 4; }
+constexpr int kLQ = kBQ + 4;
 __host__ __device__ inline int64_t bwd_fixed_floats(int P, int N) {
-    return 2LL * kBQ * (P + 1) + 2LL * kBQ * (N + 1) + 3LL * kBQ * (kBQ + 1) + 6 * kBQ + 8;
+    return 2LL * kBQ * bwd_ns(N) + 2LL * kBQ * bwd_ps(P) + 4LL * kBQ * kLQ + 6 * kBQ +
+           8 * kBQ + 8;
 }
 
-template <typename Tin>
+__device__ __forceinline__ float4 f4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ void fma4(float4 &acc, float a, const float4 &b) {
+    acc.x = fmaf(a, b.x, acc.x);
+    acc.y = fmaf(a, b.y, acc.y);
+    acc.z = fmaf(a, b.z, acc.z);
+    acc.w = fmaf(a, b.w, acc.w);
+}
+__device__ __forceinline__ float dot4(const float4 &a, const float4 &b) {
+    return fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
+}
+
+// One block per (b, c, group, slice of kHeadsPerBlock heads of the group).
+// KI = ceil(N / 32): (token, 4 state elements) items per thread.
+template <typename Tin, int KI>
 __global__ void __launch_bounds__(kBThreads)
 k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
             const Tin *__restrict__ Bm, const Tin *__restrict__ Cm, const float *__restrict__ D,
@@ -55,303 +72,356 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
             float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
             float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int P, int N, int G,
             int T, int slice_rows) {
-    constexpr int Q = kBQ, LQ = kBQ + 1;
+    constexpr int Q = kBQ, LQ = kLQ;
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    const int PS = P + 1, NS = N + 1;
-    float *bs = sm;                 // [Q][NS]
-    float *cs = bs + Q * NS;        // [Q][NS]
-    float *xs = cs + Q * NS;        // [Q][PS]
-    float *ys = xs + Q * PS;        // dy [Q][PS]
-    float *CBL = ys + Q * PS;       // [Q][LQ]
-    float *KL = CBL + Q * LQ;       // [Q][LQ]
-    float *GD = KL + Q * LQ;        // [Q][LQ]
-    float *acs_s = GD + Q * LQ;     // [Q]
-    float *dt_s = acs_s + Q;        // [Q]
-    float *cdt_s = dt_s + Q;        // [Q] sum_{k<=t} dt_k
-    float *s3d = cdt_s + Q;         // [Q] exp(Acs_last - Acs_j) x_j^T E B_j
-    float *hq = s3d + Q;            // [Q] exp(Acs_i) dy_i^T H C_i
-    float *rowg = hq + Q;           // [Q] sum_j GD[t][j] dt_j, then dAcs
-    float *red = rowg + Q;          // [8]
-    float *slab = sm + ((bwd_fixed_floats(P, N) + 3) & ~3LL);  // E or H rows, 16-byte aligned
+    const int PS = bwd_ps(P), NS = bwd_ns(N);
+    float *bs = sm;                  // [Q][NS]
+    float *cs = bs + Q * NS;         // [Q][NS]
+    float *xs = cs + Q * NS;         // [Q][PS]
+    float *ys = xs + Q * PS;         // dy [Q][PS]
+    float *CB = ys + Q * PS;         // [Q][LQ]  C_i.B_j (all i, j)
+    float *CBL = CB + Q * LQ;        // [Q][LQ]  CB L, j <= i < q
+    float *KL = CBL + Q * LQ;        // [Q][LQ]  (dy_i.x_j) L
+    float *GD = KL + Q * LQ;         // [Q][LQ]  CB KL
+    float *acs_s = GD + Q * LQ;      // [Q]
+    float *dt_s = acs_s + Q;         // [Q]
+    float *cdt_s = dt_s + Q;         // [Q] sum_{k<=t} dt_k
+    float *rowg = cdt_s + Q;         // [Q] sum_j GD[t][j] dt_j
+    float *colg = rowg + Q;          // [Q] sum_i GD[i][t]
+    float *s3h = colg + Q;           // [Q] exp(Acs_last - Acs_j) x_j^T E B_j, then exp(Acs_i) dy_i^T H C_i
+    float *part = s3h + Q;           // [2][4][Q] cross-wave partials
+    float *red = part + 8 * Q;       // [8]
+    float *slab = sm + ((bwd_fixed_floats(P, N) + 3) & ~3LL);  // E or H rows [slice][N]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.x % H;
-    const int64_t bc = blockIdx.x / H;
-    const int c = (int)(bc % T);
-    const int64_t b = bc / T;
-    const int g = h / (H / G);
+    const int R = H / G, nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    int64_t rest = blockIdx.x;
+    const int hsl = (int)(rest % nslices);
+    rest /= nslices;
+    const int g = (int)(rest % G);
+    rest /= G;
+    const int c = (int)(rest % T);
+    const int64_t b = rest / T;
+    const int h0 = g * R + hsl * kHeadsPerBlock;
+    const int nh = min(kHeadsPerBlock, g * R + R - h0);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
-    const float a = A[h];
-    const float Dh = D ? D[h] : 0.f;
     const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N, PN = (int64_t)P * N;
-    const int64_t xo = ((b * L + t0) * H + h) * P;
     const int64_t bo = ((b * L + t0) * G + g) * N;
-    const float *Hc = Hs + ((b * T + c) * H + h) * PN;
-    const float *Ec = Es + ((b * T + c) * H + h) * PN;
-
-    // ---- stage the chunk's rows (zeros past q) and its per-token scalars
-    for (int e = tid; e < Q * P; e += kBThreads) {
-        const int j = e / P, p = e - j * P;
-        const bool ok = j < q;
-        xs[j * PS + p] = ok ? Elem<Tin>::ld(x, xo + j * xrow + p) : 0.f;
-        ys[j * PS + p] = ok ? Elem<Tin>::ld(dy, xo + j * xrow + p) : 0.f;
-    }
-    for (int e = tid; e < Q * N; e += kBThreads) {
-        const int j = e / N, n = e - j * N;
-        const bool ok = j < q;
-        bs[j * NS + n] = ok ? Elem<Tin>::ld(Bm, bo + j * brow + n) : 0.f;
-        cs[j * NS + n] = ok ? Elem<Tin>::ld(Cm, bo + j * brow + n) : 0.f;
-    }
-    if (wave == 0) {
-        const float d = lane < q ? dt[(b * L + t0 + lane) * H + h] : 0.f;
-        const float cd = wave_inclusive_scan(d, lane);
-        if (lane < Q) {
-            dt_s[lane] = d;
-            cdt_s[lane] = cd;
-            acs_s[lane] = lane < q ? Acs[(b * H + h) * L + t0 + lane] : 0.f;
-            s3d[lane] = 0.f;
-            hq[lane] = 0.f;
-        }
-    }
-    __syncthreads();
-    const float alast = acs_s[q - 1];
-
-    // ---- the three masked Q x Q matrices
-    for (int e = tid; e < Q * Q; e += kBThreads) {
-        const int i = e / Q, j = e - i * Q;
-        float cbl = 0.f, kl = 0.f, gd = 0.f;
-        if (j <= i && i < q) {
-            float cb = 0.f, k = 0.f;
-            for (int n = 0; n < N; ++n) cb = fmaf(cs[i * NS + n], bs[j * NS + n], cb);
-            for (int p = 0; p < P; ++p) k = fmaf(ys[i * PS + p], xs[j * PS + p], k);
-            const float l = ssd_exp(acs_s[i] - acs_s[j]);
-            cbl = cb * l;
-            kl = k * l;
-            gd = cb * kl;
-        }
-        CBL[i * LQ + j] = cbl;
-        KL[i * LQ + j] = kl;
-        GD[i * LQ + j] = gd;
-    }
-    __syncthreads();
-    if (tid < Q) {  // row sums of GD dt (intra-chunk dAcs, + side)
-        float r = 0.f;
-        for (int j = 0; j <= tid; ++j) r = fmaf(GD[tid * LQ + j], dt_s[j], r);
-        rowg[tid] = r;
-    }
-
-    // ---- E slices: dx, and x_j^T E for dB
     const int nq = N / 4;
-    const int nitems = Q * nq;  // (row, 4 state elements)
-    float4 acc4[kMaxItems];
+    const int nitems = Q * nq;
+    // item k of this thread: token j = tid % Q, state elements 4 (tid / Q + 8 k) ..
+    const int jt = tid % Q, nq0 = tid / Q;
+    // E / H slices move through registers: the next slice's loads are issued
+    // before the current slice is used (a slice is at most 2048 floats, two
+    // float4 per thread)
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load_slice = [&](const float *src, int p0, float4 (&pf)[2]) __attribute__((always_inline)) {
+        const int n = min(slice_rows, P - p0) * nq;
+        const float4 *s4 = reinterpret_cast<const float4 *>(src + (int64_t)p0 * N);
 #pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) acc4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < P; p0 += slice_rows) {
-        const int pr = min(slice_rows, P - p0);
-        __syncthreads();  // the previous slice is no longer read
-        for (int e = tid; e < pr * nq; e += kBThreads)
-            reinterpret_cast<float4 *>(slab)[e] = reinterpret_cast<const float4 *>(Ec + p0 * N)[e];
-        __syncthreads();
-        // dx_j[p] for p in the slice
-        for (int e = tid; e < Q * pr; e += kBThreads) {
-            const int j = e % Q, pl = e / Q, p = p0 + pl;
-            if (j >= q) continue;
-            float intra = 0.f;
-            for (int i = j; i < q; ++i) intra = fmaf(CBL[i * LQ + j], ys[i * PS + p], intra);
-            float eb = 0.f;
-            for (int n = 0; n < N; ++n) eb = fmaf(slab[pl * N + n], bs[j * NS + n], eb);
-            const float v = dt_s[j] * (intra + ssd_exp(alast - acs_s[j]) * eb) + Dh * ys[j * PS + p];
-            Elem<Tin>::st(dx, xo + j * xrow + p, v);
-        }
-        // x_j^T E, items (j, n4)
-#pragma unroll
-        for (int k = 0; k < kMaxItems; ++k) {
+        for (int k = 0; k < 2; ++k) {
             const int e = tid + k * kBThreads;
-            if (e < nitems) {
-                const int j = e % Q, n4 = e / Q;
-                float4 s = acc4[k];
-                for (int pl = 0; pl < pr; ++pl) {
-                    const float xv = xs[j * PS + p0 + pl];
-                    const float4 ev = reinterpret_cast<const float4 *>(slab + pl * N)[n4];
-                    s.x = fmaf(xv, ev.x, s.x);
-                    s.y = fmaf(xv, ev.y, s.y);
-                    s.z = fmaf(xv, ev.z, s.z);
-                    s.w = fmaf(xv, ev.w, s.w);
-                }
-                acc4[k] = s;
+            pf[k] = e < n ? s4[e] : z4;
+        }
+    };
+    auto store_slice = [&](const float4 (&pf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) reinterpret_cast<float4 *>(slab)[tid + k * kBThreads] = pf[k];
+    };
+
+    // ---- B and C of the chunk (shared by the block's heads) and C.B
+    for (int e = tid; e < Q * NS; e += kBThreads) {
+        const int j = e / NS, n = e - j * NS;
+        const bool ok = j < q && n < N;
+        bs[e] = ok ? Elem<Tin>::ld(Bm, bo + j * brow + n) : 0.f;
+        cs[e] = ok ? Elem<Tin>::ld(Cm, bo + j * brow + n) : 0.f;
+    }
+    __syncthreads();
+    {  // 1 x 4 tile per thread: row i, columns 4 jq ..
+        const int i = tid >> 3, j0 = 4 * (tid & 7);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < N; n += 4) {
+            const float4 cv = f4(cs + i * NS + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += dot4(cv, f4(bs + (j0 + r) * NS + n));
+        }
+        *reinterpret_cast<float4 *>(CB + i * LQ + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+
+    float4 dbacc[KI], dcacc[KI];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        dbacc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        dcacc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    for (int hh = 0; hh < nh; ++hh) {
+        const int h = h0 + hh;
+        const float a = A[h];
+        const float Dh = D ? D[h] : 0.f;
+        const int64_t xo = ((b * L + t0) * H + h) * P;
+        const float *Hc = Hs + ((b * T + c) * H + h) * PN;
+        const float *Ec = Es + ((b * T + c) * H + h) * PN;
+        __syncthreads();  // the previous head's rows and scalars are no longer read
+        // ---- this head's x, dy and per-token scalars
+        for (int e = tid; e < Q * PS; e += kBThreads) {
+            const int j = e / PS, p = e - j * PS;
+            const bool ok = j < q && p < P;
+            xs[e] = ok ? Elem<Tin>::ld(x, xo + j * xrow + p) : 0.f;
+            ys[e] = ok ? Elem<Tin>::ld(dy, xo + j * xrow + p) : 0.f;
+        }
+        if (wave == 0) {
+            const float d = lane < q ? dt[(b * L + t0 + lane) * H + h] : 0.f;
+            const float cd = wave_inclusive_scan(d, lane);
+            if (lane < Q) {
+                dt_s[lane] = d;
+                cdt_s[lane] = cd;
+                acs_s[lane] = lane < q ? Acs[(b * H + h) * L + t0 + lane] : 0.f;
             }
         }
-    }
-    // dB, and s3 (x_j^T E B_j); the slice buffer takes the s3 partials, so
-    // every thread must be done with the last E slice first
-    __syncthreads();
+        // the first E slice is in flight while K and the masked matrices form
+        float4 pf[2];
+        load_slice(Ec, 0, pf);
+        __syncthreads();
+        const float alast = acs_s[q - 1];
+        // ---- K = dy.x^T (1 x 4 tile), then the masked CB L, K L and GD, with
+        // the row sums of GD dt and the column sums of GD
+        {
+            const int i = tid >> 3, j0 = 4 * (tid & 7);
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < PS; p += 4) {
+                const float4 yv = f4(ys + i * PS + p);
 #pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {
-        const int e = tid + k * kBThreads;
-        if (e < nitems) {
-            const int j = e % Q, n4 = e / Q;
-            if (j < q) {
+                for (int r = 0; r < 4; ++r) acc[r] += dot4(yv, f4(xs + (j0 + r) * PS + p));
+            }
+            const float4 cb4 = f4(CB + i * LQ + j0);
+            const float cbv[4] = {cb4.x, cb4.y, cb4.z, cb4.w};
+            float cbl[4], kl[4], gd[4], rs = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + r;
+                const bool m = j <= i && i < q;
+                const float l = m ? ssd_exp(acs_s[i] - acs_s[j]) : 0.f;
+                cbl[r] = cbv[r] * l;
+                kl[r] = acc[r] * l;
+                gd[r] = cbv[r] * kl[r];
+                rs = fmaf(gd[r], dt_s[j], rs);
+            }
+            *reinterpret_cast<float4 *>(CBL + i * LQ + j0) = make_float4(cbl[0], cbl[1], cbl[2], cbl[3]);
+            *reinterpret_cast<float4 *>(KL + i * LQ + j0) = make_float4(kl[0], kl[1], kl[2], kl[3]);
+            *reinterpret_cast<float4 *>(GD + i * LQ + j0) = make_float4(gd[0], gd[1], gd[2], gd[3]);
+            // row i: the 8 lanes of this row (lanes 8m .. 8m+7)
+            rs += __shfl_xor(rs, 1, kWave);
+            rs += __shfl_xor(rs, 2, kWave);
+            rs += __shfl_xor(rs, 4, kWave);
+            if ((tid & 7) == 0) rowg[i] = rs;
+            // columns j0..j0+3: lanes with the same tid & 7 hold rows 8 wave .. 8 wave + 7
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float cv = gd[r];
+                cv += __shfl_xor(cv, 8, kWave);
+                cv += __shfl_xor(cv, 16, kWave);
+                cv += __shfl_xor(cv, 32, kWave);
+                if (lane < 8) part[wave * Q + j0 + r] = cv;
+            }
+        }
+        __syncthreads();
+        if (tid < Q) colg[tid] = ((part[tid] + part[Q + tid]) + part[2 * Q + tid]) + part[3 * Q + tid];
+
+        // ---- E slices: dx, and x_j^T E for dB
+        float4 acc4[KI];
+#pragma unroll
+        for (int k = 0; k < KI; ++k) acc4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p0 = 0; p0 < P; p0 += slice_rows) {
+            const int pr = min(slice_rows, P - p0);
+            __syncthreads();  // the previous slice (or colg's partials) no longer read
+            store_slice(pf);
+            __syncthreads();
+            if (p0 + slice_rows < P) load_slice(Ec, p0 + slice_rows, pf);
+            else load_slice(Hc, 0, pf);  // the first H slice
+            // dx_j[p .. p+3]: item (j, p quad)
+            const int pqn = (pr + 3) / 4;
+            for (int e = tid; e < Q * pqn; e += kBThreads) {
+                const int j = e % Q, pl = 4 * (e / Q), p = p0 + pl;
+                if (j >= q) continue;
                 float4 intra = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int i = j; i < q; ++i) {
-                    const float kl = KL[i * LQ + j];
-                    const float *cr = cs + i * NS + 4 * n4;
-                    const float4 cv = make_float4(cr[0], cr[1], cr[2], cr[3]);
-                    intra.x = fmaf(kl, cv.x, intra.x);
-                    intra.y = fmaf(kl, cv.y, intra.y);
-                    intra.z = fmaf(kl, cv.z, intra.z);
-                    intra.w = fmaf(kl, cv.w, intra.w);
+                for (int i = j; i < q; ++i) fma4(intra, CBL[i * LQ + j], f4(ys + i * PS + p));
+                float eb[4] = {0.f, 0.f, 0.f, 0.f};
+                const int rr = min(4, pr - pl);
+                for (int n = 0; n < N; n += 4) {
+                    const float4 bv = f4(bs + j * NS + n);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (r < rr) eb[r] += dot4(bv, f4(slab + (pl + r) * N + n));
                 }
                 const float dtj = dt_s[j], f = ssd_exp(alast - acs_s[j]);
-                const float4 xe = acc4[k];
-                float *o = dB + bo + j * brow + 4 * n4;
-                atomicAdd(o + 0, dtj * (intra.x + f * xe.x));
-                atomicAdd(o + 1, dtj * (intra.y + f * xe.y));
-                atomicAdd(o + 2, dtj * (intra.z + f * xe.z));
-                atomicAdd(o + 3, dtj * (intra.w + f * xe.w));
-                const float *br = bs + j * NS + 4 * n4;
-                const float4 bv = make_float4(br[0], br[1], br[2], br[3]);
-                slab[n4 * Q + j] = f * (xe.x * bv.x + xe.y * bv.y + xe.z * bv.z + xe.w * bv.w);
-            }
-        }
-        acc4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    // s3 / dt_j per token: the partials summed in a fixed order (so ddt is the
-    // same on every run)
-    __syncthreads();
-    if (tid < q) {
-        float v = 0.f;
-        for (int n4 = 0; n4 < nq; ++n4) v += slab[n4 * Q + tid];
-        s3d[tid] = v;
-    }
-
-    // ---- H slices: dy_i^T H for dC
-    for (int p0 = 0; p0 < P; p0 += slice_rows) {
-        const int pr = min(slice_rows, P - p0);
-        __syncthreads();
-        for (int e = tid; e < pr * nq; e += kBThreads)
-            reinterpret_cast<float4 *>(slab)[e] = reinterpret_cast<const float4 *>(Hc + p0 * N)[e];
-        __syncthreads();
+                const float iv[4] = {intra.x, intra.y, intra.z, intra.w};
 #pragma unroll
-        for (int k = 0; k < kMaxItems; ++k) {
-            const int e = tid + k * kBThreads;
-            if (e < nitems) {
-                const int i = e % Q, n4 = e / Q;
-                float4 s = acc4[k];
-                for (int pl = 0; pl < pr; ++pl) {
-                    const float yv = ys[i * PS + p0 + pl];
-                    const float4 hv = reinterpret_cast<const float4 *>(slab + pl * N)[n4];
-                    s.x = fmaf(yv, hv.x, s.x);
-                    s.y = fmaf(yv, hv.y, s.y);
-                    s.z = fmaf(yv, hv.z, s.z);
-                    s.w = fmaf(yv, hv.w, s.w);
+                for (int r = 0; r < 4; ++r)
+                    if (r < rr)
+                        Elem<Tin>::st(dx, xo + j * xrow + p + r,
+                                      dtj * (iv[r] + f * eb[r]) + Dh * ys[j * PS + p + r]);
+            }
+            // x_j^T E over the slice: items (jt, nq0 + 8k)
+            for (int pl = 0; pl < pr; ++pl) {
+                const float xv = xs[jt * PS + p0 + pl];
+                const float *er = slab + pl * N;
+#pragma unroll
+                for (int k = 0; k < KI; ++k) {
+                    const int n4 = nq0 + 8 * k;
+                    if (n4 < nq) fma4(acc4[k], xv, f4(er + 4 * n4));
                 }
-                acc4[k] = s;
             }
         }
-    }
-    // dC, and the state-to-output term of dAcs (partials into the slice buffer
-    // once every thread is done with the last H slice)
-    __syncthreads();
+        // dB (accumulated over the block's heads) and s3
+        {
+            float s3 = 0.f;
+            const float dtj = dt_s[jt], f = ssd_exp(alast - acs_s[jt]);
+            const bool in = jt < q;
 #pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {
-        const int e = tid + k * kBThreads;
-        if (e < nitems) {
-            const int i = e % Q, n4 = e / Q;
-            if (i < q) {
-                float4 intra = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int j = 0; j <= i; ++j) {
-                    const float w = KL[i * LQ + j] * dt_s[j];
-                    const float *br = bs + j * NS + 4 * n4;
-                    const float4 bv = make_float4(br[0], br[1], br[2], br[3]);
-                    intra.x = fmaf(w, bv.x, intra.x);
-                    intra.y = fmaf(w, bv.y, intra.y);
-                    intra.z = fmaf(w, bv.z, intra.z);
-                    intra.w = fmaf(w, bv.w, intra.w);
+            for (int k = 0; k < KI; ++k) {
+                const int n4 = nq0 + 8 * k;
+                if (n4 < nq && in) {
+                    float4 intra = make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int i = jt; i < q; ++i) fma4(intra, KL[i * LQ + jt], f4(cs + i * NS + 4 * n4));
+                    const float4 xe = acc4[k];
+                    dbacc[k].x += dtj * (intra.x + f * xe.x);
+                    dbacc[k].y += dtj * (intra.y + f * xe.y);
+                    dbacc[k].z += dtj * (intra.z + f * xe.z);
+                    dbacc[k].w += dtj * (intra.w + f * xe.w);
+                    s3 += f * dot4(xe, f4(bs + jt * NS + 4 * n4));
                 }
-                const float ei = ssd_exp(acs_s[i]);
-                const float4 yh = acc4[k];
-                float *o = dC + bo + i * brow + 4 * n4;
-                atomicAdd(o + 0, intra.x + ei * yh.x);
-                atomicAdd(o + 1, intra.y + ei * yh.y);
-                atomicAdd(o + 2, intra.z + ei * yh.z);
-                atomicAdd(o + 3, intra.w + ei * yh.w);
-                const float *cr = cs + i * NS + 4 * n4;
-                const float4 cv = make_float4(cr[0], cr[1], cr[2], cr[3]);
-                slab[n4 * Q + i] = ei * (yh.x * cv.x + yh.y * cv.y + yh.z * cv.z + yh.w * cv.w);
+                acc4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            // token jt's partials: lanes jt and jt + 32 of every wave
+            s3 += __shfl_xor(s3, 32, kWave);
+            if (lane < 32) part[4 * Q + wave * Q + jt] = s3;
+        }
+
+        // ---- H slices: dy_i^T H for dC; <E, H> from the H rows as they pass
+        // and the same E rows (read again, from L2)
+        float eh = 0.f;
+        for (int p0 = 0; p0 < P; p0 += slice_rows) {
+            const int pr = min(slice_rows, P - p0);
+            __syncthreads();
+            store_slice(pf);
+            {
+                float4 pe[2];
+                load_slice(Ec, p0, pe);
+                eh += dot4(pe[0], pf[0]) + dot4(pe[1], pf[1]);
+            }
+            __syncthreads();
+            if (p0 + slice_rows < P) load_slice(Hc, p0 + slice_rows, pf);
+            for (int pl = 0; pl < pr; ++pl) {
+                const float yv = ys[jt * PS + p0 + pl];
+                const float *hr = slab + pl * N;
+#pragma unroll
+                for (int k = 0; k < KI; ++k) {
+                    const int n4 = nq0 + 8 * k;
+                    if (n4 < nq) fma4(acc4[k], yv, f4(hr + 4 * n4));
+                }
+            }
+        }
+        // dC (accumulated over the block's heads) and the state-to-output term
+        {
+            float hq = 0.f;
+            const int i = jt;
+            const float ei = ssd_exp(acs_s[i]);
+            const bool in = i < q;
+#pragma unroll
+            for (int k = 0; k < KI; ++k) {
+                const int n4 = nq0 + 8 * k;
+                if (n4 < nq && in) {
+                    float4 intra = make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int j = 0; j <= i; ++j)
+                        fma4(intra, KL[i * LQ + j] * dt_s[j], f4(bs + j * NS + 4 * n4));
+                    const float4 yh = acc4[k];
+                    dcacc[k].x += intra.x + ei * yh.x;
+                    dcacc[k].y += intra.y + ei * yh.y;
+                    dcacc[k].z += intra.z + ei * yh.z;
+                    dcacc[k].w += intra.w + ei * yh.w;
+                    hq += ei * dot4(yh, f4(cs + i * NS + 4 * n4));
+                }
+            }
+            hq += __shfl_xor(hq, 32, kWave);
+            if (lane < 32) part[wave * Q + i] = hq;
+        }
+        // ---- <E, H>
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) eh += __shfl_xor(eh, off, kWave);
+        if (lane == 0) red[wave] = eh;
+        __syncthreads();
+
+        // ---- per-token scalars: dAcs, ddt, dA, dD (wave 0, lane t = token)
+        if (wave == 0) {
+            const float EH = ((red[0] + red[1]) + red[2]) + red[3];
+            const int t = lane;
+            const bool in = t < q;
+            float s3d = 0.f, dacs = 0.f, kdiag = 0.f, colgd = 0.f;
+            if (in) {
+                s3d = ((part[4 * Q + t] + part[5 * Q + t]) + part[6 * Q + t]) + part[7 * Q + t];
+                const float hqt = ((part[t] + part[Q + t]) + part[2 * Q + t]) + part[3 * Q + t];
+                colgd = colg[t];
+                dacs = rowg[t] - dt_s[t] * colgd + hqt - s3d * dt_s[t];
+                kdiag = KL[t * LQ + t];
+            }
+            float s3sum = in ? s3d * dt_s[t] : 0.f;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s3sum += __shfl_xor(s3sum, off, kWave);
+            if (t == q - 1) dacs += s3sum + ssd_exp(alast) * EH;
+            float suf = dacs;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const float o = __shfl_down(suf, d, kWave);
+                if (t + d < kWave) suf += o;
+            }
+            if (in) ddt[(b * L + t0 + t) * H + h] = a * suf + colgd + s3d;
+            float da = in ? dacs * cdt_s[t] : 0.f;
+            float dd = kdiag;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                da += __shfl_xor(da, off, kWave);
+                dd += __shfl_xor(dd, off, kWave);
+            }
+            if (lane == 0) {
+                atomicAdd(&dA[h], da);
+                if (dD) atomicAdd(&dD[h], dd);
             }
         }
     }
-    __syncthreads();  // the partials written
-    if (tid < q) {
-        float v = 0.f;
-        for (int n4 = 0; n4 < nq; ++n4) v += slab[n4 * Q + tid];
-        hq[tid] = v;
-    }
-
-    // ---- <E, H>
-    float eh = 0.f;
-    for (int64_t e = tid; e < PN / 4; e += kBThreads) {
-        const float4 ev = reinterpret_cast<const float4 *>(Ec)[e];
-        const float4 hv = reinterpret_cast<const float4 *>(Hc)[e];
-        eh += ev.x * hv.x + ev.y * hv.y + ev.z * hv.z + ev.w * hv.w;
-    }
+    // ---- dB, dC of the block's heads: one atomic per element
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) eh += __shfl_xor(eh, off, kWave);
-    if (lane == 0) red[wave] = eh;
-    __syncthreads();
-
-    // ---- per-token scalars: dAcs, ddt, dA, dD (wave 0, lane t = token)
-    if (wave == 0) {
-        const float EH = red[0] + red[1] + red[2] + red[3];
-        const int t = lane;
-        const bool in = t < q;
-        float colgd = 0.f, s3 = 0.f, dacs = 0.f, kdiag = 0.f;
-        if (in) {
-            for (int i = t; i < q; ++i) colgd += GD[i * LQ + t];
-            s3 = s3d[t] * dt_s[t];
-            dacs = rowg[t] - dt_s[t] * colgd + hq[t] - s3;
-            kdiag = KL[t * LQ + t];
-        }
-        // sum_j s3_j goes to the last token, with exp(Acs_last) <E, H>
-        float s3sum = s3;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s3sum += __shfl_xor(s3sum, off, kWave);
-        if (t == q - 1) dacs += s3sum + ssd_exp(alast) * EH;
-        // suffix sums of dAcs over the chunk (lanes >= q hold 0)
-        float suf = dacs;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const float o = __shfl_down(suf, d, kWave);
-            if (t + d < kWave) suf += o;
-        }
-        if (in) ddt[(b * L + t0 + t) * H + h] = a * suf + colgd + (in ? s3d[t] : 0.f);
-        float da = in ? dacs * cdt_s[t] : 0.f;
-        float dd = kdiag;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            da += __shfl_xor(da, off, kWave);
-            dd += __shfl_xor(dd, off, kWave);
-        }
-        if (lane == 0) {
-            atomicAdd(&dA[h], da);
-            if (dD) atomicAdd(&dD[h], dd);
+    for (int k = 0; k < KI; ++k) {
+        const int n4 = nq0 + 8 * k;
+        if (n4 < nq && jt < q) {
+            float *ob = dB + bo + jt * brow + 4 * n4;
+            float *oc = dC + bo + jt * brow + 4 * n4;
+            atomicAdd(ob + 0, dbacc[k].x);
+            atomicAdd(ob + 1, dbacc[k].y);
+            atomicAdd(ob + 2, dbacc[k].z);
+            atomicAdd(ob + 3, dbacc[k].w);
+            atomicAdd(oc + 0, dcacc[k].x);
+            atomicAdd(oc + 1, dcacc[k].y);
+            atomicAdd(oc + 2, dcacc[k].z);
+            atomicAdd(oc + 3, dcacc[k].w);
         }
     }
 }
 
 // Rows of E / H per slice so that the whole block fits the 160 KB of LDS
-// (at most 16 KB of slice, at least one row).
+// (at most 8 KB of slice, so two float4 per thread carry it; at least one row).
 int bwd_slice_rows(int P, int N, size_t *lds_bytes) {
     const int64_t fixed = (bwd_fixed_floats(P, N) + 3) & ~3LL;
-    int64_t budget = (160 * 1024) / 4 - fixed;
-    int64_t rows = min((int64_t)P, min((int64_t)(4096 / N), budget / N));
+    const int64_t budget = (160 * 1024) / 4 - fixed;
+    int64_t rows = min((int64_t)P, min((int64_t)(2048 / N), budget / N));
     if (rows < 1) rows = 1;
-    *lds_bytes = (size_t)(fixed + max(rows, (int64_t)8) * N) * 4;
+    // the buffer is always 2048 floats: every thread stores its two float4
+    *lds_bytes = (size_t)(fixed + 2048) * 4;
     return (int)rows;
 }
 
-template <typename Tin>
+template <typename Tin, int KI>
 void launch_bwd_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                   const void *Bm, const void *Cm, const float *D, const float *Acs,
                   const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
@@ -360,11 +430,13 @@ void launch_bwd_t(const ScanShape &s, const void *x, const float *dt, const floa
     const int rows = bwd_slice_rows((int)s.P, (int)s.N, &lds);
     static bool attr_set = false;  // once per instantiation (per process)
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd<Tin>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd<Tin, KI>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         attr_set = true;
     }
-    k_chunk_bwd<Tin><<<(unsigned)(s.B * s.T * s.H), kBThreads, lds, st>>>(
+    const int64_t R = s.H / s.G;
+    const int64_t nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    k_chunk_bwd<Tin, KI><<<(unsigned)(s.B * s.T * s.G * nslices), kBThreads, lds, st>>>(
         (const Tin *)x, dt, A, (const Tin *)Bm, (const Tin *)Cm, D, Acs, Hs, Es,
         (const Tin *)dy, (Tin *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.P, (int)s.N,
         (int)s.G, (int)s.T, rows);
@@ -376,10 +448,21 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
                       const void *Bm, const void *Cm, const float *D, const float *Acs,
                       const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                       float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
+#define SSD_BWD(T_, KI_) \
+    launch_bwd_t<T_, KI_>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st)
+#define SSD_BWD_KI(T_)                                 \
+    do {                                               \
+        if (s.N <= 32) SSD_BWD(T_, 1);                 \
+        else if (s.N == 64) SSD_BWD(T_, 2);            \
+        else if (s.N == 128) SSD_BWD(T_, 4);           \
+        else SSD_BWD(T_, 8);                           \
+    } while (0)
     if (s.dtype == SSD_BF16)
-        launch_bwd_t<bf16>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
+        SSD_BWD_KI(bf16);
     else
-        launch_bwd_t<float>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
+        SSD_BWD_KI(float);
+#undef SSD_BWD_KI
+#undef SSD_BWD
 }
 
 }  // namespace ssd
