@@ -240,28 +240,30 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
             __syncthreads();
             if (p0 + slice_rows < P) load_slice(Ec, p0 + slice_rows, pf);
             else load_slice(Hc, 0, pf);  // the first H slice
-            // dx_j[p .. p+3]: item (j, p quad)
-            const int pqn = (pr + 3) / 4;
-            for (int e = tid; e < Q * pqn; e += kBThreads) {
-                const int j = e % Q, pl = 4 * (e / Q), p = p0 + pl;
+            // dx_j[p, p+1]: item (j, p pair), all threads busy
+            const int ppn = (pr + 1) / 2;
+            for (int e = tid; e < Q * ppn; e += kBThreads) {
+                const int j = e % Q, pl = 2 * (e / Q), p = p0 + pl;
                 if (j >= q) continue;
-                float4 intra = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int i = j; i < q; ++i) fma4(intra, CBL[i * LQ + j], f4(ys + i * PS + p));
-                float eb[4] = {0.f, 0.f, 0.f, 0.f};
-                const int rr = min(4, pr - pl);
+                const bool two = pl + 1 < pr;
+                float in0 = 0.f, in1 = 0.f;
+                for (int i = j; i < q; ++i) {
+                    const float w = CBL[i * LQ + j];
+                    in0 = fmaf(w, ys[i * PS + p], in0);
+                    in1 = fmaf(w, ys[i * PS + p + 1], in1);
+                }
+                float eb0 = 0.f, eb1 = 0.f;
+                const float *e0 = slab + pl * N, *e1 = slab + (two ? pl + 1 : pl) * N;
                 for (int n = 0; n < N; n += 4) {
                     const float4 bv = f4(bs + j * NS + n);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (r < rr) eb[r] += dot4(bv, f4(slab + (pl + r) * N + n));
+                    eb0 += dot4(bv, f4(e0 + n));
+                    eb1 += dot4(bv, f4(e1 + n));
                 }
                 const float dtj = dt_s[j], f = ssd_exp(alast - acs_s[j]);
-                const float iv[4] = {intra.x, intra.y, intra.z, intra.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (r < rr)
-                        Elem<Tin>::st(dx, xo + j * xrow + p + r,
-                                      dtj * (iv[r] + f * eb[r]) + Dh * ys[j * PS + p + r]);
+                Elem<Tin>::st(dx, xo + j * xrow + p, dtj * (in0 + f * eb0) + Dh * ys[j * PS + p]);
+                if (two)
+                    Elem<Tin>::st(dx, xo + j * xrow + p + 1,
+                                  dtj * (in1 + f * eb1) + Dh * ys[j * PS + p + 1]);
             }
             // x_j^T E over the slice: items (jt, nq0 + 8k)
             for (int pl = 0; pl < pr; ++pl) {
