@@ -179,7 +179,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(prefill would shard over batch and head groups with no exchange; see DESIGN.md)",
+              "(prefill would shard over batch and head groups with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
