@@ -80,6 +80,13 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
                       const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                       float *dB, float *dC, float *dA, float *dD, hipStream_t st);
 
+// The gradient's 32-token chunk states (and their adjoint, with x = dy and
+// B = C) on the matrix cores, for the shapes bwd_states_mfma_ok accepts.
+bool bwd_states_mfma_ok(const ScanShape &s);
+void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
+                            const float *dt, const float *Acs, float *out, bool adjoint,
+                            hipStream_t st);
+
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,

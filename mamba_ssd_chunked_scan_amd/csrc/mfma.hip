@@ -175,7 +175,9 @@ using P1 = std::integral_constant<int, 1>;
 // prefix sum of dt*A over the chunk's tokens) and writes it to Acs for the
 // later stages, instead of reading it.  It then also applies the dt
 // activation `act` and, when dt_out is given, writes the activated dt there.
-template <int Q, int N, bool kCumsum>
+// kAdjoint (the gradient's chunk term, with x = dy and B = C): the weight is
+// exp(Acs_j), the decay from the chunk's entering state to token j.
+template <int Q, int N, bool kCumsum, bool kAdjoint = false>
 __global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ A,
@@ -235,7 +237,8 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
         const float last = acs[q - 1];
         if (tid < Q) {
             const int jj = min(tid, q - 1);
-            const float v = dt[(b * L + t0 + jj) * H + h] * ssd_exp(last - acs[jj]);
+            const float v = kAdjoint ? ssd_exp(acs[jj])
+                                     : dt[(b * L + t0 + jj) * H + h] * ssd_exp(last - acs[jj]);
             w[tid] = tid < q ? v : 0.f;
         }
     }
@@ -273,7 +276,7 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     // prefetch distance two: stage s+2's loads are issued while stage s is
     // multiplied and stage s+1 (already in registers) is written to LDS
     load_stage(0, R[0]);
-    load_stage(1, R[1]);
+    if (NST > 1) load_stage(1, R[1]);
     __syncthreads();  // w complete
     store_stage(0, 0, R[0]);
     __syncthreads();
@@ -300,9 +303,13 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
         if (st + 1 < NST) store_stage(st + 1, PAR ^ 1, R[PAR ^ 1]);
         __syncthreads();
     };
-    for (int st = 0; st < NST; st += 2) {  // NST is even
-        step(st, P0{});
-        step(st + 1, P1{});
+    if constexpr (NST == 1) {  // a 32-token chunk: one stage
+        step(0, P0{});
+    } else {
+        for (int st = 0; st < NST; st += 2) {  // NST is even
+            step(st, P0{});
+            step(st + 1, P1{});
+        }
     }
     float *out = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
 #pragma unroll
@@ -891,6 +898,34 @@ bool mfma_supported(const ScanShape &s) {
             else FN<64, 64>(__VA_ARGS__);                                \
         }                                                                \
     } while (0)
+
+bool bwd_states_mfma_ok(const ScanShape &s) {
+    const bool offsets32 = (s.Q + 64) * s.H * s.P * 2 < (int64_t(1) << 31) &&
+                           (s.Q + 64) * s.G * s.N * 2 < (int64_t(1) << 31);
+    return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) && s.Q == kJT &&
+           offsets32 && !s.ctab;
+}
+
+template <int N, bool kAdj>
+void launch_bwd_states_t(const ScanShape &s, const void *xin, const void *bin, const float *dt,
+                         const float *Acs, float *out, hipStream_t st) {
+    const int64_t nb = s.B * s.T * s.H;
+    k_chunk_state_mfma<kJT, N, false, kAdj><<<padded_grid(nb), 256, 0, st>>>(
+        (const bf16 *)xin, (const bf16 *)bin, dt, nullptr, const_cast<float *>(Acs), out, s.L,
+        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr, nullptr);
+}
+
+void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
+                            const float *dt, const float *Acs, float *out, bool adjoint,
+                            hipStream_t st) {
+    if (s.N == 128) {
+        if (adjoint) launch_bwd_states_t<128, true>(s, xin, bin, dt, Acs, out, st);
+        else launch_bwd_states_t<128, false>(s, xin, bin, dt, Acs, out, st);
+    } else {
+        if (adjoint) launch_bwd_states_t<64, true>(s, xin, bin, dt, Acs, out, st);
+        else launch_bwd_states_t<64, false>(s, xin, bin, dt, Acs, out, st);
+    }
+}
 
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
                              const float *dt, const float *Acs, float *states, hipStream_t st) {

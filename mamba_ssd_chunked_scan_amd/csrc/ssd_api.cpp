@@ -287,11 +287,14 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
     ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
     if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
     // the forward's entering states at 32-token chunks
+    const bool mm = ssd::bwd_states_mfma_ok(b);
     ssd::launch_chunk_cumsum(b, dt, A, Acs, hs);
-    ssd::launch_chunk_state(b, x, B, dt, Acs, Hst, hs);
+    if (mm) ssd::launch_bwd_states_mfma(b, x, B, dt, Acs, Hst, false, hs);
+    else ssd::launch_chunk_state(b, x, B, dt, Acs, Hst, hs);
     ssd::launch_state_passing(b, Hst, Acs, init_state, nullptr, hs);
     // derivatives with respect to every chunk's end state, and the initial state's
-    ssd::launch_chunk_dstate(b, dy, C, Acs, Est, hs);
+    if (mm) ssd::launch_bwd_states_mfma(b, dy, C, nullptr, Acs, Est, true, hs);
+    else ssd::launch_chunk_dstate(b, dy, C, Acs, Est, hs);
     ssd::launch_state_passing_rev(b, Est, Acs, dfinal, dinit, hs);
     // per-chunk gradients
     ssd::launch_chunk_bwd(b, x, dt, A, B, C, D, Acs, Hst, Est, dy, dx, ddt, dB, dC, dA, dD, hs);
