@@ -242,10 +242,19 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     return after_launch();
 }
 
+// The gradient's grid is batch x (seqlen / 32) x nheads blocks at most.
+ssd_status check_bwd(const ssd_scan_desc *d, ScanShape *s) {
+    ssd_status st = check_scan(d, s);
+    if (st != SSD_OK) return st;
+    const int64_t T32 = (s->L + 31) / 32;
+    if (T32 > 0 && s->B > kMaxBlocks / T32 / s->H) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
     ScanShape s;
-    ssd_status st = check_scan(d, &s);
+    ssd_status st = check_bwd(d, &s);
     if (st != SSD_OK) return st;
     *bytes = bwd_workspace_bytes(s);
     return SSD_OK;
@@ -257,7 +266,7 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                         float *dB, float *dC, float *dD, float *dinit, void *workspace,
                         size_t ws_bytes, void *stream) {
     ScanShape s;
-    ssd_status st = check_scan(d, &s);
+    ssd_status st = check_bwd(d, &s);
     if (st != SSD_OK) return st;
     hipStream_t hs = as_stream(stream);
     if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = 0, dinit = dfinal

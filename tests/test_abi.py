@@ -343,6 +343,10 @@ def test_bwd_workspace_and_errors(L):
     assert L.ssd_scan_bwd(ctypes.byref(desc(chunk=48)), *args, P16, need, None) == UNSUP
     assert L.ssd_scan_bwd(ctypes.byref(desc(nheads=6, ngroups=4)), *args, P16, need,
                           None) == SHAPE
+    # a grid beyond 2^31 blocks at 32-token tiles, though fine for the forward's chunk
+    big = desc(batch=1 << 22, seqlen=1 << 12, nheads=8, chunk=256)
+    assert wsize(L, big)[0] == OK
+    assert L.ssd_scan_bwd_workspace_size(ctypes.byref(big), ctypes.byref(n)) == UNSUP
     # no tokens: only dA (required) and the optional state pointers are checked
     a = [None] * 16
     assert L.ssd_scan_bwd(ctypes.byref(desc(seqlen=0)), *a, None, 0, None) == NULL
