@@ -29,10 +29,13 @@
 // carried by that reverse pass.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_ops.hpp"
 #include "ssd.h"
 
 namespace ssd {
 namespace {
+
+using namespace mx;
 
 constexpr int kBQ = 32;         // tokens per gradient chunk
 constexpr int kBThreads = 256;
@@ -411,6 +414,473 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
     }
 }
 
+// ---------------------------------------------------------------- matrix cores
+// The same per-chunk gradient for bf16 x/B/C/dy, headdim 64 and d_state 64 or
+// 128, with every contraction on v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
+// bf16 inputs enter the products exactly; fp32 factors (the masked 32x32
+// matrices CB L and K L dt, and the states E and H) enter as hi/lo bf16 pairs.
+// One block (4 waves) per (b, c, g, slice of 4 heads).  Per head:
+//   K = dy x^T (every wave), then K L, CB L and GD element by element in the
+//   accumulator layout (lane: column j; registers: rows i);
+//   dx  tile t  (wave of that tile) = (dt CB L)^T dy + dt f B E^T + D dy;
+//   dB  n-tile  (its wave, summed over heads) += (dt K L)^T C + dt f x E;
+//   dC  n-tile  (its wave, summed over heads) += (K L dt) B + exp(Acs) dy H;
+// with f_j = exp(Acs_last - Acs_j).  E and H pass through LDS in two slices
+// of 32 headdim rows, the next slice in registers while the current one is
+// multiplied; <E, H> is formed from those registers in fp32.  The row sums
+// that the per-token scalars need (s3, the state-to-output term, GD dt) are
+// reduced across the lanes of the accumulator layout with ds_swizzle.
+template <int N>
+struct BwdLds {
+    static constexpr int LDN = N + 16;  // bf16 row stride: B, C and the E / H slices
+    static constexpr int LDP = 64 + 16; // bf16 row stride: x, dy
+    static constexpr int LDK = 32 + 16; // bf16 row stride: (K L dt)^T
+    static constexpr int LDC = 40;      // fp32 row stride: CB
+    static constexpr int B_ = 0;
+    static constexpr int C_ = B_ + 32 * LDN * 2;
+    static constexpr int X_ = C_ + 32 * LDN * 2;
+    static constexpr int Y_ = X_ + 32 * LDP * 2;
+    static constexpr int KH_ = Y_ + 32 * LDP * 2;
+    static constexpr int KL_ = KH_ + 32 * LDK * 2;
+    static constexpr int CB_ = KL_ + 32 * LDK * 2;
+    static constexpr int S_ = CB_ + 32 * LDC * 4;  // E hi, E lo, H hi, H lo [32][LDN]
+    static constexpr int V_ = S_ + 4 * 32 * LDN * 2;
+    // floats from V_: [2 head parities][6][32] vectors, rowg, colg, 4 x 32 s3
+    // partials, 4 x 32 state-to-output partials, 4 <E,H> partials, 4 scalars
+    static constexpr int NV = 2 * 6 * 32 + 32 + 32 + 4 * 32 + 4 * 32 + 4 + 4;
+    static constexpr int BYTES = V_ + NV * 4;
+};
+
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {  // lane l <- lane l ^ M within 32
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1f));
+}
+
+// Row of accumulator register r in this lane (column = lane % 32).
+__device__ __forceinline__ int acc_row(int r, int lane) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// Sums each accumulator register over the 32 lanes of its half wave (the 32
+// columns of its row).  Lane l returns the total of register (l % 32) / 2,
+// i.e. of row acc_row((l % 32) / 2, l); lanes 2k and 2k+1 agree.
+__device__ __forceinline__ float rowsum32(const f32x16 &v) {
+    const int l = threadIdx.x & 31;
+    float u[16], a[8];
+    // the empty asm keeps each register a separate value: otherwise the
+    // selects below fold into a lane-variable vector index (a 16-way chain
+    // of compares and selects)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        u[r] = v[r];
+        asm("" : "+v"(u[r]));
+    }
+    const bool b4 = l & 16, b3 = l & 8, b2 = l & 4, b1 = l & 2;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = (b4 ? u[k + 8] : u[k]) + swz_xor<16>(b4 ? u[k] : u[k + 8]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (b3 ? a[k + 4] : a[k]) + swz_xor<8>(b3 ? a[k] : a[k + 4]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) a[k] = (b2 ? a[k + 2] : a[k]) + swz_xor<4>(b2 ? a[k] : a[k + 2]);
+    a[0] = (b1 ? a[1] : a[0]) + swz_xor<2>(b1 ? a[0] : a[1]);
+    return a[0] + swz_xor<1>(a[0]);
+}
+
+template <int N>
+__global__ void __launch_bounds__(256, 2)
+k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
+                 const float *__restrict__ A, const bf16 *__restrict__ Bm,
+                 const bf16 *__restrict__ Cm, const float *__restrict__ D,
+                 const float *__restrict__ Acs, const float *__restrict__ Hs,
+                 const float *__restrict__ Es, const bf16 *__restrict__ dy, bf16 *__restrict__ dx,
+                 float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
+                 float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int G, int T,
+                 int nslices, int64_t nblocks) {
+    using Ly = BwdLds<N>;
+    constexpr int P = 64, NT = N / 32, LDN = Ly::LDN, LDP = Ly::LDP, LDK = Ly::LDK, LDC = Ly::LDC;
+    constexpr int NF = N / 32;   // float4 of E (and of H) per thread per slice
+    constexpr int BSEG = N / 8;  // 16-byte segments per B or C row
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16 *bs = reinterpret_cast<bf16 *>(smem + Ly::B_);
+    bf16 *cs = reinterpret_cast<bf16 *>(smem + Ly::C_);
+    bf16 *xs = reinterpret_cast<bf16 *>(smem + Ly::X_);
+    bf16 *ys = reinterpret_cast<bf16 *>(smem + Ly::Y_);
+    bf16 *klh = reinterpret_cast<bf16 *>(smem + Ly::KH_);
+    bf16 *kll = reinterpret_cast<bf16 *>(smem + Ly::KL_);
+    float *cbm = reinterpret_cast<float *>(smem + Ly::CB_);
+    bf16 *seh = reinterpret_cast<bf16 *>(smem + Ly::S_);
+    bf16 *sel = seh + 32 * LDN, *shh = sel + 32 * LDN, *shl = shh + 32 * LDN;
+    float *vec = reinterpret_cast<float *>(smem + Ly::V_);  // [2][6][32]
+    float *rowg = vec + 2 * 6 * 32, *colg = rowg + 32, *s3p = colg + 32, *hqp = s3p + 4 * 32;
+    float *red = hqp + 4 * 32, *scal = red + 4;
+
+    const uint32_t lb = xcd_block();
+    if (lb >= nblocks) return;
+    const int tid = threadIdx.x, lane = tid & 63, il = lane & 31, hw = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int R = H / G;
+    uint32_t rest = lb;
+    const int hsl = (int)(rest % (uint32_t)nslices);
+    rest /= (uint32_t)nslices;
+    const int g = (int)(rest % (uint32_t)G);
+    rest /= (uint32_t)G;
+    const int c = (int)(rest % (uint32_t)T);
+    const int64_t b = rest / (uint32_t)T;
+    const int h0 = g * R + hsl * 4;
+    const int nh = min(4, g * R + R - h0);
+    const int64_t t0 = (int64_t)c * 32;
+    const int q = (int)min((int64_t)32, L - t0);
+    const unsigned xrs = (unsigned)H * P, brs = (unsigned)G * N;
+    const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
+    const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
+    const int64_t xb = (b * L + t0) * H;  // token row base of x, dy, dx (times H)
+    const int64_t PN = (int64_t)P * N;
+
+    // wave roles: n-tiles of dB and dC, the dx p-tile (= the slice it is formed in)
+    const bool doB = NT == 4 || wave < 2;
+    const int tB = wave;
+    const bool doC = NT == 4 || wave >= 2;
+    const int tC = NT == 4 ? wave : wave - 2;
+    const bool doX = NT == 4 ? wave >= 2 : wave < 2;
+    const int tX = NT == 4 ? wave - 2 : wave;
+
+    // ---- staging helpers
+    const int xr = tid >> 3, xseg = tid & 7;
+    const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+    auto load_xy = [&](int h, u32x4 &xv, u32x4 &yv) __attribute__((always_inline)) {
+        const int64_t o = (xb + (int64_t)xr * H + h) * P + 8 * xseg;
+        xv = xr < q ? *reinterpret_cast<const u32x4 *>(x + o) : z4;
+        yv = xr < q ? *reinterpret_cast<const u32x4 *>(dy + o) : z4;
+    };
+    auto store_xy = [&](const u32x4 &xv, const u32x4 &yv) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4 *>(xs + xr * LDP + 8 * xseg) = xv;
+        *reinterpret_cast<u32x4 *>(ys + xr * LDP + 8 * xseg) = yv;
+    };
+    // per-token vectors of head h (wave 0, lane t = token): dt and Acs
+    auto load_vec = [&](int h, float &d, float &a) __attribute__((always_inline)) {
+        d = lane < q ? dt[(b * L + t0 + lane) * H + h] : 0.f;
+        a = lane < q ? Acs[(b * H + h) * L + t0 + lane] : 0.f;
+    };
+    // vectors [parity]: 0 Acs, 1 dt, 2 cumulative dt, 3 f, 4 dt f, 5 exp(Acs)
+    auto store_vec = [&](int par, float d, float a) __attribute__((always_inline)) {
+        const float cd = wave_inclusive_scan(d, lane);
+        const float alast = __shfl(a, q - 1, kWave);
+        if (lane < 32) {
+            float *v = vec + par * 6 * 32;
+            const bool in = lane < q;
+            const float f = in ? ssd_exp(alast - a) : 0.f;
+            v[lane] = a;
+            v[32 + lane] = d;
+            v[64 + lane] = cd;
+            v[96 + lane] = f;
+            v[128 + lane] = d * f;
+            v[160 + lane] = in ? ssd_exp(a) : 0.f;
+        }
+    };
+    struct SliceRegs {
+        float4 e[NF], h[NF];
+    };
+    auto load_slice = [&](int h, int s, SliceRegs &r) __attribute__((always_inline)) {
+        const int64_t o = ((b * T + c) * H + h) * PN + (int64_t)s * 32 * N;
+        const float4 *e4 = reinterpret_cast<const float4 *>(Es + o);
+        const float4 *h4 = reinterpret_cast<const float4 *>(Hs + o);
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            r.e[k] = e4[tid + 256 * k];
+            r.h[k] = h4[tid + 256 * k];
+        }
+    };
+    auto store_slice = [&](const SliceRegs &r, float &eh) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            const int e = tid + 256 * k, pl = e / (N / 4), n = 4 * (e % (N / 4));
+            uint32_t l0, l1;
+            const uint32_t h0e = split2(r.e[k].x, r.e[k].y, l0), h1e = split2(r.e[k].z, r.e[k].w, l1);
+            *reinterpret_cast<u32x2 *>(seh + pl * LDN + n) = u32x2{h0e, h1e};
+            *reinterpret_cast<u32x2 *>(sel + pl * LDN + n) = u32x2{l0, l1};
+            const uint32_t h0h = split2(r.h[k].x, r.h[k].y, l0), h1h = split2(r.h[k].z, r.h[k].w, l1);
+            *reinterpret_cast<u32x2 *>(shh + pl * LDN + n) = u32x2{h0h, h1h};
+            *reinterpret_cast<u32x2 *>(shl + pl * LDN + n) = u32x2{l0, l1};
+            eh = fmaf(r.e[k].x, r.h[k].x, eh);
+            eh = fmaf(r.e[k].y, r.h[k].y, eh);
+            eh = fmaf(r.e[k].z, r.h[k].z, eh);
+            eh = fmaf(r.e[k].w, r.h[k].w, eh);
+        }
+    };
+
+    // ---- B and C rows of the chunk (shared by the block's heads), then C.B
+    for (int e = tid; e < 32 * BSEG; e += 256) {
+        const int r = e / BSEG, sg = e % BSEG;
+        const unsigned o = (unsigned)r * brs + 8u * sg;
+        const bool in = r < q;
+        *reinterpret_cast<u32x4 *>(bs + r * LDN + 8 * sg) =
+            in ? *reinterpret_cast<const u32x4 *>(bbase + o) : z4;
+        *reinterpret_cast<u32x4 *>(cs + r * LDN + 8 * sg) =
+            in ? *reinterpret_cast<const u32x4 *>(cbase + o) : z4;
+    }
+    u32x4 nx, ny;
+    float nd = 0.f, na = 0.f;
+    SliceRegs sr;
+    load_xy(h0, nx, ny);
+    if (wave == 0) load_vec(h0, nd, na);
+    load_slice(h0, 0, sr);
+    __syncthreads();
+    if (wave == 0) {  // CB[i][j] = C_i . B_j: A = C rows, B = B rows
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < N / 16; ++ks)
+            acc = mfma32(*reinterpret_cast<const u32x4 *>(cs + il * LDN + 16 * ks + 8 * hw),
+                         *reinterpret_cast<const u32x4 *>(bs + il * LDN + 16 * ks + 8 * hw), acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cbm[acc_row(r, lane) * LDC + il] = acc[r];
+    }
+    float eh = 0.f;
+    store_xy(nx, ny);
+    if (wave == 0) store_vec(0, nd, na);
+    store_slice(sr, eh);
+    load_slice(h0, 1, sr);
+    __syncthreads();
+
+    f32x16 dBt = zero16(), dCt = zero16();
+    for (int hh = 0; hh < nh; ++hh) {
+        const int h = h0 + hh, par = hh & 1;
+        // the lane index is re-derived opaquely each head, so that the many
+        // per-lane LDS addresses and masks below are formed where they are
+        // used instead of being hoisted out of the loop (and spilled)
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int il = lane & 31, hw = lane >> 5;
+        const float *v = vec + par * 6 * 32;
+        const float *vacs = v, *vdt = v + 32, *vcd = v + 64, *vf = v + 96, *vwdf = v + 128,
+                    *vei = v + 160;
+        // ---- K = dy x^T; K L, CB L (and GD for the scalars) in the accumulator layout
+        f32x16 kl, cbl;
+        {
+            f32x16 K = zero16();
+#pragma unroll
+            for (int ks = 0; ks < P / 16; ++ks)
+                K = mfma32(*reinterpret_cast<const u32x4 *>(ys + il * LDP + 16 * ks + 8 * hw),
+                           *reinterpret_cast<const u32x4 *>(xs + il * LDP + 16 * ks + 8 * hw), K);
+            const float acs_j = vacs[il], dt_j = vdt[il];
+            float kd = 0.f, cg = 0.f;
+            f32x16 gdt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = acc_row(r, lane);
+                const bool m = il <= i && i < q;
+                const float lv = m ? ssd_exp(vacs[i] - acs_j) : 0.f;
+                const float cb = cbm[i * LDC + il];
+                kl[r] = K[r] * lv * dt_j;   // (K L)[i][j] dt_j
+                cbl[r] = cb * lv * dt_j;    // (CB L)[i][j] dt_j
+                const float gd = cb * K[r] * lv;
+                gdt[r] = gd * dt_j;
+                cg += gd;
+                if (i == il) kd += K[r];
+            }
+            if (wave == 0) {
+                // row sums of GD dt, column sums of GD, the diagonal of K
+                const float rs = rowsum32(gdt);
+                if ((lane & 1) == 0) rowg[acc_row(il >> 1, lane)] = rs;
+                cg += __shfl_xor(cg, 32, kWave);
+                if (lane < 32) colg[lane] = cg;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) kd += __shfl_xor(kd, off, kWave);
+                if (lane == 0) scal[0] = kd;
+                // (K L dt)^T as hi / lo bf16 rows j, for the dC product
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    uint32_t l0, l1;
+                    const uint32_t a0 = split2(kl[4 * gq], kl[4 * gq + 1], l0);
+                    const uint32_t a1 = split2(kl[4 * gq + 2], kl[4 * gq + 3], l1);
+                    *reinterpret_cast<u32x2 *>(klh + il * LDK + 8 * gq + 4 * hw) = u32x2{a0, a1};
+                    *reinterpret_cast<u32x2 *>(kll + il * LDK + 8 * gq + 4 * hw) = u32x2{l0, l1};
+                }
+            }
+        }
+        // ---- intra-chunk terms that need only this wave's registers
+        f32x16 accX = zero16(), accE = zero16(), accH = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float m[8];
+            u32x4 hi, lo;
+            if (doB) {  // dB[j][n] += sum_i (K L dt)[i][j] C[i][n]
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[e] = kl[8 * ks + e];
+                split8(m, hi, lo);
+                const u32x4 bo = tr_operand<true>(cs, LDN, 16 * ks, 32 * tB);
+                dBt = mfma32(hi, bo, dBt);
+                dBt = mfma32(lo, bo, dBt);
+            }
+            if (doX) {  // dx[j][p] = sum_i (CB L dt)[i][j] dy[i][p]
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m[e] = cbl[8 * ks + e];
+                split8(m, hi, lo);
+                const u32x4 bo = tr_operand<true>(ys, LDP, 16 * ks, 32 * tX);
+                accX = mfma32(hi, bo, accX);
+                accX = mfma32(lo, bo, accX);
+            }
+        }
+        // ---- one 32-row slice of E and H (in LDS)
+        auto slice = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (doB) {  // x E: A = x rows j, B = E [p][n]
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(xs + il * LDP + 32 * s + 16 * ks + 8 * hw);
+                    accE = mfma32(a, tr_operand<false>(seh, LDN, 16 * ks, 32 * tB), accE);
+                    accE = mfma32(a, tr_operand<false>(sel, LDN, 16 * ks, 32 * tB), accE);
+                }
+                if (doC) {  // dy H: A = dy rows i, B = H [p][n]
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(ys + il * LDP + 32 * s + 16 * ks + 8 * hw);
+                    accH = mfma32(a, tr_operand<false>(shh, LDN, 16 * ks, 32 * tC), accH);
+                    accH = mfma32(a, tr_operand<false>(shl, LDN, 16 * ks, 32 * tC), accH);
+                }
+            }
+            if (doX && tX == s) {  // B E^T: A = B rows j, B = E rows p; then dx of tile s
+                f32x16 accS = zero16();
+#pragma unroll
+                for (int ks = 0; ks < N / 16; ++ks) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(bs + il * LDN + 16 * ks + 8 * hw);
+                    accS = mfma32(a, *reinterpret_cast<const u32x4 *>(seh + il * LDN + 16 * ks + 8 * hw), accS);
+                    accS = mfma32(a, *reinterpret_cast<const u32x4 *>(sel + il * LDN + 16 * ks + 8 * hw), accS);
+                }
+                const float Dh = D ? D[h] : 0.f;
+                const int p = 32 * s + il;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = acc_row(r, lane);
+                    if (j < q) {
+                        const float yv = bf16_to_f32(ys[j * LDP + p]);
+                        const float o = fmaf(Dh, yv, fmaf(vwdf[j], accS[r], accX[r]));
+                        dx[(xb + (int64_t)j * H + h) * P + p] = f32_to_bf16(o);
+                    }
+                }
+            }
+        };
+        slice(0);
+        __syncthreads();  // slice 0 and (K L dt)^T: done / visible
+        if (doC) {        // dC[i][n] += sum_j (K L dt)[i][j] B[j][n]
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const u32x4 bo = tr_operand<false>(bs, LDN, 16 * ks, 32 * tC);
+                dCt = mfma32(tr_operand<false>(klh, LDK, 16 * ks, 0), bo, dCt);
+                dCt = mfma32(tr_operand<false>(kll, LDK, 16 * ks, 0), bo, dCt);
+            }
+        }
+        store_slice(sr, eh);
+        const bool more = hh + 1 < nh;
+        if (more) {
+            load_slice(h + 1, 0, sr);
+            load_xy(h + 1, nx, ny);
+            if (wave == 0) load_vec(h + 1, nd, na);
+        }
+        __syncthreads();  // slice 1 visible
+        slice(1);
+        // ---- state terms into dB, dC; row sums for s3 and the state-to-output term
+        if (doB) {
+            f32x16 sv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = acc_row(r, lane);
+                dBt[r] = fmaf(vwdf[j], accE[r], dBt[r]);
+                sv[r] = vf[j] * accE[r] * bf16_to_f32(bs[j * LDN + 32 * tB + il]);
+            }
+            const float sum = rowsum32(sv);
+            if ((lane & 1) == 0) s3p[tB * 32 + acc_row(il >> 1, lane)] = sum;
+        }
+        if (doC) {
+            f32x16 sv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = acc_row(r, lane);
+                const float t = vei[i] * accH[r];
+                dCt[r] += t;
+                sv[r] = t * bf16_to_f32(cs[i * LDN + 32 * tC + il]);
+            }
+            const float sum = rowsum32(sv);
+            if ((lane & 1) == 0) hqp[tC * 32 + acc_row(il >> 1, lane)] = sum;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) eh += __shfl_xor(eh, off, kWave);
+        if (lane == 0) red[wave] = eh;
+        eh = 0.f;
+        __syncthreads();  // partials visible; x, dy and the slice buffer free
+        // ---- per-token scalars: dAcs, ddt, dA, dD (wave 0, lane t = token)
+        if (wave == 0) {
+            const int t = lane;
+            const bool in = t < q;
+            const float EH = ((red[0] + red[1]) + red[2]) + red[3];
+            const float alast = vacs[q - 1];
+            float s3d = 0.f, dacs = 0.f, colgd = 0.f, dtt = 0.f;
+            if (in) {
+                float hqt = 0.f;
+#pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    s3d += s3p[k * 32 + t];
+                    hqt += hqp[k * 32 + t];
+                }
+                dtt = vdt[t];
+                colgd = colg[t];
+                dacs = rowg[t] - dtt * colgd + hqt - s3d * dtt;
+            }
+            float s3sum = s3d * dtt;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s3sum += __shfl_xor(s3sum, off, kWave);
+            if (t == q - 1) dacs += s3sum + ssd_exp(alast) * EH;
+            float suf = dacs;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const float o = __shfl_down(suf, d, kWave);
+                if (t + d < kWave) suf += o;
+            }
+            if (in) ddt[(b * L + t0 + t) * H + h] = A[h] * suf + colgd + s3d;
+            float da = in ? dacs * vcd[t] : 0.f;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
+            if (lane == 0) {
+                atomicAdd(&dA[h], da);
+                if (dD) atomicAdd(&dD[h], scal[0]);
+            }
+        }
+        if (more) {  // the next head's rows, vectors and first slice
+            store_xy(nx, ny);
+            if (wave == 0) store_vec(par ^ 1, nd, na);
+            store_slice(sr, eh);
+            load_slice(h + 1, 1, sr);
+        }
+        __syncthreads();
+    }
+    // ---- dB, dC of the block's heads: one atomic per element
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int j = acc_row(r, lane);
+        if (j < q) {
+            const int64_t o = (b * L + t0 + j) * G * N + (int64_t)g * N + il;
+            if (doB) atomicAdd(dB + o + 32 * tB, dBt[r]);
+            if (doC) atomicAdd(dC + o + 32 * tC, dCt[r]);
+        }
+    }
+}
+
+template <int N>
+void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const float *A,
+                       const void *Bm, const void *Cm, const float *D, const float *Acs,
+                       const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
+                       float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
+    static bool attr_set = false;  // once per instantiation (per process)
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd_mfma<N>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, BwdLds<N>::BYTES);
+        attr_set = true;
+    }
+    const int64_t R = s.H / s.G;
+    const int64_t nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    const int64_t nblocks = s.B * s.T * s.G * nslices;
+    k_chunk_bwd_mfma<N><<<padded_grid(nblocks), 256, BwdLds<N>::BYTES, st>>>(
+        (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, Hs, Es,
+        (const bf16 *)dy, (bf16 *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.G, (int)s.T,
+        (int)nslices, nblocks);
+}
+
 // Rows of E / H per slice so that the whole block fits the 160 KB of LDS
 // (at most 8 KB of slice, so two float4 per thread carry it; at least one row).
 int bwd_slice_rows(int P, int N, size_t *lds_bytes) {
@@ -459,7 +929,12 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
         else if (s.N == 128) SSD_BWD(T_, 4);           \
         else SSD_BWD(T_, 8);                           \
     } while (0)
-    if (s.dtype == SSD_BF16)
+    if (bwd_states_mfma_ok(s)) {
+        if (s.N == 64)
+            launch_bwd_mfma_t<64>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
+        else
+            launch_bwd_mfma_t<128>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
+    } else if (s.dtype == SSD_BF16)
         SSD_BWD_KI(bf16);
     else
         SSD_BWD_KI(float);

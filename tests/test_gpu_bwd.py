@@ -70,6 +70,11 @@ SHAPES = {
     "bf16_2p7b_heads": (1, 300, 4, 64, 128, 1, "bf16"),
     "f32_max_slices": (1, 40, 2, 256, 256, 2, "f32"),
     "bf16_groups": (2, 70, 8, 32, 64, 4, "bf16"),
+    # headdim 64, d_state 64 / 128 (the matrix-core kernel): 3 and 5 heads per
+    # group (partial head slices), two groups, and a last chunk of one token
+    "bf16_n64_groups": (2, 77, 6, 64, 64, 2, "bf16"),
+    "bf16_n128_groups": (1, 45, 10, 64, 128, 2, "bf16"),
+    "bf16_n64_one_token_tail": (1, 33, 4, 64, 64, 1, "bf16"),
 }
 
 
