@@ -140,8 +140,10 @@ ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes);
  *   dD      [nheads] fp32, or NULL (not computed)
  *   dinit   [batch, nheads, headdim, dstate]  fp32, or NULL (not computed)
  * dt is the activated step size (the edges of ssd_scan_fwd_ex are not
- * differentiated here).  The kernels tile by 32 tokens whatever d->chunk is;
- * like the forward, the result does not depend on the chunk beyond rounding.
+ * differentiated here).  The kernels choose their own chunking whatever
+ * d->chunk is (64 tokens for bf16 with headdim 64 and dstate 64 or 128, else
+ * 32); like the forward, the result does not depend on the chunk beyond
+ * rounding.
  * dB, dC, dA and dD are accumulated with floating-point atomics, so their
  * last bits may differ between runs.  seqlen == 0 or batch == 0: dA = dD = 0
  * and dinit = dfinal (or 0). */

@@ -112,7 +112,6 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
     const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N, PN = (int64_t)P * N;
     const int64_t bo = ((b * L + t0) * G + g) * N;
     const int nq = N / 4;
-    const int nitems = Q * nq;
     // item k of this thread: token j = tid % Q, state elements 4 (tid / Q + 8 k) ..
     const int jt = tid % Q, nq0 = tid / Q;
     // E / H slices move through registers: the next slice's loads are issued
@@ -416,40 +415,46 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
 
 // ---------------------------------------------------------------- matrix cores
 // The same per-chunk gradient for bf16 x/B/C/dy, headdim 64 and d_state 64 or
-// 128, with every contraction on v_mfma_f32_32x32x16_bf16 (fp32 accumulation).
-// bf16 inputs enter the products exactly; fp32 factors (the masked 32x32
-// matrices CB L and K L dt, and the states E and H) enter as hi/lo bf16 pairs.
-// One block (4 waves) per (b, c, g, slice of 4 heads).  Per head:
-//   K = dy x^T (every wave), then K L, CB L and GD element by element in the
-//   accumulator layout (lane: column j; registers: rows i);
-//   dx  tile t  (wave of that tile) = (dt CB L)^T dy + dt f B E^T + D dy;
-//   dB  n-tile  (its wave, summed over heads) += (dt K L)^T C + dt f x E;
-//   dC  n-tile  (its wave, summed over heads) += (K L dt) B + exp(Acs) dy H;
+// 128, with every contraction on v_mfma_f32_32x32x16_bf16 (fp32 accumulation),
+// for chunks of Q = 32 QT tokens (QT row tiles of 32).  bf16 inputs enter the
+// products exactly; fp32 factors (the masked matrices CB L dt and K L dt, and
+// the states E and H) enter as hi/lo bf16 pairs.  One block (4 QT waves) per
+// (b, c, g, slice of 4 heads); wave w works on row tile rt = w / 4 (tokens
+// 32 rt ..) with role w % 4.  Per head:
+//   K = dy x^T tiles (ti, rt), ti >= rt, then K L, CB L and GD element by
+//   element in the accumulator layout (lane: column j; registers: rows i);
+//   dx  (rt, p-tile)  = sum_ti (dt CB L)^T dy + dt f B E^T + D dy;
+//   dB  (rt, n-tile) += sum_ti (dt K L)^T C + dt f x E      (summed over heads);
+//   dC  (rt, n-tile) += sum_tj (K L dt) B + exp(Acs) dy H   (summed over heads);
 // with f_j = exp(Acs_last - Acs_j).  E and H pass through LDS in two slices
 // of 32 headdim rows, the next slice in registers while the current one is
 // multiplied; <E, H> is formed from those registers in fp32.  The row sums
 // that the per-token scalars need (s3, the state-to-output term, GD dt) are
 // reduced across the lanes of the accumulator layout with ds_swizzle.
-template <int N>
+template <int N, int QT>
 struct BwdLds {
+    static constexpr int Q = 32 * QT;
+    static constexpr int NCB = QT * (QT + 1) / 2;  // causal 32x32 tiles of C.B
     static constexpr int LDN = N + 16;  // bf16 row stride: B, C and the E / H slices
     static constexpr int LDP = 64 + 16; // bf16 row stride: x, dy
-    static constexpr int LDK = 32 + 16; // bf16 row stride: (K L dt)^T
-    static constexpr int LDC = 40;      // fp32 row stride: CB
+    static constexpr int LDK = Q + 16;  // bf16 row stride: (K L dt)^T
+    static constexpr int LDC = 40;      // fp32 row stride: C.B tiles
     static constexpr int B_ = 0;
-    static constexpr int C_ = B_ + 32 * LDN * 2;
-    static constexpr int X_ = C_ + 32 * LDN * 2;
-    static constexpr int Y_ = X_ + 32 * LDP * 2;
-    static constexpr int KH_ = Y_ + 32 * LDP * 2;
-    static constexpr int KL_ = KH_ + 32 * LDK * 2;
-    static constexpr int CB_ = KL_ + 32 * LDK * 2;
-    static constexpr int S_ = CB_ + 32 * LDC * 4;  // E hi, E lo, H hi, H lo [32][LDN]
+    static constexpr int C_ = B_ + Q * LDN * 2;
+    static constexpr int X_ = C_ + Q * LDN * 2;
+    static constexpr int Y_ = X_ + Q * LDP * 2;
+    static constexpr int KH_ = Y_ + Q * LDP * 2;
+    static constexpr int KL_ = KH_ + Q * LDK * 2;
+    static constexpr int CB_ = KL_ + Q * LDK * 2;
+    static constexpr int S_ = CB_ + NCB * 32 * LDC * 4;  // E hi, E lo, H hi, H lo [32][LDN]
     static constexpr int V_ = S_ + 4 * 32 * LDN * 2;
-    // floats from V_: [2 head parities][6][32] vectors, rowg, colg, 4 x 32 s3
-    // partials, 4 x 32 state-to-output partials, 4 <E,H> partials, 4 scalars
-    static constexpr int NV = 2 * 6 * 32 + 32 + 32 + 4 * 32 + 4 * 32 + 4 + 4;
+    // floats from V_: [2 head parities][6][Q] vectors, [QT][Q] partial row sums
+    // of GD dt, [Q] column sums of GD, [2 slices][Q] s3 partials, [2][Q]
+    // state-to-output partials, [4 QT] <E,H> partials, [4] diagonals of K
+    static constexpr int NV = 12 * Q + QT * Q + Q + 2 * Q + 2 * Q + 4 * QT + 4;
     static constexpr int BYTES = V_ + NV * 4;
 };
+static_assert(BwdLds<128, 2>::BYTES <= 160 * 1024, "LDS budget");
 
 template <int M>
 __device__ __forceinline__ float swz_xor(float v) {  // lane l <- lane l ^ M within 32
@@ -486,8 +491,21 @@ __device__ __forceinline__ float rowsum32(const f32x16 &v) {
     return a[0] + swz_xor<1>(a[0]);
 }
 
-template <int N>
-__global__ void __launch_bounds__(256, 2)
+// MFMA A operand from 8 consecutive bf16 values at p (LDS) times w, in fp32,
+// split into a hi / lo bf16 pair.
+__device__ __forceinline__ void scaled_operand(const bf16 *p, float w, u32x4 &hi, u32x4 &lo) {
+    const u32x4 raw = *reinterpret_cast<const u32x4 *>(p);
+    float m[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        m[2 * k] = lo_bf16(raw[k]) * w;
+        m[2 * k + 1] = hi_bf16(raw[k]) * w;
+    }
+    split8(m, hi, lo);
+}
+
+template <int N, int QT>
+__global__ void __launch_bounds__(256 * QT, QT == 1 ? 2 : 1)
 k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                  const float *__restrict__ A, const bf16 *__restrict__ Bm,
                  const bf16 *__restrict__ Cm, const float *__restrict__ D,
@@ -496,10 +514,11 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                  float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
                  float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int G, int T,
                  int nslices, int64_t nblocks) {
-    using Ly = BwdLds<N>;
-    constexpr int P = 64, NT = N / 32, LDN = Ly::LDN, LDP = Ly::LDP, LDK = Ly::LDK, LDC = Ly::LDC;
-    constexpr int NF = N / 32;   // float4 of E (and of H) per thread per slice
-    constexpr int BSEG = N / 8;  // 16-byte segments per B or C row
+    using Ly = BwdLds<N, QT>;
+    constexpr int Q = Ly::Q, P = 64, NT = N / 32, NTH = 256 * QT, W = 4 * QT;
+    constexpr int LDN = Ly::LDN, LDP = Ly::LDP, LDK = Ly::LDK, LDC = Ly::LDC;
+    constexpr int NF = 8 * N / NTH;  // float4 of E (and of H) per thread per slice
+    constexpr int BSEG = N / 8;      // 16-byte segments per B or C row
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16 *bs = reinterpret_cast<bf16 *>(smem + Ly::B_);
     bf16 *cs = reinterpret_cast<bf16 *>(smem + Ly::C_);
@@ -510,13 +529,13 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     float *cbm = reinterpret_cast<float *>(smem + Ly::CB_);
     bf16 *seh = reinterpret_cast<bf16 *>(smem + Ly::S_);
     bf16 *sel = seh + 32 * LDN, *shh = sel + 32 * LDN, *shl = shh + 32 * LDN;
-    float *vec = reinterpret_cast<float *>(smem + Ly::V_);  // [2][6][32]
-    float *rowg = vec + 2 * 6 * 32, *colg = rowg + 32, *s3p = colg + 32, *hqp = s3p + 4 * 32;
-    float *red = hqp + 4 * 32, *scal = red + 4;
+    float *vec = reinterpret_cast<float *>(smem + Ly::V_);  // [2][6][Q]
+    float *rowgp = vec + 2 * 6 * Q, *colg = rowgp + QT * Q, *s3p = colg + Q, *hqp = s3p + 2 * Q;
+    float *red = hqp + 2 * Q, *scal = red + 4 * QT;
 
     const uint32_t lb = xcd_block();
     if (lb >= nblocks) return;
-    const int tid = threadIdx.x, lane = tid & 63, il = lane & 31, hw = lane >> 5;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = H / G;
     uint32_t rest = lb;
@@ -526,31 +545,40 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     rest /= (uint32_t)G;
     const int c = (int)(rest % (uint32_t)T);
     const int64_t b = rest / (uint32_t)T;
-    const int h0 = g * R + hsl * 4;
-    const int nh = min(4, g * R + R - h0);
-    const int64_t t0 = (int64_t)c * 32;
-    const int q = (int)min((int64_t)32, L - t0);
-    const unsigned xrs = (unsigned)H * P, brs = (unsigned)G * N;
+    const int h0 = g * R + hsl * kHeadsPerBlock;
+    const int nh = min(kHeadsPerBlock, g * R + R - h0);
+    const int64_t t0 = (int64_t)c * Q;
+    const int q = (int)min((int64_t)Q, L - t0);
+    // block-uniform 64-bit bases, per-lane 32-bit offsets (a chunk spans fewer
+    // than 2^31 elements of every tensor)
+    const unsigned brs = (unsigned)G * N, xrs = (unsigned)H * P;
     const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
     const int64_t xb = (b * L + t0) * H;  // token row base of x, dy, dx (times H)
     const int64_t PN = (int64_t)P * N;
 
-    // wave roles: n-tiles of dB and dC, the dx p-tile (= the slice it is formed in)
-    const bool doB = NT == 4 || wave < 2;
-    const int tB = wave;
-    const bool doC = NT == 4 || wave >= 2;
-    const int tC = NT == 4 ? wave : wave - 2;
-    const bool doX = NT == 4 ? wave >= 2 : wave < 2;
-    const int tX = NT == 4 ? wave - 2 : wave;
+    // wave roles within the row tile rt: n-tiles of dB and dC, the dx p-tile
+    // (= the slice it is formed in), and the writer of the tile's shared terms
+    const int rt = wave >> 2, wk = wave & 3;
+    const bool doB = NT == 4 || wk < 2;
+    const int tB = wk;
+    const bool doC = NT == 4 || wk >= 2;
+    const int tC = NT == 4 ? wk : wk - 2;
+    const bool doX = NT == 4 ? wk >= 2 : wk < 2;
+    const int tX = NT == 4 ? wk - 2 : wk;
+    const bool writer = wk == 0;
+    // the wave's 32x32 product per E / H slice sX: B E^T (dx and s3) on the
+    // dx waves, C H^T (the state-to-output term) on the others
+    const int sX = doX ? tX : (NT == 4 ? wk : wk - 2);
 
     // ---- staging helpers
-    const int xr = tid >> 3, xseg = tid & 7;
+    const int xr = tid >> 3, xseg = tid & 7;  // one 16-byte segment of x and of dy
     const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
     auto load_xy = [&](int h, u32x4 &xv, u32x4 &yv) __attribute__((always_inline)) {
-        const int64_t o = (xb + (int64_t)xr * H + h) * P + 8 * xseg;
-        xv = xr < q ? *reinterpret_cast<const u32x4 *>(x + o) : z4;
-        yv = xr < q ? *reinterpret_cast<const u32x4 *>(dy + o) : z4;
+        const int64_t base = (xb + h) * P;
+        const unsigned o = (unsigned)xr * xrs + 8u * xseg;
+        xv = xr < q ? *reinterpret_cast<const u32x4 *>(x + base + o) : z4;
+        yv = xr < q ? *reinterpret_cast<const u32x4 *>(dy + base + o) : z4;
     };
     auto store_xy = [&](const u32x4 &xv, const u32x4 &yv) __attribute__((always_inline)) {
         *reinterpret_cast<u32x4 *>(xs + xr * LDP + 8 * xseg) = xv;
@@ -558,23 +586,27 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     };
     // per-token vectors of head h (wave 0, lane t = token): dt and Acs
     auto load_vec = [&](int h, float &d, float &a) __attribute__((always_inline)) {
-        d = lane < q ? dt[(b * L + t0 + lane) * H + h] : 0.f;
-        a = lane < q ? Acs[(b * H + h) * L + t0 + lane] : 0.f;
+        const int lane = tid & 63;
+        const float *dtb = dt + (b * L + t0) * H + h;
+        const float *ab = Acs + (b * H + h) * L + t0;
+        d = lane < q ? dtb[(unsigned)lane * H] : 0.f;
+        a = lane < q ? ab[lane] : 0.f;
     };
     // vectors [parity]: 0 Acs, 1 dt, 2 cumulative dt, 3 f, 4 dt f, 5 exp(Acs)
     auto store_vec = [&](int par, float d, float a) __attribute__((always_inline)) {
-        const float cd = wave_inclusive_scan(d, lane);
-        const float alast = __shfl(a, q - 1, kWave);
-        if (lane < 32) {
-            float *v = vec + par * 6 * 32;
+        const int lane = tid & 63;
+        const float cd = wave_scan_dpp(d);
+        const float alast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), q - 1));
+        if (lane < Q) {
+            float *v = vec + par * 6 * Q;
             const bool in = lane < q;
             const float f = in ? ssd_exp(alast - a) : 0.f;
             v[lane] = a;
-            v[32 + lane] = d;
-            v[64 + lane] = cd;
-            v[96 + lane] = f;
-            v[128 + lane] = d * f;
-            v[160 + lane] = in ? ssd_exp(a) : 0.f;
+            v[Q + lane] = d;
+            v[2 * Q + lane] = cd;
+            v[3 * Q + lane] = f;
+            v[4 * Q + lane] = d * f;
+            v[5 * Q + lane] = in ? ssd_exp(a) : 0.f;
         }
     };
     struct SliceRegs {
@@ -586,14 +618,14 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         const float4 *h4 = reinterpret_cast<const float4 *>(Hs + o);
 #pragma unroll
         for (int k = 0; k < NF; ++k) {
-            r.e[k] = e4[tid + 256 * k];
-            r.h[k] = h4[tid + 256 * k];
+            r.e[k] = e4[tid + NTH * k];
+            r.h[k] = h4[tid + NTH * k];
         }
     };
     auto store_slice = [&](const SliceRegs &r, float &eh) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < NF; ++k) {
-            const int e = tid + 256 * k, pl = e / (N / 4), n = 4 * (e % (N / 4));
+            const int e = tid + NTH * k, pl = e / (N / 4), n = 4 * (e % (N / 4));
             uint32_t l0, l1;
             const uint32_t h0e = split2(r.e[k].x, r.e[k].y, l0), h1e = split2(r.e[k].z, r.e[k].w, l1);
             *reinterpret_cast<u32x2 *>(seh + pl * LDN + n) = u32x2{h0e, h1e};
@@ -609,7 +641,7 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     };
 
     // ---- B and C rows of the chunk (shared by the block's heads), then C.B
-    for (int e = tid; e < 32 * BSEG; e += 256) {
+    for (int e = tid; e < Q * BSEG; e += NTH) {
         const int r = e / BSEG, sg = e % BSEG;
         const unsigned o = (unsigned)r * brs + 8u * sg;
         const bool in = r < q;
@@ -620,25 +652,31 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     }
     u32x4 nx, ny;
     float nd = 0.f, na = 0.f;
-    SliceRegs sr;
+    // E / H slices in registers: sr[s] holds slice s of the next head whose
+    // slice s is not yet in LDS (two slices, one head, ahead)
+    SliceRegs sr[2];
     load_xy(h0, nx, ny);
     if (wave == 0) load_vec(h0, nd, na);
-    load_slice(h0, 0, sr);
+    load_slice(h0, 0, sr[0]);
+    load_slice(h0, 1, sr[1]);
     __syncthreads();
-    if (wave == 0) {  // CB[i][j] = C_i . B_j: A = C rows, B = B rows
+    if (wave < Ly::NCB) {  // C.B tile (ti, tj): A = C rows of ti, B = B rows of tj
+        const int lane = tid & 63, il = lane & 31, hw = lane >> 5;
+        const int ti = wave == 0 ? 0 : 1, tj = wave - ti * (ti + 1) / 2;
         f32x16 acc = zero16();
 #pragma unroll
         for (int ks = 0; ks < N / 16; ++ks)
-            acc = mfma32(*reinterpret_cast<const u32x4 *>(cs + il * LDN + 16 * ks + 8 * hw),
-                         *reinterpret_cast<const u32x4 *>(bs + il * LDN + 16 * ks + 8 * hw), acc);
+            acc = mfma32(*reinterpret_cast<const u32x4 *>(cs + (32 * ti + il) * LDN + 16 * ks + 8 * hw),
+                         *reinterpret_cast<const u32x4 *>(bs + (32 * tj + il) * LDN + 16 * ks + 8 * hw),
+                         acc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cbm[acc_row(r, lane) * LDC + il] = acc[r];
+        for (int r = 0; r < 16; ++r) cbm[(wave * 32 + acc_row(r, lane)) * LDC + il] = acc[r];
     }
     float eh = 0.f;
     store_xy(nx, ny);
     if (wave == 0) store_vec(0, nd, na);
-    store_slice(sr, eh);
-    load_slice(h0, 1, sr);
+    store_slice(sr[0], eh);
+    if (nh > 1) load_slice(h0 + 1, 0, sr[0]);
     __syncthreads();
 
     f32x16 dBt = zero16(), dCt = zero16();
@@ -650,157 +688,180 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         int lane = tid & 63;
         asm volatile("" : "+v"(lane));
         const int il = lane & 31, hw = lane >> 5;
-        const float *v = vec + par * 6 * 32;
-        const float *vacs = v, *vdt = v + 32, *vcd = v + 64, *vf = v + 96, *vwdf = v + 128,
-                    *vei = v + 160;
-        // ---- K = dy x^T; K L, CB L (and GD for the scalars) in the accumulator layout
-        f32x16 kl, cbl;
+        const int jg = 32 * rt + il;  // this lane's token in row tile rt
+        const float *v = vec + par * 6 * Q;
+        const float *vacs = v, *vdt = v + Q, *vcd = v + 2 * Q, *vf = v + 3 * Q, *vwdf = v + 4 * Q,
+                    *vei = v + 5 * Q;
+        // ---- K tiles (ti, rt) = dy x^T; K L dt, CB L dt (and GD) in the
+        // accumulator layout; the intra-chunk dB and dx products from registers
+        f32x16 accX = zero16();
         {
-            f32x16 K = zero16();
+            const float acs_j = vacs[jg], dt_j = vdt[jg];
+            float cg = 0.f, kd = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < P / 16; ++ks)
-                K = mfma32(*reinterpret_cast<const u32x4 *>(ys + il * LDP + 16 * ks + 8 * hw),
-                           *reinterpret_cast<const u32x4 *>(xs + il * LDP + 16 * ks + 8 * hw), K);
-            const float acs_j = vacs[il], dt_j = vdt[il];
-            float kd = 0.f, cg = 0.f;
-            f32x16 gdt;
+            for (int ti = 0; ti < QT; ++ti) {
+                if (ti < rt) continue;
+                f32x16 K = zero16();
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = acc_row(r, lane);
-                const bool m = il <= i && i < q;
-                const float lv = m ? ssd_exp(vacs[i] - acs_j) : 0.f;
-                const float cb = cbm[i * LDC + il];
-                kl[r] = K[r] * lv * dt_j;   // (K L)[i][j] dt_j
-                cbl[r] = cb * lv * dt_j;    // (CB L)[i][j] dt_j
-                const float gd = cb * K[r] * lv;
-                gdt[r] = gd * dt_j;
-                cg += gd;
-                if (i == il) kd += K[r];
-            }
-            if (wave == 0) {
-                // row sums of GD dt, column sums of GD, the diagonal of K
-                const float rs = rowsum32(gdt);
-                if ((lane & 1) == 0) rowg[acc_row(il >> 1, lane)] = rs;
-                cg += __shfl_xor(cg, 32, kWave);
-                if (lane < 32) colg[lane] = cg;
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) kd += __shfl_xor(kd, off, kWave);
-                if (lane == 0) scal[0] = kd;
-                // (K L dt)^T as hi / lo bf16 rows j, for the dC product
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    uint32_t l0, l1;
-                    const uint32_t a0 = split2(kl[4 * gq], kl[4 * gq + 1], l0);
-                    const uint32_t a1 = split2(kl[4 * gq + 2], kl[4 * gq + 3], l1);
-                    *reinterpret_cast<u32x2 *>(klh + il * LDK + 8 * gq + 4 * hw) = u32x2{a0, a1};
-                    *reinterpret_cast<u32x2 *>(kll + il * LDK + 8 * gq + 4 * hw) = u32x2{l0, l1};
-                }
-            }
-        }
-        // ---- intra-chunk terms that need only this wave's registers
-        f32x16 accX = zero16(), accE = zero16(), accH = zero16();
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            float m[8];
-            u32x4 hi, lo;
-            if (doB) {  // dB[j][n] += sum_i (K L dt)[i][j] C[i][n]
-#pragma unroll
-                for (int e = 0; e < 8; ++e) m[e] = kl[8 * ks + e];
-                split8(m, hi, lo);
-                const u32x4 bo = tr_operand<true>(cs, LDN, 16 * ks, 32 * tB);
-                dBt = mfma32(hi, bo, dBt);
-                dBt = mfma32(lo, bo, dBt);
-            }
-            if (doX) {  // dx[j][p] = sum_i (CB L dt)[i][j] dy[i][p]
-#pragma unroll
-                for (int e = 0; e < 8; ++e) m[e] = cbl[8 * ks + e];
-                split8(m, hi, lo);
-                const u32x4 bo = tr_operand<true>(ys, LDP, 16 * ks, 32 * tX);
-                accX = mfma32(hi, bo, accX);
-                accX = mfma32(lo, bo, accX);
-            }
-        }
-        // ---- one 32-row slice of E and H (in LDS)
-        auto slice = [&](int s) __attribute__((always_inline)) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (doB) {  // x E: A = x rows j, B = E [p][n]
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(xs + il * LDP + 32 * s + 16 * ks + 8 * hw);
-                    accE = mfma32(a, tr_operand<false>(seh, LDN, 16 * ks, 32 * tB), accE);
-                    accE = mfma32(a, tr_operand<false>(sel, LDN, 16 * ks, 32 * tB), accE);
-                }
-                if (doC) {  // dy H: A = dy rows i, B = H [p][n]
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(ys + il * LDP + 32 * s + 16 * ks + 8 * hw);
-                    accH = mfma32(a, tr_operand<false>(shh, LDN, 16 * ks, 32 * tC), accH);
-                    accH = mfma32(a, tr_operand<false>(shl, LDN, 16 * ks, 32 * tC), accH);
-                }
-            }
-            if (doX && tX == s) {  // B E^T: A = B rows j, B = E rows p; then dx of tile s
-                f32x16 accS = zero16();
-#pragma unroll
-                for (int ks = 0; ks < N / 16; ++ks) {
-                    const u32x4 a = *reinterpret_cast<const u32x4 *>(bs + il * LDN + 16 * ks + 8 * hw);
-                    accS = mfma32(a, *reinterpret_cast<const u32x4 *>(seh + il * LDN + 16 * ks + 8 * hw), accS);
-                    accS = mfma32(a, *reinterpret_cast<const u32x4 *>(sel + il * LDN + 16 * ks + 8 * hw), accS);
-                }
-                const float Dh = D ? D[h] : 0.f;
-                const int p = 32 * s + il;
+                for (int ks = 0; ks < P / 16; ++ks)
+                    K = mfma32(*reinterpret_cast<const u32x4 *>(ys + (32 * ti + il) * LDP + 16 * ks + 8 * hw),
+                               *reinterpret_cast<const u32x4 *>(xs + jg * LDP + 16 * ks + 8 * hw), K);
+                const float *cbt = cbm + (ti * (ti + 1) / 2 + rt) * 32 * LDC;
+                f32x16 kl, cbl, gdt;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int j = acc_row(r, lane);
-                    if (j < q) {
-                        const float yv = bf16_to_f32(ys[j * LDP + p]);
-                        const float o = fmaf(Dh, yv, fmaf(vwdf[j], accS[r], accX[r]));
-                        dx[(xb + (int64_t)j * H + h) * P + p] = f32_to_bf16(o);
+                    const int i = 32 * ti + acc_row(r, lane);
+                    // exp for every element, then the causal / length mask as a
+                    // select (a branch per element otherwise)
+                    const float e = ssd_exp(vacs[i] - acs_j);
+                    const float lv = (jg <= i && i < q) ? e : 0.f;
+                    const float cb = cbt[acc_row(r, lane) * LDC + il];
+                    kl[r] = K[r] * lv * dt_j;   // (K L)[i][j] dt_j
+                    cbl[r] = cb * lv * dt_j;    // (CB L)[i][j] dt_j
+                    const float gd = cb * K[r] * lv;
+                    if (writer) {
+                        gdt[r] = gd * dt_j;
+                        cg += gd;
+                        kd += i == jg ? K[r] : 0.f;
                     }
                 }
+                if (writer) {
+                    // row sums of GD dt (partial over this column tile)
+                    const float rs = rowsum32(gdt);
+                    if ((lane & 1) == 0) rowgp[rt * Q + 32 * ti + acc_row(il >> 1, lane)] = rs;
+                    // (K L dt)^T as hi / lo bf16 rows j, for the dC product
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        uint32_t l0, l1;
+                        const uint32_t a0 = split2(kl[4 * gq], kl[4 * gq + 1], l0);
+                        const uint32_t a1 = split2(kl[4 * gq + 2], kl[4 * gq + 3], l1);
+                        const int o = jg * LDK + 32 * ti + 8 * gq + 4 * hw;
+                        *reinterpret_cast<u32x2 *>(klh + o) = u32x2{a0, a1};
+                        *reinterpret_cast<u32x2 *>(kll + o) = u32x2{l0, l1};
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    float m[8];
+                    u32x4 hi, lo;
+                    if (doB) {  // dB[j][n] += sum_i (K L dt)[i][j] C[i][n]
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) m[e] = kl[8 * ks + e];
+                        split8(m, hi, lo);
+                        const u32x4 bo = tr_operand<true>(cs + 32 * ti * LDN, LDN, 16 * ks, 32 * tB);
+                        dBt = mfma32(hi, bo, dBt);
+                        dBt = mfma32(lo, bo, dBt);
+                    }
+                    if (doX) {  // dx[j][p] = sum_i (CB L dt)[i][j] dy[i][p]
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) m[e] = cbl[8 * ks + e];
+                        split8(m, hi, lo);
+                        const u32x4 bo = tr_operand<true>(ys + 32 * ti * LDP, LDP, 16 * ks, 32 * tX);
+                        accX = mfma32(hi, bo, accX);
+                        accX = mfma32(lo, bo, accX);
+                    }
+                }
+                // one K tile at a time: keeps the temporaries of the two tiles
+                // from being live together
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (writer) {
+                // column sums of GD and the diagonal of K for this column tile
+                cg += __shfl_xor(cg, 32, kWave);
+                if (lane < 32) colg[jg] = cg;
+                kd = wave_sum_dpp(kd);
+                if (lane == 0) scal[rt] = kd;
+            }
+        }
+        // ---- one 32-row slice of E and H (in LDS).  The per-row scales of the
+        // state terms (dt f for x E, exp(Acs) for dy H) go into the A operand,
+        // formed in fp32 and split hi / lo, so both products accumulate
+        // straight into dB and dC
+        auto slice = [&](int s) __attribute__((always_inline)) {
+            const float wB = vwdf[jg], wC = vei[jg];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int pc = 32 * s + 16 * ks + 8 * hw;
+                u32x4 hi, lo;
+                if (doB) {  // dB[j][n] += dt_j f_j sum_p x[j][p] E[p][n]
+                    scaled_operand(xs + jg * LDP + pc, wB, hi, lo);
+                    const u32x4 bh = tr_operand<false>(seh, LDN, 16 * ks, 32 * tB);
+                    dBt = mfma32(hi, bh, dBt);
+                    dBt = mfma32(hi, tr_operand<false>(sel, LDN, 16 * ks, 32 * tB), dBt);
+                    dBt = mfma32(lo, bh, dBt);
+                }
+                if (doC) {  // dC[i][n] += exp(Acs_i) sum_p dy[i][p] H[p][n]
+                    scaled_operand(ys + jg * LDP + pc, wC, hi, lo);
+                    const u32x4 bh = tr_operand<false>(shh, LDN, 16 * ks, 32 * tC);
+                    dCt = mfma32(hi, bh, dCt);
+                    dCt = mfma32(hi, tr_operand<false>(shl, LDN, 16 * ks, 32 * tC), dCt);
+                    dCt = mfma32(lo, bh, dCt);
+                }
+            }
+            if (sX == s) {
+                // B E^T (rows j, columns p of this slice) on the dx waves,
+                // C H^T (rows i) on the others: A = B or C rows, B = E or H rows
+                const bf16 *ar = (doX ? bs : cs) + jg * LDN + 8 * hw;
+                const bf16 *sh = (doX ? seh : shh) + il * LDN + 8 * hw;
+                const bf16 *sl = (doX ? sel : shl) + il * LDN + 8 * hw;
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int ks = 0; ks < N / 16; ++ks) {
+                    const u32x4 a = *reinterpret_cast<const u32x4 *>(ar + 16 * ks);
+                    acc = mfma32(a, *reinterpret_cast<const u32x4 *>(sh + 16 * ks), acc);
+                    acc = mfma32(a, *reinterpret_cast<const u32x4 *>(sl + 16 * ks), acc);
+                }
+                const int p = 32 * s + il;
+                f32x16 sv;
+                if (doX) {  // dx of tile (rt, s); s3_j = f_j sum_p x[j][p] (B E^T)[j][p]
+                    const float Dh = D ? D[h] : 0.f;
+                    bf16 *dxh = dx + (xb + h) * P;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int j = 32 * rt + acc_row(r, lane);
+                        const float yv = bf16_to_f32(ys[j * LDP + p]);
+                        if (j < q) {
+                            const float o = fmaf(Dh, yv, fmaf(vwdf[j], acc[r], accX[r]));
+                            dxh[(unsigned)j * xrs + p] = f32_to_bf16(o);
+                        }
+                        sv[r] = vf[j] * bf16_to_f32(xs[j * LDP + p]) * acc[r];
+                    }
+                } else {  // exp(Acs_i) sum_p dy[i][p] (C H^T)[i][p]
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = 32 * rt + acc_row(r, lane);
+                        sv[r] = vei[i] * bf16_to_f32(ys[i * LDP + p]) * acc[r];
+                    }
+                }
+                const float sum = rowsum32(sv);
+                if ((lane & 1) == 0) (doX ? s3p : hqp)[s * Q + 32 * rt + acc_row(il >> 1, lane)] = sum;
             }
         };
         slice(0);
         __syncthreads();  // slice 0 and (K L dt)^T: done / visible
-        if (doC) {        // dC[i][n] += sum_j (K L dt)[i][j] B[j][n]
+        if (doC) {        // dC[i][n] += sum_{j <= i} (K L dt)[i][j] B[j][n]
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 bo = tr_operand<false>(bs, LDN, 16 * ks, 32 * tC);
-                dCt = mfma32(tr_operand<false>(klh, LDK, 16 * ks, 0), bo, dCt);
-                dCt = mfma32(tr_operand<false>(kll, LDK, 16 * ks, 0), bo, dCt);
+            for (int tj = 0; tj < QT; ++tj) {
+                if (tj > rt) continue;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int k0 = 32 * tj + 16 * ks;
+                    const u32x4 bo = tr_operand<false>(bs, LDN, k0, 32 * tC);
+                    dCt = mfma32(tr_operand<false>(klh, LDK, k0, 32 * rt), bo, dCt);
+                    dCt = mfma32(tr_operand<false>(kll, LDK, k0, 32 * rt), bo, dCt);
+                }
             }
         }
-        store_slice(sr, eh);
+        store_slice(sr[1], eh);
         const bool more = hh + 1 < nh;
         if (more) {
-            load_slice(h + 1, 0, sr);
+            load_slice(h + 1, 1, sr[1]);
             load_xy(h + 1, nx, ny);
             if (wave == 0) load_vec(h + 1, nd, na);
         }
         __syncthreads();  // slice 1 visible
         slice(1);
-        // ---- state terms into dB, dC; row sums for s3 and the state-to-output term
-        if (doB) {
-            f32x16 sv;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = acc_row(r, lane);
-                dBt[r] = fmaf(vwdf[j], accE[r], dBt[r]);
-                sv[r] = vf[j] * accE[r] * bf16_to_f32(bs[j * LDN + 32 * tB + il]);
-            }
-            const float sum = rowsum32(sv);
-            if ((lane & 1) == 0) s3p[tB * 32 + acc_row(il >> 1, lane)] = sum;
-        }
-        if (doC) {
-            f32x16 sv;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = acc_row(r, lane);
-                const float t = vei[i] * accH[r];
-                dCt[r] += t;
-                sv[r] = t * bf16_to_f32(cs[i * LDN + 32 * tC + il]);
-            }
-            const float sum = rowsum32(sv);
-            if ((lane & 1) == 0) hqp[tC * 32 + acc_row(il >> 1, lane)] = sum;
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) eh += __shfl_xor(eh, off, kWave);
+        eh = wave_sum_dpp(eh);
         if (lane == 0) red[wave] = eh;
         eh = 0.f;
         __syncthreads();  // partials visible; x, dy and the slice buffer free
@@ -808,74 +869,77 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         if (wave == 0) {
             const int t = lane;
             const bool in = t < q;
-            const float EH = ((red[0] + red[1]) + red[2]) + red[3];
+            float EH = 0.f, KD = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) EH += red[w];
+#pragma unroll
+            for (int k = 0; k < QT; ++k) KD += scal[k];
             const float alast = vacs[q - 1];
             float s3d = 0.f, dacs = 0.f, colgd = 0.f, dtt = 0.f;
             if (in) {
-                float hqt = 0.f;
+                float hqt = 0.f, rg = 0.f;
 #pragma unroll
-                for (int k = 0; k < NT; ++k) {
-                    s3d += s3p[k * 32 + t];
-                    hqt += hqp[k * 32 + t];
+                for (int k = 0; k < 2; ++k) {  // the two E / H slices
+                    s3d += s3p[k * Q + t];
+                    hqt += hqp[k * Q + t];
                 }
+#pragma unroll
+                for (int k = 0; k < QT; ++k)
+                    if (32 * k <= t) rg += rowgp[k * Q + t];  // column tiles at or left of t's
                 dtt = vdt[t];
                 colgd = colg[t];
-                dacs = rowg[t] - dtt * colgd + hqt - s3d * dtt;
+                dacs = rg - dtt * colgd + hqt - s3d * dtt;
             }
-            float s3sum = s3d * dtt;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) s3sum += __shfl_xor(s3sum, off, kWave);
+            const float s3sum = wave_sum_dpp(s3d * dtt);
             if (t == q - 1) dacs += s3sum + ssd_exp(alast) * EH;
-            float suf = dacs;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const float o = __shfl_down(suf, d, kWave);
-                if (t + d < kWave) suf += o;
-            }
-            if (in) ddt[(b * L + t0 + t) * H + h] = A[h] * suf + colgd + s3d;
-            float da = in ? dacs * vcd[t] : 0.f;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) da += __shfl_xor(da, off, kWave);
+            // suffix sums: a prefix scan of the lane-reversed values
+            const float rsum = wave_scan_dpp(__shfl(dacs, 63 - t, kWave));
+            const float suf = __shfl(rsum, 63 - t, kWave);
+            if (in) ddt[((b * L + t0) * H + h) + (unsigned)t * H] = A[h] * suf + colgd + s3d;
+            const float da = wave_sum_dpp(in ? dacs * vcd[t] : 0.f);
             if (lane == 0) {
                 atomicAdd(&dA[h], da);
-                if (dD) atomicAdd(&dD[h], scal[0]);
+                if (dD) atomicAdd(&dD[h], KD);
             }
         }
         if (more) {  // the next head's rows, vectors and first slice
             store_xy(nx, ny);
             if (wave == 0) store_vec(par ^ 1, nd, na);
-            store_slice(sr, eh);
-            load_slice(h + 1, 1, sr);
+            store_slice(sr[0], eh);
+            if (hh + 2 < nh) load_slice(h + 2, 0, sr[0]);
         }
         __syncthreads();
     }
     // ---- dB, dC of the block's heads: one atomic per element
+    const int lane = tid & 63, il = lane & 31;
+    float *dBb = dB + ((b * L + t0) * G + g) * N + 32 * tB;
+    float *dCb = dC + ((b * L + t0) * G + g) * N + 32 * tC;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int j = acc_row(r, lane);
+        const int j = 32 * rt + acc_row(r, lane);
         if (j < q) {
-            const int64_t o = (b * L + t0 + j) * G * N + (int64_t)g * N + il;
-            if (doB) atomicAdd(dB + o + 32 * tB, dBt[r]);
-            if (doC) atomicAdd(dC + o + 32 * tC, dCt[r]);
+            const unsigned o = (unsigned)j * brs + il;
+            if (doB) atomicAdd(dBb + o, dBt[r]);
+            if (doC) atomicAdd(dCb + o, dCt[r]);
         }
     }
 }
 
-template <int N>
+template <int N, int QT>
 void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                        const void *Bm, const void *Cm, const float *D, const float *Acs,
                        const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                        float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
     static bool attr_set = false;  // once per instantiation (per process)
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd_mfma<N>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, BwdLds<N>::BYTES);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd_mfma<N, QT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, BwdLds<N, QT>::BYTES);
         attr_set = true;
     }
     const int64_t R = s.H / s.G;
     const int64_t nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
     const int64_t nblocks = s.B * s.T * s.G * nslices;
-    k_chunk_bwd_mfma<N><<<padded_grid(nblocks), 256, BwdLds<N>::BYTES, st>>>(
+    k_chunk_bwd_mfma<N, QT><<<padded_grid(nblocks), 256 * QT, BwdLds<N, QT>::BYTES, st>>>(
         (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, Hs, Es,
         (const bf16 *)dy, (bf16 *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.G, (int)s.T,
         (int)nslices, nblocks);
@@ -929,11 +993,12 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
         else if (s.N == 128) SSD_BWD(T_, 4);           \
         else SSD_BWD(T_, 8);                           \
     } while (0)
-    if (bwd_states_mfma_ok(s)) {
-        if (s.N == 64)
-            launch_bwd_mfma_t<64>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
-        else
-            launch_bwd_mfma_t<128>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st);
+    if (bwd_states_mfma_ok(s)) {  // 64-token chunks (two row tiles)
+#define SSD_BWDM(N_, QT_) \
+    launch_bwd_mfma_t<N_, QT_>(s, x, dt, A, Bm, Cm, D, Acs, Hs, Es, dy, dx, ddt, dB, dC, dA, dD, st)
+        if (s.N == 64) SSD_BWDM(64, 2);
+        else SSD_BWDM(128, 2);
+#undef SSD_BWDM
     } else if (s.dtype == SSD_BF16)
         SSD_BWD_KI(bf16);
     else

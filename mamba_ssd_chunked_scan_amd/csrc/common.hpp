@@ -91,6 +91,33 @@ __device__ __forceinline__ ChunkPos chunk_pos(const int2 *ctab, int64_t c, int Q
     return ChunkPos{t0, (int)min((int64_t)Q, L - t0)};
 }
 
+// v from lane (this lane's position under DPP control CTRL); lanes whose
+// source is outside the row, or whose row is not in ROW_MASK, get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave on the DPP network: shifts
+// by 1, 2, 4 and 8 lanes within each row of 16, then each row's total carried
+// into the later rows with row_bcast:15 (into rows 1 and 3) and row_bcast:31
+// (into rows 2 and 3).  Six dependent VALU steps, no LDS.
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+    v += dpp_f<0x111>(v);       // row_shr:1
+    v += dpp_f<0x112>(v);       // row_shr:2
+    v += dpp_f<0x114>(v);       // row_shr:4
+    v += dpp_f<0x118>(v);       // row_shr:8
+    v += dpp_f<0x142, 0xa>(v);  // row_bcast:15
+    v += dpp_f<0x143, 0xc>(v);  // row_bcast:31
+    return v;
+}
+
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_scan_dpp(v)), 63));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 #pragma unroll

@@ -74,14 +74,18 @@ void launch_state_passing_rev(const ScanShape &s, float *dstates, const float *A
                               const float *dfin, float *dinit, hipStream_t st);
 // Per-chunk gradients from the entering states H and the end-state
 // derivatives E: dx and ddt written; dB, dC (fp32), dA, dD (may be null)
-// accumulated with atomics into zeroed buffers.  s.Q must be 32.
+// accumulated with atomics into zeroed buffers.  s.Q is 32, or 64 on the
+// matrix-core path.
 void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const float *A,
                       const void *Bm, const void *Cm, const float *D, const float *Acs,
                       const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                       float *dB, float *dC, float *dA, float *dD, hipStream_t st);
 
-// The gradient's 32-token chunk states (and their adjoint, with x = dy and
-// B = C) on the matrix cores, for the shapes bwd_states_mfma_ok accepts.
+// Whether the gradient takes the matrix-core path (bf16, headdim 64, d_state
+// 64 or 128, fixed length); it then runs at 64-token chunks, else at 32.
+bool bwd_mfma_ok(const ScanShape &s);
+// The gradient's 64-token chunk states (and their adjoint, with x = dy and
+// B = C) on the matrix cores, for bwd_mfma_ok shapes.
 bool bwd_states_mfma_ok(const ScanShape &s);
 void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
                             const float *dt, const float *Acs, float *out, bool adjoint,

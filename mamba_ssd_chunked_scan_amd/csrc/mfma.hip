@@ -783,18 +783,21 @@ bool mfma_supported(const ScanShape &s) {
         }                                                                \
     } while (0)
 
-bool bwd_states_mfma_ok(const ScanShape &s) {
-    const bool offsets32 = (s.Q + 64) * s.H * s.P * 2 < (int64_t(1) << 31) &&
-                           (s.Q + 64) * s.G * s.N * 2 < (int64_t(1) << 31);
-    return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) && s.Q == kJT &&
-           offsets32 && !s.ctab;
+bool bwd_mfma_ok(const ScanShape &s) {
+    // offsets within one 64-token chunk (plus two stages) stay below 2^31
+    const int64_t q = 64;
+    const bool offsets32 = (q + 64) * s.H * s.P * 2 < (int64_t(1) << 31) &&
+                           (q + 64) * s.G * s.N * 2 < (int64_t(1) << 31);
+    return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) && offsets32 && !s.ctab;
 }
 
-template <int N, bool kAdj>
+bool bwd_states_mfma_ok(const ScanShape &s) { return bwd_mfma_ok(s) && s.Q == 64; }
+
+template <int Q, int N, bool kAdj>
 void launch_bwd_states_t(const ScanShape &s, const void *xin, const void *bin, const float *dt,
                          const float *Acs, float *out, hipStream_t st) {
     const int64_t nb = s.B * s.T * s.H;
-    k_chunk_state_mfma<kJT, N, false, kAdj><<<padded_grid(nb), 256, 0, st>>>(
+    k_chunk_state_mfma<Q, N, false, kAdj><<<padded_grid(nb), 256, 0, st>>>(
         (const bf16 *)xin, (const bf16 *)bin, dt, nullptr, const_cast<float *>(Acs), out, s.L,
         (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr, nullptr);
 }
@@ -802,13 +805,14 @@ void launch_bwd_states_t(const ScanShape &s, const void *xin, const void *bin, c
 void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
                             const float *dt, const float *Acs, float *out, bool adjoint,
                             hipStream_t st) {
-    if (s.N == 128) {
-        if (adjoint) launch_bwd_states_t<128, true>(s, xin, bin, dt, Acs, out, st);
-        else launch_bwd_states_t<128, false>(s, xin, bin, dt, Acs, out, st);
-    } else {
-        if (adjoint) launch_bwd_states_t<64, true>(s, xin, bin, dt, Acs, out, st);
-        else launch_bwd_states_t<64, false>(s, xin, bin, dt, Acs, out, st);
-    }
+#define SSD_BWDS(Q_, N_)                                                     \
+    do {                                                                     \
+        if (adjoint) launch_bwd_states_t<Q_, N_, true>(s, xin, bin, dt, Acs, out, st);  \
+        else launch_bwd_states_t<Q_, N_, false>(s, xin, bin, dt, Acs, out, st);         \
+    } while (0)
+    if (s.N == 128) SSD_BWDS(64, 128);
+    else SSD_BWDS(64, 64);
+#undef SSD_BWDS
 }
 
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,

@@ -106,11 +106,13 @@ bool act_active(const ssd::DtAct &a) { return a.bias || a.softplus || a.limit; }
 // The gradient tiles by 32 tokens whatever the forward chunk (its results do
 // not depend on the chunk beyond rounding): Acs, entering states, end-state
 // derivatives at that chunk.
+// The gradient's own chunking: 64 tokens on the matrix-core path (half the
+// state traffic of 32), 32 on the generic one.
 ScanShape bwd_shape(const ScanShape &s) {
     ScanShape b = s;
-    b.Q = 32;
-    b.T = (s.L + 31) / 32;
     b.ctab = nullptr;
+    b.Q = ssd::bwd_mfma_ok(b) ? 64 : 32;
+    b.T = (s.L + b.Q - 1) / b.Q;
     b.sch = nullptr;
     return b;
 }
@@ -295,7 +297,7 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
     ssd::launch_copy_or_zero(dC, nullptr, bcn, hs);
     ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
     if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
-    // the forward's entering states at 32-token chunks
+    // the forward's entering states at the gradient's chunks
     const bool mm = ssd::bwd_states_mfma_ok(b);
     ssd::launch_chunk_cumsum(b, dt, A, Acs, hs);
     if (mm) ssd::launch_bwd_states_mfma(b, x, B, dt, Acs, Hst, false, hs);

@@ -322,12 +322,18 @@ def test_varlen_pointer_errors(L):
 
 
 def test_bwd_workspace_and_errors(L):
-    d = desc()   # batch 1, seqlen 512, 8 heads, headdim 64, dstate 128
+    d = desc()   # batch 1, seqlen 512, 8 heads, headdim 64, dstate 128, bf16
     n = ctypes.c_size_t(0)
     assert L.ssd_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == OK
-    T32 = 512 // 32
-    assert n.value == r256(8 * 512 * 4) + 2 * r256(T32 * 8 * 64 * 128 * 4)
+    # Acs, then the entering states and the end-state derivatives at the
+    # gradient's own chunking: 64 tokens on the matrix-core path ...
+    T64 = 512 // 64
+    assert n.value == r256(8 * 512 * 4) + 2 * r256(T64 * 8 * 64 * 128 * 4)
     need = n.value
+    # ... and 32 elsewhere (fp32 inputs; headdim 32)
+    for other in (desc(dtype=0), desc(headdim=32)):
+        assert L.ssd_scan_bwd_workspace_size(ctypes.byref(other), ctypes.byref(n)) == OK
+        assert n.value == r256(8 * 512 * 4) + 2 * r256(16 * 8 * other.headdim * 128 * 4)
     args = [P16] * 16  # x dt A B C D init dy dfinal dx ddt dA dB dC dD dinit
     assert L.ssd_scan_bwd(None, *args, P16, need, None) == NULL
     for which in (0, 1, 2, 3, 4, 7, 9, 10, 11, 12, 13):   # required
