@@ -513,7 +513,7 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                  const float *__restrict__ Es, const bf16 *__restrict__ dy, bf16 *__restrict__ dx,
                  float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
                  float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int G, int T,
-                 int nslices, int64_t nblocks) {
+                 int hpb, int nslices, int64_t nblocks) {
     using Ly = BwdLds<N, QT>;
     constexpr int Q = Ly::Q, P = 64, NT = N / 32, NTH = 256 * QT, W = 4 * QT;
     constexpr int LDN = Ly::LDN, LDP = Ly::LDP, LDK = Ly::LDK, LDC = Ly::LDC;
@@ -545,8 +545,8 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     rest /= (uint32_t)G;
     const int c = (int)(rest % (uint32_t)T);
     const int64_t b = rest / (uint32_t)T;
-    const int h0 = g * R + hsl * kHeadsPerBlock;
-    const int nh = min(kHeadsPerBlock, g * R + R - h0);
+    const int h0 = g * R + hsl * hpb;
+    const int nh = min(hpb, g * R + R - h0);
     const int64_t t0 = (int64_t)c * Q;
     const int q = (int)min((int64_t)Q, L - t0);
     // block-uniform 64-bit bases, per-lane 32-bit offsets (a chunk spans fewer
@@ -936,13 +936,17 @@ void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const
                                   hipFuncAttributeMaxDynamicSharedMemorySize, BwdLds<N, QT>::BYTES);
         attr_set = true;
     }
+    // heads per block: 4 (dB and dC accumulate over them before their
+    // atomics), fewer when that would leave the grid under two blocks per CU
     const int64_t R = s.H / s.G;
-    const int64_t nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
+    int hpb = kHeadsPerBlock;
+    while (hpb > 1 && s.B * s.T * s.G * ((R + hpb - 1) / hpb) < 512) hpb /= 2;
+    const int64_t nslices = (R + hpb - 1) / hpb;
     const int64_t nblocks = s.B * s.T * s.G * nslices;
     k_chunk_bwd_mfma<N, QT><<<padded_grid(nblocks), 256 * QT, BwdLds<N, QT>::BYTES, st>>>(
         (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, Hs, Es,
         (const bf16 *)dy, (bf16 *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.G, (int)s.T,
-        (int)nslices, nblocks);
+        hpb, (int)nslices, nblocks);
 }
 
 // Rows of E / H per slice so that the whole block fits the 160 KB of LDS
