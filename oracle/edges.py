@@ -47,3 +47,27 @@ def silu(z):
 def gate(y, z):
     """The gated output y * silu(z)."""
     return f64(y) * silu(z)
+
+
+def gated_rmsnorm(y, z, weight, eps: float, groups: int):
+    """Gated RMSNorm of a scan output, the step that the pyshine tour of the
+    Mamba repository (Mamba2 in the block walk-through) says replaces the
+    plain output activation.  The page names the module and gives no formula;
+    the reading taken is the gate first, then a root-mean-square
+    normalisation over channel groups, then a per-channel weight:
+
+        v   = y * silu(z)            (v = y when z is None)
+        out = v / sqrt(mean(v^2 over the group) + eps) * weight
+
+    y, z: [..., nheads, headdim]; weight: [nheads * headdim]; the channels of
+    a token, in (head, headdim) order, split into ``groups`` equal groups of
+    whole heads."""
+    v = f64(y) if z is None else gate(y, z)
+    shape = v.shape
+    H, P = shape[-2], shape[-1]
+    if H % groups:
+        raise ValueError("groups must divide nheads")
+    g = v.reshape(shape[:-2] + (groups, (H // groups) * P))
+    ms = np.mean(g * g, axis=-1, keepdims=True)
+    out = g / np.sqrt(ms + float(eps))
+    return out.reshape(shape) * f64(weight).reshape(H, P)

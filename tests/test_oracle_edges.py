@@ -71,3 +71,62 @@ def test_gate_is_linear_in_y():
     assert np.max(np.abs(edges.gate(y + 2 * y2, z)
                          - (edges.gate(y, z) + 2 * edges.gate(y2, z)))) < 1e-14
     assert np.array_equal(edges.gate(y, np.zeros_like(z)), np.zeros_like(y))
+
+
+def test_gated_rmsnorm_worked_example():
+    """[3, 4] with no gate, unit weight and eps 0: the mean square is 12.5, so
+    the output is [3, 4] / sqrt(12.5), worked by hand."""
+    y = np.array([[[3.0, 4.0]]])          # [token, head, headdim]
+    out = edges.gated_rmsnorm(y, None, np.ones(2), 0.0, 1)
+    assert np.allclose(out, [[[0.848528137423857, 1.131370849898476]]], rtol=1e-14)
+    # eps enters under the root: [3, 4] / sqrt(12.5 + 0.5) = [3, 4] / sqrt(13)
+    out = edges.gated_rmsnorm(y, None, np.ones(2), 0.5, 1)
+    assert np.allclose(out, [[[3 / np.sqrt(13.0), 4 / np.sqrt(13.0)]]], rtol=1e-14)
+
+
+def test_gated_rmsnorm_unit_rms_and_weight():
+    """With unit weight and eps 0 every group of the output has RMS exactly 1;
+    the weight then scales each channel on its own."""
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((3, 7, 6, 4))  # [batch, token, head, headdim]
+    z = rng.standard_normal((3, 7, 6, 4))
+    out = edges.gated_rmsnorm(y, z, np.ones(24), 0.0, 3)
+    g = out.reshape(3, 7, 3, 8)
+    assert np.allclose(np.sqrt(np.mean(g * g, axis=-1)), 1.0, rtol=1e-13)
+    w = rng.standard_normal(24)
+    outw = edges.gated_rmsnorm(y, z, w, 0.0, 3)
+    assert np.allclose(outw, out * w.reshape(6, 4), rtol=1e-13)
+
+
+def test_gated_rmsnorm_groups_are_independent_and_scale_free():
+    """Changing the heads of one group leaves the other groups' outputs alone;
+    with eps 0 a positive scale of y (per group) cancels."""
+    rng = np.random.default_rng(6)
+    y = rng.standard_normal((5, 4, 8))      # [token, head, headdim]
+    w = rng.standard_normal(32)
+    out = edges.gated_rmsnorm(y, None, w, 0.0, 2)
+    y2 = y.copy()
+    y2[:, 2:] *= 7.5                        # group 1 (heads 2, 3) scaled
+    out2 = edges.gated_rmsnorm(y2, None, w, 0.0, 2)
+    assert np.array_equal(out2[:, :2], out[:, :2])
+    assert np.allclose(out2[:, 2:], out[:, 2:], rtol=1e-13)
+    y3 = y.copy()
+    y3[:, 2:] = rng.standard_normal((5, 2, 8))
+    assert np.array_equal(edges.gated_rmsnorm(y3, None, w, 0.0, 2)[:, :2], out[:, :2])
+
+
+def test_gated_rmsnorm_gates_before_normalising():
+    """The gate is applied before the norm: a gate that is constant over a
+    group's channels (z equal everywhere) cancels in the norm (eps 0) up to
+    its sign, which a gate applied after the norm would not do."""
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal((4, 2, 8))
+    w = np.ones(16)
+    z = np.full_like(y, 1.3)                # silu(1.3) > 0, the same everywhere
+    assert np.allclose(edges.gated_rmsnorm(y, z, w, 0.0, 1),
+                       edges.gated_rmsnorm(y, None, w, 0.0, 1), rtol=1e-13)
+    # with eps > 0 the gate's size matters (a gate after the norm would scale
+    # the output by exactly silu(1.3))
+    a = edges.gated_rmsnorm(y, z, w, 1.0, 1)
+    b = edges.gated_rmsnorm(y, None, w, 1.0, 1) * edges.silu(1.3)
+    assert not np.allclose(a, b, rtol=1e-6)
