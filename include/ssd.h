@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -168,6 +168,19 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
  *   z           gate with the layout and dtype of x, or NULL: every output is
  *               multiplied by silu(z) = z / (1 + exp(-z)) in fp32 before its
  *               single rounding to the output dtype
+ *   norm_weight [nheads * headdim] fp32, or NULL (no norm): the gated
+ *               RMSNorm that the same tour's Mamba2 block applies to the scan
+ *               output (its layernorm_gated module).  Each token's channels
+ *               (head-major, headdim inner) split into norm_groups groups of
+ *               whole heads; within a group, after the gate,
+ *                   out = v / sqrt(mean(v^2) + norm_eps) * norm_weight
+ *               computed in fp32 from the stored gated output (one more
+ *               rounding to the output dtype).  It runs as a separate pass
+ *               over y after the scan, since a group spans heads that the scan
+ *               kernels write in different blocks.
+ *   norm_eps    >= 0 (with 0, an all-zero group gives NaN)
+ *   norm_groups groups per token, dividing nheads; 0 means ngroups (the B/C
+ *               groups: the heads that share B and C share a norm)
  * The step size the recurrence uses is the activated dt, everywhere dt enters
  * (decay and input weight).  A NULL ssd_edges pointer, or one with every field
  * zero / NULL, is the plain operation. */
@@ -177,6 +190,9 @@ typedef struct ssd_edges {
     float dt_min, dt_max;
     int32_t dt_softplus;
     int32_t dt_limit;
+    const float *norm_weight;
+    float norm_eps;
+    int32_t norm_groups;
 } ssd_edges;
 
 /* ssd_scan_fwd with the edges above (edges may be NULL).  dt here is the raw

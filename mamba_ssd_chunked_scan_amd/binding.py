@@ -53,10 +53,13 @@ class StepDesc(ctypes.Structure):
 
 
 class Edges(ctypes.Structure):
-    """ssd_edges: the dt activation and output gate fused into the scan."""
+    """ssd_edges: the dt activation and output gate fused into the scan, and
+    the gated RMSNorm pass over its output."""
     _fields_ = [("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
                 ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
-                ("dt_softplus", ctypes.c_int32), ("dt_limit", ctypes.c_int32)]
+                ("dt_softplus", ctypes.c_int32), ("dt_limit", ctypes.c_int32),
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("norm_groups", ctypes.c_int32)]
 
 
 class SSDError(RuntimeError):
@@ -67,6 +70,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
+ABI_VERSION = 6  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -82,6 +86,9 @@ def lib() -> ctypes.CDLL:
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_abi_version.argtypes = []
         L.ssd_abi_version.restype = ctypes.c_int
+        if L.ssd_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI {L.ssd_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild the library")
         L.ssd_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
                                               ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 10 + [ctypes.c_size_t, _P]
@@ -185,12 +192,19 @@ def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype
     return n.value
 
 
-def _edges(x, H, dt_bias, dt_softplus, dt_limit, z):
-    """An Edges struct for the fused dt activation / output gate, or None
-    when none is requested (the plain operation)."""
-    if dt_bias is None and not dt_softplus and dt_limit is None and z is None:
+def _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight=None, norm_eps=1e-5,
+           norm_groups=0):
+    """An Edges struct for the fused dt activation / output gate and the
+    gated RMSNorm, or None when none is requested (the plain operation)."""
+    if (dt_bias is None and not dt_softplus and dt_limit is None and z is None
+            and norm_weight is None):
         return None
     e = Edges()
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", (H * P,), torch.float32, x.device)
+        e.norm_weight = norm_weight.data_ptr()
+        e.norm_eps = float(norm_eps)
+        e.norm_groups = int(norm_groups)
     if dt_bias is not None:
         _need(dt_bias, "dt_bias", (H,), torch.float32, x.device)
         e.dt_bias = dt_bias.data_ptr()
@@ -210,7 +224,8 @@ def _eref(e):
 
 def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
              return_final_state: bool = True, final_state=None, workspace=None, y=None,
-             dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None):
+             dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None,
+             norm_weight=None, norm_eps: float = 1e-5, norm_groups: int = 0):
     """Chunked SSD scan.  Returns (y, final_state); final_state is None when not requested.
 
     ``final_state`` may be a preallocated [batch, nheads, headdim, dstate] fp32
@@ -218,7 +233,10 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
     of at least :func:`workspace_size` bytes; ``y`` a preallocated output.
     Fused edges: ``dt_bias`` [nheads] fp32 is added to dt, ``dt_softplus``
     applies softplus, ``dt_limit`` = (lo, hi) clamps the result; ``z`` (x's
-    shape and dtype) gates the output, y * silu(z).
+    shape and dtype) gates the output, y * silu(z).  ``norm_weight``
+    [nheads * headdim] fp32 then applies the gated RMSNorm over
+    ``norm_groups`` groups of whole heads per token (0: ngroups) with
+    ``norm_eps``.
     """
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
     dev = x.device
@@ -240,7 +258,7 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < n.value or workspace.device != dev:
         raise ValueError(f"workspace needs {n.value} bytes on {dev}")
-    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
     st = lib().ssd_scan_fwd_ex(ctypes.byref(desc), _eref(e), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                _ptr(C), _ptr(D), _ptr(init_state), _ptr(y), _ptr(final_state),
                                _ptr(workspace), workspace.numel(), _stream(dev))
@@ -296,7 +314,8 @@ def varlen_workspace_size(nseq, total, nheads, headdim, dstate, ngroups, chunk, 
 
 def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, chunk: int = 256, init_states=None,
                     return_final_states: bool = True, final_states=None, workspace=None,
-                    y=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None):
+                    y=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None, z=None,
+                    norm_weight=None, norm_eps: float = 1e-5, norm_groups: int = 0):
     """Ragged batch: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]) of
     the packed x [total, nheads, headdim], dt [total, nheads], B/C [total,
     ngroups, dstate]; cu_seqlens is an int32 device tensor [nseq + 1].
@@ -336,7 +355,7 @@ def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, chunk: int = 256, init_s
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < n.value or workspace.device != dev:
         raise ValueError(f"workspace needs {n.value} bytes on {dev}")
-    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
     st = lib().ssd_scan_fwd_varlen(ctypes.byref(desc), _eref(e), _ptr(cu_seqlens), _ptr(x),
                                    _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                                    _ptr(init_states), _ptr(y), _ptr(final_states),
@@ -346,7 +365,7 @@ def scan_fwd_varlen(x, dt, A, B, C, cu_seqlens, D=None, chunk: int = 256, init_s
 
 
 def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,
-         dt_limit=None, z=None):
+         dt_limit=None, z=None, norm_weight=None, norm_eps: float = 1e-5, norm_groups: int = 0):
     """One decode token; ``state`` [batch, nheads, headdim, dstate] fp32 is updated in place.
     Fused edges as for :func:`scan_fwd` (``z`` has x's shape)."""
     if state.dim() != 4 or x.dim() != 3 or B.dim() != 3:
@@ -369,7 +388,7 @@ def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool 
     else:
         _need(y, "y", x.shape, io, dev)
     desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
-    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
     st = lib().ssd_step_ex(ctypes.byref(desc), _eref(e), _ptr(state), _ptr(x), _ptr(dt), _ptr(A),
                            _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
     _check("ssd_step_ex", st)
@@ -377,7 +396,8 @@ def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool 
 
 
 def step_multi(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus: bool = False,
-               dt_limit=None, z=None):
+               dt_limit=None, z=None, norm_weight=None, norm_eps: float = 1e-5,
+               norm_groups: int = 0):
     """nsteps decode tokens in one launch (inputs in the prefill layout: x
     [batch, nsteps, nheads, headdim], dt [batch, nsteps, nheads], B/C
     [batch, nsteps, ngroups, dstate]); ``state`` is updated in place.  Equal to
@@ -402,7 +422,7 @@ def step_multi(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus:
     else:
         _need(y, "y", x.shape, io, dev)
     desc = StepDesc(Bt, H, P, N, G, _io_dtype(x), 0)
-    e = _edges(x, H, dt_bias, dt_softplus, dt_limit, z)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
     st = lib().ssd_step_multi_ex(ctypes.byref(desc), _eref(e), T, _ptr(state), _ptr(x), _ptr(dt),
                                  _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y), _stream(dev))
     _check("ssd_step_multi_ex", st)

@@ -621,6 +621,37 @@ void launch_step_t(const StepShape &s, int64_t nsteps, float *state, const void 
                                               act, (const Tin *)z);
 }
 
+// ------------------------------------------------------------- gated norm
+// One block per (token, norm group) pair (grid-stride over the pairs): the
+// group's CG channels are read twice, once for the sum of squares (a fixed
+// reduction order: lanes, then the four waves in turn) and once to scale and
+// store them, so the call needs no workspace and repeats bit for bit.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_gated_norm(T *__restrict__ y, const float *__restrict__ w, float eps, int64_t pairs,
+             int64_t HP, int CG, int NG) {
+    __shared__ float part[4];
+    const int tid = threadIdx.x;
+    for (int64_t pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
+        const int64_t tok = pr / NG;
+        const int k = (int)(pr - tok * NG);
+        T *row = y + tok * HP + (int64_t)k * CG;
+        const float *wr = w + (int64_t)k * CG;
+        float ss = 0.f;
+        for (int c = tid; c < CG; c += 256) {
+            const float v = Elem<T>::ld(row, c);
+            ss = fmaf(v, v, ss);
+        }
+        ss = wave_sum_dpp(ss);
+        if ((tid & 63) == 0) part[tid >> 6] = ss;
+        __syncthreads();
+        const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+        const float r = 1.f / sqrtf(tot / (float)CG + eps);
+        for (int c = tid; c < CG; c += 256) Elem<T>::st(row, c, Elem<T>::ld(row, c) * r * wr[c]);
+        __syncthreads();  // part[] is reused by the next pair
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ launchers
@@ -712,6 +743,20 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
 void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
                          int2 *ctab, int2 *sch, hipStream_t st) {
     k_varlen_table<<<1, 1024, 0, st>>>(cu, (int)NS, (int)total, (int)Q, (int)slots, ctab, sch);
+}
+
+void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t H, int64_t P,
+                       int64_t NG, int dtype, hipStream_t st) {
+    const int64_t pairs = ntok * NG;
+    if (pairs <= 0) return;
+    const unsigned blocks = (unsigned)(pairs < 16384 ? pairs : 16384);
+    const int CG = (int)(H / NG * P);
+    if (dtype == SSD_BF16)
+        k_gated_norm<bf16><<<blocks, 256, 0, st>>>(static_cast<bf16 *>(y), w, eps, pairs, H * P,
+                                                   CG, (int)NG);
+    else
+        k_gated_norm<float><<<blocks, 256, 0, st>>>(static_cast<float *>(y), w, eps, pairs, H * P,
+                                                    CG, (int)NG);
 }
 
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {

@@ -54,6 +54,12 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
 void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
                          int2 *ctab, int2 *sch, hipStream_t st);
 
+// Gated RMSNorm of finished outputs, in place: y is ntok rows of H*P values
+// (heads outer), each split into NG groups of whole heads; every group is
+// scaled by 1 / sqrt(mean square + eps) and then by w (per channel).
+void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t H, int64_t P,
+                       int64_t NG, int dtype, hipStream_t st);
+
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
 

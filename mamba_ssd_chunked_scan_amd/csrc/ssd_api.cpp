@@ -103,9 +103,24 @@ ssd_status read_edges(const ssd_edges *e, ssd::DtAct *act, const void **z) {
 
 bool act_active(const ssd::DtAct &a) { return a.bias || a.softplus || a.limit; }
 
-// The gradient tiles by 32 tokens whatever the forward chunk (its results do
-// not depend on the chunk beyond rounding): Acs, entering states, end-state
-// derivatives at that chunk.
+// ssd_edges' gated RMSNorm for nheads H and ngroups G (w NULL: no norm).
+struct NormEdge {
+    const float *w = nullptr;
+    float eps = 0.f;
+    int64_t groups = 0;
+};
+ssd_status read_norm(const ssd_edges *e, int64_t H, int64_t G, NormEdge *n) {
+    *n = NormEdge{};
+    if (!e || !e->norm_weight) return SSD_OK;
+    if (!(e->norm_eps >= 0.f)) return SSD_ERR_UNSUPPORTED;  // negative or NaN
+    const int64_t ng = e->norm_groups ? e->norm_groups : G;
+    if (ng < 1 || H % ng) return SSD_ERR_SHAPE;
+    n->w = e->norm_weight;
+    n->eps = e->norm_eps;
+    n->groups = ng;
+    return SSD_OK;
+}
+
 // The gradient's own chunking: 64 tokens on the matrix-core path (half the
 // state traffic of 32), 32 on the generic one.
 ScanShape bwd_shape(const ScanShape &s) {
@@ -203,7 +218,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 5; }
+int ssd_abi_version(void) { return 6; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -225,6 +240,9 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     const void *z;
     st = read_edges(edges, &act, &z);
     if (st != SSD_OK) return st;
+    NormEdge nm;
+    st = read_norm(edges, s.H, s.G, &nm);
+    if (st != SSD_OK) return st;
     if (s.B == 0) return SSD_OK;
     if (s.L == 0) {
         st = check_ptrs({}, {init_state, final_state});
@@ -234,13 +252,16 @@ ssd_status ssd_scan_fwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
                                      as_stream(stream));
         return after_launch();
     }
-    st = check_ptrs({x, dt, A, B, C, y}, {D, init_state, final_state, workspace, z, act.bias});
+    st = check_ptrs({x, dt, A, B, C, y},
+                    {D, init_state, final_state, workspace, z, act.bias, nm.w});
     if (st != SSD_OK) return st;
     const size_t need = workspace_bytes(s);
     if (ws_bytes < need) return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
+    hipStream_t hs = as_stream(stream);
     run_scan(s, act, z, x, dt, A, B, C, D, init_state, y, final_state,
-             static_cast<char *>(workspace), as_stream(stream));
+             static_cast<char *>(workspace), hs);
+    if (nm.w) ssd::launch_gated_norm(y, nm.w, nm.eps, s.B * s.L, s.H, s.P, nm.groups, s.dtype, hs);
     return after_launch();
 }
 
@@ -333,6 +354,9 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
     const void *z;
     st = read_edges(edges, &act, &z);
     if (st != SSD_OK) return st;
+    NormEdge nm;
+    st = read_norm(edges, s.H, s.G, &nm);
+    if (st != SSD_OK) return st;
     if (s.NS == 0) return SSD_OK;
     if (s.L == 0) {  // every sequence is empty
         st = check_ptrs({}, {init_states, final_states});
@@ -343,7 +367,7 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
         return after_launch();
     }
     st = check_ptrs({cu_seqlens, x, dt, A, B, C, y},
-                    {D, init_states, final_states, workspace, z, act.bias});
+                    {D, init_states, final_states, workspace, z, act.bias, nm.w});
     if (st != SSD_OK) return st;
     const size_t base = workspace_bytes(s);
     if (ws_bytes < base + varlen_table_bytes(s)) return SSD_ERR_WORKSPACE;
@@ -356,6 +380,7 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
     s.ctab = ctab;
     s.sch = sch;
     run_scan(s, act, z, x, dt, A, B, C, D, init_states, y, final_states, ws, hs);
+    if (nm.w) ssd::launch_gated_norm(y, nm.w, nm.eps, s.L, s.H, s.P, nm.groups, s.dtype, hs);
     return after_launch();
 }
 
@@ -380,12 +405,19 @@ ssd_status ssd_step_multi_ex(const ssd_step_desc *d, const ssd_edges *edges, int
     const void *z;
     st = read_edges(edges, &act, &z);
     if (st != SSD_OK) return st;
+    NormEdge nm;
+    st = read_norm(edges, d->nheads, d->ngroups, &nm);
+    if (st != SSD_OK) return st;
     if (d->batch == 0 || nsteps == 0) return SSD_OK;
     if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
-    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias});
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias, nm.w});
     if (st != SSD_OK) return st;
     StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
-    ssd::launch_step(s, nsteps, state, x, dt, A, B, C, D, y, act, z, as_stream(stream));
+    hipStream_t hs = as_stream(stream);
+    ssd::launch_step(s, nsteps, state, x, dt, A, B, C, D, y, act, z, hs);
+    if (nm.w)
+        ssd::launch_gated_norm(y, nm.w, nm.eps, d->batch * nsteps, d->nheads, d->headdim,
+                               nm.groups, d->dtype, hs);
     return after_launch();
 }
 
@@ -400,12 +432,19 @@ ssd_status ssd_step_ex(const ssd_step_desc *d, const ssd_edges *edges, float *st
     const void *z;
     st = read_edges(edges, &act, &z);
     if (st != SSD_OK) return st;
+    NormEdge nm;
+    st = read_norm(edges, d->nheads, d->ngroups, &nm);
+    if (st != SSD_OK) return st;
     if (d->batch == 0) return SSD_OK;
     if (d->batch > kMaxBlocks / d->nheads / d->headdim) return SSD_ERR_UNSUPPORTED;
-    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias});
+    st = check_ptrs({state, x, dt, A, B, C, y}, {D, z, act.bias, nm.w});
     if (st != SSD_OK) return st;
     StepShape s{d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->dtype};
-    ssd::launch_step(s, -1, state, x, dt, A, B, C, D, y, act, z, as_stream(stream));
+    hipStream_t hs = as_stream(stream);
+    ssd::launch_step(s, -1, state, x, dt, A, B, C, D, y, act, z, hs);
+    if (nm.w)
+        ssd::launch_gated_norm(y, nm.w, nm.eps, d->batch, d->nheads, d->headdim, nm.groups,
+                               d->dtype, hs);
     return after_launch();
 }
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 5
+    assert L.ssd_abi_version() == 6
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -226,6 +226,13 @@ def edges(**kw):
     (dict(dt_limit=1, dt_min=0.1, dt_max=0.01), UNSUP),       # empty clamp range
     (dict(dt_limit=1, dt_min=float("nan"), dt_max=1.0), UNSUP),
     (dict(z=P_MIS), ALIGN), (dict(dt_bias=P_MIS), ALIGN),
+    # gated RMSNorm: eps below zero or NaN, groups that do not divide the
+    # 8 heads, a misaligned weight
+    (dict(norm_weight=P16, norm_eps=-1e-5), UNSUP),
+    (dict(norm_weight=P16, norm_eps=float("nan")), UNSUP),
+    (dict(norm_weight=P16, norm_eps=1e-5, norm_groups=3), SHAPE),
+    (dict(norm_weight=P16, norm_eps=1e-5, norm_groups=-1), SHAPE),
+    (dict(norm_weight=P_MIS, norm_eps=1e-5), ALIGN),
 ])
 def test_edges_errors(L, kw, status):
     e = ctypes.byref(edges(**kw))
@@ -250,6 +257,9 @@ def test_edges_null_is_plain(L):
     assert L.ssd_step_multi_ex(ctypes.byref(sdesc()), None, -2, *([P16] * 8), None) == SHAPE
     # a valid clamp and softplus with an empty batch: nothing to do
     e = ctypes.byref(edges(dt_softplus=1, dt_limit=1, dt_min=1e-3, dt_max=0.1))
+    assert L.ssd_scan_fwd_ex(ctypes.byref(desc(batch=0)), e, *([None] * 10), 0, None) == OK
+    # without a weight the norm fields are not read
+    e = ctypes.byref(edges(norm_eps=-1.0, norm_groups=3))
     assert L.ssd_scan_fwd_ex(ctypes.byref(desc(batch=0)), e, *([None] * 10), 0, None) == OK
 
 

@@ -151,3 +151,94 @@ def test_step_edges(shape):
         yo.append(oe.gate(yt, inp["gate"][:, t]))
     assert rel_err(f64(y_chain), np.stack(yo, 1)) <= TOL[dtype]
     assert rel_err(f64(s_chain), s) <= TOL[dtype]
+
+
+def _norm_weight(H, P, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(1.0 + 0.5 * rng.standard_normal(H * P)).float()
+
+
+@pytest.mark.parametrize("gated", [True, False])
+@pytest.mark.parametrize("name,groups", [("mfma_q256_n128", 0), ("mfma_q64_n64", 2),
+                                         ("generic_f32", 1)])
+def test_scan_gated_rmsnorm(name, groups, gated):
+    """Every edge on plus the gated RMSNorm pass (norm_groups 0 = the B/C
+    groups, 2, and 1 = the whole row), against the oracle scan followed by
+    oracle.edges.gated_rmsnorm; and the norm without a gate."""
+    spec = SPECS[name]
+    announce(f"scan gated norm {name} groups {groups} gated {gated}")
+    inp = synth.scan_edge_inputs(spec)
+    H, P = spec.nheads, spec.headdim
+    w = _norm_weight(H, P, seed=41)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    y, fin = ssd.scan_fwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"], chunk=spec.chunk,
+                          init_state=d["init"], dt_bias=d["dt_bias"], dt_softplus=True,
+                          dt_limit=LIMIT, z=d["gate"] if gated else None,
+                          norm_weight=w.to(DEV), norm_eps=1e-5, norm_groups=groups)
+    torch.cuda.synchronize()
+    dt = oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT)
+    yo, fo = oracle.scan(inp["x"], dt, inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
+    ng = groups or spec.ngroups
+    yo = oe.gated_rmsnorm(yo, inp["gate"] if gated else None, w, 1e-5, ng)
+    tol = TOL[inp["x"].dtype]
+    assert rel_err(f64(y), yo) <= tol
+    assert rel_err(f64(fin), fo) <= tol
+
+
+def test_varlen_gated_rmsnorm():
+    """The norm pass over a ragged batch: every packed token normalised, as
+    for each sequence alone."""
+    announce("varlen gated norm")
+    lengths = [37, 0, 130, 64]
+    H, P, N, G = 4, 64, 64, 2
+    vin = synth.varlen_inputs(lengths, H, P, N, G, "bf16", seed=44)
+    d = {k: v.to(DEV) for k, v in vin.items()}
+    w = _norm_weight(H, P, seed=45)
+    y, fin = ssd.scan_fwd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["cu_seqlens"],
+                                 d["D"], chunk=64, init_states=d["init"], z=d["gate"],
+                                 norm_weight=w.to(DEV), norm_eps=1e-5)
+    torch.cuda.synchronize()
+    yo, fo = oracle.scan_varlen(vin["cu_seqlens"], vin["x"], vin["dt"], vin["A"], vin["B"],
+                                vin["C"], vin["D"], vin["init"])
+    yo = oe.gated_rmsnorm(yo, vin["gate"], w, 1e-5, G)
+    assert rel_err(f64(y), yo) <= TOL[torch.bfloat16]
+    assert rel_err(f64(fin), fo) <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 6, 8, 64, 128, 2, torch.bfloat16),
+    (3, 4, 4, 12, 32, 1, torch.float32),
+])
+def test_step_gated_rmsnorm(shape):
+    """Decode with the gate and the norm pass: ssd_step_ex against the oracle
+    step, and ssd_step_multi_ex bit for bit equal to the chained steps."""
+    Bt, T, H, P, N, G, dtype = shape
+    announce(f"step gated norm {shape}")
+    dn = "bf16" if dtype == torch.bfloat16 else "f32"
+    inp = synth.edge_decode_inputs(Bt, T, H, P, N, G, dn, seed=51 + T)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    w = _norm_weight(H, P, seed=52)
+    nkw = dict(dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=LIMIT, norm_weight=w.to(DEV),
+               norm_eps=1e-5)
+    s_chain = d["state"].clone()
+    ys = []
+    for t in range(T):
+        ys.append(ssd.step(s_chain, d["x"][:, t].clone(), d["dt_raw"][:, t].clone(), d["A"],
+                           d["B"][:, t].clone(), d["C"][:, t].clone(), d["D"],
+                           z=d["gate"][:, t].clone(), **nkw))
+    y_chain = torch.stack(ys, 1)
+    s_multi = d["state"].clone()
+    y_multi = ssd.step_multi(s_multi, d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["D"],
+                             z=d["gate"], **nkw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_multi, y_chain)
+    assert torch.equal(s_multi, s_chain)
+    dt = oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT)
+    s = inp["state"]
+    yo = []
+    for t in range(T):
+        yt, s = oracle.step(s, inp["x"][:, t], dt[:, t], inp["A"], inp["B"][:, t],
+                            inp["C"][:, t], inp["D"])
+        yo.append(oe.gated_rmsnorm(yt, inp["gate"][:, t], w, 1e-5, G))
+    assert rel_err(f64(y_chain), np.stack(yo, 1)) <= TOL[dtype]
+    assert rel_err(f64(s_chain), s) <= TOL[dtype]
