@@ -236,6 +236,15 @@ def main():
                       P_(ed["dt_raw"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
                       P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
     edges_ms = time_launches(torch, call_edges, max(10, args.steps))
+    # ... and with the gated RMSNorm pass over the output as well (norm groups
+    # = the B/C groups, a unit weight)
+    nw = torch.ones(H * P, dtype=torch.float32, device=dev)
+    edges_n = binding.Edges(ed["dt_bias"].data_ptr(), ed["gate"].data_ptr(), 1e-3, 0.1, 1, 1,
+                            nw.data_ptr(), 1e-5, 0)
+    call_norm = Lean(torch, lib.ssd_scan_fwd_ex, dref, ctypes.byref(edges_n), P_(d["x"]),
+                     P_(ed["dt_raw"]), P_(d["A"]), P_(d["B"]), P_(d["C"]), P_(d["D"]),
+                     P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
+    norm_ms = time_launches(torch, call_norm, max(10, args.steps))
 
     # ---- the gradient (ssd_scan_bwd) at this workload, and forward plus
     # backward at the 130M head shape with 512 tokens
@@ -445,6 +454,7 @@ def main():
                     "us_per_call_median": round(per_call[len(per_call) // 2] * 1e3, 2),
                     "us_per_call_min": round(per_call[0] * 1e3, 2),
                     "us_per_call_graph_fused_edges": round(edges_ms * 1e3, 2),
+                    "us_per_call_graph_fused_edges_gated_rmsnorm": round(norm_ms * 1e3, 2),
                     "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "hbm_GB_s_algorithmic": round(call_gbs, 1),
                     "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),

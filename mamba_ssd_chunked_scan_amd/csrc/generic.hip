@@ -11,6 +11,8 @@
 // plus the entering state.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "stages.hpp"
 #include "launch.hpp"
@@ -622,11 +624,44 @@ void launch_step_t(const StepShape &s, int64_t nsteps, float *state, const void 
 }
 
 // ------------------------------------------------------------- gated norm
-// One block per (token, norm group) pair (grid-stride over the pairs): the
-// group's CG channels are read twice, once for the sum of squares (a fixed
-// reduction order: lanes, then the four waves in turn) and once to scale and
-// store them, so the call needs no workspace and repeats bit for bit.
+// One block per (token, norm group) pair (grid-stride over the pairs), a
+// fixed reduction order (lanes, then the four waves in turn), no workspace:
+// the call repeats bit for bit.  kVec: the group's CG channels (a multiple of
+// 8, at most 8 * 256 * kVecK) are read once as 8-element vectors into
+// registers, summed, scaled and written back; otherwise they are read twice
+// element by element.
+constexpr int kVecK = 4;
+
 template <typename T>
+__device__ __forceinline__ void ld8(const T *p, float v[8]) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void st8(T *p, const float v[8]) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+template <typename T, bool kVec>
 __global__ void __launch_bounds__(256)
 k_gated_norm(T *__restrict__ y, const float *__restrict__ w, float eps, int64_t pairs,
              int64_t HP, int CG, int NG) {
@@ -638,16 +673,44 @@ k_gated_norm(T *__restrict__ y, const float *__restrict__ w, float eps, int64_t 
         T *row = y + tok * HP + (int64_t)k * CG;
         const float *wr = w + (int64_t)k * CG;
         float ss = 0.f;
-        for (int c = tid; c < CG; c += 256) {
-            const float v = Elem<T>::ld(row, c);
-            ss = fmaf(v, v, ss);
+        float v[kVec ? kVecK : 1][8];
+        if constexpr (kVec) {
+#pragma unroll
+            for (int u = 0; u < kVecK; ++u) {
+                const int c = 8 * (tid + 256 * u);
+                if (c < CG) {
+                    ld8(row + c, v[u]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss = fmaf(v[u][e], v[u][e], ss);
+                }
+            }
+        } else {
+            for (int c = tid; c < CG; c += 256) {
+                const float x = Elem<T>::ld(row, c);
+                ss = fmaf(x, x, ss);
+            }
         }
         ss = wave_sum_dpp(ss);
         if ((tid & 63) == 0) part[tid >> 6] = ss;
         __syncthreads();
         const float tot = ((part[0] + part[1]) + part[2]) + part[3];
         const float r = 1.f / sqrtf(tot / (float)CG + eps);
-        for (int c = tid; c < CG; c += 256) Elem<T>::st(row, c, Elem<T>::ld(row, c) * r * wr[c]);
+        if constexpr (kVec) {
+#pragma unroll
+            for (int u = 0; u < kVecK; ++u) {
+                const int c = 8 * (tid + 256 * u);
+                if (c < CG) {
+                    const float4 wa = *reinterpret_cast<const float4 *>(wr + c);
+                    const float4 wb = *reinterpret_cast<const float4 *>(wr + c + 4);
+                    const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[u][e] = v[u][e] * r * ww[e];
+                    st8(row + c, v[u]);
+                }
+            }
+        } else {
+            for (int c = tid; c < CG; c += 256) Elem<T>::st(row, c, Elem<T>::ld(row, c) * r * wr[c]);
+        }
         __syncthreads();  // part[] is reused by the next pair
     }
 }
@@ -751,12 +814,20 @@ void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t
     if (pairs <= 0) return;
     const unsigned blocks = (unsigned)(pairs < 16384 ? pairs : 16384);
     const int CG = (int)(H / NG * P);
-    if (dtype == SSD_BF16)
-        k_gated_norm<bf16><<<blocks, 256, 0, st>>>(static_cast<bf16 *>(y), w, eps, pairs, H * P,
-                                                   CG, (int)NG);
-    else
-        k_gated_norm<float><<<blocks, 256, 0, st>>>(static_cast<float *>(y), w, eps, pairs, H * P,
-                                                    CG, (int)NG);
+    // vectors: groups of whole 8-channel runs (P % 8 == 0 keeps every group
+    // and row start 16-byte aligned, y and w being so) that fit the registers
+    const bool vec = P % 8 == 0 && CG <= 8 * 256 * kVecK;
+#define SSD_NORM(T_, V_)                                                                     \
+    k_gated_norm<T_, V_><<<blocks, 256, 0, st>>>(static_cast<T_ *>(y), w, eps, pairs, H * P, \
+                                                 CG, (int)NG)
+    if (dtype == SSD_BF16) {
+        if (vec) SSD_NORM(bf16, true);
+        else SSD_NORM(bf16, false);
+    } else {
+        if (vec) SSD_NORM(float, true);
+        else SSD_NORM(float, false);
+    }
+#undef SSD_NORM
 }
 
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {
