@@ -184,3 +184,49 @@ def scan_vjp(x, dt, A, B, C, D=None, init=None, dy=None, dfinal=None, nthreads: 
     if rc != 0:
         raise ValueError(f"oracle vjp failed ({rc})")
     return out
+
+
+def scan_vjp_edges(x, dt_raw, A, B, C, D=None, init=None, dy=None, dfinal=None, dt_bias=None,
+                   dt_softplus: bool = False, dt_limit=None, z=None, nthreads: int = 0) -> dict:
+    """Gradients of J = sum(dy * y) + sum(dfinal * final_state) for the scan
+    with its fused edges: dt = edges.dt_activation(dt_raw, dt_bias,
+    dt_softplus, dt_limit) is the step size, and the output is gated,
+    y = scan(...) * silu(z), when z is given.  This is the chain rule over
+    scan_vjp:
+      - dy reaches the scan as dy * silu(z);
+      - dz = dy * y_scan * silu'(z), with silu'(z) = s (1 + z (1 - s)) and
+        s = sigmoid(z);
+      - ddt (with respect to dt_raw) = ddt_scan * d dt / d dt_raw, where the
+        derivative is sigmoid(dt_raw + bias) with softplus on (1 without),
+        times 0 where the clamp holds the value at a bound it was pushed past;
+      - ddt_bias = ddt summed over batch and tokens.
+    Returns scan_vjp's dict with ddt replaced, plus dz (z given) and ddt_bias
+    (dt_bias given)."""
+    from . import edges
+    dt = edges.dt_activation(dt_raw, dt_bias, dt_softplus, dt_limit)
+    dy = f64(dy)
+    if z is not None:
+        y, _ = scan(x, dt, A, B, C, D, init, nthreads=nthreads)
+        zz = f64(z)
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-zz))
+        dz = dy * y * (sg * (1.0 + zz * (1.0 - sg)))
+        dy_scan = dy * edges.silu(zz)
+    else:
+        dy_scan = dy
+    g = scan_vjp(x, dt, A, B, C, D, init, dy_scan, dfinal, nthreads=nthreads)
+    u = f64(dt_raw) + (0.0 if dt_bias is None else f64(dt_bias))
+    if dt_softplus:
+        with np.errstate(over="ignore"):
+            dact = 1.0 / (1.0 + np.exp(-u))
+    else:
+        dact = np.ones_like(u)
+    if dt_limit is not None:
+        pre = edges.softplus(u) if dt_softplus else u
+        dact = dact * ((pre >= float(dt_limit[0])) & (pre <= float(dt_limit[1])))
+    g["ddt"] = g["ddt"] * dact
+    if dt_bias is not None:
+        g["ddt_bias"] = g["ddt"].sum(axis=tuple(range(g["ddt"].ndim - 1)))
+    if z is not None:
+        g["dz"] = dz
+    return g

@@ -67,3 +67,54 @@ def test_vjp_is_deterministic():
     b = oracle.scan_vjp(**inp, dy=dy, dfinal=dfinal, nthreads=1)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def _edge_problem(Bt, L, H, P, N, G, seed):
+    spec = synth.custom_spec(Bt, L, H, P, N, G, chunk=16, dtype="f32", dt_rule="ranged",
+                             init="normal", seed=seed)
+    inp = {k: oracle.f64(v) for k, v in synth.scan_edge_inputs(spec).items()}
+    rng = np.random.default_rng(seed + 200)
+    return inp, rng.standard_normal(inp["x"].shape), rng.standard_normal(inp["init"].shape)
+
+
+def _J_edges(inp, dy, dfinal, limit, gated):
+    from oracle import edges
+    dt = edges.dt_activation(inp["dt_raw"], inp["dt_bias"], True, limit)
+    y, fin = oracle.scan(inp["x"], dt, inp["A"], inp["B"], inp["C"], inp["D"], inp["init"])
+    if gated:
+        y = edges.gate(y, inp["gate"])
+    return float(np.sum(dy * y) + np.sum(dfinal * fin))
+
+
+@pytest.mark.parametrize("limit", [None, (1e-3, 0.05)])
+@pytest.mark.parametrize("gated", [True, False])
+def test_vjp_edges_matches_finite_differences(limit, gated):
+    """The gradient through the fused edges (bias, softplus, optional clamp,
+    optional gate) against central differences of the composite forward, for
+    every input it adds or changes: dt_raw, dt_bias, z, and x and B through
+    the gated path.  The clamp's upper bound sits inside the range of the
+    synthetic dt, so some elements are held at it (gradient 0)."""
+    inp, dy, dfinal = _edge_problem(2, 11, 4, 3, 5, 2, seed=17)
+    g = oracle.scan_vjp_edges(inp["x"], inp["dt_raw"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["init"], dy=dy, dfinal=dfinal, dt_bias=inp["dt_bias"],
+                              dt_softplus=True, dt_limit=limit,
+                              z=inp["gate"] if gated else None)
+    if limit is not None:
+        from oracle import edges
+        pre = edges.softplus(inp["dt_raw"] + inp["dt_bias"])
+        assert np.any(pre > limit[1]) and np.any(g["ddt"] == 0.0)
+    rng = np.random.default_rng(9)
+    checks = [("dt_raw", "ddt"), ("dt_bias", "ddt_bias"), ("x", "dx"), ("B", "dB")]
+    if gated:
+        checks.append(("gate", "dz"))
+    for k, gk in checks:
+        V = rng.standard_normal(inp[k].shape)
+        eps = 1e-6 * max(1.0, float(np.max(np.abs(inp[k]))))
+        plus = dict(inp, **{k: inp[k] + eps * V})
+        minus = dict(inp, **{k: inp[k] - eps * V})
+        fd = (_J_edges(plus, dy, dfinal, limit, gated)
+              - _J_edges(minus, dy, dfinal, limit, gated)) / (2 * eps)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, fd, an)
+    if not gated:
+        assert "dz" not in g
