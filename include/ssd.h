@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -119,6 +119,8 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------- gradient */
+
+typedef struct ssd_edges ssd_edges; /* the fused edges, defined below */
 
 /* Bytes of device workspace ssd_scan_bwd needs for shape *d. */
 ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes);
@@ -153,6 +155,30 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                         float *dB, float *dC, float *dD, float *dinit, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* The gradient of ssd_scan_fwd_ex: the same J with y the edged output, with
+ * respect to every input of that call.  dt is the raw step size and ddt its
+ * gradient: the scan's step-size gradient times the activation's derivative
+ * (sigmoid(dt + bias) under softplus, 1 without, 0 where the clamp holds the
+ * value at a bound it was pushed past).  Further outputs:
+ *   dz        [batch, seqlen, nheads, headdim] dtype: the gate's gradient
+ *             dy * y * silu'(z), y the ungated output; required when
+ *             edges->z is set, else ignored
+ *   ddt_bias  [nheads] fp32, or NULL: the gradient of dt_bias, ddt summed
+ *             over batch and tokens in a fixed order
+ * The ungated output comes from the chunk-output stage run on the entering
+ * states the gradient forms anyway (no second forward pass).  edges with a
+ * norm_weight: SSD_ERR_UNSUPPORTED (the norm's gradient is not built).
+ * edges == NULL is ssd_scan_bwd.  Workspace: ssd_scan_bwd_ex_workspace_size
+ * bytes for the same edges. */
+ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edges *edges,
+                                          size_t *bytes);
+ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const void *x,
+                           const float *dt, const float *A, const void *B, const void *C,
+                           const float *D, const float *init_state, const void *dy,
+                           const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
+                           float *dC, float *dD, float *dinit, void *dz, float *ddt_bias,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------- fused scan edges */
 
 /* The elementwise steps that surround the scan in a Mamba block, fused into
@@ -184,7 +210,7 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
  * The step size the recurrence uses is the activated dt, everywhere dt enters
  * (decay and input weight).  A NULL ssd_edges pointer, or one with every field
  * zero / NULL, is the plain operation. */
-typedef struct ssd_edges {
+struct ssd_edges {
     const float *dt_bias;
     const void *z;
     float dt_min, dt_max;
@@ -193,7 +219,7 @@ typedef struct ssd_edges {
     const float *norm_weight;
     float norm_eps;
     int32_t norm_groups;
-} ssd_edges;
+};
 
 /* ssd_scan_fwd with the edges above (edges may be NULL).  dt here is the raw
  * pre-activation value; the first kernel to read it writes the activated dt

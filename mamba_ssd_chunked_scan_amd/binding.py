@@ -26,7 +26,8 @@ EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "s
            "ssd_step", "ssd_step_multi", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
            "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen",
-           "ssd_scan_bwd_workspace_size", "ssd_scan_bwd")
+           "ssd_scan_bwd_workspace_size", "ssd_scan_bwd", "ssd_scan_bwd_ex_workspace_size",
+           "ssd_scan_bwd_ex")
 
 
 class ScanDesc(ctypes.Structure):
@@ -70,7 +71,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 6  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 7  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -108,6 +109,11 @@ def lib() -> ctypes.CDLL:
         L.ssd_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
                                                   ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_bwd.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 17 + [ctypes.c_size_t, _P]
+        L.ssd_scan_bwd_ex_workspace_size.argtypes = [ctypes.POINTER(ScanDesc),
+                                                     ctypes.POINTER(Edges),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_bwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
+                                      + [_P] * 19 + [ctypes.c_size_t, _P])
         L.ssd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
@@ -267,11 +273,16 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
 
 
 def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: int = 256,
-             workspace=None) -> dict:
+             workspace=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None,
+             z=None) -> dict:
     """Gradient of :func:`scan_fwd`: derivatives of sum(dy * y) + sum(dfinal *
     final_state) with respect to x, dt, A, B, C, D and init_state.  Returns a
     dict: dx (x's dtype), ddt, dA, dB, dC (fp32), dD (None without D) and
-    dinit (None without init_state and dfinal)."""
+    dinit (None without init_state and dfinal).
+
+    With the fused edges of :func:`scan_fwd` (``dt_bias``, ``dt_softplus``,
+    ``dt_limit``, gate ``z``), dt is the raw step size and ddt its gradient;
+    the dict also holds ``dz`` (with z) and ``ddt_bias`` (with dt_bias)."""
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
     dev = x.device
     _need(dy, "dy", x.shape, x.dtype, dev)
@@ -280,9 +291,10 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: in
     if dfinal is not None:
         _need(dfinal, "dfinal", (Bt, H, P, N), torch.float32, dev)
     desc = _scan_desc(x, B, chunk)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z)
     n = ctypes.c_size_t(0)
-    _check("ssd_scan_bwd_workspace_size",
-           lib().ssd_scan_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    _check("ssd_scan_bwd_ex_workspace_size",
+           lib().ssd_scan_bwd_ex_workspace_size(ctypes.byref(desc), _eref(e), ctypes.byref(n)))
     if workspace is None:
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
     elif workspace.numel() < n.value or workspace.device != dev:
@@ -294,12 +306,18 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: in
            "dD": torch.empty(H, **f32) if D is not None else None,
            "dinit": (torch.empty((Bt, H, P, N), **f32)
                      if init_state is not None or dfinal is not None else None)}
-    st = lib().ssd_scan_bwd(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                            _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
-                            _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
-                            _ptr(out["dD"]), _ptr(out["dinit"]), _ptr(workspace),
-                            workspace.numel(), _stream(dev))
-    _check("ssd_scan_bwd", st)
+    if z is not None:
+        out["dz"] = torch.empty_like(x)
+    if dt_bias is not None:
+        out["ddt_bias"] = torch.empty(H, **f32)
+    st = lib().ssd_scan_bwd_ex(ctypes.byref(desc), _eref(e), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                               _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),
+                               _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+                               _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+                               _ptr(out["dinit"]), _ptr(out.get("dz")),
+                               _ptr(out.get("ddt_bias")), _ptr(workspace), workspace.numel(),
+                               _stream(dev))
+    _check("ssd_scan_bwd_ex", st)
     return out
 
 

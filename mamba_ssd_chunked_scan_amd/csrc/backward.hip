@@ -949,6 +949,82 @@ void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const
         hpb, (int)nslices, nblocks);
 }
 
+// ------------------------------------------------------- edges, backward
+// The output gate y_out = y * silu(z): dys = dy * z s and dz = dy * y * s
+// (1 + z (1 - s)) with s = sigmoid(z), 8 values per thread per step.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_gate_bwd(const T *__restrict__ dy, const T *__restrict__ y, const T *__restrict__ z,
+           T *__restrict__ dys, T *__restrict__ dz, int64_t n) {
+    const int64_t n8 = n / 8;
+    if (blockIdx.x == 0 && threadIdx.x < n - 8 * n8) {  // the last n % 8 values
+        const int64_t i = 8 * n8 + threadIdx.x;
+        const float g = Elem<T>::ld(dy, i), zz = Elem<T>::ld(z, i);
+        const float sg = sigmoid_f(zz);
+        Elem<T>::st(dys, i, g * (zz * sg));
+        Elem<T>::st(dz, i, g * Elem<T>::ld(y, i) * (sg * (1.f + zz * (1.f - sg))));
+    }
+    for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+        float g[8], yy[8], zz[8], a[8], b[8];
+        ld8(dy + 8 * i, g);
+        ld8(y + 8 * i, yy);
+        ld8(z + 8 * i, zz);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sg = sigmoid_f(zz[e]);
+            a[e] = g[e] * (zz[e] * sg);
+            b[e] = g[e] * yy[e] * (sg * (1.f + zz[e] * (1.f - sg)));
+        }
+        st8(dys + 8 * i, a);
+        st8(dz + 8 * i, b);
+    }
+}
+
+// The dt activation: block (h, y) turns rows [y R, (y+1) R) of head h's
+// ddt column into the raw-dt gradient (the activation's derivative: sigmoid
+// of the biased value under softplus, 1 without, 0 where the clamp holds a
+// bound it was pushed past) and writes its sum to part[h][y].
+constexpr int kDtRows = 4096;
+__global__ void __launch_bounds__(256)
+k_dt_act_bwd(float *__restrict__ ddt, const float *__restrict__ dt_raw, DtAct act,
+             float *__restrict__ part, int64_t rows, int H) {
+    __shared__ float red[4];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * kDtRows;
+    const int64_t r1 = r0 + kDtRows < rows ? r0 + kDtRows : rows;
+    const float bias = act.bias ? act.bias[h] : 0.f;
+    float acc = 0.f;
+    for (int64_t r = r0 + tid; r < r1; r += 256) {
+        const int64_t i = r * H + h;
+        const float u = dt_raw[i] + bias;
+        float d = 1.f, pre = u;
+        if (act.softplus) {
+            d = sigmoid_f(u);
+            pre = softplus_f(u);
+        }
+        if (act.limit && (pre < act.lo || pre > act.hi)) d = 0.f;
+        const float v = ddt[i] * d;
+        ddt[i] = v;
+        acc += v;
+    }
+    if (part) {
+        acc = wave_sum_dpp(acc);
+        if ((tid & 63) == 0) red[tid >> 6] = acc;
+        __syncthreads();
+        if (tid == 0) part[(int64_t)h * gridDim.y + blockIdx.y] = ((red[0] + red[1]) + red[2]) + red[3];
+    }
+}
+
+// dbias[h] = the parts of head h summed in order.
+__global__ void k_sum_parts(const float *__restrict__ part, int64_t nparts,
+                            float *__restrict__ dbias, int H) {
+    const int h = blockIdx.x * blockDim.x + threadIdx.x;
+    if (h >= H) return;
+    float s = 0.f;
+    for (int64_t k = 0; k < nparts; ++k) s += part[h * nparts + k];
+    dbias[h] = s;
+}
+
 // Rows of E / H per slice so that the whole block fits the 160 KB of LDS
 // (at most 8 KB of slice, so two float4 per thread carry it; at least one row).
 int bwd_slice_rows(int P, int N, size_t *lds_bytes) {
@@ -1009,6 +1085,31 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
         SSD_BWD_KI(float);
 #undef SSD_BWD_KI
 #undef SSD_BWD
+}
+
+void launch_gate_bwd(const void *dy, const void *y, const void *z, void *dys, void *dz,
+                     int64_t n, int dtype, hipStream_t st) {
+    if (n <= 0) return;
+    const int64_t want = (n / 8 + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 1 ? 1 : (want < 65536 ? want : 65536));
+    if (dtype == SSD_BF16)
+        k_gate_bwd<bf16><<<blocks, 256, 0, st>>>((const bf16 *)dy, (const bf16 *)y, (const bf16 *)z,
+                                                 (bf16 *)dys, (bf16 *)dz, n);
+    else
+        k_gate_bwd<float><<<blocks, 256, 0, st>>>((const float *)dy, (const float *)y,
+                                                  (const float *)z, (float *)dys, (float *)dz, n);
+}
+
+int64_t dt_bias_parts(int64_t rows) { return (rows + kDtRows - 1) / kDtRows; }
+
+void launch_dt_act_bwd(float *ddt, const float *dt_raw, const DtAct &act, int64_t rows,
+                       int64_t H, float *part, float *dbias, hipStream_t st) {
+    const int64_t np = dt_bias_parts(rows);
+    if (np <= 0) return;
+    k_dt_act_bwd<<<dim3((unsigned)H, (unsigned)np), 256, 0, st>>>(ddt, dt_raw, act,
+                                                                  dbias ? part : nullptr, rows,
+                                                                  (int)H);
+    if (dbias) k_sum_parts<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(part, np, dbias, (int)H);
 }
 
 }  // namespace ssd

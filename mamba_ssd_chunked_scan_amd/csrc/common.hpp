@@ -75,6 +75,42 @@ __device__ __forceinline__ float silu_f(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// sigmoid(z) = 1 / (1 + e^-z) with the same base-2 exponential and
+// reciprocal as silu_f (the gate's derivative pairs with the gate itself).
+__device__ __forceinline__ float sigmoid_f(float z) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
+// 8 consecutive values of a storage type as fp32 (16 bytes of bf16 or 32 of
+// fp32; the address aligned to that) and back.
+template <typename T>
+__device__ __forceinline__ void ld8(const T *p, float v[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+template <typename T>
+__device__ __forceinline__ void st8(T *p, const float v[8]) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
 // First token (within its batch row) and length of chunk slot c.  Fixed
 // chunking: t0 = c*Q, q = min(Q, L - t0).  Variable-length batches: the slot's
 // entry of the chunk table (q = 0 for an unused slot).

@@ -632,35 +632,6 @@ void launch_step_t(const StepShape &s, int64_t nsteps, float *state, const void 
 // element by element.
 constexpr int kVecK = 4;
 
-template <typename T>
-__device__ __forceinline__ void ld8(const T *p, float v[8]) {
-    if constexpr (std::is_same<T, bf16>::value) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(p);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(w[k] << 16);
-            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-    } else {
-        const float4 a = *reinterpret_cast<const float4 *>(p);
-        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void st8(T *p, const float v[8]) {
-    if constexpr (std::is_same<T, bf16>::value) {
-        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
-    } else {
-        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    }
-}
-
 template <typename T, bool kVec>
 __global__ void __launch_bounds__(256)
 k_gated_norm(T *__restrict__ y, const float *__restrict__ w, float eps, int64_t pairs,

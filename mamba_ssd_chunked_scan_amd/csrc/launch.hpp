@@ -90,6 +90,18 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
 // Whether the gradient takes the matrix-core path (bf16, headdim 64, d_state
 // 64 or 128, fixed length); it then runs at 64-token chunks, else at 32.
 bool bwd_mfma_ok(const ScanShape &s);
+// Gradient through the output gate y_out = y * silu(z), elementwise over n
+// values of x's layout: dys = dy * silu(z), dz = dy * y * silu'(z).
+void launch_gate_bwd(const void *dy, const void *y, const void *z, void *dys, void *dz,
+                     int64_t n, int dtype, hipStream_t st);
+// Gradient through the dt activation, in place: ddt [rows][H] with respect
+// to the activated dt becomes the gradient with respect to the raw dt; when
+// dbias is non-null it gets the per-head sums over the rows (fixed order,
+// through part: H * dt_bias_parts(rows) floats of workspace).
+int64_t dt_bias_parts(int64_t rows);
+void launch_dt_act_bwd(float *ddt, const float *dt_raw, const DtAct &act, int64_t rows,
+                       int64_t H, float *part, float *dbias, hipStream_t st);
+
 // The gradient's 64-token chunk states (and their adjoint, with x = dy and
 // B = C) on the matrix cores, for bwd_mfma_ok shapes.
 bool bwd_states_mfma_ok(const ScanShape &s);

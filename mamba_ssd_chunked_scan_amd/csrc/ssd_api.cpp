@@ -218,7 +218,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 6; }
+int ssd_abi_version(void) { return 7; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -274,12 +274,40 @@ ssd_status check_bwd(const ssd_scan_desc *d, ScanShape *s) {
     return SSD_OK;
 }
 
+// Workspace of ssd_scan_bwd_ex beyond the plain gradient's: the activated dt
+// (dt activation on); the ungated output, the gate's dy and the chunk-output
+// stage's workspace (gate on); the partial sums of ddt_bias (any edges).
+size_t bwd_edges_bytes(const ScanShape &s, bool act, bool gate, bool dbias) {
+    size_t n = 0;
+    if (act) n += dt_eff_bytes(s);
+    if (gate) {
+        const size_t elem = s.dtype == SSD_BF16 ? 2 : 4;
+        n += 2 * round_up((size_t)(s.B * s.L * s.H * s.P) * elem);
+        n += round_up(ssd::chunk_scan_ws_bytes(bwd_shape(s)));
+    }
+    if (dbias) n += round_up((size_t)(s.H * ssd::dt_bias_parts(s.B * s.L)) * 4);
+    return n;
+}
+
 ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
+    return ssd_scan_bwd_ex_workspace_size(d, nullptr, bytes);
+}
+
+ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edges *edges,
+                                          size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
     ScanShape s;
     ssd_status st = check_bwd(d, &s);
     if (st != SSD_OK) return st;
-    *bytes = bwd_workspace_bytes(s);
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
+    if (st != SSD_OK) return st;
+    if (edges && edges->norm_weight) return SSD_ERR_UNSUPPORTED;
+    *bytes = (s.B == 0 || s.L == 0)
+                 ? 0
+                 : bwd_workspace_bytes(s) +
+                       bwd_edges_bytes(s, act_active(act), z != nullptr, edges != nullptr);
     return SSD_OK;
 }
 
@@ -288,29 +316,65 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                         const void *dy, const float *dfinal, void *dx, float *ddt, float *dA,
                         float *dB, float *dC, float *dD, float *dinit, void *workspace,
                         size_t ws_bytes, void *stream) {
+    return ssd_scan_bwd_ex(d, nullptr, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA,
+                           dB, dC, dD, dinit, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const void *x,
+                           const float *dt, const float *A, const void *B, const void *C,
+                           const float *D, const float *init_state, const void *dy,
+                           const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
+                           float *dC, float *dD, float *dinit, void *dz, float *ddt_bias,
+                           void *workspace, size_t ws_bytes, void *stream) {
     ScanShape s;
     ssd_status st = check_bwd(d, &s);
     if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    st = read_edges(edges, &act, &z);
+    if (st != SSD_OK) return st;
+    if (edges && edges->norm_weight) return SSD_ERR_UNSUPPORTED;  // the norm's gradient
+    if (!edges) ddt_bias = nullptr;
     hipStream_t hs = as_stream(stream);
-    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = 0, dinit = dfinal
-        st = check_ptrs({dA}, {dD, dinit, dfinal});
+    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = ddt_bias = 0, dinit = dfinal
+        st = check_ptrs({dA}, {dD, dinit, dfinal, ddt_bias});
         if (st != SSD_OK) return st;
         ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
         if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
+        if (ddt_bias) ssd::launch_copy_or_zero(ddt_bias, nullptr, s.H, hs);
         if (dinit) ssd::launch_copy_or_zero(dinit, dfinal, s.B * s.H * s.P * s.N, hs);
         return after_launch();
     }
+    const bool gate = z != nullptr, actv = act_active(act);
+    if (gate && !dz) return SSD_ERR_NULL_PTR;
     st = check_ptrs({x, dt, A, B, C, dy, dx, ddt, dA, dB, dC},
-                    {D, init_state, dfinal, dD, dinit, workspace});
+                    {D, init_state, dfinal, dD, dinit, workspace, z, dz, act.bias, ddt_bias});
     if (st != SSD_OK) return st;
-    const size_t need = bwd_workspace_bytes(s);
-    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    const size_t base = bwd_workspace_bytes(s);
+    if (ws_bytes < base + bwd_edges_bytes(s, actv, gate, edges != nullptr))
+        return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
     const ScanShape b = bwd_shape(s);
     char *ws = static_cast<char *>(workspace);
     float *Acs = reinterpret_cast<float *>(ws);
     float *Hst = reinterpret_cast<float *>(ws + acs_bytes(b));
     float *Est = reinterpret_cast<float *>(ws + acs_bytes(b) + states_bytes(b));
+    char *extra = ws + base;
+    float *dt_eff = nullptr;
+    if (actv) {
+        dt_eff = reinterpret_cast<float *>(extra);
+        extra += dt_eff_bytes(s);
+    }
+    void *yun = nullptr, *dys = nullptr, *cbws = nullptr;
+    const int64_t nel = s.B * s.L * s.H * s.P;
+    if (gate) {
+        const size_t eb = round_up((size_t)nel * (s.dtype == SSD_BF16 ? 2 : 4));
+        yun = extra;
+        dys = extra + eb;
+        cbws = extra + 2 * eb;
+        extra += 2 * eb + round_up(ssd::chunk_scan_ws_bytes(b));
+    }
+    float *part = ddt_bias ? reinterpret_cast<float *>(extra) : nullptr;
     // outputs accumulated with atomics start from zero (a fill kernel, so the
     // call can be captured in a HIP graph)
     const int64_t bcn = s.B * s.L * s.G * s.N;
@@ -318,18 +382,31 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
     ssd::launch_copy_or_zero(dC, nullptr, bcn, hs);
     ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
     if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
-    // the forward's entering states at the gradient's chunks
+    // the forward's Acs (and the activated dt) and entering states at the
+    // gradient's chunks
     const bool mm = ssd::bwd_states_mfma_ok(b);
-    ssd::launch_chunk_cumsum(b, dt, A, Acs, hs);
-    if (mm) ssd::launch_bwd_states_mfma(b, x, B, dt, Acs, Hst, false, hs);
-    else ssd::launch_chunk_state(b, x, B, dt, Acs, Hst, hs);
+    ssd::launch_chunk_cumsum(b, dt, A, Acs, hs, act, dt_eff);
+    const float *dtu = dt_eff ? dt_eff : dt;
+    if (mm) ssd::launch_bwd_states_mfma(b, x, B, dtu, Acs, Hst, false, hs);
+    else ssd::launch_chunk_state(b, x, B, dtu, Acs, Hst, hs);
     ssd::launch_state_passing(b, Hst, Acs, init_state, nullptr, hs);
+    // gate: the ungated output from the chunk-output stage on those states,
+    // then dy * silu(z) for the scan and dz
+    const void *dyu = dy;
+    if (gate) {
+        ssd::launch_chunk_cb(b, B, C, cbws, hs);
+        ssd::launch_chunk_scan(b, x, dtu, B, C, D, Acs, Hst, cbws, yun, hs);
+        ssd::launch_gate_bwd(dy, yun, z, dys, dz, nel, s.dtype, hs);
+        dyu = dys;
+    }
     // derivatives with respect to every chunk's end state, and the initial state's
-    if (mm) ssd::launch_bwd_states_mfma(b, dy, C, nullptr, Acs, Est, true, hs);
-    else ssd::launch_chunk_dstate(b, dy, C, Acs, Est, hs);
+    if (mm) ssd::launch_bwd_states_mfma(b, dyu, C, nullptr, Acs, Est, true, hs);
+    else ssd::launch_chunk_dstate(b, dyu, C, Acs, Est, hs);
     ssd::launch_state_passing_rev(b, Est, Acs, dfinal, dinit, hs);
     // per-chunk gradients
-    ssd::launch_chunk_bwd(b, x, dt, A, B, C, D, Acs, Hst, Est, dy, dx, ddt, dB, dC, dA, dD, hs);
+    ssd::launch_chunk_bwd(b, x, dtu, A, B, C, D, Acs, Hst, Est, dyu, dx, ddt, dB, dC, dA, dD, hs);
+    // through the dt activation, and the bias's gradient
+    if (actv || ddt_bias) ssd::launch_dt_act_bwd(ddt, dt, act, s.B * s.L, s.H, part, ddt_bias, hs);
     return after_launch();
 }
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 6
+    assert L.ssd_abi_version() == 7
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -409,3 +409,39 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libssd.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         binding.lib()
+
+
+def test_bwd_ex_workspace_and_errors(L):
+    """ssd_scan_bwd_ex: NULL edges is ssd_scan_bwd (same workspace); a dt
+    activation adds the activated dt; a gate adds the ungated output, the
+    gated dy and the chunk-output stage's workspace; the norm's gradient is
+    not built; a gate needs dz; dz and ddt_bias are alignment-checked."""
+    d = desc()   # batch 1, seqlen 512, 8 heads, headdim 64, dstate 128, bf16
+    n0, n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.ssd_scan_bwd_workspace_size(ctypes.byref(d), ctypes.byref(n0)) == OK
+    assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), None, ctypes.byref(n1)) == OK
+    assert n0.value == n1.value
+    ea = edges(dt_bias=P16, dt_softplus=1)
+    assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(ea),
+                                            ctypes.byref(n1)) == OK
+    parts = r256(8 * 1 * 4)                       # 8 heads x one 4096-row part
+    assert n1.value == n0.value + r256(512 * 8 * 4) + parts
+    eg = edges(dt_bias=P16, dt_softplus=1, z=P16)
+    assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(eg),
+                                            ctypes.byref(n2)) == OK
+    assert n2.value > n1.value + 2 * r256(512 * 8 * 64 * 2)
+    en = edges(norm_weight=P16, norm_eps=1e-5)
+    assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(en),
+                                            ctypes.byref(n1)) == UNSUP
+    need = n2.value
+    args = [P16] * 16  # x dt A B C D init dy dfinal dx ddt dA dB dC dD dinit
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(en), *args, P16, P16, P16, need,
+                             None) == UNSUP
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, None, P16, P16, need,
+                             None) == NULL                      # gate without dz
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P_MIS, P16, P16, need,
+                             None) == ALIGN
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P16, P_MIS, P16, need,
+                             None) == ALIGN
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P16, P16, P16, need - 1,
+                             None) == WS
