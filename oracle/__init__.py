@@ -187,7 +187,8 @@ def scan_vjp(x, dt, A, B, C, D=None, init=None, dy=None, dfinal=None, nthreads: 
 
 
 def scan_vjp_edges(x, dt_raw, A, B, C, D=None, init=None, dy=None, dfinal=None, dt_bias=None,
-                   dt_softplus: bool = False, dt_limit=None, z=None, nthreads: int = 0) -> dict:
+                   dt_softplus: bool = False, dt_limit=None, z=None, norm_weight=None,
+                   norm_eps: float = 1e-5, norm_groups: int = 1, nthreads: int = 0) -> dict:
     """Gradients of J = sum(dy * y) + sum(dfinal * final_state) for the scan
     with its fused edges: dt = edges.dt_activation(dt_raw, dt_bias,
     dt_softplus, dt_limit) is the step size, and the output is gated,
@@ -200,13 +201,34 @@ def scan_vjp_edges(x, dt_raw, A, B, C, D=None, init=None, dy=None, dfinal=None, 
         derivative is sigmoid(dt_raw + bias) with softplus on (1 without),
         times 0 where the clamp holds the value at a bound it was pushed past;
       - ddt_bias = ddt summed over batch and tokens.
-    Returns scan_vjp's dict with ddt replaced, plus dz (z given) and ddt_bias
-    (dt_bias given)."""
+    With ``norm_weight``, the output is edges.gated_rmsnorm(y, z, norm_weight,
+    norm_eps, norm_groups) instead: per token and group, with v the gated
+    output, r = 1 / sqrt(mean(v^2) + eps) and S = sum(dy w v) over the group's
+    CG channels, the gradient reaching v is dv = r (w dy - v r^2 S / CG), and
+    dnorm_weight = dy v r summed over the leading axes; the gate's rule above
+    then applies with dv in place of dy.
+    Returns scan_vjp's dict with ddt replaced, plus dz (z given), ddt_bias
+    (dt_bias given) and dnorm_weight (norm_weight given)."""
     from . import edges
     dt = edges.dt_activation(dt_raw, dt_bias, dt_softplus, dt_limit)
     dy = f64(dy)
-    if z is not None:
+    extra = {}
+    if z is not None or norm_weight is not None:
         y, _ = scan(x, dt, A, B, C, D, init, nthreads=nthreads)
+    if norm_weight is not None:
+        v = y if z is None else edges.gate(y, z)
+        shape = v.shape
+        H, P = shape[-2], shape[-1]
+        CG = (H // norm_groups) * P
+        gshape = shape[:-2] + (norm_groups, CG)
+        vg, dg = v.reshape(gshape), dy.reshape(gshape)
+        wg = f64(norm_weight).reshape(norm_groups, CG)
+        r = 1.0 / np.sqrt(np.mean(vg * vg, axis=-1, keepdims=True) + float(norm_eps))
+        S = np.sum(dg * wg * vg, axis=-1, keepdims=True)
+        dv = r * (wg * dg - vg * r * r * S / CG)
+        extra["dnorm_weight"] = np.sum(dg * vg * r, axis=tuple(range(len(gshape) - 2))).reshape(-1)
+        dy = dv.reshape(shape)
+    if z is not None:
         zz = f64(z)
         with np.errstate(over="ignore"):
             sg = 1.0 / (1.0 + np.exp(-zz))
@@ -229,4 +251,5 @@ def scan_vjp_edges(x, dt_raw, A, B, C, D=None, init=None, dy=None, dfinal=None, 
         g["ddt_bias"] = g["ddt"].sum(axis=tuple(range(g["ddt"].ndim - 1)))
     if z is not None:
         g["dz"] = dz
+    g.update(extra)
     return g

@@ -118,3 +118,36 @@ def test_vjp_edges_matches_finite_differences(limit, gated):
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, fd, an)
     if not gated:
         assert "dz" not in g
+
+
+
+@pytest.mark.parametrize("gated,groups", [(True, 2), (False, 1)])
+def test_vjp_edges_norm_matches_finite_differences(gated, groups):
+    """The gradient through the gated RMSNorm as well: dnorm_weight, z, dt_raw
+    and x against central differences of the composite forward
+    (edges.gated_rmsnorm after the gated scan)."""
+    from oracle import edges
+    inp, dy, dfinal = _edge_problem(2, 9, 4, 3, 5, 2, seed=23)
+    rng = np.random.default_rng(24)
+    inp["normw"] = 1.0 + 0.5 * rng.standard_normal(4 * 3)
+    eps = 1e-3
+
+    def J(q):
+        dt = edges.dt_activation(q["dt_raw"], q["dt_bias"], True, None)
+        y, fin = oracle.scan(q["x"], dt, q["A"], q["B"], q["C"], q["D"], q["init"])
+        y = edges.gated_rmsnorm(y, q["gate"] if gated else None, q["normw"], eps, groups)
+        return float(np.sum(dy * y) + np.sum(dfinal * fin))
+
+    g = oracle.scan_vjp_edges(inp["x"], inp["dt_raw"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["init"], dy=dy, dfinal=dfinal, dt_bias=inp["dt_bias"],
+                              dt_softplus=True, z=inp["gate"] if gated else None,
+                              norm_weight=inp["normw"], norm_eps=eps, norm_groups=groups)
+    checks = [("normw", "dnorm_weight"), ("dt_raw", "ddt"), ("x", "dx"), ("dt_bias", "ddt_bias")]
+    if gated:
+        checks.append(("gate", "dz"))
+    for k, gk in checks:
+        V = rng.standard_normal(inp[k].shape)
+        h = 1e-6 * max(1.0, float(np.max(np.abs(inp[k]))))
+        fd = (J(dict(inp, **{k: inp[k] + h * V})) - J(dict(inp, **{k: inp[k] - h * V}))) / (2 * h)
+        an = float(np.sum(g[gk] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, fd, an)
