@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 7. */
+/* ABI version of this header: 8. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -165,9 +165,14 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
  *             edges->z is set, else ignored
  *   ddt_bias  [nheads] fp32, or NULL: the gradient of dt_bias, ddt summed
  *             over batch and tokens in a fixed order
+ *   dnorm_weight [nheads * headdim] fp32, or NULL: the gradient of the gated
+ *             RMSNorm's weight (edges->norm_weight set), summed over tokens
+ *             in a fixed order; the norm's gradient also flows into dz and
+ *             everything before it.  It needs headdim a multiple of 8 and
+ *             norm groups of at most 8192 channels (SSD_ERR_UNSUPPORTED
+ *             otherwise).
  * The ungated output comes from the chunk-output stage run on the entering
- * states the gradient forms anyway (no second forward pass).  edges with a
- * norm_weight: SSD_ERR_UNSUPPORTED (the norm's gradient is not built).
+ * states the gradient forms anyway (no second forward pass).
  * edges == NULL is ssd_scan_bwd.  Workspace: ssd_scan_bwd_ex_workspace_size
  * bytes for the same edges. */
 ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edges *edges,
@@ -177,7 +182,8 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
                            const float *D, const float *init_state, const void *dy,
                            const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
                            float *dC, float *dD, float *dinit, void *dz, float *ddt_bias,
-                           void *workspace, size_t workspace_bytes, void *stream);
+                           float *dnorm_weight, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* ------------------------------------------------------- fused scan edges */
 

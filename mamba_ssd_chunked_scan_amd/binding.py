@@ -71,7 +71,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 7  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 8  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -113,7 +113,7 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.POINTER(Edges),
                                                      ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_bwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
-                                      + [_P] * 19 + [ctypes.c_size_t, _P])
+                                      + [_P] * 20 + [ctypes.c_size_t, _P])
         L.ssd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
@@ -274,15 +274,16 @@ def scan_fwd(x, dt, A, B, C, D=None, chunk: int = 256, init_state=None,
 
 def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: int = 256,
              workspace=None, dt_bias=None, dt_softplus: bool = False, dt_limit=None,
-             z=None) -> dict:
+             z=None, norm_weight=None, norm_eps: float = 1e-5, norm_groups: int = 0) -> dict:
     """Gradient of :func:`scan_fwd`: derivatives of sum(dy * y) + sum(dfinal *
     final_state) with respect to x, dt, A, B, C, D and init_state.  Returns a
     dict: dx (x's dtype), ddt, dA, dB, dC (fp32), dD (None without D) and
     dinit (None without init_state and dfinal).
 
     With the fused edges of :func:`scan_fwd` (``dt_bias``, ``dt_softplus``,
-    ``dt_limit``, gate ``z``), dt is the raw step size and ddt its gradient;
-    the dict also holds ``dz`` (with z) and ``ddt_bias`` (with dt_bias)."""
+    ``dt_limit``, gate ``z``, gated RMSNorm ``norm_weight``), dt is the raw
+    step size and ddt its gradient; the dict also holds ``dz`` (with z),
+    ``ddt_bias`` (with dt_bias) and ``dnorm_weight`` (with norm_weight)."""
     Bt, L, H, P, N, G = _check_scan_inputs(x, dt, A, B, C, D)
     dev = x.device
     _need(dy, "dy", x.shape, x.dtype, dev)
@@ -291,7 +292,7 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: in
     if dfinal is not None:
         _need(dfinal, "dfinal", (Bt, H, P, N), torch.float32, dev)
     desc = _scan_desc(x, B, chunk)
-    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
     n = ctypes.c_size_t(0)
     _check("ssd_scan_bwd_ex_workspace_size",
            lib().ssd_scan_bwd_ex_workspace_size(ctypes.byref(desc), _eref(e), ctypes.byref(n)))
@@ -310,12 +311,15 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: in
         out["dz"] = torch.empty_like(x)
     if dt_bias is not None:
         out["ddt_bias"] = torch.empty(H, **f32)
+    if norm_weight is not None:
+        out["dnorm_weight"] = torch.empty(H * P, **f32)
     st = lib().ssd_scan_bwd_ex(ctypes.byref(desc), _eref(e), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                _ptr(C), _ptr(D), _ptr(init_state), _ptr(dy), _ptr(dfinal),
                                _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
                                _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
                                _ptr(out["dinit"]), _ptr(out.get("dz")),
-                               _ptr(out.get("ddt_bias")), _ptr(workspace), workspace.numel(),
+                               _ptr(out.get("ddt_bias")), _ptr(out.get("dnorm_weight")),
+                               _ptr(workspace), workspace.numel(),
                                _stream(dev))
     _check("ssd_scan_bwd_ex", st)
     return out

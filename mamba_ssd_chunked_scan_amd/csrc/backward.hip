@@ -1015,6 +1015,118 @@ k_dt_act_bwd(float *__restrict__ ddt, const float *__restrict__ dt_raw, DtAct ac
     }
 }
 
+// The gated RMSNorm with the gate under it, backward.  Block (range, k)
+// takes tokens [range kNormTok, +kNormTok) of norm group k: CG channels as
+// 8-value vectors, vector u of thread t at channel 8 (t + 256 u).  Per token,
+// with v the gated output (v = y without a gate), r = 1 / sqrt(mean(v^2) +
+// eps) and S = sum(dout w v) (two block sums, fixed order):
+//   dv = r (w dout - v r^2 S / CG),  dys = dv silu(z),  dz = dv y silu'(z);
+// the thread's sum over its tokens of dout v r goes to part[range][k CG + c].
+constexpr int kNormTok = 16;
+constexpr int kNormVec = 4;  // vectors per thread: CG <= 8 * 256 * kNormVec
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_norm_gate_bwd(const T *__restrict__ dout, const T *__restrict__ y, const T *__restrict__ z,
+                const float *__restrict__ w, float eps, T *__restrict__ dys, T *__restrict__ dz,
+                float *__restrict__ part, int64_t ntok, int64_t HP, int CG) {
+    __shared__ float red[2][4];
+    const int tid = threadIdx.x, k = blockIdx.y;
+    const int64_t t0 = (int64_t)blockIdx.x * kNormTok;
+    const int64_t t1 = t0 + kNormTok < ntok ? t0 + kNormTok : ntok;
+    float dw[kNormVec][8];
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dw[u][e] = 0.f;
+    // v = y silu(z) (or y) of vector u at offset o
+    auto gated = [&](int64_t o, float yv[8], float zv[8], float v[8]) __attribute__((always_inline)) {
+        ld8(y + o, yv);
+        if (z) {
+            ld8(z + o, zv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = yv[e] * (zv[e] * sigmoid_f(zv[e]));
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = yv[e];
+        }
+    };
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t base = t * HP + (int64_t)k * CG;
+        float ss = 0.f, sd = 0.f;
+#pragma unroll
+        for (int u = 0; u < kNormVec; ++u) {
+            const int c = 8 * (tid + 256 * u);
+            if (c < CG) {
+                float yv[8], zv[8], v[8], g[8], ww[8];
+                gated(base + c, yv, zv, v);
+                ld8(dout + base + c, g);
+                ld8(w + (int64_t)k * CG + c, ww);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ss = fmaf(v[e], v[e], ss);
+                    sd = fmaf(g[e] * ww[e], v[e], sd);
+                }
+            }
+        }
+        ss = wave_sum_dpp(ss);
+        sd = wave_sum_dpp(sd);
+        if ((tid & 63) == 0) {
+            red[0][tid >> 6] = ss;
+            red[1][tid >> 6] = sd;
+        }
+        __syncthreads();
+        const float sst = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+        const float sdt = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+        const float r = 1.f / sqrtf(sst / (float)CG + eps);
+        const float a = r * r * sdt / (float)CG;
+#pragma unroll
+        for (int u = 0; u < kNormVec; ++u) {
+            const int c = 8 * (tid + 256 * u);
+            if (c < CG) {
+                float yv[8], zv[8], v[8], g[8], ww[8], o1[8], o2[8];
+                gated(base + c, yv, zv, v);
+                ld8(dout + base + c, g);
+                ld8(w + (int64_t)k * CG + c, ww);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float dv = r * (ww[e] * g[e] - v[e] * a);
+                    dw[u][e] = fmaf(g[e] * v[e], r, dw[u][e]);
+                    if (z) {
+                        const float sg = sigmoid_f(zv[e]);
+                        o1[e] = dv * (zv[e] * sg);
+                        o2[e] = dv * yv[e] * (sg * (1.f + zv[e] * (1.f - sg)));
+                    } else {
+                        o1[e] = dv;
+                    }
+                }
+                st8(dys + base + c, o1);
+                if (z) st8(dz + base + c, o2);
+            }
+        }
+        __syncthreads();  // red[] is reused by the next token
+    }
+    float *pr = part + (int64_t)blockIdx.x * HP + (int64_t)k * CG;
+#pragma unroll
+    for (int u = 0; u < kNormVec; ++u) {
+        const int c = 8 * (tid + 256 * u);
+        if (c < CG) {
+            *reinterpret_cast<float4 *>(pr + c) = make_float4(dw[u][0], dw[u][1], dw[u][2], dw[u][3]);
+            *reinterpret_cast<float4 *>(pr + c + 4) = make_float4(dw[u][4], dw[u][5], dw[u][6], dw[u][7]);
+        }
+    }
+}
+
+// out[c] = the rows of part [rows][n] summed in order, one thread per column.
+__global__ void k_sum_cols(const float *__restrict__ part, int64_t rows, int64_t n,
+                           float *__restrict__ out) {
+    const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    float s = 0.f;
+    for (int64_t r = 0; r < rows; ++r) s += part[r * n + c];
+    out[c] = s;
+}
+
 // dbias[h] = the parts of head h summed in order.
 __global__ void k_sum_parts(const float *__restrict__ part, int64_t nparts,
                             float *__restrict__ dbias, int H) {
@@ -1110,6 +1222,30 @@ void launch_dt_act_bwd(float *ddt, const float *dt_raw, const DtAct &act, int64_
                                                                   dbias ? part : nullptr, rows,
                                                                   (int)H);
     if (dbias) k_sum_parts<<<(unsigned)((H + 63) / 64), 64, 0, st>>>(part, np, dbias, (int)H);
+}
+
+bool norm_bwd_ok(int64_t H, int64_t P, int64_t NG) {
+    return P % 8 == 0 && (H / NG) * P <= 8 * 256 * kNormVec;
+}
+
+int64_t norm_bwd_parts(int64_t ntok) { return (ntok + kNormTok - 1) / kNormTok; }
+
+void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const float *w,
+                          float eps, int64_t ntok, int64_t H, int64_t P, int64_t NG, void *dys,
+                          void *dz, float *part, float *dw, int dtype, hipStream_t st) {
+    const int64_t nr = norm_bwd_parts(ntok);
+    if (nr <= 0) return;
+    const int CG = (int)((H / NG) * P);
+    const dim3 grid((unsigned)nr, (unsigned)NG);
+    if (dtype == SSD_BF16)
+        k_norm_gate_bwd<bf16><<<grid, 256, 0, st>>>((const bf16 *)dout, (const bf16 *)y,
+                                                    (const bf16 *)z, w, eps, (bf16 *)dys,
+                                                    (bf16 *)dz, part, ntok, H * P, CG);
+    else
+        k_norm_gate_bwd<float><<<grid, 256, 0, st>>>((const float *)dout, (const float *)y,
+                                                     (const float *)z, w, eps, (float *)dys,
+                                                     (float *)dz, part, ntok, H * P, CG);
+    if (dw) k_sum_cols<<<(unsigned)((H * P + 255) / 256), 256, 0, st>>>(part, nr, H * P, dw);
 }
 
 }  // namespace ssd

@@ -218,7 +218,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 7; }
+int ssd_abi_version(void) { return 8; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -275,12 +275,14 @@ ssd_status check_bwd(const ssd_scan_desc *d, ScanShape *s) {
 }
 
 // Workspace of ssd_scan_bwd_ex beyond the plain gradient's: the activated dt
-// (dt activation on); the ungated output, the gate's dy and the chunk-output
-// stage's workspace (gate on); the partial sums of ddt_bias (any edges).
-size_t bwd_edges_bytes(const ScanShape &s, bool act, bool gate, bool dbias) {
+// (dt activation on); the ungated output, the dy reaching the scan and the
+// chunk-output stage's workspace (gate or norm on); the partial sums of
+// ddt_bias (any edges) and of dnorm_weight (norm on).
+size_t bwd_edges_bytes(const ScanShape &s, bool act, bool gate, bool dbias, bool norm) {
     size_t n = 0;
     if (act) n += dt_eff_bytes(s);
-    if (gate) {
+    if (norm) n += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
+    if (gate || norm) {
         const size_t elem = s.dtype == SSD_BF16 ? 2 : 4;
         n += 2 * round_up((size_t)(s.B * s.L * s.H * s.P) * elem);
         n += round_up(ssd::chunk_scan_ws_bytes(bwd_shape(s)));
@@ -293,6 +295,18 @@ ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     return ssd_scan_bwd_ex_workspace_size(d, nullptr, bytes);
 }
 
+// The edges of a gradient call: as for the forward, and the norm's gradient
+// only for the shapes its kernel tiles.
+ssd_status read_bwd_edges(const ssd_edges *edges, const ScanShape &s, ssd::DtAct *act,
+                          const void **z, NormEdge *nm) {
+    ssd_status st = read_edges(edges, act, z);
+    if (st != SSD_OK) return st;
+    st = read_norm(edges, s.H, s.G, nm);
+    if (st != SSD_OK) return st;
+    if (nm->w && !ssd::norm_bwd_ok(s.H, s.P, nm->groups)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edges *edges,
                                           size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -301,13 +315,13 @@ ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edge
     if (st != SSD_OK) return st;
     ssd::DtAct act;
     const void *z;
-    st = read_edges(edges, &act, &z);
+    NormEdge nm;
+    st = read_bwd_edges(edges, s, &act, &z, &nm);
     if (st != SSD_OK) return st;
-    if (edges && edges->norm_weight) return SSD_ERR_UNSUPPORTED;
     *bytes = (s.B == 0 || s.L == 0)
                  ? 0
-                 : bwd_workspace_bytes(s) +
-                       bwd_edges_bytes(s, act_active(act), z != nullptr, edges != nullptr);
+                 : bwd_workspace_bytes(s) + bwd_edges_bytes(s, act_active(act), z != nullptr,
+                                                            edges != nullptr, nm.w != nullptr);
     return SSD_OK;
 }
 
@@ -317,7 +331,8 @@ ssd_status ssd_scan_bwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                         float *dB, float *dC, float *dD, float *dinit, void *workspace,
                         size_t ws_bytes, void *stream) {
     return ssd_scan_bwd_ex(d, nullptr, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA,
-                           dB, dC, dD, dinit, nullptr, nullptr, workspace, ws_bytes, stream);
+                           dB, dC, dD, dinit, nullptr, nullptr, nullptr, workspace, ws_bytes,
+                           stream);
 }
 
 ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const void *x,
@@ -325,33 +340,37 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
                            const float *D, const float *init_state, const void *dy,
                            const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
                            float *dC, float *dD, float *dinit, void *dz, float *ddt_bias,
-                           void *workspace, size_t ws_bytes, void *stream) {
+                           float *dnorm_weight, void *workspace, size_t ws_bytes,
+                           void *stream) {
     ScanShape s;
     ssd_status st = check_bwd(d, &s);
     if (st != SSD_OK) return st;
     ssd::DtAct act;
     const void *z;
-    st = read_edges(edges, &act, &z);
+    NormEdge nm;
+    st = read_bwd_edges(edges, s, &act, &z, &nm);
     if (st != SSD_OK) return st;
-    if (edges && edges->norm_weight) return SSD_ERR_UNSUPPORTED;  // the norm's gradient
     if (!edges) ddt_bias = nullptr;
+    if (!nm.w) dnorm_weight = nullptr;
     hipStream_t hs = as_stream(stream);
-    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = ddt_bias = 0, dinit = dfinal
-        st = check_ptrs({dA}, {dD, dinit, dfinal, ddt_bias});
+    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = ddt_bias = dnorm_weight = 0, dinit = dfinal
+        st = check_ptrs({dA}, {dD, dinit, dfinal, ddt_bias, dnorm_weight});
         if (st != SSD_OK) return st;
         ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
         if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
         if (ddt_bias) ssd::launch_copy_or_zero(ddt_bias, nullptr, s.H, hs);
+        if (dnorm_weight) ssd::launch_copy_or_zero(dnorm_weight, nullptr, s.H * s.P, hs);
         if (dinit) ssd::launch_copy_or_zero(dinit, dfinal, s.B * s.H * s.P * s.N, hs);
         return after_launch();
     }
-    const bool gate = z != nullptr, actv = act_active(act);
+    const bool gate = z != nullptr, actv = act_active(act), norm = nm.w != nullptr;
     if (gate && !dz) return SSD_ERR_NULL_PTR;
     st = check_ptrs({x, dt, A, B, C, dy, dx, ddt, dA, dB, dC},
-                    {D, init_state, dfinal, dD, dinit, workspace, z, dz, act.bias, ddt_bias});
+                    {D, init_state, dfinal, dD, dinit, workspace, z, dz, act.bias, ddt_bias,
+                     nm.w, dnorm_weight});
     if (st != SSD_OK) return st;
     const size_t base = bwd_workspace_bytes(s);
-    if (ws_bytes < base + bwd_edges_bytes(s, actv, gate, edges != nullptr))
+    if (ws_bytes < base + bwd_edges_bytes(s, actv, gate, edges != nullptr, norm))
         return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
     const ScanShape b = bwd_shape(s);
@@ -365,9 +384,14 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
         dt_eff = reinterpret_cast<float *>(extra);
         extra += dt_eff_bytes(s);
     }
+    float *npart = nullptr;
+    if (norm) {
+        npart = reinterpret_cast<float *>(extra);
+        extra += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
+    }
     void *yun = nullptr, *dys = nullptr, *cbws = nullptr;
     const int64_t nel = s.B * s.L * s.H * s.P;
-    if (gate) {
+    if (gate || norm) {
         const size_t eb = round_up((size_t)nel * (s.dtype == SSD_BF16 ? 2 : 4));
         yun = extra;
         dys = extra + eb;
@@ -390,13 +414,17 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     if (mm) ssd::launch_bwd_states_mfma(b, x, B, dtu, Acs, Hst, false, hs);
     else ssd::launch_chunk_state(b, x, B, dtu, Acs, Hst, hs);
     ssd::launch_state_passing(b, Hst, Acs, init_state, nullptr, hs);
-    // gate: the ungated output from the chunk-output stage on those states,
-    // then dy * silu(z) for the scan and dz
+    // gate / norm: the ungated output from the chunk-output stage on those
+    // states, then the gradient reaching the scan output, dz and dnorm_weight
     const void *dyu = dy;
-    if (gate) {
+    if (gate || norm) {
         ssd::launch_chunk_cb(b, B, C, cbws, hs);
         ssd::launch_chunk_scan(b, x, dtu, B, C, D, Acs, Hst, cbws, yun, hs);
-        ssd::launch_gate_bwd(dy, yun, z, dys, dz, nel, s.dtype, hs);
+        if (norm)
+            ssd::launch_norm_gate_bwd(dy, yun, z, nm.w, nm.eps, s.B * s.L, s.H, s.P, nm.groups,
+                                      dys, dz, npart, dnorm_weight, s.dtype, hs);
+        else
+            ssd::launch_gate_bwd(dy, yun, z, dys, dz, nel, s.dtype, hs);
         dyu = dys;
     }
     // derivatives with respect to every chunk's end state, and the initial state's

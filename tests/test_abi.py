@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 7
+    assert L.ssd_abi_version() == 8
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -430,18 +430,24 @@ def test_bwd_ex_workspace_and_errors(L):
     assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(eg),
                                             ctypes.byref(n2)) == OK
     assert n2.value > n1.value + 2 * r256(512 * 8 * 64 * 2)
-    en = edges(norm_weight=P16, norm_eps=1e-5)
+    # the norm's gradient: within the kernel's tiling it adds its partial sums;
+    # headdim 12 (not a multiple of 8) is refused
+    en = edges(dt_bias=P16, dt_softplus=1, z=P16, norm_weight=P16, norm_eps=1e-5)
+    n3 = ctypes.c_size_t(0)
     assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(en),
-                                            ctypes.byref(n1)) == UNSUP
-    need = n2.value
+                                            ctypes.byref(n3)) == OK
+    assert n3.value == n2.value + r256(32 * 8 * 64 * 4)   # 512 / 16 token ranges x 512 channels
+    assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(desc(headdim=12, dtype=0)),
+                                            ctypes.byref(en), ctypes.byref(n1)) == UNSUP
+    need = n3.value
     args = [P16] * 16  # x dt A B C D init dy dfinal dx ddt dA dB dC dD dinit
-    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(en), *args, P16, P16, P16, need,
-                             None) == UNSUP
-    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, None, P16, P16, need,
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, None, P16, P16, P16, need,
                              None) == NULL                      # gate without dz
-    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P_MIS, P16, P16, need,
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P_MIS, P16, P16, P16, need,
                              None) == ALIGN
-    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P16, P_MIS, P16, need,
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P16, P_MIS, P16, P16, need,
                              None) == ALIGN
-    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(eg), *args, P16, P16, P16, need - 1,
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(en), *args, P16, P16, P_MIS, P16, need,
+                             None) == ALIGN
+    assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(en), *args, P16, P16, P16, P16, need - 1,
                              None) == WS

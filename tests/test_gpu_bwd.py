@@ -188,3 +188,36 @@ def test_bwd_edges_vs_oracle(name, which):
     if use_dt:
         # the clamp holds some values: their raw-dt gradient is exactly zero
         assert bool((g["ddt"] == 0).any())
+
+
+@pytest.mark.parametrize("gated", [True, False])
+@pytest.mark.parametrize("name", ["bf16_mfma_groups", "f32_generic"])
+def test_bwd_edges_norm_vs_oracle(name, gated):
+    """The gradient through the gated RMSNorm as well (norm groups = the B/C
+    groups): dnorm_weight, dz and every other gradient against the oracle."""
+    Bt, L, H, P, N, G, dt_ = EDGE_SHAPES[name]
+    announce(f"bwd edges norm {name} gated {gated}")
+    spec = synth.custom_spec(Bt, L, H, P, N, G, chunk=64, dtype=dt_, dt_rule="ranged",
+                             init="normal", seed=63)
+    inp = synth.scan_edge_inputs(spec)
+    rng = np.random.default_rng(64)
+    io = torch.bfloat16 if dt_ == "bf16" else torch.float32
+    dy = torch.from_numpy(rng.standard_normal(inp["x"].shape, dtype=np.float32)).to(io)
+    dfinal = torch.from_numpy(rng.standard_normal(inp["init"].shape, dtype=np.float32))
+    w = torch.from_numpy(1.0 + 0.5 * rng.standard_normal(H * P)).float()
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    g = ssd.scan_bwd(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], dy.to(DEV), d["D"], d["init"],
+                     dfinal.to(DEV), chunk=64, dt_bias=d["dt_bias"], dt_softplus=True,
+                     dt_limit=EDGE_LIMIT, z=d["gate"] if gated else None,
+                     norm_weight=w.to(DEV), norm_eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.scan_vjp_edges(inp["x"], inp["dt_raw"], inp["A"], inp["B"], inp["C"],
+                                inp["D"], inp["init"], dy=dy, dfinal=dfinal,
+                                dt_bias=inp["dt_bias"], dt_softplus=True, dt_limit=EDGE_LIMIT,
+                                z=inp["gate"] if gated else None, norm_weight=w, norm_eps=1e-5,
+                                norm_groups=G)
+    keys = list(GRADS) + ["ddt_bias", "dnorm_weight"] + (["dz"] if gated else [])
+    tol = TOL[io]
+    for k in keys:
+        e = rel_err(f64(g[k]), ref[k])
+        assert e <= tol, (k, e)
