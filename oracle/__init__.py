@@ -253,3 +253,36 @@ def scan_vjp_edges(x, dt_raw, A, B, C, D=None, init=None, dy=None, dfinal=None, 
         g["dz"] = dz
     g.update(extra)
     return g
+
+
+def scan_vjp_varlen(cu_seqlens, x, dt, A, B, C, D=None, init=None, dy=None, dfinal=None,
+                    nthreads: int = 0) -> dict:
+    """Gradients for a ragged batch (scan_varlen): every sequence's own
+    scan_vjp on its tokens (a sequence sees no other's tokens, starts from its
+    init and ends in its final state).  dx, ddt, dB, dC are per packed token,
+    dinit per sequence, dA and dD summed over the sequences."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    x, dt, B, C, dy = f64(x), f64(dt), f64(B), f64(C), f64(dy)
+    total, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    ns = len(cu) - 1
+    out = {"dx": np.zeros_like(x), "ddt": np.zeros((total, H)), "dA": np.zeros(H),
+           "dB": np.zeros((total, G, N)), "dC": np.zeros((total, G, N)), "dD": np.zeros(H),
+           "dinit": np.zeros((ns, H, P, N))}
+    for s in range(ns):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            if dfinal is not None:
+                out["dinit"][s] = f64(dfinal)[s]
+            continue
+        g = scan_vjp(x[None, a:b], dt[None, a:b], A, B[None, a:b], C[None, a:b], D,
+                     None if init is None else f64(init)[s:s + 1], dy[None, a:b],
+                     None if dfinal is None else f64(dfinal)[s:s + 1], nthreads=nthreads)
+        out["dx"][a:b] = g["dx"][0]
+        out["ddt"][a:b] = g["ddt"][0]
+        out["dB"][a:b] = g["dB"][0]
+        out["dC"][a:b] = g["dC"][0]
+        out["dinit"][s] = g["dinit"][0]
+        out["dA"] += g["dA"]
+        out["dD"] += g["dD"]
+    return out
