@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 8. */
+/* ABI version of this header: 9. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -273,6 +273,32 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
                                const float *A, const void *B, const void *C, const float *D,
                                const float *init_states, void *y, float *final_states,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* The gradient of ssd_scan_fwd_varlen (its edges as for ssd_scan_bwd_ex):
+ * every sequence's gradient on its own tokens, as ssd_scan_bwd_ex would give
+ * for it alone (batch 1), with the sequences' layouts of
+ * ssd_scan_fwd_varlen.
+ *   dy             [total, nheads, headdim]                 dtype
+ *   dfinal_states  [nseq, nheads, headdim, dstate] fp32, or NULL
+ *   dx, ddt, dB, dC, dz   per packed token (layouts of x, dt, B, C, x)
+ *   dA, dD, ddt_bias, dnorm_weight   summed over all sequences
+ *   dinit_states   [nseq, nheads, headdim, dstate] fp32, or NULL; an empty
+ *                  sequence gets its dfinal (or zeros)
+ *   workspace      ssd_scan_bwd_varlen_workspace_size bytes for the same
+ *                  edges.
+ * The gradient cuts each sequence into chunks of its own size from its first
+ * token (64 or 32 tokens, as for ssd_scan_bwd_ex), with a chunk table built
+ * on the device: no host copy of the lengths, graph-capturable. */
+ssd_status ssd_scan_bwd_varlen_workspace_size(const ssd_varlen_desc *d, const ssd_edges *edges,
+                                              size_t *bytes);
+ssd_status ssd_scan_bwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
+                               const int32_t *cu_seqlens, const void *x, const float *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *init_states, const void *dy,
+                               const float *dfinal_states, void *dx, float *ddt, float *dA,
+                               float *dB, float *dC, float *dD, float *dinit_states, void *dz,
+                               float *ddt_bias, float *dnorm_weight, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------- decode step */
 

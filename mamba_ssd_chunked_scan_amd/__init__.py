@@ -11,6 +11,6 @@ synthetic input generator used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
     SSDError, chunk_cb, chunk_cumsum, chunk_scan, chunk_scan_workspace_size, chunk_state, lib,
-    scan_bwd, scan_fwd, scan_fwd_varlen, state_passing, step, step_multi, varlen_workspace_size,
-    workspace_size,
+    scan_bwd, scan_bwd_varlen, scan_fwd, scan_fwd_varlen, state_passing, step, step_multi,
+    varlen_workspace_size, workspace_size,
 )

@@ -27,7 +27,7 @@ EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "s
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
            "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen",
            "ssd_scan_bwd_workspace_size", "ssd_scan_bwd", "ssd_scan_bwd_ex_workspace_size",
-           "ssd_scan_bwd_ex")
+           "ssd_scan_bwd_ex", "ssd_scan_bwd_varlen_workspace_size", "ssd_scan_bwd_varlen")
 
 
 class ScanDesc(ctypes.Structure):
@@ -71,7 +71,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 8  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 9  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -114,6 +114,11 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_bwd_ex.argtypes = ([ctypes.POINTER(ScanDesc), ctypes.POINTER(Edges)]
                                       + [_P] * 20 + [ctypes.c_size_t, _P])
+        L.ssd_scan_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
+                                                         ctypes.POINTER(Edges),
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_bwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
+                                          + [_P] * 21 + [ctypes.c_size_t, _P])
         L.ssd_varlen_workspace_size.argtypes = [ctypes.POINTER(VarlenDesc),
                                                 ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_scan_fwd_varlen.argtypes = ([ctypes.POINTER(VarlenDesc), ctypes.POINTER(Edges)]
@@ -322,6 +327,58 @@ def scan_bwd(x, dt, A, B, C, dy, D=None, init_state=None, dfinal=None, chunk: in
                                _ptr(workspace), workspace.numel(),
                                _stream(dev))
     _check("ssd_scan_bwd_ex", st)
+    return out
+
+
+def scan_bwd_varlen(x, dt, A, B, C, cu_seqlens, dy, D=None, chunk: int = 256,
+                    init_states=None, dfinal_states=None, workspace=None, dt_bias=None,
+                    dt_softplus: bool = False, dt_limit=None, z=None, norm_weight=None,
+                    norm_eps: float = 1e-5, norm_groups: int = 0) -> dict:
+    """Gradient of :func:`scan_fwd_varlen` (edges as for :func:`scan_bwd`):
+    every sequence's own gradient.  Returns a dict like scan_bwd's, with dinit
+    per sequence [nseq, nheads, headdim, dstate]."""
+    if x.dim() != 3 or B.dim() != 3 or dt.dim() != 2:
+        raise ValueError("x [total,h,p], dt [total,h], B/C [total,g,n] expected")
+    total, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    ns = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", (ns + 1,), torch.int32, dev)
+    _need(dy, "dy", x.shape, x.dtype, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (ns, H, P, N), torch.float32, dev)
+    if dfinal_states is not None:
+        _need(dfinal_states, "dfinal_states", (ns, H, P, N), torch.float32, dev)
+    desc = VarlenDesc(ns, total, H, P, N, G, chunk, _io_dtype(x), 0)
+    e = _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight, norm_eps, norm_groups)
+    n = ctypes.c_size_t(0)
+    _check("ssd_scan_bwd_varlen_workspace_size",
+           lib().ssd_scan_bwd_varlen_workspace_size(ctypes.byref(desc), _eref(e),
+                                                    ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() < n.value or workspace.device != dev:
+        raise ValueError(f"workspace needs {n.value} bytes on {dev}")
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty((total, H), **f32),
+           "dA": torch.empty(H, **f32), "dB": torch.empty((total, G, N), **f32),
+           "dC": torch.empty((total, G, N), **f32),
+           "dD": torch.empty(H, **f32) if D is not None else None,
+           "dinit": (torch.empty((ns, H, P, N), **f32)
+                     if init_states is not None or dfinal_states is not None else None)}
+    if z is not None:
+        out["dz"] = torch.empty_like(x)
+    if dt_bias is not None:
+        out["ddt_bias"] = torch.empty(H, **f32)
+    if norm_weight is not None:
+        out["dnorm_weight"] = torch.empty(H * P, **f32)
+    st = lib().ssd_scan_bwd_varlen(
+        ctypes.byref(desc), _eref(e), _ptr(cu_seqlens), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+        _ptr(C), _ptr(D), _ptr(init_states), _ptr(dy), _ptr(dfinal_states), _ptr(out["dx"]),
+        _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+        _ptr(out["dinit"]), _ptr(out.get("dz")), _ptr(out.get("ddt_bias")),
+        _ptr(out.get("dnorm_weight")), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("ssd_scan_bwd_varlen", st)
     return out
 
 

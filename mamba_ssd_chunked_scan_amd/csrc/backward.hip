@@ -74,7 +74,7 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
             const float *__restrict__ Es, const Tin *__restrict__ dy, Tin *__restrict__ dx,
             float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
             float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int P, int N, int G,
-            int T, int slice_rows) {
+            int T, int slice_rows, const int2 *__restrict__ ctab) {
     constexpr int Q = kBQ, LQ = kLQ;
     extern __shared__ __attribute__((aligned(16))) float sm[];
     const int PS = bwd_ps(P), NS = bwd_ns(N);
@@ -107,8 +107,10 @@ k_chunk_bwd(const Tin *__restrict__ x, const float *__restrict__ dt, const float
     const int64_t b = rest / T;
     const int h0 = g * R + hsl * kHeadsPerBlock;
     const int nh = min(kHeadsPerBlock, g * R + R - h0);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
     const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N, PN = (int64_t)P * N;
     const int64_t bo = ((b * L + t0) * G + g) * N;
     const int nq = N / 4;
@@ -513,7 +515,7 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
                  const float *__restrict__ Es, const bf16 *__restrict__ dy, bf16 *__restrict__ dx,
                  float *__restrict__ ddt, float *__restrict__ dB, float *__restrict__ dC,
                  float *__restrict__ dA, float *__restrict__ dD, int64_t L, int H, int G, int T,
-                 int hpb, int nslices, int64_t nblocks) {
+                 int hpb, int nslices, int64_t nblocks, const int2 *__restrict__ ctab) {
     using Ly = BwdLds<N, QT>;
     constexpr int Q = Ly::Q, P = 64, NT = N / 32, NTH = 256 * QT, W = 4 * QT;
     constexpr int LDN = Ly::LDN, LDP = Ly::LDP, LDK = Ly::LDK, LDC = Ly::LDC;
@@ -547,8 +549,10 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     const int64_t b = rest / (uint32_t)T;
     const int h0 = g * R + hsl * hpb;
     const int nh = min(hpb, g * R + R - h0);
-    const int64_t t0 = (int64_t)c * Q;
-    const int q = (int)min((int64_t)Q, L - t0);
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
     // block-uniform 64-bit bases, per-lane 32-bit offsets (a chunk spans fewer
     // than 2^31 elements of every tensor)
     const unsigned brs = (unsigned)G * N, xrs = (unsigned)H * P;
@@ -946,7 +950,7 @@ void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const
     k_chunk_bwd_mfma<N, QT><<<padded_grid(nblocks), 256 * QT, BwdLds<N, QT>::BYTES, st>>>(
         (const bf16 *)x, dt, A, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, Hs, Es,
         (const bf16 *)dy, (bf16 *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.G, (int)s.T,
-        hpb, (int)nslices, nblocks);
+        hpb, (int)nslices, nblocks, s.ctab);
 }
 
 // ------------------------------------------------------- edges, backward
@@ -955,13 +959,14 @@ void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_gate_bwd(const T *__restrict__ dy, const T *__restrict__ y, const T *__restrict__ z,
-           T *__restrict__ dys, T *__restrict__ dz, int64_t n) {
+           T *__restrict__ dys, T *__restrict__ dz, float *__restrict__ dys32, int64_t n) {
     const int64_t n8 = n / 8;
     if (blockIdx.x == 0 && threadIdx.x < n - 8 * n8) {  // the last n % 8 values
         const int64_t i = 8 * n8 + threadIdx.x;
         const float g = Elem<T>::ld(dy, i), zz = Elem<T>::ld(z, i);
         const float sg = sigmoid_f(zz);
         Elem<T>::st(dys, i, g * (zz * sg));
+        if (dys32) dys32[i] = g * (zz * sg);
         Elem<T>::st(dz, i, g * Elem<T>::ld(y, i) * (sg * (1.f + zz * (1.f - sg))));
     }
     for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
@@ -976,6 +981,7 @@ k_gate_bwd(const T *__restrict__ dy, const T *__restrict__ y, const T *__restric
             b[e] = g[e] * yy[e] * (sg * (1.f + zz[e] * (1.f - sg)));
         }
         st8(dys + 8 * i, a);
+        if (dys32) st8(dys32 + 8 * i, a);
         st8(dz + 8 * i, b);
     }
 }
@@ -1029,7 +1035,8 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 k_norm_gate_bwd(const T *__restrict__ dout, const T *__restrict__ y, const T *__restrict__ z,
                 const float *__restrict__ w, float eps, T *__restrict__ dys, T *__restrict__ dz,
-                float *__restrict__ part, int64_t ntok, int64_t HP, int CG) {
+                float *__restrict__ part, int64_t ntok, int64_t HP, int CG,
+                float *__restrict__ dys32) {
     __shared__ float red[2][4];
     const int tid = threadIdx.x, k = blockIdx.y;
     const int64_t t0 = (int64_t)blockIdx.x * kNormTok;
@@ -1101,6 +1108,7 @@ k_norm_gate_bwd(const T *__restrict__ dout, const T *__restrict__ y, const T *__
                     }
                 }
                 st8(dys + base + c, o1);
+                if (dys32) st8(dys32 + base + c, o1);
                 if (z) st8(dz + base + c, o2);
             }
         }
@@ -1167,7 +1175,7 @@ void launch_bwd_t(const ScanShape &s, const void *x, const float *dt, const floa
     k_chunk_bwd<Tin, KI><<<(unsigned)(s.B * s.T * s.G * nslices), kBThreads, lds, st>>>(
         (const Tin *)x, dt, A, (const Tin *)Bm, (const Tin *)Cm, D, Acs, Hs, Es,
         (const Tin *)dy, (Tin *)dx, ddt, dB, dC, dA, dD, s.L, (int)s.H, (int)s.P, (int)s.N,
-        (int)s.G, (int)s.T, rows);
+        (int)s.G, (int)s.T, rows, s.ctab);
 }
 
 }  // namespace
@@ -1200,16 +1208,17 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
 }
 
 void launch_gate_bwd(const void *dy, const void *y, const void *z, void *dys, void *dz,
-                     int64_t n, int dtype, hipStream_t st) {
+                     int64_t n, int dtype, hipStream_t st, float *dys32) {
     if (n <= 0) return;
     const int64_t want = (n / 8 + 255) / 256;
     const unsigned blocks = (unsigned)(want < 1 ? 1 : (want < 65536 ? want : 65536));
     if (dtype == SSD_BF16)
         k_gate_bwd<bf16><<<blocks, 256, 0, st>>>((const bf16 *)dy, (const bf16 *)y, (const bf16 *)z,
-                                                 (bf16 *)dys, (bf16 *)dz, n);
+                                                 (bf16 *)dys, (bf16 *)dz, dys32, n);
     else
         k_gate_bwd<float><<<blocks, 256, 0, st>>>((const float *)dy, (const float *)y,
-                                                  (const float *)z, (float *)dys, (float *)dz, n);
+                                                  (const float *)z, (float *)dys, (float *)dz,
+                                                  dys32, n);
 }
 
 int64_t dt_bias_parts(int64_t rows) { return (rows + kDtRows - 1) / kDtRows; }
@@ -1232,7 +1241,8 @@ int64_t norm_bwd_parts(int64_t ntok) { return (ntok + kNormTok - 1) / kNormTok; 
 
 void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const float *w,
                           float eps, int64_t ntok, int64_t H, int64_t P, int64_t NG, void *dys,
-                          void *dz, float *part, float *dw, int dtype, hipStream_t st) {
+                          void *dz, float *part, float *dw, int dtype, hipStream_t st,
+                          float *dys32) {
     const int64_t nr = norm_bwd_parts(ntok);
     if (nr <= 0) return;
     const int CG = (int)((H / NG) * P);
@@ -1240,11 +1250,12 @@ void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const 
     if (dtype == SSD_BF16)
         k_norm_gate_bwd<bf16><<<grid, 256, 0, st>>>((const bf16 *)dout, (const bf16 *)y,
                                                     (const bf16 *)z, w, eps, (bf16 *)dys,
-                                                    (bf16 *)dz, part, ntok, H * P, CG);
+                                                    (bf16 *)dz, part, ntok, H * P, CG, dys32);
     else
         k_norm_gate_bwd<float><<<grid, 256, 0, st>>>((const float *)dout, (const float *)y,
                                                      (const float *)z, w, eps, (float *)dys,
-                                                     (float *)dz, part, ntok, H * P, CG);
+                                                     (float *)dz, part, ntok, H * P, CG,
+                                                     dys32);
     if (dw) k_sum_cols<<<(unsigned)((H * P + 255) / 256), 256, 0, st>>>(part, nr, H * P, dw);
 }
 

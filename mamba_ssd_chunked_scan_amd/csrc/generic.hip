@@ -82,9 +82,9 @@ k_chunk_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
 // so each token costs a thread two 16-byte LDS reads for 16 FMAs.
 constexpr int kStateJT = 32;
 
-template <typename Tin, bool kAdjoint = false>
+template <typename Tin, bool kAdjoint = false, typename TX = Tin>
 __global__ void __launch_bounds__(256)
-k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
+k_chunk_state_generic(const TX *__restrict__ x, const Tin *__restrict__ Bm,
                       const float *__restrict__ dt, const float *__restrict__ Acs,
                       float *__restrict__ states, int64_t L, int H, int P, int N, int G, int Q,
                       int T, const int2 *__restrict__ ctab) {
@@ -114,14 +114,14 @@ k_chunk_state_generic(const Tin *__restrict__ x, const Tin *__restrict__ Bm,
     const bool active = 4 * pi < pb;
     float acc[4][4] = {};
     const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
-    const Tin *xb = x + ((b * L + t0) * H + h) * P + p0;
+    const TX *xb = x + ((b * L + t0) * H + h) * P + p0;
     const Tin *bb = Bm + ((b * L + t0) * G + g) * N;
     for (int j0 = 0; j0 < q; j0 += kStateJT) {
         const int jn = min(kStateJT, q - j0);
         __syncthreads();  // w ready / the previous tile no longer read
         for (int e = threadIdx.x; e < jn * PBS; e += 256) {
             const int j = e / PBS, pl = e - j * PBS;
-            xs[e] = pl < pb ? Elem<Tin>::ld(xb, (j0 + j) * xrow + pl) : 0.f;
+            xs[e] = pl < pb ? Elem<TX>::ld(xb, (j0 + j) * xrow + pl) : 0.f;
         }
         for (int e = threadIdx.x; e < jn * N; e += 256) {
             const int j = e / N, n = e - j * N;
@@ -181,18 +181,33 @@ k_state_passing(float *__restrict__ states, const float *__restrict__ Acs,
 __global__ void __launch_bounds__(256)
 k_state_passing_rev(float *__restrict__ ds, const float *__restrict__ Acs,
                     const float *__restrict__ dfin, float *__restrict__ dinit, int64_t L, int H,
-                    int64_t PN, int Q, int T) {
+                    int64_t PN, int Q, int T, const int2 *__restrict__ ctab,
+                    const int2 *__restrict__ sch) {
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     if (e >= PN) return;
+    // a row: a batch row (slots b T .. b T + T - 1) or a sequence of a
+    // variable-length batch (its slots from sch, chunk ends from ctab)
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H;
     const int h = (int)(bh % H);
+    int64_t k0;
+    int n;
+    const float *acs;
+    if (sch) {
+        const int2 r = sch[b];
+        k0 = r.x;
+        n = r.y;
+        acs = Acs + (int64_t)h * L;
+    } else {
+        k0 = b * T;
+        n = T;
+        acs = Acs + bh * L;
+    }
     float4 E = make_float4(0.f, 0.f, 0.f, 0.f);
     if (dfin) E = *reinterpret_cast<const float4 *>(dfin + bh * PN + e);
-    const float *acs = Acs + bh * L;
     const int64_t cstride = (int64_t)H * PN;
-    float *base = ds + (b * T * H + h) * PN + e;
-    for (int c0 = T - 1; c0 >= 0; c0 -= kPassAhead) {
+    float *base = ds + (k0 * H + h) * PN + e;
+    for (int c0 = n - 1; c0 >= 0; c0 -= kPassAhead) {
         float4 sv[kPassAhead];
         float r[kPassAhead];
 #pragma unroll
@@ -200,7 +215,14 @@ k_state_passing_rev(float *__restrict__ ds, const float *__restrict__ Acs,
             const int c = c0 - k;
             if (c >= 0) {
                 sv[k] = *reinterpret_cast<const float4 *>(base + c * cstride);
-                r[k] = ssd_exp(acs[min(L, (int64_t)(c + 1) * Q) - 1]);
+                int64_t last;
+                if (ctab) {
+                    const int2 cp = ctab[k0 + c];
+                    last = (int64_t)cp.x + cp.y - 1;
+                } else {
+                    last = min(L, (int64_t)(c + 1) * Q) - 1;
+                }
+                r[k] = ssd_exp(acs[last]);
             }
         }
 #pragma unroll
@@ -715,25 +737,31 @@ void launch_chunk_state(const ScanShape &s, const void *x, const void *Bm, const
 }
 
 void launch_chunk_dstate(const ScanShape &s, const void *dy, const void *Cm, const float *Acs,
-                         float *dstates, hipStream_t st) {
+                         float *dstates, hipStream_t st, bool dy_f32) {
     const dim3 grid = state_generic_grid(s);
     const size_t lds = state_generic_lds(s);
-    if (s.dtype == SSD_BF16)
+    if (s.dtype == SSD_BF16 && dy_f32)
+        k_chunk_state_generic<bf16, true, float><<<grid, 256, lds, st>>>(
+            (const float *)dy, (const bf16 *)Cm, nullptr, Acs, dstates, s.L, (int)s.H, (int)s.P,
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
+    else if (s.dtype == SSD_BF16)
         k_chunk_state_generic<bf16, true><<<grid, 256, lds, st>>>(
             (const bf16 *)dy, (const bf16 *)Cm, nullptr, Acs, dstates, s.L, (int)s.H, (int)s.P,
-            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, nullptr);
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
     else
         k_chunk_state_generic<float, true><<<grid, 256, lds, st>>>(
             (const float *)dy, (const float *)Cm, nullptr, Acs, dstates, s.L, (int)s.H, (int)s.P,
-            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, nullptr);
+            (int)s.N, (int)s.G, (int)s.Q, (int)s.T, s.ctab);
 }
 
 void launch_state_passing_rev(const ScanShape &s, float *dstates, const float *Acs,
                               const float *dfin, float *dinit, hipStream_t st) {
     const int64_t PN = s.P * s.N;
-    dim3 grid((unsigned)(s.B * s.H), (unsigned)((PN / 4 + 255) / 256));
+    const int64_t rows = s.sch ? s.NS : s.B;  // batch rows, or sequences
+    if (rows == 0) return;
+    dim3 grid((unsigned)(rows * s.H), (unsigned)((PN / 4 + 255) / 256));
     k_state_passing_rev<<<grid, 256, 0, st>>>(dstates, Acs, dfin, dinit, s.L, (int)s.H, PN,
-                                               (int)s.Q, (int)s.T);
+                                               (int)s.Q, (int)s.T, s.ctab, s.sch);
 }
 
 void launch_state_passing(const ScanShape &s, float *states, const float *Acs,

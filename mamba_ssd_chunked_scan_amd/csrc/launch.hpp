@@ -73,7 +73,7 @@ void launch_step(const StepShape &s, int64_t nsteps, float *state, const void *x
 // Gradient (fixed chunking, generic kernels):
 // dS_c = sum_s exp(Acs_s) dy_s C_s^T per chunk (states layout) ...
 void launch_chunk_dstate(const ScanShape &s, const void *dy, const void *Cm, const float *Acs,
-                         float *dstates, hipStream_t st);
+                         float *dstates, hipStream_t st, bool dy_f32 = false);
 // ... turned in place, last chunk first, into the derivative with respect to
 // each chunk's end state; dinit (may be null) gets the initial state's.
 void launch_state_passing_rev(const ScanShape &s, float *dstates, const float *Acs,
@@ -92,8 +92,9 @@ void launch_chunk_bwd(const ScanShape &s, const void *x, const float *dt, const 
 bool bwd_mfma_ok(const ScanShape &s);
 // Gradient through the output gate y_out = y * silu(z), elementwise over n
 // values of x's layout: dys = dy * silu(z), dz = dy * y * silu'(z).
+// dys32 (may be null): the same dys in fp32, unrounded.
 void launch_gate_bwd(const void *dy, const void *y, const void *z, void *dys, void *dz,
-                     int64_t n, int dtype, hipStream_t st);
+                     int64_t n, int dtype, hipStream_t st, float *dys32 = nullptr);
 // Gradient through the dt activation, in place: ddt [rows][H] with respect
 // to the activated dt becomes the gradient with respect to the raw dt; when
 // dbias is non-null it gets the per-head sums over the rows (fixed order,
@@ -111,14 +112,16 @@ bool norm_bwd_ok(int64_t H, int64_t P, int64_t NG);
 int64_t norm_bwd_parts(int64_t ntok);
 void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const float *w,
                           float eps, int64_t ntok, int64_t H, int64_t P, int64_t NG, void *dys,
-                          void *dz, float *part, float *dw, int dtype, hipStream_t st);
+                          void *dz, float *part, float *dw, int dtype, hipStream_t st,
+                          float *dys32 = nullptr);
 
 // The gradient's 64-token chunk states (and their adjoint, with x = dy and
 // B = C) on the matrix cores, for bwd_mfma_ok shapes.
 bool bwd_states_mfma_ok(const ScanShape &s);
+// x_f32: xin is fp32 (adjoint only), not the call's dtype.
 void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
                             const float *dt, const float *Acs, float *out, bool adjoint,
-                            hipStream_t st);
+                            hipStream_t st, bool x_f32 = false);
 
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);

@@ -36,11 +36,12 @@ constexpr int kJT = 32;  // tokens per streamed stage (one 32-row tile)
 using namespace mx;
 
 // Registers holding one 32-token stage between its global load and its LDS
-// store: one 16-byte x segment and NBV 16-byte B segments per thread.  Two sets
-// give a prefetch distance of two stages.
-template <int NBV>
+// store: one 8-value x segment (XW 16-byte words: 1 for bf16 x, 2 for fp32)
+// and NBV 16-byte B segments per thread.  Two sets give a prefetch distance
+// of two stages.
+template <int NBV, int XW>
 struct StageRegs {
-    u32x4 x;
+    u32x4 x[XW];
     u32x4 b[NBV];
 };
 
@@ -60,10 +61,12 @@ using P1 = std::integral_constant<int, 1>;
 // later stages, instead of reading it.  It then also applies the dt
 // activation `act` and, when dt_out is given, writes the activated dt there.
 // kAdjoint (the gradient's chunk term, with x = dy and B = C): the weight is
-// exp(Acs_j), the decay from the chunk's entering state to token j.
-template <int Q, int N, bool kCumsum, bool kAdjoint = false>
+// exp(Acs_j), the decay from the chunk's entering state to token j.  TX: x's
+// type; fp32 x (the gradient's dy behind a gate, kept unrounded) is weighted
+// and split like bf16 x.
+template <int Q, int N, bool kCumsum, bool kAdjoint = false, typename TX = bf16>
 __global__ void __launch_bounds__(256, 2)
-k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
+k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ A,
                    float *__restrict__ Acs, float *__restrict__ states, int64_t L, int H, int G,
                    int T, int64_t nblocks, DtAct act, float *__restrict__ dt_out,
@@ -88,7 +91,7 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     const int64_t t0 = cp.t0;
     const int q = cp.q;
     if (q <= 0) return;  // an unused slot of a variable-length batch
-    const bf16 *xbase = x + ((b * L + t0) * H + h) * kP;
+    const TX *xbase = x + ((b * L + t0) * H + h) * kP;
     const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     // per-thread offsets are unsigned 32-bit from block-uniform bases (a
     // chunk spans < 2^31 elements of x, B, C and y), so loads and stores use
@@ -126,24 +129,32 @@ k_chunk_state_mfma(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
             w[tid] = tid < q ? v : 0.f;
         }
     }
-    StageRegs<NBV> R[2];
-    auto load_stage = [&](int st, StageRegs<NBV> &r) {
+    constexpr int XW = sizeof(TX) / 2;
+    StageRegs<NBV, XW> R[2];
+    auto load_stage = [&](int st, StageRegs<NBV, XW> &r) {
         const int j = st * kJT + xrow;
-        r.x = *reinterpret_cast<const u32x4 *>(xbase + ((unsigned)min(j, q - 1) * xrs + xseg * 8u));
+        const TX *xp = xbase + ((unsigned)min(j, q - 1) * xrs + xseg * 8u);
+#pragma unroll
+        for (int k = 0; k < XW; ++k) r.x[k] = *reinterpret_cast<const u32x4 *>(xp + k * (8 / XW));
 #pragma unroll
         for (int i = 0; i < NBV; ++i) {
             const int e = tid + 256 * i, rr = e / BSEG, sg = e % BSEG;
             r.b[i] = *reinterpret_cast<const u32x4 *>(bbase + ((unsigned)min(st * kJT + rr, q - 1) * brs + sg * 8u));
         }
     };
-    auto store_stage = [&](int st, int buf, const StageRegs<NBV> &r) {
+    auto store_stage = [&](int st, int buf, const StageRegs<NBV, XW> &r) {
         const int j = st * kJT + xrow;
         const float wj = w[j];  // zero at and beyond q
         float v[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[2 * k] = lo_bf16(r.x[k]) * wj;
-            v[2 * k + 1] = hi_bf16(r.x[k]) * wj;
+            if constexpr (XW == 1) {
+                v[2 * k] = lo_bf16(r.x[0][k]) * wj;
+                v[2 * k + 1] = hi_bf16(r.x[0][k]) * wj;
+            } else {
+                v[2 * k] = __uint_as_float(r.x[(2 * k) / 4][(2 * k) % 4]) * wj;
+                v[2 * k + 1] = __uint_as_float(r.x[(2 * k + 1) / 4][(2 * k + 1) % 4]) * wj;
+            }
         }
         u32x4 hi, lo;
         split8(v, hi, lo);
@@ -788,27 +799,29 @@ bool bwd_mfma_ok(const ScanShape &s) {
     const int64_t q = 64;
     const bool offsets32 = (q + 64) * s.H * s.P * 2 < (int64_t(1) << 31) &&
                            (q + 64) * s.G * s.N * 2 < (int64_t(1) << 31);
-    return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) && offsets32 && !s.ctab;
+    return s.dtype == SSD_BF16 && s.P == kP && (s.N == 64 || s.N == 128) && offsets32;
 }
 
 bool bwd_states_mfma_ok(const ScanShape &s) { return bwd_mfma_ok(s) && s.Q == 64; }
 
-template <int Q, int N, bool kAdj>
+template <int Q, int N, bool kAdj, typename TX = bf16>
 void launch_bwd_states_t(const ScanShape &s, const void *xin, const void *bin, const float *dt,
                          const float *Acs, float *out, hipStream_t st) {
     const int64_t nb = s.B * s.T * s.H;
-    k_chunk_state_mfma<Q, N, false, kAdj><<<padded_grid(nb), 256, 0, st>>>(
-        (const bf16 *)xin, (const bf16 *)bin, dt, nullptr, const_cast<float *>(Acs), out, s.L,
-        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr, nullptr);
+    k_chunk_state_mfma<Q, N, false, kAdj, TX><<<padded_grid(nb), 256, 0, st>>>(
+        (const TX *)xin, (const bf16 *)bin, dt, nullptr, const_cast<float *>(Acs), out, s.L,
+        (int)s.H, (int)s.G, (int)s.T, nb, DtAct{}, nullptr, s.ctab);
 }
 
 void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
                             const float *dt, const float *Acs, float *out, bool adjoint,
-                            hipStream_t st) {
-#define SSD_BWDS(Q_, N_)                                                     \
-    do {                                                                     \
-        if (adjoint) launch_bwd_states_t<Q_, N_, true>(s, xin, bin, dt, Acs, out, st);  \
-        else launch_bwd_states_t<Q_, N_, false>(s, xin, bin, dt, Acs, out, st);         \
+                            hipStream_t st, bool x_f32) {
+#define SSD_BWDS(Q_, N_)                                                                   \
+    do {                                                                                   \
+        if (adjoint && x_f32)                                                              \
+            launch_bwd_states_t<Q_, N_, true, float>(s, xin, bin, dt, Acs, out, st);      \
+        else if (adjoint) launch_bwd_states_t<Q_, N_, true>(s, xin, bin, dt, Acs, out, st); \
+        else launch_bwd_states_t<Q_, N_, false>(s, xin, bin, dt, Acs, out, st);           \
     } while (0)
     if (s.N == 128) SSD_BWDS(64, 128);
     else SSD_BWDS(64, 64);

@@ -132,10 +132,16 @@ ScanShape bwd_shape(const ScanShape &s) {
     return b;
 }
 
-size_t bwd_workspace_bytes(const ScanShape &s) {
-    if (s.B == 0 || s.L == 0) return 0;
-    const ScanShape b = bwd_shape(s);
-    return acs_bytes(b) + 2 * states_bytes(b);
+// The same for a variable-length batch (s from check_varlen): slots of the
+// gradient's chunk for its sequences (total / Q + nseq covers every
+// sequence's chunks); the caller sets the chunk table.
+ScanShape bwd_varlen_shape(const ScanShape &s) {
+    ScanShape b = s;
+    b.ctab = nullptr;
+    b.sch = nullptr;
+    b.Q = ssd::bwd_mfma_ok(b) ? 64 : 32;
+    b.T = s.L / b.Q + s.NS;
+    return b;
 }
 
 // Chunk table and sequence table of a variable-length batch, after the rest.
@@ -218,7 +224,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 8; }
+int ssd_abi_version(void) { return 9; }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -274,25 +280,26 @@ ssd_status check_bwd(const ssd_scan_desc *d, ScanShape *s) {
     return SSD_OK;
 }
 
-// Workspace of ssd_scan_bwd_ex beyond the plain gradient's: the activated dt
-// (dt activation on); the ungated output, the dy reaching the scan and the
-// chunk-output stage's workspace (gate or norm on); the partial sums of
-// ddt_bias (any edges) and of dnorm_weight (norm on).
-size_t bwd_edges_bytes(const ScanShape &s, bool act, bool gate, bool dbias, bool norm) {
+// Workspace of a gradient beyond its core (Acs, entering states, end-state
+// derivatives at the gradient's chunking b): the activated dt (dt activation
+// on); the partial sums of dnorm_weight (norm on); the ungated output, the dy
+// reaching the scan and the chunk-output stage's workspace (gate or norm
+// on); the partial sums of ddt_bias (any edges).
+size_t bwd_core_bytes(const ScanShape &b) { return acs_bytes(b) + 2 * states_bytes(b); }
+
+size_t bwd_edges_bytes(const ScanShape &s, const ScanShape &b, bool act, bool gate, bool dbias,
+                       bool norm) {
     size_t n = 0;
     if (act) n += dt_eff_bytes(s);
     if (norm) n += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
     if (gate || norm) {
         const size_t elem = s.dtype == SSD_BF16 ? 2 : 4;
-        n += 2 * round_up((size_t)(s.B * s.L * s.H * s.P) * elem);
-        n += round_up(ssd::chunk_scan_ws_bytes(bwd_shape(s)));
+        const size_t nel = (size_t)(s.B * s.L * s.H * s.P);
+        n += 2 * round_up(nel * elem) + round_up(ssd::chunk_scan_ws_bytes(b));
+        if (s.dtype == SSD_BF16) n += round_up(nel * 4);  // the gated dy unrounded
     }
     if (dbias) n += round_up((size_t)(s.H * ssd::dt_bias_parts(s.B * s.L)) * 4);
     return n;
-}
-
-ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
-    return ssd_scan_bwd_ex_workspace_size(d, nullptr, bytes);
 }
 
 // The edges of a gradient call: as for the forward, and the norm's gradient
@@ -307,6 +314,124 @@ ssd_status read_bwd_edges(const ssd_edges *edges, const ScanShape &s, ssd::DtAct
     return SSD_OK;
 }
 
+// Inputs and outputs of a gradient call.
+struct BwdIn {
+    const void *x;
+    const float *dt, *A;
+    const void *B, *C;
+    const float *D, *init;
+    const void *dy;
+    const float *dfinal;
+};
+struct BwdOut {
+    void *dx;
+    float *ddt, *dA, *dB, *dC, *dD, *dinit;
+    void *dz;
+    float *ddt_bias, *dnorm_weight;
+};
+
+// Nothing to differentiate (no tokens): dA = dD = ddt_bias = dnorm_weight = 0
+// and dinit = dfinal for every row (rows states).
+ssd_status bwd_empty(const ScanShape &s, int64_t rows, const BwdIn &in, const BwdOut &o,
+                     hipStream_t hs) {
+    ssd_status st = check_ptrs({o.dA}, {o.dD, o.dinit, in.dfinal, o.ddt_bias, o.dnorm_weight});
+    if (st != SSD_OK) return st;
+    ssd::launch_copy_or_zero(o.dA, nullptr, s.H, hs);
+    if (o.dD) ssd::launch_copy_or_zero(o.dD, nullptr, s.H, hs);
+    if (o.ddt_bias) ssd::launch_copy_or_zero(o.ddt_bias, nullptr, s.H, hs);
+    if (o.dnorm_weight) ssd::launch_copy_or_zero(o.dnorm_weight, nullptr, s.H * s.P, hs);
+    if (o.dinit) ssd::launch_copy_or_zero(o.dinit, in.dfinal, rows * s.H * s.P * s.N, hs);
+    return after_launch();
+}
+
+// The gradient after the argument checks: s the call's shape, b the
+// gradient's chunking (with the chunk table of a variable-length batch), ws
+// at least bwd_core_bytes(b) + bwd_edges_bytes(...) bytes.
+void run_bwd(const ScanShape &s, const ScanShape &b, const ssd::DtAct &act, const void *z,
+             const NormEdge &nm, bool edges_given, const BwdIn &in, const BwdOut &o, char *ws,
+             hipStream_t hs) {
+    const bool gate = z != nullptr, actv = act_active(act), norm = nm.w != nullptr;
+    float *Acs = reinterpret_cast<float *>(ws);
+    float *Hst = reinterpret_cast<float *>(ws + acs_bytes(b));
+    float *Est = reinterpret_cast<float *>(ws + acs_bytes(b) + states_bytes(b));
+    char *extra = ws + bwd_core_bytes(b);
+    float *dt_eff = nullptr;
+    if (actv) {
+        dt_eff = reinterpret_cast<float *>(extra);
+        extra += dt_eff_bytes(s);
+    }
+    float *npart = nullptr;
+    if (norm) {
+        npart = reinterpret_cast<float *>(extra);
+        extra += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
+    }
+    void *yun = nullptr, *dys = nullptr, *cbws = nullptr;
+    float *dys32 = nullptr;  // bf16 calls: the gated dy in fp32 for the state derivatives
+    const int64_t nel = s.B * s.L * s.H * s.P;
+    if (gate || norm) {
+        const size_t eb = round_up((size_t)nel * (s.dtype == SSD_BF16 ? 2 : 4));
+        yun = extra;
+        dys = extra + eb;
+        cbws = extra + 2 * eb;
+        extra += 2 * eb + round_up(ssd::chunk_scan_ws_bytes(b));
+        if (s.dtype == SSD_BF16) {
+            dys32 = reinterpret_cast<float *>(extra);
+            extra += round_up((size_t)nel * 4);
+        }
+    }
+    float *part = (edges_given && o.ddt_bias) ? reinterpret_cast<float *>(extra) : nullptr;
+    // outputs accumulated with atomics start from zero (a fill kernel, so the
+    // call can be captured in a HIP graph)
+    const int64_t bcn = s.B * s.L * s.G * s.N;
+    ssd::launch_copy_or_zero(o.dB, nullptr, bcn, hs);
+    ssd::launch_copy_or_zero(o.dC, nullptr, bcn, hs);
+    ssd::launch_copy_or_zero(o.dA, nullptr, s.H, hs);
+    if (o.dD) ssd::launch_copy_or_zero(o.dD, nullptr, s.H, hs);
+    // the forward's Acs (and the activated dt) and entering states at the
+    // gradient's chunks
+    const bool mm = ssd::bwd_states_mfma_ok(b);
+    ssd::launch_chunk_cumsum(b, in.dt, in.A, Acs, hs, act, dt_eff);
+    const float *dtu = dt_eff ? dt_eff : in.dt;
+    if (mm) ssd::launch_bwd_states_mfma(b, in.x, in.B, dtu, Acs, Hst, false, hs);
+    else ssd::launch_chunk_state(b, in.x, in.B, dtu, Acs, Hst, hs);
+    ssd::launch_state_passing(b, Hst, Acs, in.init, nullptr, hs);
+    // gate / norm: the ungated output from the chunk-output stage on those
+    // states, then the gradient reaching the scan output, dz and dnorm_weight
+    const void *dyu = in.dy;
+    if (gate || norm) {
+        ssd::launch_chunk_cb(b, in.B, in.C, cbws, hs);
+        ssd::launch_chunk_scan(b, in.x, dtu, in.B, in.C, in.D, Acs, Hst, cbws, yun, hs);
+        if (norm)
+            ssd::launch_norm_gate_bwd(in.dy, yun, z, nm.w, nm.eps, s.B * s.L, s.H, s.P, nm.groups,
+                                      dys, o.dz, npart, o.dnorm_weight, s.dtype, hs, dys32);
+        else
+            ssd::launch_gate_bwd(in.dy, yun, z, dys, o.dz, nel, s.dtype, hs, dys32);
+        dyu = dys;
+    }
+    // derivatives with respect to every chunk's end state, and the initial
+    // state's: from the unrounded gated dy when there is one (the bf16 copy
+    // would put one more rounding into sums that can cancel)
+    if (mm) {
+        if (dys32) ssd::launch_bwd_states_mfma(b, dys32, in.C, nullptr, Acs, Est, true, hs, true);
+        else ssd::launch_bwd_states_mfma(b, dyu, in.C, nullptr, Acs, Est, true, hs);
+    } else {
+        ssd::launch_chunk_dstate(b, dys32 ? static_cast<const void *>(dys32) : dyu, in.C, Acs,
+                                 Est, hs, dys32 != nullptr);
+    }
+    ssd::launch_state_passing_rev(b, Est, Acs, in.dfinal, o.dinit, hs);
+    // per-chunk gradients
+    ssd::launch_chunk_bwd(b, in.x, dtu, in.A, in.B, in.C, in.D, Acs, Hst, Est, dyu, o.dx, o.ddt,
+                          o.dB, o.dC, o.dA, o.dD, hs);
+    // through the dt activation, and the bias's gradient
+    if (actv || part)
+        ssd::launch_dt_act_bwd(o.ddt, in.dt, act, s.B * s.L, s.H, part, part ? o.ddt_bias : nullptr,
+                               hs);
+}
+
+ssd_status ssd_scan_bwd_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
+    return ssd_scan_bwd_ex_workspace_size(d, nullptr, bytes);
+}
+
 ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edges *edges,
                                           size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -318,10 +443,13 @@ ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edge
     NormEdge nm;
     st = read_bwd_edges(edges, s, &act, &z, &nm);
     if (st != SSD_OK) return st;
-    *bytes = (s.B == 0 || s.L == 0)
-                 ? 0
-                 : bwd_workspace_bytes(s) + bwd_edges_bytes(s, act_active(act), z != nullptr,
-                                                            edges != nullptr, nm.w != nullptr);
+    if (s.B == 0 || s.L == 0) {
+        *bytes = 0;
+        return SSD_OK;
+    }
+    const ScanShape b = bwd_shape(s);
+    *bytes = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
+                                                 edges != nullptr, nm.w != nullptr);
     return SSD_OK;
 }
 
@@ -350,91 +478,22 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     NormEdge nm;
     st = read_bwd_edges(edges, s, &act, &z, &nm);
     if (st != SSD_OK) return st;
-    if (!edges) ddt_bias = nullptr;
-    if (!nm.w) dnorm_weight = nullptr;
+    const BwdIn in{x, dt, A, B, C, D, init_state, dy, dfinal};
+    const BwdOut o{dx, ddt, dA, dB, dC, dD, dinit, z ? dz : nullptr,
+                   edges ? ddt_bias : nullptr, nm.w ? dnorm_weight : nullptr};
     hipStream_t hs = as_stream(stream);
-    if (s.B == 0 || s.L == 0) {  // no tokens: dA = dD = ddt_bias = dnorm_weight = 0, dinit = dfinal
-        st = check_ptrs({dA}, {dD, dinit, dfinal, ddt_bias, dnorm_weight});
-        if (st != SSD_OK) return st;
-        ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
-        if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
-        if (ddt_bias) ssd::launch_copy_or_zero(ddt_bias, nullptr, s.H, hs);
-        if (dnorm_weight) ssd::launch_copy_or_zero(dnorm_weight, nullptr, s.H * s.P, hs);
-        if (dinit) ssd::launch_copy_or_zero(dinit, dfinal, s.B * s.H * s.P * s.N, hs);
-        return after_launch();
-    }
-    const bool gate = z != nullptr, actv = act_active(act), norm = nm.w != nullptr;
-    if (gate && !dz) return SSD_ERR_NULL_PTR;
+    if (s.B == 0 || s.L == 0) return bwd_empty(s, s.B, in, o, hs);
+    if (z && !dz) return SSD_ERR_NULL_PTR;
     st = check_ptrs({x, dt, A, B, C, dy, dx, ddt, dA, dB, dC},
-                    {D, init_state, dfinal, dD, dinit, workspace, z, dz, act.bias, ddt_bias,
-                     nm.w, dnorm_weight});
+                    {D, init_state, dfinal, dD, dinit, workspace, z, o.dz, act.bias, o.ddt_bias,
+                     nm.w, o.dnorm_weight});
     if (st != SSD_OK) return st;
-    const size_t base = bwd_workspace_bytes(s);
-    if (ws_bytes < base + bwd_edges_bytes(s, actv, gate, edges != nullptr, norm))
-        return SSD_ERR_WORKSPACE;
-    if (!workspace) return SSD_ERR_NULL_PTR;
     const ScanShape b = bwd_shape(s);
-    char *ws = static_cast<char *>(workspace);
-    float *Acs = reinterpret_cast<float *>(ws);
-    float *Hst = reinterpret_cast<float *>(ws + acs_bytes(b));
-    float *Est = reinterpret_cast<float *>(ws + acs_bytes(b) + states_bytes(b));
-    char *extra = ws + base;
-    float *dt_eff = nullptr;
-    if (actv) {
-        dt_eff = reinterpret_cast<float *>(extra);
-        extra += dt_eff_bytes(s);
-    }
-    float *npart = nullptr;
-    if (norm) {
-        npart = reinterpret_cast<float *>(extra);
-        extra += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
-    }
-    void *yun = nullptr, *dys = nullptr, *cbws = nullptr;
-    const int64_t nel = s.B * s.L * s.H * s.P;
-    if (gate || norm) {
-        const size_t eb = round_up((size_t)nel * (s.dtype == SSD_BF16 ? 2 : 4));
-        yun = extra;
-        dys = extra + eb;
-        cbws = extra + 2 * eb;
-        extra += 2 * eb + round_up(ssd::chunk_scan_ws_bytes(b));
-    }
-    float *part = ddt_bias ? reinterpret_cast<float *>(extra) : nullptr;
-    // outputs accumulated with atomics start from zero (a fill kernel, so the
-    // call can be captured in a HIP graph)
-    const int64_t bcn = s.B * s.L * s.G * s.N;
-    ssd::launch_copy_or_zero(dB, nullptr, bcn, hs);
-    ssd::launch_copy_or_zero(dC, nullptr, bcn, hs);
-    ssd::launch_copy_or_zero(dA, nullptr, s.H, hs);
-    if (dD) ssd::launch_copy_or_zero(dD, nullptr, s.H, hs);
-    // the forward's Acs (and the activated dt) and entering states at the
-    // gradient's chunks
-    const bool mm = ssd::bwd_states_mfma_ok(b);
-    ssd::launch_chunk_cumsum(b, dt, A, Acs, hs, act, dt_eff);
-    const float *dtu = dt_eff ? dt_eff : dt;
-    if (mm) ssd::launch_bwd_states_mfma(b, x, B, dtu, Acs, Hst, false, hs);
-    else ssd::launch_chunk_state(b, x, B, dtu, Acs, Hst, hs);
-    ssd::launch_state_passing(b, Hst, Acs, init_state, nullptr, hs);
-    // gate / norm: the ungated output from the chunk-output stage on those
-    // states, then the gradient reaching the scan output, dz and dnorm_weight
-    const void *dyu = dy;
-    if (gate || norm) {
-        ssd::launch_chunk_cb(b, B, C, cbws, hs);
-        ssd::launch_chunk_scan(b, x, dtu, B, C, D, Acs, Hst, cbws, yun, hs);
-        if (norm)
-            ssd::launch_norm_gate_bwd(dy, yun, z, nm.w, nm.eps, s.B * s.L, s.H, s.P, nm.groups,
-                                      dys, dz, npart, dnorm_weight, s.dtype, hs);
-        else
-            ssd::launch_gate_bwd(dy, yun, z, dys, dz, nel, s.dtype, hs);
-        dyu = dys;
-    }
-    // derivatives with respect to every chunk's end state, and the initial state's
-    if (mm) ssd::launch_bwd_states_mfma(b, dyu, C, nullptr, Acs, Est, true, hs);
-    else ssd::launch_chunk_dstate(b, dyu, C, Acs, Est, hs);
-    ssd::launch_state_passing_rev(b, Est, Acs, dfinal, dinit, hs);
-    // per-chunk gradients
-    ssd::launch_chunk_bwd(b, x, dtu, A, B, C, D, Acs, Hst, Est, dyu, dx, ddt, dB, dC, dA, dD, hs);
-    // through the dt activation, and the bias's gradient
-    if (actv || ddt_bias) ssd::launch_dt_act_bwd(ddt, dt, act, s.B * s.L, s.H, part, ddt_bias, hs);
+    const size_t need = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
+                                                            edges != nullptr, nm.w != nullptr);
+    if (ws_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL_PTR;
+    run_bwd(s, b, act, z, nm, edges != nullptr, in, o, static_cast<char *>(workspace), hs);
     return after_launch();
 }
 
@@ -486,6 +545,78 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
     s.sch = sch;
     run_scan(s, act, z, x, dt, A, B, C, D, init_states, y, final_states, ws, hs);
     if (nm.w) ssd::launch_gated_norm(y, nm.w, nm.eps, s.L, s.H, s.P, nm.groups, s.dtype, hs);
+    return after_launch();
+}
+
+// The gradient of a ragged batch: checks of ssd_scan_fwd_varlen, the
+// gradient's own chunking with its chunk table.
+ssd_status check_bwd_varlen(const ssd_varlen_desc *d, ScanShape *s, ScanShape *b) {
+    ssd_status st = check_varlen(d, s);
+    if (st != SSD_OK) return st;
+    *b = bwd_varlen_shape(*s);
+    if (b->T > kMaxBlocks || (b->T > 0 && s->H > kMaxBlocks / b->T)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status ssd_scan_bwd_varlen_workspace_size(const ssd_varlen_desc *d, const ssd_edges *edges,
+                                              size_t *bytes) {
+    if (!bytes) return SSD_ERR_NULL_PTR;
+    ScanShape s, b;
+    ssd_status st = check_bwd_varlen(d, &s, &b);
+    if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    NormEdge nm;
+    st = read_bwd_edges(edges, s, &act, &z, &nm);
+    if (st != SSD_OK) return st;
+    if (s.NS == 0 || s.L == 0) {
+        *bytes = 0;
+        return SSD_OK;
+    }
+    *bytes = bwd_core_bytes(b) +
+             bwd_edges_bytes(s, b, act_active(act), z != nullptr, edges != nullptr,
+                             nm.w != nullptr) +
+             varlen_table_bytes(b);
+    return SSD_OK;
+}
+
+ssd_status ssd_scan_bwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
+                               const int32_t *cu_seqlens, const void *x, const float *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *init_states, const void *dy,
+                               const float *dfinal_states, void *dx, float *ddt, float *dA,
+                               float *dB, float *dC, float *dD, float *dinit_states, void *dz,
+                               float *ddt_bias, float *dnorm_weight, void *workspace,
+                               size_t ws_bytes, void *stream) {
+    ScanShape s, b;
+    ssd_status st = check_bwd_varlen(d, &s, &b);
+    if (st != SSD_OK) return st;
+    ssd::DtAct act;
+    const void *z;
+    NormEdge nm;
+    st = read_bwd_edges(edges, s, &act, &z, &nm);
+    if (st != SSD_OK) return st;
+    const BwdIn in{x, dt, A, B, C, D, init_states, dy, dfinal_states};
+    const BwdOut o{dx, ddt, dA, dB, dC, dD, dinit_states, z ? dz : nullptr,
+                   edges ? ddt_bias : nullptr, nm.w ? dnorm_weight : nullptr};
+    hipStream_t hs = as_stream(stream);
+    if (s.NS == 0 || s.L == 0) return bwd_empty(s, s.NS, in, o, hs);
+    if (z && !dz) return SSD_ERR_NULL_PTR;
+    st = check_ptrs({cu_seqlens, x, dt, A, B, C, dy, dx, ddt, dA, dB, dC},
+                    {D, init_states, dfinal_states, dD, dinit_states, workspace, z, o.dz,
+                     act.bias, o.ddt_bias, nm.w, o.dnorm_weight});
+    if (st != SSD_OK) return st;
+    const size_t base = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
+                                                            edges != nullptr, nm.w != nullptr);
+    if (ws_bytes < base + varlen_table_bytes(b)) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL_PTR;
+    char *ws = static_cast<char *>(workspace);
+    int2 *ctab = reinterpret_cast<int2 *>(ws + base);
+    int2 *sch = reinterpret_cast<int2 *>(ws + base + round_up((size_t)b.T * 8));
+    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, b.Q, b.T, ctab, sch, hs);
+    b.ctab = ctab;
+    b.sch = sch;
+    run_bwd(s, b, act, z, nm, edges != nullptr, in, o, ws, hs);
     return after_launch();
 }
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 8
+    assert L.ssd_abi_version() == 9
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -451,3 +451,31 @@ def test_bwd_ex_workspace_and_errors(L):
                              None) == ALIGN
     assert L.ssd_scan_bwd_ex(ctypes.byref(d), ctypes.byref(en), *args, P16, P16, P16, P16, need - 1,
                              None) == WS
+
+
+def test_bwd_varlen_workspace_and_errors(L):
+    """ssd_scan_bwd_varlen: the gradient's core at 64-token slots (total / 64
+    + nseq of them) plus the chunk and sequence tables; nothing for an empty
+    batch; the same edge and pointer checks as ssd_scan_bwd_ex."""
+    d = vdesc()   # 3 sequences, 700 tokens, 8 heads, headdim 64, dstate 128, bf16
+    n = ctypes.c_size_t(0)
+    assert L.ssd_scan_bwd_varlen_workspace_size(ctypes.byref(d), None, ctypes.byref(n)) == OK
+    slots = 700 // 64 + 3
+    core = r256(8 * 700 * 4) + 2 * r256(slots * 8 * 64 * 128 * 4)
+    assert n.value == core + r256(slots * 8) + r256(3 * 8)
+    assert L.ssd_scan_bwd_varlen_workspace_size(ctypes.byref(vdesc(nseq=0, total=0)), None,
+                                                ctypes.byref(n)) == OK and n.value == 0
+    eg = edges(dt_bias=P16, dt_softplus=1, z=P16)
+    assert L.ssd_scan_bwd_varlen_workspace_size(ctypes.byref(d), ctypes.byref(eg),
+                                                ctypes.byref(n)) == OK
+    need = n.value
+    args = [P16] * 17  # cu x dt A B C D init dy dfinal dx ddt dA dB dC dD dinit
+    assert L.ssd_scan_bwd_varlen(ctypes.byref(d), ctypes.byref(eg), *args, None, P16, P16, P16,
+                                 need, None) == NULL                # gate without dz
+    for which in range(17):
+        a = list(args)
+        a[which] = P_MIS
+        assert L.ssd_scan_bwd_varlen(ctypes.byref(d), ctypes.byref(eg), *a, P16, P16, P16, P16,
+                                     need, None) == ALIGN, which
+    assert L.ssd_scan_bwd_varlen(ctypes.byref(d), ctypes.byref(eg), *args, P16, P16, P16, P16,
+                                 need - 1, None) == WS

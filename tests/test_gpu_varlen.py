@@ -138,3 +138,79 @@ def test_graph_replay_with_new_lengths():
         call(ye, fe)
         torch.cuda.synchronize()
         assert torch.equal(y, ye) and torch.equal(fin, fe), lens
+
+
+BWD_CASES = {
+    # lengths cross the gradient's 64-token chunks: 63 / 64 / 65, one token, empty
+    "bwd_mfma": ([64, 63, 0, 65, 1, 200, 130], 4, 64, 128, 2, "bf16"),
+    "bwd_mfma_n64": ([5, 0, 129, 64], 6, 64, 64, 2, "bf16"),
+    "bwd_generic_f32": ([0, 17, 33, 32, 90, 1], 4, 16, 16, 2, "f32"),
+}
+
+
+def _ragged_grads(name, seed):
+    lengths, H, P, N, G, dt_ = BWD_CASES[name]
+    vin = synth.varlen_inputs(lengths, H, P, N, G, dt_, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    io = torch.bfloat16 if dt_ == "bf16" else torch.float32
+    dy = torch.from_numpy(rng.standard_normal(tuple(vin["x"].shape), dtype=np.float32)).to(io)
+    dfin = torch.from_numpy(rng.standard_normal(tuple(vin["init"].shape), dtype=np.float32))
+    return vin, dy, dfin, io
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_varlen_bwd_vs_oracle(name):
+    """ssd_scan_bwd_varlen against the per-sequence fp64 adjoint (itself
+    pinned by finite differences of the ragged forward oracle)."""
+    announce(f"varlen bwd {name}")
+    vin, dy, dfin, io = _ragged_grads(name, seed=81)
+    d = _dev(vin)
+    g = ssd.scan_bwd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["cu_seqlens"],
+                            dy.to(DEV), d["D"], chunk=64, init_states=d["init"],
+                            dfinal_states=dfin.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.scan_vjp_varlen(vin["cu_seqlens"], vin["x"], vin["dt"], vin["A"], vin["B"],
+                                 vin["C"], vin["D"], vin["init"], dy=dy, dfinal=dfin)
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit"):
+        e = rel_err(f64(g[k]), ref[k])
+        assert e <= TOL[io], (k, e)
+
+
+@pytest.mark.parametrize("name", ["bwd_mfma", "bwd_generic_f32"])
+def test_varlen_bwd_edges_vs_oracle(name):
+    """The ragged gradient with every edge (dt bias, softplus, clamp, gate):
+    each sequence against oracle.scan_vjp_edges on its own tokens; dt_bias's
+    gradient summed over the sequences."""
+    announce(f"varlen bwd edges {name}")
+    vin, dy, dfin, io = _ragged_grads(name, seed=83)
+    lim = (1e-3, 0.05)
+    d = _dev(vin)
+    g = ssd.scan_bwd_varlen(d["x"], d["dt_raw"], d["A"], d["B"], d["C"], d["cu_seqlens"],
+                            dy.to(DEV), d["D"], chunk=64, init_states=d["init"],
+                            dfinal_states=dfin.to(DEV), dt_bias=d["dt_bias"], dt_softplus=True,
+                            dt_limit=lim, z=d["gate"])
+    torch.cuda.synchronize()
+    cu = vin["cu_seqlens"].numpy()
+    H = vin["A"].shape[0]
+    ref = {k: np.zeros(tuple(vin[s].shape)) for k, s in
+           (("dx", "x"), ("ddt", "dt"), ("dB", "B"), ("dC", "C"), ("dz", "x"),
+            ("dinit", "init"))}
+    ref.update(dA=np.zeros(H), dD=np.zeros(H), ddt_bias=np.zeros(H))
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            ref["dinit"][s] = dfin[s].double().numpy()
+            continue
+        r = oracle.scan_vjp_edges(vin["x"][None, a:b], vin["dt_raw"][None, a:b], vin["A"],
+                                  vin["B"][None, a:b], vin["C"][None, a:b], vin["D"],
+                                  vin["init"][s:s + 1], dy=dy[None, a:b], dfinal=dfin[s:s + 1],
+                                  dt_bias=vin["dt_bias"], dt_softplus=True, dt_limit=lim,
+                                  z=vin["gate"][None, a:b])
+        for k in ("dx", "ddt", "dB", "dC", "dz"):
+            ref[k][a:b] = r[k][0]
+        ref["dinit"][s] = r["dinit"][0]
+        for k in ("dA", "dD", "ddt_bias"):
+            ref[k] += r[k]
+    for k in ref:
+        e = rel_err(f64(g[k]), ref[k])
+        assert e <= TOL[io], (k, e)
