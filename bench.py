@@ -282,6 +282,20 @@ def main():
                 "fwd_plus_bwd_us": round((f_ms + b_ms) * 1e3, 2),
                 "bwd_tokens_per_s": round(bB * bL / (b_ms * 1e-3), 1)}
     grad = {"m2p7b_4096": bwd_case(spec, inp)}
+    # the same gradient through the fused edges (dt bias + softplus + clamp,
+    # gate), and with the gated RMSNorm as well
+    def bwd_edges_us(norm):
+        bd = {k: (None if v is None else v.to(dev).contiguous()) for k, v in einp.items()}
+        gdy = torch.randn_like(bd["x"].float()).to(bd["x"].dtype)
+        nw = torch.ones(H * P, dtype=torch.float32, device=dev) if norm else None
+        dfin = torch.randn((Bt, H, P, N), dtype=torch.float32, device=dev)
+        def run():
+            ssd.scan_bwd(bd["x"], bd["dt_raw"], bd["A"], bd["B"], bd["C"], gdy, bd["D"],
+                         bd["init"], dfin, chunk=Q, dt_bias=bd["dt_bias"], dt_softplus=True,
+                         dt_limit=(1e-3, 0.1), z=bd["gate"], norm_weight=nw, norm_eps=1e-5)
+        return round(time_launches(torch, run, 10) * 1e3, 2)
+    grad["m2p7b_4096"]["bwd_edges_us"] = bwd_edges_us(False)
+    grad["m2p7b_4096"]["bwd_edges_gated_rmsnorm_us"] = bwd_edges_us(True)
     s130 = synth.custom_spec(1, 512, 24, 64, 128, 1, chunk=256, dtype="bf16", dt_rule="ranged",
                              init="zero", seed=2, name="m130m_512")
     grad["m130m_512"] = bwd_case(s130, synth.scan_inputs(s130))

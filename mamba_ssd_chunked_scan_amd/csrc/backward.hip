@@ -1022,13 +1022,12 @@ k_dt_act_bwd(float *__restrict__ ddt, const float *__restrict__ dt_raw, DtAct ac
 }
 
 // The gated RMSNorm with the gate under it, backward.  Block (range, k)
-// takes tokens [range kNormTok, +kNormTok) of norm group k: CG channels as
+// takes tokens [range tr, +tr) of norm group k: CG channels as
 // 8-value vectors, vector u of thread t at channel 8 (t + 256 u).  Per token,
 // with v the gated output (v = y without a gate), r = 1 / sqrt(mean(v^2) +
 // eps) and S = sum(dout w v) (two block sums, fixed order):
 //   dv = r (w dout - v r^2 S / CG),  dys = dv silu(z),  dz = dv y silu'(z);
 // the thread's sum over its tokens of dout v r goes to part[range][k CG + c].
-constexpr int kNormTok = 16;
 constexpr int kNormVec = 4;  // vectors per thread: CG <= 8 * 256 * kNormVec
 
 template <typename T>
@@ -1036,11 +1035,11 @@ __global__ void __launch_bounds__(256)
 k_norm_gate_bwd(const T *__restrict__ dout, const T *__restrict__ y, const T *__restrict__ z,
                 const float *__restrict__ w, float eps, T *__restrict__ dys, T *__restrict__ dz,
                 float *__restrict__ part, int64_t ntok, int64_t HP, int CG,
-                float *__restrict__ dys32) {
+                float *__restrict__ dys32, int tr) {
     __shared__ float red[2][4];
     const int tid = threadIdx.x, k = blockIdx.y;
-    const int64_t t0 = (int64_t)blockIdx.x * kNormTok;
-    const int64_t t1 = t0 + kNormTok < ntok ? t0 + kNormTok : ntok;
+    const int64_t t0 = (int64_t)blockIdx.x * tr;
+    const int64_t t1 = t0 + tr < ntok ? t0 + tr : ntok;
     float dw[kNormVec][8];
 #pragma unroll
     for (int u = 0; u < kNormVec; ++u)
@@ -1125,14 +1124,20 @@ k_norm_gate_bwd(const T *__restrict__ dout, const T *__restrict__ y, const T *__
     }
 }
 
-// out[c] = the rows of part [rows][n] summed in order, one thread per column.
-__global__ void k_sum_cols(const float *__restrict__ part, int64_t rows, int64_t n,
-                           float *__restrict__ out) {
-    const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+// out[y][c] = rows [y R, (y+1) R) of part [rows][n] summed in order: one
+// thread per column, block (column block, y).
+constexpr int kSumRows = 64;
+__global__ void __launch_bounds__(256)
+k_sum_cols(const float *__restrict__ part, int64_t rows, int64_t n, int64_t R,
+           float *__restrict__ out) {
+    const int64_t c = blockIdx.x * 256LL + threadIdx.x;
     if (c >= n) return;
+    const int64_t r0 = (int64_t)blockIdx.y * R;
+    const int64_t r1 = r0 + R < rows ? r0 + R : rows;
     float s = 0.f;
-    for (int64_t r = 0; r < rows; ++r) s += part[r * n + c];
-    out[c] = s;
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r) s += part[r * n + c];
+    out[(int64_t)blockIdx.y * n + c] = s;
 }
 
 // dbias[h] = the parts of head h summed in order.
@@ -1237,26 +1242,48 @@ bool norm_bwd_ok(int64_t H, int64_t P, int64_t NG) {
     return P % 8 == 0 && (H / NG) * P <= 8 * 256 * kNormVec;
 }
 
-int64_t norm_bwd_parts(int64_t ntok) { return (ntok + kNormTok - 1) / kNormTok; }
+// Tokens per block of the norm's gradient: about 2048 blocks over the
+// (token, group) pairs, 1 to 64 tokens each (more tokens per block, fewer
+// partial sums of the weight's gradient to add up).
+int64_t norm_bwd_rows(int64_t ntok, int64_t NG) {
+    const int64_t tr = (ntok * NG + 2047) / 2048;
+    return tr < 1 ? 1 : (tr > 64 ? 64 : tr);
+}
+
+// Rows of partial sums of the weight's gradient: one per block range, then
+// one per kSumRows of those (the first level of their sum).
+int64_t norm_bwd_parts(int64_t ntok, int64_t NG) {
+    const int64_t tr = norm_bwd_rows(ntok, NG);
+    const int64_t nr = (ntok + tr - 1) / tr;
+    return nr + (nr + kSumRows - 1) / kSumRows;
+}
 
 void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const float *w,
                           float eps, int64_t ntok, int64_t H, int64_t P, int64_t NG, void *dys,
                           void *dz, float *part, float *dw, int dtype, hipStream_t st,
                           float *dys32) {
-    const int64_t nr = norm_bwd_parts(ntok);
+    const int tr = (int)norm_bwd_rows(ntok, NG);
+    const int64_t nr = (ntok + tr - 1) / tr;
     if (nr <= 0) return;
     const int CG = (int)((H / NG) * P);
     const dim3 grid((unsigned)nr, (unsigned)NG);
     if (dtype == SSD_BF16)
         k_norm_gate_bwd<bf16><<<grid, 256, 0, st>>>((const bf16 *)dout, (const bf16 *)y,
                                                     (const bf16 *)z, w, eps, (bf16 *)dys,
-                                                    (bf16 *)dz, part, ntok, H * P, CG, dys32);
+                                                    (bf16 *)dz, part, ntok, H * P, CG, dys32,
+                                                    tr);
     else
         k_norm_gate_bwd<float><<<grid, 256, 0, st>>>((const float *)dout, (const float *)y,
                                                      (const float *)z, w, eps, (float *)dys,
                                                      (float *)dz, part, ntok, H * P, CG,
-                                                     dys32);
-    if (dw) k_sum_cols<<<(unsigned)((H * P + 255) / 256), 256, 0, st>>>(part, nr, H * P, dw);
+                                                     dys32, tr);
+    if (dw) {  // two levels: kSumRows rows at a time, then those sums
+        const int64_t n2 = (nr + kSumRows - 1) / kSumRows;
+        float *part2 = part + nr * H * P;
+        const unsigned cb = (unsigned)((H * P + 255) / 256);
+        k_sum_cols<<<dim3(cb, (unsigned)n2), 256, 0, st>>>(part, nr, H * P, kSumRows, part2);
+        k_sum_cols<<<dim3(cb, 1), 256, 0, st>>>(part2, n2, H * P, n2, dw);
+    }
 }
 
 }  // namespace ssd

@@ -105,11 +105,11 @@ void launch_dt_act_bwd(float *ddt, const float *dt_raw, const DtAct &act, int64_
 
 // Gradient through the gated RMSNorm (and the gate under it when z is
 // non-null): dys gets the gradient reaching the scan output, dz the gate's,
-// dw (may be null) the weight's, through part (norm_bwd_parts(ntok) x H*P
-// floats).  Shapes norm_bwd_ok accepts: headdim a multiple of 8, groups of
-// at most 8192 channels.
+// dw (may be null) the weight's, through part (norm_bwd_parts(ntok, NG) x
+// H*P floats).  Shapes norm_bwd_ok accepts: headdim a multiple of 8, groups
+// of at most 8192 channels.
 bool norm_bwd_ok(int64_t H, int64_t P, int64_t NG);
-int64_t norm_bwd_parts(int64_t ntok);
+int64_t norm_bwd_parts(int64_t ntok, int64_t NG);
 void launch_norm_gate_bwd(const void *dout, const void *y, const void *z, const float *w,
                           float eps, int64_t ntok, int64_t H, int64_t P, int64_t NG, void *dys,
                           void *dz, float *part, float *dw, int dtype, hipStream_t st,

@@ -288,10 +288,12 @@ ssd_status check_bwd(const ssd_scan_desc *d, ScanShape *s) {
 size_t bwd_core_bytes(const ScanShape &b) { return acs_bytes(b) + 2 * states_bytes(b); }
 
 size_t bwd_edges_bytes(const ScanShape &s, const ScanShape &b, bool act, bool gate, bool dbias,
-                       bool norm) {
+                       int64_t norm_groups) {
+    const bool norm = norm_groups > 0;
     size_t n = 0;
     if (act) n += dt_eff_bytes(s);
-    if (norm) n += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
+    if (norm)
+        n += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L, norm_groups) * s.H * s.P) * 4);
     if (gate || norm) {
         const size_t elem = s.dtype == SSD_BF16 ? 2 : 4;
         const size_t nel = (size_t)(s.B * s.L * s.H * s.P);
@@ -363,7 +365,7 @@ void run_bwd(const ScanShape &s, const ScanShape &b, const ssd::DtAct &act, cons
     float *npart = nullptr;
     if (norm) {
         npart = reinterpret_cast<float *>(extra);
-        extra += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L) * s.H * s.P) * 4);
+        extra += round_up((size_t)(ssd::norm_bwd_parts(s.B * s.L, nm.groups) * s.H * s.P) * 4);
     }
     void *yun = nullptr, *dys = nullptr, *cbws = nullptr;
     float *dys32 = nullptr;  // bf16 calls: the gated dy in fp32 for the state derivatives
@@ -449,7 +451,7 @@ ssd_status ssd_scan_bwd_ex_workspace_size(const ssd_scan_desc *d, const ssd_edge
     }
     const ScanShape b = bwd_shape(s);
     *bytes = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
-                                                 edges != nullptr, nm.w != nullptr);
+                                                 edges != nullptr, nm.w ? nm.groups : 0);
     return SSD_OK;
 }
 
@@ -490,7 +492,7 @@ ssd_status ssd_scan_bwd_ex(const ssd_scan_desc *d, const ssd_edges *edges, const
     if (st != SSD_OK) return st;
     const ScanShape b = bwd_shape(s);
     const size_t need = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
-                                                            edges != nullptr, nm.w != nullptr);
+                                                            edges != nullptr, nm.w ? nm.groups : 0);
     if (ws_bytes < need) return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
     run_bwd(s, b, act, z, nm, edges != nullptr, in, o, static_cast<char *>(workspace), hs);
@@ -575,7 +577,7 @@ ssd_status ssd_scan_bwd_varlen_workspace_size(const ssd_varlen_desc *d, const ss
     }
     *bytes = bwd_core_bytes(b) +
              bwd_edges_bytes(s, b, act_active(act), z != nullptr, edges != nullptr,
-                             nm.w != nullptr) +
+                             nm.w ? nm.groups : 0) +
              varlen_table_bytes(b);
     return SSD_OK;
 }
@@ -607,7 +609,7 @@ ssd_status ssd_scan_bwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
                      act.bias, o.ddt_bias, nm.w, o.dnorm_weight});
     if (st != SSD_OK) return st;
     const size_t base = bwd_core_bytes(b) + bwd_edges_bytes(s, b, act_active(act), z != nullptr,
-                                                            edges != nullptr, nm.w != nullptr);
+                                                            edges != nullptr, nm.w ? nm.groups : 0);
     if (ws_bytes < base + varlen_table_bytes(b)) return SSD_ERR_WORKSPACE;
     if (!workspace) return SSD_ERR_NULL_PTR;
     char *ws = static_cast<char *>(workspace);

@@ -436,7 +436,10 @@ def test_bwd_ex_workspace_and_errors(L):
     n3 = ctypes.c_size_t(0)
     assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(d), ctypes.byref(en),
                                             ctypes.byref(n3)) == OK
-    assert n3.value == n2.value + r256(32 * 8 * 64 * 4)   # 512 / 16 token ranges x 512 channels
+    # 512 tokens x 2 groups over ~2048 blocks: one token per block, so 512
+    # ranges of partial sums over the 512 channels, plus 512 / 64 rows of
+    # their first-level sums
+    assert n3.value == n2.value + r256((512 + 8) * 8 * 64 * 4)
     assert L.ssd_scan_bwd_ex_workspace_size(ctypes.byref(desc(headdim=12, dtype=0)),
                                             ctypes.byref(en), ctypes.byref(n1)) == UNSUP
     need = n3.value
