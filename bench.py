@@ -6,8 +6,10 @@ One step is one ssd_scan_fwd call (all prefill stages: chunk cumsum, chunk
 states, state passing, chunk scan) on the Mamba-2 2.7B head shape: batch 1,
 seqlen 4096, 80 heads, headdim 64, d_state 128, 1 group, chunk 256, bf16
 x/B/C, fp32 dt/A/D and a random fp32 initial state, with inputs resident in
-HBM.  W untimed steps, then exactly K timed steps between device
-synchronisations.  The cached decode step (ssd_step) at the same head shape
+HBM.  W untimed calls; then exactly K calls, captured as one HIP graph,
+replayed once between device synchronisations (the per-call median and
+minimum of plain host calls are reported beside it).  The cached decode step
+(ssd_step) at the same head shape
 is timed alongside at batch 1 and 64.  Prints ONE JSON line.
 
 `value` is prefill tokens/s.  `roofline` is for the dominant kernel: its
@@ -169,7 +171,7 @@ def cpu_baseline(spec, inp, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=4096)
@@ -206,25 +208,38 @@ def main():
     call = Lean(torch, lib.ssd_scan_fwd, dref, P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]),
                 P_(d["C"]), P_(d["D"]), P_(d["init"]), P_(y), P_(fin), P_(ws), ws.numel())
 
-    # ---- timed prefill steps: K back-to-back C-ABI calls from a lean host loop
-    # (arguments and stream bound once), with a HIP event between calls for the
-    # per-call median and minimum
+    # ---- timed prefill steps: the K calls (three launches each) captured as
+    # one HIP graph, the way a launch-bound loop of fixed-shape calls is run,
+    # and that graph replayed once between the synchronisations; every step
+    # is the whole call on the same resident inputs
     run = call.bound()
     for _ in range(args.warmup):
         run()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    steps_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(steps_graph):
+        for _ in range(args.steps):
+            call()  # launches on the capture stream (the bound form keeps its own)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    steps_graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    tokens_per_s = Bt * L * args.steps / elapsed
+    # per-call median and minimum of plain C-ABI calls from a lean host loop
+    # (arguments and stream bound once), a HIP event between calls
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     ev[0].record()
     for i in range(args.steps):
         run()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    ms = elapsed * 1e3 / args.steps
-    tokens_per_s = Bt * L * args.steps / elapsed
     graph_ms = time_launches(torch, call, max(10, args.steps))
+    if ms < 0.8 * graph_ms:  # a step cannot beat its own kernels: the capture missed them
+        raise RuntimeError(f"timed step {ms:.4f} ms against {graph_ms:.4f} ms of kernels")
 
     # ---- the same call with the fused edges on (dt bias + softplus + clamp
     # in the first kernel, y * silu(z) in the output store)
