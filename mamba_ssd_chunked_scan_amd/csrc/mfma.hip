@@ -224,12 +224,10 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
 // once here and read by every head of group g.  One wave per tile: the tile is
 // S^T = B_jt C_ti^T (rows j, columns i), stored as 4 KB in the register layout
 // of that 32x32 accumulator (lane l: column i = l%32; register r: row
-// j = 8(r/4) + 4(l/32) + r%4) so the chunk scan reads it as an MFMA operand
-// with one 16-byte load per lane, 16-byte unit k*64 + lane:
-//   off-diagonal tile: k = 2u   -> bf16 hi part of registers 8u..8u+7,
-//                      k = 2u+1 -> bf16 residual lo of the same registers;
-//   diagonal tile:     k = v    -> fp32 registers 4v..4v+3 (the scan applies
-//                                  the per-head decay and the mask first).
+// j = 8(r/4) + 4(l/32) + r%4), fp32, so the chunk scan reads it with one
+// 16-byte load per lane per unit: unit v (16 bytes at v*1024 + 16 lane) holds
+// registers 4v..4v+3.  The scan applies the per-head weights (and on the
+// diagonal the mask) before it rounds the tile into MFMA operands.
 // Tiles of (b, c, g) are consecutive, tile (ti, jt) at ti(ti+1)/2 + jt.
 // The wave of each diagonal tile also stores the row tile's C rows as the
 // MFMA operands the chunk scan's state term uses (lane l: row 32 ti + l%32,
@@ -273,22 +271,11 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = mfma32(brow[s], crow[s], acc);
     u32x4 *o = cb + (bcg * NT + tile) * 256;
-    if (jt < ti) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float m[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m[e] = acc[8 * u + e];
-            u32x4 hi, lo;
-            split8(m, hi, lo);
-            o[(2 * u) * 64 + lane] = hi;
-            o[(2 * u + 1) * 64 + lane] = lo;
-        }
-    } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
-                                     __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+    for (int v = 0; v < 4; ++v)
+        o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
+                                 __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+    if (jt == ti) {
         u32x4 *cf = cfr + (bcg * NI + ti) * KS * 64 + lane;
 #pragma unroll
         for (int s = 0; s < KS; ++s) cf[s * 64] = crow[s];
@@ -331,32 +318,34 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // One block per (b, c, h) with one wave per 32-row output tile (NI = Q/32
 // waves).  Wave w owns tile w for w < NI/2 and tile 3NI/2-1-w otherwise, so
 // the two waves that share a SIMD (w and w + NI/2 when waves are dealt to the
-// 4 SIMDs in turn) together make NI+1 causal tile visits, and a CU running two
-// blocks keeps four waves per SIMD to hide latency.  The wave keeps Z = Y^T
-// of its tile (64 x 32 fp32, two accumulators over p).  With e(t) = 32t + 31
-// the last row of tile t and Acs_{e(-1)} = 0, the output row i of tile ti is
+// 4 SIMDs in turn) together make NI+1 causal tile visits.  The wave keeps
+// Z = Y^T of its tile (64 x 32 fp32, two accumulators over p).  With
+// e(t) = 32t + 31 the last row of tile t and Acs_{e(-1)} = 0, the output row
+// i of tile ti is
 //   y_i = exp(Acs_i - Acs_{e(ti-1)}) Z_i + diagonal-tile part + D x_i,
 //   Z   = C_i.H, then for jt = 0..ti-1:
-//         Z <- exp(Acs_{e(jt)} - Acs_{e(jt-1)}) Z + sum_{j in jt} CB[i][j] xw_j,
-//         xw_j = exp(Acs_{e(jt)} - Acs_j) dt_j x_j,
+//         Z <- exp(Acs_{e(jt)} - Acs_{e(jt-1)}) Z + sum_{j in jt} CB[i][j] w_j x_j,
+//         w_j = exp(Acs_{e(jt)} - Acs_j) dt_j,
 // which is the chunk output of the reference form regrouped by 32-row tiles:
 // every exponent is <= 0, so nothing overflows, and an underflow drops only
-// terms that are at least as small in the exact result.  xw depends on the
-// stage alone, so it is formed once per 32-token stage (as a hi/lo bf16 pair)
-// by all threads together; CB comes pre-split from the C.B tile kernel, and
-// the off-diagonal product takes three MFMAs (hi.hi, lo.hi, hi.lo).  The
-// diagonal tile applies exp(Acs_i - Acs_j) dt_j to the fp32 CB element by
-// element under the causal mask and multiplies raw x; that masked matrix
-// (hi/lo) is built one step ahead by the wave of tile 0, which has no other
-// work after its own tile, and handed over through LDS, so the step's
-// critical path is MFMA work.
+// terms that are at least as small in the exact result.
 //
-// Every global access is a whole-line wave access: x stages, H, the C
-// operand fragments and C.B tiles (1 KB each) from the C.B kernel, and y
-// rows, which go out through LDS as full 128-byte rows one step after their
-// tile's diagonal.  Stages (raw x, xw hi, xw lo) stream through two LDS
-// slots, loaded two stages ahead; the C.B tile of the next step is loaded one
-// step ahead.  The tile loop branches on wave-uniform values only.
+// The block stages the chunk's raw x (bf16, exact) and the entering state H
+// in LDS once.  After two block barriers (everything staged; H read by the
+// state term) each wave runs its own visits with no further barrier, so the
+// waves on a SIMD interleave freely and none waits for another's tile.  The
+// off-diagonal weight w_j (one value per token, formed once per block) goes
+// onto the fp32 C.B tile: the wave forms CBw[i][j] = CB[i][j] w_j in
+// registers as a hi/lo bf16 pair, and the product with exact x takes two
+// MFMAs.  The diagonal tile applies exp(Acs_i - Acs_j) dt_j under the causal
+// mask element by element (hi/lo too), and the state term takes H as a hi/lo
+// pair against the exact C operand fragments from the C.B kernel.  The next
+// visit's C.B tile is loaded while the current one is multiplied.
+//
+// Every global access is a whole-line wave access: x rows, H, the C operand
+// fragments and C.B tiles (1 KB each) from the C.B kernel, and y rows, which
+// go out through the wave's own LDS rows as full 128-byte rows.  Loops and
+// branches depend on wave-uniform values only.
 //
 // kGate: every y value is multiplied by silu(z) (z in y's layout) in fp32
 // before its rounding to bf16.
@@ -371,23 +360,20 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     constexpr int TH = Q * 2;             // threads: NI waves
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
-    constexpr int LDX = kP + 16;          // stage rows, read transposed
+    constexpr int LDX = kP + 16;          // x rows, read transposed
     constexpr int LDY = kP + 8;           // bf16 y staging rows
     constexpr int H_BYTES = 2 * kP * LDH * 2;
     constexpr int Y_BYTES = NI * 32 * LDY * 2;
     constexpr int U_BYTES = H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES;
-    constexpr int XE = 2048 / TH;         // x elements per thread per stage (4, 8 or 16)
+    constexpr int NXV = Q * kP / 8 / TH;  // 16-byte x segments per thread
     constexpr int NHV = kP * N / 4 / TH;  // float4 of H per thread
-    constexpr int SLOT = 3 * kJT * LDX;   // raw x, xw hi, xw lo of one stage
-    static_assert(XE == 4 || XE == 8 || XE == 16, "stage split");
-    typedef unsigned XR __attribute__((ext_vector_type(XE / 2)));
-    // H (prologue), then the per-wave y staging rows
+    static_assert(NXV * TH * 8 == Q * kP && NHV * TH * 4 == kP * N, "staging split");
+    // H (until the state term is done), then the per-wave y staging rows
     __shared__ __attribute__((aligned(16))) char hu[U_BYTES];
-    __shared__ __attribute__((aligned(16))) bf16 sa[2 * SLOT];
+    __shared__ __attribute__((aligned(16))) bf16 xs[Q * LDX];
     __shared__ __attribute__((aligned(16))) float acs_s[Q];
     __shared__ __attribute__((aligned(16))) float dt_s[Q];
-    // masked diagonal matrix of the next diagonal tile: [buffer][u][hi/lo][lane]
-    __shared__ __attribute__((aligned(16))) u32x4 mdiag[2][4][64];
+    __shared__ __attribute__((aligned(16))) float w_s[Q];
     const uint32_t lb = xcd_block();
     if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -413,92 +399,16 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     // x rows of this chunk and head: bytes up to the end of row q-1, so rows
     // past a short chunk's end read as zeros; y rows likewise (stores dropped)
     const uint32_t xy_bytes = ((unsigned)(q - 1) * xrs + kP) * 2u;
-    // thread (row, seg) of a stage: XE consecutive p of one row
-    constexpr int SPR = kP / XE;          // threads per row
-    const int xrow = tid / SPR, xseg = tid % SPR;
-    const uint32_t xvoff = ((unsigned)xrow * xrs + xseg * XE) * 2u;
-    XR R[2];
-    auto load_stage = [&](int st, XR &r) __attribute__((always_inline)) {
-        const rsrc_t rs = buffer_rsrc_at(xbase, xy_bytes, (unsigned)(st * kJT) * xrs * 2u);
-        if constexpr (XE == 4) {
-            r = __builtin_bit_cast(XR, __builtin_amdgcn_raw_buffer_load_b64(rs, xvoff, 0, 0));
-        } else if constexpr (XE == 8) {
-            r = __builtin_bit_cast(XR, buffer_load16(rs, xvoff));
-        } else {
-            const u32x4 a = buffer_load16(rs, xvoff), b2 = buffer_load16(rs, xvoff + 16u);
-            r = XR{a[0], a[1], a[2], a[3], b2[0], b2[1], b2[2], b2[3]};
-        }
-    };
-    // raw x and xw = exp(Acs_{e(st)} - Acs_j) dt_j x_j (hi/lo) of stage st
-    auto store_stage = [&](int st, bf16 *sl, const XR &raw) __attribute__((always_inline)) {
-        const float ae = acs_s[st * kJT + kJT - 1];
-        const int j = st * kJT + xrow;
-        const float wj = ssd_exp(ae - acs_s[j]) * dt_s[j];  // dt_s is 0 past q (raw is 0 too)
-        XR hi, lo;
-#pragma unroll
-        for (int k = 0; k < XE / 2; ++k) {
-            uint32_t l;
-            hi[k] = split2(lo_bf16(raw[k]) * wj, hi_bf16(raw[k]) * wj, l);
-            lo[k] = l;
-        }
-        *reinterpret_cast<XR *>(&sl[xrow * LDX + xseg * XE]) = raw;
-        *reinterpret_cast<XR *>(&sl[(kJT + xrow) * LDX + xseg * XE]) = hi;
-        *reinterpret_cast<XR *>(&sl[(2 * kJT + xrow) * LDX + xseg * XE]) = lo;
-    };
-    // the 4 KB C.B tile (ti, jt) as four 16-byte operands of this lane; a
-    // tile outside the causal range (jt > ti) gets an empty range: the loads
-    // still issue, so every path has the same loads in flight, but read zeros
-    // and touch no memory
+    // the fp32 C.B tile (ti, jt <= ti) as four 16-byte operands of this lane
     const uint32_t cbvoff = lane * 16u;
     auto load_cb = [&](int jt, u32x4 (&o)[4]) __attribute__((always_inline)) {
-        const int tile = ti * (ti + 1) / 2 + min(jt, ti);
-        const rsrc_t r = buffer_rsrc_at(cbg, jt <= ti ? (tile + 1) * 4096u : 0u, tile * 4096u);
+        const int tile = ti * (ti + 1) / 2 + jt;
+        const rsrc_t r = buffer_rsrc_at(cbg, (tile + 1) * 4096u, tile * 4096u);
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = buffer_load16(r, cbvoff + k * 1024u);
     };
 
-    // masked diagonal matrix of row tile tt from its fp32 C.B tile: registers
-    // 8u+4v..+3 of this lane hold rows jl..jl+3, jl = 16u + 8v + 4(l/32);
-    // M[i][j] = CB[i][j] exp(Acs_i - Acs_j) dt_j for j <= i, as hi/lo pairs
-    // in o[2u] (hi) and o[2u+1] (lo).  Masked elements are computed anyway and
-    // replaced by 0 with a select (their exponent may be positive and their
-    // product not finite; the select discards it), so no branch diverges.
-    auto make_m = [&](int tt, const u32x4 (&cbd)[4], u32x4 (&o)[4]) __attribute__((always_inline)) {
-        const float ai = acs_s[tt * kJT + il];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float m[8];
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-                const int jl = 16 * u + 8 * v + 4 * g2;
-                const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[tt * kJT + jl]);
-                const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[tt * kJT + jl]);
-                const u32x4 cv = cbd[2 * u + v];
-                const float e0 = __uint_as_float(cv[0]) * ssd_exp(ai - aj.x) * dj.x;
-                const float e1 = __uint_as_float(cv[1]) * ssd_exp(ai - aj.y) * dj.y;
-                const float e2 = __uint_as_float(cv[2]) * ssd_exp(ai - aj.z) * dj.z;
-                const float e3 = __uint_as_float(cv[3]) * ssd_exp(ai - aj.w) * dj.w;
-                m[4 * v + 0] = jl + 0 <= il ? e0 : 0.f;
-                m[4 * v + 1] = jl + 1 <= il ? e1 : 0.f;
-                m[4 * v + 2] = jl + 2 <= il ? e2 : 0.f;
-                m[4 * v + 3] = jl + 3 <= il ? e3 : 0.f;
-            }
-            split8(m, o[2 * u], o[2 * u + 1]);
-        }
-    };
-    // the diagonal C.B tile (tt, tt) as four 16-byte operands of this lane
-    auto load_cbd = [&](int tt, u32x4 (&o)[4]) __attribute__((always_inline)) {
-        const int tile = tt * (tt + 1) / 2 + tt;
-        const rsrc_t r = buffer_rsrc_at(cbg, (tile + 1) * 4096u, tile * 4096u);
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) o[k2] = buffer_load16(r, cbvoff + k2 * 1024u);
-    };
-    auto store_m = [&](int mb, const u32x4 (&o)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) mdiag[mb][k2][lane] = o[k2];
-    };
-    // ---- prologue: global loads in the order they are needed: acs/dt and H
-    // (before the first barrier), C operands (state term), stages 0-1, C.B
+    // ---- prologue: global loads in the order they are needed
     float acs_v = 0.f, dt_v = 0.f;
     if (tid < Q) {
         const float *acs = Acs + (b * H + h) * L + t0;
@@ -514,19 +424,29 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     float4 hv[NHV];
 #pragma unroll
     for (int i = 0; i < NHV; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * i));
+    u32x4 xv[NXV];
+    {
+        const rsrc_t xr = buffer_rsrc_at(xbase, xy_bytes, 0u);
+#pragma unroll
+        for (int i = 0; i < NXV; ++i) {
+            const int e = tid + TH * i;
+            xv[i] = buffer_load16(xr, ((unsigned)(e >> 3) * xrs + 8u * (e & 7)) * 2u);
+        }
+    }
     u32x4 cf[KS];
     {
         const u32x4 *f = cfr + (bcg * NI + ti) * KS * 64 + lane;
 #pragma unroll
         for (int s = 0; s < KS; ++s) cf[s] = f[s * 64];
     }
-    load_stage(0, R[0]);
-    load_stage(1, R[1]);
-    u32x4 cbr[4];  // this step's C.B tile; reloaded for the next step once read
+    u32x4 cbr[4];  // the C.B tile of the wave's next visit
     load_cb(0, cbr);
     if (tid < Q) {
+        // w_j needs Acs at its tile's last row, held by lane 31 of its half-wave
+        const float ae = __shfl(acs_v, lane | 31);
         acs_s[tid] = acs_v;
         dt_s[tid] = dt_v;
+        w_s[tid] = ssd_exp(ae - acs_v) * dt_v;  // 0 past q
     }
     bf16 *Hh = reinterpret_cast<bf16 *>(hu);
     bf16 *Hl = Hh + kP * LDH;
@@ -542,19 +462,13 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
         *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
     }
-    __syncthreads();  // acs_s, dt_s, H
-    store_stage(0, sa, R[0]);
-    if (wave < 2) {  // masked diagonal matrices of tiles 0 and 1 (buffers 0, 1)
-        u32x4 cbd[4], mo[4];
-        if (wave == 0) {
 #pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) cbd[k2] = cbr[k2];  // tile 0's C.B is its diagonal
-        } else {
-            load_cbd(1, cbd);
-        }
-        make_m(wave, cbd, mo);
-        store_m(wave, mo);
+    for (int i = 0; i < NXV; ++i) {
+        const int e = tid + TH * i;
+        *reinterpret_cast<u32x4 *>(&xs[(e >> 3) * LDX + 8 * (e & 7)]) = xv[i];
     }
+    __syncthreads();  // acs_s, dt_s, w_s, H, x
+
     // state term Z = H C_i^T
     f32x16 Z[2] = {zero16(), zero16()};
 #pragma unroll
@@ -568,7 +482,7 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             Z[pt] = mfma32(al, cf[s], Z[pt]);
         }
     }
-    __syncthreads();  // stage 0 visible; H no longer read (its LDS becomes y staging)
+    __syncthreads();  // H no longer read: its LDS becomes the y staging rows
 
     bf16 *ys = reinterpret_cast<bf16 *>(hu) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
@@ -588,38 +502,78 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     }
     const float Dh = D ? D[h] : 0.f;
 
-    // off-diagonal visit of column tile jt
-    auto offdiag = [&](int jt, const bf16 *sl, const u32x4 (&cbt)[4]) __attribute__((always_inline)) {
-        const float f = ssd_exp(acs_s[jt * kJT + kJT - 1] - (jt > 0 ? acs_s[jt * kJT - 1] : 0.f));
+    // off-diagonal visits: CBw = CB w_j (hi/lo) against the exact x rows of tile jt
+#pragma unroll 1
+    for (int jt = 0; jt < ti; ++jt) {
+        u32x4 wh[2], wl[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float m[8];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const float4 wj = *reinterpret_cast<const float4 *>(&w_s[jt * 32 + 16 * u + 8 * v + 4 * g2]);
+                const u32x4 cv = cbr[2 * u + v];
+                m[4 * v + 0] = __uint_as_float(cv[0]) * wj.x;
+                m[4 * v + 1] = __uint_as_float(cv[1]) * wj.y;
+                m[4 * v + 2] = __uint_as_float(cv[2]) * wj.z;
+                m[4 * v + 3] = __uint_as_float(cv[3]) * wj.w;
+            }
+            split8(m, wh[u], wl[u]);
+        }
+        load_cb(jt + 1, cbr);  // the next visit's tile (the diagonal one last)
+        const float f = ssd_exp(acs_s[jt * 32 + 31] - (jt > 0 ? acs_s[jt * 32 - 1] : 0.f));
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) Z[pt][r] *= f;
+        const bf16 *xt = xs + jt * 32 * LDX;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const u32x4 ah = tr_operand<true>(sl + kJT * LDX, LDX, 16 * u, 32 * pt);
-                const u32x4 al = tr_operand<true>(sl + 2 * kJT * LDX, LDX, 16 * u, 32 * pt);
-                Z[pt] = mfma32(ah, cbt[2 * u], Z[pt]);
-                Z[pt] = mfma32(al, cbt[2 * u], Z[pt]);
-                Z[pt] = mfma32(ah, cbt[2 * u + 1], Z[pt]);
+                const u32x4 xa = tr_operand<true>(xt, LDX, 16 * u, 32 * pt);
+                Z[pt] = mfma32(xa, wh[u], Z[pt]);
+                Z[pt] = mfma32(xa, wl[u], Z[pt]);
             }
-    };
-    // diagonal visit (jt == ti) with M from LDS buffer mb
-    auto diag = [&](const bf16 *sl, int mb) __attribute__((always_inline)) {
-        const float ai = acs_s[ti * kJT + il];
-        const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * kJT - 1] : 0.f));
+    }
+
+    // diagonal visit: M[i][j] = CB[i][j] exp(Acs_i - Acs_j) dt_j for j <= i
+    // (registers 8u+4v..+3 of this lane hold rows jl..jl+3, jl = 16u + 8v +
+    // 4(l/32)), as hi/lo pairs in mo[2u], mo[2u+1].  Masked elements are
+    // computed anyway and replaced by 0 with a select (their exponent may be
+    // positive and their product not finite; the select discards it).
+    {
+        const float ai = acs_s[ti * 32 + il];
         u32x4 mo[4];
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) mo[k2] = mdiag[mb][k2][lane];
-        // rescale to exp(Acs_i) and add D x (x rows of this tile are this stage)
+        for (int u = 0; u < 2; ++u) {
+            float m[8];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int jl = 16 * u + 8 * v + 4 * g2;
+                const float4 aj = *reinterpret_cast<const float4 *>(&acs_s[ti * 32 + jl]);
+                const float4 dj = *reinterpret_cast<const float4 *>(&dt_s[ti * 32 + jl]);
+                const u32x4 cv = cbr[2 * u + v];
+                const float e0 = __uint_as_float(cv[0]) * ssd_exp(ai - aj.x) * dj.x;
+                const float e1 = __uint_as_float(cv[1]) * ssd_exp(ai - aj.y) * dj.y;
+                const float e2 = __uint_as_float(cv[2]) * ssd_exp(ai - aj.z) * dj.z;
+                const float e3 = __uint_as_float(cv[3]) * ssd_exp(ai - aj.w) * dj.w;
+                m[4 * v + 0] = jl + 0 <= il ? e0 : 0.f;
+                m[4 * v + 1] = jl + 1 <= il ? e1 : 0.f;
+                m[4 * v + 2] = jl + 2 <= il ? e2 : 0.f;
+                m[4 * v + 3] = jl + 3 <= il ? e3 : 0.f;
+            }
+            split8(m, mo[2 * u], mo[2 * u + 1]);
+        }
+        const bf16 *xt = xs + ti * 32 * LDX;
+        // rescale to exp(Acs_i) and add D x (x rows of this tile)
+        const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * 32 - 1] : 0.f));
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                const u32x2 xr = *reinterpret_cast<const u32x2 *>(&sl[il * LDX + p0]);
+                const u32x2 xr = *reinterpret_cast<const u32x2 *>(&xt[il * LDX + p0]);
                 const int r0 = 4 * rg;
                 Z[pt][r0 + 0] = Z[pt][r0 + 0] * rf + Dh * lo_bf16(xr[0]);
                 Z[pt][r0 + 1] = Z[pt][r0 + 1] * rf + Dh * hi_bf16(xr[0]);
@@ -630,85 +584,54 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const u32x4 xa = tr_operand<true>(sl, LDX, 16 * u, 32 * pt);
+                const u32x4 xa = tr_operand<true>(xt, LDX, 16 * u, 32 * pt);
                 Z[pt] = mfma32(xa, mo[2 * u], Z[pt]);
                 Z[pt] = mfma32(xa, mo[2 * u + 1], Z[pt]);
             }
-    };
+    }
+
     // y rows of the tile as bf16 via this wave's LDS rows, written as full
     // 128-byte rows (8 lanes per row, 8 rows per store)
-    const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
-    auto epilogue = [&]() __attribute__((always_inline)) {
-        if constexpr (kGate) {
-            // z of this lane's accumulator elements (token il, channels
-            // p0..p0+3), from the copy the wave prefetched into its staging
-            // rows; the multiply is in fp32, before the single rounding below
-            const bf16 *zl = ys;
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                    const u32x2 zz = *reinterpret_cast<const u32x2 *>(&zl[il * kP + p0]);
-                    Z[pt][4 * rg + 0] *= silu_f(lo_bf16(zz[0]));
-                    Z[pt][4 * rg + 1] *= silu_f(hi_bf16(zz[0]));
-                    Z[pt][4 * rg + 2] *= silu_f(lo_bf16(zz[1]));
-                    Z[pt][4 * rg + 3] *= silu_f(hi_bf16(zz[1]));
-                }
-            // the z reads above feed the products the stores below write, so
-            // they have completed before the staging rows are overwritten
-        }
+    if constexpr (kGate) {
+        // z of this lane's accumulator elements (token il, channels
+        // p0..p0+3), from the copy the wave prefetched into its staging
+        // rows; the multiply is in fp32, before the single rounding below
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the z copy has landed
+        const bf16 *zl = ys;
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int p0 = pt * 32 + 8 * rg + 4 * g2;
-                u32x2 o;
-                o[0] = pack_bf16x2(Z[pt][4 * rg + 0], Z[pt][4 * rg + 1]);
-                o[1] = pack_bf16x2(Z[pt][4 * rg + 2], Z[pt][4 * rg + 3]);
-                *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
+                const u32x2 zz = *reinterpret_cast<const u32x2 *>(&zl[il * kP + p0]);
+                Z[pt][4 * rg + 0] *= silu_f(lo_bf16(zz[0]));
+                Z[pt][4 * rg + 1] *= silu_f(hi_bf16(zz[0]));
+                Z[pt][4 * rg + 2] *= silu_f(lo_bf16(zz[1]));
+                Z[pt][4 * rg + 3] *= silu_f(hi_bf16(zz[1]));
             }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
-            const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
-            buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32 + 8 * kk) * xrs * 2u),
-                           yvoff);
-        }
-    };
-
-    auto jstep = [&](int jt, auto par) __attribute__((always_inline)) {
-        constexpr int cur = decltype(par)::value;  // jt % 2: LDS slot and stage registers
-        const bf16 *sl = sa + cur * SLOT;
-        // unconditional prefetches (empty ranges past the end): the same loads
-        // are in flight on every path, so waits count exactly.  The next C.B
-        // tile reuses this tile's registers once its MFMAs have read them.
-        load_stage(jt + 2, R[cur]);
-        if (jt < ti) offdiag(jt, sl, cbr);
-        else if (jt == ti) diag(sl, cur);
-        load_cb(jt + 1, cbr);
-        // a finished tile is written one step later, off the diagonal step
-        if (jt == ti + 1) epilogue();
-        // tile 0's wave (done with its own tile) builds the masked diagonal
-        // matrix of tile jt+1 into buffer (jt+1) % 2, read last in step jt-1
-        // (before the barrier that ended it); the barrier below publishes it
-        if (wave == 0 && jt >= 1 && jt + 1 < NI) {
-            u32x4 cbd[4], mo[4];
-            load_cbd(jt + 1, cbd);
-            make_m(jt + 1, cbd, mo);
-            store_m(cur ^ 1, mo);
-        }
-        if (jt + 1 < NI) store_stage(jt + 1, sa + (cur ^ 1) * SLOT, R[cur ^ 1]);
-        __syncthreads();
-    };
-#pragma unroll 1
-    for (int jt = 0; jt < NI; jt += 2) {  // NI is even
-        jstep(jt, P0{});
-        jstep(jt + 1, P1{});
+        // the z reads above feed the products the stores below write, so
+        // they have completed before the staging rows are overwritten
     }
-    if (ti == NI - 1) epilogue();
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int p0 = pt * 32 + 8 * rg + 4 * g2;
+            u32x2 o;
+            o[0] = pack_bf16x2(Z[pt][4 * rg + 0], Z[pt][4 * rg + 1]);
+            o[1] = pack_bf16x2(Z[pt][4 * rg + 2], Z[pt][4 * rg + 3]);
+            *reinterpret_cast<u32x2 *>(&ys[il * LDY + p0]) = o;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
+        const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
+        buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32 + 8 * kk) * xrs * 2u),
+                       yvoff);
+    }
 }
 
 template <int Q, int N>
