@@ -330,14 +330,14 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // every exponent is <= 0, so nothing overflows, and an underflow drops only
 // terms that are at least as small in the exact result.
 //
-// The block stages the chunk's raw x (bf16, exact) and the entering state H
-// in LDS once.  After two block barriers (everything staged; H read by the
-// state term) each wave runs its own visits with no further barrier, so the
-// waves on a SIMD interleave freely and none waits for another's tile.  The
-// off-diagonal weight w_j (one value per token, formed once per block) goes
-// onto the fp32 C.B tile: the wave forms CBw[i][j] = CB[i][j] w_j in
-// registers as a hi/lo bf16 pair, and the product with exact x takes two
-// MFMAs.  The diagonal tile applies exp(Acs_i - Acs_j) dt_j under the causal
+// The block stages the entering state H and the chunk's raw x (bf16, exact)
+// in LDS once: H first, for the state term, while x is still arriving, and x
+// after it.  After those two block barriers each wave runs its own visits
+// with no further barrier, so the waves on a SIMD interleave freely and none
+// waits for another's tile.  The off-diagonal weight (w_j, one value per
+// token, formed once per block, times a per-visit decay) goes onto the fp32
+// C.B tile: the wave forms CBw[i][j] = CB[i][j] w_j in registers as a hi/lo
+// bf16 pair, and the product with exact x takes two MFMAs.  The diagonal tile applies exp(Acs_i - Acs_j) dt_j under the causal
 // mask element by element (hi/lo too), and the state term takes H as a hi/lo
 // pair against the exact C operand fragments from the C.B kernel.  The next
 // visit's C.B tile is loaded while the current one is multiplied.
@@ -424,6 +424,13 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     float4 hv[NHV];
 #pragma unroll
     for (int i = 0; i < NHV; ++i) hv[i] = *reinterpret_cast<const float4 *>(Hc + 4 * (tid + TH * i));
+    u32x4 cf[KS];
+    {
+        const u32x4 *f = cfr + (bcg * NI + ti) * KS * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cf[s] = f[s * 64];
+    }
+    // x after what the state term needs (loads complete in issue order)
     u32x4 xv[NXV];
     {
         const rsrc_t xr = buffer_rsrc_at(xbase, xy_bytes, 0u);
@@ -432,12 +439,6 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             const int e = tid + TH * i;
             xv[i] = buffer_load16(xr, ((unsigned)(e >> 3) * xrs + 8u * (e & 7)) * 2u);
         }
-    }
-    u32x4 cf[KS];
-    {
-        const u32x4 *f = cfr + (bcg * NI + ti) * KS * 64 + lane;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) cf[s] = f[s * 64];
     }
     u32x4 cbr[4];  // the C.B tile of the wave's next visit
     load_cb(0, cbr);
@@ -462,12 +463,7 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         *reinterpret_cast<u32x2 *>(Hh + p * LDH + n) = hh;
         *reinterpret_cast<u32x2 *>(Hl + p * LDH + n) = hl;
     }
-#pragma unroll
-    for (int i = 0; i < NXV; ++i) {
-        const int e = tid + TH * i;
-        *reinterpret_cast<u32x4 *>(&xs[(e >> 3) * LDX + 8 * (e & 7)]) = xv[i];
-    }
-    __syncthreads();  // acs_s, dt_s, w_s, H, x
+    __syncthreads();  // acs_s, dt_s, w_s, H (x is still arriving)
 
     // state term Z = H C_i^T
     f32x16 Z[2] = {zero16(), zero16()};
@@ -482,7 +478,12 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             Z[pt] = mfma32(al, cf[s], Z[pt]);
         }
     }
-    __syncthreads();  // H no longer read: its LDS becomes the y staging rows
+#pragma unroll
+    for (int i = 0; i < NXV; ++i) {
+        const int e = tid + TH * i;
+        *reinterpret_cast<u32x4 *>(&xs[(e >> 3) * LDX + 8 * (e & 7)]) = xv[i];
+    }
+    __syncthreads();  // x staged; H no longer read: its LDS becomes the y staging rows
 
     bf16 *ys = reinterpret_cast<bf16 *>(hu) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
@@ -502,9 +503,24 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     }
     const float Dh = D ? D[h] : 0.f;
 
-    // off-diagonal visits: CBw = CB w_j (hi/lo) against the exact x rows of tile jt
+    // off-diagonal visits.  With ae = Acs_{e(ti-1)}, the state term and every
+    // off-diagonal term reach row i through the diagonal's exp(Acs_i - ae), so
+    // Z is scaled by exp(ae) once and tile jt enters with the weight
+    // exp(ae - Acs_j) dt_j = F_jt w_j, F_jt = exp(ae - Acs_{e(jt)}): the visits
+    // are independent accumulations, and none waits on another's result.
+    // CBw = CB F_jt w_j (hi/lo) multiplies the exact x rows of tile jt; the
+    // next visit's C.B tile is loaded once this one is weighted.
+    const float ae = ti > 0 ? acs_s[ti * 32 - 1] : 0.f;
+    {
+        const float fs = ssd_exp(ae);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Z[pt][r] *= fs;
+    }
 #pragma unroll 1
     for (int jt = 0; jt < ti; ++jt) {
+        const float F = ssd_exp(ae - acs_s[jt * 32 + 31]);
         u32x4 wh[2], wl[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -513,19 +529,14 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
             for (int v = 0; v < 2; ++v) {
                 const float4 wj = *reinterpret_cast<const float4 *>(&w_s[jt * 32 + 16 * u + 8 * v + 4 * g2]);
                 const u32x4 cv = cbr[2 * u + v];
-                m[4 * v + 0] = __uint_as_float(cv[0]) * wj.x;
-                m[4 * v + 1] = __uint_as_float(cv[1]) * wj.y;
-                m[4 * v + 2] = __uint_as_float(cv[2]) * wj.z;
-                m[4 * v + 3] = __uint_as_float(cv[3]) * wj.w;
+                m[4 * v + 0] = __uint_as_float(cv[0]) * (wj.x * F);
+                m[4 * v + 1] = __uint_as_float(cv[1]) * (wj.y * F);
+                m[4 * v + 2] = __uint_as_float(cv[2]) * (wj.z * F);
+                m[4 * v + 3] = __uint_as_float(cv[3]) * (wj.w * F);
             }
             split8(m, wh[u], wl[u]);
         }
         load_cb(jt + 1, cbr);  // the next visit's tile (the diagonal one last)
-        const float f = ssd_exp(acs_s[jt * 32 + 31] - (jt > 0 ? acs_s[jt * 32 - 1] : 0.f));
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Z[pt][r] *= f;
         const bf16 *xt = xs + jt * 32 * LDX;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -567,7 +578,7 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         }
         const bf16 *xt = xs + ti * 32 * LDX;
         // rescale to exp(Acs_i) and add D x (x rows of this tile)
-        const float rf = ssd_exp(ai - (ti > 0 ? acs_s[ti * 32 - 1] : 0.f));
+        const float rf = ssd_exp(ai - ae);
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
