@@ -261,6 +261,37 @@ def main():
                      P_(d["init"]), P_(ye), P_(fin), P_(ws), ws.numel())
     norm_ms = time_launches(torch, call_norm, max(10, args.steps))
 
+    # ---- the same call at the other prefill configurations: the 130M head
+    # shape (24 heads, 2048 tokens) and the batched long prefill (8 x 16384
+    # tokens, 8 groups); graph-replayed, inputs resident
+    def prefill_case(name, iters):
+        cs = synth.WORKLOADS[name]
+        cd = {k: (None if v is None else v.to(dev).contiguous())
+              for k, v in synth.scan_inputs(cs).items()}
+        cB, cL, cH, cP, cN, cG, cQ = (cs.batch, cs.seqlen, cs.nheads, cs.headdim, cs.dstate,
+                                      cs.ngroups, cs.chunk)
+        cy = torch.empty_like(cd["x"])
+        cfin = torch.empty((cB, cH, cP, cN), dtype=torch.float32, device=dev)
+        cws = torch.empty(max(ssd.workspace_size(cB, cL, cH, cP, cN, cG, cQ, torch.bfloat16), 1),
+                          dtype=torch.uint8, device=dev)
+        cdesc = binding.ScanDesc(cB, cL, cH, cP, cN, cG, cQ, binding.SSD_BF16, 0)
+        ccall = Lean(torch, lib.ssd_scan_fwd, ctypes.byref(cdesc), P_(cd["x"]), P_(cd["dt"]),
+                     P_(cd["A"]), P_(cd["B"]), P_(cd["C"]), P_(cd["D"]),
+                     None if cd["init"] is None else P_(cd["init"]), P_(cy), P_(cfin), P_(cws),
+                     cws.numel())
+        c_ms = time_launches(torch, ccall, iters)
+        cflops, cbytes = prefill_flops(cs), prefill_bytes(cs)["call"]
+        out = {"us_per_call_graph": round(c_ms * 1e3, 2),
+               "tokens_per_s": round(cB * cL / (c_ms * 1e-3), 1),
+               "tflops_causal": round(cflops / (c_ms * 1e-3) / 1e12, 2),
+               "frac_mfma_peak": round(cflops / (c_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "hbm_GB_s_algorithmic": round(cbytes / (c_ms * 1e-3) / 1e9, 1)}
+        del cd, cy, cfin, cws
+        torch.cuda.empty_cache()
+        return out
+    other_configs = {"m130m_bf16": prefill_case("m130m_bf16", 20),
+                     "batched_long_bf16": prefill_case("batched_long_bf16", 5)}
+
     # ---- the gradient (ssd_scan_bwd) at this workload, and forward plus
     # backward at the 130M head shape with 512 tokens
     def bwd_case(bspec, binp):
@@ -484,6 +515,7 @@ def main():
                     "us_per_call_min": round(per_call[0] * 1e3, 2),
                     "us_per_call_graph_fused_edges": round(edges_ms * 1e3, 2),
                     "us_per_call_graph_fused_edges_gated_rmsnorm": round(norm_ms * 1e3, 2),
+                    "other_configs": other_configs,
                     "frac_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                     "hbm_GB_s_algorithmic": round(call_gbs, 1),
                     "frac_hbm_roofline": round(call_gbs / HBM_PEAK_GBS, 4),

@@ -93,6 +93,8 @@ SHAPES = [
     (1, 384, 2, 64, 128, 1, 64, "bf16"),
     (1, 200, 2, 64, 128, 2, 128, "f32"),
     (3, 96, 4, 32, 256, 4, 32, "bf16"),
+    (1, 100, 3, 64, 64, 1, 256, "bf16"),     # one partial chunk: half its row tiles empty
+    (2, 33, 2, 64, 128, 2, 64, "bf16"),      # 33 tokens: a one-row second tile
 ]
 
 
