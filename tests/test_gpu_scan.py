@@ -95,6 +95,8 @@ SHAPES = [
     (3, 96, 4, 32, 256, 4, 32, "bf16"),
     (1, 100, 3, 64, 64, 1, 256, "bf16"),     # one partial chunk: half its row tiles empty
     (2, 33, 2, 64, 128, 2, 64, "bf16"),      # 33 tokens: a one-row second tile
+    (1, 70, 2, 256, 256, 1, 32, "f32"),      # the largest headdim and d_state accepted
+    (2, 50, 4, 8, 4, 2, 16, "bf16"),         # the smallest d_state and chunk accepted
 ]
 
 
