@@ -162,10 +162,18 @@ def cpu_baseline(spec, inp, budget_s=10.0):
         if reps >= 2 and el >= budget_s:
             break
     tokens = spec.batch * spec.seqlen * reps
+    # the same on one core: two passes (a few seconds); the thread count is
+    # left at one afterwards, and nothing after this uses the oracle
+    t1 = time.perf_counter()
+    for _ in range(2):
+        oracle.scan(**args, nthreads=1)
+    el1 = time.perf_counter() - t1
     return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "single_core_tokens_per_s": round(2 * spec.batch * spec.seqlen / el1, 1),
             "sample": f"full {spec.name} prefill ({spec.batch}x{spec.seqlen} tokens, "
                       f"{spec.nheads} heads) repeated {reps}x in {el:.1f} s, fp64 recurrence "
-                      f"with {cores} OpenMP threads"}
+                      f"with {cores} OpenMP threads; single_core_tokens_per_s: the same "
+                      f"prefill twice on one thread ({el1:.1f} s)"}
 
 
 def main():
