@@ -510,6 +510,11 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     // are independent accumulations, and none waits on another's result.
     // CBw = CB F_jt w_j (hi/lo) multiplies the exact x rows of tile jt; the
     // next visit's C.B tile is loaded once this one is weighted.
+    // the waves with the longest chains of visits issue first when several
+    // are ready: a block ends with its slowest wave
+    if (ti >= 6) __builtin_amdgcn_s_setprio(3);
+    else if (ti >= 4) __builtin_amdgcn_s_setprio(2);
+    else if (ti >= 2) __builtin_amdgcn_s_setprio(1);
     const float ae = ti > 0 ? acs_s[ti * 32 - 1] : 0.f;
     {
         const float fs = ssd_exp(ae);
