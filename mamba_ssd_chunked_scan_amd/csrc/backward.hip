@@ -929,17 +929,27 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     }
 }
 
+// Raises a kernel's dynamic-LDS limit on the current device, once per device
+// (the attribute belongs to each device's copy of the kernel).  A failure
+// shows up as the launch's own error.
+template <auto *Kernel>
+void allow_dynamic_lds(int bytes) {
+    static bool done[64];
+    int dev = 0;
+    const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+    if (known && done[dev]) return;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess &&
+        known)
+        done[dev] = true;
+}
+
 template <int N, int QT>
 void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                        const void *Bm, const void *Cm, const float *D, const float *Acs,
                        const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                        float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
-    static bool attr_set = false;  // once per instantiation (per process)
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd_mfma<N, QT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, BwdLds<N, QT>::BYTES);
-        attr_set = true;
-    }
+    allow_dynamic_lds<&k_chunk_bwd_mfma<N, QT>>(BwdLds<N, QT>::BYTES);
     // heads per block: 4 (dB and dC accumulate over them before their
     // atomics), fewer when that would leave the grid under two blocks per CU
     const int64_t R = s.H / s.G;
@@ -1169,12 +1179,7 @@ void launch_bwd_t(const ScanShape &s, const void *x, const float *dt, const floa
                   float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
     size_t lds = 0;
     const int rows = bwd_slice_rows((int)s.P, (int)s.N, &lds);
-    static bool attr_set = false;  // once per instantiation (per process)
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_chunk_bwd<Tin, KI>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        attr_set = true;
-    }
+    allow_dynamic_lds<&k_chunk_bwd<Tin, KI>>(160 * 1024);
     const int64_t R = s.H / s.G;
     const int64_t nslices = (R + kHeadsPerBlock - 1) / kHeadsPerBlock;
     k_chunk_bwd<Tin, KI><<<(unsigned)(s.B * s.T * s.G * nslices), kBThreads, lds, st>>>(
