@@ -320,27 +320,29 @@ k_state_passing_cb(float *__restrict__ states, const float *__restrict__ Acs, co
 // the two waves that share a SIMD (w and w + NI/2 when waves are dealt to the
 // 4 SIMDs in turn) together make NI+1 causal tile visits.  The wave keeps
 // Z = Y^T of its tile (64 x 32 fp32, two accumulators over p).  With
-// e(t) = 32t + 31 the last row of tile t and Acs_{e(-1)} = 0, the output row
-// i of tile ti is
-//   y_i = exp(Acs_i - Acs_{e(ti-1)}) Z_i + diagonal-tile part + D x_i,
-//   Z   = C_i.H, then for jt = 0..ti-1:
-//         Z <- exp(Acs_{e(jt)} - Acs_{e(jt-1)}) Z + sum_{j in jt} CB[i][j] w_j x_j,
-//         w_j = exp(Acs_{e(jt)} - Acs_j) dt_j,
+// e(t) = 32t + 31 the last row of tile t, Acs_{e(-1)} = 0 and ae =
+// Acs_{e(ti-1)}, the output row i of tile ti is
+//   y_i = exp(Acs_i - ae) Z_i + diagonal-tile part + D x_i,
+//   Z   = exp(ae) C_i.H + sum_{jt < ti} sum_{j in jt} CB[i][j] F_jt w_j x_j,
+//         w_j = exp(Acs_{e(jt)} - Acs_j) dt_j,  F_jt = exp(ae - Acs_{e(jt)}),
 // which is the chunk output of the reference form regrouped by 32-row tiles:
 // every exponent is <= 0, so nothing overflows, and an underflow drops only
-// terms that are at least as small in the exact result.
+// terms that are at least as small in the exact result.  The off-diagonal
+// visits are independent accumulations into Z.
 //
 // The block stages the entering state H and the chunk's raw x (bf16, exact)
 // in LDS once: H first, for the state term, while x is still arriving, and x
 // after it.  After those two block barriers each wave runs its own visits
 // with no further barrier, so the waves on a SIMD interleave freely and none
-// waits for another's tile.  The off-diagonal weight (w_j, one value per
-// token, formed once per block, times a per-visit decay) goes onto the fp32
-// C.B tile: the wave forms CBw[i][j] = CB[i][j] w_j in registers as a hi/lo
-// bf16 pair, and the product with exact x takes two MFMAs.  The diagonal tile applies exp(Acs_i - Acs_j) dt_j under the causal
-// mask element by element (hi/lo too), and the state term takes H as a hi/lo
-// pair against the exact C operand fragments from the C.B kernel.  The next
-// visit's C.B tile is loaded while the current one is multiplied.
+// waits for another's tile; the waves with longer chains of visits run at a
+// higher wave priority.  The off-diagonal weight F_jt w_j (w_j one value per
+// token, formed once per block) goes onto the fp32 C.B tile: the wave forms
+// CBw[i][j] = CB[i][j] F_jt w_j in registers as a hi/lo bf16 pair, and the
+// product with exact x takes two MFMAs.  The diagonal tile applies
+// exp(Acs_i - Acs_j) dt_j under the causal mask element by element (hi/lo
+// too), and the state term takes H as a hi/lo pair against the exact C
+// operand fragments from the C.B kernel.  The next visit's C.B tile is loaded
+// while the current one is multiplied.
 //
 // Every global access is a whole-line wave access: x rows, H, the C operand
 // fragments and C.B tiles (1 KB each) from the C.B kernel, and y rows, which
