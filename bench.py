@@ -150,6 +150,33 @@ class Lean:
         return call
 
 
+def device_info(torch) -> dict:
+    """The part's CU count and peak engine / memory clocks as the HIP runtime
+    reports them, and the bf16 MFMA peak they imply (4096 dense flop per clock
+    per CU: four SIMDs, one v_mfma_f32_32x32x16_bf16 of 32768 flop every 32
+    clocks on each)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = ctypes.c_int(0)
+        hip.hipGetDevice(ctypes.byref(dev))
+        def attr(code):  # hipDeviceAttribute_t values of the ROCm 7 headers
+            v = ctypes.c_int(0)
+            return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev) == 0 else None
+        sclk_khz, mclk_khz, bus_bits = attr(5), attr(60), attr(59)
+        out.update({"sclk_mhz": None if sclk_khz is None else sclk_khz / 1e3,
+                    "memory_clock_mhz": None if mclk_khz is None else mclk_khz / 1e3,
+                    "memory_bus_bits": bus_bits})
+        if sclk_khz:
+            out["mfma_bf16_peak_tflops_from_clock"] = round(
+                props.multi_processor_count * sclk_khz * 1e3 * 4096 / 1e12, 1)
+    except OSError:
+        pass
+    return out
+
+
 def cpu_baseline(spec, inp, budget_s=10.0):
     import oracle
     args = {k: oracle.f64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init")}
@@ -535,6 +562,7 @@ def main():
                    "tokens_per_s": round(vtot / (varlen_ms * 1e-3), 1),
                    "padded_batch_us_per_call_graph": round(padded_ms * 1e3, 2),
                    "speedup_vs_padded": round(padded_ms / varlen_ms, 2)},
+        "device": device_info(torch),
         "copy_GB_s": round(copy_gbs, 1),
         "frac_of_copy": {f"prefill_{dom}": round(dom_gbs / copy_gbs, 4),
                          "decode_batch64": round(decode["batch64"]["GB_s"] / copy_gbs, 4)},
