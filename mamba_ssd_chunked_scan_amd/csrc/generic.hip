@@ -241,19 +241,68 @@ k_state_passing_rev(float *__restrict__ ds, const float *__restrict__ Acs,
 }
 
 // ----------------------------------------------------------- chunk scan
-// One block per (b, c, h) and 16 output rows.  M[i][j] = (C_i.B_j) exp(Acs_i -
-// Acs_j) dt_j for j <= i is built in LDS, then each output (i, p) is
-// sum_j M[i][j] x[j,p] + exp(Acs_i) (C_i . H_c[p]) + D x[i,p].
 constexpr int kScanRows = 16;
+
+// CB[i][j] = C_i . B_j in fp32 for one (b, c, g) and a tile of 16 rows i, every
+// column j <= i, into a Q x Q buffer per (b, c, g) (the rest of it is neither
+// written nor read).  It does not involve the head, so it is formed once here
+// and read by every head of the group.  C rows of the tile and 16 B rows at a
+// time are staged in LDS; each thread forms one (i, j) dot product in the
+// order n = 0..N-1.
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_chunk_cb_generic(const Tin *__restrict__ Bm, const Tin *__restrict__ Cm, float *__restrict__ cb,
+                   int64_t L, int N, int G, int Q, int T, const int2 *__restrict__ ctab) {
+    __shared__ float Cs[kScanRows][257];
+    __shared__ float Bs[kScanRows][257];
+    const int64_t bcg = blockIdx.x;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % T);
+    const int64_t b = bc / T;
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int64_t t0 = cp.t0;
+    const int q = cp.q;
+    const int i0 = blockIdx.y * kScanRows;
+    if (i0 >= q) return;
+    const int rows = min(kScanRows, q - i0);
+    for (int e = threadIdx.x; e < kScanRows * N; e += 256) {
+        const int ii = e / N, n = e % N;
+        Cs[ii][n] = ii < rows ? Elem<Tin>::ld(Cm, ((b * L + t0 + i0 + ii) * G + g) * N + n) : 0.f;
+    }
+    const int ii = threadIdx.x / kScanRows, jj = threadIdx.x % kScanRows;
+    float *out = cb + (bcg * Q + i0 + ii) * (int64_t)Q;
+    const int jend = i0 + rows;  // columns j < jend can be needed
+    for (int j0 = 0; j0 < jend; j0 += kScanRows) {
+        __syncthreads();  // Cs staged; the previous B rows no longer read
+        for (int e = threadIdx.x; e < kScanRows * N; e += 256) {
+            const int r = e / N, n = e % N;
+            Bs[r][n] = j0 + r < jend ? Elem<Tin>::ld(Bm, ((b * L + t0 + j0 + r) * G + g) * N + n)
+                                     : 0.f;
+        }
+        __syncthreads();
+        const int j = j0 + jj;
+        if (ii < rows && j <= i0 + ii) {
+            float dot = 0.f;
+            for (int n = 0; n < N; ++n) dot += Cs[ii][n] * Bs[jj][n];
+            out[j] = dot;
+        }
+    }
+}
+
+// One block per (b, c, h) and 16 output rows.  M[i][j] = CB[i][j] exp(Acs_i -
+// Acs_j) dt_j for j <= i is built in LDS from the group's C.B buffer, then
+// each output (i, p) is sum_j M[i][j] x[j,p] + exp(Acs_i) (C_i . H_c[p]) +
+// D x[i,p].
 
 template <typename Tin>
 __global__ void __launch_bounds__(256)
 k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
                      const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
                      const float *__restrict__ D, const float *__restrict__ Acs,
-                     const float *__restrict__ states, Tin *__restrict__ y,
-                     const Tin *__restrict__ z, int64_t L, int H, int P, int N, int G, int Q,
-                     int T, const int2 *__restrict__ ctab) {
+                     const float *__restrict__ states, const float *__restrict__ cbuf,
+                     Tin *__restrict__ y, const Tin *__restrict__ z, int64_t L, int H, int P,
+                     int N, int G, int Q, int T, const int2 *__restrict__ ctab) {
     __shared__ float Ms[kScanRows][257];
     __shared__ float Cs[kScanRows][257];
     __shared__ float acs_s[256];
@@ -279,16 +328,13 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
     }
     __syncthreads();
     const int jmax = i0 + rows;  // columns j < jmax can be non-zero
+    const float *cbr = cbuf + (((b * T + c) * G + g) * Q) * (int64_t)Q;
+    (void)Bm;  // B enters through the group's C.B buffer
     for (int e = threadIdx.x; e < kScanRows * jmax; e += 256) {
         const int ii = e / jmax, j = e % jmax;
         const int i = i0 + ii;
         float m = 0.f;
-        if (ii < rows && j <= i) {
-            const Tin *br = Bm + ((b * L + t0 + j) * G + g) * N;
-            float dot = 0.f;
-            for (int n = 0; n < N; ++n) dot += Cs[ii][n] * Elem<Tin>::ld(br, n);
-            m = dot * ssd_exp(acs_s[i] - acs_s[j]) * dt_s[j];
-        }
+        if (ii < rows && j <= i) m = cbr[(int64_t)i * Q + j] * ssd_exp(acs_s[i] - acs_s[j]) * dt_s[j];
         Ms[ii][j] = m;
     }
     __syncthreads();
@@ -775,11 +821,26 @@ void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
 }
 
 size_t chunk_scan_ws_bytes(const ScanShape &s) {
-    return mfma_supported(s) ? chunk_cb_bytes(s) : 0;
+    // the MFMA kernels' tiles, or a Q x Q fp32 C.B buffer per (b, c, g)
+    return mfma_supported(s) ? chunk_cb_bytes(s)
+                             : (size_t)(s.B * s.T * s.G) * (size_t)(s.Q * s.Q) * 4;
 }
 
 void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *ws, hipStream_t st) {
-    if (mfma_supported(s)) launch_chunk_cb_mfma(s, Bm, Cm, ws, st);
+    if (mfma_supported(s)) {
+        launch_chunk_cb_mfma(s, Bm, Cm, ws, st);
+        return;
+    }
+    if (s.B * s.T * s.G == 0) return;
+    dim3 grid((unsigned)(s.B * s.T * s.G), (unsigned)((s.Q + kScanRows - 1) / kScanRows));
+    if (s.dtype == SSD_BF16)
+        k_chunk_cb_generic<bf16><<<grid, 256, 0, st>>>((const bf16 *)Bm, (const bf16 *)Cm,
+                                                        (float *)ws, s.L, (int)s.N, (int)s.G,
+                                                        (int)s.Q, (int)s.T, s.ctab);
+    else
+        k_chunk_cb_generic<float><<<grid, 256, 0, st>>>((const float *)Bm, (const float *)Cm,
+                                                         (float *)ws, s.L, (int)s.N, (int)s.G,
+                                                         (int)s.Q, (int)s.T, s.ctab);
 }
 
 void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const void *Bm,
@@ -792,14 +853,14 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
     dim3 grid((unsigned)(s.B * s.T * s.H), (unsigned)((s.Q + kScanRows - 1) / kScanRows));
     if (s.dtype == SSD_BF16)
         k_chunk_scan_generic<bf16><<<grid, 256, 0, st>>>(
-            (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states, (bf16 *)y,
-            (const bf16 *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q, (int)s.T,
-            s.ctab);
+            (const bf16 *)x, dt, (const bf16 *)Bm, (const bf16 *)Cm, D, Acs, states,
+            (const float *)ws, (bf16 *)y, (const bf16 *)z, s.L, (int)s.H, (int)s.P, (int)s.N,
+            (int)s.G, (int)s.Q, (int)s.T, s.ctab);
     else
         k_chunk_scan_generic<float><<<grid, 256, 0, st>>>(
             (const float *)x, dt, (const float *)Bm, (const float *)Cm, D, Acs, states,
-            (float *)y, (const float *)z, s.L, (int)s.H, (int)s.P, (int)s.N, (int)s.G, (int)s.Q,
-            (int)s.T, s.ctab);
+            (const float *)ws, (float *)y, (const float *)z, s.L, (int)s.H, (int)s.P, (int)s.N,
+            (int)s.G, (int)s.Q, (int)s.T, s.ctab);
 }
 
 void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,

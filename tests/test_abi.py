@@ -84,11 +84,12 @@ def test_chunk_scan_workspace_size(L):
             assert st == OK and n == r256(1 * T * 2 * per)
     # ragged last chunk counts as a chunk
     assert cb_size(L, desc(seqlen=300, chunk=128)) == (OK, 3 * 2 * (10 * 4096 + 128 * 128 * 2))
-    # shapes the generic kernels run need none
-    assert cb_size(L, desc(dtype=0)) == (OK, 0)
-    assert cb_size(L, desc(headdim=32)) == (OK, 0)
-    assert cb_size(L, desc(chunk=32)) == (OK, 0)
-    assert cb_size(L, desc(dstate=256)) == (OK, 0)
+    # shapes the generic kernels run keep one chunk x chunk fp32 C.B matrix
+    # per (batch, chunk, group)
+    assert cb_size(L, desc(dtype=0)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
+    assert cb_size(L, desc(headdim=32)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
+    assert cb_size(L, desc(chunk=32)) == (OK, 1 * 16 * 2 * 32 * 32 * 4)
+    assert cb_size(L, desc(dstate=256)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
     assert cb_size(L, desc(seqlen=0)) == (OK, 0)
     assert cb_size(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_chunk_scan_workspace_size(ctypes.byref(desc()), None) == NULL
@@ -107,7 +108,7 @@ def test_workspace_size(L):
     assert st == OK and n == (r256(8 * 300 * 4) + r256(3 * 8 * 64 * 128 * 4)
                               + cb_size(L, desc(seqlen=300, chunk=128))[1] + r256(8 * 300 * 4))
     st, n = wsize(L, desc(dtype=0))
-    assert st == OK and n == r256(acs) + r256(states) + r256(acs)
+    assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc(dtype=0))[1] + r256(acs)
     assert wsize(L, desc(seqlen=0)) == (OK, 0)
     assert wsize(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_scan_workspace_size(ctypes.byref(desc()), None) == NULL
@@ -176,8 +177,14 @@ def test_chunk_cb_errors(L):
     assert L.ssd_chunk_cb(ctypes.byref(d), P16, P16, None, need, None) == NULL
     assert L.ssd_chunk_cb(ctypes.byref(d), P_MIS, P16, P16, need, None) == ALIGN
     assert L.ssd_chunk_cb(ctypes.byref(desc(chunk=48)), P16, P16, P16, need, None) == UNSUP
+    # the generic kernels' C.B matrices are checked the same way
+    g = desc(dtype=0)
+    _, gneed = cb_size(L, g)
+    assert gneed > 0
+    assert L.ssd_chunk_cb(ctypes.byref(g), P16, P16, P16, gneed - 1, None) == WS
+    assert L.ssd_chunk_cb(ctypes.byref(g), P16, P16, None, gneed, None) == NULL
     # shapes that need no workspace: a no-op, pointers untouched
-    for kw in (dict(dtype=0), dict(headdim=32), dict(seqlen=0), dict(batch=0)):
+    for kw in (dict(seqlen=0), dict(batch=0)):
         assert L.ssd_chunk_cb(ctypes.byref(desc(**kw)), None, None, None, 0, None) == OK
 
 
