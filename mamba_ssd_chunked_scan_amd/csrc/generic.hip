@@ -340,19 +340,42 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
     __syncthreads();
     const float Dh = D ? D[h] : 0.f;
     const float *Hc = states + ((b * T + c) * H + h) * (int64_t)P * N;
-    for (int e = threadIdx.x; e < rows * P; e += 256) {
-        const int ii = e / P, p = e % P;
-        const int i = i0 + ii;
-        float acc = 0.f;
-        for (int j = 0; j <= i; ++j)
-            acc += Ms[ii][j] * Elem<Tin>::ld(x, ((b * L + t0 + j) * H + h) * P + p);
-        float off = 0.f;
+    // each work item is one channel p and four rows ii0..ii0+3: every x and H
+    // value it loads feeds four rows.  Row i sums j = 0..i only (a later
+    // token's x never enters an earlier output, even through a 0 weight),
+    // in the order j = 0.., n = 0..; C rows past the chunk are 0.
+    constexpr int kRq = 4;
+    for (int e = threadIdx.x; e < (kScanRows / kRq) * P; e += 256) {
+        const int p = e % P, ii0 = (e / P) * kRq;
+        if (ii0 >= rows) continue;
+        float acc[kRq] = {0.f, 0.f, 0.f, 0.f}, off[kRq] = {0.f, 0.f, 0.f, 0.f};
+        const int ifirst = i0 + ii0;  // the first row of the item: j <= ifirst serves all four
+        for (int j = 0; j <= ifirst; ++j) {
+            const float xv = Elem<Tin>::ld(x, ((b * L + t0 + j) * H + h) * P + p);
+#pragma unroll
+            for (int r = 0; r < kRq; ++r) acc[r] += Ms[ii0 + r][j] * xv;
+        }
+        for (int j = ifirst + 1; j < min(jmax, ifirst + kRq); ++j) {
+            const float xv = Elem<Tin>::ld(x, ((b * L + t0 + j) * H + h) * P + p);
+#pragma unroll
+            for (int r = 1; r < kRq; ++r)
+                if (j <= ifirst + r) acc[r] += Ms[ii0 + r][j] * xv;
+        }
         const float *hr = Hc + (int64_t)p * N;
-        for (int n = 0; n < N; ++n) off += Cs[ii][n] * hr[n];
-        const int64_t xi = ((b * L + t0 + i) * H + h) * P + p;
-        float yv = acc + ssd_exp(acs_s[i]) * off + Dh * Elem<Tin>::ld(x, xi);
-        if (z) yv *= silu_f(Elem<Tin>::ld(z, xi));
-        Elem<Tin>::st(y, xi, yv);
+        for (int n = 0; n < N; ++n) {
+            const float hv = hr[n];
+#pragma unroll
+            for (int r = 0; r < kRq; ++r) off[r] += Cs[ii0 + r][n] * hv;
+        }
+#pragma unroll
+        for (int r = 0; r < kRq; ++r) {
+            const int ii = ii0 + r, i = i0 + ii;
+            if (ii >= rows) break;
+            const int64_t xi = ((b * L + t0 + i) * H + h) * P + p;
+            float yv = acc[r] + ssd_exp(acs_s[i]) * off[r] + Dh * Elem<Tin>::ld(x, xi);
+            if (z) yv *= silu_f(Elem<Tin>::ld(z, xi));
+            Elem<Tin>::st(y, xi, yv);
+        }
     }
 }
 
