@@ -193,6 +193,7 @@ def test_deterministic():
     (1, 256, 4, 16, 16, 1, 64, "f32"),
     (2, 300, 4, 64, 128, 2, 128, "bf16"),
     (1, 520, 3, 64, 64, 1, 256, "bf16"),
+    (2, 150, 6, 32, 32, 3, 32, "bf16"),      # generic kernels: groups, ragged tail
 ])
 def test_stages_against_chunked_form(shape):
     Bt, L, H, P, N, G, chunk, dt_ = shape
