@@ -90,7 +90,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 9. */
+/* ABI version of this header: 10. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -111,12 +111,34 @@ ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes);
  *   final_state [batch, nheads, headdim, dstate] fp32, or NULL (not written);
  *               may equal init_state (in-place continuation); no other aliasing.
  *   workspace   device buffer of at least ssd_scan_workspace_size bytes
- *               (may be NULL when that size is 0).
- * seqlen == 0 writes final_state = init_state (or zeros); batch == 0 is a no-op. */
+ *               (may be NULL when that size is 0).  Its contents need no
+ *               initialisation and are scratch after the call, except the
+ *               error word described at ssd_scan_error_word.
+ * seqlen == 0 writes final_state = init_state (or zeros); batch == 0 is a no-op.
+ *
+ * The chunked stages run as separate kernels.  For chunk 256 with bf16 x/B/C,
+ * headdim 64 and dstate 64 or 128, the environment variable
+ * SSD_PREFILL_PATH=fused selects instead a single kernel (after a small one
+ * that forms the C.B products shared by the heads of a group): each (batch
+ * row, chunk, head) block hands the state entering the next chunk on to the
+ * block of that chunk through the workspace ("a lightweight scan" of
+ * summary states between chunks, §3 "Chunked recurrence").  Its waits
+ * between blocks are bounded; see ssd_scan_error_word.  Both give the
+ * operation's result within the same tolerance; they differ in speed. */
 ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         const float *A, const void *B, const void *C, const float *D,
                         const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Byte offset, within the workspace of an ssd_scan_fwd(_ex) call of shape *d,
+ * of a 32-bit error word that the call sets to 0 before its hand-off kernel
+ * runs and to a nonzero value if one of that kernel's bounded waits for the
+ * state of an earlier chunk ran out (the results of such a call are not
+ * valid).  The caller may read it after the call completes.
+ * SSD_ERR_UNSUPPORTED when shape *d does not run the single-kernel path
+ * (there is no such wait then); the answer follows SSD_PREFILL_PATH as
+ * ssd_scan_fwd reads it. */
+ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset);
 
 /* ---------------------------------------------------------------- gradient */
 
@@ -267,12 +289,17 @@ ssd_status ssd_varlen_workspace_size(const ssd_varlen_desc *d, size_t *bytes);
  *   workspace    at least ssd_varlen_workspace_size bytes.
  * nseq == 0 is a no-op; total == 0 writes final = init for every sequence.
  * The chunk table is built on the device from cu_seqlens, so the call needs
- * no host copy of the lengths and can be captured in a HIP graph. */
+ * no host copy of the lengths and can be captured in a HIP graph.  Shapes of
+ * the single-kernel path of ssd_scan_fwd take it here too, with one
+ * hand-off chain per (sequence, head). */
 ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
                                const int32_t *cu_seqlens, const void *x, const float *dt,
                                const float *A, const void *B, const void *C, const float *D,
                                const float *init_states, void *y, float *final_states,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* As ssd_scan_error_word, for ssd_scan_fwd_varlen of shape *d. */
+ssd_status ssd_varlen_error_word(const ssd_varlen_desc *d, size_t *offset);
 
 /* The gradient of ssd_scan_fwd_varlen (its edges as for ssd_scan_bwd_ex):
  * every sequence's gradient on its own tokens, as ssd_scan_bwd_ex would give

@@ -27,7 +27,8 @@ EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "s
            "ssd_chunk_scan_workspace_size", "ssd_chunk_cb", "ssd_chunk_scan", "ssd_scan_fwd_ex",
            "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen",
            "ssd_scan_bwd_workspace_size", "ssd_scan_bwd", "ssd_scan_bwd_ex_workspace_size",
-           "ssd_scan_bwd_ex", "ssd_scan_bwd_varlen_workspace_size", "ssd_scan_bwd_varlen")
+           "ssd_scan_bwd_ex", "ssd_scan_bwd_varlen_workspace_size", "ssd_scan_bwd_varlen",
+           "ssd_scan_error_word", "ssd_varlen_error_word")
 
 
 class ScanDesc(ctypes.Structure):
@@ -71,7 +72,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 9  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 10  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -125,6 +126,9 @@ def lib() -> ctypes.CDLL:
                                           + [_P] * 11 + [ctypes.c_size_t, _P])
         L.ssd_step_multi_ex.argtypes = ([ctypes.POINTER(StepDesc), ctypes.POINTER(Edges),
                                          ctypes.c_int64] + [_P] * 9)
+        L.ssd_scan_error_word.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_varlen_error_word.argtypes = [ctypes.POINTER(VarlenDesc),
+                                            ctypes.POINTER(ctypes.c_size_t)]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -201,6 +205,21 @@ def workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype
     _check("ssd_scan_workspace_size", lib().ssd_scan_workspace_size(ctypes.byref(d),
                                                                     ctypes.byref(n)))
     return n.value
+
+
+def error_word(workspace, desc, varlen: bool = False):
+    """The error word of a finished ssd_scan_fwd(_ex) / ssd_scan_fwd_varlen call
+    that used ``workspace`` (a uint8 device tensor) for shape ``desc`` (a
+    ScanDesc or VarlenDesc): 0 when every hand-off wait of the call completed,
+    None when that shape runs no hand-off.  Reads device memory (synchronises
+    with the workspace's device)."""
+    off = ctypes.c_size_t(0)
+    fn = lib().ssd_varlen_error_word if varlen else lib().ssd_scan_error_word
+    st = fn(ctypes.byref(desc), ctypes.byref(off))
+    if st == 3:  # SSD_ERR_UNSUPPORTED: no hand-off on this shape's path
+        return None
+    _check("ssd_varlen_error_word" if varlen else "ssd_scan_error_word", st)
+    return int(workspace[off.value:off.value + 4].cpu().view(torch.int32).item())
 
 
 def _edges(x, H, P, dt_bias, dt_softplus, dt_limit, z, norm_weight=None, norm_eps=1e-5,

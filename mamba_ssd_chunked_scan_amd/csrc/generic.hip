@@ -394,7 +394,7 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
 // them.
 __global__ void __launch_bounds__(1024)
 k_varlen_table(const int32_t *__restrict__ cu, int NS, int total, int Q, int slots,
-               int2 *__restrict__ ctab, int2 *__restrict__ sch) {
+               int2 *__restrict__ ctab, int2 *__restrict__ sch, int2 *__restrict__ spos) {
     __shared__ int64_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int per = (NS + 1023) / 1024;
@@ -421,14 +421,36 @@ k_varlen_table(const int32_t *__restrict__ cu, int NS, int total, int Q, int slo
         const int t0 = start(s), len = length(s), nk = (len + Q - 1) / Q;
         const int64_t room = max((int64_t)0, (int64_t)slots - first);
         sch[s] = make_int2((int)min(first, (int64_t)slots), (int)min((int64_t)nk, room));
-        for (int j = 0; j < nk && j < room; ++j)
+        for (int j = 0; j < nk && j < room; ++j) {
             ctab[first + j] = make_int2(t0 + j * Q, min(Q, len - j * Q));
+            if (spos) spos[first + j] = make_int2(s, j);
+        }
         first += nk;
     }
-    for (int64_t k = nall + tid; k < slots; k += 1024) ctab[k] = make_int2(0, 0);
+    for (int64_t k = nall + tid; k < slots; k += 1024) {
+        ctab[k] = make_int2(0, 0);
+        if (spos) spos[k] = make_int2(-1, 0);
+    }
 }
 
 // ----------------------------------------------------------- misc
+// Final states of the sequences of a variable-length batch that have no
+// tokens (no chunk slot): their init state passes through (zeros without
+// one).  Grid-stride over (sequence, 4 state values).
+__global__ void k_empty_finals(const int2 *__restrict__ sch, int64_t NS, const float *init,
+                               float *fin, int64_t per) {
+    const int64_t n4 = NS * (per / 4);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = i / (per / 4);
+        if (sch[s].y != 0) continue;
+        const int64_t e = i * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (init) v = *reinterpret_cast<const float4 *>(init + e);
+        *reinterpret_cast<float4 *>(fin + e) = v;
+    }
+}
+
 __global__ void k_copy_or_zero(float *dst, const float *src, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src ? src[i] : 0.f;
@@ -887,8 +909,9 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
 }
 
 void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
-                         int2 *ctab, int2 *sch, hipStream_t st) {
-    k_varlen_table<<<1, 1024, 0, st>>>(cu, (int)NS, (int)total, (int)Q, (int)slots, ctab, sch);
+                         int2 *ctab, int2 *sch, int2 *spos, hipStream_t st) {
+    k_varlen_table<<<1, 1024, 0, st>>>(cu, (int)NS, (int)total, (int)Q, (int)slots, ctab, sch,
+                                       spos);
 }
 
 void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t H, int64_t P,
@@ -911,6 +934,14 @@ void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t
         else SSD_NORM(float, false);
     }
 #undef SSD_NORM
+}
+
+void launch_empty_finals(const int2 *sch, int64_t NS, const float *init, float *fin,
+                         int64_t per, hipStream_t st) {
+    if (!fin || NS <= 0) return;
+    const int64_t n4 = NS * (per / 4);
+    const unsigned blocks = (unsigned)(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
+    k_empty_finals<<<blocks, 256, 0, st>>>(sch, NS, init, fin, per);
 }
 
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {

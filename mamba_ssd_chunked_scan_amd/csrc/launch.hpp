@@ -16,6 +16,8 @@ struct ScanShape {
     const int2 *ctab = nullptr;
     const int2 *sch = nullptr;
     int64_t NS = 0;
+    // slot -> {sequence, position within it} (sequence -1: unused slot)
+    const int2 *spos = nullptr;
 };
 
 struct StepShape {
@@ -49,16 +51,23 @@ void launch_chunk_scan(const ScanShape &s, const void *x, const float *dt, const
                        const void *Cm, const float *D, const float *Acs, const float *states,
                        const void *ws, void *y, hipStream_t st, const void *z = nullptr);
 
-// Chunk table of a variable-length batch (ScanShape::ctab / sch) from the
-// sequences' token offsets cu[0..NS]; slots >= the number of chunks.
+// Chunk table of a variable-length batch (ScanShape::ctab / sch / spos) from
+// the sequences' token offsets cu[0..NS]; slots >= the number of chunks.
+// spos may be null.
 void launch_varlen_table(const int32_t *cu, int64_t NS, int64_t total, int64_t Q, int64_t slots,
-                         int2 *ctab, int2 *sch, hipStream_t st);
+                         int2 *ctab, int2 *sch, int2 *spos, hipStream_t st);
 
 // Gated RMSNorm of finished outputs, in place: y is ntok rows of H*P values
 // (heads outer), each split into NG groups of whole heads; every group is
 // scaled by 1 / sqrt(mean square + eps) and then by w (per channel).
 void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t H, int64_t P,
                        int64_t NG, int dtype, hipStream_t st);
+
+// Final states of a variable-length batch's empty sequences (sch[s].y == 0):
+// init (or zeros) copied to fin; per = state values per sequence (H P N, a
+// multiple of 4).  No-op when fin is null.
+void launch_empty_finals(const int2 *sch, int64_t NS, const float *init, float *fin,
+                         int64_t per, hipStream_t st);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
@@ -143,5 +152,25 @@ void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, 
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,
                             const float *D, const float *Acs, const float *states, const void *cb,
                             void *y, hipStream_t st, const void *z = nullptr);
+
+// The single-kernel prefill (chunk 256, MFMA shapes): chunk states handed on
+// from block to block.  Workspace: a 256-byte control block (ticket, error
+// word at byte 4), the hand-off flags, the C.B tiles and fragments, the
+// hand-off states.
+struct FusedWs {
+    unsigned *ctl;
+    unsigned long long *flags;
+    void *cb;
+    float *hand;
+};
+bool fused_supported(const ScanShape &s);
+size_t fused_ws_bytes(const ScanShape &s);
+FusedWs fused_ws_carve(const ScanShape &s, void *ws);
+// grp: chunks per hand-off group (>= 1); nq: work queues (1, or 8: one per
+// XCD); max_blocks: the persistent grid.
+void launch_scan_fused_chain(const ScanShape &s, const FusedWs &w, const void *x, const float *dt,
+                             const float *A, const void *Bm, const void *Cm, const float *D,
+                             const float *init, void *y, float *fin, hipStream_t st,
+                             const DtAct &act, const void *z, int grp, int nq, int max_blocks);
 
 }  // namespace ssd

@@ -4,6 +4,9 @@
 // hipGetLastError.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "launch.hpp"
 #include "ssd.h"
@@ -81,9 +84,64 @@ size_t scan_ws_bytes(const ScanShape &s) {
 // the activated dt of ssd_scan_fwd_ex, [B, L, H] fp32
 size_t dt_eff_bytes(const ScanShape &s) { return round_up((size_t)(s.B * s.L * s.H) * 4); }
 
+size_t staged_ws_bytes(const ScanShape &s) {
+    return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s) + dt_eff_bytes(s);
+}
+
+// Either path's workspace fits (the single-kernel path's, where it applies, or
+// the separate stages').
 size_t workspace_bytes(const ScanShape &s) {
     if (s.B == 0 || s.L == 0) return 0;
-    return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s) + dt_eff_bytes(s);
+    const size_t st = staged_ws_bytes(s);
+    if (!ssd::fused_supported(s)) return st;
+    const size_t fu = round_up(ssd::fused_ws_bytes(s));
+    return fu > st ? fu : st;
+}
+
+// Blocks the single-kernel prefill keeps resident: two per compute unit of
+// the current device (looked up once per device).
+int resident_blocks() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    v = 2 * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// The single-kernel prefill is opt-in (SSD_PREFILL_PATH=fused): measured side
+// by side it is slower than the separate stage kernels on every workload
+// shape so far.  The workspace fits either path.
+bool staged_forced() {
+    const char *e = getenv("SSD_PREFILL_PATH");
+    return !(e && e[0] == 'f');
+}
+
+// Work queues of the single-kernel prefill: one per XCD (heads split into 8
+// ranges), or one for all (SSD_CHAIN_QUEUES=1).
+int work_queues() {
+    const char *e = getenv("SSD_CHAIN_QUEUES");
+    return (e && atoi(e) == 1) ? 1 : 8;
+}
+
+// Chunks per hand-off group of the single-kernel prefill.  A chain of chunks
+// per (sequence, head) is handed on link by link; when there are fewer chains
+// than resident blocks, consecutive chunks of a chain run at the same time
+// and each link's latency is exposed, so the chain is cut into groups whose
+// chunks share one link.  SSD_CHAIN_GROUP (1, 2, 4 or 8) overrides the choice.
+int chain_group(int64_t chains, int resident) {
+    const char *e = getenv("SSD_CHAIN_GROUP");
+    const int forced = e ? atoi(e) : 0;
+    if (forced == 1 || forced == 2 || forced == 4 || forced == 8) return forced;
+    if (chains >= resident) return 1;
+    if (2 * chains >= resident) return 2;
+    return 4;
 }
 
 // ssd_edges -> the kernels' dt activation and gate pointer (NULL: neither).
@@ -144,9 +202,10 @@ ScanShape bwd_varlen_shape(const ScanShape &s) {
     return b;
 }
 
-// Chunk table and sequence table of a variable-length batch, after the rest.
+// Chunk table, sequence table and slot positions of a variable-length batch,
+// after the rest.
 size_t varlen_table_bytes(const ScanShape &s) {
-    return round_up((size_t)s.T * 8) + round_up((size_t)s.NS * 8);
+    return 2 * round_up((size_t)s.T * 8) + round_up((size_t)s.NS * 8);
 }
 
 ssd_status check_varlen(const ssd_varlen_desc *d, ScanShape *s) {
@@ -186,7 +245,15 @@ void run_scan(const ScanShape &s, const ssd::DtAct &act, const void *z, const vo
                         ? reinterpret_cast<float *>(ws + acs_bytes(s) + states_bytes(s) +
                                                     scan_ws_bytes(s))
                         : nullptr;
-    if (ssd::mfma_supported(s)) {
+    if (ssd::fused_supported(s) && !staged_forced()) {
+        const int res = resident_blocks();
+        const int64_t chains = (s.sch ? s.NS : s.B) * s.H;
+        ssd::launch_scan_fused_chain(s, ssd::fused_ws_carve(s, ws), x, dt, A, B, C, D, init_state,
+                                     y, final_state, hs, act, z, chain_group(chains, res),
+                                     work_queues(), res);
+        // a sequence without tokens has no block: its final state is its init
+        if (s.sch) ssd::launch_empty_finals(s.sch, s.NS, init_state, final_state, s.H * s.P * s.N, hs);
+    } else if (ssd::mfma_supported(s)) {
         ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
                                     scan_ws, hs, act, dt_eff, z);
     } else {
@@ -224,7 +291,29 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 9; }
+int ssd_abi_version(void) { return 10; }
+
+ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset) {
+    if (!offset) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0 || s.L == 0 || !ssd::fused_supported(s) || staged_forced())
+        return SSD_ERR_UNSUPPORTED;
+    *offset = 4;
+    return SSD_OK;
+}
+
+ssd_status ssd_varlen_error_word(const ssd_varlen_desc *d, size_t *offset) {
+    if (!offset) return SSD_ERR_NULL_PTR;
+    ScanShape s;
+    ssd_status st = check_varlen(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.NS == 0 || s.L == 0 || !ssd::fused_supported(s) || staged_forced())
+        return SSD_ERR_UNSUPPORTED;
+    *offset = 4;
+    return SSD_OK;
+}
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {
     if (!bytes) return SSD_ERR_NULL_PTR;
@@ -541,10 +630,13 @@ ssd_status ssd_scan_fwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
     char *ws = static_cast<char *>(workspace);
     int2 *ctab = reinterpret_cast<int2 *>(ws + base);
     int2 *sch = reinterpret_cast<int2 *>(ws + base + round_up((size_t)s.T * 8));
+    int2 *spos = reinterpret_cast<int2 *>(ws + base + round_up((size_t)s.T * 8) +
+                                          round_up((size_t)s.NS * 8));
     hipStream_t hs = as_stream(stream);
-    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, s.Q, s.T, ctab, sch, hs);
+    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, s.Q, s.T, ctab, sch, spos, hs);
     s.ctab = ctab;
     s.sch = sch;
+    s.spos = spos;
     run_scan(s, act, z, x, dt, A, B, C, D, init_states, y, final_states, ws, hs);
     if (nm.w) ssd::launch_gated_norm(y, nm.w, nm.eps, s.L, s.H, s.P, nm.groups, s.dtype, hs);
     return after_launch();
@@ -615,7 +707,7 @@ ssd_status ssd_scan_bwd_varlen(const ssd_varlen_desc *d, const ssd_edges *edges,
     char *ws = static_cast<char *>(workspace);
     int2 *ctab = reinterpret_cast<int2 *>(ws + base);
     int2 *sch = reinterpret_cast<int2 *>(ws + base + round_up((size_t)b.T * 8));
-    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, b.Q, b.T, ctab, sch, hs);
+    ssd::launch_varlen_table(cu_seqlens, s.NS, s.L, b.Q, b.T, ctab, sch, nullptr, hs);
     b.ctab = ctab;
     b.sch = sch;
     run_bwd(s, b, act, z, nm, edges != nullptr, in, o, ws, hs);

@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 9
+    assert L.ssd_abi_version() == 10
     for s in range(7):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -97,12 +97,27 @@ def test_chunk_scan_workspace_size(L):
 
 
 def test_workspace_size(L):
-    # Acs, chunk states, the chunk-output workspace, the activated dt
-    st, n = wsize(L, desc())
+    # the single-kernel path (chunk 256, bf16, headdim 64, dstate 64/128): a
+    # 256-byte control block, one 8-byte flag per 32x32 state tile of every
+    # (chunk, head), the C.B tiles and fragments, one hand-off state per
+    # (chunk, head); or, if larger, the staged path's workspace (Acs, chunk
+    # states, C.B tiles, activated dt), which the same shapes can also run
     T = 2
+    for dstate in (64, 128):
+        st, n = wsize(L, desc(dstate=dstate))
+        tiles = 2 * dstate // 32
+        cbn = cb_size(L, desc(dstate=dstate))[1]
+        fused = 256 + r256(T * 8 * tiles * 8) + cbn + r256(T * 8 * 64 * dstate * 4)
+        staged = 2 * r256(8 * 512 * 4) + r256(T * 8 * 64 * dstate * 4) + cbn
+        assert st == OK and n == max(fused, staged)
+    # the staged path: Acs, chunk states, the chunk-output workspace, the
+    # activated dt
     acs = 1 * 8 * 512 * 4
     states = 1 * T * 8 * 64 * 128 * 4
-    assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc())[1] + r256(acs)
+    st, n = wsize(L, desc(chunk=128))
+    T128 = 4
+    assert st == OK and n == (r256(acs) + r256(T128 * 8 * 64 * 128 * 4)
+                              + cb_size(L, desc(chunk=128))[1] + r256(acs))
     # ragged last chunk counts as a chunk
     st, n = wsize(L, desc(seqlen=300, chunk=128))
     assert st == OK and n == (r256(8 * 300 * 4) + r256(3 * 8 * 64 * 128 * 4)
@@ -112,6 +127,28 @@ def test_workspace_size(L):
     assert wsize(L, desc(seqlen=0)) == (OK, 0)
     assert wsize(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_scan_workspace_size(ctypes.byref(desc()), None) == NULL
+
+
+def test_error_word_offset(L, monkeypatch):
+    off = ctypes.c_size_t(99)
+    # the staged path (the default) has no hand-off wait
+    monkeypatch.delenv("SSD_PREFILL_PATH", raising=False)
+    assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == UNSUP
+    monkeypatch.setenv("SSD_PREFILL_PATH", "fused")
+    # the single-kernel path keeps its error word at byte 4 of the workspace
+    assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == OK and off.value == 4
+    assert L.ssd_scan_error_word(ctypes.byref(desc(dstate=64)), ctypes.byref(off)) == OK
+    # other paths have no hand-off wait
+    for kw in (dict(chunk=128), dict(dtype=0), dict(headdim=32), dict(seqlen=0)):
+        assert L.ssd_scan_error_word(ctypes.byref(desc(**kw)), ctypes.byref(off)) == UNSUP
+    assert L.ssd_scan_error_word(ctypes.byref(desc(chunk=48)), ctypes.byref(off)) == UNSUP
+    assert L.ssd_scan_error_word(ctypes.byref(desc(nheads=0)), ctypes.byref(off)) == SHAPE
+    assert L.ssd_scan_error_word(ctypes.byref(desc()), None) == NULL
+    assert L.ssd_scan_error_word(None, ctypes.byref(off)) == NULL
+    vd = binding.VarlenDesc(3, 900, 8, 64, 128, 2, 256, 1, 0)
+    assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == OK and off.value == 4
+    vd = binding.VarlenDesc(3, 900, 8, 64, 128, 2, 64, 1, 0)
+    assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == UNSUP
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -284,16 +321,27 @@ def vwsize(L, d):
 
 
 def test_varlen_workspace_size(L):
-    # the fixed-chunking workspace of one 700-token row with 700/256 + 3 = 5
-    # chunk slots (every sequence may end in a short chunk), then the chunk
-    # table (8 bytes a slot) and the sequence table (8 bytes a sequence)
+    # the workspace of one 700-token row with 700/256 + 3 = 5 chunk slots
+    # (every sequence may end in a short chunk) on the single-kernel path
+    # (control block, flags, C.B tiles, hand-off states), then the chunk
+    # table (8 bytes a slot), the sequence table (8 bytes a sequence) and the
+    # slot positions (8 bytes a slot)
     slots = 700 // 256 + 3
-    acs = 8 * 700 * 4
-    states = slots * 8 * 64 * 128 * 4
     cbw = slots * 2 * (36 * 4096 + 256 * 128 * 2)
     st, n = vwsize(L, vdesc())
     assert st == OK
-    assert n == r256(acs) + r256(states) + r256(cbw) + r256(acs) + r256(slots * 8) + r256(3 * 8)
+    fused = 256 + r256(slots * 8 * 8 * 8) + r256(cbw) + r256(slots * 8 * 64 * 128 * 4)
+    staged = 2 * r256(8 * 700 * 4) + r256(slots * 8 * 64 * 128 * 4) + r256(cbw)
+    assert n == max(fused, staged) + 2 * r256(slots * 8) + r256(3 * 8)
+    # the staged path (chunk 128): Acs, chunk states, C.B, activated dt
+    slots = 700 // 128 + 3
+    acs = 8 * 700 * 4
+    states = slots * 8 * 64 * 128 * 4
+    cbw = slots * 2 * (10 * 4096 + 128 * 128 * 2)
+    st, n = vwsize(L, vdesc(chunk=128))
+    assert st == OK
+    assert n == (r256(acs) + r256(states) + r256(cbw) + r256(acs) + 2 * r256(slots * 8)
+                 + r256(3 * 8))
     assert vwsize(L, vdesc(nseq=0)) == (OK, 0)
     assert vwsize(L, vdesc(total=0)) == (OK, 0)
     assert L.ssd_varlen_workspace_size(ctypes.byref(vdesc()), None) == NULL
@@ -465,14 +513,14 @@ def test_bwd_ex_workspace_and_errors(L):
 
 def test_bwd_varlen_workspace_and_errors(L):
     """ssd_scan_bwd_varlen: the gradient's core at 64-token slots (total / 64
-    + nseq of them) plus the chunk and sequence tables; nothing for an empty
+    + nseq of them) plus the chunk, sequence and slot tables; nothing for an empty
     batch; the same edge and pointer checks as ssd_scan_bwd_ex."""
     d = vdesc()   # 3 sequences, 700 tokens, 8 heads, headdim 64, dstate 128, bf16
     n = ctypes.c_size_t(0)
     assert L.ssd_scan_bwd_varlen_workspace_size(ctypes.byref(d), None, ctypes.byref(n)) == OK
     slots = 700 // 64 + 3
     core = r256(8 * 700 * 4) + 2 * r256(slots * 8 * 64 * 128 * 4)
-    assert n.value == core + r256(slots * 8) + r256(3 * 8)
+    assert n.value == core + 2 * r256(slots * 8) + r256(3 * 8)
     assert L.ssd_scan_bwd_varlen_workspace_size(ctypes.byref(vdesc(nseq=0, total=0)), None,
                                                 ctypes.byref(n)) == OK and n.value == 0
     eg = edges(dt_bias=P16, dt_softplus=1, z=P16)

@@ -65,11 +65,15 @@ def _reference(inp, which):
     return yo, fo
 
 
+@pytest.mark.parametrize("path", ["staged", "fused"])
 @pytest.mark.parametrize("which", ["all", "dt", "gate"])
 @pytest.mark.parametrize("name", list(SPECS))
-def test_scan_edges_vs_oracle(name, which):
+def test_scan_edges_vs_oracle(name, which, path, monkeypatch):
     spec = SPECS[name]
-    announce(f"scan edges {name} {which}")
+    if path == "fused" and spec.chunk != 256:
+        pytest.skip("the single-kernel path covers chunk 256 only")
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    announce(f"scan edges {name} {which} path={path}")
     inp = synth.scan_edge_inputs(spec)
     y, fin = _run(spec, which, inp)
     yo, fo = _reference(inp, which)

@@ -14,7 +14,7 @@ import torch
 import oracle
 from oracle.chunked import chunked_scan
 import mamba_ssd_chunked_scan_amd as ssd
-from mamba_ssd_chunked_scan_amd import synth
+from mamba_ssd_chunked_scan_amd import binding, synth
 
 from helpers import TOL, f64, oracle_args, rel_err, to_dev
 
@@ -28,10 +28,18 @@ def announce(msg):
 
 
 def run_gpu(inp, chunk, **kw):
+    """ssd_scan_fwd on the device copies of inp; on shapes that run the
+    single-kernel path, also checks that every hand-off wait completed."""
     d = to_dev(inp, DEV)
-    y, fin = ssd.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=chunk,
-                          init_state=d["init"], **kw)
+    x = d["x"]
+    ws = torch.empty(max(ssd.workspace_size(x.shape[0], x.shape[1], x.shape[2], x.shape[3],
+                                            d["B"].shape[3], d["B"].shape[2], chunk, x.dtype), 1),
+                     dtype=torch.uint8, device=DEV)
+    y, fin = ssd.scan_fwd(x, d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=chunk,
+                          init_state=d["init"], workspace=ws, **kw)
     torch.cuda.synchronize()
+    err = binding.error_word(ws, binding._scan_desc(x, d["B"], chunk))
+    assert err in (None, 0), f"a hand-off wait ran out (error word {err})"
     return y, fin
 
 
@@ -254,3 +262,61 @@ def test_fwd_repeats_bit_for_bit():
     for y, fin in outs[1:]:
         assert torch.equal(y, outs[0][0])
         assert torch.equal(fin, outs[0][1])
+
+
+@pytest.mark.parametrize("grp", ["1", "2", "4", "8"])
+def test_chain_groups(grp, monkeypatch):
+    """Every hand-off grouping of the single-kernel path (chunks per group,
+    forced through SSD_CHAIN_GROUP): several batch rows, a ragged last chunk,
+    a chain longer than a group, and the final state written over the init
+    state it started from."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", "fused")
+    monkeypatch.setenv("SSD_CHAIN_GROUP", grp)
+    spec = synth.custom_spec(2, 9 * 256 + 77, 6, 64, 128, 2, 256, "bf16", dt_rule="ranged",
+                             init="normal", seed=21)
+    announce(f"chain group {grp} {spec}")
+    inp = synth.scan_inputs(spec)
+    d = to_dev(inp, DEV)
+    h = d["init"].clone()
+    x = d["x"]
+    ws = torch.empty(ssd.workspace_size(2, spec.seqlen, 6, 64, 128, 2, 256, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    y, fin = ssd.scan_fwd(x, d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=256, init_state=h,
+                          final_state=h, workspace=ws)
+    torch.cuda.synchronize()
+    assert binding.error_word(ws, binding._scan_desc(x, d["B"], 256)) == 0
+    yo, fo = oracle.scan(**oracle_args(inp))
+    ey, ef = rel_err(f64(y), yo), rel_err(f64(h), fo)
+    print(f"  rel_err y {ey:.3e} final {ef:.3e}", flush=True)
+    assert ey <= TOL[torch.bfloat16] and ef <= TOL[torch.bfloat16]
+
+
+FUSED_SHAPES = [
+    # Bt, L, H, P, N, G: chunk 256, bf16 (the single-kernel path's scope)
+    (2, 513, 4, 64, 128, 2),     # ragged last chunk, two groups
+    (1, 100, 3, 64, 64, 1),      # one partial chunk
+    (3, 1024, 8, 64, 128, 4),    # four full chunks, four groups
+    (1, 2048, 24, 64, 128, 1),   # the 130M head shape
+]
+
+
+@pytest.mark.parametrize("queues", ["1", "8"])
+@pytest.mark.parametrize("shape", FUSED_SHAPES)
+def test_fused_path_shapes(shape, queues, monkeypatch):
+    """The opt-in single-kernel prefill against the oracle, with one work
+    queue and with one queue per XCD."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", "fused")
+    monkeypatch.setenv("SSD_CHAIN_QUEUES", queues)
+    Bt, L, H, P, N, G = shape
+    announce(f"fused path {shape} queues {queues}")
+    spec = synth.custom_spec(Bt, L, H, P, N, G, 256, "bf16", dt_rule="ranged", init="normal",
+                             seed=31 + FUSED_SHAPES.index(shape))
+    check_full(synth.scan_inputs(spec), 256, torch.bfloat16)
+
+
+def test_fused_path_2p7b_sampled(monkeypatch):
+    monkeypatch.setenv("SSD_PREFILL_PATH", "fused")
+    spec = synth.WORKLOADS["m2p7b_bf16"]
+    announce(f"fused path {spec.name} sampled heads")
+    sampled_check(synth.scan_inputs(spec), spec.chunk, [(0, 0), (0, 33), (0, 79)],
+                  torch.bfloat16)

@@ -51,11 +51,15 @@ def _run(d, chunk, edges=False, **kw):
     return y, fin
 
 
+@pytest.mark.parametrize("path", ["staged", "fused"])
 @pytest.mark.parametrize("edges", [False, True])
 @pytest.mark.parametrize("name", list(CASES))
-def test_varlen_vs_oracle(name, edges):
+def test_varlen_vs_oracle(name, edges, path, monkeypatch):
     lengths, H, P, N, G, Q, dt_ = CASES[name]
-    announce(f"varlen {name} edges={edges}")
+    if path == "fused" and Q != 256:
+        pytest.skip("the single-kernel path covers chunk 256 only")
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    announce(f"varlen {name} edges={edges} path={path}")
     inp = synth.varlen_inputs(lengths, H, P, N, G, dt_, seed=41)
     y, fin = _run(_dev(inp), Q, edges)
     dt = (oe.dt_activation(inp["dt_raw"], inp["dt_bias"], True, LIMIT) if edges else inp["dt"])
@@ -89,12 +93,14 @@ def test_equal_lengths_equal_batched_call(Bt, L, H, P, N, G, Q, dt_):
     assert torch.equal(y, yb.view(y.shape)) and torch.equal(fin, fb)
 
 
-def test_serving_mix_2p7b_sampled():
+@pytest.mark.parametrize("path", ["staged", "fused"])
+def test_serving_mix_2p7b_sampled(path, monkeypatch):
     """32 requests of log-uniform length in [16, 4096] at the 2.7B head shape
     (80 heads), in the launch configuration the bench times; 8 sampled
     (sequence, head) pairs against the oracle one by one."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
     lengths = synth.serving_lengths(32, seed=7)
-    announce(f"varlen serving mix total={sum(lengths)}")
+    announce(f"varlen serving mix total={sum(lengths)} path={path}")
     inp = synth.varlen_inputs(lengths, 80, 64, 128, 1, "bf16", seed=43)
     y, fin = _run(_dev(inp), 256)
     cu = inp["cu_seqlens"].tolist()
