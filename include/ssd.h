@@ -56,7 +56,9 @@ typedef enum ssd_status {
                                 unknown dtype, or dt_limit with dt_min > dt_max  */
     SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                 */
     SSD_ERR_WORKSPACE = 5,   /* workspace smaller than its *_workspace_size      */
-    SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch      */
+    SSD_ERR_HIP = 6,         /* the HIP runtime reported an error at launch      */
+    SSD_ERR_SCRATCH = 7      /* the call needs more than SSD_NOALLOC_SCRATCH_BYTES
+                                of built-in scratch (ssd_scan_fwd_noalloc only)   */
 } ssd_status;
 
 typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -90,7 +92,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 10. */
+/* ABI version of this header: 11. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */
@@ -129,6 +131,28 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         const float *A, const void *B, const void *C, const float *D,
                         const float *init_state, void *y, float *final_state,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device scratch built into the library for ssd_scan_fwd_noalloc:
+ * 64 MiB on each device the library is loaded on (the 2.7B head shape at
+ * 4096 tokens needs about 48 MB). */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* ssd_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the workspace ssd_scan_workspace_size
+ * reports for *d is taken from SSD_NOALLOC_SCRATCH_BYTES of scratch that the
+ * library holds on each device (a static device array, not an allocation).
+ * The call allocates nothing and frees nothing; its results are those of
+ * ssd_scan_fwd on the same arguments.  A shape that needs more than the
+ * scratch holds returns SSD_ERR_SCRATCH before anything is enqueued.  Every
+ * call on one device shares that device's scratch: two calls that may
+ * overlap on one device (different streams, or threads) race and must not be
+ * made.  The first call on a device looks up the scratch's device address
+ * (hipGetSymbolAddress); a failure there returns SSD_ERR_HIP. */
+ssd_status ssd_scan_fwd_noalloc(const ssd_scan_desc *d, const void *x, const float *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, void *y, float *final_state,
+                                void *stream);
 
 /* Byte offset, within the workspace of an ssd_scan_fwd(_ex) call of shape *d,
  * of a 32-bit error word that the call sets to 0 before its hand-off kernel

@@ -19,7 +19,8 @@ SSD_OK = 0
 SSD_F32, SSD_BF16 = 0, 1
 _STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_NULL_PTR", 2: "SSD_ERR_SHAPE",
                  3: "SSD_ERR_UNSUPPORTED", 4: "SSD_ERR_ALIGN", 5: "SSD_ERR_WORKSPACE",
-                 6: "SSD_ERR_HIP"}
+                 6: "SSD_ERR_HIP", 7: "SSD_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # include/ssd.h SSD_NOALLOC_SCRATCH_BYTES
 
 # Every function include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "ssd_scan_fwd",
@@ -28,7 +29,7 @@ EXPORTS = ("ssd_status_string", "ssd_abi_version", "ssd_scan_workspace_size", "s
            "ssd_step_ex", "ssd_step_multi_ex", "ssd_varlen_workspace_size", "ssd_scan_fwd_varlen",
            "ssd_scan_bwd_workspace_size", "ssd_scan_bwd", "ssd_scan_bwd_ex_workspace_size",
            "ssd_scan_bwd_ex", "ssd_scan_bwd_varlen_workspace_size", "ssd_scan_bwd_varlen",
-           "ssd_scan_error_word", "ssd_varlen_error_word")
+           "ssd_scan_error_word", "ssd_varlen_error_word", "ssd_scan_fwd_noalloc")
 
 
 class ScanDesc(ctypes.Structure):
@@ -72,7 +73,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 10  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 11  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:
@@ -127,6 +128,7 @@ def lib() -> ctypes.CDLL:
         L.ssd_step_multi_ex.argtypes = ([ctypes.POINTER(StepDesc), ctypes.POINTER(Edges),
                                          ctypes.c_int64] + [_P] * 9)
         L.ssd_scan_error_word.argtypes = [ctypes.POINTER(ScanDesc), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanDesc)] + [_P] * 10
         L.ssd_varlen_error_word.argtypes = [ctypes.POINTER(VarlenDesc),
                                             ctypes.POINTER(ctypes.c_size_t)]
         for name in EXPORTS[2:]:

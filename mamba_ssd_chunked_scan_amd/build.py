@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libssd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ssd_api.cpp", "generic.hip", "mfma.hip", "fused.hip", "backward.hip"]
+SOURCES = ["ssd_api.cpp", "generic.hip", "mfma.hip", "fused.hip", "backward.hip", "noalloc.hip"]
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

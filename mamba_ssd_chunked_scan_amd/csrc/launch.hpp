@@ -69,6 +69,10 @@ void launch_gated_norm(void *y, const float *w, float eps, int64_t ntok, int64_t
 void launch_empty_finals(const int2 *sch, int64_t NS, const float *init, float *fin,
                          int64_t per, hipStream_t st);
 
+// The current device's address of the built-in scratch of
+// ssd_scan_fwd_noalloc (SSD_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t scratch_ptr(void **out);
+
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
 

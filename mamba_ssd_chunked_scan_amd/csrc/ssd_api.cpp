@@ -287,11 +287,14 @@ const char *ssd_status_string(int status) {
     case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case SSD_ERR_WORKSPACE: return "workspace is smaller than the size its query function reports";
     case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case SSD_ERR_SCRATCH:
+        return "the call needs more device scratch than the library's built-in "
+               "SSD_NOALLOC_SCRATCH_BYTES (use ssd_scan_fwd with a workspace)";
     default: return "unknown status";
     }
 }
 
-int ssd_abi_version(void) { return 10; }
+int ssd_abi_version(void) { return 11; }
 
 ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset) {
     if (!offset) return SSD_ERR_NULL_PTR;
@@ -720,6 +723,33 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt, 
                         void *stream) {
     return ssd_scan_fwd_ex(d, nullptr, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                            ws_bytes, stream);
+}
+
+ssd_status ssd_scan_fwd_noalloc(const ssd_scan_desc *d, const void *x, const float *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *init_state, void *y, float *final_state,
+                                void *stream) {
+    ScanShape s;
+    ssd_status st = check_scan(d, &s);
+    if (st != SSD_OK) return st;
+    if (s.B == 0) return SSD_OK;
+    if (s.L == 0) {
+        st = check_ptrs({}, {init_state, final_state});
+        if (st != SSD_OK) return st;
+        if (final_state)
+            ssd::launch_copy_or_zero(final_state, init_state, s.B * s.H * s.P * s.N,
+                                     as_stream(stream));
+        return after_launch();
+    }
+    st = check_ptrs({x, dt, A, B, C, y}, {D, init_state, final_state});
+    if (st != SSD_OK) return st;
+    const size_t need = workspace_bytes(s);
+    if (need > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (ssd::scratch_ptr(&ws) != hipSuccess || !ws) return SSD_ERR_HIP;
+    run_scan(s, ssd::DtAct{}, nullptr, x, dt, A, B, C, D, init_state, y, final_state,
+             static_cast<char *>(ws), as_stream(stream));
+    return after_launch();
 }
 
 ssd_status ssd_step_multi_ex(const ssd_step_desc *d, const ssd_edges *edges, int64_t nsteps,

@@ -11,7 +11,7 @@ import pytest
 from mamba_ssd_chunked_scan_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP = range(7)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, SCRATCH = range(8)
 
 # fake device addresses: never dereferenced, since validation fails first
 P16 = 0x10000
@@ -37,8 +37,8 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 10
-    for s in range(7):
+    assert L.ssd_abi_version() == 11
+    for s in range(8):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
 
@@ -537,3 +537,29 @@ def test_bwd_varlen_workspace_and_errors(L):
                                      need, None) == ALIGN, which
     assert L.ssd_scan_bwd_varlen(ctypes.byref(d), ctypes.byref(eg), *args, P16, P16, P16, P16,
                                  need - 1, None) == WS
+
+
+def test_noalloc_checks(L):
+    """ssd_scan_fwd_noalloc: every argument check runs before its first HIP
+    call, and a shape whose workspace exceeds the built-in scratch is refused
+    with SSD_ERR_SCRATCH (all of this without a device)."""
+    ptrs = [P16] * 9  # x dt A B C D init y final
+    assert L.ssd_scan_fwd_noalloc(None, *ptrs, None) == NULL
+    assert L.ssd_scan_fwd_noalloc(ctypes.byref(desc(nheads=6, ngroups=4)), *ptrs, None) == SHAPE
+    assert L.ssd_scan_fwd_noalloc(ctypes.byref(desc(chunk=48)), *ptrs, None) == UNSUP
+    for which in (0, 1, 2, 3, 4, 7):   # the required pointers
+        p = list(ptrs)
+        p[which] = None
+        assert L.ssd_scan_fwd_noalloc(ctypes.byref(desc()), *p, None) == NULL
+    for which in range(9):
+        p = list(ptrs)
+        p[which] = P_MIS
+        assert L.ssd_scan_fwd_noalloc(ctypes.byref(desc()), *p, None) == ALIGN
+    # the batched long prefill (8 x 16384 tokens, 80 heads) needs ~2.3 GB
+    big = desc(batch=8, seqlen=16384, nheads=80, ngroups=8)
+    assert wsize(L, big)[1] > binding.NOALLOC_SCRATCH_BYTES
+    assert L.ssd_scan_fwd_noalloc(ctypes.byref(big), *ptrs, None) == SCRATCH
+    # the 2.7B head shape at 4096 tokens fits
+    assert wsize(L, desc(seqlen=4096, nheads=80, ngroups=1))[1] <= binding.NOALLOC_SCRATCH_BYTES
+    assert L.ssd_scan_fwd_noalloc(ctypes.byref(desc(batch=0)), *ptrs, None) == OK
+    assert binding.status_string(SCRATCH).startswith("the call needs more device scratch")
