@@ -13,7 +13,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libssd.so")
+# SSD_LIB names another build of the library to load instead (the sanitizer
+# test runs the argument checks against a host-sanitized build this way)
+LIB_PATH = os.environ.get("SSD_LIB") or os.path.join(HERE, "libssd.so")
 
 SSD_OK = 0
 SSD_F32, SSD_BF16 = 0, 1

@@ -26,7 +26,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_LIB names another build of ssd_oracle.c to load instead (the
+# sanitizer test runs the pins against an ASan/UBSan build this way)
+_LIB_PATH = os.environ.get("SSD_ORACLE_LIB") or os.path.join(_HERE, "libssd_oracle.so")
 _lib = None
 
 _D = ctypes.POINTER(ctypes.c_double)
@@ -94,6 +96,8 @@ def scan(x, dt, A, B, C, D=None, init=None, nthreads: int = 0):
     rc = _load().ssd_oracle_scan(Bt, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                  _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final),
                                  int(nthreads))
+    if rc == -2:
+        raise MemoryError("oracle: the per-thread state rows could not be allocated")
     if rc != 0:
         raise ValueError("oracle: invalid shape")
     return y, final

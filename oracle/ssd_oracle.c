@@ -86,7 +86,8 @@ int ssd_oracle_max_threads(void)
 }
 
 /* Full-sequence scan.  D, init and final_state may be NULL (D, init -> 0;
- * final -> not written).  Returns 0, or -1 for an invalid shape. */
+ * final -> not written).  Returns 0, -1 for an invalid shape, or -2 when the
+ * per-thread state rows cannot be allocated (nothing is written then). */
 int ssd_oracle_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                     const double *x, const double *dt, const double *A,
                     const double *Bm, const double *Cm, const double *D,
@@ -96,9 +97,17 @@ int ssd_oracle_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int6
     set_threads(nthreads);
     const int64_t R = H / G;
     const int64_t rows = Bt * H * P;
+    /* one state row per thread, allocated (and checked) before the threads start */
+    const int nt = ssd_oracle_max_threads();
+    double *srows = (double *)malloc((size_t)(nt > 0 ? nt : 1) * (size_t)N * sizeof(double));
+    if (!srows) return -2;
 #pragma omp parallel
     {
-        double *s = (double *)malloc((size_t)N * sizeof(double));
+#ifdef _OPENMP
+        double *s = srows + (size_t)omp_get_thread_num() * (size_t)N;
+#else
+        double *s = srows;
+#endif
 #pragma omp for schedule(static)
         for (int64_t row = 0; row < rows; ++row) {
             const int64_t p = row % P;
@@ -120,8 +129,8 @@ int ssd_oracle_scan(int64_t Bt, int64_t L, int64_t H, int64_t P, int64_t N, int6
             if (final_state)
                 for (int64_t n = 0; n < N; ++n) final_state[sbase + n] = s[n];
         }
-        free(s);
     }
+    free(srows);
     return 0;
 }
 
