@@ -12,10 +12,21 @@ graph-replayed time per call are reported beside it).  The cached decode step
 (ssd_step) at the same head shape
 is timed alongside at batch 1 and 64.  Prints ONE JSON line.
 
-`value` is prefill tokens/s.  `roofline` is for the dominant kernel: its
-algorithmic HBM bytes per launch over its average launch time, measured here
-with HIP events on the stream it runs on.  `cpu_baseline` is the fp64 CPU
-oracle on the same workload.  A second GPU is never used.
+`value` is prefill tokens/s.  `roofline` is for the dominant kernel: the
+method's own HBM bytes of one call (x, y, B, C, dt, the initial and final
+states, A, D) over that kernel's average launch time, measured here with HIP
+events on the stream it runs on; the same bytes over the whole call
+(`call_frac`), the kernel's bytes with the intermediates it moves, and the
+kernel-trace sum and counted HBM traffic of one call from the committed
+rocprofv3 summary (while that summary matches the sources) sit beside it.
+`hbm_ceiling_GB_s` is what plain copy / read / write kernels reach on this
+part.  Decode figures are cold: every timed step follows a 1 GiB read that
+evicts the state from the caches.  `cpu_baseline` is the fp64 CPU oracle on
+the same workload.  A second GPU is never used.
+
+    --prefill-only       only the W + K prefill calls (kernel traces, counters)
+    --decode-cold-only   only the cold decode steps
+    --calibrate          end with 256 MiB reads and writes (counter calibration)
 """
 from __future__ import annotations
 
@@ -75,29 +86,122 @@ def decode_bytes(batch, H, P, N, G, e=2) -> int:
         + 2 * batch * G * N * e + 2 * H * 4
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "chunk_scan_m2p7b_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "mamba_ssd_chunked_scan_amd", "csrc", "mfma.hip")
+PROFILE = os.path.join(ROOT, "profiles", "prefill_m2p7b_summary.md")
+SRC_DIRS = (os.path.join(ROOT, "mamba_ssd_chunked_scan_amd", "csrc"), os.path.join(ROOT, "include"))
+FLUSH_BYTES = 1 << 30   # what the cold decode steps read first to evict every cache
 
 
-def measured_traffic():
-    """HBM bytes per chunk-output launch from the committed counter summary
-    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter read for a
-    plain device copy of known size), or None when that summary is missing or
-    was taken on a different kernel source than the one built now."""
+def source_sha256() -> str:
+    """SHA-256 over libssd's sources (csrc/ and include/ by name, without the
+    benchmark's own bandwidth kernels): the profile summaries record the value
+    they were taken on."""
     import hashlib
+    h = hashlib.sha256()
+    for d in SRC_DIRS:
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if (os.path.isfile(path) and name.endswith((".hip", ".hpp", ".cpp", ".h"))
+                    and not name.startswith("bw_probe")):
+                h.update(name.encode())
+                h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def profile_figures() -> dict:
+    """Figures of the committed rocprofv3 summary of the bench workload
+    (kernel-trace sum of one call, HBM traffic from FETCH_SIZE / WRITE_SIZE),
+    or {} when the summary is missing or was taken on other sources."""
     try:
-        text = open(COUNTERS).read()
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        text = open(PROFILE).read()
     except OSError:
-        return None
-    fields = dict(line.split(":", 1) for line in text.splitlines()
-                  if line.startswith(("kernel_source_sha256:", "traffic_bytes_per_launch:")))
-    if fields.get("kernel_source_sha256", "").strip() != src:
-        return None
-    try:
-        return int(fields["traffic_bytes_per_launch"].strip())
-    except (KeyError, ValueError):
-        return None
+        return {}
+    fields = {}
+    for line in text.splitlines():
+        key, sep, val = line.partition(":")
+        if sep and key.strip().replace("_", "").isalnum():
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != source_sha256():
+        return {}
+    figs = {}
+    for k in ("call_kernel_sum_us", "call_traffic_bytes", "dominant_traffic_bytes_per_launch",
+              "dominant_trace_avg_us"):
+        try:
+            figs[k] = float(fields[k])
+        except (KeyError, ValueError):
+            pass
+    return figs
+
+
+def roofline(method_bytes, kernel, kernel_us, kernel_bytes, call_us, prof) -> dict:
+    """The roofline line of the dominant kernel.  `achieved` counts the
+    method's own bytes of one call (x, y, B, C, dt, init and final states, A,
+    D: every one of the call's (batch, chunk, head) units passes through this
+    kernel) over the kernel's average launch time; the kernel's bytes
+    including the intermediates it moves (entering states, C.B tiles) are
+    reported beside it, as is the whole call on the same basis."""
+    ach = method_bytes / (kernel_us * 1e-6) / 1e9
+    out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(ach / HBM_PEAK_GBS, 4),
+           "traffic": prof.get("dominant_traffic_bytes_per_launch"),
+           "kernel": kernel, "avg_launch_us": round(kernel_us, 2),
+           "algorithmic_bytes_per_launch": method_bytes,
+           "kernel_bytes_with_intermediates": kernel_bytes,
+           "kernel_frac_with_intermediates": round(
+               kernel_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "call_frac": round(method_bytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "call_kernel_sum_us": prof.get("call_kernel_sum_us"),
+           "call_traffic_bytes": prof.get("call_traffic_bytes")}
+    if out["call_traffic_bytes"]:
+        out["call_traffic_ratio"] = round(out["call_traffic_bytes"] / method_bytes, 3)
+    if "dominant_trace_avg_us" in prof:
+        out["trace_avg_launch_us"] = prof["dominant_trace_avg_us"]
+    return out
+
+
+class BandwidthProbe:
+    """Plain copy / read / write kernels of known size (libssd_bw.so, built
+    beside libssd): the practical HBM ceiling on this part."""
+
+    def __init__(self, torch):
+        import ctypes
+        path = os.path.join(ROOT, "mamba_ssd_chunked_scan_amd", "libssd_bw.so")
+        self.torch = torch
+        self.lib = ctypes.CDLL(path)
+        self.lib.ssd_bw_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        self.lib.ssd_bw_run.restype = ctypes.c_int
+
+    def run(self, kind, dst, src, nbytes):
+        import ctypes
+        st = self.torch.cuda.current_stream().cuda_stream
+        rc = self.lib.ssd_bw_run(kind, ctypes.c_void_p(dst.data_ptr()),
+                                 None if src is None else ctypes.c_void_p(src.data_ptr()),
+                                 nbytes, ctypes.c_void_p(st))
+        if rc != 0:
+            raise RuntimeError(f"ssd_bw_run({kind}) returned {rc}")
+
+    def rates(self, nbytes=1 << 30, reps=10):
+        """GB/s of a copy (bytes read + bytes written), a read and a write of
+        nbytes, timed with HIP events over reps launches after one warm-up."""
+        torch = self.torch
+        a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        res = {}
+        for name, kind, moved in (("copy", 0, 2 * nbytes), ("read", 1, nbytes),
+                                  ("write", 2, nbytes)):
+            src = None if kind == 2 else a
+            self.run(kind, b, src, nbytes)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                self.run(kind, b, src, nbytes)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del a, b
+        torch.cuda.empty_cache()
+        return res
 
 
 def time_launches(torch, fn, iters, warmup=2):
@@ -177,8 +281,77 @@ def device_info(torch) -> dict:
     return out
 
 
+def calibrate(torch):
+    """Two launches each of the plain read kernel and the plain write kernel
+    over 256 MiB (262144 KiB read, then 262144 KiB written, per launch): the
+    known-size dispatches that FETCH_SIZE and WRITE_SIZE are scaled by."""
+    probe = BandwidthProbe(torch)
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        probe.run(1, dst, src, src.numel() * 4)
+        probe.run(2, dst, None, dst.numel() * 4)
+    torch.cuda.synchronize()
+
+
+def step_call(torch, db, H, P, N):
+    """One bf16 ssd_step at batch db on the given head shape (one group), its
+    arguments bound: (call, the decode stream, the descriptor, the tensors)."""
+    import ctypes
+    from mamba_ssd_chunked_scan_amd import binding, synth
+    dev = "cuda:0"
+    ds = synth.DecodeStream(synth.DecodeSpec(f"decode_2p7b_b{db}", db, H, P, N, 1, 1, "bf16", 5))
+    s0 = ds.next_step()
+    t = {k: s0[k].to(dev) for k in ("x", "dt", "B", "C")}
+    t.update(state=ds.state.to(dev), A=ds.A.to(dev), D=ds.D.to(dev))
+    t["y"] = torch.empty_like(t["x"])
+    sdesc = binding.StepDesc(db, H, P, N, 1, binding.SSD_BF16, 0)
+    P_ = lambda v: ctypes.c_void_p(v.data_ptr())
+    fn = Lean(torch, binding.lib().ssd_step, ctypes.byref(sdesc), P_(t["state"]), P_(t["x"]),
+              P_(t["dt"]), P_(t["A"]), P_(t["B"]), P_(t["C"]), P_(t["D"]), P_(t["y"]))
+    return fn, ds, sdesc, t
+
+
+def cold_steps(torch, probe, fn, n):
+    """Median milliseconds of n decode steps, each queued right after a read of
+    FLUSH_BYTES (which evicts the state from L2 and the Infinity Cache), with a
+    HIP event on each side of the step alone.  Everything is queued back to
+    back, so the events time the step on the GPU, not the host's launch."""
+    src = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    sink = torch.empty(FLUSH_BYTES // 4096, dtype=torch.float32, device="cuda:0")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    fn()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        probe.run(1, sink, src, FLUSH_BYTES)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    del src, sink
+    return sorted(a.elapsed_time(b) for a, b in ev)[n // 2]
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(spec, inp, budget_s=10.0):
+    """The fp64 CPU oracle as it stands, on the host cores: the full bench
+    prefill repeated for about budget_s with every OpenMP thread, then one
+    thread on the same prefill and on the tiny and 130M-head-shape workloads."""
     import oracle
+    from mamba_ssd_chunked_scan_amd import synth
     args = {k: oracle.f64(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "init")}
     cores = oracle.max_threads()
     reps, t0 = 0, time.perf_counter()
@@ -189,18 +362,28 @@ def cpu_baseline(spec, inp, budget_s=10.0):
         if reps >= 2 and el >= budget_s:
             break
     tokens = spec.batch * spec.seqlen * reps
-    # the same on one core: two passes (a few seconds); the thread count is
-    # left at one afterwards, and nothing after this uses the oracle
-    t1 = time.perf_counter()
-    for _ in range(2):
-        oracle.scan(**args, nthreads=1)
-    el1 = time.perf_counter() - t1
+    # one thread (the thread count stays at one afterwards; nothing after this
+    # uses the oracle): the bench prefill twice, then the other workloads
+    single = {}
+    for name, sp, sargs, n in (
+            (spec.name, spec, args, 2),
+            ("tiny_f32", synth.WORKLOADS["tiny_f32"], None, 20),
+            ("m130m_bf16", synth.WORKLOADS["m130m_bf16"], None, 2)):
+        if sargs is None:
+            si = synth.scan_inputs(sp)
+            sargs = {k: oracle.f64(si[k]) for k in ("x", "dt", "A", "B", "C", "D", "init")}
+        t1 = time.perf_counter()
+        for _ in range(n):
+            oracle.scan(**sargs, nthreads=1)
+        single[name] = round(n * sp.batch * sp.seqlen / (time.perf_counter() - t1), 1)
     return {"value": tokens / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "single_core_tokens_per_s": round(2 * spec.batch * spec.seqlen / el1, 1),
+            "cpu_model": cpu_model(),
+            "single_core_tokens_per_s": single,
             "sample": f"full {spec.name} prefill ({spec.batch}x{spec.seqlen} tokens, "
                       f"{spec.nheads} heads) repeated {reps}x in {el:.1f} s, fp64 recurrence "
-                      f"with {cores} OpenMP threads; single_core_tokens_per_s: the same "
-                      f"prefill twice on one thread ({el1:.1f} s)"}
+                      f"with {cores} OpenMP threads; single_core_tokens_per_s: one thread on "
+                      f"the same prefill (2 passes), the tiny workload (20) and the 130M head "
+                      f"shape (2)"}
 
 
 def main():
@@ -210,9 +393,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the W + K prefill calls (for kernel traces and counters)")
+    ap.add_argument("--decode-cold-only", action="store_true",
+                    help="time only the cold decode steps (batch 1 and 64), for a kernel trace "
+                         "whose step rows are the cold ones")
     ap.add_argument("--calibrate", action="store_true",
-                    help="end with a plain 256 MiB device copy (twice), the known-size kernel "
-                         "that hardware byte counters are scaled by")
+                    help="end with plain 256 MiB read and write kernels (twice each), the "
+                         "known-size launches that hardware byte counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -226,6 +414,18 @@ def main():
 
     dev = "cuda:0"
     spec = synth.WORKLOADS[WORKLOAD]
+    if args.decode_cold_only:
+        probe = BandwidthProbe(torch)
+        res = {}
+        for db in (1, 64):
+            fn, _, _, _ = step_call(torch, db, spec.nheads, spec.headdim, spec.dstate)
+            cms = cold_steps(torch, probe, fn, 50)
+            res[f"batch{db}"] = {"cold_us_per_step_median": round(cms * 1e3, 3),
+                                 "cold_GB_s": round(decode_bytes(db, spec.nheads, spec.headdim,
+                                                                 spec.dstate, 1)
+                                                    / (cms * 1e-3) / 1e9, 1)}
+        print(json.dumps({"decode_cold": res}))
+        return
     inp = synth.scan_inputs(spec)
     d = {k: (None if v is None else v.to(dev).contiguous()) for k, v in inp.items()}
     Bt, L, H, P, N, G, Q = (spec.batch, spec.seqlen, spec.nheads, spec.headdim, spec.dstate,
@@ -252,6 +452,17 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    if args.prefill_only:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        if args.calibrate:
+            calibrate(torch)
+        print(json.dumps({"prefill_only": spec.name, "steps": args.steps,
+                          "ms_per_step": round(el * 1e3 / args.steps, 5)}))
+        return
     t0 = time.perf_counter()
     for _ in range(args.steps):
         run()
@@ -438,43 +649,29 @@ def main():
     stage_ms = {k: time_launches(torch, f, iters) for k, f in stage_fns.items()}
     bytes_ = prefill_bytes(spec)
     dom = max(stage_ms, key=stage_ms.get)
-    dom_gbs = bytes_[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    dom_us = stage_ms[dom] * 1e3
+    method_bytes = bytes_["call"]
+    prof = profile_figures()
 
     flops = prefill_flops(spec)
     tflops = flops / (ms * 1e-3) / 1e12
-    call_gbs = bytes_["call"] / (ms * 1e-3) / 1e9
+    call_gbs = method_bytes / (ms * 1e-3) / 1e9
 
-    # ---- plain device copy (1 GiB read + 1 GiB written): the attainable HBM rate
-    csrc_ = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev).fill_(1.0)
-    cdst_ = torch.empty_like(csrc_)
-    cdst_.copy_(csrc_)
-    torch.cuda.synchronize()
-    ca, cb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ca.record()
-    for _ in range(10):
-        cdst_.copy_(csrc_)
-    cb_.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * csrc_.numel() * 4 * 10 / (ca.elapsed_time(cb_) * 1e-3) / 1e9
-    del csrc_, cdst_
+    # ---- plain copy / read / write kernels over 1 GiB: the attainable HBM rates
+    probe = BandwidthProbe(torch)
+    ceiling = probe.rates()
 
     # ---- decode steps
     decode = {}
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     for db in (1, 64):
-        dspec = synth.DecodeSpec(f"decode_2p7b_b{db}", db, H, P, N, 1, 1, "bf16", 5)
-        ds = synth.DecodeStream(dspec)
-        state = ds.state.to(dev)
-        s0 = ds.next_step()
-        xs, dts, Bs, Cs = (s0[k].to(dev) for k in ("x", "dt", "B", "C"))
-        A, D = ds.A.to(dev), ds.D.to(dev)
-        yd = torch.empty_like(xs)
-        sdesc = binding.StepDesc(db, H, P, N, 1, binding.SSD_BF16, 0)
-        fn = Lean(torch, lib.ssd_step, ctypes.byref(sdesc), P_(state), P_(xs), P_(dts), P_(A),
-                  P_(Bs), P_(Cs), P_(D), P_(yd))
+        fn, ds, sdesc, t = step_call(torch, db, H, P, N)
+        state, A, D = t["state"], t["A"], t["D"]
+        db_bytes = decode_bytes(db, H, P, N, 1)
+        cold_ms = cold_steps(torch, probe, fn, 50)
+        cold_gbs = db_bytes / (cold_ms * 1e-3) / 1e9
+        # warm: graph-replayed single steps (the state may stay resident in the
+        # 256 MB Infinity Cache between steps), and the same launched one by one
         dms = time_launches(torch, fn, args.decode_steps, warmup=5)
-        # the same steps launched one by one from the host, for comparison
-        # with the graph-replayed (device-resident) loop above
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -483,20 +680,6 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / args.decode_steps
-        # cold: a 512 MB write evicts the state from L2 and the Infinity Cache
-        # before each step; events bracket the step launch alone
-        n_cold = 50
-        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_cold)]
-        for ca0, ca1 in cev:
-            flush.fill_(0.0)
-            ca0.record()
-            fn()
-            ca1.record()
-        torch.cuda.synchronize()
-        cold_ms = sorted(a.elapsed_time(b) for a, b in cev)[n_cold // 2]
-        db_bytes = decode_bytes(db, H, P, N, 1)
-        gbs = db_bytes / (dms * 1e-3) / 1e9
         # K tokens per launch with the state kept in registers (ssd_step_multi)
         K = 16
         steps = [ds.next_step() for _ in range(K)]
@@ -509,20 +692,21 @@ def main():
         m_bytes = 2 * db * H * P * N * 4 + K * (decode_bytes(db, H, P, N, 1)
                                                 - 2 * db * H * P * N * 4)
         decode[f"batch{db}"] = {
-            "us_per_step": round(dms * 1e3, 3), "GB_s": round(gbs, 1),
-            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": db_bytes,
-            "eager_us_per_step": round(eager_ms * 1e3, 3),
-            "cold_us_per_step_median": round(cold_ms * 1e3, 3),
-            "cold_GB_s": round(db_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "us_per_step": round(cold_ms * 1e3, 3), "GB_s": round(cold_gbs, 1),
+            "frac_hbm": round(cold_gbs / HBM_PEAK_GBS, 4), "bytes_per_step": db_bytes,
+            "warm_us_per_step_graph": round(dms * 1e3, 3),
+            "warm_GB_s_graph": round(db_bytes / (dms * 1e-3) / 1e9, 1),
+            "warm_us_per_step_eager": round(eager_ms * 1e3, 3),
             "multi16_us_per_token": round(mms * 1e3 / K, 3),
             "multi16_GB_s": round(m_bytes / (mms * 1e-3) / 1e9, 1),
             "multi16_bytes_per_launch": m_bytes,
-            "note": f"us_per_step: {args.decode_steps} graph-replayed single steps, warm (the "
-                    "state may be resident in the 256 MB Infinity Cache); eager: the same "
-                    "launched one by one from the host; cold: median over 50 steps each "
-                    "after a 512 MB cache-evicting write, events around the step alone; "
-                    "multi16: 16 tokens per ssd_step_multi launch (state read and written "
-                    "once)"}
+            "note": "us_per_step / GB_s: cold, the median over 50 steps, each queued right "
+                    "after a 1 GiB read that evicts the state from L2 and the Infinity Cache, "
+                    "HIP events around the step alone; warm_*: "
+                    f"{args.decode_steps} steps back to back, graph-replayed or launched one "
+                    "by one; multi16: 16 tokens per ssd_step_multi launch (state read and "
+                    "written once)"}
+        del state, t, xm, ym
 
     out = {
         "metric": METRIC,
@@ -563,25 +747,18 @@ def main():
                    "padded_batch_us_per_call_graph": round(padded_ms * 1e3, 2),
                    "speedup_vs_padded": round(padded_ms / varlen_ms, 2)},
         "device": device_info(torch),
-        "copy_GB_s": round(copy_gbs, 1),
-        "frac_of_copy": {f"prefill_{dom}": round(dom_gbs / copy_gbs, 4),
-                         "decode_batch64": round(decode["batch64"]["GB_s"] / copy_gbs, 4)},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic() if dom == "chunk_scan" else None,
-                     "algorithmic_bytes_per_launch": bytes_[dom],
-                     "avg_launch_us": round(stage_ms[dom] * 1e3, 2)},
+        "hbm_ceiling_GB_s": {k: round(v, 1) for k, v in ceiling.items()},
+        "frac_of_copy": {
+            "prefill_call": round(call_gbs / ceiling["copy"], 4),
+            "prefill_dominant_kernel": round(
+                method_bytes / (dom_us * 1e-6) / 1e9 / ceiling["copy"], 4),
+            "decode_batch64_cold": round(decode["batch64"]["GB_s"] / ceiling["copy"], 4)},
+        "roofline": roofline(method_bytes, dom, dom_us, bytes_[dom], ms * 1e3, prof),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, inp)
     if args.calibrate:
-        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(2):
-            torch.mul(src, 2.0, out=dst)   # reads 256 MiB, writes 256 MiB
-        torch.cuda.synchronize()
+        calibrate(torch)
     print(json.dumps(out))
 
 

@@ -19,6 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libssd.so")
+# plain copy / read / write kernels for the benchmark's HBM ceiling (not part of libssd)
+BW_LIB = os.path.join(HERE, "libssd_bw.so")
+BW_SOURCES = ["bw_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["ssd_api.cpp", "generic.hip", "mfma.hip", "fused.hip", "backward.hip", "noalloc.hip"]
@@ -47,16 +50,19 @@ def _compile(src):
 
 
 def build(verbose: bool = False) -> str:
+    """Builds libssd.so and the benchmark's bandwidth helper libssd_bw.so."""
     os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        results = list(ex.map(_compile, SOURCES + BW_SOURCES))
     for _, out in results:
         if out.strip() and verbose:
             print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-          *[o for o, _ in results]])
-    os.replace(tmp, LIB)
+    objs = [o for o, _ in results]
+    for lib, srcs in ((LIB, SOURCES), (BW_LIB, BW_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+              *[objs[(SOURCES + BW_SOURCES).index(s)] for s in srcs]])
+        os.replace(tmp, lib)
     return LIB
 
 

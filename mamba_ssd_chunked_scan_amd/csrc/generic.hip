@@ -515,6 +515,62 @@ k_step(float *__restrict__ state, const Tin *__restrict__ x, const float *__rest
     }
 }
 
+// One token with 16 state values per lane: the float4 groups sub, sub+L,
+// sub+2L and sub+3L of a row's N/4 groups, L = N/16 lanes per row.  Four
+// 16-byte state loads per lane are in flight at once (k_step has one), which
+// is what the state stream needs to approach the HBM rate when it is not in a
+// cache.  The lane adds its four partials as (g0 + g2) + (g1 + g3) and then
+// butterflies over its L lanes: exactly the pairing of k_step's butterfly
+// over N/4 lanes (its first two levels pair g with g ^ 2L and then with
+// g ^ L), so y and the state are bit for bit those of k_step.  N >= 16.
+template <typename Tin>
+__global__ void __launch_bounds__(256)
+k_step_wide(float *__restrict__ state, const Tin *__restrict__ x, const float *__restrict__ dt,
+            const float *__restrict__ A, const Tin *__restrict__ Bm, const Tin *__restrict__ Cm,
+            const float *__restrict__ D, Tin *__restrict__ y, int64_t rows, int H, int P, int N,
+            int G, int l_log2, DtAct act, const Tin *__restrict__ z) {
+    const int L = 1 << l_log2;
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gt >> l_log2;
+    const int sub = (int)(gt & (L - 1));
+    const bool active = row < rows;
+    float part = 0.f, xv = 0.f;
+    int h = 0;
+    if (active) {
+        const int64_t bh = row / P;
+        h = (int)(bh % H);
+        const int64_t b = bh / H;
+        const int g = h / (H / G);
+        const float d = act_dt(act, dt[b * H + h], h);
+        const float r = ssd_exp(d * A[h]);
+        xv = Elem<Tin>::ld(x, row);
+        const float u = d * xv;
+        float4 *sp = reinterpret_cast<float4 *>(state + row * N) + sub;
+        float4 sv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sv[k] = sp[k * L];
+        const int64_t bc = (b * G + g) * N + sub * 4;
+        float pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float bv[4], cv[4];
+            ld4(Bm, bc + (int64_t)k * L * 4, bv);
+            ld4(Cm, bc + (int64_t)k * L * 4, cv);
+            pk[k] = step_update(sv[k], r, u, bv, cv);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sp[k * L] = sv[k];
+        part = (pk[0] + pk[2]) + (pk[1] + pk[3]);
+    }
+    for (int off = L >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+    if (active && sub == 0) {
+        float yv = fmaf(D ? D[h] : 0.f, xv, part);
+        if (z) yv *= silu_f(Elem<Tin>::ld(z, row));
+        Elem<Tin>::st(y, row, yv);
+    }
+}
+
+
 // nsteps consecutive decode tokens in one launch.  Same thread layout and
 // per-token arithmetic as k_step (so the result equals nsteps chained steps
 // bit for bit), but the thread's 4 state elements stay in registers across
@@ -718,6 +774,15 @@ void launch_step_t(const StepShape &s, int64_t nsteps, float *state, const void 
     int lpr_log2 = 0;
     while ((4LL << lpr_log2) < s.N) ++lpr_log2;  // lanes per row = N / 4
     const unsigned blocks = (unsigned)(((rows << lpr_log2) + 255) / 256);
+    if (nsteps < 0 && s.N >= 16) {  // a single step, 16 state values per lane
+        const int l_log2 = lpr_log2 - 2;
+        const unsigned wblocks = (unsigned)(((rows << l_log2) + 255) / 256);
+        k_step_wide<Tin><<<wblocks, 256, 0, st>>>(state, (const Tin *)x, dt, A,
+                                                  (const Tin *)Bm, (const Tin *)Cm, D, (Tin *)y,
+                                                  rows, (int)s.H, (int)s.P, (int)s.N, (int)s.G,
+                                                  l_log2, act, (const Tin *)z);
+        return;
+    }
     if (nsteps < 0) {  // a single step, [B, ...] layouts
         k_step<Tin><<<blocks, 256, 0, st>>>(state, (const Tin *)x, dt, A, (const Tin *)Bm,
                                             (const Tin *)Cm, D, (Tin *)y, rows, (int)s.H,

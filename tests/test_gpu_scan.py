@@ -75,19 +75,40 @@ def sampled_check(inp, chunk, pairs, dtype):
     assert ef <= TOL[dtype], f"final rel err {ef:.3e}"
 
 
-def test_workload_2p7b_sampled():
+def test_workload_2p7b_full():
+    """The 2.7B head shape prefill (4096 tokens, 80 heads): every element of y
+    and of the final state against the oracle."""
     spec = synth.WORKLOADS["m2p7b_bf16"]
+    announce(f"scan_fwd {spec.name} all heads")
+    check_full(synth.scan_inputs(spec), spec.chunk, torch.bfloat16)
+
+
+def test_workload_2p7b_f32_sampled():
+    """The same shape with fp32 x/B/C (the generic kernels): sampled heads."""
+    spec = synth.custom_spec(1, 4096, 80, 64, 128, 1, 256, "f32", dt_rule="ranged",
+                             init="normal", seed=3, name="m2p7b_f32")
     announce(f"scan_fwd {spec.name} sampled heads")
-    inp = synth.scan_inputs(spec)
-    sampled_check(inp, spec.chunk, [(0, 0), (0, 17), (0, 41), (0, 63), (0, 79)],
-                  torch.bfloat16)
+    sampled_check(synth.scan_inputs(spec), spec.chunk, [(0, 0), (0, 33), (0, 79)],
+                  torch.float32)
 
 
-def test_workload_batched_long_sampled():
+def test_workload_batched_long_rows():
+    """The batched long prefill (8 x 16384 tokens, 8 groups): every head of
+    batch rows 0 and 7, each row's oracle run on its own (the oracle holds one
+    row at a time)."""
     spec = synth.WORKLOADS["batched_long_bf16"]
-    announce(f"scan_fwd {spec.name} sampled (batch, head)")
+    announce(f"scan_fwd {spec.name}, rows 0 and 7, all heads")
     inp = synth.scan_inputs(spec)
-    sampled_check(inp, spec.chunk, [(0, 0), (3, 37), (5, 50), (7, 79)], torch.bfloat16)
+    y, fin = run_gpu(inp, spec.chunk)
+    for b in (0, 7):
+        row = {k: (v if k in ("A", "D") or v is None else v[b:b + 1]) for k, v in inp.items()}
+        yo, fo = oracle.scan(**oracle_args(row))
+        ey = rel_err(f64(y[b:b + 1]), yo)
+        ef = rel_err(f64(fin[b:b + 1]), fo)
+        print(f"  row {b}: rel_err y {ey:.3e} final {ef:.3e}", flush=True)
+        assert ey <= TOL[torch.bfloat16], f"row {b} y rel err {ey:.3e}"
+        assert ef <= TOL[torch.bfloat16], f"row {b} final rel err {ef:.3e}"
+        del yo, fo
 
 
 SHAPES = [
@@ -105,6 +126,7 @@ SHAPES = [
     (2, 33, 2, 64, 128, 2, 64, "bf16"),      # 33 tokens: a one-row second tile
     (1, 70, 2, 256, 256, 1, 32, "f32"),      # the largest headdim and d_state accepted
     (2, 50, 4, 8, 4, 2, 16, "bf16"),         # the smallest d_state and chunk accepted
+    (1, 600, 4, 64, 128, 2, 256, "f32"),     # fp32 at chunk 256: three chunks, ragged
 ]
 
 
@@ -202,6 +224,7 @@ def test_deterministic():
     (2, 300, 4, 64, 128, 2, 128, "bf16"),
     (1, 520, 3, 64, 64, 1, 256, "bf16"),
     (2, 150, 6, 32, 32, 3, 32, "bf16"),      # generic kernels: groups, ragged tail
+    (1, 600, 4, 64, 128, 2, 256, "f32"),     # fp32 at chunk 256, ragged
 ])
 def test_stages_against_chunked_form(shape):
     Bt, L, H, P, N, G, chunk, dt_ = shape

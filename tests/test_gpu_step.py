@@ -89,6 +89,34 @@ def test_decode_chain_4096(name):
     assert ef <= TOL[torch.bfloat16], f"state rel err {ef:.3e}"
 
 
+def test_decode_chain_batch64_all_rows():
+    """The batch-64 decode workload over a 256-step chain of single steps:
+    every y of every step and the whole final state against the oracle run as
+    one recurrence over the same 256 tokens."""
+    spec = synth.DECODE_WORKLOADS["decode_2p7b_b64"]
+    print("[case] decode chain batch 64, all rows, 256 steps", flush=True)
+    stream = synth.DecodeStream(spec)
+    state0 = stream.state.clone()
+    sd = stream.state.to(DEV)
+    A, D = stream.A.to(DEV), stream.D.to(DEV)
+    steps, ys = [], []
+    for t in range(256):
+        s = stream.next_step()
+        steps.append(s)
+        ys.append(ssd.step(sd, s["x"].to(DEV), s["dt"].to(DEV), A, s["B"].to(DEV),
+                           s["C"].to(DEV), D).cpu())
+    torch.cuda.synchronize()
+    x = torch.stack([s["x"] for s in steps], dim=1)
+    dt = torch.stack([s["dt"] for s in steps], dim=1)
+    B = torch.stack([s["B"] for s in steps], dim=1)
+    C = torch.stack([s["C"] for s in steps], dim=1)
+    yo, fo = oracle.scan(x, dt, stream.A, B, C, stream.D, state0)
+    ey = rel_err(f64(torch.stack(ys, dim=1)), yo)
+    ef = rel_err(f64(sd), fo)
+    assert ey <= TOL[torch.bfloat16], f"y rel err {ey:.3e}"
+    assert ef <= TOL[torch.bfloat16], f"state rel err {ef:.3e}"
+
+
 def test_decode_steps_match_prefill_on_gpu():
     """Steps through the GPU decode path agree with the GPU prefill path."""
     print("[case] decode == prefill", flush=True)
@@ -132,6 +160,7 @@ def _multi_inputs(Bt, T, H, P, N, G, dtype, seed):
     (2, 20, 3, 64, 16, 1, torch.float32),     # 64 rows per block, ragged token group
     (2, 5, 2, 96, 32, 2, torch.float32),      # 32 rows per block, headdim 3 blocks
     (1, 3, 2, 12, 32, 1, torch.bfloat16),     # headdim not a multiple of a block's rows
+    (64, 3, 80, 64, 128, 1, torch.bfloat16),  # the batch-64 decode shape: 10240 step blocks
 ])
 def test_step_multi_equals_chained_steps(shape):
     """nsteps tokens in one launch: bit for bit the chained single steps, and
