@@ -126,7 +126,8 @@ def profile_figures() -> dict:
     for k in ("call_kernel_sum_us", "call_traffic_bytes", "dominant_traffic_bytes_per_launch",
               "dominant_trace_avg_us"):
         try:
-            figs[k] = float(fields[k])
+            v = float(fields[k])
+            figs[k] = int(v) if v.is_integer() else v
         except (KeyError, ValueError):
             pass
     return figs
@@ -395,6 +396,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the W + K prefill calls (for kernel traces and counters)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="with --prefill-only: the prefill workload (m2p7b_bf16, m130m_bf16, "
+                         "batched_long_bf16)")
     ap.add_argument("--decode-cold-only", action="store_true",
                     help="time only the cold decode steps (batch 1 and 64), for a kernel trace "
                          "whose step rows are the cold ones")
@@ -413,7 +417,7 @@ def main():
     from mamba_ssd_chunked_scan_amd import binding, synth
 
     dev = "cuda:0"
-    spec = synth.WORKLOADS[WORKLOAD]
+    spec = synth.WORKLOADS[args.workload if args.prefill_only else WORKLOAD]
     if args.decode_cold_only:
         probe = BandwidthProbe(torch)
         res = {}
@@ -438,10 +442,11 @@ def main():
     import ctypes
     lib = binding.lib()
     P_ = lambda t: ctypes.c_void_p(t.data_ptr())
+    Pn = lambda t: None if t is None else P_(t)
     desc = binding.ScanDesc(Bt, L, H, P, N, G, Q, binding.SSD_BF16, 0)
     dref = ctypes.byref(desc)
     call = Lean(torch, lib.ssd_scan_fwd, dref, P_(d["x"]), P_(d["dt"]), P_(d["A"]), P_(d["B"]),
-                P_(d["C"]), P_(d["D"]), P_(d["init"]), P_(y), P_(fin), P_(ws), ws.numel())
+                P_(d["C"]), P_(d["D"]), Pn(d["init"]), P_(y), P_(fin), P_(ws), ws.numel())
 
     # ---- timed prefill steps: W untimed calls, then exactly K calls (three
     # launches each) from a host loop that keeps its stream handle, bracketed

@@ -71,5 +71,86 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
     }
 }
 
+// The same tiles and C fragments, a block at a time: 256 threads form every
+// causal tile of 8 / NI consecutive (b, c, g) (one for chunk 256, two for
+// 128, four for 64).  The block first stages the B rows of its (b, c, g)s in
+// LDS with whole-row (coalesced) loads; each wave then holds the C rows of
+// one row tile in registers at a time and forms the tiles of that row from
+// the staged B rows.  Wave w of a (b, c, g) takes row tiles p and NI-1-p
+// (p = w mod NI/2), NI+1 tiles in all, so the waves are evenly loaded.  The
+// C rows of a row tile are loaded once for all its tiles (cb_tile loads them
+// per tile).  Rows past the end of a short chunk are clamped to its last row,
+// as in cb_tile.  `bs` is the block's LDS: 256 rows of N + 8 bf16.
+template <int Q, int N>
+__device__ __forceinline__ void cb_block(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+                                         u32x4 *__restrict__ cb, u32x4 *__restrict__ cfr,
+                                         int64_t L, int G, int T, int64_t blk, int64_t ncg,
+                                         const int2 *__restrict__ ctab, bf16 *bs) {
+    constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
+    constexpr int BPB = 8 / NI;          // (b, c, g)s per block
+    constexpr int LDB = N + 8;
+    constexpr int SEG = N / 8;           // 16-byte segments per row
+    const int tid = threadIdx.x, lane = tid & 63, il = lane & 31, g2 = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned rs = G * N;
+    // stage: row r of the block's 256 is row r % Q of (b, c, g) number r / Q
+#pragma unroll
+    for (int i = 0; i < 256 * SEG / 256; ++i) {
+        const int e = tid + 256 * i, r = e / SEG, sg = e % SEG;
+        const int64_t bcg = blk * BPB + r / Q;
+        u32x4 v{0u, 0u, 0u, 0u};
+        if (bcg < ncg) {
+            const int g = (int)(bcg % G);
+            const int64_t bc = bcg / G;
+            const int c = (int)(bc % T);
+            const int64_t b = bc / T;
+            const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+            if (cp.q > 0) {
+                const bf16 *bbase = Bm + ((b * L + cp.t0) * G + g) * N;
+                v = *reinterpret_cast<const u32x4 *>(bbase + (unsigned)min(r % Q, cp.q - 1) * rs + 8u * sg);
+            }
+        }
+        *reinterpret_cast<u32x4 *>(bs + r * LDB + 8 * sg) = v;
+    }
+    __syncthreads();
+    const int64_t bcg = blk * BPB + wave / (NI / 2);
+    if (bcg >= ncg) return;
+    const int g = (int)(bcg % G);
+    const int64_t bc = bcg / G;
+    const int c = (int)(bc % T);
+    const int64_t b = bc / T;
+    const ChunkPos cp = chunk_pos(ctab, c, Q, L);
+    const int q = cp.q;
+    if (q <= 0) return;  // an unused slot of a variable-length batch
+    const bf16 *cbase = Cm + ((b * L + cp.t0) * G + g) * N;
+    const bf16 *bsg = bs + (wave / (NI / 2)) * Q * LDB;
+    const int p = wave % (NI / 2);
+#pragma unroll 1
+    for (int side = 0; side < 2; ++side) {
+        const int ti = side == 0 ? p : NI - 1 - p;
+        const unsigned co = (unsigned)min(32 * ti + il, q - 1) * rs + 8u * g2;
+        u32x4 crow[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) crow[s] = *reinterpret_cast<const u32x4 *>(cbase + (co + 16u * s));
+#pragma unroll 1
+        for (int jt = 0; jt <= ti; ++jt) {
+            f32x16 acc = zero16();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 bb = *reinterpret_cast<const u32x4 *>(bsg + (32 * jt + il) * LDB + 16 * s + 8 * g2);
+                acc = mfma32(bb, crow[s], acc);
+            }
+            u32x4 *o = cb + (bcg * NT + ti * (ti + 1) / 2 + jt) * 256;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                o[v * 64 + lane] = u32x4{__float_as_uint(acc[4 * v]), __float_as_uint(acc[4 * v + 1]),
+                                         __float_as_uint(acc[4 * v + 2]), __float_as_uint(acc[4 * v + 3])};
+        }
+        u32x4 *cf = cfr + (bcg * NI + ti) * KS * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cf[s * 64] = crow[s];
+    }
+}
+
 }  // namespace mx
 }  // namespace ssd

@@ -41,14 +41,10 @@
 // with a zero state, so a broken hand-off shows up as a flagged wrong result
 // instead of a hang.
 //
-// Visibility across XCDs.  A device-wide release or acquire fence writes back
-// or invalidates a whole L2, so the hand-off avoids them: state tiles and flags
-// are written and read with device-scope (sc1) accesses, which bypass the
-// non-coherent caches, and a wave's stores are complete (s_waitcnt vmcnt(0))
-// before it writes the flag that publishes them; a reader issues its tile
-// loads only after the flag load has returned.
+// Visibility across XCDs: the sc1 hand-off of handoff.hpp.
 #include "cb_tile.hpp"
 #include "common.hpp"
+#include "handoff.hpp"
 #include "launch.hpp"
 #include "mfma_ops.hpp"
 #include "ssd.h"
@@ -64,7 +60,6 @@ constexpr int kNI = kQ / 32;  // 32-row output tiles per chunk = waves per block
 constexpr int kTH = kNI * 64;  // threads per block
 constexpr int kJS = 32;    // tokens per streamed stage of the state product
 constexpr int kNST = kQ / kJS;
-constexpr uint32_t kSpinLimit = 1u << 20;  // flag polls before a wait gives up
 
 struct FusedArgs {
     const bf16 *x;
@@ -97,44 +92,6 @@ constexpr int kQueues = 8;
 __device__ __forceinline__ void queue_heads(int q, int nq, int H, int &h0, int &h1) {
     h0 = (int)(((int64_t)q * H) / nq);
     h1 = (int)(((int64_t)(q + 1) * H) / nq);
-}
-
-// Device-scope stores and loads of 16 bytes (cache policy sc1) at byte
-// offset voff of a wave-uniform buffer resource.
-__device__ __forceinline__ void st16_dev(rsrc_t r, uint32_t voff, float a, float b, float c, float d) {
-    const u32x4 v{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 16);
-}
-__device__ __forceinline__ u32x4 ld16_dev(rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 16));
-}
-
-// Wait (bounded) until the flag at f is set; returns its decay word.  The
-// caller's loads that follow are issued after the flag load returned.
-__device__ __forceinline__ float wait_flag(const unsigned long long *f, unsigned *err) {
-    unsigned long long v = 0;
-    uint32_t n = 0;
-    while (true) {
-        v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v & 1ull) break;
-        if (++n >= kSpinLimit) {
-            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v = 1ull;  // a zero state and no decay from here on
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return __uint_as_float((uint32_t)(v >> 32));
-}
-
-// Publish: the wave's stores are complete before the flag is written.
-__device__ __forceinline__ void set_flag(unsigned long long *f, float r) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __hip_atomic_store(f, ((unsigned long long)__float_as_uint(r) << 32) | 1ull, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int N, bool kGate>

@@ -144,13 +144,18 @@ void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
 size_t chunk_cb_bytes(const ScanShape &s);
 void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
                           hipStream_t st);
-// ssd_scan_fwd on the MFMA path: three launches (the cumsum inside the
-// chunk-state kernel, the C.B tiles inside the state-passing launch).
-// With an active act, the chunk-state kernel writes the activated dt to
-// dt_out, which the chunk-output kernel then reads; z may be null.
+// Workspace of the chained state pass: control words (the error word at byte
+// 4, a ticket) and one flag per (chunk slot, head, wave).
+size_t chain_ws_bytes(const ScanShape &s);
+// ssd_scan_fwd on the MFMA path, three launches.  With `chain` (a region of
+// chain_ws_bytes): the C.B tiles, the chunk states with the in-block cumsum
+// and the chained state pass, the chunk output.  Without: the chunk states,
+// the separate state pass with the C.B tiles, the chunk output.  With an
+// active act, the chunk-state kernel writes the activated dt to dt_out, which
+// the chunk-output kernel then reads; z may be null.
 void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
-                            void *y, float *fin, float *Acs, float *states, void *cb,
+                            void *y, float *fin, float *Acs, float *states, void *cb, void *chain,
                             hipStream_t st, const DtAct &act = DtAct{},
                             float *dt_out = nullptr, const void *z = nullptr);
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,

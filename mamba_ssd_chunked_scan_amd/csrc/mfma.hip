@@ -26,12 +26,14 @@
 #include "mfma_ops.hpp"
 #include "stages.hpp"
 #include "cb_tile.hpp"
+#include "handoff.hpp"
 #include "ssd.h"
 
 namespace ssd {
 namespace {
 
 constexpr int kP = 64;   // headdim handled here
+constexpr int kChainCtlWords = 64;  // control words before the hand-off flags
 constexpr int kJT = 32;  // tokens per streamed stage (one 32-row tile)
 
 using namespace mx;
@@ -65,13 +67,42 @@ using P1 = std::integral_constant<int, 1>;
 // exp(Acs_j), the decay from the chunk's entering state to token j.  TX: x's
 // type; fp32 x (the gradient's dy behind a gate, kept unrounded) is weighted
 // and split like bf16 x.
-template <int Q, int N, bool kCumsum, bool kAdjoint = false, typename TX = bf16>
+//
+// kChain: the block also passes the state on ("Chunked recurrence": the state
+// entering chunk c+1 is the one entering chunk c decayed over the chunk plus
+// the chunk's own state), so the chunk states never take a separate pass.
+// Blocks take their items by an atomic ticket in chunk-major order (every
+// batch row and head of chunk c before chunk c+1; chunk slots in order for a
+// variable-length batch).  A block waits only for its predecessor chunk of
+// the same (sequence, head), which holds a smaller ticket: it was taken by a
+// block that is already running and waits only for smaller tickets itself, so
+// progress never depends on the order in which blocks are dispatched.  Each
+// wave waits for and publishes its own two 32x32 tiles of the 64 x N state
+// (one flag per (chunk, head, wave)), through the sc1 hand-off of
+// handoff.hpp: it reads the state entering its chunk from the `states` slot
+// of the chunk (written there by the predecessor; the initial state or zero
+// for a sequence's first chunk, which the block stores there itself for the
+// output stage) and stores the state entering the next chunk into the next
+// slot, or the final state after a sequence's last chunk.
+struct ChainArgs {
+    const float *init;            // [sequences][H][P][N] or null (zero)
+    float *fin;                   // [sequences][H][P][N] or null
+    unsigned long long *flags;    // [slots][H][4]: the state entering slot+1 is stored
+    unsigned *ctl;                // [1] error word, [2] ticket; zeroed before the launch
+    const int2 *sch;              // variable-length batch: sequence -> (first slot, slots)
+    const int2 *spos;             // slot -> (sequence, position in it)
+    int64_t B;                    // batch rows (fixed-length batch)
+};
+
+template <int Q, int N, bool kCumsum, bool kAdjoint = false, typename TX = bf16,
+          bool kChain = false>
 __global__ void __launch_bounds__(256, 2)
 k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
                    const float *__restrict__ dt, const float *__restrict__ A,
                    float *__restrict__ Acs, float *__restrict__ states, int64_t L, int H, int G,
                    int T, int64_t nblocks, DtAct act, float *__restrict__ dt_out,
-                   const int2 *__restrict__ ctab) {
+                   const int2 *__restrict__ ctab, const ChainArgs ca = ChainArgs{}) {
+    static_assert(!kChain || (kCumsum && !kAdjoint), "the chain runs with the in-block cumsum");
     constexpr int LDX = kP + 16;              // x stage row stride (bf16)
     constexpr int LDB = N + 16;               // B stage row stride (bf16)
     constexpr int NST = Q / kJT;              // stages per chunk
@@ -81,12 +112,29 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
     __shared__ __attribute__((aligned(16))) bf16 xlo[2][kJT * LDX];
     __shared__ __attribute__((aligned(16))) bf16 bst[2][kJT * LDB];
     __shared__ float w[Q];
-    const uint32_t lb = xcd_block();
-    if (lb >= nblocks) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const BCH ix = split_bch(lb, H, T);
-    const int h = ix.h, c = ix.c;
-    const int64_t b = ix.b;
+    int h, c;
+    int64_t b;
+    if constexpr (kChain) {
+        __shared__ unsigned tk_s;
+        if (tid == 0)
+            tk_s = __hip_atomic_fetch_add(ca.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t tk = __builtin_amdgcn_readfirstlane(tk_s);
+        if (tk >= nblocks) return;
+        // chunk-major: ticket = (c * B + b) * H + h (B = 1 for a variable-length batch)
+        const uint32_t cb_ = tk / H, rows = ctab ? 1u : (uint32_t)ca.B;
+        h = (int)(tk - cb_ * H);
+        c = (int)(cb_ / rows);
+        b = cb_ - (uint32_t)c * rows;
+    } else {
+        const uint32_t lb = xcd_block();
+        if (lb >= nblocks) return;
+        const BCH ix = split_bch(lb, H, T);
+        h = ix.h;
+        c = ix.c;
+        b = ix.b;
+    }
     const int g = h / (H / G);
     const ChunkPos cp = chunk_pos(ctab, c, Q, L);
     const int64_t t0 = cp.t0;
@@ -102,6 +150,7 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
     const int xrow = tid >> 3, xseg = tid & 7;
 
     // weights first: every stage needs them (Q <= 256: one token per thread)
+    float total = 0.f;  // Acs at the chunk's last token: its whole log-decay
     if constexpr (kCumsum) {
         __shared__ float wsum[4];
         __shared__ float last_s;
@@ -119,7 +168,8 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
         if (tid < q) Acs[(b * H + h) * L + t0 + tid] = acs;
         if (tid == q - 1) last_s = acs;
         __syncthreads();
-        if (tid < Q) w[tid] = tid < q ? d * ssd_exp(last_s - acs) : 0.f;
+        total = last_s;
+        if (tid < Q) w[tid] = tid < q ? d * ssd_exp(total - acs) : 0.f;
     } else {
         const float *acs = Acs + (b * H + h) * L + t0;
         const float last = acs[q - 1];
@@ -207,14 +257,70 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
             step(st + 1, P1{});
         }
     }
-    float *out = states + ((b * T + c) * H + h) * (int64_t)(kP * N);
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    // this lane's element r of tile t: row p, column n of the 64 x N state
+    auto eoff = [&](int t, int r) {
         const int tile = wave + 4 * t, pt = tile / NT, nt = tile % NT;
+        const int p = pt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        return (uint32_t)(p * N + nt * 32 + (lane & 31));
+    };
+    constexpr int64_t PN = (int64_t)kP * N;
+    const int64_t here = ((b * T + c) * H + h);  // this chunk's state slot
+    if constexpr (!kChain) {
+        float *out = states + here * PN;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int p = pt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            out[p * N + nt * 32 + (lane & 31)] = acc[t][r];
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) out[eoff(t, r)] = acc[t][r];
+    } else {
+        int64_t seq = b;
+        int pos = c, npos = T;
+        if (ctab) {
+            const int2 sp = ca.spos[c];
+            seq = sp.x;
+            pos = sp.y;
+            npos = ca.sch[seq].y;
+        }
+        unsigned long long *flag = ca.flags + here * 4 + wave;
+        float hin[TPW][16];
+        if (pos == 0) {
+            // the initial state (read before anything of this sequence is
+            // published: the final state may overwrite it), also stored as
+            // the state entering this chunk for the output stage
+            const float *ip = ca.init ? ca.init + (seq * H + h) * PN : nullptr;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) hin[t][r] = ip ? ip[eoff(t, r)] : 0.f;
+            float *out = states + here * PN;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) out[eoff(t, r)] = hin[t][r];
+        } else {
+            wait_flag(flag - 4 * H, ca.ctl + 1);  // the previous chunk, same head and wave
+            const rsrc_t rs = buffer_rsrc(states + here * PN, (uint32_t)(PN * 4));
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) hin[t][r] = ld4_dev(rs, eoff(t, r) * 4u);
+        }
+        const float rc = ssd_exp(total);
+        if (pos == npos - 1) {
+            if (ca.fin) {
+                float *fp = ca.fin + (seq * H + h) * PN;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) fp[eoff(t, r)] = fmaf(rc, hin[t][r], acc[t][r]);
+            }
+        } else {
+            const rsrc_t rs = buffer_rsrc(states + (here + H) * PN, (uint32_t)(PN * 4));
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    st4_dev(rs, eoff(t, r) * 4u, fmaf(rc, hin[t][r], acc[t][r]));
+            set_flag(flag, rc);
         }
     }
 }
@@ -227,6 +333,41 @@ k_chunk_cb_mfma(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 
     if (w >= ntiles) return;
     cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w, ctab);
 }
+
+// Before the chained chunk-state launch: the first nzb blocks clear its
+// hand-off flags and control words (a kernel, not a memset, so that the call
+// can be captured in a graph), the rest form the C.B tiles: a block per
+// 8 / NI (b, c, g)s (cb_block) when there are many of them (kBlock), else a
+// wave per tile (cb_tile), whose short waves finish sooner when the few
+// blocks of a small grid cannot fill the chip.
+template <int Q, int N, bool kBlock>
+__global__ void __launch_bounds__(256)
+k_chain_prep(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, u32x4 *__restrict__ cb,
+             int64_t L, int G, int T, int64_t ntiles, const int2 *__restrict__ ctab,
+             unsigned long long *__restrict__ flags, int64_t nflags, unsigned *__restrict__ ctl,
+             int64_t nzb, int64_t ncg) {
+    __shared__ __attribute__((aligned(16))) bf16 bs[kBlock ? 256 * (N + 8) : 8];
+    const int64_t blk = blockIdx.x;
+    if (blk < nzb) {
+        const int64_t i = blk * 256 + threadIdx.x;
+        if (i < nflags) flags[i] = 0ull;
+        if (blk == 0 && threadIdx.x < kChainCtlWords) ctl[threadIdx.x] = 0u;
+        return;
+    }
+    if constexpr (kBlock) {
+        cb_block<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, blk - nzb, ncg, ctab, bs);
+    } else {
+        const int64_t w = (blk - nzb) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (w >= ntiles) return;
+        cb_tile<Q, N>(Bm, Cm, cb, cb + ntiles * 256, L, G, T, w, ctab);
+    }
+}
+
+// (b, c, g)s from which the C.B tiles are formed a block at a time: below,
+// the blocks of cb_block would be too few to fill the chip (measured on
+// MI355X: 16 (b, c, g)s of chunk 256 take 23 us that way against 6 us a wave
+// per tile; 4096 take 321 us against 579 us).
+constexpr int64_t kCbBlockMin = 512;
 
 // The inter-chunk state pass and the C.B tiles in one launch: the first
 // nsp blocks pass states (memory-bound), the rest form C.B tiles on the
@@ -626,13 +767,51 @@ void launch_scan_t(const ScanShape &s, const void *x, const float *dt, const voi
             (int)s.G, (int)s.T, nb, s.ctab);
 }
 
-// The whole chunked scan in three launches: chunk states with the in-block
-// cumsum, state passing with the C.B tiles, chunk output.
+// The whole chunked scan in three launches: the C.B tiles (with the hand-off
+// flags cleared), the chunk states with the in-block cumsum and the chained
+// state pass, the chunk output.
 template <int Q, int N>
 void launch_fused_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                     const void *Bm, const void *Cm, const float *D, const float *init, void *y,
-                    float *fin, float *Acs, float *states, void *cb, hipStream_t st,
+                    float *fin, float *Acs, float *states, void *cb, void *chain, hipStream_t st,
                     const DtAct &act, float *dt_out, const void *z) {
+    constexpr int NI = Q / 32;
+    const int64_t nb = s.B * s.T * s.H;
+    const int64_t ntiles = s.B * s.T * s.G * (NI * (NI + 1) / 2);
+    unsigned *ctl = static_cast<unsigned *>(chain);
+    unsigned long long *flags =
+        reinterpret_cast<unsigned long long *>(static_cast<char *>(chain) + kChainCtlWords * 4);
+    const int64_t nflags = nb * 4, nzb = (nflags + 255) / 256;
+    const int64_t ncg = s.B * s.T * s.G;
+    if (ncg >= kCbBlockMin)
+        k_chain_prep<Q, N, true><<<(unsigned)(nzb + (ncg + 8 / NI - 1) / (8 / NI)), 256, 0, st>>>(
+            (const bf16 *)Bm, (const bf16 *)Cm, (u32x4 *)cb, s.L, (int)s.G, (int)s.T, ntiles,
+            s.ctab, flags, nflags, ctl, nzb, ncg);
+    else
+        k_chain_prep<Q, N, false><<<(unsigned)(nzb + (ntiles + 3) / 4), 256, 0, st>>>(
+            (const bf16 *)Bm, (const bf16 *)Cm, (u32x4 *)cb, s.L, (int)s.G, (int)s.T, ntiles,
+            s.ctab, flags, nflags, ctl, nzb, ncg);
+    ChainArgs ca;
+    ca.init = init;
+    ca.fin = fin;
+    ca.flags = flags;
+    ca.ctl = ctl;
+    ca.sch = s.sch;
+    ca.spos = s.spos;
+    ca.B = s.B;
+    k_chunk_state_mfma<Q, N, true, false, bf16, true><<<(unsigned)nb, 256, 0, st>>>(
+        (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, states, s.L, (int)s.H, (int)s.G, (int)s.T,
+        nb, act, dt_out, s.ctab, ca);
+    launch_scan_t<Q, N>(s, x, dt_out ? dt_out : dt, Cm, D, Acs, states, cb, y, st, z);
+}
+
+// The earlier arrangement, kept for comparison: chunk states, then the state
+// pass and the C.B tiles in one launch, then the chunk output.
+template <int Q, int N>
+void launch_staged3_t(const ScanShape &s, const void *x, const float *dt, const float *A,
+                      const void *Bm, const void *Cm, const float *D, const float *init, void *y,
+                      float *fin, float *Acs, float *states, void *cb, hipStream_t st,
+                      const DtAct &act, float *dt_out, const void *z) {
     constexpr int NI = Q / 32;
     const int64_t nb = s.B * s.T * s.H;
     k_chunk_state_mfma<Q, N, true><<<padded_grid(nb), 256, 0, st>>>(
@@ -722,12 +901,20 @@ void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, vo
     SSD_DISPATCH_QN(launch_cb_t, s, Bm, Cm, cb, st);
 }
 
+size_t chain_ws_bytes(const ScanShape &s) {
+    return kChainCtlWords * 4 + (size_t)(s.B * s.T * s.H) * 4 * 8;
+}
+
 void launch_scan_fused_mfma(const ScanShape &s, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
-                            void *y, float *fin, float *Acs, float *states, void *cb,
+                            void *y, float *fin, float *Acs, float *states, void *cb, void *chain,
                             hipStream_t st, const DtAct &act, float *dt_out, const void *z) {
-    SSD_DISPATCH_QN(launch_fused_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb, st,
-                    act, dt_out, z);
+    if (chain)
+        SSD_DISPATCH_QN(launch_fused_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb,
+                        chain, st, act, dt_out, z);
+    else
+        SSD_DISPATCH_QN(launch_staged3_t, s, x, dt, A, Bm, Cm, D, init, y, fin, Acs, states, cb,
+                        st, act, dt_out, z);
 }
 
 void launch_chunk_scan_mfma(const ScanShape &s, const void *x, const float *dt, const void *Cm,

@@ -2,6 +2,7 @@
 // launch sequence.  Every check happens before the first HIP call; the only
 // HIP calls made here are kernel launches (through the launchers) and
 // hipGetLastError.
+#include <cstring>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -84,9 +85,16 @@ size_t scan_ws_bytes(const ScanShape &s) {
 // the activated dt of ssd_scan_fwd_ex, [B, L, H] fp32
 size_t dt_eff_bytes(const ScanShape &s) { return round_up((size_t)(s.B * s.L * s.H) * 4); }
 
-size_t staged_ws_bytes(const ScanShape &s) {
+// the chained state pass's flags and control words (MFMA shapes)
+size_t chain_bytes(const ScanShape &s) {
+    return ssd::mfma_supported(s) ? round_up(ssd::chain_ws_bytes(s)) : 0;
+}
+
+size_t chain_offset(const ScanShape &s) {
     return acs_bytes(s) + states_bytes(s) + scan_ws_bytes(s) + dt_eff_bytes(s);
 }
+
+size_t staged_ws_bytes(const ScanShape &s) { return chain_offset(s) + chain_bytes(s); }
 
 // Either path's workspace fits (the single-kernel path's, where it applies, or
 // the separate stages').
@@ -121,6 +129,25 @@ int resident_blocks() {
 bool staged_forced() {
     const char *e = getenv("SSD_PREFILL_PATH");
     return !(e && e[0] == 'f');
+}
+
+// The MFMA stage kernels pass the state on either inside the chunk-state
+// launch (a chain of hand-offs between its blocks) or in a launch of its own.
+// A hand-off costs about 2.4 us (a device-scope load, the store's
+// acknowledgement and a flag poll, in series), so a chain of T chunks is
+// hidden only while the chunk-state grid spans several rounds of resident
+// blocks; the separate pass instead moves the chunk states through HBM twice
+// more.  Measured (MI355X, chunk 256, 4 chunk-state blocks resident per CU):
+// 1280 blocks (T = 16) 105.7 us chained against 82.8 us separate; 40960
+// blocks (T = 64) 2.73 ms against 3.06 ms.  The chain is taken from four
+// rounds of resident blocks on; SSD_PREFILL_PATH=chained or =separate forces
+// either.
+bool chain_state_pass(const ScanShape &s) {
+    const char *e = getenv("SSD_PREFILL_PATH");
+    if (e && strcmp(e, "chained") == 0) return true;
+    if (e && strcmp(e, "separate") == 0) return false;
+    const int64_t blocks = s.B * s.T * s.H;
+    return blocks >= 4 * (int64_t)(2 * resident_blocks());
 }
 
 // Work queues of the single-kernel prefill: one per XCD (heads split into 8
@@ -254,8 +281,12 @@ void run_scan(const ScanShape &s, const ssd::DtAct &act, const void *z, const vo
         // a sequence without tokens has no block: its final state is its init
         if (s.sch) ssd::launch_empty_finals(s.sch, s.NS, init_state, final_state, s.H * s.P * s.N, hs);
     } else if (ssd::mfma_supported(s)) {
+        void *chain = chain_state_pass(s) ? ws + chain_offset(s) : nullptr;
         ssd::launch_scan_fused_mfma(s, x, dt, A, B, C, D, init_state, y, final_state, Acs, states,
-                                    scan_ws, hs, act, dt_eff, z);
+                                    scan_ws, chain, hs, act, dt_eff, z);
+        // a sequence without tokens has no block: its final state is its init
+        if (chain && s.sch)
+            ssd::launch_empty_finals(s.sch, s.NS, init_state, final_state, s.H * s.P * s.N, hs);
     } else {
         ssd::launch_chunk_cumsum(s, dt, A, Acs, hs, act, dt_eff);
         const float *dts = dt_eff ? dt_eff : dt;
@@ -271,6 +302,20 @@ ssd_status after_launch() {
 }
 
 hipStream_t as_stream(void *stream) { return reinterpret_cast<hipStream_t>(stream); }
+
+// Where the path a call takes keeps its hand-off error word, if it has one.
+ssd_status error_word_at(const ScanShape &s, bool empty, size_t *offset) {
+    if (empty) return SSD_ERR_UNSUPPORTED;
+    if (ssd::fused_supported(s) && !staged_forced()) {
+        *offset = 4;
+        return SSD_OK;
+    }
+    if (ssd::mfma_supported(s) && chain_state_pass(s)) {
+        *offset = chain_offset(s) + 4;
+        return SSD_OK;
+    }
+    return SSD_ERR_UNSUPPORTED;
+}
 
 }  // namespace
 
@@ -301,10 +346,7 @@ ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset) {
     ScanShape s;
     ssd_status st = check_scan(d, &s);
     if (st != SSD_OK) return st;
-    if (s.B == 0 || s.L == 0 || !ssd::fused_supported(s) || staged_forced())
-        return SSD_ERR_UNSUPPORTED;
-    *offset = 4;
-    return SSD_OK;
+    return error_word_at(s, s.B == 0 || s.L == 0, offset);
 }
 
 ssd_status ssd_varlen_error_word(const ssd_varlen_desc *d, size_t *offset) {
@@ -312,10 +354,7 @@ ssd_status ssd_varlen_error_word(const ssd_varlen_desc *d, size_t *offset) {
     ScanShape s;
     ssd_status st = check_varlen(d, &s);
     if (st != SSD_OK) return st;
-    if (s.NS == 0 || s.L == 0 || !ssd::fused_supported(s) || staged_forced())
-        return SSD_ERR_UNSUPPORTED;
-    *offset = 4;
-    return SSD_OK;
+    return error_word_at(s, s.NS == 0 || s.L == 0, offset);
 }
 
 ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes) {

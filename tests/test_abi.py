@@ -101,27 +101,32 @@ def test_workspace_size(L):
     # 256-byte control block, one 8-byte flag per 32x32 state tile of every
     # (chunk, head), the C.B tiles and fragments, one hand-off state per
     # (chunk, head); or, if larger, the staged path's workspace (Acs, chunk
-    # states, C.B tiles, activated dt), which the same shapes can also run
+    # states, C.B tiles, activated dt, and on MFMA shapes the chained state
+    # pass's 256 control bytes and one 8-byte flag per (chunk, head, wave)),
+    # which the same shapes can also run
     T = 2
+    chain = lambda slots, H=8: r256(256 + slots * H * 4 * 8)
     for dstate in (64, 128):
         st, n = wsize(L, desc(dstate=dstate))
         tiles = 2 * dstate // 32
         cbn = cb_size(L, desc(dstate=dstate))[1]
         fused = 256 + r256(T * 8 * tiles * 8) + cbn + r256(T * 8 * 64 * dstate * 4)
-        staged = 2 * r256(8 * 512 * 4) + r256(T * 8 * 64 * dstate * 4) + cbn
+        staged = (2 * r256(8 * 512 * 4) + r256(T * 8 * 64 * dstate * 4) + cbn) + chain(T)
         assert st == OK and n == max(fused, staged)
     # the staged path: Acs, chunk states, the chunk-output workspace, the
-    # activated dt
+    # activated dt, the chain's flags
     acs = 1 * 8 * 512 * 4
     states = 1 * T * 8 * 64 * 128 * 4
     st, n = wsize(L, desc(chunk=128))
     T128 = 4
     assert st == OK and n == (r256(acs) + r256(T128 * 8 * 64 * 128 * 4)
-                              + cb_size(L, desc(chunk=128))[1] + r256(acs))
+                              + cb_size(L, desc(chunk=128))[1] + r256(acs) + chain(T128))
     # ragged last chunk counts as a chunk
     st, n = wsize(L, desc(seqlen=300, chunk=128))
     assert st == OK and n == (r256(8 * 300 * 4) + r256(3 * 8 * 64 * 128 * 4)
-                              + cb_size(L, desc(seqlen=300, chunk=128))[1] + r256(8 * 300 * 4))
+                              + cb_size(L, desc(seqlen=300, chunk=128))[1] + r256(8 * 300 * 4)
+                              + chain(3))
+    # the generic kernels (fp32) pass states in a launch of their own: no chain
     st, n = wsize(L, desc(dtype=0))
     assert st == OK and n == r256(acs) + r256(states) + cb_size(L, desc(dtype=0))[1] + r256(acs)
     assert wsize(L, desc(seqlen=0)) == (OK, 0)
@@ -131,14 +136,35 @@ def test_workspace_size(L):
 
 def test_error_word_offset(L, monkeypatch):
     off = ctypes.c_size_t(99)
-    # the staged path (the default) has no hand-off wait
+    # on small grids the stage kernels (the default) pass states in a launch
+    # of their own: no hand-off wait
     monkeypatch.delenv("SSD_PREFILL_PATH", raising=False)
+    assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == UNSUP
+    # large grids chain the state pass through the chunk-state blocks (from
+    # 4096 blocks on when no device is visible to count compute units)
+    big = desc(batch=8, seqlen=16384, nheads=80, ngroups=8)
+    assert L.ssd_scan_error_word(ctypes.byref(big), ctypes.byref(off)) == OK
+    # forced, the chain keeps its error word in its control words, after Acs,
+    # the chunk states, the C.B tiles and the activated dt
+    monkeypatch.setenv("SSD_PREFILL_PATH", "chained")
+    T = 2
+    cbn = cb_size(L, desc())[1]
+    assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == OK
+    assert off.value == 2 * r256(8 * 512 * 4) + r256(T * 8 * 64 * 128 * 4) + cbn + 4
+    st = L.ssd_scan_error_word(ctypes.byref(desc(chunk=128)), ctypes.byref(off))
+    assert st == OK and off.value == (2 * r256(8 * 512 * 4) + r256(4 * 8 * 64 * 128 * 4)
+                                      + cb_size(L, desc(chunk=128))[1] + 4)
+    # the generic kernels have no hand-off wait, nor has the separate state pass
+    for kw in (dict(dtype=0), dict(headdim=32), dict(seqlen=0)):
+        assert L.ssd_scan_error_word(ctypes.byref(desc(**kw)), ctypes.byref(off)) == UNSUP
+    monkeypatch.setenv("SSD_PREFILL_PATH", "separate")
     assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == UNSUP
     monkeypatch.setenv("SSD_PREFILL_PATH", "fused")
     # the single-kernel path keeps its error word at byte 4 of the workspace
     assert L.ssd_scan_error_word(ctypes.byref(desc()), ctypes.byref(off)) == OK and off.value == 4
     assert L.ssd_scan_error_word(ctypes.byref(desc(dstate=64)), ctypes.byref(off)) == OK
-    # other paths have no hand-off wait
+    # shapes the single kernel does not run: the stage kernels' path (here
+    # small grids: the separate state pass), or the generic kernels
     for kw in (dict(chunk=128), dict(dtype=0), dict(headdim=32), dict(seqlen=0)):
         assert L.ssd_scan_error_word(ctypes.byref(desc(**kw)), ctypes.byref(off)) == UNSUP
     assert L.ssd_scan_error_word(ctypes.byref(desc(chunk=48)), ctypes.byref(off)) == UNSUP
@@ -148,6 +174,10 @@ def test_error_word_offset(L, monkeypatch):
     vd = binding.VarlenDesc(3, 900, 8, 64, 128, 2, 256, 1, 0)
     assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == OK and off.value == 4
     vd = binding.VarlenDesc(3, 900, 8, 64, 128, 2, 64, 1, 0)
+    assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == UNSUP
+    monkeypatch.setenv("SSD_PREFILL_PATH", "chained")
+    assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == OK
+    vd = binding.VarlenDesc(3, 900, 8, 64, 128, 2, 64, 0, 0)
     assert L.ssd_varlen_error_word(ctypes.byref(vd), ctypes.byref(off)) == UNSUP
 
 
@@ -331,7 +361,8 @@ def test_varlen_workspace_size(L):
     st, n = vwsize(L, vdesc())
     assert st == OK
     fused = 256 + r256(slots * 8 * 8 * 8) + r256(cbw) + r256(slots * 8 * 64 * 128 * 4)
-    staged = 2 * r256(8 * 700 * 4) + r256(slots * 8 * 64 * 128 * 4) + r256(cbw)
+    staged = (2 * r256(8 * 700 * 4) + r256(slots * 8 * 64 * 128 * 4) + r256(cbw)
+              + r256(256 + slots * 8 * 4 * 8))
     assert n == max(fused, staged) + 2 * r256(slots * 8) + r256(3 * 8)
     # the staged path (chunk 128): Acs, chunk states, C.B, activated dt
     slots = 700 // 128 + 3
@@ -340,8 +371,8 @@ def test_varlen_workspace_size(L):
     cbw = slots * 2 * (10 * 4096 + 128 * 128 * 2)
     st, n = vwsize(L, vdesc(chunk=128))
     assert st == OK
-    assert n == (r256(acs) + r256(states) + r256(cbw) + r256(acs) + 2 * r256(slots * 8)
-                 + r256(3 * 8))
+    assert n == (r256(acs) + r256(states) + r256(cbw) + r256(acs)
+                 + r256(256 + slots * 8 * 4 * 8) + 2 * r256(slots * 8) + r256(3 * 8))
     assert vwsize(L, vdesc(nseq=0)) == (OK, 0)
     assert vwsize(L, vdesc(total=0)) == (OK, 0)
     assert L.ssd_varlen_workspace_size(ctypes.byref(vdesc()), None) == NULL

@@ -65,7 +65,7 @@ def _reference(inp, which):
     return yo, fo
 
 
-@pytest.mark.parametrize("path", ["staged", "fused"])
+@pytest.mark.parametrize("path", ["separate", "chained", "fused"])
 @pytest.mark.parametrize("which", ["all", "dt", "gate"])
 @pytest.mark.parametrize("name", list(SPECS))
 def test_scan_edges_vs_oracle(name, which, path, monkeypatch):

@@ -75,11 +75,14 @@ def sampled_check(inp, chunk, pairs, dtype):
     assert ef <= TOL[dtype], f"final rel err {ef:.3e}"
 
 
-def test_workload_2p7b_full():
+@pytest.mark.parametrize("path", ["auto", "chained"])
+def test_workload_2p7b_full(path, monkeypatch):
     """The 2.7B head shape prefill (4096 tokens, 80 heads): every element of y
     and of the final state against the oracle."""
+    if path == "chained":
+        monkeypatch.setenv("SSD_PREFILL_PATH", "chained")
     spec = synth.WORKLOADS["m2p7b_bf16"]
-    announce(f"scan_fwd {spec.name} all heads")
+    announce(f"scan_fwd {spec.name} all heads path={path}")
     check_full(synth.scan_inputs(spec), spec.chunk, torch.bfloat16)
 
 
@@ -92,12 +95,15 @@ def test_workload_2p7b_f32_sampled():
                   torch.float32)
 
 
-def test_workload_batched_long_rows():
+@pytest.mark.parametrize("path", ["auto", "separate"])
+def test_workload_batched_long_rows(path, monkeypatch):
     """The batched long prefill (8 x 16384 tokens, 8 groups): every head of
     batch rows 0 and 7, each row's oracle run on its own (the oracle holds one
-    row at a time)."""
+    row at a time).  The automatic choice chains the state pass here."""
+    if path == "separate":
+        monkeypatch.setenv("SSD_PREFILL_PATH", "separate")
     spec = synth.WORKLOADS["batched_long_bf16"]
-    announce(f"scan_fwd {spec.name}, rows 0 and 7, all heads")
+    announce(f"scan_fwd {spec.name}, rows 0 and 7, all heads path={path}")
     inp = synth.scan_inputs(spec)
     y, fin = run_gpu(inp, spec.chunk)
     for b in (0, 7):
@@ -130,11 +136,20 @@ SHAPES = [
 ]
 
 
+def mfma_shape(P, N, chunk, dt_):
+    return dt_ == "bf16" and P == 64 and N in (64, 128) and chunk in (64, 128, 256)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("with_init", [True, False])
-def test_shapes_full(shape, with_init):
+@pytest.mark.parametrize("path", ["auto", "chained"])
+def test_shapes_full(shape, with_init, path, monkeypatch):
     Bt, L, H, P, N, G, chunk, dt_ = shape
-    announce(f"scan_fwd shape {shape} init={with_init}")
+    if path == "chained":
+        if not mfma_shape(P, N, chunk, dt_):
+            pytest.skip("the chained state pass runs on the MFMA shapes")
+        monkeypatch.setenv("SSD_PREFILL_PATH", "chained")
+    announce(f"scan_fwd shape {shape} init={with_init} path={path}")
     spec = synth.custom_spec(Bt, L, H, P, N, G, chunk, dt_, dt_rule="ranged",
                              init="normal" if with_init else "zero", seed=SHAPES.index(shape))
     inp = synth.scan_inputs(spec)
@@ -142,8 +157,10 @@ def test_shapes_full(shape, with_init):
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
-def test_chunk_sizes_agree_with_oracle(chunk):
-    announce(f"chunk invariance chunk={chunk}")
+@pytest.mark.parametrize("path", ["separate", "chained"])
+def test_chunk_sizes_agree_with_oracle(chunk, path, monkeypatch):
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    announce(f"chunk invariance chunk={chunk} path={path}")
     spec = synth.custom_spec(1, 512, 4, 64, 128, 1, chunk, "bf16", dt_rule="ranged",
                              init="normal", seed=5)
     inp = synth.scan_inputs(spec)

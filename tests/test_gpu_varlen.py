@@ -51,7 +51,7 @@ def _run(d, chunk, edges=False, **kw):
     return y, fin
 
 
-@pytest.mark.parametrize("path", ["staged", "fused"])
+@pytest.mark.parametrize("path", ["separate", "chained", "fused"])
 @pytest.mark.parametrize("edges", [False, True])
 @pytest.mark.parametrize("name", list(CASES))
 def test_varlen_vs_oracle(name, edges, path, monkeypatch):
@@ -93,7 +93,7 @@ def test_equal_lengths_equal_batched_call(Bt, L, H, P, N, G, Q, dt_):
     assert torch.equal(y, yb.view(y.shape)) and torch.equal(fin, fb)
 
 
-@pytest.mark.parametrize("path", ["staged", "fused"])
+@pytest.mark.parametrize("path", ["separate", "chained", "fused"])
 def test_serving_mix_2p7b_sampled(path, monkeypatch):
     """32 requests of log-uniform length in [16, 4096] at the 2.7B head shape
     (80 heads), in the launch configuration the bench times; 8 sampled
