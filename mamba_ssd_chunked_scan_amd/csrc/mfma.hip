@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kP = 64;   // headdim handled here
 constexpr int kChainCtlWords = 64;  // control words before the hand-off flags
+constexpr int kChainQueues = 8;     // work queues of the chained state pass, one per XCD
 constexpr int kJT = 32;  // tokens per streamed stage (one 32-row tile)
 
 using namespace mx;
@@ -71,12 +72,19 @@ using P1 = std::integral_constant<int, 1>;
 // kChain: the block also passes the state on ("Chunked recurrence": the state
 // entering chunk c+1 is the one entering chunk c decayed over the chunk plus
 // the chunk's own state), so the chunk states never take a separate pass.
-// Blocks take their items by an atomic ticket in chunk-major order (every
-// batch row and head of chunk c before chunk c+1; chunk slots in order for a
-// variable-length batch).  A block waits only for its predecessor chunk of
-// the same (sequence, head), which holds a smaller ticket: it was taken by a
-// block that is already running and waits only for smaller tickets itself, so
-// progress never depends on the order in which blocks are dispatched.  Each
+// Blocks take their items by atomic tickets from eight work queues, one per
+// XCD, each holding a contiguous range of heads (for 8 groups of 10 heads,
+// queue q is group q), in chunk-major order within the queue (every batch row
+// and head of the range for chunk c before chunk c+1; chunk slots in order for
+// a variable-length batch).  A block draws from the queue of the XCD it runs
+// on (the XCC_ID hardware register), so the heads that share B rows share that
+// XCD's L2 copy, and from the others in turn once its own is empty.  A block
+// waits only for its predecessor chunk of the same (sequence, head), which
+// sits in the same queue under a smaller ticket: it was taken by a block that
+// is already running and waits only for smaller tickets itself, so progress
+// never depends on the order in which blocks are dispatched or on which XCD
+// runs what.  There are as many blocks as items and each takes exactly one, so
+// every item is taken.  Each
 // wave waits for and publishes its own two 32x32 tiles of the 64 x N state
 // (one flag per (chunk, head, wave)), through the sc1 hand-off of
 // handoff.hpp: it reads the state entering its chunk from the `states` slot
@@ -88,7 +96,7 @@ struct ChainArgs {
     const float *init;            // [sequences][H][P][N] or null (zero)
     float *fin;                   // [sequences][H][P][N] or null
     unsigned long long *flags;    // [slots][H][4]: the state entering slot+1 is stored
-    unsigned *ctl;                // [1] error word, [2] ticket; zeroed before the launch
+    unsigned *ctl;                // [1] error word, [8 + q] ticket of queue q; zeroed before the launch
     const int2 *sch;              // variable-length batch: sequence -> (first slot, slots)
     const int2 *spos;             // slot -> (sequence, position in it)
     int64_t B;                    // batch rows (fixed-length batch)
@@ -116,17 +124,35 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
     int h, c;
     int64_t b;
     if constexpr (kChain) {
-        __shared__ unsigned tk_s;
-        if (tid == 0)
-            tk_s = __hip_atomic_fetch_add(ca.ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __shared__ int item_s[3];
+        if (tid == 0) {
+            const uint32_t rows = ctab ? 1u : (uint32_t)ca.B;
+            const int home = (int)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7);
+            int hh = -1, cc = 0, bb = 0;
+            for (int k = 0; k < kChainQueues && hh < 0; ++k) {
+                const int qu = (home + k) % kChainQueues;
+                const int h0 = (int)(((int64_t)qu * H) / kChainQueues);
+                const int h1 = (int)(((int64_t)(qu + 1) * H) / kChainQueues);
+                const uint32_t nh = (uint32_t)(h1 - h0);
+                if (nh == 0) continue;
+                const uint32_t tk = __hip_atomic_fetch_add(ca.ctl + 8 + qu, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                if (tk >= rows * (uint32_t)T * nh) continue;
+                // chunk-major within the queue: ticket = (c * rows + b) * nh + (h - h0)
+                const uint32_t cb_ = tk / nh;
+                hh = h0 + (int)(tk - cb_ * nh);
+                cc = (int)(cb_ / rows);
+                bb = (int)(cb_ - (uint32_t)cc * rows);
+            }
+            item_s[0] = hh;
+            item_s[1] = cc;
+            item_s[2] = bb;
+        }
         __syncthreads();
-        const uint32_t tk = __builtin_amdgcn_readfirstlane(tk_s);
-        if (tk >= nblocks) return;
-        // chunk-major: ticket = (c * B + b) * H + h (B = 1 for a variable-length batch)
-        const uint32_t cb_ = tk / H, rows = ctab ? 1u : (uint32_t)ca.B;
-        h = (int)(tk - cb_ * H);
-        c = (int)(cb_ / rows);
-        b = cb_ - (uint32_t)c * rows;
+        h = __builtin_amdgcn_readfirstlane(item_s[0]);
+        if (h < 0) return;  // not reached: there are as many blocks as items
+        c = __builtin_amdgcn_readfirstlane(item_s[1]);
+        b = __builtin_amdgcn_readfirstlane(item_s[2]);
     } else {
         const uint32_t lb = xcd_block();
         if (lb >= nblocks) return;
