@@ -1009,6 +1009,31 @@ void launch_empty_finals(const int2 *sch, int64_t NS, const float *init, float *
     k_empty_finals<<<blocks, 256, 0, st>>>(sch, NS, init, fin, per);
 }
 
+// Zero up to four fp32 buffers in one launch (null pointers are skipped).
+struct ZeroSet {
+    float *p[4];
+    int64_t n[4];
+};
+
+__global__ void k_zero_set(ZeroSet z) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int k = 0; k < 4; ++k) {
+        if (!z.p[k]) continue;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < z.n[k]; i += stride)
+            z.p[k][i] = 0.f;
+    }
+}
+
+void launch_zero4(float *a, int64_t na, float *b, int64_t nb, float *c, int64_t nc, float *d,
+                  int64_t nd, hipStream_t st) {
+    ZeroSet z{{a, b, c, d}, {a ? na : 0, b ? nb : 0, c ? nc : 0, d ? nd : 0}};
+    int64_t m = 0;
+    for (int k = 0; k < 4; ++k) m = z.n[k] > m ? z.n[k] : m;
+    if (m == 0) return;
+    const int64_t blocks = (m + 255) / 256;
+    k_zero_set<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>(z);
+}
+
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st) {
     if (n <= 0 || dst == src) return;
     k_copy_or_zero<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(dst, src, n);

@@ -75,6 +75,10 @@ hipError_t scratch_ptr(void **out);
 
 // dst[i] = src ? src[i] : 0 for i < n (no-op when dst == src).
 void launch_copy_or_zero(float *dst, const float *src, int64_t n, hipStream_t st);
+// Zero up to four fp32 buffers of the given element counts in one launch
+// (null pointers are skipped).
+void launch_zero4(float *a, int64_t na, float *b, int64_t nb, float *c, int64_t nc, float *d,
+                  int64_t nd, hipStream_t st);
 
 // Decode: nsteps < 0 is one token with [B, ...] inputs; nsteps >= 1 tokens
 // in one launch with inputs in the prefill layout [B, nsteps, ...].  z (the
@@ -135,6 +139,11 @@ bool bwd_states_mfma_ok(const ScanShape &s);
 void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin,
                             const float *dt, const float *Acs, float *out, bool adjoint,
                             hipStream_t st, bool x_f32 = false);
+// The gradient's forward chunk states with the chunk cumsum formed in the same
+// launch (written to Acs; with an active act, the activated dt to dt_out).
+void launch_bwd_states_cumsum_mfma(const ScanShape &s, const void *x, const void *Bm,
+                                   const float *dt, const float *A, float *Acs, float *out,
+                                   const DtAct &act, float *dt_out, hipStream_t st);
 
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);

@@ -911,6 +911,20 @@ void launch_bwd_states_mfma(const ScanShape &s, const void *xin, const void *bin
 #undef SSD_BWDS
 }
 
+void launch_bwd_states_cumsum_mfma(const ScanShape &s, const void *x, const void *Bm,
+                                   const float *dt, const float *A, float *Acs, float *out,
+                                   const DtAct &act, float *dt_out, hipStream_t st) {
+    const int64_t nb = s.B * s.T * s.H;
+    if (s.N == 128)
+        k_chunk_state_mfma<64, 128, true><<<padded_grid(nb), 256, 0, st>>>(
+            (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, out, s.L, (int)s.H, (int)s.G, (int)s.T,
+            nb, act, dt_out, s.ctab);
+    else
+        k_chunk_state_mfma<64, 64, true><<<padded_grid(nb), 256, 0, st>>>(
+            (const bf16 *)x, (const bf16 *)Bm, dt, A, Acs, out, s.L, (int)s.H, (int)s.G, (int)s.T,
+            nb, act, dt_out, s.ctab);
+}
+
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,
                              const float *dt, const float *Acs, float *states, hipStream_t st) {
     SSD_DISPATCH_QN(launch_state_t, s, x, Bm, dt, Acs, states, st);

@@ -516,17 +516,17 @@ void run_bwd(const ScanShape &s, const ScanShape &b, const ssd::DtAct &act, cons
     // outputs accumulated with atomics start from zero (a fill kernel, so the
     // call can be captured in a HIP graph)
     const int64_t bcn = s.B * s.L * s.G * s.N;
-    ssd::launch_copy_or_zero(o.dB, nullptr, bcn, hs);
-    ssd::launch_copy_or_zero(o.dC, nullptr, bcn, hs);
-    ssd::launch_copy_or_zero(o.dA, nullptr, s.H, hs);
-    if (o.dD) ssd::launch_copy_or_zero(o.dD, nullptr, s.H, hs);
+    ssd::launch_zero4(o.dB, bcn, o.dC, bcn, o.dA, s.H, o.dD, s.H, hs);
     // the forward's Acs (and the activated dt) and entering states at the
-    // gradient's chunks
+    // gradient's chunks (on the matrix cores, the cumsum in the same launch)
     const bool mm = ssd::bwd_states_mfma_ok(b);
-    ssd::launch_chunk_cumsum(b, in.dt, in.A, Acs, hs, act, dt_eff);
     const float *dtu = dt_eff ? dt_eff : in.dt;
-    if (mm) ssd::launch_bwd_states_mfma(b, in.x, in.B, dtu, Acs, Hst, false, hs);
-    else ssd::launch_chunk_state(b, in.x, in.B, dtu, Acs, Hst, hs);
+    if (mm) {
+        ssd::launch_bwd_states_cumsum_mfma(b, in.x, in.B, in.dt, in.A, Acs, Hst, act, dt_eff, hs);
+    } else {
+        ssd::launch_chunk_cumsum(b, in.dt, in.A, Acs, hs, act, dt_eff);
+        ssd::launch_chunk_state(b, in.x, in.B, dtu, Acs, Hst, hs);
+    }
     ssd::launch_state_passing(b, Hst, Acs, in.init, nullptr, hs);
     // gate / norm: the ungated output from the chunk-output stage on those
     // states, then the gradient reaching the scan output, dz and dnorm_weight
