@@ -92,7 +92,7 @@ typedef struct ssd_step_desc {
 /* Static English text for a status code (never NULL). */
 const char *ssd_status_string(int status);
 
-/* ABI version of this header: 11. */
+/* ABI version of this header: 12. */
 int ssd_abi_version(void);
 
 /* ---------------------------------------------------------------- prefill */

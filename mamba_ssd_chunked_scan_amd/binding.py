@@ -75,7 +75,7 @@ class SSDError(RuntimeError):
 
 _lib = None
 _P = ctypes.c_void_p
-ABI_VERSION = 11  # include/ssd.h: the structs above must match the library's
+ABI_VERSION = 12  # include/ssd.h: the structs above must match the library's
 
 
 def lib() -> ctypes.CDLL:

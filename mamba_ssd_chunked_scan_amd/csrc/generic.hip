@@ -244,9 +244,9 @@ k_state_passing_rev(float *__restrict__ ds, const float *__restrict__ Acs,
 constexpr int kScanRows = 16;
 
 // CB[i][j] = C_i . B_j in fp32 for one (b, c, g) and a tile of 16 rows i, every
-// column j <= i, into a Q x Q buffer per (b, c, g) (the rest of it is neither
-// written nor read).  It does not involve the head, so it is formed once here
-// and read by every head of the group.  C rows of the tile and 16 B rows at a
+// column j <= i, into the lower triangle of the chunk stored row after row
+// (row i at i(i+1)/2, Q(Q+1)/2 values per (b, c, g)).  It does not involve
+// the head, so it is formed once here and read by every head of the group.  C rows of the tile and 16 B rows at a
 // time are staged in LDS; each thread forms one (i, j) dot product in the
 // order n = 0..N-1.
 template <typename Tin>
@@ -271,7 +271,8 @@ k_chunk_cb_generic(const Tin *__restrict__ Bm, const Tin *__restrict__ Cm, float
         Cs[ii][n] = ii < rows ? Elem<Tin>::ld(Cm, ((b * L + t0 + i0 + ii) * G + g) * N + n) : 0.f;
     }
     const int ii = threadIdx.x / kScanRows, jj = threadIdx.x % kScanRows;
-    float *out = cb + (bcg * Q + i0 + ii) * (int64_t)Q;
+    const int64_t irow = i0 + ii;
+    float *out = cb + bcg * ((int64_t)Q * (Q + 1) / 2) + irow * (irow + 1) / 2;
     const int jend = i0 + rows;  // columns j < jend can be needed
     for (int j0 = 0; j0 < jend; j0 += kScanRows) {
         __syncthreads();  // Cs staged; the previous B rows no longer read
@@ -328,13 +329,13 @@ k_chunk_scan_generic(const Tin *__restrict__ x, const float *__restrict__ dt,
     }
     __syncthreads();
     const int jmax = i0 + rows;  // columns j < jmax can be non-zero
-    const float *cbr = cbuf + (((b * T + c) * G + g) * Q) * (int64_t)Q;
+    const float *cbr = cbuf + ((b * T + c) * G + g) * ((int64_t)Q * (Q + 1) / 2);
     (void)Bm;  // B enters through the group's C.B buffer
     for (int e = threadIdx.x; e < kScanRows * jmax; e += 256) {
         const int ii = e / jmax, j = e % jmax;
         const int i = i0 + ii;
         float m = 0.f;
-        if (ii < rows && j <= i) m = cbr[(int64_t)i * Q + j] * ssd_exp(acs_s[i] - acs_s[j]) * dt_s[j];
+        if (ii < rows && j <= i) m = cbr[(int64_t)i * (i + 1) / 2 + j] * ssd_exp(acs_s[i] - acs_s[j]) * dt_s[j];
         Ms[ii][j] = m;
     }
     __syncthreads();
@@ -931,9 +932,10 @@ void launch_state_passing(const ScanShape &s, float *states, const float *Acs,
 }
 
 size_t chunk_scan_ws_bytes(const ScanShape &s) {
-    // the MFMA kernels' tiles, or a Q x Q fp32 C.B buffer per (b, c, g)
+    // the MFMA kernels' tiles, or the lower triangle of a Q x Q fp32 C.B
+    // matrix per (b, c, g)
     return mfma_supported(s) ? chunk_cb_bytes(s)
-                             : (size_t)(s.B * s.T * s.G) * (size_t)(s.Q * s.Q) * 4;
+                             : (size_t)(s.B * s.T * s.G) * (size_t)(s.Q * (s.Q + 1) / 2) * 4;
 }
 
 void launch_chunk_cb(const ScanShape &s, const void *Bm, const void *Cm, void *ws, hipStream_t st) {

@@ -339,7 +339,7 @@ const char *ssd_status_string(int status) {
     }
 }
 
-int ssd_abi_version(void) { return 11; }
+int ssd_abi_version(void) { return 12; }
 
 ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset) {
     if (!offset) return SSD_ERR_NULL_PTR;

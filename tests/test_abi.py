@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.ssd_abi_version() == 11
+    assert L.ssd_abi_version() == 12
     for s in range(8):
         assert binding.status_string(s)
     assert binding.status_string(99) == "unknown status"
@@ -84,12 +84,12 @@ def test_chunk_scan_workspace_size(L):
             assert st == OK and n == r256(1 * T * 2 * per)
     # ragged last chunk counts as a chunk
     assert cb_size(L, desc(seqlen=300, chunk=128)) == (OK, 3 * 2 * (10 * 4096 + 128 * 128 * 2))
-    # shapes the generic kernels run keep one chunk x chunk fp32 C.B matrix
-    # per (batch, chunk, group)
-    assert cb_size(L, desc(dtype=0)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
-    assert cb_size(L, desc(headdim=32)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
-    assert cb_size(L, desc(chunk=32)) == (OK, 1 * 16 * 2 * 32 * 32 * 4)
-    assert cb_size(L, desc(dstate=256)) == (OK, 1 * 2 * 2 * 256 * 256 * 4)
+    # shapes the generic kernels run keep the lower triangle (chunk (chunk+1)/2
+    # values) of the fp32 C.B matrix per (batch, chunk, group)
+    assert cb_size(L, desc(dtype=0)) == (OK, 1 * 2 * 2 * (256 * 257 // 2) * 4)
+    assert cb_size(L, desc(headdim=32)) == (OK, 1 * 2 * 2 * (256 * 257 // 2) * 4)
+    assert cb_size(L, desc(chunk=32)) == (OK, 1 * 16 * 2 * (32 * 33 // 2) * 4)
+    assert cb_size(L, desc(dstate=256)) == (OK, 1 * 2 * 2 * (256 * 257 // 2) * 4)
     assert cb_size(L, desc(seqlen=0)) == (OK, 0)
     assert cb_size(L, desc(batch=0)) == (OK, 0)
     assert L.ssd_chunk_scan_workspace_size(ctypes.byref(desc()), None) == NULL

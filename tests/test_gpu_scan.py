@@ -178,8 +178,13 @@ def test_no_D_no_final():
     assert rel_err(f64(y), yo) <= TOL[torch.float32]
 
 
-def test_final_state_in_place():
-    announce("final_state aliases init_state")
+@pytest.mark.parametrize("path", ["separate", "chained"])
+def test_final_state_in_place(path, monkeypatch):
+    """final_state may be init_state: every initial state is read before the
+    final one overwrites it (on the chained path, by the chunk that ends the
+    sequence, long after its first chunk read the initial state)."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    announce(f"final_state aliases init_state path={path}")
     spec = synth.custom_spec(2, 200, 4, 64, 128, 2, 64, "bf16", dt_rule="ranged",
                              init="normal", seed=10)
     inp = synth.scan_inputs(spec)

@@ -76,6 +76,26 @@ def test_varlen_vs_oracle(name, edges, path, monkeypatch):
             assert torch.equal(fin[s].cpu(), inp["init"][s])
 
 
+@pytest.mark.parametrize("path", ["separate", "chained"])
+def test_varlen_final_in_place(path, monkeypatch):
+    """final_states may be init_states in a ragged call too, empty sequences
+    included (their final state is their initial one)."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    lengths, H, P, N, G, Q, dt_ = CASES["mfma_edges"]
+    announce(f"varlen final in place path={path}")
+    inp = synth.varlen_inputs(lengths, H, P, N, G, dt_, seed=45)
+    d = _dev(inp)
+    h = d["init"].clone()
+    y, fin = ssd.scan_fwd_varlen(d["x"], d["dt"], d["A"], d["B"], d["C"], d["cu_seqlens"],
+                                 d["D"], chunk=Q, init_states=h, final_states=h)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == h.data_ptr()
+    yo, fo = oracle.scan_varlen(inp["cu_seqlens"], inp["x"], inp["dt"], inp["A"], inp["B"],
+                                inp["C"], inp["D"], inp["init"])
+    assert rel_err(f64(y), yo) <= TOL[inp["x"].dtype]
+    assert rel_err(f64(h), fo) <= TOL[inp["x"].dtype]
+
+
 @pytest.mark.parametrize("Bt,L,H,P,N,G,Q,dt_", [
     (3, 700, 8, 64, 128, 2, 256, "bf16"),   # MFMA path
     (2, 333, 4, 16, 16, 2, 64, "f32"),      # generic path
