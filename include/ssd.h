@@ -118,15 +118,20 @@ ssd_status ssd_scan_workspace_size(const ssd_scan_desc *d, size_t *bytes);
  *               error word described at ssd_scan_error_word.
  * seqlen == 0 writes final_state = init_state (or zeros); batch == 0 is a no-op.
  *
- * The chunked stages run as separate kernels.  For chunk 256 with bf16 x/B/C,
- * headdim 64 and dstate 64 or 128, the environment variable
- * SSD_PREFILL_PATH=fused selects instead a single kernel (after a small one
- * that forms the C.B products shared by the heads of a group): each (batch
- * row, chunk, head) block hands the state entering the next chunk on to the
- * block of that chunk through the workspace ("a lightweight scan" of
- * summary states between chunks, §3 "Chunked recurrence").  Its waits
- * between blocks are bounded; see ssd_scan_error_word.  Both give the
- * operation's result within the same tolerance; they differ in speed. */
+ * The chunked stages run as separate kernels.  On the matrix-core shapes
+ * (bf16 x/B/C, headdim 64, dstate 64 or 128, chunk 64, 128 or 256) the pass
+ * of the state between chunks ("a lightweight scan" of summary states, §3
+ * "Chunked recurrence") runs either in a launch of its own or, when the
+ * chunk-state grid spans at least four rounds of resident blocks, inside
+ * the chunk-state launch: each (batch row, chunk, head) block then hands the
+ * state entering the next chunk on to that chunk's block through the
+ * workspace.  SSD_PREFILL_PATH=separate or =chained forces either.  For
+ * chunk 256 with bf16 x/B/C, headdim 64 and dstate 64 or 128,
+ * SSD_PREFILL_PATH=fused selects instead a single kernel for all stages
+ * (after a small one that forms the C.B products shared by the heads of a
+ * group), with the same hand-off.  The hand-off's waits between blocks are
+ * bounded; see ssd_scan_error_word.  Every arrangement gives the operation's
+ * result within the same tolerance; they differ in speed. */
 ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
                         const float *A, const void *B, const void *C, const float *D,
                         const float *init_state, void *y, float *final_state,
@@ -159,9 +164,10 @@ ssd_status ssd_scan_fwd_noalloc(const ssd_scan_desc *d, const void *x, const flo
  * runs and to a nonzero value if one of that kernel's bounded waits for the
  * state of an earlier chunk ran out (the results of such a call are not
  * valid).  The caller may read it after the call completes.
- * SSD_ERR_UNSUPPORTED when shape *d does not run the single-kernel path
- * (there is no such wait then); the answer follows SSD_PREFILL_PATH as
- * ssd_scan_fwd reads it. */
+ * SSD_ERR_UNSUPPORTED when the call of shape *d hands no state between
+ * blocks (the separate state pass, or an empty call: there is no such wait
+ * then); the answer follows SSD_PREFILL_PATH and the shape as ssd_scan_fwd
+ * reads them. */
 ssd_status ssd_scan_error_word(const ssd_scan_desc *d, size_t *offset);
 
 /* ---------------------------------------------------------------- gradient */

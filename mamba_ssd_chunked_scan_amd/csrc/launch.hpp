@@ -154,7 +154,8 @@ size_t chunk_cb_bytes(const ScanShape &s);
 void launch_chunk_cb_mfma(const ScanShape &s, const void *Bm, const void *Cm, void *cb,
                           hipStream_t st);
 // Workspace of the chained state pass: control words (the error word at byte
-// 4, a ticket) and one flag per (chunk slot, head, wave).
+// 4, the tickets of the eight per-XCD work queues at words 8..15) and one
+// 64-bit flag per (chunk slot, head, wave).
 size_t chain_ws_bytes(const ScanShape &s);
 // ssd_scan_fwd on the MFMA path, three launches.  With `chain` (a region of
 // chain_ws_bytes): the C.B tiles, the chunk states with the in-block cumsum

@@ -261,7 +261,8 @@ ssd_status check_varlen(const ssd_varlen_desc *d, ScanShape *s) {
 }
 
 // The scan after argument checks: workspace = Acs | states | C.B tiles |
-// activated dt (layout of workspace_bytes).
+// activated dt | hand-off flags of the chained state pass (layout of
+// staged_ws_bytes; the single-kernel path carves its own).
 void run_scan(const ScanShape &s, const ssd::DtAct &act, const void *z, const void *x,
               const float *dt, const float *A, const void *B, const void *C, const float *D,
               const float *init_state, void *y, float *final_state, char *ws, hipStream_t hs) {
