@@ -42,7 +42,9 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
     const ChunkPos cp = chunk_pos(ctab, c, Q, L);
     const int64_t t0 = cp.t0;
     const int q = cp.q;
-    if (q <= 0) return;  // an unused slot of a variable-length batch
+    // an unused slot of a variable-length batch, or a row tile wholly past
+    // the end of a short chunk: the chunk output has no rows there
+    if (32 * ti >= q) return;
     const unsigned rs = G * N;
     const bf16 *bbase = Bm + ((b * L + t0) * G + g) * N;
     const bf16 *cbase = Cm + ((b * L + t0) * G + g) * N;
@@ -80,7 +82,8 @@ __device__ __forceinline__ void cb_tile(const bf16 *__restrict__ Bm, const bf16 
 // (p = w mod NI/2), NI+1 tiles in all, so the waves are evenly loaded.  The
 // C rows of a row tile are loaded once for all its tiles (cb_tile loads them
 // per tile).  Rows past the end of a short chunk are clamped to its last row,
-// as in cb_tile.  `bs` is the block's LDS: 256 rows of N + 8 bf16.
+// as in cb_tile, and row tiles wholly past it are skipped.  `bs` is the
+// block's LDS: 256 rows of N + 8 bf16.
 template <int Q, int N>
 __device__ __forceinline__ void cb_block(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
                                          u32x4 *__restrict__ cb, u32x4 *__restrict__ cfr,
@@ -128,6 +131,7 @@ __device__ __forceinline__ void cb_block(const bf16 *__restrict__ Bm, const bf16
 #pragma unroll 1
     for (int side = 0; side < 2; ++side) {
         const int ti = side == 0 ? p : NI - 1 - p;
+        if (32 * ti >= q) continue;  // wholly past the end of a short chunk
         const unsigned co = (unsigned)min(32 * ti + il, q - 1) * rs + 8u * g2;
         u32x4 crow[KS];
 #pragma unroll

@@ -245,6 +245,14 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
         }
     };
 
+    // stages that hold tokens of this chunk: a short chunk (the last of a
+    // sequence) skips the stages after them, rounded up to the pair the loop
+    // below takes at a time (their x and B rows are masked to zero, so they
+    // would add exact zeros)
+    const int nst = NST == 1 ? 1
+                              : __builtin_amdgcn_readfirstlane(
+                                    min(NST, 2 * ((q + 2 * kJT - 1) / (2 * kJT))));
+
     // prefetch distance two: stage s+2's loads are issued while stage s is
     // multiplied and stage s+1 (already in registers) is written to LDS
     load_stage(0, R[0]);
@@ -257,9 +265,10 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
     f32x16 acc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[t] = zero16();
-    auto step = [&](int st, auto par) {
+    // lim: the stages run (nst, or the constant NST for a whole chunk)
+    auto step = [&](int st, int lim, auto par) {
         constexpr int PAR = decltype(par)::value;  // st % 2, the LDS buffer
-        if (st + 2 < NST) load_stage(st + 2, R[PAR]);
+        if (st + 2 < lim) load_stage(st + 2, R[PAR]);
 #pragma unroll
         for (int ks = 0; ks < kJT / 16; ++ks) {
 #pragma unroll
@@ -272,15 +281,21 @@ k_chunk_state_mfma(const TX *__restrict__ x, const bf16 *__restrict__ Bm,
                 acc[t] = mfma32(al, bb, acc[t]);
             }
         }
-        if (st + 1 < NST) store_stage(st + 1, PAR ^ 1, R[PAR ^ 1]);
+        if (st + 1 < lim) store_stage(st + 1, PAR ^ 1, R[PAR ^ 1]);
         __syncthreads();
     };
     if constexpr (NST == 1) {  // a 32-token chunk: one stage
-        step(0, P0{});
-    } else {
+        step(0, 1, P0{});
+    } else if (nst == NST) {  // a whole chunk: the loop unrolled at compile time
         for (int st = 0; st < NST; st += 2) {  // NST is even
-            step(st, P0{});
-            step(st + 1, P1{});
+            step(st, NST, P0{});
+            step(st + 1, NST, P1{});
+        }
+    } else {  // a short chunk
+#pragma unroll 1
+        for (int st = 0; st < nst; st += 2) {  // nst is even
+            step(st, nst, P0{});
+            step(st + 1, nst, P1{});
         }
     }
     // this lane's element r of tile t: row p, column n of the 64 x N state
@@ -590,6 +605,9 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         *reinterpret_cast<u32x4 *>(&xs[(e >> 3) * LDX + 8 * (e & 7)]) = xv[i];
     }
     __syncthreads();  // x staged; H no longer read: its LDS becomes the y staging rows
+    // a wave whose 32 rows all lie past the end of a short chunk (the last of
+    // a sequence) has no output: it leaves here (no block barrier follows)
+    if (ti * 32 >= q) return;
 
     bf16 *ys = reinterpret_cast<bf16 *>(hu) + wave * 32 * LDY;
     const bf16 *ybase = y + ((b * L + t0) * H + h) * kP;
