@@ -31,6 +31,12 @@ def announce(msg):
 CASES = {
     "mfma_edges": ([0, 1, 255, 256, 257, 700, 3, 0, 512, 33], 8, 64, 128, 2, 256, "bf16"),
     "mfma_q64_n64": ([64, 63, 65, 1, 200, 0, 130], 4, 64, 64, 1, 64, "bf16"),
+    # last chunks ending at, before and after the 32-row tiles and the
+    # 64-token stage pairs (short chunks skip their empty stages, output
+    # rows and C.B row tiles)
+    "mfma_tile_bounds": ([32, 64, 95, 96, 97, 160, 224, 225, 288, 287], 4, 64, 64, 1, 256,
+                         "bf16"),
+    "mfma_q128_tails": ([31, 32, 33, 96, 97, 127, 192, 193, 0, 5], 4, 64, 128, 1, 128, "bf16"),
     "generic_f32": ([0, 17, 64, 65, 150, 1, 90], 4, 16, 16, 2, 64, "f32"),
     "generic_bf16_p32": ([5, 128, 129, 0, 300], 4, 32, 32, 2, 128, "bf16"),
 }
