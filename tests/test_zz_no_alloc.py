@@ -32,14 +32,19 @@ def noalloc(d, chunk):
     return y, fin
 
 
-def test_noalloc_matches_scan_fwd_twice():
+@pytest.mark.parametrize("path", ["auto", "chained"])
+def test_noalloc_matches_scan_fwd_twice(path, monkeypatch):
+    """Both state-pass arrangements: the chained one keeps its hand-off flags
+    in the scratch too, cleared by a kernel on every call."""
+    if path != "auto":
+        monkeypatch.setenv("SSD_PREFILL_PATH", path)
     specs = [synth.WORKLOADS["m2p7b_bf16"],
              synth.custom_spec(2, 777, 8, 64, 128, 2, 256, "bf16", dt_rule="ranged",
                                init="normal", seed=51)]
     assert specs[1].batch * specs[1].seqlen * specs[1].nheads < \
         specs[0].batch * specs[0].seqlen * specs[0].nheads
     for spec in specs:
-        print(f"[case] noalloc {spec}", flush=True)
+        print(f"[case] noalloc path={path} {spec}", flush=True)
         sys.stdout.flush()
         d = to_dev(synth.scan_inputs(spec), DEV)
         y0, f0 = ssd.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
