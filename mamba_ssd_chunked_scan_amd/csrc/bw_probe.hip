@@ -49,6 +49,7 @@ extern "C" {
 // for invalid arguments, or 1 if the launch failed.
 int ssd_bw_run(int kind, void *dst, const void *src, size_t bytes, void *stream) {
     if (bytes % 16 || !dst || (kind != 2 && !src) || kind < 0 || kind > 2) return -1;
+    if (((uintptr_t)dst | (uintptr_t)src) & 15) return -1;
     const int64_t n = (int64_t)(bytes / 16);
     if (n == 0) return 0;
     const int64_t nb = (n + 255) / 256;

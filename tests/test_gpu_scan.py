@@ -28,8 +28,9 @@ def announce(msg):
 
 
 def run_gpu(inp, chunk, **kw):
-    """ssd_scan_fwd on the device copies of inp; on shapes that run the
-    single-kernel path, also checks that every hand-off wait completed."""
+    """ssd_scan_fwd on the device copies of inp; on calls that hand states
+    between blocks (the chained state pass or the single-kernel path), also
+    checks that every hand-off wait completed."""
     d = to_dev(inp, DEV)
     x = d["x"]
     ws = torch.empty(max(ssd.workspace_size(x.shape[0], x.shape[1], x.shape[2], x.shape[3],

@@ -13,7 +13,7 @@ import torch
 import oracle
 from oracle import edges as oe
 import mamba_ssd_chunked_scan_amd as ssd
-from mamba_ssd_chunked_scan_amd import synth
+from mamba_ssd_chunked_scan_amd import binding, synth
 
 from helpers import TOL, f64, rel_err
 
@@ -47,13 +47,25 @@ def _dev(inp):
 
 
 def _run(d, chunk, edges=False, **kw):
+    """ssd_scan_fwd_varlen on device inputs; on calls that hand states between
+    blocks, also checks that every hand-off wait completed."""
     e = {}
     if edges:
         e = dict(dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=LIMIT, z=d["gate"])
+    total, H, P = d["x"].shape
+    G, N = d["B"].shape[1], d["B"].shape[2]
+    nseq = d["cu_seqlens"].numel() - 1
+    io = binding.SSD_BF16 if d["x"].dtype == torch.bfloat16 else binding.SSD_F32
+    ws = torch.empty(max(binding.varlen_workspace_size(nseq, total, H, P, N, G, chunk,
+                                                       d["x"].dtype), 1),
+                     dtype=torch.uint8, device=DEV)
     y, fin = ssd.scan_fwd_varlen(d["x"], d["dt_raw"] if edges else d["dt"], d["A"], d["B"],
                                  d["C"], d["cu_seqlens"], d["D"], chunk=chunk,
-                                 init_states=d["init"], **e, **kw)
+                                 init_states=d["init"], workspace=ws, **e, **kw)
     torch.cuda.synchronize()
+    desc = binding.VarlenDesc(nseq, total, H, P, N, G, chunk, io, 0)
+    err = binding.error_word(ws, desc, varlen=True)
+    assert err in (None, 0), f"a hand-off wait ran out (error word {err})"
     return y, fin
 
 
