@@ -14,7 +14,7 @@ import torch
 import oracle
 from oracle import edges as oe
 import mamba_ssd_chunked_scan_amd as ssd
-from mamba_ssd_chunked_scan_amd import synth
+from mamba_ssd_chunked_scan_amd import binding, synth
 
 from helpers import TOL, f64, rel_err
 
@@ -49,9 +49,17 @@ def _run(spec, which, inp):
         kw.update(dt_bias=d["dt_bias"], dt_softplus=True, dt_limit=LIMIT)
     if use_gate:
         kw["z"] = d["gate"]
-    y, fin = ssd.scan_fwd(d["x"], d["dt_raw"] if use_dt else d["dt"], d["A"], d["B"], d["C"],
-                          d["D"], chunk=spec.chunk, init_state=d["init"], **kw)
+    x = d["x"]
+    ws = torch.empty(max(ssd.workspace_size(x.shape[0], x.shape[1], x.shape[2], x.shape[3],
+                                            d["B"].shape[3], d["B"].shape[2], spec.chunk,
+                                            x.dtype), 1),
+                     dtype=torch.uint8, device=DEV)
+    y, fin = ssd.scan_fwd(x, d["dt_raw"] if use_dt else d["dt"], d["A"], d["B"], d["C"],
+                          d["D"], chunk=spec.chunk, init_state=d["init"], workspace=ws, **kw)
     torch.cuda.synchronize()
+    # every hand-off wait of the call completed (None: the call has none)
+    err = binding.error_word(ws, binding._scan_desc(x, d["B"], spec.chunk))
+    assert err in (None, 0), f"a hand-off wait ran out (error word {err})"
     return y, fin
 
 
