@@ -39,7 +39,7 @@ using namespace mx;
 
 constexpr int kBQ = 32;         // tokens per gradient chunk
 constexpr int kBThreads = 256;
-constexpr int kHeadsPerBlock = 4;
+constexpr int kHeadsPerBlock = 4;  // of the generic (VALU) kernel
 
 // LDS layout (floats), rows padded to multiples of 4 plus 4 (16-byte rows,
 // staggered banks): B, C [Q][NS]; x, dy [Q][PS]; CB, CB L, K L, GD [Q][LQ];
@@ -944,17 +944,38 @@ void allow_dynamic_lds(int bytes) {
         done[dev] = true;
 }
 
+// Heads per block of the per-chunk gradient.  One block fits a CU (its LDS),
+// so the grid of groups * ceil(R / hpb) blocks runs in rounds of one block
+// per CU, and a block takes about hpb + 0.5 head-times (the heads one after
+// another, plus the staging of B, C and C.B and the dB / dC atomics it does
+// once).  The choice minimises rounds * (hpb + 0.5), the larger hpb on a tie
+// (fewer atomics).  Measured at the 2.7B workload (64 chunk groups, 80
+// heads): hpb 20 (one round of 256 blocks) 472-481 us per gradient call, 10
+// 490-496, 5 498-499, 4 501-517, 8 527-531, 2 533-545, 16 (1.25 rounds) 612,
+// 40 (half the CUs idle) 688-690.
+int bwd_heads_per_block(int64_t groups, int64_t R, int cus) {
+    int best = 1;
+    double best_cost = 0.0;
+    for (int hpb = 1; hpb <= R; ++hpb) {
+        const int64_t nb = groups * ((R + hpb - 1) / hpb);
+        const int64_t rounds = (nb + cus - 1) / cus;
+        const double cost = (double)rounds * (hpb + 0.5);
+        if (hpb == 1 || cost <= best_cost) {
+            best = hpb;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <int N, int QT>
 void launch_bwd_mfma_t(const ScanShape &s, const void *x, const float *dt, const float *A,
                        const void *Bm, const void *Cm, const float *D, const float *Acs,
                        const float *Hs, const float *Es, const void *dy, void *dx, float *ddt,
                        float *dB, float *dC, float *dA, float *dD, hipStream_t st) {
     allow_dynamic_lds<&k_chunk_bwd_mfma<N, QT>>(BwdLds<N, QT>::BYTES);
-    // heads per block: 4 (dB and dC accumulate over them before their
-    // atomics), fewer when that would leave the grid under two blocks per CU
     const int64_t R = s.H / s.G;
-    int hpb = kHeadsPerBlock;
-    while (hpb > 1 && s.B * s.T * s.G * ((R + hpb - 1) / hpb) < 512) hpb /= 2;
+    const int hpb = bwd_heads_per_block(s.B * s.T * s.G, R, device_cus());
     const int64_t nslices = (R + hpb - 1) / hpb;
     const int64_t nblocks = s.B * s.T * s.G * nslices;
     k_chunk_bwd_mfma<N, QT><<<padded_grid(nblocks), 256 * QT, BwdLds<N, QT>::BYTES, st>>>(

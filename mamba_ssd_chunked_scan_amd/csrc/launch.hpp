@@ -145,6 +145,9 @@ void launch_bwd_states_cumsum_mfma(const ScanShape &s, const void *x, const void
                                    const float *dt, const float *A, float *Acs, float *out,
                                    const DtAct &act, float *dt_out, hipStream_t st);
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 // Whether the MFMA kernels handle this shape (otherwise the generic ones run).
 bool mfma_supported(const ScanShape &s);
 void launch_chunk_state_mfma(const ScanShape &s, const void *x, const void *Bm,

@@ -1,7 +1,7 @@
 // C-ABI layer of libssd: argument validation, workspace carving and the
 // launch sequence.  Every check happens before the first HIP call; the only
-// HIP calls made here are kernel launches (through the launchers) and
-// hipGetLastError.
+// HIP calls made here are kernel launches (through the launchers),
+// hipGetLastError and, once per device, the query of its compute units.
 #include <cstring>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -14,6 +14,24 @@
 
 using ssd::ScanShape;
 using ssd::StepShape;
+
+namespace ssd {
+
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+        v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+}  // namespace ssd
 
 namespace {
 
@@ -107,21 +125,8 @@ size_t workspace_bytes(const ScanShape &s) {
 }
 
 // Blocks the single-kernel prefill keeps resident: two per compute unit of
-// the current device (looked up once per device).
-int resident_blocks() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    int v = cache[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    v = 2 * cus;
-    cache[dev].store(v, std::memory_order_relaxed);
-    return v;
-}
+// the current device.
+int resident_blocks() { return 2 * ssd::device_cus(); }
 
 // The single-kernel prefill is opt-in (SSD_PREFILL_PATH=fused): measured side
 // by side it is slower than the separate stage kernels on every workload

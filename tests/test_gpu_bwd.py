@@ -75,9 +75,9 @@ SHAPES = {
     "bf16_n64_groups": (2, 77, 6, 64, 64, 2, "bf16"),
     "bf16_n128_groups": (1, 45, 10, 64, 128, 2, "bf16"),
     "bf16_n64_one_token_tail": (1, 33, 4, 64, 64, 1, "bf16"),
-    # enough 64-token chunks that the kernel takes two heads per block (11
-    # heads: the last block of each group has one)
-    "bf16_two_heads_per_block": (4, 2048, 11, 64, 64, 1, "bf16"),
+    # enough 64-token chunks that the kernel takes several heads per block,
+    # with a shorter last slice (11 heads: slices of 6 and 5 on 256 CUs)
+    "bf16_heads_per_block": (4, 2048, 11, 64, 64, 1, "bf16"),
 }
 
 
