@@ -118,6 +118,56 @@ def test_workload_batched_long_rows(path, monkeypatch):
         del yo, fo
 
 
+@pytest.mark.parametrize("path", ["auto", "separate"])
+def test_offsets_past_2gib(path, monkeypatch):
+    """x, y, B and C past 2^31 bytes: 4,194,381 tokens x 8 heads of headdim 64
+    (4.3 GB of bf16 x, 16,385 chunks with a 77-token last one), inputs drawn
+    on the device.  The oracle checks 333 tokens from two cut points, the
+    chunk that starts at byte 2^31 of x and the last full chunk with the
+    tail (and the final state), each from the state the GPU reaches at the
+    cut (a prefix call).  The automatic choice chains the state pass."""
+    if path == "separate":
+        monkeypatch.setenv("SSD_PREFILL_PATH", "separate")
+    Bt, L, H, P, N, G, Q = 1, (1 << 22) + 77, 8, 64, 128, 1, 256
+    announce(f"scan_fwd {L} tokens x {H} heads, past 2 GiB, path={path}")
+    gen = torch.Generator(device=DEV).manual_seed(61)
+    bf = torch.bfloat16
+    x = torch.randn((Bt, L, H, P), generator=gen, device=DEV, dtype=bf)
+    B = torch.randn((Bt, L, G, N), generator=gen, device=DEV, dtype=bf)
+    C = torch.randn((Bt, L, G, N), generator=gen, device=DEV, dtype=bf)
+    dt = torch.rand((Bt, L, H), generator=gen, device=DEV) * 0.099 + 0.001
+    A = -torch.exp(torch.rand((H,), generator=gen, device=DEV) * float(np.log(16.0)))
+    D = torch.randn((H,), generator=gen, device=DEV)
+    init = torch.randn((Bt, H, P, N), generator=gen, device=DEV) * 0.1
+    assert x.numel() * x.element_size() > (1 << 32)
+    ws = torch.empty(ssd.workspace_size(Bt, L, H, P, N, G, Q, bf), dtype=torch.uint8, device=DEV)
+    y, fin = ssd.scan_fwd(x, dt, A, B, C, D, chunk=Q, init_state=init, workspace=ws)
+    torch.cuda.synchronize()
+    err = binding.error_word(ws, binding._scan_desc(x, B, Q))
+    assert err in (None, 0), f"a hand-off wait ran out (error word {err})"
+    del ws
+    T = -(-L // Q)
+    tol = TOL[bf]
+    for L0 in ((T // 2) * Q, (T - 2) * Q):
+        _, f0 = ssd.scan_fwd(x[:, :L0], dt[:, :L0], A, B[:, :L0], C[:, :L0], D, chunk=Q,
+                             init_state=init)
+        torch.cuda.synchronize()
+        n = min(333, L - L0)
+        sl = slice(L0, L0 + n)
+        yo, fo = oracle.scan(x[:, sl].cpu(), dt[:, sl].cpu(), A.cpu(), B[:, sl].cpu(),
+                             C[:, sl].cpu(), D.cpu(), f0.cpu())
+        ey = rel_err(f64(y[:, sl]), yo)
+        print(f"  tokens {L0}..{L0 + n}: rel_err y {ey:.3e}", flush=True)
+        assert ey <= tol, f"y rel err {ey:.3e} from token {L0}"
+        if L0 + n == L:
+            ef = rel_err(f64(fin), fo)
+            print(f"  final state rel_err {ef:.3e}", flush=True)
+            assert ef <= tol, f"final rel err {ef:.3e}"
+        del f0
+    del x, B, C, y
+    torch.cuda.empty_cache()
+
+
 SHAPES = [
     # Bt, L, H, P, N, G, chunk, dtype
     (1, 256, 4, 16, 16, 1, 64, "f32"),
