@@ -46,6 +46,37 @@ def test_single_step(shape):
     assert rel_err(f64(sd), so) <= TOL[dtype]
 
 
+def test_step_state_past_2gib():
+    """One step at batch 1024 with the 2.7B head shape: 2.7 GB of fp32 state,
+    rows past byte 2^31 of it.  Sampled batch rows (the first, the one that
+    starts past 2^31 bytes, the last) against the oracle step; the inputs are
+    drawn on the device."""
+    Bt, H, P, N, G = 1024, 80, 64, 128, 1
+    print(f"[case] step batch {Bt}, state past 2 GiB", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(71)
+    bf = torch.bfloat16
+    sd = torch.randn((Bt, H, P, N), generator=gen, device=DEV) * 0.1
+    assert sd.numel() * 4 > (1 << 31)
+    x = torch.randn((Bt, H, P), generator=gen, device=DEV, dtype=bf)
+    dt = torch.rand((Bt, H), generator=gen, device=DEV) * 0.1
+    A = -torch.rand((H,), generator=gen, device=DEV) * 8
+    B = torch.randn((Bt, G, N), generator=gen, device=DEV, dtype=bf)
+    C = torch.randn((Bt, G, N), generator=gen, device=DEV, dtype=bf)
+    D = torch.randn((H,), generator=gen, device=DEV)
+    rows = [0, (1 << 31) // (H * P * N * 4) + 1, Bt - 1]
+    before = {b: sd[b:b + 1].cpu() for b in rows}
+    y = ssd.step(sd, x, dt, A, B, C, D)
+    torch.cuda.synchronize()
+    for b in rows:
+        sl = slice(b, b + 1)
+        yo, so = oracle.step(before[b], x[sl].cpu(), dt[sl].cpu(), A.cpu(), B[sl].cpu(),
+                             C[sl].cpu(), D.cpu())
+        assert rel_err(f64(y[sl]), yo) <= TOL[bf], b
+        assert rel_err(f64(sd[sl]), so) <= TOL[bf], b
+    del sd
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["decode_2p7b_b1", "decode_2p7b_b64"])
 def test_decode_chain_4096(name):
     spec = synth.DECODE_WORKLOADS[name]

@@ -131,6 +131,42 @@ def test_equal_lengths_equal_batched_call(Bt, L, H, P, N, G, Q, dt_):
     assert torch.equal(y, yb.view(y.shape)) and torch.equal(fin, fb)
 
 
+@pytest.mark.parametrize("path", ["separate", "chained"])
+def test_sequence_past_2gib(path, monkeypatch):
+    """A ragged batch whose second sequence (333 tokens) starts past byte
+    2^31 of the packed x: 2,097,300 + 333 tokens x 8 heads of headdim 64,
+    inputs drawn on the device.  The oracle checks the second sequence whole
+    (y and final state) and the first 333 tokens of the first one."""
+    monkeypatch.setenv("SSD_PREFILL_PATH", path)
+    lens = [2_097_300, 333]
+    total, H, P, N, G, Q = sum(lens), 8, 64, 128, 1, 256
+    print(f"[case] varlen {lens} x {H} heads, past 2 GiB, path={path}", flush=True)
+    gen = torch.Generator(device=DEV).manual_seed(63)
+    bf = torch.bfloat16
+    d = {
+        "x": torch.randn((total, H, P), generator=gen, device=DEV, dtype=bf),
+        "B": torch.randn((total, G, N), generator=gen, device=DEV, dtype=bf),
+        "C": torch.randn((total, G, N), generator=gen, device=DEV, dtype=bf),
+        "dt": torch.rand((total, H), generator=gen, device=DEV) * 0.099 + 0.001,
+        "A": -torch.exp(torch.rand((H,), generator=gen, device=DEV) * float(np.log(16.0))),
+        "D": torch.randn((H,), generator=gen, device=DEV),
+        "init": torch.randn((len(lens), H, P, N), generator=gen, device=DEV) * 0.1,
+        "cu_seqlens": torch.tensor([0, lens[0], total], dtype=torch.int32, device=DEV),
+    }
+    assert lens[0] * H * P * 2 > (1 << 31)
+    y, fin = _run(d, Q)
+    for s, (t0, n) in enumerate([(lens[0], lens[1]), (0, 333)]):
+        sl = slice(t0, t0 + n)
+        cpu = {k: d[k][sl].cpu().unsqueeze(0) for k in ("x", "dt", "B", "C")}
+        yo, fo = oracle.scan(cpu["x"], cpu["dt"], d["A"].cpu(), cpu["B"], cpu["C"],
+                             d["D"].cpu(), d["init"][1 - s:2 - s].cpu())
+        assert rel_err(f64(y[sl].unsqueeze(0)), yo) <= TOL[bf], s
+        if s == 0:  # the second sequence, whole
+            assert rel_err(f64(fin[1:2]), fo) <= TOL[bf]
+    del d, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("path", ["separate", "chained", "fused"])
 def test_serving_mix_2p7b_sampled(path, monkeypatch):
     """32 requests of log-uniform length in [16, 4096] at the 2.7B head shape
