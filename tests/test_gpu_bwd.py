@@ -142,6 +142,44 @@ def test_bwd_2p7b_sampled_and_repeatable():
         assert rel_err(np.array([float(g["dD"][h])]), ref["dD"]) <= tol, h
 
 
+def test_bwd_past_2gib():
+    """The gradient of a 4,194,381-token x 8-head prefill (4.3 GB of bf16 x
+    and dy, 65,537 gradient chunks), inputs drawn on the device.  The last
+    333 tokens (byte offsets past 2^32) are checked: the oracle's VJP of that
+    suffix, started from the forward state the GPU reaches at the cut (a
+    prefix call), with the same dy and dfinal, gives their dx, ddt, dB and
+    dC (dA, dD and dinit sum over the whole sequence)."""
+    Bt, L, H, P, N, G, Q = 1, (1 << 22) + 77, 8, 64, 128, 1, 256
+    announce(f"bwd {L} tokens x {H} heads, past 2 GiB")
+    gen = torch.Generator(device=DEV).manual_seed(65)
+    bf = torch.bfloat16
+    x = torch.randn((Bt, L, H, P), generator=gen, device=DEV, dtype=bf)
+    dy = torch.randn((Bt, L, H, P), generator=gen, device=DEV, dtype=bf)
+    B = torch.randn((Bt, L, G, N), generator=gen, device=DEV, dtype=bf)
+    C = torch.randn((Bt, L, G, N), generator=gen, device=DEV, dtype=bf)
+    dt = torch.rand((Bt, L, H), generator=gen, device=DEV) * 0.099 + 0.001
+    A = -torch.exp(torch.rand((H,), generator=gen, device=DEV) * float(np.log(16.0)))
+    D = torch.randn((H,), generator=gen, device=DEV)
+    init = torch.randn((Bt, H, P, N), generator=gen, device=DEV) * 0.1
+    dfinal = torch.randn((Bt, H, P, N), generator=gen, device=DEV)
+    g = ssd.scan_bwd(x, dt, A, B, C, dy, D, init, dfinal, chunk=Q)
+    torch.cuda.synchronize()
+    L0 = L - 333
+    _, h0 = ssd.scan_fwd(x[:, :L0], dt[:, :L0], A, B[:, :L0], C[:, :L0], D, chunk=Q,
+                         init_state=init)
+    torch.cuda.synchronize()
+    sl = slice(L0, L)
+    ref = oracle.scan_vjp(x[:, sl].cpu(), dt[:, sl].cpu(), A.cpu(), B[:, sl].cpu(),
+                          C[:, sl].cpu(), D.cpu(), h0.cpu(), dy=dy[:, sl].cpu(),
+                          dfinal=dfinal.cpu())
+    for k in ("dx", "ddt", "dB", "dC"):
+        e = rel_err(f64(g[k][:, sl]), ref[k])
+        print(f"  {k} rel_err {e:.3e}", flush=True)
+        assert e <= TOL[bf], (k, e)
+    del g, x, dy, B, C
+    torch.cuda.empty_cache()
+
+
 EDGE_SHAPES = {
     "bf16_mfma": (1, 300, 4, 64, 128, 1, "bf16"),
     "bf16_mfma_groups": (2, 77, 6, 64, 64, 2, "bf16"),
