@@ -27,6 +27,8 @@
 // weight).  H and E of every chunk come from the forward state pass and its
 // reverse, run by the caller; the derivative with respect to H itself is
 // carried by that reverse pass.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_ops.hpp"
@@ -934,14 +936,14 @@ k_chunk_bwd_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
 // shows up as the launch's own error.
 template <auto *Kernel>
 void allow_dynamic_lds(int bytes) {
-    static bool done[64];
+    static std::atomic<bool> done[64];  // host threads may launch concurrently
     int dev = 0;
     const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
-    if (known && done[dev]) return;
+    if (known && done[dev].load(std::memory_order_relaxed)) return;
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess &&
         known)
-        done[dev] = true;
+        done[dev].store(true, std::memory_order_relaxed);
 }
 
 // Heads per block of the per-chunk gradient.  One block fits a CU (its LDS),
