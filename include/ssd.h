@@ -153,7 +153,10 @@ ssd_status ssd_scan_fwd(const ssd_scan_desc *d, const void *x, const float *dt,
  * call on one device shares that device's scratch: two calls that may
  * overlap on one device (different streams, or threads) race and must not be
  * made.  The first call on a device looks up the scratch's device address
- * (hipGetSymbolAddress); a failure there returns SSD_ERR_HIP. */
+ * (hipGetSymbolAddress); a failure there returns SSD_ERR_HIP.  A call that
+ * takes the chained state pass (see ssd_scan_fwd) keeps its error word in
+ * the scratch too, where the caller cannot read it; a caller that must check
+ * it uses ssd_scan_fwd with a workspace, or SSD_PREFILL_PATH=separate. */
 ssd_status ssd_scan_fwd_noalloc(const ssd_scan_desc *d, const void *x, const float *dt,
                                 const float *A, const void *B, const void *C, const float *D,
                                 const float *init_state, void *y, float *final_state,
