@@ -168,6 +168,43 @@ def test_offsets_past_2gib(path, monkeypatch):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("path", ["auto", "chained"])
+def test_two_streams_at_once(path, monkeypatch):
+    """Two prefill calls on two streams at the same time, each with its own
+    workspace, give bit for bit what each gives alone: the library keeps no
+    per-call state outside the caller's buffers (the chained state pass's
+    flags and error word included)."""
+    if path == "chained":
+        monkeypatch.setenv("SSD_PREFILL_PATH", "chained")
+    specs = [synth.WORKLOADS["m130m_bf16"],
+             synth.custom_spec(2, 1000, 16, 64, 128, 2, 256, "bf16", dt_rule="ranged",
+                               init="normal", seed=81)]
+    announce(f"two streams path={path}")
+    runs = []
+    for spec in specs:
+        d = to_dev(synth.scan_inputs(spec), DEV)
+        x = d["x"]
+        ws = torch.empty(ssd.workspace_size(*x.shape, d["B"].shape[3], d["B"].shape[2],
+                                            spec.chunk, x.dtype), dtype=torch.uint8, device=DEV)
+        y0, f0 = ssd.scan_fwd(x, d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=spec.chunk,
+                              init_state=d["init"], workspace=ws)
+        runs.append((spec, d, ws, y0, f0))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in runs]
+    outs = []
+    for rep in range(3):
+        for (spec, d, ws, _, _), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                outs.append(ssd.scan_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                         chunk=spec.chunk, init_state=d["init"], workspace=ws))
+    torch.cuda.synchronize()
+    for i, (y, f) in enumerate(outs):
+        spec, d, ws, y0, f0 = runs[i % len(runs)]
+        assert torch.equal(y, y0) and torch.equal(f, f0), (i, spec.name)
+        err = binding.error_word(ws, binding._scan_desc(d["x"], d["B"], spec.chunk))
+        assert err in (None, 0)
+
+
 SHAPES = [
     # Bt, L, H, P, N, G, chunk, dtype
     (1, 256, 4, 16, 16, 1, 64, "f32"),
