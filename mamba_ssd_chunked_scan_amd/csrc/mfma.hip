@@ -764,13 +764,15 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
         }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
     __builtin_amdgcn_wave_barrier();
+    // nontemporal (y is not read again here; measured 1 us less per call at
+    // the 2.7B shape than plain stores, bit for bit the same)
     const uint32_t yvoff = ((unsigned)(lane >> 3) * xrs + 8u * (lane & 7)) * 2u;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int r = (lane >> 3) + 8 * kk, sg = lane & 7;
         const u32x4 o = *reinterpret_cast<const u32x4 *>(&ys[r * LDY + 8 * sg]);
-        buffer_store16(o, buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32 + 8 * kk) * xrs * 2u),
-                       yvoff);
+        buffer_store16_nt(o, buffer_rsrc_at(ybase, xy_bytes, (unsigned)(ti * 32 + 8 * kk) * xrs * 2u),
+                          yvoff);
     }
 }
 

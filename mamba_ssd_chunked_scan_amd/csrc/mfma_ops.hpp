@@ -128,6 +128,11 @@ __device__ __forceinline__ u32x4 buffer_load16(rsrc_t r, uint32_t voff) {
 __device__ __forceinline__ void buffer_store16(u32x4 v, rsrc_t r, uint32_t voff) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
 }
+// The same with the nontemporal cache policy (nt), for data not read again
+// soon.
+__device__ __forceinline__ void buffer_store16_nt(u32x4 v, rsrc_t r, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 2);
+}
 
 }  // namespace mx
 }  // namespace ssd
