@@ -481,7 +481,7 @@ k_chunk_scan_mfma(const bf16 *__restrict__ x, const float *__restrict__ dt,
     constexpr int NI = Q / 32, NT = NI * (NI + 1) / 2, KS = N / 16;
     constexpr int TH = Q * 2;             // threads: NI waves
     constexpr int LDH = N + 8;            // H rows, read as plain 16-byte operands
-    constexpr int LDX = kP + 16;          // x rows, read transposed
+    constexpr int LDX = kP + 8;           // x rows, read transposed
     constexpr int LDY = kP + 8;           // bf16 y staging rows
     constexpr int H_BYTES = 2 * kP * LDH * 2;
     constexpr int Y_BYTES = NI * 32 * LDY * 2;
